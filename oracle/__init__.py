@@ -1,0 +1,228 @@
+"""CPU oracle for the Q4_K fused dequantize-and-multiply GEMV (test infrastructure).
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  The product path (the HIP library and its binding) never
+does and shares no code with it.  The arithmetic lives in ``q4k_oracle.c``
+(plain C, built with ``-ffp-contract=off``); this module only builds it with
+gcc, loads it with ctypes and marshals numpy arrays.
+
+Functions (names follow the problem's notation: d, dmin, sc_j, m_j, q):
+  f16_to_f32(bits)            binary16 decode from its definition
+  f32_to_f16_rne(values)      binary16 encode, round-to-nearest-even
+  unpack_scales(s12)          12 packed bytes -> (sc[8], m[8])
+  pack_scales(sc, m)          the inverse, written from the same bit table
+  dequant(w, n, k)            f32 weights [n, k], one rounding per weight
+  gemv(w, x)                  y and sum|w||x| in f64, x is [m, k]
+  gemv_rows(w, x, rows)       the same for listed rows only
+  quantize_rows(x)            simple reference quantizer -> Q4_K bytes
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "q4k_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle_q4k.so")
+
+QK = 256
+SB_BYTES = 144
+
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (OpenMP, no FP contraction)."""
+    if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
+        return _LIB
+    tmp = _LIB + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+           "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra",
+           "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        u8p = ctypes.POINTER(ctypes.c_uint8)
+        f32p = ctypes.POINTER(ctypes.c_float)
+        f64p = ctypes.POINTER(ctypes.c_double)
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        i64 = ctypes.c_int64
+        lib.oq_f16_to_f32.argtypes = [ctypes.c_uint16]
+        lib.oq_f16_to_f32.restype = ctypes.c_float
+        lib.oq_f32_to_f16_rne.argtypes = [ctypes.c_float]
+        lib.oq_f32_to_f16_rne.restype = ctypes.c_uint16
+        lib.oq_unpack_scales.argtypes = [u8p, u8p, u8p]
+        lib.oq_unpack_scales.restype = None
+        lib.oq_pack_scales.argtypes = [u8p, u8p, u8p]
+        lib.oq_pack_scales.restype = None
+        lib.oq_dequant_superblock.argtypes = [u8p, f32p]
+        lib.oq_dequant_superblock.restype = None
+        lib.oq_dequant.argtypes = [u8p, i64, i64, f32p]
+        lib.oq_dequant.restype = ctypes.c_int
+        lib.oq_gemv.argtypes = [u8p, f32p, i64, i64, i64, f64p, f64p]
+        lib.oq_gemv.restype = ctypes.c_int
+        lib.oq_gemv_rows.argtypes = [u8p, f32p, i64, i64, i64, i64p, i64, f64p, f64p]
+        lib.oq_gemv_rows.restype = ctypes.c_int
+        lib.oq_quantize_row.argtypes = [f32p, i64, u8p]
+        lib.oq_quantize_row.restype = ctypes.c_int
+        lib.oq_num_threads.argtypes = []
+        lib.oq_num_threads.restype = ctypes.c_int
+        lib.oq_set_num_threads.argtypes = [ctypes.c_int]
+        lib.oq_set_num_threads.restype = None
+        _lib = lib
+        return lib
+
+
+def _ptr(a: np.ndarray, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def _u8(w) -> np.ndarray:
+    a = np.ascontiguousarray(np.asarray(w, dtype=np.uint8)).reshape(-1)
+    return a
+
+
+def num_threads() -> int:
+    return int(_load().oq_num_threads())
+
+
+def set_num_threads(t: int) -> None:
+    _load().oq_set_num_threads(int(t))
+
+
+def f16_to_f32(bits) -> np.ndarray:
+    lib = _load()
+    b = np.asarray(bits, dtype=np.uint16).reshape(-1)
+    out = np.empty(b.shape, dtype=np.float32)
+    for i, v in enumerate(b.tolist()):
+        out[i] = lib.oq_f16_to_f32(v)
+    return out
+
+
+def f32_to_f16_rne(values) -> np.ndarray:
+    lib = _load()
+    v = np.asarray(values, dtype=np.float32).reshape(-1)
+    out = np.empty(v.shape, dtype=np.uint16)
+    for i, x in enumerate(v.tolist()):
+        out[i] = lib.oq_f32_to_f16_rne(x)
+    return out
+
+
+def unpack_scales(s12) -> tuple[np.ndarray, np.ndarray]:
+    lib = _load()
+    s = _u8(s12)
+    assert s.size == 12
+    sc = np.zeros(8, dtype=np.uint8)
+    m = np.zeros(8, dtype=np.uint8)
+    lib.oq_unpack_scales(_ptr(s, ctypes.c_uint8), _ptr(sc, ctypes.c_uint8), _ptr(m, ctypes.c_uint8))
+    return sc, m
+
+
+def pack_scales(sc, m) -> np.ndarray:
+    lib = _load()
+    a = _u8(sc)
+    b = _u8(m)
+    assert a.size == 8 and b.size == 8 and int(a.max()) < 64 and int(b.max()) < 64
+    s = np.zeros(12, dtype=np.uint8)
+    lib.oq_pack_scales(_ptr(a, ctypes.c_uint8), _ptr(b, ctypes.c_uint8), _ptr(s, ctypes.c_uint8))
+    return s
+
+
+def dequant_superblock(blk) -> np.ndarray:
+    lib = _load()
+    b = _u8(blk)
+    assert b.size == SB_BYTES
+    out = np.empty(QK, dtype=np.float32)
+    lib.oq_dequant_superblock(_ptr(b, ctypes.c_uint8), _ptr(out, ctypes.c_float))
+    return out
+
+
+def _check_shape(w: np.ndarray, n: int, k: int) -> None:
+    if k <= 0 or k % QK != 0 or n < 0:
+        raise ValueError("bad shape n=%d k=%d" % (n, k))
+    if w.size != n * (k // QK) * SB_BYTES:
+        raise ValueError("weight bytes %d != n*(k/256)*144 = %d" % (w.size, n * (k // QK) * SB_BYTES))
+
+
+def dequant(w, n: int, k: int) -> np.ndarray:
+    lib = _load()
+    wb = _u8(w)
+    _check_shape(wb, n, k)
+    out = np.empty((n, k), dtype=np.float32)
+    rc = lib.oq_dequant(_ptr(wb, ctypes.c_uint8), n, k, _ptr(out, ctypes.c_float))
+    if rc != 0:
+        raise RuntimeError("oq_dequant rc=%d" % rc)
+    return out
+
+
+def gemv(w, x, n: int) -> tuple[np.ndarray, np.ndarray]:
+    """y[b, r] and bound[b, r] = sum_c |w[r,c]| |x[b,c]|, both float64 [m, n]."""
+    lib = _load()
+    xa = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    if xa.ndim == 1:
+        xa = xa.reshape(1, -1)
+    m, k = xa.shape
+    wb = _u8(w)
+    _check_shape(wb, n, k)
+    y = np.empty((m, n), dtype=np.float64)
+    bound = np.empty((m, n), dtype=np.float64)
+    rc = lib.oq_gemv(_ptr(wb, ctypes.c_uint8), _ptr(xa, ctypes.c_float), n, k, m,
+                     _ptr(y, ctypes.c_double), _ptr(bound, ctypes.c_double))
+    if rc != 0:
+        raise RuntimeError("oq_gemv rc=%d" % rc)
+    return y, bound
+
+
+def gemv_rows(w, x, n: int, rows) -> tuple[np.ndarray, np.ndarray]:
+    """The oracle on listed rows only: y[b, t], bound[b, t] for row rows[t]."""
+    lib = _load()
+    xa = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    if xa.ndim == 1:
+        xa = xa.reshape(1, -1)
+    m, k = xa.shape
+    wb = _u8(w)
+    _check_shape(wb, n, k)
+    r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1))
+    y = np.empty((m, r.size), dtype=np.float64)
+    bound = np.empty((m, r.size), dtype=np.float64)
+    rc = lib.oq_gemv_rows(_ptr(wb, ctypes.c_uint8), _ptr(xa, ctypes.c_float), n, k, m,
+                          _ptr(r, ctypes.c_int64), r.size,
+                          _ptr(y, ctypes.c_double), _ptr(bound, ctypes.c_double))
+    if rc != 0:
+        raise RuntimeError("oq_gemv_rows rc=%d" % rc)
+    return y, bound
+
+
+def quantize_rows(x) -> np.ndarray:
+    """Reference quantizer: float32 [n, k] -> Q4_K bytes [n * k/256 * 144]."""
+    lib = _load()
+    xa = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    if xa.ndim == 1:
+        xa = xa.reshape(1, -1)
+    n, k = xa.shape
+    if k % QK != 0:
+        raise ValueError("k must be a multiple of 256")
+    out = np.zeros(n * (k // QK) * SB_BYTES, dtype=np.uint8)
+    rb = (k // QK) * SB_BYTES
+    for r in range(n):
+        row = np.ascontiguousarray(xa[r])
+        seg = out[r * rb:(r + 1) * rb]
+        rc = lib.oq_quantize_row(_ptr(row, ctypes.c_float), k, _ptr(seg, ctypes.c_uint8))
+        if rc != 0:
+            raise RuntimeError("oq_quantize_row rc=%d" % rc)
+    return out

@@ -1,0 +1,381 @@
+/*
+ * q4k_oracle.c -- plain, slow, obviously correct CPU oracle for the Q4_K
+ * fused dequantize-and-multiply GEMV  y[b][r] = sum_c W[r][c] * x[b][c].
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path loads, links or
+ * calls this file: only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg do.  It shares no code, header, table or constant with the
+ * HIP library; it has its own binary16 decode, its own 6-bit scale unpack and
+ * its own nibble walk.  Build with -ffp-contract=off so that every float
+ * operation below rounds exactly where it is written.
+ *
+ * What it follows (the pages are docs.rs source listings; cited by page title
+ * and the function or doc comment the fact sits in):
+ *  - memra-engine 0.83.1, src/f16_ffi.rs, extern block, doc comment of
+ *    `memra_q4_K_dequant_f16`: a Q4_K tensor is a sequence of 144-byte
+ *    superblocks; `ensure_f16_mirror`: a row of `in_f` weights holds
+ *    in_f/256 superblocks of 144 bytes, so k must be a multiple of 256.
+ *  - realizar 0.8.5, src/cuda/executor/uses.rs, doc of
+ *    `batched_q4k_gemv_into`: weights are N x K/256 superblocks shared by the
+ *    batch; the input is M x K row-major and the output M x N row-major.
+ *  - The superblock field layout inside the 144 bytes is not printed on the
+ *    pages.  It is fixed by the problem statement this build implements:
+ *    fp16 d at byte 0, fp16 dmin at byte 2, twelve bytes of packed 6-bit
+ *    (scale, min) pairs for the eight 32-element sub-blocks at byte 4, and 128
+ *    bytes of 4-bit quants at byte 16 where, in each 64-element chunk c, byte i
+ *    holds element 64c+i in its low nibble and element 64c+32+i in its high
+ *    nibble; each weight is w = d*sc_j*q - dmin*m_j.
+ *  - The bit packing of the twelve scale bytes is not on the pages either;
+ *    the reading taken is the GGUF K-quant packing (see oq_unpack_scales).
+ *  - memra-engine 0.83.1, src/f16_ffi.rs, `f16_bits_to_f32` inside
+ *    `ensure_f16_mirror`: binary16 decode keeping subnormals, infinities and
+ *    NaN.  The decode below is written from the IEEE-754 binary16 definition.
+ *
+ * Pins (tests/, CPU only): exhaustive binary16 decode against numpy's
+ * float16 conversion; exhaustive scale pack/unpack; one-hot layout brute
+ * force; hand-computed golden superblocks; closed forms; exact dyadic dots;
+ * quantizer round-trip.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define OQ_QK 256     /* elements per superblock */
+#define OQ_SB 144     /* bytes per superblock    */
+
+/* ---------------------------------------------------------------------------
+ * binary16 -> binary32, from the definition:
+ *   e == 0          : (-1)^s * 2^-14 * f/1024            (zero, subnormal)
+ *   0 < e < 31      : (-1)^s * 2^(e-15) * (1 + f/1024)   (normal)
+ *   e == 31, f == 0 : (-1)^s * inf
+ *   e == 31, f != 0 : NaN
+ * Every finite binary16 value is exactly representable in binary32, so the
+ * double computation below followed by the cast is exact.
+ * ------------------------------------------------------------------------- */
+float oq_f16_to_f32(uint16_t h)
+{
+    const int s = (h >> 15) & 1;
+    const int e = (h >> 10) & 0x1f;
+    const int f = h & 0x3ff;
+    double v;
+    if (e == 0) {
+        v = ldexp((double)f, -24);                 /* 2^-14 * f / 2^10 */
+    } else if (e == 31) {
+        if (f == 0) {
+            v = INFINITY;
+        } else {
+            v = NAN;
+        }
+    } else {
+        v = ldexp((double)(1024 + f), e - 25);     /* 2^(e-15) * (1024+f) / 2^10 */
+    }
+    return (float)(s ? -v : v);
+}
+
+/* ---------------------------------------------------------------------------
+ * binary32 -> binary16 with round-to-nearest-even, from the definition.  Used
+ * only by the reference quantizer (the pages' own encoder rounds half up on
+ * the normal path, so it is deliberately not the model here).
+ * ------------------------------------------------------------------------- */
+uint16_t oq_f32_to_f16_rne(float vf)
+{
+    double v = (double)vf;
+    uint16_t sign = 0;
+    if (signbit(v)) {
+        sign = 0x8000;
+        v = -v;
+    }
+    if (isnan(v)) {
+        return (uint16_t)(sign | 0x7e00);
+    }
+    if (isinf(v)) {
+        return (uint16_t)(sign | 0x7c00);
+    }
+    if (v == 0.0) {
+        return sign;
+    }
+    /* subnormal range: multiples of 2^-24 below 2^-14 */
+    if (v < ldexp(1.0, -14)) {
+        double units = nearbyint(ldexp(v, 24));    /* RNE in the default mode */
+        /* rounding up to 1024 units is exactly the smallest normal, 0x0400 */
+        return (uint16_t)(sign | (uint16_t)units);
+    }
+    int ex;
+    double fr = frexp(v, &ex);            /* v = fr * 2^ex, fr in [0.5, 1) */
+    /* significand with 11 bits: 1024 <= sig < 2048, value = sig * 2^(ex-11) */
+    double sig = nearbyint(ldexp(fr, 11));
+    int e2 = ex - 11;
+    if (sig == 2048.0) {                  /* carry out of the significand */
+        sig = 1024.0;
+        e2 += 1;
+    }
+    int biased = e2 + 10 + 15;            /* value = (sig/1024) * 2^(biased-15) */
+    if (biased >= 31) {
+        return (uint16_t)(sign | 0x7c00); /* overflow -> inf */
+    }
+    return (uint16_t)(sign | (uint16_t)(biased << 10) | (uint16_t)((int)sig - 1024));
+}
+
+/* ---------------------------------------------------------------------------
+ * The twelve scale bytes s[0..11] hold eight 6-bit scales sc_0..sc_7 and
+ * eight 6-bit mins m_0..m_7 (GGUF K-quant packing):
+ *   j < 4 : sc_j = low 6 bits of s[j],   m_j = low 6 bits of s[j+4]
+ *   j >= 4: sc_j = low nibble of s[j+4]  plus (top two bits of s[j-4]) << 4
+ *           m_j  = high nibble of s[j+4] plus (top two bits of s[j])   << 4
+ * ------------------------------------------------------------------------- */
+void oq_unpack_scales(const uint8_t s[12], uint8_t sc[8], uint8_t m[8])
+{
+    for (int j = 0; j < 8; ++j) {
+        if (j < 4) {
+            sc[j] = (uint8_t)(s[j] % 64);
+            m[j] = (uint8_t)(s[j + 4] % 64);
+        } else {
+            sc[j] = (uint8_t)((s[j + 4] % 16) + (s[j - 4] / 64) * 16);
+            m[j] = (uint8_t)((s[j + 4] / 16) + (s[j] / 64) * 16);
+        }
+    }
+}
+
+/* The inverse, written from the same table one byte at a time (used by the
+ * reference quantizer).  Inputs must be < 64. */
+void oq_pack_scales(const uint8_t sc[8], const uint8_t m[8], uint8_t s[12])
+{
+    for (int j = 0; j < 4; ++j) {
+        s[j] = (uint8_t)(sc[j] + (sc[j + 4] / 16) * 64);
+        s[j + 4] = (uint8_t)(m[j] + (m[j + 4] / 16) * 64);
+        s[j + 8] = (uint8_t)((sc[j + 4] % 16) + (m[j + 4] % 16) * 16);
+    }
+}
+
+/* Sub-block index and 4-bit code of element e (0..255) of one superblock. */
+static void oq_element_code(const uint8_t* qs, int e, int* j, int* q)
+{
+    const int c = e / 64;            /* 64-element chunk            */
+    const int within = e % 64;
+    const int hi = within / 32;      /* 0: low nibble, 1: high      */
+    const int i = within % 32;       /* byte inside the chunk       */
+    const uint8_t byte = qs[32 * c + i];
+    *q = hi ? (byte / 16) : (byte % 16);
+    *j = 2 * c + hi;                 /* sub-blocks in element order */
+}
+
+/* Dequantize one 144-byte superblock to 256 floats:
+ *   w = fl32( fl32(d*sc_j) * q  -  fl32(dmin*m_j) )
+ * d*sc_j, (d*sc_j)*q and dmin*m_j are exact in binary32 (at most 11+6+4
+ * significant bits), so the only rounding is the subtraction. */
+void oq_dequant_superblock(const uint8_t* blk, float* out)
+{
+    const float d = oq_f16_to_f32((uint16_t)(blk[0] | (blk[1] << 8)));
+    const float dmin = oq_f16_to_f32((uint16_t)(blk[2] | (blk[3] << 8)));
+    uint8_t sc[8], m[8];
+    oq_unpack_scales(blk + 4, sc, m);
+    const uint8_t* qs = blk + 16;
+    for (int e = 0; e < OQ_QK; ++e) {
+        int j, q;
+        oq_element_code(qs, e, &j, &q);
+        const float dsc = d * (float)sc[j];
+        const float dm = dmin * (float)m[j];
+        const float prod = dsc * (float)q;
+        out[e] = prod - dm;
+    }
+}
+
+static int oq_shape_ok(int64_t n, int64_t k)
+{
+    return n >= 0 && k > 0 && k % OQ_QK == 0;
+}
+
+/* out[r][c] for r < n, c < k. Returns 0, or -1 on a bad shape. */
+int oq_dequant(const uint8_t* w, int64_t n, int64_t k, float* out)
+{
+    if (!oq_shape_ok(n, k)) {
+        return -1;
+    }
+    const int64_t S = k / OQ_QK;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; ++r) {
+        for (int64_t s = 0; s < S; ++s) {
+            oq_dequant_superblock(w + (r * S + s) * OQ_SB, out + r * k + s * OQ_QK);
+        }
+    }
+    return 0;
+}
+
+/* One row: dequantize to f32, then for every vector b accumulate the dot in
+ * f64 together with sum |w|*|x| (the tolerance scale). */
+static void oq_row(const uint8_t* w, const float* x, int64_t k, int64_t m, int64_t r,
+                   float* wrow, double* y_out, double* bound_out, int64_t ystride)
+{
+    const int64_t S = k / OQ_QK;
+    for (int64_t s = 0; s < S; ++s) {
+        oq_dequant_superblock(w + (r * S + s) * OQ_SB, wrow + s * OQ_QK);
+    }
+    for (int64_t b = 0; b < m; ++b) {
+        const float* xb = x + b * k;
+        double acc = 0.0, mag = 0.0;
+        for (int64_t c = 0; c < k; ++c) {
+            const double wv = (double)wrow[c];
+            const double xv = (double)xb[c];
+            acc += wv * xv;
+            mag += fabs(wv) * fabs(xv);
+        }
+        y_out[b * ystride] = acc;
+        if (bound_out) {
+            bound_out[b * ystride] = mag;
+        }
+    }
+}
+
+/* y[b][r], bound[b][r] for b < m, r < n (both m x n, row-major). */
+int oq_gemv(const uint8_t* w, const float* x, int64_t n, int64_t k, int64_t m,
+            double* y, double* bound)
+{
+    if (!oq_shape_ok(n, k) || m < 1) {
+        return -1;
+    }
+    int bad = 0;
+#pragma omp parallel
+    {
+        float* wrow = (float*)malloc((size_t)k * sizeof(float));
+        if (!wrow) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t r = 0; r < n; ++r) {
+                oq_row(w, x, k, m, r, wrow, y + r, bound ? bound + r : NULL, n);
+            }
+            free(wrow);
+        }
+    }
+    return bad ? -2 : 0;
+}
+
+/* The same for a list of rows: y[b][t], bound[b][t] for the t-th listed row. */
+int oq_gemv_rows(const uint8_t* w, const float* x, int64_t n, int64_t k, int64_t m,
+                 const int64_t* rows, int64_t nrows, double* y, double* bound)
+{
+    if (!oq_shape_ok(n, k) || m < 1) {
+        return -1;
+    }
+    for (int64_t t = 0; t < nrows; ++t) {
+        if (rows[t] < 0 || rows[t] >= n) {
+            return -1;
+        }
+    }
+    int bad = 0;
+#pragma omp parallel
+    {
+        float* wrow = (float*)malloc((size_t)k * sizeof(float));
+        if (!wrow) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t t = 0; t < nrows; ++t) {
+                oq_row(w, x, k, m, rows[t], wrow, y + t, bound ? bound + t : NULL, nrows);
+            }
+            free(wrow);
+        }
+    }
+    return bad ? -2 : 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Simple reference quantizer (tests only): one row of k floats -> k/256
+ * superblocks.  Per 32-element sub-block j: lo_j = min(0, min x), hi_j =
+ * max x, step_j = (hi_j - lo_j)/15.  d = max_j step_j / 63 and
+ * dmin = max_j(-lo_j) / 63, both rounded to binary16 (RNE).  sc_j and m_j are
+ * nearbyint(step_j/d) and nearbyint(-lo_j/dmin), clamped to 0..63, and
+ * q = clamp(nearbyint((x + dmin*m_j) / (d*sc_j)), 0, 15).
+ * ------------------------------------------------------------------------- */
+static int oq_clampi(double v, int lo, int hi)
+{
+    if (!(v >= lo)) {         /* also catches NaN */
+        return lo;
+    }
+    if (v > hi) {
+        return hi;
+    }
+    return (int)v;
+}
+
+int oq_quantize_row(const float* x, int64_t k, uint8_t* out)
+{
+    if (k <= 0 || k % OQ_QK != 0) {
+        return -1;
+    }
+    const int64_t S = k / OQ_QK;
+    for (int64_t s = 0; s < S; ++s) {
+        const float* xs = x + s * OQ_QK;
+        uint8_t* blk = out + s * OQ_SB;
+        double step[8], neglo[8];
+        double dmax = 0.0, mmax = 0.0;
+        for (int j = 0; j < 8; ++j) {
+            double lo = 0.0, hi = -INFINITY;
+            for (int t = 0; t < 32; ++t) {
+                /* sub-block j holds elements 64*(j/2) + 32*(j%2) + t */
+                const double v = xs[64 * (j / 2) + 32 * (j % 2) + t];
+                if (v < lo) lo = v;
+                if (v > hi) hi = v;
+            }
+            if (hi < lo) hi = lo;
+            step[j] = (hi - lo) / 15.0;
+            neglo[j] = -lo;
+            if (step[j] > dmax) dmax = step[j];
+            if (neglo[j] > mmax) mmax = neglo[j];
+        }
+        const uint16_t dbits = oq_f32_to_f16_rne((float)(dmax / 63.0));
+        const uint16_t mbits = oq_f32_to_f16_rne((float)(mmax / 63.0));
+        const float d = oq_f16_to_f32(dbits);
+        const float dmin = oq_f16_to_f32(mbits);
+        uint8_t sc[8], mn[8];
+        for (int j = 0; j < 8; ++j) {
+            sc[j] = (uint8_t)(d > 0.0f ? oq_clampi(nearbyint(step[j] / d), 0, 63) : 0);
+            mn[j] = (uint8_t)(dmin > 0.0f ? oq_clampi(nearbyint(neglo[j] / dmin), 0, 63) : 0);
+        }
+        blk[0] = (uint8_t)(dbits & 0xff);
+        blk[1] = (uint8_t)(dbits >> 8);
+        blk[2] = (uint8_t)(mbits & 0xff);
+        blk[3] = (uint8_t)(mbits >> 8);
+        oq_pack_scales(sc, mn, blk + 4);
+        uint8_t* qs = blk + 16;
+        memset(qs, 0, 128);
+        for (int e = 0; e < OQ_QK; ++e) {
+            const int c = e / 64, within = e % 64, hi = within / 32, i = within % 32;
+            const int j = 2 * c + hi;
+            const double dsc = (double)d * sc[j];
+            const double dm = (double)dmin * mn[j];
+            int q = 0;
+            if (dsc > 0.0) {
+                q = oq_clampi(nearbyint(((double)xs[e] + dm) / dsc), 0, 15);
+            }
+            qs[32 * c + i] = (uint8_t)(qs[32 * c + i] | (hi ? q * 16 : q));
+        }
+    }
+    return 0;
+}
+
+int oq_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+void oq_set_num_threads(int t)
+{
+#ifdef _OPENMP
+    if (t > 0) {
+        omp_set_num_threads(t);
+    }
+#else
+    (void)t;
+#endif
+}

@@ -1,0 +1,438 @@
+"""Pin checks of the CPU oracle against facts fixed outside it (CPU only).
+
+Each test checks the oracle against something other than itself: numpy's
+binary16 conversion, a hand-worked superblock, bytes placed by hand from the
+layout, closed forms, exact rational arithmetic and a quantizer round-trip.
+Together they are chosen so that a dropped term, a wrong sign, a swapped
+nibble or sub-block index, or a transposed scale/min fails at least one test
+(test_oracle_mutations.py plants such mistakes in a copy of the oracle and
+checks exactly that).  test_oracle_pins.py runs every check on the oracle.
+"""
+from fractions import Fraction
+import os
+
+import numpy as np
+
+from block_quantized_decode_q4_amd import synth  # seeded generator: draws and bit placement only
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ----------------------------------------------------------------- helpers
+def f32bits(a):
+    return np.asarray(a, dtype=np.float32).view(np.uint32)
+
+
+def block_bytes(d_bits, dmin_bits, s12, qs128):
+    """Place header and quants at the offsets of the layout (0, 2, 4, 16)."""
+    b = np.zeros(144, dtype=np.uint8)
+    b[0] = d_bits & 0xFF
+    b[1] = d_bits >> 8
+    b[2] = dmin_bits & 0xFF
+    b[3] = dmin_bits >> 8
+    b[4:16] = np.asarray(s12, dtype=np.uint8)
+    b[16:144] = np.asarray(qs128, dtype=np.uint8)
+    return b
+
+
+def scale_bytes_single(j, field):
+    """Twelve scale bytes with exactly one 6-bit field equal to 1: sc_j
+    (field='sc') or m_j (field='m'); placed by hand from the bit table."""
+    s = np.zeros(12, dtype=np.uint8)
+    if field == "sc":
+        if j < 4:
+            s[j] = 1                 # low six bits of s[j]
+        else:
+            s[j + 4] = 0x01          # low nibble of s[j+4]
+    else:
+        if j < 4:
+            s[j + 4] = 1             # low six bits of s[j+4]
+        else:
+            s[j + 4] = 0x10          # high nibble of s[j+4]
+    return s
+
+
+def element_of(c, hi, i):
+    return 64 * c + 32 * hi + i
+
+
+F16_ONE = 0x3C00
+F16_HALF = 0x3800
+
+
+# ------------------------------------------------------- binary16 decoding
+def check_f16_decode_exhaustive_matches_numpy(oracle_mod):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ours = oracle_mod.f16_to_f32(bits)
+    ref = bits.view(np.float16).astype(np.float32)
+    nan_ours = np.isnan(ours)
+    nan_ref = np.isnan(ref)
+    assert np.array_equal(nan_ours, nan_ref)
+    keep = ~nan_ref
+    assert np.array_equal(f32bits(ours[keep]), f32bits(ref[keep]))
+    # spot values from the definition
+    assert oracle_mod.f16_to_f32([0x0001])[0] == 2.0 ** -24
+    assert oracle_mod.f16_to_f32([0x03FF])[0] == 1023 * 2.0 ** -24
+    assert oracle_mod.f16_to_f32([0x0400])[0] == 2.0 ** -14
+    assert oracle_mod.f16_to_f32([0x7BFF])[0] == 65504.0
+    assert oracle_mod.f16_to_f32([0xC000])[0] == -2.0
+    assert np.isinf(oracle_mod.f16_to_f32([0xFC00])[0]) and oracle_mod.f16_to_f32([0xFC00])[0] < 0
+    assert f32bits(oracle_mod.f16_to_f32([0x8000]))[0] == 0x80000000
+
+
+def check_f16_encode_rne_matches_numpy(oracle_mod):
+    rng = np.random.default_rng(7)
+    # random bit patterns across the whole float32 range plus the binary16
+    # boundaries and every exact tie between neighbouring binary16 values
+    vals = rng.integers(0, 2 ** 32, size=200000, dtype=np.uint64).astype(np.uint32).view(np.float32)
+    f16 = np.arange(0, 0x7C00, dtype=np.uint32).astype(np.uint16).view(np.float16).astype(np.float64)
+    ties = ((f16[:-1] + f16[1:]) / 2).astype(np.float32)
+    extra = np.array([0.0, -0.0, 65504.0, 65519.99, 65520.0, 2.0 ** -25, 2.0 ** -26, 3 * 2.0 ** -26,
+                      np.inf, -np.inf, 1e-4, 1e-2], dtype=np.float32)
+    allv = np.concatenate([vals, ties, -ties, extra])
+    ours = oracle_mod.f32_to_f16_rne(allv)
+    with np.errstate(over="ignore"):
+        ref = allv.astype(np.float16).view(np.uint16)
+    isn = np.isnan(allv)
+    assert np.array_equal(ours[~isn], ref[~isn])
+    assert np.all(np.isnan(ours[isn].view(np.float16)))
+
+
+# ------------------------------------------------------------ scale bytes
+def check_scale_unpack_handworked_golden(oracle_mod):
+    header, sc, m, _, _ = load_golden()
+    got_sc, got_m = oracle_mod.unpack_scales(header[4:16])
+    assert got_sc.tolist() == sc
+    assert got_m.tolist() == m
+
+
+def check_scale_pack_unpack_exhaustive(oracle_mod):
+    """Every (sc, m) pair at every j, with the other fields random, survives
+    pack -> unpack; the oracle's packer and the generator's packer (two
+    independent writings of the table) give identical bytes."""
+    rng = np.random.default_rng(11)
+    for j in range(8):
+        for sc_v in range(64):
+            others_sc = rng.integers(0, 64, size=(64, 8), dtype=np.uint8)
+            others_m = rng.integers(0, 64, size=(64, 8), dtype=np.uint8)
+            others_sc[:, j] = sc_v
+            others_m[:, j] = np.arange(64, dtype=np.uint8)
+            # generator packer, vectorised over the 64 m values
+            f = synth.Fields(np.zeros((64, 1), np.uint16), np.zeros((64, 1), np.uint16),
+                             others_sc.reshape(64, 1, 8), others_m.reshape(64, 1, 8),
+                             np.zeros((64, 1, 256), np.uint8))
+            gen = synth.pack(f).reshape(64, 144)[:, 4:16]
+            for t in range(64):
+                s = oracle_mod.pack_scales(others_sc[t], others_m[t])
+                assert np.array_equal(s, gen[t])
+                usc, um = oracle_mod.unpack_scales(s)
+                assert np.array_equal(usc, others_sc[t])
+                assert np.array_equal(um, others_m[t])
+
+
+def check_scale_single_field_by_hand(oracle_mod):
+    """One 6-bit field set to 1 via bytes placed by hand; only that field is 1."""
+    for j in range(8):
+        for field in ("sc", "m"):
+            sc, m = oracle_mod.unpack_scales(scale_bytes_single(j, field))
+            exp_sc = np.zeros(8, np.uint8)
+            exp_m = np.zeros(8, np.uint8)
+            (exp_sc if field == "sc" else exp_m)[j] = 1
+            assert np.array_equal(sc, exp_sc), (j, field)
+            assert np.array_equal(m, exp_m), (j, field)
+    # top bits: s[0..3] bits 6-7 feed sc_4..sc_7 bits 4-5, s[4..7] feed m_4..m_7
+    for j in range(4):
+        s = np.zeros(12, np.uint8)
+        s[j] = 0xC0
+        sc, m = oracle_mod.unpack_scales(s)
+        assert sc[j] == 0 and sc[j + 4] == 48 and m.sum() == 0
+        s = np.zeros(12, np.uint8)
+        s[j + 4] = 0x80
+        sc, m = oracle_mod.unpack_scales(s)
+        assert m[j] == 0 and m[j + 4] == 32 and sc.sum() == 0
+
+
+# --------------------------------------------------------- golden block
+def load_golden():
+    header = []
+    qs = []
+    sc = m = None
+    w = []
+    with open(os.path.join(GOLDEN, "q4k_superblock_handbuilt.txt")) as fh:
+        for line in fh:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, val = line.split(":", 1)
+            if key == "header":
+                header = [int(t, 16) for t in val.split()]
+            elif key == "qs":
+                qs += [int(t, 16) for t in val.split()]
+            elif key == "sc":
+                sc = [int(t) for t in val.split()]
+            elif key == "m":
+                m = [int(t) for t in val.split()]
+            elif key == "w":
+                e, v = val.split()
+                w.append((int(e), float(v)))
+    blk = np.array(header + qs, dtype=np.uint8)
+    assert blk.size == 144
+    return blk, sc, m, w, qs
+
+
+def check_golden_handbuilt_superblock(oracle_mod):
+    blk, _, _, w, _ = load_golden()
+    out = oracle_mod.dequant_superblock(blk)
+    for e, v in w:
+        assert out[e] == np.float32(v), (e, out[e], v)
+
+
+def check_golden_superblock_through_gemv(oracle_mod):
+    """x = e_i picks out weight i: the GEMV path agrees with the hand values."""
+    blk, _, _, w, _ = load_golden()
+    x = np.zeros((len(w), 256), np.float32)
+    for t, (e, _) in enumerate(w):
+        x[t, e] = 1.0
+    y, bound = oracle_mod.gemv(blk, x, n=1)
+    for t, (e, v) in enumerate(w):
+        assert y[t, 0] == v
+        assert bound[t, 0] == abs(v)
+
+
+# ---------------------------------------------------------- layout, one-hot
+def check_onehot_scale_layout_bruteforce(oracle_mod, js=range(8)):
+    """d=1, dmin=0, sc_j=1 and every other scale 0: w equals the 4-bit code on
+    sub-block j and 0 elsewhere.  All 16 codes at every position."""
+    for j in js:
+        s12 = scale_bytes_single(j, "sc")
+        c, hi = j // 2, j % 2
+        for v in range(16):
+            qs = np.zeros(128, np.uint8)
+            # code v in the nibble of sub-block j for every byte of chunk c,
+            # and code 15-v in the other nibble of every byte
+            other = 15 - v
+            for cc in range(4):
+                for i in range(32):
+                    lo_code = v if (cc == c and hi == 0) else other
+                    hi_code = v if (cc == c and hi == 1) else other
+                    qs[32 * cc + i] = lo_code | (hi_code << 4)
+            out = oracle_mod.dequant_superblock(block_bytes(F16_ONE, 0, s12, qs))
+            expect = np.zeros(256, np.float32)
+            for i in range(32):
+                expect[element_of(c, hi, i)] = v
+            assert np.array_equal(out, expect), (j, v)
+
+
+def check_onehot_min_layout_bruteforce(oracle_mod, js=range(8)):
+    """q=0, dmin=1, m_j=1 and every other min 0: w = -1 on sub-block j only."""
+    for j in js:
+        s12 = scale_bytes_single(j, "m")
+        out = oracle_mod.dequant_superblock(block_bytes(F16_ONE, F16_ONE, s12, np.zeros(128, np.uint8)))
+        expect = np.zeros(256, np.float32)
+        c, hi = j // 2, j % 2
+        for i in range(32):
+            expect[element_of(c, hi, i)] = -1.0
+        assert np.array_equal(out, expect), j
+
+
+def check_position_map_every_byte(oracle_mod):
+    """Each byte of the 128 quant bytes is decoded at the positions the layout
+    names: a distinct code pattern per byte, all scales 1, dmin 0."""
+    s12 = np.zeros(12, np.uint8)
+    s12[0:4] = 1                                  # sc_0..sc_3 = 1
+    s12[8:12] = 0x01                              # sc_4..sc_7 = 1 (low nibbles)
+    rng = np.random.default_rng(3)
+    for _ in range(8):
+        qs = rng.integers(0, 256, size=128, dtype=np.uint8)
+        out = oracle_mod.dequant_superblock(block_bytes(F16_ONE, 0, s12, qs))
+        for c in range(4):
+            for i in range(32):
+                b = int(qs[32 * c + i])
+                assert out[64 * c + i] == (b & 15)
+                assert out[64 * c + 32 + i] == (b >> 4)
+
+
+# ------------------------------------------------------------ closed forms
+def check_closed_form_uniform_row_is_constant(oracle_mod):
+    """Uniform q, sc, m and the same d, dmin in every superblock give a
+    constant row c = d*sc*q - dmin*m, so y = c * sum(x)."""
+    rng = np.random.default_rng(5)
+    S, n = 6, 3
+    k = 256 * S
+    cases = [(0x2E66, 0x2A00, 37, 12, 9), (0x3C00, 0x3800, 5, 7, 3), (0x1400, 0x0C00, 63, 63, 15)]
+    for d_bits, dm_bits, scv, mv, qv in cases:
+        f = synth.Fields(np.full((n, S), d_bits, np.uint16), np.full((n, S), dm_bits, np.uint16),
+                         np.full((n, S, 8), scv, np.uint8), np.full((n, S, 8), mv, np.uint8),
+                         np.full((n, S, 256), qv, np.uint8))
+        w = synth.pack(f)
+        d = Fraction(float(np.uint16(d_bits).view(np.float16)))
+        dm = Fraction(float(np.uint16(dm_bits).view(np.float16)))
+        cval = np.float32(float(d * scv * qv - dm * mv))   # one RNE rounding
+        deq = oracle_mod.dequant(w, n, k)
+        assert np.all(deq == cval)
+        x = rng.standard_normal((2, k)).astype(np.float32)
+        y, bound = oracle_mod.gemv(w, x, n)
+        for b in range(2):
+            exact = float(sum(Fraction(float(cval)) * Fraction(float(v)) for v in x[b]))
+            assert np.allclose(y[b], exact, rtol=0, atol=1e-12 * bound[b].max())
+
+
+def check_closed_form_zero_quants(oracle_mod):
+    """All codes 0: y = -sum_j dmin*m_j * (sum of x over sub-block j)."""
+    rng = np.random.default_rng(6)
+    n, S = 5, 4
+    k = 256 * S
+    f = synth.draw_fields(rng, n, S)
+    f.q[:] = 0
+    w = synth.pack(f)
+    x = rng.standard_normal((3, k)).astype(np.float32)
+    y, bound = oracle_mod.gemv(w, x, n)
+    dmin = f.dmin_bits.view(np.float16).astype(np.float64)
+    for b in range(3):
+        xs = x[b].astype(np.float64).reshape(S, 4, 2, 32).sum(axis=3).reshape(S, 8)  # [sb][j]
+        for r in range(n):
+            exp = -np.sum(dmin[r][:, None] * f.m[r].astype(np.float64) * xs)
+            assert abs(y[b, r] - exp) <= 1e-12 * bound[b, r]
+
+
+def check_exact_dyadic_bruteforce(oracle_mod):
+    """Dyadic d and dmin and small-integer x make every weight and every
+    product exact, so y is known exactly; rational arithmetic from the
+    fields, not from the oracle, gives it."""
+    rng = np.random.default_rng(9)
+    n, S = 4, 2
+    k = 256 * S
+    f = synth.draw_fields(rng, n, S)
+    dyadic = np.array([0x3800, 0x3400, 0x3C00, 0x4000, 0x3000, 0x2C00], np.uint16)  # .5 .25 1 2 .125 .0625
+    f.d_bits[:] = rng.choice(dyadic, size=(n, S))
+    f.dmin_bits[:] = rng.choice(dyadic, size=(n, S))
+    w = synth.pack(f)
+    x = rng.integers(-8, 9, size=(2, k)).astype(np.float32)
+    y, bound = oracle_mod.gemv(w, x, n)
+    for r in range(n):
+        for b in range(2):
+            tot = Fraction(0)
+            mag = Fraction(0)
+            for s in range(S):
+                d = Fraction(float(f.d_bits[r, s].view(np.float16)))
+                dm = Fraction(float(f.dmin_bits[r, s].view(np.float16)))
+                for e in range(256):
+                    j = 2 * (e // 64) + (e % 64) // 32
+                    wv = d * int(f.sc[r, s, j]) * int(f.q[r, s, e]) - dm * int(f.m[r, s, j])
+                    xv = int(x[b, 256 * s + e])
+                    tot += wv * xv
+                    mag += abs(wv) * abs(xv)
+            assert y[b, r] == float(tot)
+            assert bound[b, r] == float(mag)
+
+
+def check_single_rounding_of_the_subtraction(oracle_mod):
+    """When d*sc*q - dmin*m needs more than 24 bits, the weight is the exact
+    value rounded once to binary32 (round-to-nearest-even)."""
+    rng = np.random.default_rng(12)
+    n, S = 64, 1
+    f = synth.draw_fields(rng, n, S)
+    # tiny d (subnormal and near the bottom of the normal range), dmin near 1
+    f.d_bits[:] = rng.choice(np.array([0x0001, 0x0155, 0x03FF, 0x0401, 0x07FF, 0x0ABC], np.uint16), size=(n, S))
+    f.dmin_bits[:] = rng.choice(np.array([0x3C01, 0x3BFF, 0x3E7B, 0x4123], np.uint16), size=(n, S))
+    w = synth.pack(f)
+    deq = oracle_mod.dequant(w, n, 256)
+    for r in range(n):
+        d = Fraction(float(f.d_bits[r, 0].view(np.float16)))
+        dm = Fraction(float(f.dmin_bits[r, 0].view(np.float16)))
+        for e in range(256):
+            j = 2 * (e // 64) + (e % 64) // 32
+            exact = d * int(f.sc[r, 0, j]) * int(f.q[r, 0, e]) - dm * int(f.m[r, 0, j])
+            # the exact value fits a double (< 53 significant bits); casting it
+            # to float32 is the single RNE rounding
+            assert Fraction(float(exact)) == exact
+            assert deq[r, e] == np.float32(float(exact)), (r, e)
+
+
+def check_special_d_values(oracle_mod):
+    """Signed zeros, subnormal, largest finite, infinities and NaN in d/dmin
+    follow IEEE arithmetic on the decoded values."""
+    specials = np.array([0x0000, 0x8000, 0x0001, 0x03FF, 0x7BFF, 0xFBFF, 0x7C00, 0xFC00, 0x7E00,
+                         0xBC00, 0x3C00], np.uint16)
+    rng = np.random.default_rng(4)
+    n = specials.size * specials.size
+    f = synth.draw_fields(rng, n, 1)
+    f.d_bits[:, 0] = np.repeat(specials, specials.size)
+    f.dmin_bits[:, 0] = np.tile(specials, specials.size)
+    w = synth.pack(f)
+    deq = oracle_mod.dequant(w, n, 256)
+    with np.errstate(invalid="ignore", over="ignore"):
+        for r in range(n):
+            d = np.float32(f.d_bits[r, 0].view(np.float16))
+            dm = np.float32(f.dmin_bits[r, 0].view(np.float16))
+            for e in range(0, 256, 7):
+                j = 2 * (e // 64) + (e % 64) // 32
+                exp = np.float32(np.float32(d * np.float32(f.sc[r, 0, j])) * np.float32(f.q[r, 0, e])) \
+                    - np.float32(dm * np.float32(f.m[r, 0, j]))
+                got = deq[r, e]
+                if np.isnan(exp):
+                    assert np.isnan(got)
+                else:
+                    assert f32bits(got) == f32bits(exp), (r, e, got, exp)
+
+
+# ------------------------------------------------------ quantizer round trip
+def check_quantizer_round_trip(oracle_mod):
+    rng = np.random.default_rng(21)
+    n, k = 48, 1024
+    x = rng.standard_normal((n, k)).astype(np.float32)
+    wq = oracle_mod.quantize_rows(x)
+    deq = oracle_mod.dequant(wq, n, k)
+    blocks = wq.reshape(n, k // 256, 144)
+    checked = 0
+    for r in range(n):
+        for s in range(k // 256):
+            blk = blocks[r, s]
+            d = float(np.uint16(blk[0] | (blk[1].astype(np.uint16) << 8)).view(np.float16))
+            dm = float(np.uint16(blk[2] | (blk[3].astype(np.uint16) << 8)).view(np.float16))
+            sc, m = oracle_mod.unpack_scales(blk[4:16])
+            assert sc.max() < 64 and m.max() < 64
+            for e in range(256):
+                j = 2 * (e // 64) + (e % 64) // 32
+                lo = -dm * int(m[j])
+                hi = 15 * d * int(sc[j]) - dm * int(m[j])
+                xv = float(x[r, 256 * s + e])
+                if lo <= xv <= hi and sc[j] > 0:
+                    err = abs(xv - float(deq[r, 256 * s + e]))
+                    assert err <= 0.5 * d * int(sc[j]) + 2.0 ** -20 * max(abs(xv), dm * int(m[j])), (r, s, e)
+                    checked += 1
+    assert checked > 0.9 * n * k
+
+
+def check_shape_errors(oracle_mod):
+    for args in ((np.zeros(144, np.uint8), 1, 255), (np.zeros(143, np.uint8), 1, 256)):
+        try:
+            oracle_mod.dequant(*args)
+        except ValueError:
+            pass
+        else:
+            raise AssertionError("bad shape accepted")
+    y, bound = oracle_mod.gemv(np.zeros(0, np.uint8), np.zeros((1, 256), np.float32), 0)
+    assert y.shape == (1, 0)
+
+
+# fastest first: the mutation test stops at the first failing check
+ALL_CHECKS = (
+    check_golden_handbuilt_superblock,
+    check_golden_superblock_through_gemv,
+    check_scale_unpack_handworked_golden,
+    check_scale_single_field_by_hand,
+    check_onehot_min_layout_bruteforce,
+    check_position_map_every_byte,
+    check_onehot_scale_layout_bruteforce,
+    check_closed_form_zero_quants,
+    check_closed_form_uniform_row_is_constant,
+    check_exact_dyadic_bruteforce,
+    check_single_rounding_of_the_subtraction,
+    check_special_d_values,
+    check_f16_decode_exhaustive_matches_numpy,
+    check_shape_errors,
+    check_quantizer_round_trip,
+    check_f16_encode_rne_matches_numpy,
+    check_scale_pack_unpack_exhaustive,
+)

@@ -1,0 +1,82 @@
+"""Planted mistakes: each mutant of the oracle must fail at least one pin.
+
+A copy of oracle/q4k_oracle.c gets one plausible mistake (a swapped nibble, a
+wrong sub-block index, a flipped sign, a dropped term, transposed scale/min
+fields, a wrong exponent bias, ...), is built into a temporary library, and
+the checks of oracle_pins.py run against it.  The real oracle is untouched;
+the mistakes live only in the temporary copies, on the CPU.
+"""
+import importlib.util
+import os
+import shutil
+import subprocess
+
+import pytest
+
+import oracle_pins
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "q4k_oracle.c")
+
+MUTANTS = {
+    "nibble_swap": ("*q = hi ? (byte / 16) : (byte % 16);", "*q = hi ? (byte % 16) : (byte / 16);"),
+    "subblock_index": ("*j = 2 * c + hi;", "*j = c + 4 * hi;"),
+    "chunk_stride": ("const uint8_t byte = qs[32 * c + i];", "const uint8_t byte = qs[32 * (c % 2) + i];"),
+    "min_sign": ("out[e] = prod - dm;", "out[e] = prod + dm;"),
+    "min_dropped": ("out[e] = prod - dm;", "out[e] = prod;"),
+    "scale_min_transposed": (
+        "sc[j] = (uint8_t)(s[j] % 64);\n            m[j] = (uint8_t)(s[j + 4] % 64);",
+        "sc[j] = (uint8_t)(s[j + 4] % 64);\n            m[j] = (uint8_t)(s[j] % 64);"),
+    "high_bits_from_wrong_byte": ("(s[j - 4] / 64) * 16", "(s[j] / 64) * 16"),
+    "six_bit_mask": ("sc[j] = (uint8_t)(s[j] % 64);", "sc[j] = (uint8_t)(s[j] % 32);"),
+    "d_dmin_swapped": (
+        "const float d = oq_f16_to_f32((uint16_t)(blk[0] | (blk[1] << 8)));\n"
+        "    const float dmin = oq_f16_to_f32((uint16_t)(blk[2] | (blk[3] << 8)));",
+        "const float d = oq_f16_to_f32((uint16_t)(blk[2] | (blk[3] << 8)));\n"
+        "    const float dmin = oq_f16_to_f32((uint16_t)(blk[0] | (blk[1] << 8)));"),
+    "big_endian_d": ("oq_f16_to_f32((uint16_t)(blk[0] | (blk[1] << 8)))", "oq_f16_to_f32((uint16_t)(blk[1] | (blk[0] << 8)))"),
+    "exponent_bias": ("v = ldexp((double)(1024 + f), e - 25);", "v = ldexp((double)(1024 + f), e - 24);"),
+    "subnormal_scale": ("v = ldexp((double)f, -24);", "v = ldexp((double)f, -25);"),
+    "implicit_bit_dropped": ("v = ldexp((double)(1024 + f), e - 25);", "v = ldexp((double)f, e - 25);"),
+    "x_vector_ignored": ("const double xv = (double)xb[c];", "const double xv = (double)x[c];"),
+    "bound_without_abs": ("mag += fabs(wv) * fabs(xv);", "mag += wv * xv;"),
+    "dot_in_float": ("acc += wv * xv;", "acc = (float)(acc + (float)(wv * xv));"),
+    "encoder_truncates": ("double sig = nearbyint(ldexp(fr, 11));", "double sig = floor(ldexp(fr, 11));"),
+    "quantizer_min_sign": ("q = oq_clampi(nearbyint(((double)xs[e] + dm) / dsc), 0, 15);",
+                           "q = oq_clampi(nearbyint(((double)xs[e] - dm) / dsc), 0, 15);"),
+}
+
+
+def _load_variant(lib_path, src_path):
+    spec = importlib.util.spec_from_file_location("oracle_mutant_%d" % abs(hash(lib_path)),
+                                                  os.path.join(ROOT, "oracle", "__init__.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    mod._SRC = src_path
+    mod._LIB = lib_path
+    mod._lib = None
+    mod._load()
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(tmp_path, name):
+    old, new = MUTANTS[name]
+    text = open(SRC).read()
+    assert text.count(old) >= 1, "mutation anchor not found: %s" % name
+    mutated = text.replace(old, new, 1)
+    src = tmp_path / "q4k_oracle.c"
+    src.write_text(mutated)
+    lib = tmp_path / "liboracle_q4k.so"
+    subprocess.run(["gcc", "-O1", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+                    "-o", str(lib), str(src), "-lm"], check=True)
+    mod = _load_variant(str(lib), str(src))
+    failed = None
+    for check in oracle_pins.ALL_CHECKS:
+        try:
+            check(mod)
+        except AssertionError:
+            failed = check.__name__
+            break
+    assert failed is not None, "mutant %s passed every pin" % name
+    shutil.rmtree(tmp_path, ignore_errors=True)
