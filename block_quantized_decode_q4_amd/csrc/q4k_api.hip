@@ -1,0 +1,319 @@
+// q4k_api.hip -- the C ABI of libq4k.so (declared in include/q4k.h):
+// argument validation, variant selection and launch.
+//
+// Every argument is checked before the first HIP call, so a bad call returns
+// its status without touching the device (realizar 0.8.5,
+// q4k_gemv_cached.rs: `q4k_gemv_indexed_async` validates the weight pointer
+// because a launch with a null pointer poisons the context).  Size arithmetic
+// is overflow-checked (turbospark-runtime 0.1.0, real_forward_dispatch.rs:
+// `validate_block_quant_embedding`).  Unsupported batch widths are refused by
+// name, never looped (real_forward_dispatch.rs: doc of `encode_gemm_any`).
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/q4k.h"
+#include "q4k_kernels.h"
+
+namespace {
+
+using q4k::GemvPlan;
+
+constexpr int64_t kInt32Max = 2147483647;
+// Single-stage x budget: 48 KiB, the pages' 12288-float shared-memory limit
+// (realizar 0.8.5, q4k_gemv_cached.rs: MAX_TILED_K in `q4k_gemv_cached`),
+// i.e. three 4096-element spans of one vector.
+constexpr int64_t kSingleStageBytes = 48 * 1024;
+constexpr int64_t kSpanBytes = (int64_t)q4k::kSpan * 4;          // 16 KiB per vector
+constexpr int64_t kSpanSumBytes = 64 * 8;                        // per vector
+constexpr int kMaxDevices = 64;
+
+std::atomic<int> g_lds_max[kMaxDevices];  // 0 = not queried yet
+
+inline bool aligned16(const void* p)
+{
+    return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+inline int hip_status(hipError_t e)
+{
+    return e == hipSuccess ? Q4K_OK : Q4K_ERR_HIP + (int)e;
+}
+
+// Shape rules shared by every entry point: 1 <= n <= 2^31-1,
+// 256 <= k <= 2^31-1, k % 256 == 0.
+inline int check_nk(int64_t n, int64_t k)
+{
+    if (n < 1 || n > kInt32Max || k < q4k::kQK || k > kInt32Max || k % q4k::kQK != 0) {
+        return Q4K_ERR_SHAPE;
+    }
+    return Q4K_OK;
+}
+
+int device_lds_max(size_t* out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        return hip_status(e);
+    }
+    if (dev < 0 || dev >= kMaxDevices) {
+        return Q4K_ERR_UNSUPPORTED;
+    }
+    int v = g_lds_max[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        e = hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+        if (e != hipSuccess) {
+            return hip_status(e);
+        }
+        g_lds_max[dev].store(v, std::memory_order_relaxed);
+    }
+    *out = (size_t)v;
+    return Q4K_OK;
+}
+
+// Resolve launch options into a plan.  Pure host arithmetic, no HIP calls.
+// Plans needing more LDS than lds_max are returned as they are; the caller
+// refuses them.
+int make_plan(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t lds_max, GemvPlan* p)
+{
+    const int S = (int)(k / q4k::kQK);
+    const int nspans = (S + q4k::kSpanSB - 1) / q4k::kSpanSB;
+    const int variant = o ? o->variant : 0;
+    if (variant < 0 || variant > 2) {
+        return Q4K_ERR_UNSUPPORTED;
+    }
+    const bool fits_single = m * nspans * kSpanBytes <= kSingleStageBytes;
+    const int auto_chunk = (int)(kSingleStageBytes / (m * kSpanBytes)) > 0
+                               ? (int)(kSingleStageBytes / (m * kSpanBytes)) : 1;
+    int spc;
+    if (variant == 1) {
+        spc = nspans;
+    } else if (variant == 2) {
+        spc = (o->spans_per_chunk > 0) ? o->spans_per_chunk : auto_chunk;
+    } else {
+        spc = fits_single ? nspans : auto_chunk;
+    }
+    if (spc > nspans) {
+        spc = nspans;
+    }
+    const int nchunks = (nspans + spc - 1) / spc;
+
+    int nw = (o && o->waves_per_block) ? o->waves_per_block : 4;
+    if (nw != 4 && nw != 8) {
+        return Q4K_ERR_UNSUPPORTED;
+    }
+    int R = (o && o->rows_per_wave) ? o->rows_per_wave : (m == 1 ? 2 : 1);
+    if (!(R == 1 || R == 2 || (R == 4 && m == 1))) {
+        return Q4K_ERR_UNSUPPORTED;
+    }
+    const int xo = o ? o->x_in_registers : 0;
+    if (xo < 0 || xo > 2) {
+        return Q4K_ERR_UNSUPPORTED;
+    }
+    int xreg = (m == 1 && nspans == 1) ? 1 : 0;
+    if (xo == 1) {
+        if (!xreg) {
+            return Q4K_ERR_UNSUPPORTED;
+        }
+    } else if (xo == 2) {
+        xreg = 0;
+    }
+
+    int64_t rpb;
+    if (o && o->rows_per_block > 0) {
+        rpb = o->rows_per_block;
+    } else {
+        // about two workgroups per CU of a 256-CU part, whole row groups
+        const int64_t unit = (int64_t)R * nw;
+        rpb = (n + 511) / 512;
+        rpb = ((rpb + unit - 1) / unit) * unit;
+        if (rpb < unit) {
+            rpb = unit;
+        }
+    }
+    if (rpb > kInt32Max) {
+        rpb = kInt32Max;
+    }
+    const size_t lds_x = (size_t)m * spc * (kSpanBytes + kSpanSumBytes);
+    const size_t lds_row = nchunks > 1 ? (size_t)m * 64 * 4 : 0;   // parked lane partials
+    if (lds_row && !(o && o->rows_per_block > 0) && lds_x + (size_t)rpb * lds_row > lds_max) {
+        // automatic row blocks shrink to whole row groups that fit the LDS
+        const int64_t unit = (int64_t)R * nw;
+        const int64_t fit = lds_x < lds_max ? (int64_t)((lds_max - lds_x) / lds_row) : 0;
+        if (fit >= unit) {
+            rpb = (fit / unit) * unit;
+        }
+    }
+    const int64_t grid = (n + rpb - 1) / rpb;
+    if (grid > kInt32Max) {
+        return Q4K_ERR_SHAPE;
+    }
+    // partial sums are parked per row group, so round the rows up to whole groups
+    const size_t lds = lds_x + (size_t)((rpb + R - 1) / R) * R * lds_row;
+
+    p->n = (int)n;
+    p->k = (int)k;
+    p->S = S;
+    p->m = (int)m;
+    p->nspans = nspans;
+    p->spans_per_chunk = spc;
+    p->nchunks = nchunks;
+    p->rows_per_block = (int)rpb;
+    p->rows_per_wave = R;
+    p->waves_per_block = nw;
+    p->x_in_registers = xreg;
+    p->grid = (int)grid;
+    p->lds_bytes = lds;
+    return Q4K_OK;
+}
+
+int gemv_checked(const void* w, const float* x, float* y, int64_t n, int64_t k, int64_t m,
+                 const q4k_launch* opts, void* stream)
+{
+    if (!w || !x || !y) {
+        return Q4K_ERR_NULL;
+    }
+    int rc = check_nk(n, k);
+    if (rc != Q4K_OK) {
+        return rc;
+    }
+    if (m < 1) {
+        return Q4K_ERR_SHAPE;
+    }
+    if (m > q4k::kMaxM) {
+        return Q4K_ERR_UNSUPPORTED;
+    }
+    if (!aligned16(w) || !aligned16(x) || !aligned16(y)) {
+        return Q4K_ERR_ALIGN;
+    }
+    // options are validated before the first HIP call (unbounded LDS), then
+    // planned for the device's LDS size
+    GemvPlan plan;
+    rc = make_plan(n, k, m, opts, SIZE_MAX, &plan);
+    if (rc != Q4K_OK) {
+        return rc;
+    }
+    size_t lds_max = 0;
+    rc = device_lds_max(&lds_max);
+    if (rc != Q4K_OK) {
+        return rc;
+    }
+    rc = make_plan(n, k, m, opts, lds_max, &plan);
+    if (rc != Q4K_OK) {
+        return rc;
+    }
+    if (plan.lds_bytes > lds_max) {
+        return Q4K_ERR_UNSUPPORTED;
+    }
+    return hip_status(q4k::launch_gemv(plan, w, x, y, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t q4k_row_bytes(int64_t k)
+{
+    if (k < q4k::kQK || k % q4k::kQK != 0) {
+        return 0;
+    }
+    return (size_t)(k / q4k::kQK) * q4k::kBlockBytes;
+}
+
+int q4k_load(void* w_dev, const void* src_host, size_t src_bytes, int64_t n, int64_t k,
+             void* stream)
+{
+    if (!w_dev || !src_host) {
+        return Q4K_ERR_NULL;
+    }
+    const int rc = check_nk(n, k);
+    if (rc != Q4K_OK) {
+        return rc;
+    }
+    const size_t row = q4k_row_bytes(k);
+    if ((size_t)n > SIZE_MAX / row || (size_t)n * row != src_bytes) {
+        return Q4K_ERR_SIZE;
+    }
+    if (!aligned16(w_dev)) {
+        return Q4K_ERR_ALIGN;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(w_dev, src_host, src_bytes, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) {
+        e = hipStreamSynchronize(s);
+    }
+    return hip_status(e);
+}
+
+int q4k_gemv(const void* w, const float* x, float* y, int64_t n, int64_t k, int64_t m,
+             void* stream)
+{
+    return gemv_checked(w, x, y, n, k, m, nullptr, stream);
+}
+
+int q4k_gemv_ex(const void* w, const float* x, float* y, int64_t n, int64_t k, int64_t m,
+                const q4k_launch* opts, void* stream)
+{
+    return gemv_checked(w, x, y, n, k, m, opts, stream);
+}
+
+int q4k_dequantize(const void* w, float* out, int64_t n, int64_t k, void* stream)
+{
+    if (!w || !out) {
+        return Q4K_ERR_NULL;
+    }
+    const int rc = check_nk(n, k);
+    if (rc != Q4K_OK) {
+        return rc;
+    }
+    if (!aligned16(w) || !aligned16(out)) {
+        return Q4K_ERR_ALIGN;
+    }
+    const int64_t nsb = n * (k / q4k::kQK);
+    if ((nsb * 32 + 255) / 256 > kInt32Max) {
+        return Q4K_ERR_SHAPE;
+    }
+    return hip_status(q4k::launch_dequant(w, out, nsb, static_cast<hipStream_t>(stream)));
+}
+
+const char* q4k_status_string(int rc)
+{
+    switch (rc) {
+    case Q4K_OK: return "ok";
+    case Q4K_ERR_NULL: return "a required pointer is NULL";
+    case Q4K_ERR_SHAPE: return "bad shape: need 1 <= n, 256 <= k, k % 256 == 0, 1 <= m, n and k below 2^31";
+    case Q4K_ERR_SIZE: return "byte count does not match n*(k/256)*144";
+    case Q4K_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case Q4K_ERR_UNSUPPORTED: return "unsupported: m > 8, or launch options that do not fit the shape or the device";
+    default: break;
+    }
+    if (rc >= Q4K_ERR_HIP) {
+        return "HIP runtime error (status - 1000 is the hipError_t)";
+    }
+    return "unknown status";
+}
+
+int q4k_read_calibrate_blocks(void)
+{
+    return q4k::kReadBlocks;
+}
+
+int q4k_read_calibrate(const void* buf, size_t bytes, float* out, void* stream)
+{
+    if (!buf || !out) {
+        return Q4K_ERR_NULL;
+    }
+    if (bytes == 0 || bytes % 16 != 0) {
+        return Q4K_ERR_SIZE;
+    }
+    if (!aligned16(buf)) {
+        return Q4K_ERR_ALIGN;
+    }
+    return hip_status(q4k::launch_read(buf, bytes / 16, out, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,37 @@
+// q4k_kernels.h -- internal interface between the C-ABI layer (q4k_api.hip)
+// and the kernels (q4k_kernels.hip).  Not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace q4k {
+
+constexpr int kQK = 256;          // weights per superblock
+constexpr int kBlockBytes = 144;  // bytes per superblock
+constexpr int kSpanSB = 16;       // superblocks per wave pass (4 lanes each)
+constexpr int kSpan = kSpanSB * kQK;
+constexpr int kMaxM = 8;
+constexpr int kReadBlocks = 2048;
+
+// One resolved launch of the GEMV kernel.
+struct GemvPlan {
+    int n, k, S, m;
+    int nspans;            // ceil(S / 16)
+    int spans_per_chunk;   // spans of x staged at once (== nspans: single-stage)
+    int nchunks;
+    int rows_per_block;
+    int rows_per_wave;     // R: 1, 2 or 4 (4 only for m = 1)
+    int waves_per_block;   // 4 or 8
+    int x_in_registers;    // 1: x kept in VGPRs (single span, m = 1)
+    int grid;
+    size_t lds_bytes;
+};
+
+hipError_t launch_gemv(const GemvPlan& p, const void* w, const float* x, float* y,
+                       hipStream_t stream);
+hipError_t launch_dequant(const void* w, float* out, int64_t nsb, hipStream_t stream);
+hipError_t launch_read(const void* buf, size_t n16, float* out, hipStream_t stream);
+
+}  // namespace q4k

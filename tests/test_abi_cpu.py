@@ -1,0 +1,124 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol include/q4k.h
+declares, and refuses bad arguments with the documented status before any
+HIP call (so none of these calls touches a device).
+
+The refusal cases follow the pages' own validation tests (turbospark-runtime
+0.1.0, real_forward_dispatch.rs, test module: valid shape, wrong shape, a byte
+count short by one block) and the pre-launch pointer checks of realizar 0.8.5
+(q4k_gemv_cached.rs: `q4k_gemv_indexed_async`).
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from block_quantized_decode_q4_amd import q4k
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q4k.h")
+
+A = 0x100000          # a 16-byte-aligned fake device address (never dereferenced)
+MIS = 0x100004        # misaligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(q4k_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return q4k.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(q4k.EXPORTED)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for rc in (0, 1, 2, 3, 4, 5, 1001, 77):
+        s = q4k.status_string(rc)
+        assert isinstance(s, str) and s
+    assert q4k.status_string(0) == "ok"
+
+
+def test_row_bytes():
+    assert q4k.q4k_row_bytes(256) == 144
+    assert q4k.q4k_row_bytes(4096) == 16 * 144
+    assert q4k.q4k_row_bytes(14336) == 56 * 144
+    for bad in (0, -256, 255, 257, 100):
+        assert q4k.q4k_row_bytes(bad) == 0
+
+
+def raw_gemv(lib, w, x, y, n, k, m):
+    return lib.q4k_gemv(w, x, y, n, k, m, None)
+
+
+def test_gemv_refusals(lib):
+    assert raw_gemv(lib, None, A, A, 16, 256, 1) == q4k.Q4K_ERR_NULL
+    assert raw_gemv(lib, A, None, A, 16, 256, 1) == q4k.Q4K_ERR_NULL
+    assert raw_gemv(lib, A, A, None, 16, 256, 1) == q4k.Q4K_ERR_NULL
+    for n, k, m in ((0, 256, 1), (-1, 256, 1), (16, 255, 1), (16, 0, 1), (16, 384, 1),
+                    (16, 256, 0), (16, 256, -3), (2 ** 31, 256, 1), (16, 2 ** 31 + 256, 1)):
+        assert raw_gemv(lib, A, A, A, n, k, m) == q4k.Q4K_ERR_SHAPE, (n, k, m)
+    for m in (9, 16, 32):
+        assert raw_gemv(lib, A, A, A, 16, 256, m) == q4k.Q4K_ERR_UNSUPPORTED
+    assert raw_gemv(lib, MIS, A, A, 16, 256, 1) == q4k.Q4K_ERR_ALIGN
+    assert raw_gemv(lib, A, MIS, A, 16, 256, 1) == q4k.Q4K_ERR_ALIGN
+    assert raw_gemv(lib, A, A, MIS, 16, 256, 1) == q4k.Q4K_ERR_ALIGN
+
+
+def test_gemv_ex_refusals(lib):
+    bad_opts = [dict(variant=3), dict(variant=-1), dict(waves_per_block=2), dict(rows_per_wave=3),
+                dict(x_in_registers=5)]
+    for o in bad_opts:
+        cfg = q4k.q4k_launch(**o)
+        rc = lib.q4k_gemv_ex(A, A, A, 16, 256, 1, ctypes.byref(cfg), None)
+        assert rc == q4k.Q4K_ERR_UNSUPPORTED, o
+    # x in registers needs one span and one vector
+    cfg = q4k.q4k_launch(x_in_registers=1)
+    assert lib.q4k_gemv_ex(A, A, A, 16, 8192, 1, ctypes.byref(cfg), None) == q4k.Q4K_ERR_UNSUPPORTED
+    assert lib.q4k_gemv_ex(A, A, A, 16, 256, 2, ctypes.byref(cfg), None) == q4k.Q4K_ERR_UNSUPPORTED
+    # four rows per wave only for one vector
+    cfg = q4k.q4k_launch(rows_per_wave=4)
+    assert lib.q4k_gemv_ex(A, A, A, 16, 256, 2, ctypes.byref(cfg), None) == q4k.Q4K_ERR_UNSUPPORTED
+
+
+def test_load_refusals(lib):
+    host = np.zeros(4 * 144 * 2, np.uint8)
+    hp = host.ctypes.data
+    assert lib.q4k_load(None, hp, host.nbytes, 2, 1024, None) == q4k.Q4K_ERR_NULL
+    assert lib.q4k_load(A, None, host.nbytes, 2, 1024, None) == q4k.Q4K_ERR_NULL
+    assert lib.q4k_load(A, hp, host.nbytes, 2, 1000, None) == q4k.Q4K_ERR_SHAPE
+    assert lib.q4k_load(A, hp, host.nbytes - 144, 2, 1024, None) == q4k.Q4K_ERR_SIZE   # short by one block
+    assert lib.q4k_load(A, hp, host.nbytes + 1, 2, 1024, None) == q4k.Q4K_ERR_SIZE
+    assert lib.q4k_load(A, hp, host.nbytes, 3, 1024, None) == q4k.Q4K_ERR_SIZE           # wrong row count
+    assert lib.q4k_load(MIS, hp, host.nbytes, 2, 1024, None) == q4k.Q4K_ERR_ALIGN
+
+
+def test_dequant_and_calibrate_refusals(lib):
+    assert lib.q4k_dequantize(None, A, 4, 256, None) == q4k.Q4K_ERR_NULL
+    assert lib.q4k_dequantize(A, None, 4, 256, None) == q4k.Q4K_ERR_NULL
+    assert lib.q4k_dequantize(A, A, 4, 300, None) == q4k.Q4K_ERR_SHAPE
+    assert lib.q4k_dequantize(A, A, 0, 256, None) == q4k.Q4K_ERR_SHAPE
+    assert lib.q4k_dequantize(A, MIS, 4, 256, None) == q4k.Q4K_ERR_ALIGN
+    assert lib.q4k_read_calibrate(None, 16, A, None) == q4k.Q4K_ERR_NULL
+    assert lib.q4k_read_calibrate(A, 20, A, None) == q4k.Q4K_ERR_SIZE
+    assert lib.q4k_read_calibrate(A, 0, A, None) == q4k.Q4K_ERR_SIZE
+    assert lib.q4k_read_calibrate(MIS, 32, A, None) == q4k.Q4K_ERR_ALIGN
+    assert q4k.q4k_read_calibrate_blocks() > 0
+
+
+def test_binding_raises_with_status():
+    with pytest.raises(q4k.Q4KError) as ei:
+        q4k.q4k_gemv(0, A, A, 16, 256, 1, stream=0)
+    assert ei.value.rc == q4k.Q4K_ERR_NULL
+    with pytest.raises(q4k.Q4KError) as ei:
+        q4k.q4k_gemv(A, A, A, 16, 256, 9, stream=0)
+    assert ei.value.rc == q4k.Q4K_ERR_UNSUPPORTED
