@@ -102,11 +102,29 @@ int make_plan(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t lds_m
     }
     const int nchunks = (nspans + spc - 1) / spc;
 
-    int nw = (o && o->waves_per_block) ? o->waves_per_block : 4;
-    if (nw != 4 && nw != 8) {
+    const int kernel = (o && o->kernel) ? o->kernel : (m == 1 ? 2 : 1);
+    if (kernel < 1 || kernel > 2 || (kernel == 2 && m != 1)) {
         return Q4K_ERR_UNSUPPORTED;
     }
-    int R = (o && o->rows_per_wave) ? o->rows_per_wave : (m == 1 ? 2 : 1);
+    int nw = (o && o->waves_per_block) ? o->waves_per_block
+                                       : (kernel == 2 ? (nspans > 8 ? 16 : 8) : 8);
+    if (nw != 4 && nw != 8 && !(nw == 16 && kernel == 2)) {
+        return Q4K_ERR_UNSUPPORTED;
+    }
+    // streaming kernel: about 2048 wave tasks (8 per CU of a 256-CU part);
+    // measured best on MI355X for the 4096- to 32000-row shapes
+    int64_t auto_rpt = ((int64_t)nspans * n + 2047) / 2048;
+    auto_rpt = auto_rpt < 1 ? 1 : auto_rpt > 64 ? 64 : auto_rpt;
+    const int64_t rows_per_task = (o && o->rows_per_task) ? o->rows_per_task : auto_rpt;
+    const int ring_cap = nw == 16 ? 2 : 3;
+    const int ring_depth = (o && o->ring_depth) ? o->ring_depth
+                                                : (rows_per_task >= 8 ? ring_cap : 1);
+    // 16-wave workgroups cap a lane at 128 VGPRs: at most 2 rows in flight there
+    if (kernel == 2 && (ring_depth < 1 || ring_depth > 4 || rows_per_task < 1 ||
+                        rows_per_task > kInt32Max || (nw == 16 && ring_depth > 2))) {
+        return Q4K_ERR_UNSUPPORTED;
+    }
+    int R = (o && o->rows_per_wave) ? o->rows_per_wave : 2;
     if (!(R == 1 || R == 2 || (R == 4 && m == 1))) {
         return Q4K_ERR_UNSUPPORTED;
     }
@@ -126,10 +144,15 @@ int make_plan(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t lds_m
     int64_t rpb;
     if (o && o->rows_per_block > 0) {
         rpb = o->rows_per_block;
+    } else if (kernel == 2) {
+        // as many row groups as give every wave one task
+        const int64_t groups = nw > nspans ? nw / nspans : 1;
+        rpb = groups * rows_per_task;
     } else {
-        // about two workgroups per CU of a 256-CU part, whole row groups
+        // about two workgroups per CU of a 256-CU part (one for several
+        // vectors, whose x stage fills most of the LDS), whole row groups
         const int64_t unit = (int64_t)R * nw;
-        rpb = (n + 511) / 512;
+        rpb = m == 1 ? (n + 511) / 512 : (n + 255) / 256;
         rpb = ((rpb + unit - 1) / unit) * unit;
         if (rpb < unit) {
             rpb = unit;
@@ -139,7 +162,7 @@ int make_plan(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t lds_m
         rpb = kInt32Max;
     }
     const size_t lds_x = (size_t)m * spc * (kSpanBytes + kSpanSumBytes);
-    const size_t lds_row = nchunks > 1 ? (size_t)m * 64 * 4 : 0;   // parked lane partials
+    const size_t lds_row = kernel == 2 ? 0 : nchunks > 1 ? (size_t)m * 64 * 4 : 0;   // parked lane partials
     if (lds_row && !(o && o->rows_per_block > 0) && lds_x + (size_t)rpb * lds_row > lds_max) {
         // automatic row blocks shrink to whole row groups that fit the LDS
         const int64_t unit = (int64_t)R * nw;
@@ -152,8 +175,14 @@ int make_plan(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t lds_m
     if (grid > kInt32Max) {
         return Q4K_ERR_SHAPE;
     }
-    // partial sums are parked per row group, so round the rows up to whole groups
-    const size_t lds = lds_x + (size_t)((rpb + R - 1) / R) * R * lds_row;
+    size_t lds;
+    if (kernel == 2) {
+        // x chunk (no LDS sums: each wave sums its own x) + per-span row sums
+        lds = (size_t)spc * kSpanBytes + (nspans > 1 ? (size_t)nspans * rpb * 4 : 0);
+    } else {
+        // partial sums are parked per row group, so round the rows up to whole groups
+        lds = lds_x + (size_t)((rpb + R - 1) / R) * R * lds_row;
+    }
 
     p->n = (int)n;
     p->k = (int)k;
@@ -168,6 +197,9 @@ int make_plan(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t lds_m
     p->x_in_registers = xreg;
     p->grid = (int)grid;
     p->lds_bytes = lds;
+    p->kernel = kernel;
+    p->ring_depth = ring_depth;
+    p->rows_per_task = (int)rows_per_task;
     return Q4K_OK;
 }
 

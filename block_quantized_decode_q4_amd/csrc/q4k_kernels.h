@@ -13,7 +13,7 @@ constexpr int kBlockBytes = 144;  // bytes per superblock
 constexpr int kSpanSB = 16;       // superblocks per wave pass (4 lanes each)
 constexpr int kSpan = kSpanSB * kQK;
 constexpr int kMaxM = 8;
-constexpr int kReadBlocks = 2048;
+constexpr int kReadBlocks = 4096;
 
 // One resolved launch of the GEMV kernel.
 struct GemvPlan {
@@ -27,6 +27,9 @@ struct GemvPlan {
     int x_in_registers;    // 1: x kept in VGPRs (single span, m = 1)
     int grid;
     size_t lds_bytes;
+    int kernel;            // 1: x-stager kernel, 2: DMA streaming kernel (m = 1)
+    int ring_depth;        // streaming kernel: row passes in flight per wave
+    int rows_per_task;     // streaming kernel: rows per wave task
 };
 
 hipError_t launch_gemv(const GemvPlan& p, const void* w, const float* x, float* y,

@@ -129,10 +129,13 @@ __device__ __forceinline__ float wave_sum(float v)
     return v;
 }
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ uint4 load16(const uint8_t* p)
 {
     return *reinterpret_cast<const uint4*>(p);
 }
+
 
 // ------------------------------------------------------------ x stager
 // Stage spans [span0, span0 + nsp) of every vector into LDS in lane order
@@ -145,24 +148,34 @@ __device__ __forceinline__ void stage_x(const float* __restrict__ x, int k, int 
                                         int nsp, float4* xs, float2* sums, int tid, int nthreads)
 {
     const int per_vec = nsp * 1024;
-    for (int slot = tid; slot < M * per_vec; slot += nthreads) {
-        const int b = slot / per_vec;
-        const int rem = slot - b * per_vec;
-        const int sp = rem >> 10;
-        const int v = (rem >> 6) & 15;
-        const int ln = rem & 63;
-        const int sb = (span0 + sp) * 16 + (ln >> 2);
-        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (sb < S) {
-            const int c = ln & 3;
-            const int u = v >> 1;
-            const int h = v & 1;
-            const int e = sb * 256 + 64 * c + 32 * h + 4 * u;
-            const float4 g = *reinterpret_cast<const float4*>(x + (size_t)b * k + e);
-            const float sc = h ? 0.0625f : 1.0f;
-            o = make_float4(g.x * sc, g.z * sc, g.y * sc, g.w * sc);
+    const int total = M * per_vec;
+    // loads in batches of four per thread before the writes (one memory
+    // latency per batch rather than per element)
+    for (int base = tid; base < total; base += 4 * nthreads) {
+        float4 g[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int slot = base + i * nthreads;
+            const int b = slot / per_vec;
+            const int rem = slot - b * per_vec;
+            const int sp = rem >> 10;
+            const int v = (rem >> 6) & 15;
+            const int ln = rem & 63;
+            const int sb = (span0 + sp) * 16 + (ln >> 2);
+            g[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (slot < total && sb < S) {
+                const int e = sb * 256 + 64 * (ln & 3) + 32 * (v & 1) + 4 * (v >> 1);
+                g[i] = *reinterpret_cast<const float4*>(x + (size_t)b * k + e);
+            }
         }
-        xs[slot] = o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int slot = base + i * nthreads;
+            if (slot < total) {
+                const float sc = (((slot - (slot / per_vec) * per_vec) >> 6) & 1) ? 0.0625f : 1.0f;
+                xs[slot] = make_float4(g[i].x * sc, g[i].z * sc, g[i].y * sc, g[i].w * sc);
+            }
+        }
     }
     __syncthreads();
     for (int t = tid; t < M * nsp * 64; t += nthreads) {
@@ -334,6 +347,260 @@ gemv_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x, float* _
     }
 }
 
+// Stage spans [span0, span0 + nsp) of one vector into LDS in lane order
+// (slot (sp*16 + v)*64 + lane; see stage_x).  Loads are issued in batches of
+// four per thread before any of them is written, so the stage costs about
+// one memory latency rather than one per loop trip.
+template <int NT>
+__device__ __forceinline__ void stage_x_batched(const float* __restrict__ x, int S, int span0,
+                                                int nsp, float4* xs, int tid)
+{
+    const int total = nsp * 1024;
+    for (int base = tid; base < total; base += 4 * NT) {
+        float4 g[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int slot = base + i * NT;
+            const int sp = slot >> 10;
+            const int v = (slot >> 6) & 15;
+            const int ln = slot & 63;
+            const int sb = (span0 + sp) * 16 + (ln >> 2);
+            g[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (slot < total && sb < S) {
+                const int e = sb * 256 + 64 * (ln & 3) + 32 * (v & 1) + 4 * (v >> 1);
+                g[i] = *reinterpret_cast<const float4*>(x + e);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int slot = base + i * NT;
+            if (slot < total) {
+                const float sc = ((slot >> 6) & 1) ? 0.0625f : 1.0f;
+                xs[slot] = make_float4(g[i].x * sc, g[i].z * sc, g[i].y * sc, g[i].w * sc);
+            }
+        }
+    }
+}
+
+// ------------------------------------------------ streaming GEMV (m = 1)
+// One vector, x held in VGPRs, rows streamed with a register prefetch.
+//
+// Work split.  A workgroup owns rows_per_block consecutive rows.  A task is
+// (span s, group of rows_per_task rows): one wave decodes those rows'
+// superblocks 16s .. 16s+15 against the 64 x values of its lane (the span's
+// x, read once per task from the LDS stage into VGPRs) and produces one
+// partial dot per row.  With one span the partial is y; with several, the
+// partials go to LDS and are added in span order after a barrier.
+//
+// Streaming.  Each wave keeps P rows of its task in flight: row t+P is
+// requested before row t is decoded, with branch-free (clamped) addresses so
+// the compiler's counter waits let the younger loads stay outstanding.  The
+// first P rows are requested before the x stage, so their HBM latency
+// overlaps it.
+//
+// x stage.  x is staged per K-chunk (spans_per_chunk spans, bounded LDS)
+// in the lane order of gemv_kernel; every wave copies its span into VGPRs
+// right after the stage, so a chunk's LDS is free again once the next
+// barrier is passed.
+//
+// Reduction: one DPP butterfly per row (no LDS traffic); lane 63 holds the
+// row total.
+
+struct RowData {
+    uint4 h, a, b;    // header, quant bytes 32c..32c+15, 32c+16..32c+31
+};
+
+__device__ __forceinline__ RowData load_row(const uint8_t* p, int c)
+{
+    RowData r;
+    r.h = load16(p);
+    r.a = load16(p + 16 + 32 * c);
+    r.b = load16(p + 32 + 32 * c);
+    return r;
+}
+
+// Sum over the 64 lanes with DPP (quad, half-row, row, row broadcasts);
+// the total lands in lane 63.
+__device__ __forceinline__ float dpp_sum_to_lane63(float v)
+{
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+             0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));    // quad_perm 1,0,3,2
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+             0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));    // quad_perm 2,3,0,1
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+             0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));   // row_half_mirror
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+             0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));   // row_mirror
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+             0, __builtin_bit_cast(int, v), 0x142, 0xA, 0xF, false));   // row_bcast:15
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+             0, __builtin_bit_cast(int, v), 0x143, 0xC, 0xF, false));   // row_bcast:31
+    return v;
+}
+
+// Lane constants for the header decode of chunk c (see decode_header).
+struct LaneDecode {
+    uint32_t sh;     // 16 * (c & 1)
+    uint32_t sel;    // all ones for c < 2 (j < 4 form), zero otherwise
+};
+
+// One row's partial dot for this lane: 64 weights of chunk c.
+__device__ __forceinline__ float row_partial(const RowData& q, const float4* xr, float Xl, float Xh,
+                                             const LaneDecode& ld)
+{
+    float alo = 0.f, ahi = 0.f;
+    dot8(q.a.x, xr[0], xr[1], alo, ahi);
+    dot8(q.a.y, xr[2], xr[3], alo, ahi);
+    dot8(q.a.z, xr[4], xr[5], alo, ahi);
+    dot8(q.a.w, xr[6], xr[7], alo, ahi);
+    dot8(q.b.x, xr[8], xr[9], alo, ahi);
+    dot8(q.b.y, xr[10], xr[11], alo, ahi);
+    dot8(q.b.z, xr[12], xr[13], alo, ahi);
+    dot8(q.b.w, xr[14], xr[15], alo, ahi);
+    const half2_t dd = __builtin_bit_cast(half2_t, q.h.x);
+    const uint32_t y = q.h.y >> ld.sh;
+    const uint32_t z = q.h.z >> ld.sh;
+    const uint32_t wv = q.h.w >> ld.sh;
+    const uint32_t sc_b = (wv & 0x0F0Fu) | ((y >> 2) & 0x3030u);
+    const uint32_t m_b = ((wv >> 4) & 0x0F0Fu) | ((z >> 2) & 0x3030u);
+    // select without a branch: (a & sel) | (b & ~sel)
+    const uint32_t sc = ((y & 0x3F3Fu) & ld.sel) | (sc_b & ~ld.sel);
+    const uint32_t mm = ((z & 0x3F3Fu) & ld.sel) | (m_b & ~ld.sel);
+    float t1 = (float)(sc & 0xFFu) * alo;
+    t1 = __builtin_fmaf((float)((sc >> 8) & 0xFFu), ahi, t1);
+    float t2 = (float)(mm & 0xFFu) * Xl;
+    t2 = __builtin_fmaf((float)((mm >> 8) & 0xFFu), Xh, t2);
+    float acc = ((float)dd.x * 16777216.0f) * t1;
+    return __builtin_fmaf(-(float)dd.y, t2, acc);
+}
+
+template <int NW, int P>
+__global__ void __launch_bounds__(NW * 64)
+gemv_stream_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
+                   float* __restrict__ y, int n, int k, int S, int rows_per_block,
+                   int rows_per_task, int spans_per_chunk)
+{
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+    const int c = lane & 3;
+    const int sbl = lane >> 2;
+    LaneDecode ld;
+    ld.sh = (uint32_t)(c & 1) * 16u;
+    ld.sel = c < 2 ? 0xFFFFFFFFu : 0u;
+
+    const int nspans = (S + 15) >> 4;
+    const int chunk_spans = spans_per_chunk < nspans ? spans_per_chunk : nspans;
+    const int nchunks = (nspans + chunk_spans - 1) / chunk_spans;
+    const int row0 = blockIdx.x * rows_per_block;
+    const int rows_here = min(rows_per_block, n - row0);
+    const int ngroups = (rows_here + rows_per_task - 1) / rows_per_task;
+    const size_t row_bytes = (size_t)S * 144;
+
+    float4* xs = reinterpret_cast<float4*>(smem);
+    float* ypart = reinterpret_cast<float*>(xs + chunk_spans * 1024);
+
+    for (int ch = 0; ch < nchunks; ++ch) {
+        const int span0 = ch * chunk_spans;
+        const int nsp = min(chunk_spans, nspans - span0);
+        const int ntasks = nsp * ngroups;
+
+        // the first task's prologue goes out before the stage
+        int task = wave;
+        RowData buf[P];
+        if (task < ntasks) {
+            const int span = span0 + task % nsp;
+            const int rb = (task / nsp) * rows_per_task;
+            const int T = min(rows_per_task, rows_here - rb);
+            const int sb = min(span * 16 + sbl, S - 1);        // clamped: in bounds
+            const uint8_t* base = w + (size_t)(row0 + rb) * row_bytes + (size_t)sb * 144;
+#pragma unroll
+            for (int j = 0; j < P; ++j) {
+                buf[j] = load_row(base + (size_t)min(j, T - 1) * row_bytes, c);
+            }
+        }
+        if (ch > 0) {
+            __syncthreads();          // every wave has copied its x of the previous chunk
+        }
+        stage_x_batched<NW * 64>(x, S, span0, nsp, xs, tid);
+        __syncthreads();
+
+        for (; task < ntasks; task += NW) {
+            const int sp = task % nsp;
+            const int span = span0 + sp;
+            const int rb = (task / nsp) * rows_per_task;
+            const int T = min(rows_per_task, rows_here - rb);
+            const int sb = min(span * 16 + sbl, S - 1);
+            const uint8_t* base = w + (size_t)(row0 + rb) * row_bytes + (size_t)sb * 144;
+            if (task != wave) {
+#pragma unroll
+                for (int j = 0; j < P; ++j) {
+                    buf[j] = load_row(base + (size_t)min(j, T - 1) * row_bytes, c);
+                }
+            }
+            float4 xr[16];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                xr[v] = xs[(sp * 16 + v) * 64 + lane];
+            }
+            float Xl = 0.f, Xh = 0.f;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                Xl += (xr[2 * u].x + xr[2 * u].y) + (xr[2 * u].z + xr[2 * u].w);
+                Xh += (xr[2 * u + 1].x + xr[2 * u + 1].y) + (xr[2 * u + 1].z + xr[2 * u + 1].w);
+            }
+            Xh *= 16.0f;                    // exact: undoes the 1/16 of the stage
+
+            // y (global) or the per-span row sums (LDS): two typed pointers, so
+            // that neither store becomes a flat access, which would make the
+            // compiler drain the prefetched loads at every row
+            float* yout = y + row0 + rb;
+            float* pout = ypart + span * rows_per_block + rb;
+            const bool direct = nspans == 1;
+            int t = 0;
+            for (; t + P <= T; t += P) {
+#pragma unroll
+                for (int j = 0; j < P; ++j) {
+                    const RowData q = buf[j];
+                    buf[j] = load_row(base + (size_t)min(t + j + P, T - 1) * row_bytes, c);
+                    const float v = dpp_sum_to_lane63(row_partial(q, xr, Xl, Xh, ld));
+                    if (lane == 63) {
+                        if (direct) {
+                            yout[t + j] = v;
+                        } else {
+                            pout[t + j] = v;
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < P; ++j) {
+                if (t + j < T) {
+                    const float v = dpp_sum_to_lane63(row_partial(buf[j], xr, Xl, Xh, ld));
+                    if (lane == 63) {
+                        if (direct) {
+                            yout[t + j] = v;
+                        } else {
+                            pout[t + j] = v;
+                        }
+                    }
+                }
+            }
+        }
+    }
+    if (nspans > 1) {
+        __syncthreads();
+        for (int r = tid; r < rows_here; r += NW * 64) {
+            float acc = 0.f;
+            for (int sp = 0; sp < nspans; ++sp) {
+                acc += ypart[sp * rows_per_block + r];
+            }
+            y[row0 + r] = acc;
+        }
+    }
+}
+
 // ------------------------------------------------------------- dequant
 // One thread per (superblock, chunk c, dword u): decodes 8 weights and
 // writes them as two float4.  w = fma(d*sc, q, -dmin*m); d*sc and dmin*m
@@ -383,35 +650,38 @@ dequant_kernel(const uint8_t* __restrict__ w, float* __restrict__ out, int64_t n
 // --------------------------------------------------------- calibration
 // Streaming read of n16 16-byte words with the same load width the GEMV
 // uses; the xor checksum keeps the loads alive.
-__global__ void __launch_bounds__(256)
-read_kernel(const uint4* __restrict__ buf, size_t n16, float* __restrict__ out)
+// Each workgroup streams one contiguous slice with non-temporal loads (the
+// fastest of the plain read patterns measured on MI355X: about 7 TB/s,
+// against about 5 TB/s with ordinary loads).  The GEMV itself uses ordinary
+// loads: its lanes read parts of 144-byte superblocks with several
+// instructions, and those share cache lines that a non-temporal load would
+// not keep.
+__global__ void __launch_bounds__(1024)
+read_kernel(const u32x4_t* __restrict__ buf, size_t n16, float* __restrict__ out)
 {
     uint32_t acc = 0;
-    const size_t stride = (size_t)gridDim.x * blockDim.x;
-    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    for (; i + 3 * stride < n16; i += 4 * stride) {
-        const uint4 a = buf[i];
-        const uint4 b = buf[i + stride];
-        const uint4 c = buf[i + 2 * stride];
-        const uint4 d = buf[i + 3 * stride];
-        acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w;
-        acc ^= c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
-    }
-    for (; i < n16; i += stride) {
-        const uint4 a = buf[i];
+    const size_t per = (n16 + gridDim.x - 1) / gridDim.x;
+    const size_t b0 = (size_t)blockIdx.x * per;
+    const size_t b1 = b0 + per < n16 ? b0 + per : n16;
+    for (size_t i = b0 + threadIdx.x; i < b1; i += blockDim.x) {
+        const u32x4_t a = __builtin_nontemporal_load(buf + i);
         acc ^= a.x ^ a.y ^ a.z ^ a.w;
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
         acc ^= (uint32_t)__shfl_xor((int)acc, off, 64);
     }
-    __shared__ uint32_t part[4];
+    __shared__ uint32_t part[16];
     if ((threadIdx.x & 63) == 0) {
         part[threadIdx.x >> 6] = acc;
     }
     __syncthreads();
     if (threadIdx.x == 0) {
-        out[blockIdx.x] = (float)((part[0] ^ part[1] ^ part[2] ^ part[3]) & 0xFFFFu);
+        uint32_t t = 0;
+        for (int i = 0; i < (int)(blockDim.x >> 6); ++i) {
+            t ^= part[i];
+        }
+        out[blockIdx.x] = (float)(t & 0xFFFFu);
     }
 }
 
@@ -458,10 +728,40 @@ static hipError_t launch_m(const GemvPlan& p, const uint8_t* w, const float* x, 
     }
 }
 
+template <int NW, int P>
+static hipError_t launch_stream(const GemvPlan& p, const uint8_t* w, const float* x, float* y,
+                                hipStream_t stream)
+{
+    hipLaunchKernelGGL((gemv_stream_kernel<NW, P>), dim3(p.grid), dim3(NW * 64), p.lds_bytes,
+                       stream, w, x, y, p.n, p.k, p.S, p.rows_per_block, p.rows_per_task,
+                       p.spans_per_chunk);
+    return hipGetLastError();
+}
+
+template <int NW>
+static hipError_t launch_stream_nw(const GemvPlan& p, const uint8_t* w, const float* x, float* y,
+                                   hipStream_t stream)
+{
+    if (p.ring_depth == 1) return launch_stream<NW, 1>(p, w, x, y, stream);
+    if constexpr (NW == 16) {
+        // 1024-thread workgroups leave 128 VGPRs per lane: two rows in flight
+        return launch_stream<NW, 2>(p, w, x, y, stream);
+    } else {
+        if (p.ring_depth == 2) return launch_stream<NW, 2>(p, w, x, y, stream);
+        if (p.ring_depth == 3) return launch_stream<NW, 3>(p, w, x, y, stream);
+        return launch_stream<NW, 4>(p, w, x, y, stream);
+    }
+}
+
 hipError_t launch_gemv(const GemvPlan& p, const void* w, const float* x, float* y,
                        hipStream_t stream)
 {
     const uint8_t* wb = static_cast<const uint8_t*>(w);
+    if (p.kernel == 2) {
+        if (p.waves_per_block == 16) return launch_stream_nw<16>(p, wb, x, y, stream);
+        if (p.waves_per_block == 8) return launch_stream_nw<8>(p, wb, x, y, stream);
+        return launch_stream_nw<4>(p, wb, x, y, stream);
+    }
     switch (p.m) {
     case 1: return launch_m<1>(p, wb, x, y, stream);
     case 2: return launch_m<2>(p, wb, x, y, stream);
@@ -486,8 +786,8 @@ hipError_t launch_dequant(const void* w, float* out, int64_t nsb, hipStream_t st
 
 hipError_t launch_read(const void* buf, size_t n16, float* out, hipStream_t stream)
 {
-    hipLaunchKernelGGL(read_kernel, dim3(kReadBlocks), dim3(256), 0, stream,
-                       static_cast<const uint4*>(buf), n16, out);
+    hipLaunchKernelGGL(read_kernel, dim3(kReadBlocks), dim3(1024), 0, stream,
+                       static_cast<const u32x4_t*>(buf), n16, out);
     return hipGetLastError();
 }
 

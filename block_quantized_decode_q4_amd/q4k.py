@@ -50,6 +50,9 @@ class q4k_launch(ctypes.Structure):
         ("rows_per_wave", ctypes.c_int32),
         ("waves_per_block", ctypes.c_int32),
         ("x_in_registers", ctypes.c_int32),
+        ("kernel", ctypes.c_int32),
+        ("ring_depth", ctypes.c_int32),
+        ("rows_per_task", ctypes.c_int32),
     ]
 
 

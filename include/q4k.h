@@ -116,8 +116,11 @@ typedef struct q4k_launch {
     int32_t spans_per_chunk;  /* K-chunked: spans per stage, >= 1 (0 = automatic)  */
     int32_t rows_per_block;   /* rows per workgroup (0 = automatic)                */
     int32_t rows_per_wave;    /* rows a wave decodes per pass: 0 auto, 1, 2 or 4   */
-    int32_t waves_per_block;  /* 0 auto, 4 or 8                                    */
+    int32_t waves_per_block;  /* 0 auto, 4 or 8 (streaming kernel: also 16)        */
     int32_t x_in_registers;   /* 0 auto, 1 keep x in VGPRs (one span, m = 1), 2 LDS */
+    int32_t kernel;           /* 0 auto, 1 x-stager kernel, 2 streaming kernel (m = 1) */
+    int32_t ring_depth;       /* streaming: rows in flight per wave, 0 auto, 1..4      */
+    int32_t rows_per_task;    /* streaming: rows per wave task, 0 auto, >= 1           */
 } q4k_launch;
 
 /* q4k_gemv with explicit launch options (NULL = automatic).  Options that do

@@ -107,26 +107,67 @@ def test_load_then_gemv(oracle_mod):
 
 
 VARIANTS = [
-    dict(variant=1),
-    dict(variant=2, spans_per_chunk=1),
-    dict(variant=2, spans_per_chunk=2),
-    dict(variant=1, rows_per_wave=1),
-    dict(variant=1, rows_per_wave=4),
-    dict(variant=1, waves_per_block=8),
-    dict(variant=2, spans_per_chunk=1, rows_per_wave=4, waves_per_block=8),
-    dict(variant=1, rows_per_block=5, rows_per_wave=2),
-    dict(variant=2, spans_per_chunk=1, rows_per_block=3, rows_per_wave=4),
-    dict(variant=1, rows_per_block=1000, rows_per_wave=4),
-    dict(variant=1, x_in_registers=2),
+    dict(kernel=1, variant=1),
+    dict(kernel=1, variant=2, spans_per_chunk=1),
+    dict(kernel=1, variant=2, spans_per_chunk=2),
+    dict(kernel=1, variant=1, rows_per_wave=1),
+    dict(kernel=1, variant=1, rows_per_wave=4),
+    dict(kernel=1, variant=1, waves_per_block=8),
+    dict(kernel=1, variant=2, spans_per_chunk=1, rows_per_wave=4, waves_per_block=8),
+    dict(kernel=1, variant=1, rows_per_block=5, rows_per_wave=2),
+    dict(kernel=1, variant=2, spans_per_chunk=1, rows_per_block=3, rows_per_wave=4),
+    dict(kernel=1, variant=1, rows_per_block=1000, rows_per_wave=4),
+    dict(kernel=1, variant=1, x_in_registers=2),
 ]
+
+
+STREAM_VARIANTS = [
+    dict(kernel=2),
+    dict(kernel=2, ring_depth=2, rows_per_task=7),
+    dict(kernel=2, ring_depth=2, rows_per_task=64, waves_per_block=16),
+    dict(kernel=2, ring_depth=4, rows_per_task=16, waves_per_block=8),
+    dict(kernel=2, ring_depth=3, rows_per_task=1, waves_per_block=4, rows_per_block=3),
+    dict(kernel=2, ring_depth=1, rows_per_task=3, waves_per_block=16),
+    dict(kernel=2, variant=2, spans_per_chunk=1, rows_per_task=5, rows_per_block=37),
+    dict(kernel=2, variant=1, rows_per_task=33, rows_per_block=200),
+]
+
+
+@pytest.mark.parametrize("i", [0, 1, 2, 3])
+def test_streaming_kernel_variants(oracle_mod, i):
+    """The streaming kernel: within tolerance and bit-identical across its
+    launch options (each row-span partial is one wave's fixed sequence; spans
+    are added in a fixed order)."""
+    wl, w, x, y_ref, bound = workload(i, oracle_mod)
+    w_d = dev(w)
+    base = None
+    for opts in STREAM_VARIANTS:
+        _say("workload %d streaming %r" % (i, opts))
+        y = run_gemv(w_d, x, wl.n, wl.k, wl.m, **opts)
+        assert_within(y, y_ref, bound, "streaming %r" % opts)
+        if base is None:
+            base = y
+        else:
+            assert np.array_equal(y.view(np.uint32), base.view(np.uint32)), opts
+
+
+@pytest.mark.parametrize("n,k", [(1, 256), (5, 768), (130, 4096 + 2304), (65, 12544), (3, 65536)])
+def test_streaming_kernel_shapes(oracle_mod, n, k):
+    w, x = synth.make_inputs(n, k, 1, seed=n + 3 * k)
+    y_ref, bound = oracle_mod.gemv(w, x, n)
+    w_d = dev(w)
+    for opts in STREAM_VARIANTS[:3]:
+        _say("streaming n=%d k=%d %r" % (n, k, opts))
+        y = run_gemv(w_d, x, n, k, 1, **opts)
+        assert_within(y, y_ref, bound, "streaming n=%d k=%d %r" % (n, k, opts))
 
 
 @pytest.mark.parametrize("i", [0, 1, 2])
 def test_variants_bit_identical(oracle_mod, i):
     wl, w, x, y_ref, bound = workload(i, oracle_mod)
     w_d = dev(w)
-    base = run_gemv(w_d, x, wl.n, wl.k, wl.m)
-    assert_within(base, y_ref, bound, "auto")
+    base = run_gemv(w_d, x, wl.n, wl.k, wl.m, kernel=1)
+    assert_within(base, y_ref, bound, "x-stager kernel")
     for opts in VARIANTS:
         _say("workload %d variant %r" % (i, opts))
         try:
@@ -146,11 +187,17 @@ def test_batched_equals_separate_calls(oracle_mod, m):
     _say("batched m=%d n=%d k=%d" % (m, n, k))
     y_ref, bound = oracle_mod.gemv(w, x, n)
     w_d = dev(w)
-    yb = run_gemv(w_d, x, n, k, m)
-    assert_within(yb, y_ref, bound, "batched m=%d" % m)
+    yauto = run_gemv(w_d, x, n, k, m)
+    assert_within(yauto, y_ref, bound, "batched m=%d" % m)
+    yb = run_gemv(w_d, x, n, k, m, kernel=1)
+    assert_within(yb, y_ref, bound, "batched m=%d, x-stager kernel" % m)
     for b in range(m):
-        y1 = run_gemv(w_d, x[b:b + 1], n, k, 1)
+        # the same kernel family at m = 1 is bit-identical; the default m = 1
+        # kernel (streaming) reduces in another order and is within tolerance
+        y1 = run_gemv(w_d, x[b:b + 1], n, k, 1, kernel=1)
         assert np.array_equal(y1[0].view(np.uint32), yb[b].view(np.uint32)), b
+        y2 = run_gemv(w_d, x[b:b + 1], n, k, 1)
+        assert_within(y2, y_ref[b:b + 1], bound[b:b + 1], "m=1 default, vector %d" % b)
 
 
 def test_batched_workload_against_separate(oracle_mod):
@@ -158,7 +205,7 @@ def test_batched_workload_against_separate(oracle_mod):
     w_d = dev(w)
     yb = run_gemv(w_d, x, wl.n, wl.k, wl.m)
     for b in range(wl.m):
-        y1 = run_gemv(w_d, x[b:b + 1], wl.n, wl.k, 1)
+        y1 = run_gemv(w_d, x[b:b + 1], wl.n, wl.k, 1, kernel=1)
         assert np.array_equal(y1[0].view(np.uint32), yb[b].view(np.uint32)), b
 
 
