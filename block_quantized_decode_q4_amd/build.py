@@ -16,8 +16,9 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libq4k.so")
-SOURCES = [os.path.join(CSRC, "q4k_kernels.hip"), os.path.join(CSRC, "q4k_api.hip")]
-HEADERS = [os.path.join(CSRC, "q4k_kernels.h"),
+SOURCES = [os.path.join(CSRC, "q4k_kernels.hip"), os.path.join(CSRC, "q4k_mfma.hip"),
+           os.path.join(CSRC, "q4k_api.hip")]
+HEADERS = [os.path.join(CSRC, "q4k_kernels.h"), os.path.join(CSRC, "q4k_device.h"),
            os.path.join(os.path.dirname(PKG), "include", "q4k.h")]
 ARCH = "gfx950"
 

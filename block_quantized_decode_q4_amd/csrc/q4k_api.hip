@@ -75,10 +75,180 @@ int device_lds_max(size_t* out)
     return Q4K_OK;
 }
 
+// Plan of the matrix-core kernel (m = 1).  A task is a group of superblock
+// columns times 1, 2 or 4 tiles of 16 rows; the automatic choice makes about
+// 4096 tasks (16 per CU of a 256-CU part) and gives every wave of a workgroup
+// one task per x stage.
+int make_plan_mfma(int64_t n, int64_t k, int kernel, const q4k_launch* o, GemvPlan* p)
+{
+    const int S = (int)(k / q4k::kQK);
+    const int nw = (o && o->waves_per_block) ? o->waves_per_block : 8;
+    const int tpt = (o && o->tiles_per_task) ? o->tiles_per_task : 1;
+    // ring: f16 kernel 1, 2 or 4 steps; int8 kernel 1, 2 or 3 columns in flight
+    const int ring = (o && o->ring_depth) ? o->ring_depth : 2;
+    const bool ring_ok = kernel == 4 ? (ring >= 1 && ring <= 3) : (ring == 1 || ring == 2 || ring == 4);
+    if ((nw != 4 && nw != 8) || (tpt != 1 && tpt != 2 && tpt != 4) || !ring_ok) {
+        return Q4K_ERR_UNSUPPORTED;
+    }
+    if (o && (o->cols_per_task < 0 || o->cols_per_chunk < 0 || o->rows_per_block < 0 ||
+              o->variant != 0 || o->spans_per_chunk != 0 || o->rows_per_wave != 0 ||
+              o->x_in_registers != 0 || o->rows_per_task != 0)) {
+        return Q4K_ERR_UNSUPPORTED;
+    }
+    const int64_t ntiles = (n + 15) / 16;
+    const int64_t ntg = (ntiles + tpt - 1) / tpt;
+    int64_t cpt = (o && o->cols_per_task) ? o->cols_per_task : ((int64_t)S * ntg + 4095) / 4096;
+    cpt = cpt < 1 ? 1 : cpt > S ? S : cpt;
+    const int64_t ncg = (S + cpt - 1) / cpt;
+    // x stage: the requested columns (whole tasks), else about 64 KiB
+    int64_t chunk_cols = (o && o->cols_per_chunk) ? o->cols_per_chunk
+                                                  : (64 * 1024) / (int64_t)q4k::mfma_col_bytes(kernel);
+    int64_t gpc = chunk_cols / cpt;
+    gpc = gpc < 1 ? 1 : gpc > ncg ? ncg : gpc;
+    int64_t rpb;
+    if (o && o->rows_per_block > 0) {
+        rpb = o->rows_per_block;
+    } else {
+        const int64_t tile_groups = nw > ncg ? nw / ncg : 1;
+        rpb = tile_groups * tpt * 16;
+    }
+    if (rpb > kInt32Max / (ncg > 1 ? ncg : 1)) {
+        return Q4K_ERR_SHAPE;
+    }
+    const int64_t grid = (n + rpb - 1) / rpb;
+    const int64_t cols_chunk = gpc * cpt < S ? gpc * cpt : S;
+    const size_t lds = q4k::mfma_lds_bytes(kernel, (int)cols_chunk) +
+                       (ncg > 1 ? (size_t)ncg * rpb * 4 : 0);
+
+    p->n = (int)n;
+    p->k = (int)k;
+    p->S = S;
+    p->m = 1;
+    p->nspans = (S + q4k::kSpanSB - 1) / q4k::kSpanSB;
+    p->spans_per_chunk = 0;
+    p->nchunks = (int)((ncg + gpc - 1) / gpc);
+    p->rows_per_block = (int)rpb;
+    p->rows_per_wave = 0;
+    p->waves_per_block = nw;
+    p->x_in_registers = 0;
+    p->grid = (int)grid;
+    p->lds_bytes = lds;
+    p->kernel = kernel;
+    p->ring_depth = ring;
+    p->rows_per_task = 0;
+    p->cols_per_task = (int)cpt;
+    p->tiles_per_task = tpt;
+    p->groups_per_chunk = (int)gpc;
+    return Q4K_OK;
+}
+
+// Plan of the line-streamed kernel (m = 1, k a multiple of 2048, weights
+// 128-byte aligned).  A task is a 16-row tile times a group of slabs of
+// eight superblock columns; x is staged whole.
+int make_plan_lines(int64_t n, int64_t k, const q4k_launch* o, GemvPlan* p)
+{
+    const int S = (int)(k / q4k::kQK);
+    if (S % 8 != 0) {
+        return Q4K_ERR_UNSUPPORTED;
+    }
+    const int nslabs = S / 8;
+    const int nw = (o && o->waves_per_block) ? o->waves_per_block : 8;
+    if (nw != 4 && nw != 8 && nw != 16) {
+        return Q4K_ERR_UNSUPPORTED;
+    }
+    if (o && (o->cols_per_task < 0 || o->rows_per_block < 0 || o->variant != 0 ||
+              o->spans_per_chunk != 0 || o->rows_per_wave != 0 || o->x_in_registers != 0 ||
+              o->rows_per_task != 0 || o->tiles_per_task != 0 || o->cols_per_chunk != 0 ||
+              (o->ring_depth != 0 && o->ring_depth != 3 && o->ring_depth != 9))) {
+        return Q4K_ERR_UNSUPPORTED;
+    }
+    const int ring = (o && o->ring_depth) ? o->ring_depth : 3;
+    if (nw == 16 && ring == 9) {
+        return Q4K_ERR_UNSUPPORTED;    // 1024-lane workgroups cap a lane at 128 VGPRs
+    }
+    const int64_t ntiles = (n + 15) / 16;
+    int64_t spt;
+    if (o && o->cols_per_task) {
+        if (o->cols_per_task % 8 != 0 || nslabs % (o->cols_per_task / 8) != 0) {
+            return Q4K_ERR_UNSUPPORTED;
+        }
+        spt = o->cols_per_task / 8;
+    } else {
+        spt = 1;          // one slab per task: measured best on MI355X
+    }
+    const int64_t ncg = nslabs / spt;
+    int64_t rpb;
+    if (o && o->rows_per_block > 0) {
+        rpb = o->rows_per_block;
+    } else {
+        // about one workgroup per CU of a 256-CU part: each stages x once
+        const int64_t tiles_pb = (ntiles + 128) / 256;
+        rpb = 16 * (tiles_pb < 1 ? 1 : tiles_pb);
+    }
+    if (rpb > kInt32Max / ncg) {
+        return Q4K_ERR_SHAPE;
+    }
+    const int64_t grid = (n + rpb - 1) / rpb;
+    const size_t lds = q4k::lines_lds_bytes(S, nw) + (ncg > 1 ? (size_t)ncg * rpb * 4 : 0);
+
+    p->n = (int)n;
+    p->k = (int)k;
+    p->S = S;
+    p->m = 1;
+    p->nspans = (S + q4k::kSpanSB - 1) / q4k::kSpanSB;
+    p->spans_per_chunk = 0;
+    p->nchunks = 1;
+    p->rows_per_block = (int)rpb;
+    p->rows_per_wave = 0;
+    p->waves_per_block = nw;
+    p->x_in_registers = 0;
+    p->grid = (int)grid;
+    p->lds_bytes = lds;
+    p->kernel = 5;
+    p->ring_depth = ring;
+    p->rows_per_task = 0;
+    p->cols_per_task = (int)(spt * 8);
+    p->tiles_per_task = 1;
+    p->groups_per_chunk = 1;
+    return Q4K_OK;
+}
+
 // Resolve launch options into a plan.  Pure host arithmetic, no HIP calls.
 // Plans needing more LDS than lds_max are returned as they are; the caller
 // refuses them.
-int make_plan(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t lds_max, GemvPlan* p)
+// The automatic kernel.  m > 1: the x-stager kernel.  m = 1: the
+// line-streamed kernel where it applies (k a multiple of 2048, 128-byte
+// aligned weights, its LDS fits) and the weights are at least 16 MiB, else
+// the streaming kernel, whose shorter start wins on smaller matrices
+// (measured on MI355X).  Options other than `kernel` keep the earlier
+// families: streaming for m = 1, x-stager otherwise.
+bool any_option(const q4k_launch* o)
+{
+    return o && (o->variant || o->spans_per_chunk || o->rows_per_block || o->rows_per_wave ||
+                 o->waves_per_block || o->x_in_registers || o->ring_depth || o->rows_per_task ||
+                 o->cols_per_task || o->tiles_per_task || o->cols_per_chunk);
+}
+
+int auto_kernel(int64_t n, int64_t k, int64_t m, const q4k_launch* o, bool w_aligned128,
+                size_t lds_max)
+{
+    if (m != 1) {
+        return 1;
+    }
+    if (any_option(o)) {
+        return 2;
+    }
+    const int64_t bytes = n * (k / q4k::kQK) * q4k::kBlockBytes;
+    GemvPlan lp;
+    if (w_aligned128 && bytes >= ((int64_t)16 << 20) &&
+        make_plan_lines(n, k, nullptr, &lp) == Q4K_OK && lp.lds_bytes <= lds_max) {
+        return 5;
+    }
+    return 2;
+}
+
+int make_plan(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t lds_max, GemvPlan* p,
+              bool w_aligned128 = true)
 {
     const int S = (int)(k / q4k::kQK);
     const int nspans = (S + q4k::kSpanSB - 1) / q4k::kSpanSB;
@@ -102,9 +272,18 @@ int make_plan(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t lds_m
     }
     const int nchunks = (nspans + spc - 1) / spc;
 
-    const int kernel = (o && o->kernel) ? o->kernel : (m == 1 ? 2 : 1);
-    if (kernel < 1 || kernel > 2 || (kernel == 2 && m != 1)) {
+    const int kernel = (o && o->kernel) ? o->kernel : auto_kernel(n, k, m, o, w_aligned128, lds_max);
+    if (kernel < 1 || kernel > 5 || (kernel >= 2 && m != 1)) {
         return Q4K_ERR_UNSUPPORTED;
+    }
+    if (kernel == 5) {
+        return make_plan_lines(n, k, o, p);
+    }
+    if (kernel >= 3) {
+        return make_plan_mfma(n, k, kernel, o, p);
+    }
+    if (o && (o->cols_per_task || o->tiles_per_task || o->cols_per_chunk)) {
+        return Q4K_ERR_UNSUPPORTED;   // matrix-core options only
     }
     int nw = (o && o->waves_per_block) ? o->waves_per_block
                                        : (kernel == 2 ? (nspans > 8 ? 16 : 8) : 8);
@@ -164,9 +343,17 @@ int make_plan(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t lds_m
     const size_t lds_x = (size_t)m * spc * (kSpanBytes + kSpanSumBytes);
     const size_t lds_row = kernel == 2 ? 0 : nchunks > 1 ? (size_t)m * 64 * 4 : 0;   // parked lane partials
     if (lds_row && !(o && o->rows_per_block > 0) && lds_x + (size_t)rpb * lds_row > lds_max) {
-        // automatic row blocks shrink to whole row groups that fit the LDS
-        const int64_t unit = (int64_t)R * nw;
+        // automatic row blocks shrink to whole row groups that fit the LDS;
+        // an automatic row count per wave, then wave count, shrinks first
+        // when not even one group fits
         const int64_t fit = lds_x < lds_max ? (int64_t)((lds_max - lds_x) / lds_row) : 0;
+        if (!(o && o->rows_per_wave) && fit < (int64_t)R * nw) {
+            R = 1;
+        }
+        if (!(o && o->waves_per_block) && fit < (int64_t)R * nw) {
+            nw = 4;
+        }
+        const int64_t unit = (int64_t)R * nw;
         if (fit >= unit) {
             rpb = (fit / unit) * unit;
         }
@@ -200,6 +387,9 @@ int make_plan(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t lds_m
     p->kernel = kernel;
     p->ring_depth = ring_depth;
     p->rows_per_task = (int)rows_per_task;
+    p->cols_per_task = 0;
+    p->tiles_per_task = 0;
+    p->groups_per_chunk = 0;
     return Q4K_OK;
 }
 
@@ -224,8 +414,9 @@ int gemv_checked(const void* w, const float* x, float* y, int64_t n, int64_t k, 
     }
     // options are validated before the first HIP call (unbounded LDS), then
     // planned for the device's LDS size
+    const bool w128 = (reinterpret_cast<uintptr_t>(w) & 127u) == 0;
     GemvPlan plan;
-    rc = make_plan(n, k, m, opts, SIZE_MAX, &plan);
+    rc = make_plan(n, k, m, opts, SIZE_MAX, &plan, w128);
     if (rc != Q4K_OK) {
         return rc;
     }
@@ -234,12 +425,15 @@ int gemv_checked(const void* w, const float* x, float* y, int64_t n, int64_t k, 
     if (rc != Q4K_OK) {
         return rc;
     }
-    rc = make_plan(n, k, m, opts, lds_max, &plan);
+    rc = make_plan(n, k, m, opts, lds_max, &plan, w128);
     if (rc != Q4K_OK) {
         return rc;
     }
     if (plan.lds_bytes > lds_max) {
         return Q4K_ERR_UNSUPPORTED;
+    }
+    if (plan.kernel == 5 && (reinterpret_cast<uintptr_t>(w) & 127u) != 0) {
+        return Q4K_ERR_UNSUPPORTED;    // whole-line reads need 128-byte aligned rows
     }
     return hip_status(q4k::launch_gemv(plan, w, x, y, static_cast<hipStream_t>(stream)));
 }

@@ -27,13 +27,22 @@ struct GemvPlan {
     int x_in_registers;    // 1: x kept in VGPRs (single span, m = 1)
     int grid;
     size_t lds_bytes;
-    int kernel;            // 1: x-stager kernel, 2: DMA streaming kernel (m = 1)
-    int ring_depth;        // streaming kernel: row passes in flight per wave
+    int kernel;            // 1: x-stager, 2: streaming, 3: f16 matrix-core, 4: int8 matrix-core,
+                           // 5: line-streamed int8 matrix-core (m = 1)
+    int ring_depth;        // kernels 2, 3: loads in flight per wave
     int rows_per_task;     // streaming kernel: rows per wave task
+    int cols_per_task;     // matrix-core kernel: superblock columns per task
+    int tiles_per_task;    // matrix-core kernel: 16-row tiles per task (1, 2, 4)
+    int groups_per_chunk;  // matrix-core kernel: column groups per x stage
 };
 
 hipError_t launch_gemv(const GemvPlan& p, const void* w, const float* x, float* y,
                        hipStream_t stream);
+hipError_t launch_gemv_mfma(const GemvPlan& p, const void* w, const float* x, float* y,
+                            hipStream_t stream);
+size_t mfma_col_bytes(int kernel);
+size_t mfma_lds_bytes(int kernel, int cols_chunk);
+size_t lines_lds_bytes(int S, int waves);
 hipError_t launch_dequant(const void* w, float* out, int64_t nsb, hipStream_t stream);
 hipError_t launch_read(const void* buf, size_t n16, float* out, hipStream_t stream);
 

@@ -53,6 +53,9 @@ class q4k_launch(ctypes.Structure):
         ("kernel", ctypes.c_int32),
         ("ring_depth", ctypes.c_int32),
         ("rows_per_task", ctypes.c_int32),
+        ("cols_per_task", ctypes.c_int32),
+        ("tiles_per_task", ctypes.c_int32),
+        ("cols_per_chunk", ctypes.c_int32),
     ]
 
 

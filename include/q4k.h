@@ -101,7 +101,11 @@ const char* q4k_status_string(int rc);
 
 /* ---------------------------------------------------------------------
  * Launch options for q4k_gemv_ex (tests and tuning).  q4k_gemv is
- * q4k_gemv_ex with every field 0 (automatic).
+ * q4k_gemv_ex with every field 0 (automatic): for m = 1 the line-streamed
+ * matrix-core kernel when k % 2048 == 0, w is 128-byte aligned and the
+ * weights take at least 16 MiB, else the streaming kernel; for m > 1 the
+ * x-stager kernel.  With kernel = 0 and another field set, m = 1 uses the
+ * streaming kernel.
  *
  * x is staged in LDS in spans of 4096 elements per vector.  The single-stage
  * variant holds all of x at once; the K-chunked variant stages
@@ -118,9 +122,19 @@ typedef struct q4k_launch {
     int32_t rows_per_wave;    /* rows a wave decodes per pass: 0 auto, 1, 2 or 4   */
     int32_t waves_per_block;  /* 0 auto, 4 or 8 (streaming kernel: also 16)        */
     int32_t x_in_registers;   /* 0 auto, 1 keep x in VGPRs (one span, m = 1), 2 LDS */
-    int32_t kernel;           /* 0 auto, 1 x-stager kernel, 2 streaming kernel (m = 1) */
-    int32_t ring_depth;       /* streaming: rows in flight per wave, 0 auto, 1..4      */
+    int32_t kernel;           /* 0 auto, 1 x-stager kernel, 2 streaming kernel (m = 1),
+                                 3 f16 matrix-core kernel (m = 1), 4 int8 matrix-core
+                                 kernel (m = 1), 5 line-streamed int8 matrix-core
+                                 kernel (m = 1, k % 2048 == 0, w 128-byte aligned)   */
+    int32_t ring_depth;       /* kernels 2-5: loads in flight per wave, 0 auto;
+                                 streaming 1..4 rows; f16 matrix-core 1, 2 or 4
+                                 steps; int8 matrix-core 1..3 columns; line-streamed
+                                 3 or 9 lines                                        */
     int32_t rows_per_task;    /* streaming: rows per wave task, 0 auto, >= 1           */
+    int32_t cols_per_task;    /* matrix-core: superblock columns per task, 0 auto      */
+    int32_t tiles_per_task;   /* matrix-core: 16-row tiles per task, 0 auto, 1, 2, 4   */
+    int32_t cols_per_chunk;   /* matrix-core: superblock columns of x staged at once
+                                 (rounded down to whole tasks), 0 auto               */
 } q4k_launch;
 
 /* q4k_gemv with explicit launch options (NULL = automatic).  Options that do

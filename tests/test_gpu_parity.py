@@ -162,6 +162,164 @@ def test_streaming_kernel_shapes(oracle_mod, n, k):
         assert_within(y, y_ref, bound, "streaming n=%d k=%d %r" % (n, k, opts))
 
 
+# matrix-core kernel: options that keep the column grouping (cols_per_task)
+# are bit-identical; every option is within tolerance
+MFMA_VARIANTS = [
+    dict(kernel=3),
+    dict(kernel=3, cols_per_task=1),
+    dict(kernel=3, cols_per_task=1, tiles_per_task=2, ring_depth=4, waves_per_block=4),
+    dict(kernel=3, cols_per_task=3, tiles_per_task=4, ring_depth=1, rows_per_block=40),
+    dict(kernel=3, cols_per_task=5, tiles_per_task=1, ring_depth=4, cols_per_chunk=5),
+    dict(kernel=3, cols_per_task=5, tiles_per_task=4, ring_depth=2, cols_per_chunk=11,
+         rows_per_block=100, waves_per_block=4),
+    dict(kernel=3, cols_per_task=64, tiles_per_task=2, ring_depth=2, rows_per_block=16),
+    dict(kernel=4),
+    dict(kernel=4, cols_per_task=1),
+    dict(kernel=4, cols_per_task=1, tiles_per_task=2, ring_depth=2, waves_per_block=4),
+    dict(kernel=4, cols_per_task=3, tiles_per_task=4, ring_depth=1, rows_per_block=40),
+    dict(kernel=4, cols_per_task=5, tiles_per_task=1, ring_depth=2, cols_per_chunk=5),
+    dict(kernel=4, cols_per_task=5, tiles_per_task=4, ring_depth=2, cols_per_chunk=11,
+         rows_per_block=100, waves_per_block=4),
+    dict(kernel=4, cols_per_task=64, tiles_per_task=2, ring_depth=3, rows_per_block=16),
+]
+
+
+def _mfma_group(opts, S):
+    if "cols_per_task" not in opts:
+        return None
+    return (opts["kernel"], min(opts["cols_per_task"], S))
+
+
+@pytest.mark.parametrize("i", [0, 1, 2, 3])
+def test_mfma_kernel_variants(oracle_mod, i):
+    wl, w, x, y_ref, bound = workload(i, oracle_mod)
+    w_d = dev(w)
+    S = wl.k // 256
+    seen = {}
+    for opts in MFMA_VARIANTS:
+        _say("workload %d matrix-core %r" % (i, opts))
+        y = run_gemv(w_d, x, wl.n, wl.k, wl.m, **opts)
+        assert_within(y, y_ref, bound, "matrix-core %r" % opts)
+        key = _mfma_group(opts, S)
+        if key is not None:
+            if key in seen:
+                assert np.array_equal(y.view(np.uint32), seen[key].view(np.uint32)), opts
+            else:
+                seen[key] = y
+
+
+@pytest.mark.parametrize("n,k", [(1, 256), (5, 768), (17, 4096 + 2304), (130, 12544),
+                                 (3, 65536), (257, 1024)])
+def test_mfma_kernel_shapes(oracle_mod, n, k):
+    w, x = synth.make_inputs(n, k, 1, seed=n + 5 * k)
+    y_ref, bound = oracle_mod.gemv(w, x, n)
+    w_d = dev(w)
+    for opts in MFMA_VARIANTS:
+        _say("matrix-core n=%d k=%d %r" % (n, k, opts))
+        y = run_gemv(w_d, x, n, k, 1, **opts)
+        assert_within(y, y_ref, bound, "matrix-core n=%d k=%d %r" % (n, k, opts))
+
+
+# line-streamed kernel (k a multiple of 2048): the same arithmetic as the
+# int8 matrix-core kernel with the same column grouping, so bit-identical to it
+LINES_VARIANTS = [
+    dict(kernel=5),
+    dict(kernel=5, cols_per_task=8),
+    dict(kernel=5, waves_per_block=4, rows_per_block=48),
+    dict(kernel=5, waves_per_block=16, rows_per_block=320, cols_per_task=8),
+    dict(kernel=5, rows_per_block=40),
+    dict(kernel=5, waves_per_block=4, rows_per_block=16),
+    dict(kernel=5, ring_depth=9),
+    dict(kernel=5, ring_depth=9, cols_per_task=8, rows_per_block=16),
+    dict(kernel=5, ring_depth=9, waves_per_block=4, rows_per_block=80),
+]
+
+
+def _lines_check(w_d, w, x, n, k, y_ref, bound, what):
+    S = k // 256
+    for opts in LINES_VARIANTS:
+        _say("%s line-streamed %r" % (what, opts))
+        try:
+            y = run_gemv(w_d, x, n, k, 1, **opts)
+        except q4k.Q4KError as e:
+            # refused: a task's column group must divide the slabs of a row,
+            # and the whole staged x (960 bytes per superblock column) plus
+            # the line rings (4352 bytes per wave) must fit the 160 KiB LDS
+            nw = opts.get("waves_per_block", 8)
+            bad_group = "cols_per_task" in opts and (S // 8) % (opts["cols_per_task"] // 8) != 0
+            too_big = (S + 1) * 960 + nw * 4352 > 160 * 1024
+            assert e.rc == q4k.Q4K_ERR_UNSUPPORTED and (bad_group or too_big), opts
+            continue
+        assert_within(y, y_ref, bound, "%s line-streamed %r" % (what, opts))
+        cpt = opts.get("cols_per_task", 8)     # automatic grouping: one slab of 8 columns
+        y4 = run_gemv(w_d, x, n, k, 1, kernel=4, cols_per_task=cpt)
+        assert np.array_equal(y.view(np.uint32), y4.view(np.uint32)), opts
+
+
+@pytest.mark.parametrize("i", [1, 2, 3])
+def test_lines_kernel_workloads(oracle_mod, i):
+    wl, w, x, y_ref, bound = workload(i, oracle_mod)
+    _lines_check(dev(w), w, x, wl.n, wl.k, y_ref, bound, "workload %d" % i)
+
+
+@pytest.mark.parametrize("n,k", [(1, 2048), (17, 4096), (130, 14336), (3, 65536), (257, 2048),
+                                 (33, 18432)])
+def test_lines_kernel_shapes(oracle_mod, n, k):
+    w, x = synth.make_inputs(n, k, 1, seed=n + 11 * k)
+    y_ref, bound = oracle_mod.gemv(w, x, n)
+    _lines_check(dev(w), w, x, n, k, y_ref, bound, "n=%d k=%d" % (n, k))
+
+
+def test_lines_kernel_refusals():
+    """Shapes and pointers the line-streamed kernel cannot take are refused
+    without launching (k not a multiple of 2048, rows not 128-byte aligned)."""
+    n, k = 8, 2048
+    w, x = synth.make_inputs(n, k, 1, seed=5)
+    w_d = torch.zeros(w.size + 128, dtype=torch.uint8, device="cuda")
+    w_d[16:16 + w.size] = torch.from_numpy(w).cuda()
+    x_d = dev(x)
+    y_d = torch.zeros((1, n), dtype=torch.float32, device="cuda")
+    with pytest.raises(q4k.Q4KError) as e:
+        q4k.q4k_gemv_ex(w_d.data_ptr() + 16, x_d, y_d, n, k, 1, kernel=5)
+    assert e.value.rc == q4k.Q4K_ERR_UNSUPPORTED
+    w2, x2 = synth.make_inputs(n, 1024, 1, seed=6)
+    with pytest.raises(q4k.Q4KError) as e:
+        q4k.q4k_gemv_ex(dev(w2), dev(x2), y_d, n, 1024, 1, kernel=5)
+    assert e.value.rc == q4k.Q4K_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(y_d).item() == 0
+
+
+def _x_cases(rng, k):
+    """x with wide dynamic range: outliers, tiny and zero columns, mixed
+    magnitudes across 256-element columns, subnormal f32 values."""
+    base = rng.standard_normal(k)
+    out = base.copy()
+    out[::97] *= 1e4                       # outliers
+    out[256:512] = 0.0                     # an all-zero column
+    if k >= 1024:
+        out[512:768] *= 1e-30              # tiny column
+        out[768:1024] *= 1e25              # huge column
+    out[5] = 1e-40                         # f32 subnormal
+    out[7] = -3e-39
+    return np.stack([base, out]).astype(np.float32)
+
+
+@pytest.mark.parametrize("n,k", [(64, 2048), (33, 4096)])
+def test_mfma_kernel_x_dynamic_range(oracle_mod, n, k):
+    rng = np.random.default_rng(n * k)
+    w, _ = synth.make_inputs(n, k, 1, seed=n + k)
+    xs = _x_cases(rng, k)
+    w_d = dev(w)
+    for b in range(xs.shape[0]):
+        x = xs[b:b + 1]
+        y_ref, bound = oracle_mod.gemv(w, x, n)
+        for opts in MFMA_VARIANTS[:3] + MFMA_VARIANTS[7:10] + LINES_VARIANTS[:2]:
+            _say("matrix-core dynamic range n=%d k=%d case %d %r" % (n, k, b, opts))
+            y = run_gemv(w_d, x, n, k, 1, **opts)
+            assert_within(y, y_ref, bound, "matrix-core x case %d %r" % (b, opts))
+
+
 @pytest.mark.parametrize("i", [0, 1, 2])
 def test_variants_bit_identical(oracle_mod, i):
     wl, w, x, y_ref, bound = workload(i, oracle_mod)
