@@ -142,10 +142,11 @@ int make_plan_mfma(int64_t n, int64_t k, int kernel, const q4k_launch* o, GemvPl
     return Q4K_OK;
 }
 
-// Plan of the line-streamed kernel (m = 1, k a multiple of 2048, weights
-// 128-byte aligned).  A task is a 16-row tile times a group of slabs of
-// eight superblock columns; x is staged whole.
-int make_plan_lines(int64_t n, int64_t k, const q4k_launch* o, GemvPlan* p)
+// Plan of the line-streamed kernel (k a multiple of 2048, weights 128-byte
+// aligned, m <= 8).  A task is a 16-row tile times a group of slabs of
+// eight superblock columns; x (every vector) is staged whole.
+int make_plan_lines(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t lds_max,
+                    GemvPlan* p)
 {
     const int S = (int)(k / q4k::kQK);
     if (S % 8 != 0) {
@@ -166,35 +167,42 @@ int make_plan_lines(int64_t n, int64_t k, const q4k_launch* o, GemvPlan* p)
     if (nw == 16 && ring == 9) {
         return Q4K_ERR_UNSUPPORTED;    // 1024-lane workgroups cap a lane at 128 VGPRs
     }
+    if (m > 1 && (nw != 8 || ring != 3)) {
+        return Q4K_ERR_UNSUPPORTED;    // several vectors: eight waves, three lines in flight
+    }
     const int64_t ntiles = (n + 15) / 16;
-    int64_t spt;
+    int64_t spt = 1;
     if (o && o->cols_per_task) {
         if (o->cols_per_task % 8 != 0 || nslabs % (o->cols_per_task / 8) != 0) {
             return Q4K_ERR_UNSUPPORTED;
         }
         spt = o->cols_per_task / 8;
-    } else {
-        spt = 1;          // one slab per task: measured best on MI355X
     }
-    const int64_t ncg = nslabs / spt;
     int64_t rpb;
     if (o && o->rows_per_block > 0) {
         rpb = o->rows_per_block;
     } else {
-        // about one workgroup per CU of a 256-CU part: each stages x once
-        const int64_t tiles_pb = (ntiles + 128) / 256;
-        rpb = 16 * (tiles_pb < 1 ? 1 : tiles_pb);
+        // at most about one workgroup per CU of a 256-CU part: each stages
+        // all of x, which costs as much as decoding a few tiles
+        rpb = 16 * ((ntiles + 255) / 256);
     }
-    if (rpb > kInt32Max / ncg) {
+    const size_t lds_x = q4k::lines_lds_bytes(S, (int)m, nw);
+    if (!(o && o->cols_per_task)) {
+        // one slab per task (measured best on MI355X) unless its per-group
+        // row sums do not fit the LDS; then whole rows per task
+        spt = lds_x + (size_t)nslabs * rpb * 4 * m <= lds_max || nslabs == 1 ? 1 : nslabs;
+    }
+    const int64_t ncg = nslabs / spt;
+    if (rpb > kInt32Max / (ncg * m)) {
         return Q4K_ERR_SHAPE;
     }
     const int64_t grid = (n + rpb - 1) / rpb;
-    const size_t lds = q4k::lines_lds_bytes(S, nw) + (ncg > 1 ? (size_t)ncg * rpb * 4 : 0);
+    const size_t lds = lds_x + (ncg > 1 ? (size_t)ncg * rpb * 4 * m : 0);
 
     p->n = (int)n;
     p->k = (int)k;
     p->S = S;
-    p->m = 1;
+    p->m = (int)m;
     p->nspans = (S + q4k::kSpanSB - 1) / q4k::kSpanSB;
     p->spans_per_chunk = 0;
     p->nchunks = 1;
@@ -216,12 +224,14 @@ int make_plan_lines(int64_t n, int64_t k, const q4k_launch* o, GemvPlan* p)
 // Resolve launch options into a plan.  Pure host arithmetic, no HIP calls.
 // Plans needing more LDS than lds_max are returned as they are; the caller
 // refuses them.
-// The automatic kernel.  m > 1: the x-stager kernel.  m = 1: the
-// line-streamed kernel where it applies (k a multiple of 2048, 128-byte
-// aligned weights, its LDS fits) and the weights are at least 16 MiB, else
-// the streaming kernel, whose shorter start wins on smaller matrices
-// (measured on MI355X).  Options other than `kernel` keep the earlier
-// families: streaming for m = 1, x-stager otherwise.
+// The automatic kernel (choices measured on MI355X).  The line-streamed
+// kernel applies when k is a multiple of 2048, the weights are 128-byte
+// aligned and its LDS (x of every vector, the line rings) fits.  m > 1: the
+// line-streamed kernel where it applies, else the x-stager kernel.  m = 1:
+// the line-streamed kernel where it applies and the weights take at least
+// 16 MiB, else the streaming kernel, whose shorter start wins on smaller
+// matrices.  Options other than `kernel` keep the earlier families:
+// streaming for m = 1, x-stager otherwise.
 bool any_option(const q4k_launch* o)
 {
     return o && (o->variant || o->spans_per_chunk || o->rows_per_block || o->rows_per_wave ||
@@ -232,16 +242,21 @@ bool any_option(const q4k_launch* o)
 int auto_kernel(int64_t n, int64_t k, int64_t m, const q4k_launch* o, bool w_aligned128,
                 size_t lds_max)
 {
+    GemvPlan lp;
     if (m != 1) {
+        // several vectors: the line-streamed kernel whenever it applies
+        if (!any_option(o) && w_aligned128 &&
+            make_plan_lines(n, k, m, nullptr, lds_max, &lp) == Q4K_OK && lp.lds_bytes <= lds_max) {
+            return 5;
+        }
         return 1;
     }
     if (any_option(o)) {
         return 2;
     }
     const int64_t bytes = n * (k / q4k::kQK) * q4k::kBlockBytes;
-    GemvPlan lp;
     if (w_aligned128 && bytes >= ((int64_t)16 << 20) &&
-        make_plan_lines(n, k, nullptr, &lp) == Q4K_OK && lp.lds_bytes <= lds_max) {
+        make_plan_lines(n, k, 1, nullptr, lds_max, &lp) == Q4K_OK && lp.lds_bytes <= lds_max) {
         return 5;
     }
     return 2;
@@ -273,11 +288,11 @@ int make_plan(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t lds_m
     const int nchunks = (nspans + spc - 1) / spc;
 
     const int kernel = (o && o->kernel) ? o->kernel : auto_kernel(n, k, m, o, w_aligned128, lds_max);
-    if (kernel < 1 || kernel > 5 || (kernel >= 2 && m != 1)) {
+    if (kernel < 1 || kernel > 5 || (kernel >= 2 && kernel <= 4 && m != 1)) {
         return Q4K_ERR_UNSUPPORTED;
     }
     if (kernel == 5) {
-        return make_plan_lines(n, k, o, p);
+        return make_plan_lines(n, k, m, o, lds_max, p);
     }
     if (kernel >= 3) {
         return make_plan_mfma(n, k, kernel, o, p);

@@ -42,7 +42,7 @@ hipError_t launch_gemv_mfma(const GemvPlan& p, const void* w, const float* x, fl
                             hipStream_t stream);
 size_t mfma_col_bytes(int kernel);
 size_t mfma_lds_bytes(int kernel, int cols_chunk);
-size_t lines_lds_bytes(int S, int waves);
+size_t lines_lds_bytes(int S, int m, int waves);
 hipError_t launch_dequant(const void* w, float* out, int64_t nsb, hipStream_t stream);
 hipError_t launch_read(const void* buf, size_t n16, float* out, hipStream_t stream);
 

@@ -544,23 +544,47 @@ __device__ __forceinline__ float digits_value(const i32x4_t& D)
     return __builtin_fmaf((float)D[2], 65536.0f, (float)(D[1] * 256 + D[0]));
 }
 
-// One (tile, column) step: the lane's partial of its row.
+// The weight side of one (tile, column) step: unpacked codes and the
+// lane's chunk scales, shared by every vector.
+struct StepW {
+    i32x4_t lo0, lo1, hi0, hi1;
+    ChunkScalesD s;
+};
+
+__device__ __forceinline__ StepW step_weights(const TileI8& cur, uint32_t sh, uint32_t sel)
+{
+    StepW t;
+    t.lo0 = lo_codes(cur.q0);
+    t.lo1 = lo_codes(cur.q1);
+    t.hi0 = hi_codes(cur.q0);
+    t.hi1 = hi_codes(cur.q1);
+    t.s = decode_chunk(cur.h, sh, sel);
+    return t;
+}
+
+// One vector's part of a step: four MFMAs and the scaling; the lane's
+// partial of its row.
+__device__ __forceinline__ float step_vector(const StepW& t, const ColI8& col)
+{
+    const i32x4_t zero = {0, 0, 0, 0};
+    i32x4_t Dl = __builtin_amdgcn_mfma_i32_16x16x64_i8(col.a[0], t.lo0, zero, 0, 0, 0);
+    Dl = __builtin_amdgcn_mfma_i32_16x16x64_i8(col.a[1], t.lo1, Dl, 0, 0, 0);
+    i32x4_t Dh = __builtin_amdgcn_mfma_i32_16x16x64_i8(col.a[2], t.hi0, zero, 0, 0, 0);
+    Dh = __builtin_amdgcn_mfma_i32_16x16x64_i8(col.a[3], t.hi1, Dh, 0, 0, 0);
+    const float u_lo = col.c0 * digits_value(Dl);
+    const float u_hi = __builtin_fmaf(col.c1, digits_value(Dh), col.c2);
+    float t1 = t.s.sc_lo * u_lo;
+    t1 = __builtin_fmaf(t.s.sc_hi, u_hi, t1);
+    float t2 = t.s.m_lo * col.xlo;
+    t2 = __builtin_fmaf(t.s.m_hi, col.xhi, t2);
+    return __builtin_fmaf(-t.s.dmin, t2, t.s.d * t1);
+}
+
+// One (tile, column) step for one vector.
 __device__ __forceinline__ float i8_step(const TileI8& cur, const ColI8& col, uint32_t sh,
                                          uint32_t sel)
 {
-    const i32x4_t zero = {0, 0, 0, 0};
-    i32x4_t Dl = __builtin_amdgcn_mfma_i32_16x16x64_i8(col.a[0], lo_codes(cur.q0), zero, 0, 0, 0);
-    Dl = __builtin_amdgcn_mfma_i32_16x16x64_i8(col.a[1], lo_codes(cur.q1), Dl, 0, 0, 0);
-    i32x4_t Dh = __builtin_amdgcn_mfma_i32_16x16x64_i8(col.a[2], hi_codes(cur.q0), zero, 0, 0, 0);
-    Dh = __builtin_amdgcn_mfma_i32_16x16x64_i8(col.a[3], hi_codes(cur.q1), Dh, 0, 0, 0);
-    const ChunkScalesD s = decode_chunk(cur.h, sh, sel);
-    const float u_lo = col.c0 * digits_value(Dl);
-    const float u_hi = __builtin_fmaf(col.c1, digits_value(Dh), col.c2);
-    float t1 = s.sc_lo * u_lo;
-    t1 = __builtin_fmaf(s.sc_hi, u_hi, t1);
-    float t2 = s.m_lo * col.xlo;
-    t2 = __builtin_fmaf(s.m_hi, col.xhi, t2);
-    return __builtin_fmaf(-s.dmin, t2, s.d * t1);
+    return step_vector(step_weights(cur, sh, sel), col);
 }
 
 // Tasks: (column group, TPT tiles of 16 rows).  A ring holds the tiles of
@@ -724,7 +748,7 @@ __device__ __forceinline__ uint4 load_line_nt(const uint8_t* p)
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-template <int NW, int P, int XC>
+template <int NW, int P, int XC, int M>
 __global__ void __launch_bounds__(NW * 64)
 gemv_i8_lines_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
                      float* __restrict__ y, int n, int S, int rows_per_block, int slabs_per_task)
@@ -753,9 +777,13 @@ gemv_i8_lines_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
     const int my_slabs = my_tasks * slabs_per_task;
     const size_t row_bytes = (size_t)S * 144;
 
-    // LDS: staged x (S columns and a spare one), the line rings, row sums
-    unsigned char* ring = smem + (size_t)(S + 1) * kI8ColBytes + wave * kRingWave;
-    float* ypart = reinterpret_cast<float*>(smem + (size_t)(S + 1) * kI8ColBytes + NW * kRingWave);
+    // LDS: staged x (S columns of M vectors, column-major, and a spare
+    // slot), the line rings, row sums
+    const int npairs = S * M;
+    const size_t xbytes = (size_t)(npairs + 1) * kI8ColBytes;
+    unsigned char* ring = smem + xbytes + wave * kRingWave;
+    float* ypart = reinterpret_cast<float*>(smem + xbytes + NW * kRingWave);
+    const int k = S * 256;
 
     // slab sig of this wave -> (tile, absolute slab); clamped into the
     // wave's slabs (and into the block's tasks for a wave without any), so
@@ -768,17 +796,21 @@ gemv_i8_lines_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
     };
     // the two global addresses (rows lrow and 8 + lrow) of line l of slab
     // sig; past the wave's last slab the prefetch reads the first 128 bytes
-    // of x instead (cached, so the surplus loads cost no HBM traffic)
-    const uint8_t* spare = reinterpret_cast<const uint8_t*>(x) + 16 * lunit;
+    // of x instead (cached, so the surplus loads cost no HBM traffic).  The
+    // choice is a mask on the byte offset from w: a select of two pointers
+    // makes the compiler branch around the address arithmetic, which costs
+    // registers across the unrolled slab.
+    const uint64_t dx = (uint64_t)(reinterpret_cast<const uint8_t*>(x) - w);
     auto line_ptrs = [&](int sig, int l, const uint8_t** p) {
         int tile, slab;
         slab_of(sig, tile, slab);
-        const size_t off = (size_t)(9 * slab + l) * 128 + 16 * lunit;
-        const bool past = sig >= my_slabs;
+        const uint64_t mask = sig >= my_slabs ? ~0ull : 0ull;     // wave-uniform
+        const uint64_t off = (uint64_t)(9 * slab + l) * 128;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int r = min(tile * 16 + 8 * h + lrow, rows_here - 1);
-            p[h] = past ? spare : w + (size_t)(row0 + r) * row_bytes + off;
+            const uint64_t full = (uint64_t)(row0 + r) * row_bytes + off;
+            p[h] = w + (((full & ~mask) | (dx & mask)) + 16 * lunit);
         }
     };
 
@@ -786,11 +818,13 @@ gemv_i8_lines_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
     // x loads first, then the first lines of weights, then the conversion:
     // waiting for x (the counter of loads returns in order) then leaves the
     // weight lines in flight
-    // XC columns of x per wave: all of them when S <= XC * NW
+    // XC (column, vector) pairs of x per wave: all of them when
+    // S * M <= XC * NW; pair p is column p / M of vector p % M
     float4 xv[XC];
 #pragma unroll
     for (int i = 0; i < XC; ++i) {
-        xv[i] = load_x_col(x, min(wave + i * NW, S - 1), lane);
+        const int pr = min(wave + i * NW, npairs - 1);
+        xv[i] = load_x_col(x + (size_t)(pr % M) * k, pr / M, lane);
     }
     uint4 lines[P][2];
 #pragma unroll
@@ -805,14 +839,19 @@ gemv_i8_lines_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
     // the last go to a spare slot
 #pragma unroll
     for (int i = 0; i < XC; ++i) {
-        convert_col_i8(xv[i], smem + (size_t)min(wave + i * NW, S) * kI8ColBytes, lane);
+        convert_col_i8(xv[i], smem + (size_t)min(wave + i * NW, npairs) * kI8ColBytes, lane);
     }
-    if (S > XC * NW) {
-        stage_x_i8<4>(x, XC * NW, S - XC * NW, smem + (size_t)XC * NW * kI8ColBytes, lane, wave, NW);
+    for (int pr = XC * NW + wave; pr < npairs; pr += NW) {
+        convert_col_i8(load_x_col(x + (size_t)(pr % M) * k, pr / M, lane),
+                       smem + (size_t)pr * kI8ColBytes, lane);
     }
     __syncthreads();
 
-    float acc = 0.f;
+    float acc[M];
+#pragma unroll
+    for (int b = 0; b < M; ++b) {
+        acc[b] = 0.f;
+    }
     for (int sig = 0; sig < my_slabs; ++sig) {
         int tile, slab;
         slab_of(sig, tile, slab);
@@ -841,58 +880,67 @@ gemv_i8_lines_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
             t.h = *reinterpret_cast<const uint4*>(rr + (b0 & 255u));
             t.q0 = *reinterpret_cast<const uint4*>(rr + ((b0 + 16u + 32u * (uint32_t)g) & 255u));
             t.q1 = *reinterpret_cast<const uint4*>(rr + ((b0 + 32u + 32u * (uint32_t)g) & 255u));
-            const ColI8 col = read_col_i8(smem + (size_t)c * kI8ColBytes, a_off, g);
-            acc += i8_step(t, col, sh, sel);
+            const StepW sw = step_weights(t, sh, sel);
+#pragma unroll
+            for (int b = 0; b < M; ++b) {
+                const ColI8 col = read_col_i8(smem + (size_t)(c * M + b) * kI8ColBytes, a_off, g);
+                acc[b] += step_vector(sw, col);
+            }
         }
         if (sig % slabs_per_task == slabs_per_task - 1) {
-            float v = acc;
-            v += __shfl_xor(v, 16, 64);
-            v += __shfl_xor(v, 32, 64);
             const int task = wave + (sig / slabs_per_task) * NW;
             const int r = (task / ncg) * 16 + j;
-            if (g == 0 && r < rows_here) {
-                if (ncg == 1) {
-                    y[row0 + r] = v;
-                } else {
-                    ypart[(task % ncg) * rows_per_block + r] = v;
+#pragma unroll
+            for (int b = 0; b < M; ++b) {
+                float v = acc[b];
+                v += __shfl_xor(v, 16, 64);
+                v += __shfl_xor(v, 32, 64);
+                if (g == 0 && r < rows_here) {
+                    if (ncg == 1) {
+                        y[(size_t)b * n + row0 + r] = v;
+                    } else {
+                        ypart[(b * ncg + task % ncg) * rows_per_block + r] = v;
+                    }
                 }
+                acc[b] = 0.f;
             }
-            acc = 0.f;
         }
     }
     if (ncg > 1) {
         __syncthreads();
-        for (int r = tid; r < rows_here; r += NW * 64) {
+        for (int i = tid; i < rows_here * M; i += NW * 64) {
+            const int b = i / rows_here;
+            const int r = i - b * rows_here;
             float a = 0.f;
             for (int cg = 0; cg < ncg; ++cg) {
-                a += ypart[cg * rows_per_block + r];
+                a += ypart[(b * ncg + cg) * rows_per_block + r];
             }
-            y[row0 + r] = a;
+            y[(size_t)b * n + row0 + r] = a;
         }
     }
 }
 
-template <int NW, int P, int XC>
+template <int NW, int P, int XC, int M>
 static hipError_t launch_lines_x(const GemvPlan& p, const uint8_t* w, const float* x, float* y,
                                  hipStream_t stream)
 {
-    hipLaunchKernelGGL((gemv_i8_lines_kernel<NW, P, XC>), dim3(p.grid), dim3(NW * 64),
+    hipLaunchKernelGGL((gemv_i8_lines_kernel<NW, P, XC, M>), dim3(p.grid), dim3(NW * 64),
                        p.lds_bytes, stream, w, x, y, p.n, p.S, p.rows_per_block,
                        p.cols_per_task / 8);
     return hipGetLastError();
 }
 
-// x columns each wave converts before the first barrier: the power of two
-// covering S / NW, at most 8 (the rest are staged in a loop)
+// (column, vector) pairs of x each wave converts before the first barrier:
+// the power of two covering S * m / NW, at most 8 (the rest follow in a loop)
 template <int NW, int P>
 static hipError_t launch_lines_p(const GemvPlan& p, const uint8_t* w, const float* x, float* y,
                                  hipStream_t stream)
 {
     const int per = (p.S + NW - 1) / NW;
-    if (per <= 1) return launch_lines_x<NW, P, 1>(p, w, x, y, stream);
-    if (per <= 2) return launch_lines_x<NW, P, 2>(p, w, x, y, stream);
-    if (per <= 4) return launch_lines_x<NW, P, 4>(p, w, x, y, stream);
-    return launch_lines_x<NW, P, 8>(p, w, x, y, stream);
+    if (per <= 1) return launch_lines_x<NW, P, 1, 1>(p, w, x, y, stream);
+    if (per <= 2) return launch_lines_x<NW, P, 2, 1>(p, w, x, y, stream);
+    if (per <= 4) return launch_lines_x<NW, P, 4, 1>(p, w, x, y, stream);
+    return launch_lines_x<NW, P, 8, 1>(p, w, x, y, stream);
 }
 
 template <int NW>
@@ -901,6 +949,16 @@ static hipError_t launch_lines(const GemvPlan& p, const uint8_t* w, const float*
 {
     if (p.ring_depth == 9) return launch_lines_p<NW, 9>(p, w, x, y, stream);
     return launch_lines_p<NW, 3>(p, w, x, y, stream);
+}
+
+// several vectors: eight waves, three lines in flight
+template <int M>
+static hipError_t launch_lines_m(const GemvPlan& p, const uint8_t* w, const float* x, float* y,
+                                 hipStream_t stream)
+{
+    const int per = (p.S * M + 7) / 8;
+    if (per <= 2) return launch_lines_x<8, 3, 2, M>(p, w, x, y, stream);
+    return launch_lines_x<8, 3, 8, M>(p, w, x, y, stream);
 }
 
 template <int NW, int TPT, int UC>
@@ -964,6 +1022,16 @@ hipError_t launch_gemv_mfma(const GemvPlan& p, const void* w, const float* x, fl
 {
     const uint8_t* wb = static_cast<const uint8_t*>(w);
     if (p.kernel == 5) {
+        switch (p.m) {
+        case 1: break;
+        case 2: return launch_lines_m<2>(p, wb, x, y, stream);
+        case 3: return launch_lines_m<3>(p, wb, x, y, stream);
+        case 4: return launch_lines_m<4>(p, wb, x, y, stream);
+        case 5: return launch_lines_m<5>(p, wb, x, y, stream);
+        case 6: return launch_lines_m<6>(p, wb, x, y, stream);
+        case 7: return launch_lines_m<7>(p, wb, x, y, stream);
+        default: return launch_lines_m<8>(p, wb, x, y, stream);
+        }
         if (p.waves_per_block == 8) return launch_lines<8>(p, wb, x, y, stream);
         if (p.waves_per_block == 16) return launch_lines_p<16, 3>(p, wb, x, y, stream);
         return launch_lines<4>(p, wb, x, y, stream);
@@ -981,9 +1049,9 @@ size_t mfma_col_bytes(int kernel)
     return kernel == 4 ? (size_t)kI8ColBytes : (size_t)kMfmaColBytes;
 }
 
-size_t lines_lds_bytes(int S, int waves)
+size_t lines_lds_bytes(int S, int m, int waves)
 {
-    return (size_t)(S + 1) * kI8ColBytes + (size_t)waves * kRingWave;
+    return (size_t)(S * m + 1) * kI8ColBytes + (size_t)waves * kRingWave;
 }
 
 size_t mfma_lds_bytes(int kernel, int cols_chunk)

@@ -101,11 +101,13 @@ const char* q4k_status_string(int rc);
 
 /* ---------------------------------------------------------------------
  * Launch options for q4k_gemv_ex (tests and tuning).  q4k_gemv is
- * q4k_gemv_ex with every field 0 (automatic): for m = 1 the line-streamed
- * matrix-core kernel when k % 2048 == 0, w is 128-byte aligned and the
- * weights take at least 16 MiB, else the streaming kernel; for m > 1 the
- * x-stager kernel.  With kernel = 0 and another field set, m = 1 uses the
- * streaming kernel.
+ * q4k_gemv_ex with every field 0 (automatic).  The line-streamed
+ * matrix-core kernel applies when k % 2048 == 0, w is 128-byte aligned and
+ * the staged x of all m vectors (960 bytes per 256 elements per vector) plus
+ * its line rings fit the LDS.  m = 1: that kernel when it applies and the
+ * weights take at least 16 MiB, else the streaming kernel.  m > 1: that
+ * kernel when it applies, else the x-stager kernel.  With kernel = 0 and
+ * another field set, m = 1 uses the streaming kernel and m > 1 the x-stager.
  *
  * x is staged in LDS in spans of 4096 elements per vector.  The single-stage
  * variant holds all of x at once; the K-chunked variant stages
@@ -125,7 +127,8 @@ typedef struct q4k_launch {
     int32_t kernel;           /* 0 auto, 1 x-stager kernel, 2 streaming kernel (m = 1),
                                  3 f16 matrix-core kernel (m = 1), 4 int8 matrix-core
                                  kernel (m = 1), 5 line-streamed int8 matrix-core
-                                 kernel (m = 1, k % 2048 == 0, w 128-byte aligned)   */
+                                 kernel (m <= 8, k % 2048 == 0, w 128-byte aligned;
+                                 m > 1: 8 waves and 3 lines in flight)               */
     int32_t ring_depth;       /* kernels 2-5: loads in flight per wave, 0 auto;
                                  streaming 1..4 rows; f16 matrix-core 1, 2 or 4
                                  steps; int8 matrix-core 1..3 columns; line-streamed

@@ -270,6 +270,34 @@ def test_lines_kernel_shapes(oracle_mod, n, k):
     _lines_check(dev(w), w, x, n, k, y_ref, bound, "n=%d k=%d" % (n, k))
 
 
+@pytest.mark.parametrize("n,k,m", [(300, 4096, 2), (17, 2048, 3), (130, 4096, 8), (64, 4096, 5),
+                                   (33, 2048, 8), (40, 16384, 2)])
+def test_lines_kernel_batched(oracle_mod, n, k, m):
+    """m vectors in one launch: within tolerance, and bit-identical to m
+    single-vector launches of the same kernel (each vector's sums run in
+    the same order)."""
+    w, x = synth.make_inputs(n, k, m, seed=n * 31 + k + m)
+    y_ref, bound = oracle_mod.gemv(w, x, n)
+    w_d = dev(w)
+    _say("line-streamed batched n=%d k=%d m=%d" % (n, k, m))
+    y = run_gemv(w_d, x, n, k, m, kernel=5)
+    assert_within(y, y_ref, bound, "line-streamed m=%d" % m)
+    for b in range(m):
+        y1 = run_gemv(w_d, x[b:b + 1], n, k, 1, kernel=5)
+        assert np.array_equal(y1[0].view(np.uint32), y[b].view(np.uint32)), b
+
+
+def test_lines_kernel_batched_workload(oracle_mod):
+    wl, w, x, y_ref, bound = workload(4, oracle_mod)
+    w_d = dev(w)
+    _say("line-streamed batched workload 4")
+    y = run_gemv(w_d, x, wl.n, wl.k, wl.m, kernel=5)
+    assert_within(y, y_ref, bound, "line-streamed workload 4")
+    for b in range(wl.m):
+        y1 = run_gemv(w_d, x[b:b + 1], wl.n, wl.k, 1, kernel=5)
+        assert np.array_equal(y1[0].view(np.uint32), y[b].view(np.uint32)), b
+
+
 def test_lines_kernel_refusals():
     """Shapes and pointers the line-streamed kernel cannot take are refused
     without launching (k not a multiple of 2048, rows not 128-byte aligned)."""
@@ -286,6 +314,14 @@ def test_lines_kernel_refusals():
     with pytest.raises(q4k.Q4KError) as e:
         q4k.q4k_gemv_ex(dev(w2), dev(x2), y_d, n, 1024, 1, kernel=5)
     assert e.value.rc == q4k.Q4K_ERR_UNSUPPORTED
+    # staged x of every vector must fit the LDS: 32 columns x 5 vectors do not
+    w3, x3 = synth.make_inputs(n, 8192, 5, seed=7)
+    y3 = torch.zeros((5, n), dtype=torch.float32, device="cuda")
+    with pytest.raises(q4k.Q4KError) as e:
+        q4k.q4k_gemv_ex(dev(w3), dev(x3), y3, n, 8192, 5, kernel=5)
+    assert e.value.rc == q4k.Q4K_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(y3).item() == 0
     torch.cuda.synchronize()
     assert torch.count_nonzero(y_d).item() == 0
 
@@ -359,12 +395,18 @@ def test_batched_equals_separate_calls(oracle_mod, m):
 
 
 def test_batched_workload_against_separate(oracle_mod):
+    """The batched workload: the automatic kernel (line-streamed) and the
+    x-stager kernel, each bit-identical to m single-vector launches of
+    itself."""
     wl, w, x, y_ref, bound = workload(4, oracle_mod)
     w_d = dev(w)
-    yb = run_gemv(w_d, x, wl.n, wl.k, wl.m)
-    for b in range(wl.m):
-        y1 = run_gemv(w_d, x[b:b + 1], wl.n, wl.k, 1, kernel=1)
-        assert np.array_equal(y1[0].view(np.uint32), yb[b].view(np.uint32)), b
+    for opts, single in ((dict(), dict(kernel=5)), (dict(kernel=1), dict(kernel=1))):
+        _say("batched workload 4 %r" % opts)
+        yb = run_gemv(w_d, x, wl.n, wl.k, wl.m, **opts)
+        assert_within(yb, y_ref, bound, "batched workload %r" % opts)
+        for b in range(wl.m):
+            y1 = run_gemv(w_d, x[b:b + 1], wl.n, wl.k, 1, **single)
+            assert np.array_equal(y1[0].view(np.uint32), yb[b].view(np.uint32)), (opts, b)
 
 
 EDGE_SHAPES = [
