@@ -188,9 +188,12 @@ int make_plan_lines(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t
     }
     const size_t lds_x = q4k::lines_lds_bytes(S, (int)m, nw);
     if (!(o && o->cols_per_task)) {
-        // one slab per task (measured best on MI355X) unless its per-group
-        // row sums do not fit the LDS; then whole rows per task
-        spt = lds_x + (size_t)nslabs * rpb * 4 * m <= lds_max || nslabs == 1 ? 1 : nslabs;
+        // whole rows per task when there are at least four tiles per CU of a
+        // 256-CU part (no row sums to combine), else one slab per task for
+        // more parallel tasks; whole rows too when the per-slab row sums do
+        // not fit the LDS (choices measured on MI355X)
+        const bool fits = lds_x + (size_t)nslabs * rpb * 4 * m <= lds_max;
+        spt = (ntiles >= 1024 || !fits) ? nslabs : 1;
     }
     const int64_t ncg = nslabs / spt;
     if (rpb > kInt32Max / (ncg * m)) {

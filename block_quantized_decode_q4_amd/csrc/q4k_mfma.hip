@@ -463,6 +463,90 @@ __device__ __forceinline__ void convert_col_i8(const float4& v, unsigned char* c
     }
 }
 
+// Convert four (column, vector) pairs at once, one per 16-lane group: lane
+// l takes elements 16 (l % 16) .. 16 (l % 16) + 15 of its pair, half of a
+// sub-block, so each lane writes three whole 16-byte digit slots and the
+// per-lane costs (largest |x|, scale, sums) are shared by 16 elements.
+// `col` is the LDS slot of the lane's pair.  Produces exactly the bytes and
+// constants of convert_col_i8.
+__device__ __forceinline__ void convert4_i8(const float4 (&v)[4], unsigned char* col, int lane)
+{
+    const int le = lane & 15;
+    const int s = le >> 1;                    // sub-block
+    const int half = le & 1;                  // its elements 0-15 or 16-31
+    const int g = s >> 1;
+    const int mu = 2 * (s & 1) + half;
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        m = fmaxf(m, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
+    }
+    m = fmaxf(m, __builtin_bit_cast(float, dpp_i<0xB1>(__builtin_bit_cast(int, m))));  // lane l ^ 1
+    int sigma = 0;
+    if (m > 0.f) {
+        sigma = 22 - __builtin_amdgcn_frexp_expf(m);
+        sigma = sigma < -126 ? -126 : sigma > 126 ? 126 : sigma;
+    }
+    const float scale = __builtin_bit_cast(float, (uint32_t)(sigma + 127) << 23);
+    uint32_t usum = 0;
+    uint4 dig[3];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float vals[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+        uint32_t u[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            u[t] = __builtin_bit_cast(uint32_t, __builtin_fmaf(vals[t], scale, 12582912.0f)) -
+                   0x4ABF7F80u;
+            usum += u[t];
+        }
+        const uint32_t lo01 = __builtin_amdgcn_perm(u[1], u[0], 0x05010400u);
+        const uint32_t lo23 = __builtin_amdgcn_perm(u[3], u[2], 0x05010400u);
+        const uint32_t hi01 = __builtin_amdgcn_perm(u[1], u[0], 0x07030602u);
+        const uint32_t hi23 = __builtin_amdgcn_perm(u[3], u[2], 0x07030602u);
+        const uint32_t d0 = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u) ^ 0x80808080u;
+        const uint32_t d1 = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u) ^ 0x80808080u;
+        const uint32_t d2 = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u) ^ 0x80808080u;
+        (&dig[0].x)[i] = d0;
+        (&dig[1].x)[i] = d1;
+        (&dig[2].x)[i] = d2;
+    }
+    unsigned char* slot = col + mu * kI8MuBytes + g * 48;
+    *reinterpret_cast<uint4*>(slot) = dig[0];
+    *reinterpret_cast<uint4*>(slot + 16) = dig[1];
+    *reinterpret_cast<uint4*>(slot + 32) = dig[2];
+    if (le < 4) {
+        *reinterpret_cast<uint4*>(col + le * kI8MuBytes + kI8ZeroSlot) = make_uint4(0, 0, 0, 0);
+    }
+    const uint32_t us2 = usum + (uint32_t)dpp_i<0xB1>((int)usum);
+    const int XI = (int)us2 - 32 * 0x808080;
+    if (half == 0) {
+        float* c = reinterpret_cast<float*>(col + kI8ColA + g * 32);
+        const float inv = __builtin_bit_cast(float, (uint32_t)(127 - sigma) << 23);
+        const float xq = inv * (float)XI;
+        if ((s & 1) == 0) {
+            c[0] = inv;
+            c[3] = xq;
+        } else {
+            c[1] = inv * 0.0625f;
+            c[2] = 8.0f * xq;
+            c[4] = xq;
+        }
+    }
+}
+
+// The 16 x elements lane l converts in convert4_i8, of pair p (column p / m
+// of vector p % m).
+__device__ __forceinline__ void load_x_quarter(const float* __restrict__ x, int k, int m, int p,
+                                               int lane, float4 (&v)[4])
+{
+    const float* src = x + (size_t)(p % m) * k + (size_t)(p / m) * 256 + 16 * (lane & 15);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[i] = reinterpret_cast<const float4*>(src)[i];
+    }
+}
+
 __device__ __forceinline__ float4 load_x_col(const float* __restrict__ x, int col, int lane)
 {
     return *reinterpret_cast<const float4*>(x + (size_t)col * 256 + 4 * lane);
@@ -818,13 +902,14 @@ gemv_i8_lines_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
     // x loads first, then the first lines of weights, then the conversion:
     // waiting for x (the counter of loads returns in order) then leaves the
     // weight lines in flight
-    // XC (column, vector) pairs of x per wave: all of them when
-    // S * M <= XC * NW; pair p is column p / M of vector p % M
-    float4 xv[XC];
+    // XC groups of four (column, vector) pairs of x per wave, one pair per
+    // 16-lane group: all of them when S * M <= 4 * XC * NW; pair p is column
+    // p / M of vector p % M
+    float4 xv[XC][4];
 #pragma unroll
     for (int i = 0; i < XC; ++i) {
-        const int pr = min(wave + i * NW, npairs - 1);
-        xv[i] = load_x_col(x + (size_t)(pr % M) * k, pr / M, lane);
+        const int pr = min(4 * (wave + i * NW) + (lane >> 4), npairs - 1);
+        load_x_quarter(x, k, M, pr, lane, xv[i]);
     }
     uint4 lines[P][2];
 #pragma unroll
@@ -839,11 +924,15 @@ gemv_i8_lines_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
     // the last go to a spare slot
 #pragma unroll
     for (int i = 0; i < XC; ++i) {
-        convert_col_i8(xv[i], smem + (size_t)min(wave + i * NW, npairs) * kI8ColBytes, lane);
+        const int pr = min(4 * (wave + i * NW) + (lane >> 4), npairs);
+        convert4_i8(xv[i], smem + (size_t)pr * kI8ColBytes, lane);
     }
-    for (int pr = XC * NW + wave; pr < npairs; pr += NW) {
-        convert_col_i8(load_x_col(x + (size_t)(pr % M) * k, pr / M, lane),
-                       smem + (size_t)pr * kI8ColBytes, lane);
+    for (int q = XC * NW + wave; 4 * q < npairs; q += NW) {
+        const int pr = min(4 * q + (lane >> 4), npairs - 1);
+        float4 v[4];
+        load_x_quarter(x, k, M, pr, lane, v);
+        convert4_i8(v, smem + (size_t)(4 * q + (lane >> 4) < npairs ? pr : npairs) * kI8ColBytes,
+                    lane);
     }
     __syncthreads();
 
@@ -865,7 +954,9 @@ gemv_i8_lines_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
                 const uint32_t lpos = ((par + (uint32_t)l) & 1u) * 128u + 16u * (uint32_t)lunit;
                 *reinterpret_cast<uint4*>(ring + lrow * kRingRow + lpos) = lines[slot][0];
                 *reinterpret_cast<uint4*>(ring + (8 + lrow) * kRingRow + lpos) = lines[slot][1];
-                __builtin_amdgcn_sched_barrier(0);
+                // memory operations stay in order here (the refill after the
+                // write of its slot); arithmetic may move across
+                __builtin_amdgcn_sched_barrier(0x000F);
                 const int ln = l + P;              // refill: P lines ahead
                 const uint8_t* p[2];
                 line_ptrs(ln >= 9 ? sig + 1 : sig, ln >= 9 ? ln - 9 : ln, p);
@@ -930,17 +1021,17 @@ static hipError_t launch_lines_x(const GemvPlan& p, const uint8_t* w, const floa
     return hipGetLastError();
 }
 
-// (column, vector) pairs of x each wave converts before the first barrier:
-// the power of two covering S * m / NW, at most 8 (the rest follow in a loop)
+// groups of four (column, vector) pairs of x each wave converts before the
+// first barrier: the power of two covering S * m / (4 NW), at most 4 (the
+// rest follow in a loop)
 template <int NW, int P>
 static hipError_t launch_lines_p(const GemvPlan& p, const uint8_t* w, const float* x, float* y,
                                  hipStream_t stream)
 {
-    const int per = (p.S + NW - 1) / NW;
+    const int per = (p.S + 4 * NW - 1) / (4 * NW);
     if (per <= 1) return launch_lines_x<NW, P, 1, 1>(p, w, x, y, stream);
     if (per <= 2) return launch_lines_x<NW, P, 2, 1>(p, w, x, y, stream);
-    if (per <= 4) return launch_lines_x<NW, P, 4, 1>(p, w, x, y, stream);
-    return launch_lines_x<NW, P, 8, 1>(p, w, x, y, stream);
+    return launch_lines_x<NW, P, 4, 1>(p, w, x, y, stream);
 }
 
 template <int NW>
@@ -956,9 +1047,10 @@ template <int M>
 static hipError_t launch_lines_m(const GemvPlan& p, const uint8_t* w, const float* x, float* y,
                                  hipStream_t stream)
 {
-    const int per = (p.S * M + 7) / 8;
+    const int per = (p.S * M + 31) / 32;
+    if (per <= 1) return launch_lines_x<8, 3, 1, M>(p, w, x, y, stream);
     if (per <= 2) return launch_lines_x<8, 3, 2, M>(p, w, x, y, stream);
-    return launch_lines_x<8, 3, 8, M>(p, w, x, y, stream);
+    return launch_lines_x<8, 3, 4, M>(p, w, x, y, stream);
 }
 
 template <int NW, int TPT, int UC>

@@ -235,6 +235,18 @@ LINES_VARIANTS = [
 ]
 
 
+def _lines_auto_cols(n, k, m, opts):
+    """The line-streamed kernel's automatic column grouping: whole rows for
+    at least 1024 tiles of 16 rows or when the per-slab row sums do not fit
+    the LDS, else one slab of 8 columns."""
+    S = k // 256
+    ntiles = (n + 15) // 16
+    rpb = opts.get("rows_per_block") or 16 * ((ntiles + 255) // 256)
+    nw = opts.get("waves_per_block", 8)
+    fits = (S * m + 1) * 960 + nw * 4352 + (S // 8) * rpb * 4 * m <= 160 * 1024
+    return S if (ntiles >= 1024 or not fits) else 8
+
+
 def _lines_check(w_d, w, x, n, k, y_ref, bound, what):
     S = k // 256
     for opts in LINES_VARIANTS:
@@ -251,7 +263,7 @@ def _lines_check(w_d, w, x, n, k, y_ref, bound, what):
             assert e.rc == q4k.Q4K_ERR_UNSUPPORTED and (bad_group or too_big), opts
             continue
         assert_within(y, y_ref, bound, "%s line-streamed %r" % (what, opts))
-        cpt = opts.get("cols_per_task", 8)     # automatic grouping: one slab of 8 columns
+        cpt = opts.get("cols_per_task") or _lines_auto_cols(n, k, 1, opts)
         y4 = run_gemv(w_d, x, n, k, 1, kernel=4, cols_per_task=cpt)
         assert np.array_equal(y.view(np.uint32), y4.view(np.uint32)), opts
 
