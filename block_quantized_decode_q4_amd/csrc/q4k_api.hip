@@ -142,11 +142,13 @@ int make_plan_mfma(int64_t n, int64_t k, int kernel, const q4k_launch* o, GemvPl
     return Q4K_OK;
 }
 
-// Plan of the line-streamed kernel (k a multiple of 2048, weights 128-byte
-// aligned, m <= 8).  A task is a 16-row tile times a group of slabs of
-// eight superblock columns; x (every vector) is staged whole.
+// Plan of the line-streamed kernels (k a multiple of 2048, weights 128-byte
+// aligned, m <= 8): kernel 5 (one MFMA group per vector) and kernel 6 (one
+// MFMA per sub-block and quad of vectors).  A task is a 16-row tile times a
+// group of slabs of eight superblock columns; x (every vector) is staged
+// whole.
 int make_plan_lines(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t lds_max,
-                    GemvPlan* p)
+                    GemvPlan* p, int kernel = 5)
 {
     const int S = (int)(k / q4k::kQK);
     if (S % 8 != 0) {
@@ -167,7 +169,7 @@ int make_plan_lines(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t
     if (nw == 16 && ring == 9) {
         return Q4K_ERR_UNSUPPORTED;    // 1024-lane workgroups cap a lane at 128 VGPRs
     }
-    if (m > 1 && (nw != 8 || ring != 3)) {
+    if ((m > 1 || kernel == 6) && (nw != 8 || ring != 3)) {
         return Q4K_ERR_UNSUPPORTED;    // several vectors: eight waves, three lines in flight
     }
     const int64_t ntiles = (n + 15) / 16;
@@ -186,7 +188,7 @@ int make_plan_lines(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t
         // all of x, which costs as much as decoding a few tiles
         rpb = 16 * ((ntiles + 255) / 256);
     }
-    const size_t lds_x = q4k::lines_lds_bytes(S, (int)m, nw);
+    const size_t lds_x = kernel == 6 ? q4k::sub_lds_bytes(S, (int)m) : q4k::lines_lds_bytes(S, (int)m, nw);
     if (!(o && o->cols_per_task)) {
         // whole rows per task when there are at least four tiles per CU of a
         // 256-CU part (no row sums to combine), else one slab per task for
@@ -215,7 +217,7 @@ int make_plan_lines(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t
     p->x_in_registers = 0;
     p->grid = (int)grid;
     p->lds_bytes = lds;
-    p->kernel = 5;
+    p->kernel = kernel;
     p->ring_depth = ring;
     p->rows_per_task = 0;
     p->cols_per_task = (int)(spt * 8);
@@ -228,9 +230,10 @@ int make_plan_lines(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t
 // Plans needing more LDS than lds_max are returned as they are; the caller
 // refuses them.
 // The automatic kernel (choices measured on MI355X).  The line-streamed
-// kernel applies when k is a multiple of 2048, the weights are 128-byte
-// aligned and its LDS (x of every vector, the line rings) fits.  m > 1: the
-// line-streamed kernel where it applies, else the x-stager kernel.  m = 1:
+// kernels apply when k is a multiple of 2048, the weights are 128-byte
+// aligned and their LDS (x of every vector, the line rings) fits.  m > 1:
+// the sub-block kernel (m >= 3) or the per-vector line-streamed kernel
+// (m = 2), the other one if only it fits, else the x-stager kernel.  m = 1:
 // the line-streamed kernel where it applies and the weights take at least
 // 16 MiB, else the streaming kernel, whose shorter start wins on smaller
 // matrices.  Options other than `kernel` keep the earlier families:
@@ -247,10 +250,16 @@ int auto_kernel(int64_t n, int64_t k, int64_t m, const q4k_launch* o, bool w_ali
 {
     GemvPlan lp;
     if (m != 1) {
-        // several vectors: the line-streamed kernel whenever it applies
-        if (!any_option(o) && w_aligned128 &&
-            make_plan_lines(n, k, m, nullptr, lds_max, &lp) == Q4K_OK && lp.lds_bytes <= lds_max) {
-            return 5;
+        // several vectors: a line-streamed kernel whenever one applies; the
+        // sub-block kernel from three vectors on
+        if (!any_option(o) && w_aligned128) {
+            const int first = m >= 3 ? 6 : 5;
+            for (int kern : {first, 11 - first}) {
+                if (make_plan_lines(n, k, m, nullptr, lds_max, &lp, kern) == Q4K_OK &&
+                    lp.lds_bytes <= lds_max) {
+                    return kern;
+                }
+            }
         }
         return 1;
     }
@@ -291,11 +300,11 @@ int make_plan(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t lds_m
     const int nchunks = (nspans + spc - 1) / spc;
 
     const int kernel = (o && o->kernel) ? o->kernel : auto_kernel(n, k, m, o, w_aligned128, lds_max);
-    if (kernel < 1 || kernel > 5 || (kernel >= 2 && kernel <= 4 && m != 1)) {
+    if (kernel < 1 || kernel > 6 || (kernel >= 2 && kernel <= 4 && m != 1)) {
         return Q4K_ERR_UNSUPPORTED;
     }
-    if (kernel == 5) {
-        return make_plan_lines(n, k, m, o, lds_max, p);
+    if (kernel >= 5) {
+        return make_plan_lines(n, k, m, o, lds_max, p, kernel);
     }
     if (kernel >= 3) {
         return make_plan_mfma(n, k, kernel, o, p);
@@ -450,7 +459,7 @@ int gemv_checked(const void* w, const float* x, float* y, int64_t n, int64_t k, 
     if (plan.lds_bytes > lds_max) {
         return Q4K_ERR_UNSUPPORTED;
     }
-    if (plan.kernel == 5 && (reinterpret_cast<uintptr_t>(w) & 127u) != 0) {
+    if (plan.kernel >= 5 && (reinterpret_cast<uintptr_t>(w) & 127u) != 0) {
         return Q4K_ERR_UNSUPPORTED;    // whole-line reads need 128-byte aligned rows
     }
     return hip_status(q4k::launch_gemv(plan, w, x, y, static_cast<hipStream_t>(stream)));

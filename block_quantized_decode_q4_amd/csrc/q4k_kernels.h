@@ -28,7 +28,7 @@ struct GemvPlan {
     int grid;
     size_t lds_bytes;
     int kernel;            // 1: x-stager, 2: streaming, 3: f16 matrix-core, 4: int8 matrix-core,
-                           // 5: line-streamed int8 matrix-core (m = 1)
+                           // 5: line-streamed int8 matrix-core, 6: sub-block int8 matrix-core
     int ring_depth;        // kernels 2, 3: loads in flight per wave
     int rows_per_task;     // streaming kernel: rows per wave task
     int cols_per_task;     // matrix-core kernel: superblock columns per task
@@ -43,6 +43,7 @@ hipError_t launch_gemv_mfma(const GemvPlan& p, const void* w, const float* x, fl
 size_t mfma_col_bytes(int kernel);
 size_t mfma_lds_bytes(int kernel, int cols_chunk);
 size_t lines_lds_bytes(int S, int m, int waves);
+size_t sub_lds_bytes(int S, int m);
 hipError_t launch_dequant(const void* w, float* out, int64_t nsb, hipStream_t stream);
 hipError_t launch_read(const void* buf, size_t n16, float* out, hipStream_t stream);
 

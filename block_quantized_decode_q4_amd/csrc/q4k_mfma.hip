@@ -832,21 +832,26 @@ __device__ __forceinline__ uint4 load_line_nt(const uint8_t* p)
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-template <int NW, int P, int XC, int M>
-__global__ void __launch_bounds__(NW * 64)
-gemv_i8_lines_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
-                     float* __restrict__ y, int n, int S, int rows_per_block, int slabs_per_task)
+// The line stream shared by the line-streamed kernels.  Work: the
+// workgroup's rows in 16-row tiles, each row in slabs of eight superblocks;
+// a task is (tile, group of slabs_per_task slabs) and wave w takes tasks w,
+// w + NW, ...  Calls, in order: issue_x() (the x loads), the first P lines
+// of weights go out, convert_x() (x into LDS), a workgroup barrier, then
+// step(c, rr, b0) for every superblock column c of the wave's tasks in order
+// (rr: the ring row of the lane's tile row j, b0: the superblock's byte
+// offset in that row's two-line ring window, mod 256) and task_end(task)
+// after each task's last slab.
+template <int NW, int P, typename IssueX, typename ConvertX, typename Step, typename TaskEnd>
+__device__ __forceinline__ void line_stream(const uint8_t* __restrict__ w,
+                                            const float* __restrict__ x, int n, int S,
+                                            int rows_per_block, int slabs_per_task,
+                                            unsigned char* ring, IssueX issue_x,
+                                            ConvertX convert_x, Step step, TaskEnd task_end)
 {
-    extern __shared__ __align__(16) unsigned char smem[];
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int g = lane >> 4;
+    static_assert(P == 3 || P == 9, "line slots must divide the nine lines of a slab");
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int j = lane & 15;
-    const bool active = (j >> 2) == g && (j & 3) < 3;
-    const uint32_t a_off = active ? (uint32_t)((g * 3 + (j & 3)) * 16) : (uint32_t)kI8ZeroSlot;
-    const uint32_t sh = (uint32_t)(g & 1) * 16u;
-    const uint32_t sel = g < 2 ? 0xFFFFFFFFu : 0u;
     // load role: eight lanes per row and line
     const int lrow = lane >> 3;
     const int lunit = lane & 7;
@@ -854,20 +859,11 @@ gemv_i8_lines_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
     const int row0 = blockIdx.x * rows_per_block;
     const int rows_here = min(rows_per_block, n - row0);
     const int ntiles = (rows_here + 15) >> 4;
-    const int nslabs = S >> 3;
-    const int ncg = nslabs / slabs_per_task;
+    const int ncg = (S >> 3) / slabs_per_task;
     const int ntasks = ntiles * ncg;
     const int my_tasks = ntasks > wave ? (ntasks - wave + NW - 1) / NW : 0;
     const int my_slabs = my_tasks * slabs_per_task;
     const size_t row_bytes = (size_t)S * 144;
-
-    // LDS: staged x (S columns of M vectors, column-major, and a spare
-    // slot), the line rings, row sums
-    const int npairs = S * M;
-    const size_t xbytes = (size_t)(npairs + 1) * kI8ColBytes;
-    unsigned char* ring = smem + xbytes + wave * kRingWave;
-    float* ypart = reinterpret_cast<float*>(smem + xbytes + NW * kRingWave);
-    const int k = S * 256;
 
     // slab sig of this wave -> (tile, absolute slab); clamped into the
     // wave's slabs (and into the block's tasks for a wave without any), so
@@ -898,19 +894,10 @@ gemv_i8_lines_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
         }
     };
 
-    static_assert(P == 3 || P == 9, "line slots must divide the nine lines of a slab");
     // x loads first, then the first lines of weights, then the conversion:
     // waiting for x (the counter of loads returns in order) then leaves the
     // weight lines in flight
-    // XC groups of four (column, vector) pairs of x per wave, one pair per
-    // 16-lane group: all of them when S * M <= 4 * XC * NW; pair p is column
-    // p / M of vector p % M
-    float4 xv[XC][4];
-#pragma unroll
-    for (int i = 0; i < XC; ++i) {
-        const int pr = min(4 * (wave + i * NW) + (lane >> 4), npairs - 1);
-        load_x_quarter(x, k, M, pr, lane, xv[i]);
-    }
+    issue_x();
     uint4 lines[P][2];
 #pragma unroll
     for (int l = 0; l < P; ++l) {
@@ -919,28 +906,9 @@ gemv_i8_lines_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
         lines[l][0] = load_line_nt(p[0]);
         lines[l][1] = load_line_nt(p[1]);
     }
-    // unconditional conversions (a load feeding a conditional use would be
-    // sunk into the branch and wait for every load before it); columns past
-    // the last go to a spare slot
-#pragma unroll
-    for (int i = 0; i < XC; ++i) {
-        const int pr = min(4 * (wave + i * NW) + (lane >> 4), npairs);
-        convert4_i8(xv[i], smem + (size_t)pr * kI8ColBytes, lane);
-    }
-    for (int q = XC * NW + wave; 4 * q < npairs; q += NW) {
-        const int pr = min(4 * q + (lane >> 4), npairs - 1);
-        float4 v[4];
-        load_x_quarter(x, k, M, pr, lane, v);
-        convert4_i8(v, smem + (size_t)(4 * q + (lane >> 4) < npairs ? pr : npairs) * kI8ColBytes,
-                    lane);
-    }
+    convert_x();
     __syncthreads();
 
-    float acc[M];
-#pragma unroll
-    for (int b = 0; b < M; ++b) {
-        acc[b] = 0.f;
-    }
     for (int sig = 0; sig < my_slabs; ++sig) {
         int tile, slab;
         slab_of(sig, tile, slab);
@@ -963,40 +931,108 @@ gemv_i8_lines_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
                 lines[slot][0] = load_line_nt(p[0]);
                 lines[slot][1] = load_line_nt(p[1]);
             }
-            // operands of superblock c = 8 slab + cp from the ring
-            const int c = 8 * slab + cp;
-            const uint32_t b0 = (uint32_t)(144 * cp) + par * 128u;   // ring byte of the superblock
-            const unsigned char* rr = ring + j * kRingRow;
-            TileI8 t;
-            t.h = *reinterpret_cast<const uint4*>(rr + (b0 & 255u));
-            t.q0 = *reinterpret_cast<const uint4*>(rr + ((b0 + 16u + 32u * (uint32_t)g) & 255u));
-            t.q1 = *reinterpret_cast<const uint4*>(rr + ((b0 + 32u + 32u * (uint32_t)g) & 255u));
-            const StepW sw = step_weights(t, sh, sel);
-#pragma unroll
-            for (int b = 0; b < M; ++b) {
-                const ColI8 col = read_col_i8(smem + (size_t)(c * M + b) * kI8ColBytes, a_off, g);
-                acc[b] += step_vector(sw, col);
-            }
+            // superblock c = 8 slab + cp, in the ring of tile row j
+            step(8 * slab + cp, ring + j * kRingRow, (uint32_t)(144 * cp) + par * 128u);
         }
         if (sig % slabs_per_task == slabs_per_task - 1) {
-            const int task = wave + (sig / slabs_per_task) * NW;
-            const int r = (task / ncg) * 16 + j;
-#pragma unroll
-            for (int b = 0; b < M; ++b) {
-                float v = acc[b];
-                v += __shfl_xor(v, 16, 64);
-                v += __shfl_xor(v, 32, 64);
-                if (g == 0 && r < rows_here) {
-                    if (ncg == 1) {
-                        y[(size_t)b * n + row0 + r] = v;
-                    } else {
-                        ypart[(b * ncg + task % ncg) * rows_per_block + r] = v;
-                    }
-                }
-                acc[b] = 0.f;
-            }
+            task_end(wave + (sig / slabs_per_task) * NW);
         }
     }
+}
+
+template <int NW, int P, int XC, int M>
+__global__ void __launch_bounds__(NW * 64)
+gemv_i8_lines_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
+                     float* __restrict__ y, int n, int S, int rows_per_block, int slabs_per_task)
+{
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4;
+    const int j = lane & 15;
+    const bool active = (j >> 2) == g && (j & 3) < 3;
+    const uint32_t a_off = active ? (uint32_t)((g * 3 + (j & 3)) * 16) : (uint32_t)kI8ZeroSlot;
+    const uint32_t sh = (uint32_t)(g & 1) * 16u;
+    const uint32_t sel = g < 2 ? 0xFFFFFFFFu : 0u;
+    const int row0 = blockIdx.x * rows_per_block;
+    const int rows_here = min(rows_per_block, n - row0);
+    const int ncg = (S >> 3) / slabs_per_task;
+
+    // LDS: staged x (S columns of M vectors, column-major, and a spare
+    // slot), the line rings, row sums
+    const int npairs = S * M;
+    const size_t xbytes = (size_t)(npairs + 1) * kI8ColBytes;
+    unsigned char* ring = smem + xbytes + wave * kRingWave;
+    float* ypart = reinterpret_cast<float*>(smem + xbytes + NW * kRingWave);
+    const int k = S * 256;
+
+    // XC groups of four (column, vector) pairs of x per wave, one pair per
+    // 16-lane group: all of them when S * M <= 4 * XC * NW; pair p is column
+    // p / M of vector p % M
+    float4 xv[XC][4];
+    auto issue_x = [&]() {
+#pragma unroll
+        for (int i = 0; i < XC; ++i) {
+            const int pr = min(4 * (wave + i * NW) + (lane >> 4), npairs - 1);
+            load_x_quarter(x, k, M, pr, lane, xv[i]);
+        }
+    };
+    // unconditional conversions (a load feeding a conditional use would be
+    // sunk into the branch and wait for every load before it); pairs past
+    // the last go to a spare slot
+    auto convert_x = [&]() {
+#pragma unroll
+        for (int i = 0; i < XC; ++i) {
+            const int pr = min(4 * (wave + i * NW) + (lane >> 4), npairs);
+            convert4_i8(xv[i], smem + (size_t)pr * kI8ColBytes, lane);
+        }
+        for (int q = XC * NW + wave; 4 * q < npairs; q += NW) {
+            const int pr = min(4 * q + (lane >> 4), npairs - 1);
+            float4 v[4];
+            load_x_quarter(x, k, M, pr, lane, v);
+            convert4_i8(v, smem + (size_t)(4 * q + (lane >> 4) < npairs ? pr : npairs) * kI8ColBytes,
+                        lane);
+        }
+    };
+
+    float acc[M];
+#pragma unroll
+    for (int b = 0; b < M; ++b) {
+        acc[b] = 0.f;
+    }
+    auto step = [&](int c, const unsigned char* rr, uint32_t b0) {
+        TileI8 t;
+        t.h = *reinterpret_cast<const uint4*>(rr + (b0 & 255u));
+        t.q0 = *reinterpret_cast<const uint4*>(rr + ((b0 + 16u + 32u * (uint32_t)g) & 255u));
+        t.q1 = *reinterpret_cast<const uint4*>(rr + ((b0 + 32u + 32u * (uint32_t)g) & 255u));
+        const StepW sw = step_weights(t, sh, sel);
+#pragma unroll
+        for (int b = 0; b < M; ++b) {
+            const ColI8 col = read_col_i8(smem + (size_t)(c * M + b) * kI8ColBytes, a_off, g);
+            acc[b] += step_vector(sw, col);
+        }
+    };
+    auto task_end = [&](int task) {
+        const int r = (task / ncg) * 16 + j;
+#pragma unroll
+        for (int b = 0; b < M; ++b) {
+            float v = acc[b];
+            v += __shfl_xor(v, 16, 64);
+            v += __shfl_xor(v, 32, 64);
+            if (g == 0 && r < rows_here) {
+                if (ncg == 1) {
+                    y[(size_t)b * n + row0 + r] = v;
+                } else {
+                    ypart[(b * ncg + task % ncg) * rows_per_block + r] = v;
+                }
+            }
+            acc[b] = 0.f;
+        }
+    };
+    line_stream<NW, P>(w, x, n, S, rows_per_block, slabs_per_task, ring, issue_x, convert_x, step,
+                       task_end);
+
     if (ncg > 1) {
         __syncthreads();
         for (int i = tid; i < rows_here * M; i += NW * 64) {
@@ -1009,6 +1045,290 @@ gemv_i8_lines_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
             y[(size_t)b * n + row0 + r] = a;
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// Sub-block int8 matrix-core kernel for several vectors
+// (v_mfma_i32_16x16x32_i8, line-streamed weights).
+//
+// Operands of one MFMA (16 x 16 x 32): lane l = 16 g + j holds
+//   A[i = j][k = 8g .. 8g+7] (8 bytes), B[k = 8g .. 8g+7][j], D[4g + r][j].
+//
+// One MFMA covers one 32-element sub-block s for four vectors: B = the codes
+// of sub-block s of the 16 rows of the tile (lane group g: elements 8g ..
+// 8g+7, taken from bytes 8g .. 8g+7 of the chunk, low or high nibbles as in
+// the kernels above), A row 4 b' + l = digit l of vector b' of the quad (row
+// 4 b' + 3 zero).  A is dense, so a superblock costs eight small MFMAs per
+// quad of vectors instead of four large ones per vector, and lane (g, j) ends
+// with the three digit sums of vector g of the quad for row j: it needs no
+// other lane, but it scales all eight sub-blocks of its row:
+//   acc += d * sum_s sc_s * u_s - dmin * sum_s m_s * X_s,
+//   u_s = 2^-sigma_s * T_s (low sub-blocks), 2^-sigma_s / 16 * T_s + 8 X_s (high),
+// T = D0 + 256 D1 + 65536 D2, X_s the quantized x sum of the sub-block.
+// ---------------------------------------------------------------------------
+
+constexpr int kSbBlock = 49 * 8;              // 48 digit slots of 8 bytes and a zero slot
+constexpr int kSbZero = 48 * 8;
+constexpr int kSbQuad = 8 * kSbBlock;         // A operands of one column and vector quad
+constexpr int kSbConst = 8 * 8;               // {scale, X} of the eight sub-blocks of one vector
+constexpr int kSbGroup = kSbQuad + 4 * kSbConst;   // one column, one quad: A, then constants
+
+// Convert one (column, vector quad): lane l takes vector l / 16 of the quad
+// and elements 16 (l % 16) .. +15 of the column (half of sub-block (l % 16) /
+// 2).  Digits as in convert4_i8; here digit l of elements 8g .. 8g+7 of
+// sub-block s of vector b' goes to slot (g, b', l) of block s.
+__device__ __forceinline__ void convert4_sb(const float4 (&v)[4], unsigned char* grp, int lane)
+{
+    const int le = lane & 15;
+    const int bq = lane >> 4;                 // vector within the quad
+    const int s = le >> 1;                    // sub-block
+    const int half = le & 1;
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        m = fmaxf(m, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
+    }
+    m = fmaxf(m, __builtin_bit_cast(float, dpp_i<0xB1>(__builtin_bit_cast(int, m))));  // lane l ^ 1
+    int sigma = 0;
+    if (m > 0.f) {
+        sigma = 22 - __builtin_amdgcn_frexp_expf(m);
+        sigma = sigma < -126 ? -126 : sigma > 126 ? 126 : sigma;
+    }
+    const float scale = __builtin_bit_cast(float, (uint32_t)(sigma + 127) << 23);
+    uint32_t usum = 0;
+    uint32_t dig[3][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float vals[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+        uint32_t u[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            u[t] = __builtin_bit_cast(uint32_t, __builtin_fmaf(vals[t], scale, 12582912.0f)) -
+                   0x4ABF7F80u;
+            usum += u[t];
+        }
+        const uint32_t lo01 = __builtin_amdgcn_perm(u[1], u[0], 0x05010400u);
+        const uint32_t lo23 = __builtin_amdgcn_perm(u[3], u[2], 0x05010400u);
+        const uint32_t hi01 = __builtin_amdgcn_perm(u[1], u[0], 0x07030602u);
+        const uint32_t hi23 = __builtin_amdgcn_perm(u[3], u[2], 0x07030602u);
+        dig[0][i] = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u) ^ 0x80808080u;
+        dig[1][i] = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u) ^ 0x80808080u;
+        dig[2][i] = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u) ^ 0x80808080u;
+    }
+    unsigned char* blk = grp + s * kSbBlock;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int gk = 2 * half + h;          // k-group of these eight elements
+#pragma unroll
+        for (int l = 0; l < 3; ++l) {
+            *reinterpret_cast<uint2*>(blk + ((gk * 4 + bq) * 3 + l) * 8) =
+                make_uint2(dig[l][2 * h], dig[l][2 * h + 1]);
+        }
+    }
+    if (bq == 0 && half == 0) {
+        *reinterpret_cast<uint2*>(blk + kSbZero) = make_uint2(0, 0);
+    }
+    const uint32_t us2 = usum + (uint32_t)dpp_i<0xB1>((int)usum);
+    const int XI = (int)us2 - 32 * 0x808080;
+    if (half == 0) {
+        const float inv = __builtin_bit_cast(float, (uint32_t)(127 - sigma) << 23);
+        *reinterpret_cast<float2*>(grp + kSbQuad + bq * kSbConst + s * 8) =
+            make_float2((s & 1) ? inv * 0.0625f : inv, inv * (float)XI);
+    }
+}
+
+// The eight sub-block scales and mins of a header as floats.
+struct RowScales {
+    float d, dmin;
+    float sc[8], m[8];
+};
+
+__device__ __forceinline__ RowScales decode_row(const uint4& h)
+{
+    RowScales r;
+    const half2_t dd = __builtin_bit_cast(half2_t, h.x);
+    r.d = (float)dd.x;
+    r.dmin = (float)dd.y;
+    const uint32_t sc03 = h.y & 0x3F3F3F3Fu;
+    const uint32_t m03 = h.z & 0x3F3F3F3Fu;
+    const uint32_t sc47 = (h.w & 0x0F0F0F0Fu) | ((h.y >> 2) & 0x30303030u);
+    const uint32_t m47 = ((h.w >> 4) & 0x0F0F0F0Fu) | ((h.z >> 2) & 0x30303030u);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        r.sc[b] = (float)((sc03 >> (8 * b)) & 0xFFu);
+        r.m[b] = (float)((m03 >> (8 * b)) & 0xFFu);
+        r.sc[4 + b] = (float)((sc47 >> (8 * b)) & 0xFFu);
+        r.m[4 + b] = (float)((m47 >> (8 * b)) & 0xFFu);
+    }
+    return r;
+}
+
+template <int NW, int XC, int NQ>
+__global__ void __launch_bounds__(NW * 64)
+gemv_i8_sub_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
+                   float* __restrict__ y, int n, int S, int m, int rows_per_block,
+                   int slabs_per_task)
+{
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4;
+    const int j = lane & 15;
+    // A row of this lane: vector j / 4 of the quad, digit j % 4 (3: zero)
+    const uint32_t a_off = (j & 3) < 3 ? (uint32_t)(((g * 4 + (j >> 2)) * 3 + (j & 3)) * 8)
+                                       : (uint32_t)kSbZero;
+    const int row0 = blockIdx.x * rows_per_block;
+    const int rows_here = min(rows_per_block, n - row0);
+    const int ncg = (S >> 3) / slabs_per_task;
+    const int k = S * 256;
+
+    // LDS: staged x (S columns x NQ quads and a spare group), the line
+    // rings, row sums
+    const int ngroups = S * NQ;
+    const size_t xbytes = (size_t)(ngroups + 1) * kSbGroup;
+    unsigned char* ring = smem + xbytes + wave * kRingWave;
+    float* ypart = reinterpret_cast<float*>(smem + xbytes + NW * kRingWave);
+
+    // group q0 = column q0 / NQ, quad q0 % NQ; 16-lane group l / 16 takes
+    // vector 4 (q0 % NQ) + l / 16 (zero past the last vector)
+    float4 xv[XC][4];
+    auto load_group = [&](int q0, float4 (&v)[4]) {
+        const int qc = min(q0, ngroups - 1);
+        const int b = 4 * (qc % NQ) + (lane >> 4);
+        const float* src = x + (size_t)min(b, m - 1) * k + (size_t)(qc / NQ) * 256 + 16 * (lane & 15);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[i] = reinterpret_cast<const float4*>(src)[i];
+        }
+    };
+    auto zero_past = [&](int q0, float4 (&v)[4]) {
+        const bool past = 4 * (min(q0, ngroups - 1) % NQ) + (lane >> 4) >= m;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[i] = past ? make_float4(0.f, 0.f, 0.f, 0.f) : v[i];
+        }
+    };
+    auto issue_x = [&]() {
+#pragma unroll
+        for (int i = 0; i < XC; ++i) {
+            load_group(wave + i * NW, xv[i]);
+        }
+    };
+    auto convert_x = [&]() {
+#pragma unroll
+        for (int i = 0; i < XC; ++i) {
+            const int q0 = wave + i * NW;
+            zero_past(q0, xv[i]);
+            convert4_sb(xv[i], smem + (size_t)min(q0, ngroups) * kSbGroup, lane);
+        }
+        for (int q0 = XC * NW + wave; q0 < ngroups; q0 += NW) {
+            float4 v[4];
+            load_group(q0, v);
+            zero_past(q0, v);
+            convert4_sb(v, smem + (size_t)q0 * kSbGroup, lane);
+        }
+    };
+
+    float acc[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        acc[q] = 0.f;
+    }
+    auto step = [&](int c, const unsigned char* rr, uint32_t b0) {
+        const uint4 hdr = *reinterpret_cast<const uint4*>(rr + (b0 & 255u));
+        uint2 raw[4];
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+            raw[cc] = *reinterpret_cast<const uint2*>(rr + ((b0 + 16u + 32u * cc + 8u * g) & 255u));
+        }
+        long codes[8];
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+            codes[2 * cc] = __builtin_bit_cast(long, make_uint2(raw[cc].x & 0x0F0F0F0Fu,
+                                                                 raw[cc].y & 0x0F0F0F0Fu));
+            codes[2 * cc + 1] = __builtin_bit_cast(
+                long, make_uint2((raw[cc].x & 0xF0F0F0F0u) ^ 0x80808080u,
+                                 (raw[cc].y & 0xF0F0F0F0u) ^ 0x80808080u));
+        }
+        const RowScales rs = decode_row(hdr);
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const unsigned char* grp = smem + (size_t)(c * NQ + q) * kSbGroup;
+            const float4* cst = reinterpret_cast<const float4*>(grp + kSbQuad + g * kSbConst);
+            float t1 = 0.f, t2 = 0.f;
+#pragma unroll
+            for (int sp = 0; sp < 4; ++sp) {
+                const float4 k2 = cst[sp];        // {scale, X} of sub-blocks 2sp, 2sp+1
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int sb = 2 * sp + h;
+                    const long a = *reinterpret_cast<const long*>(grp + sb * kSbBlock + a_off);
+                    const i32x4_t zero = {0, 0, 0, 0};
+                    const i32x4_t D = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, codes[sb], zero, 0, 0, 0);
+                    const float T = digits_value(D);
+                    const float sca = h ? k2.z : k2.x;
+                    const float X = h ? k2.w : k2.y;
+                    const float u = h ? __builtin_fmaf(sca, T, 8.0f * X) : sca * T;
+                    t1 = __builtin_fmaf(rs.sc[sb], u, t1);
+                    t2 = __builtin_fmaf(rs.m[sb], X, t2);
+                }
+            }
+            acc[q] = __builtin_fmaf(rs.d, t1, acc[q]);
+            acc[q] = __builtin_fmaf(-rs.dmin, t2, acc[q]);
+        }
+    };
+    auto task_end = [&](int task) {
+        const int r = (task / ncg) * 16 + j;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const int b = 4 * q + g;
+            if (b < m && r < rows_here) {
+                if (ncg == 1) {
+                    y[(size_t)b * n + row0 + r] = acc[q];
+                } else {
+                    ypart[(b * ncg + task % ncg) * rows_per_block + r] = acc[q];
+                }
+            }
+            acc[q] = 0.f;
+        }
+    };
+    line_stream<NW, 3>(w, x, n, S, rows_per_block, slabs_per_task, ring, issue_x, convert_x, step,
+                       task_end);
+
+    if (ncg > 1) {
+        __syncthreads();
+        for (int i = tid; i < rows_here * m; i += NW * 64) {
+            const int b = i / rows_here;
+            const int r = i - b * rows_here;
+            float a = 0.f;
+            for (int cg = 0; cg < ncg; ++cg) {
+                a += ypart[(b * ncg + cg) * rows_per_block + r];
+            }
+            y[(size_t)b * n + row0 + r] = a;
+        }
+    }
+}
+
+template <int XC, int NQ>
+static hipError_t launch_sub_x(const GemvPlan& p, const uint8_t* w, const float* x, float* y,
+                               hipStream_t stream)
+{
+    hipLaunchKernelGGL((gemv_i8_sub_kernel<8, XC, NQ>), dim3(p.grid), dim3(512), p.lds_bytes,
+                       stream, w, x, y, p.n, p.S, p.m, p.rows_per_block, p.cols_per_task / 8);
+    return hipGetLastError();
+}
+
+// (column, quad) groups each of the eight waves converts before the first
+// barrier: the power of two covering S * NQ / 8, at most 4
+template <int NQ>
+static hipError_t launch_sub(const GemvPlan& p, const uint8_t* w, const float* x, float* y,
+                             hipStream_t stream)
+{
+    const int per = (p.S * NQ + 7) / 8;
+    if (per <= 1) return launch_sub_x<1, NQ>(p, w, x, y, stream);
+    if (per <= 2) return launch_sub_x<2, NQ>(p, w, x, y, stream);
+    return launch_sub_x<4, NQ>(p, w, x, y, stream);
 }
 
 template <int NW, int P, int XC, int M>
@@ -1113,6 +1433,10 @@ hipError_t launch_gemv_mfma(const GemvPlan& p, const void* w, const float* x, fl
                             hipStream_t stream)
 {
     const uint8_t* wb = static_cast<const uint8_t*>(w);
+    if (p.kernel == 6) {
+        if (p.m > 4) return launch_sub<2>(p, wb, x, y, stream);
+        return launch_sub<1>(p, wb, x, y, stream);
+    }
     if (p.kernel == 5) {
         switch (p.m) {
         case 1: break;
@@ -1139,6 +1463,12 @@ hipError_t launch_gemv_mfma(const GemvPlan& p, const void* w, const float* x, fl
 size_t mfma_col_bytes(int kernel)
 {
     return kernel == 4 ? (size_t)kI8ColBytes : (size_t)kMfmaColBytes;
+}
+
+size_t sub_lds_bytes(int S, int m)
+{
+    const int nq = (m + 3) / 4;
+    return (size_t)(S * nq + 1) * kSbGroup + (size_t)8 * kRingWave;
 }
 
 size_t lines_lds_bytes(int S, int m, int waves)

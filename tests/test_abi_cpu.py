@@ -90,6 +90,48 @@ def test_gemv_ex_refusals(lib):
     assert lib.q4k_gemv_ex(A, A, A, 16, 256, 2, ctypes.byref(cfg), None) == q4k.Q4K_ERR_UNSUPPORTED
 
 
+def test_launch_struct_matches_header():
+    """The binding's q4k_launch has the fields of the C struct, in order,
+    all int32."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    body = re.search(r"typedef struct q4k_launch \{(.*?)\} q4k_launch;", text, re.S).group(1)
+    fields = re.findall(r"int32_t\s+([a-z_0-9]+)\s*;", body)
+    assert fields == [f for f, _ in q4k.q4k_launch._fields_]
+    assert all(t is ctypes.c_int32 for _, t in q4k.q4k_launch._fields_)
+    assert ctypes.sizeof(q4k.q4k_launch) == 4 * len(fields)
+
+
+def test_gemv_ex_kernel_option_refusals(lib):
+    """Options that no kernel can honour are refused before any HIP call."""
+    cases = [
+        (dict(kernel=7), 16, 2048, 1),
+        (dict(kernel=6), 16, 1024, 1),                       # k not a multiple of 2048
+        (dict(kernel=6, waves_per_block=4), 16, 4096, 2),    # eight waves only
+        (dict(kernel=6, ring_depth=9), 16, 4096, 2),         # three lines in flight only
+        (dict(kernel=-1), 16, 2048, 1),
+        (dict(kernel=2), 16, 2048, 2),                       # streaming: one vector
+        (dict(kernel=3), 16, 2048, 2),                       # f16 matrix cores: one vector
+        (dict(kernel=4), 16, 2048, 3),
+        (dict(kernel=4, tiles_per_task=3), 16, 2048, 1),
+        (dict(kernel=4, ring_depth=4), 16, 2048, 1),
+        (dict(kernel=3, ring_depth=3), 16, 2048, 1),
+        (dict(kernel=5), 16, 1024, 1),                       # k not a multiple of 2048
+        (dict(kernel=5, cols_per_task=12), 16, 4096, 1),     # whole slabs only
+        (dict(kernel=5, cols_per_task=24), 16, 4096, 1),     # must divide the row's slabs
+        (dict(kernel=5, ring_depth=4), 16, 4096, 1),
+        (dict(kernel=5, waves_per_block=16, ring_depth=9), 16, 4096, 1),
+        (dict(kernel=5, waves_per_block=4), 16, 4096, 2),    # several vectors: 8 waves
+        (dict(kernel=5, tiles_per_task=2), 16, 4096, 1),
+        (dict(kernel=1, cols_per_task=8), 16, 4096, 1),      # matrix-core options only
+        (dict(kernel=2, tiles_per_task=1), 16, 4096, 1),
+    ]
+    for o, n, k, m in cases:
+        cfg = q4k.q4k_launch(**o)
+        rc = lib.q4k_gemv_ex(A, A, A, n, k, m, ctypes.byref(cfg), None)
+        assert rc == q4k.Q4K_ERR_UNSUPPORTED, (o, n, k, m, rc)
+
+
 def test_load_refusals(lib):
     host = np.zeros(4 * 144 * 2, np.uint8)
     hp = host.ctypes.data

@@ -310,6 +310,45 @@ def test_lines_kernel_batched_workload(oracle_mod):
         assert np.array_equal(y1[0].view(np.uint32), y[b].view(np.uint32)), b
 
 
+@pytest.mark.parametrize("n,k,m", [(300, 4096, 1), (300, 4096, 2), (17, 2048, 3), (130, 4096, 8),
+                                   (64, 4096, 5), (33, 2048, 8), (40, 8192, 4), (1, 2048, 6)])
+def test_sub_kernel(oracle_mod, n, k, m):
+    """The sub-block kernel: within tolerance, bit-identical to m
+    single-vector launches of itself, and across workgroup shapes with the
+    same column grouping."""
+    w, x = synth.make_inputs(n, k, m, seed=n * 17 + k + 3 * m)
+    y_ref, bound = oracle_mod.gemv(w, x, n)
+    w_d = dev(w)
+    _say("sub-block kernel n=%d k=%d m=%d" % (n, k, m))
+    y = run_gemv(w_d, x, n, k, m, kernel=6, cols_per_task=8)
+    assert_within(y, y_ref, bound, "sub-block m=%d" % m)
+    for b in range(m):
+        y1 = run_gemv(w_d, x[b:b + 1], n, k, 1, kernel=6, cols_per_task=8)
+        assert np.array_equal(y1[0].view(np.uint32), y[b].view(np.uint32)), b
+    for opts in (dict(rows_per_block=48), dict(rows_per_block=16), dict(rows_per_block=200)):
+        y2 = run_gemv(w_d, x, n, k, m, kernel=6, cols_per_task=8, **opts)
+        assert np.array_equal(y2.view(np.uint32), y.view(np.uint32)), opts
+    y3 = run_gemv(w_d, x, n, k, m, kernel=6, cols_per_task=k // 256)
+    assert_within(y3, y_ref, bound, "sub-block whole rows m=%d" % m)
+
+
+def test_sub_kernel_workload(oracle_mod):
+    wl, w, x, y_ref, bound = workload(4, oracle_mod)
+    _say("sub-block kernel workload 4")
+    y = run_gemv(dev(w), x, wl.n, wl.k, wl.m, kernel=6)
+    assert_within(y, y_ref, bound, "sub-block workload 4")
+
+
+def test_sub_kernel_x_dynamic_range(oracle_mod):
+    n, k = 40, 4096
+    rng = np.random.default_rng(99)
+    w, _ = synth.make_inputs(n, k, 1, seed=123)
+    xs = _x_cases(rng, k)
+    y_ref, bound = oracle_mod.gemv(w, xs, n)
+    y = run_gemv(dev(w), xs, n, k, 2, kernel=6)
+    assert_within(y, y_ref, bound, "sub-block dynamic-range x")
+
+
 def test_lines_kernel_refusals():
     """Shapes and pointers the line-streamed kernel cannot take are refused
     without launching (k not a multiple of 2048, rows not 128-byte aligned)."""
@@ -412,7 +451,8 @@ def test_batched_workload_against_separate(oracle_mod):
     itself."""
     wl, w, x, y_ref, bound = workload(4, oracle_mod)
     w_d = dev(w)
-    for opts, single in ((dict(), dict(kernel=5)), (dict(kernel=1), dict(kernel=1))):
+    for opts, single in ((dict(), dict(kernel=6)), (dict(kernel=5), dict(kernel=5)),
+                         (dict(kernel=1), dict(kernel=1))):
         _say("batched workload 4 %r" % opts)
         yb = run_gemv(w_d, x, wl.n, wl.k, wl.m, **opts)
         assert_within(yb, y_ref, bound, "batched workload %r" % opts)
