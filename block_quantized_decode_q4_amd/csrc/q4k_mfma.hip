@@ -875,12 +875,15 @@ __device__ __forceinline__ void line_stream(const uint8_t* __restrict__ w,
         slab = (task % ncg) * slabs_per_task + sig % slabs_per_task;
     };
     // the two global addresses (rows lrow and 8 + lrow) of line l of slab
-    // sig; past the wave's last slab the prefetch reads the first 128 bytes
-    // of x instead (cached, so the surplus loads cost no HBM traffic).  The
-    // choice is a mask on the byte offset from w: a select of two pointers
-    // makes the compiler branch around the address arithmetic, which costs
-    // registers across the unrolled slab.
-    const uint64_t dx = (uint64_t)(reinterpret_cast<const uint8_t*>(x) - w);
+    // sig; past the wave's last slab the prefetch reads a 128-byte line of x
+    // instead (cached, so the surplus loads cost no HBM traffic; each wave
+    // takes its own line, or the tails of all waves would queue on one L2
+    // channel).  The choice is a mask on the byte offset from w: a select of
+    // two pointers makes the compiler branch around the address arithmetic,
+    // which costs registers across the unrolled slab.
+    const int xlines = S * 8;                        // 128-byte lines of one x vector
+    const uint64_t dx = (uint64_t)(reinterpret_cast<const uint8_t*>(x) - w) +
+                        (uint64_t)((blockIdx.x * NW + wave) % xlines) * 128u;
     auto line_ptrs = [&](int sig, int l, const uint8_t** p) {
         int tile, slab;
         slab_of(sig, tile, slab);
