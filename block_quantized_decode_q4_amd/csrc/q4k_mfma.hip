@@ -899,8 +899,13 @@ __device__ __forceinline__ void line_stream(const uint8_t* __restrict__ w,
 
     // x loads first, then the first lines of weights, then the conversion:
     // waiting for x (the counter of loads returns in order) then leaves the
-    // weight lines in flight
+    // weight lines in flight.  No wave sends weight loads before every wave
+    // of the workgroup has sent its x loads (a barrier with no wait for
+    // memory), so x is not queued behind the workgroup's own weight lines.
     issue_x();
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
     uint4 lines[P][2];
 #pragma unroll
     for (int l = 0; l < P; ++l) {
@@ -909,6 +914,7 @@ __device__ __forceinline__ void line_stream(const uint8_t* __restrict__ w,
         lines[l][0] = load_line_nt(p[0]);
         lines[l][1] = load_line_nt(p[1]);
     }
+    __builtin_amdgcn_sched_barrier(0);
     convert_x();
     __syncthreads();
 
