@@ -16,10 +16,10 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libq4k.so")
-SOURCES = [os.path.join(CSRC, "q4k_kernels.hip"), os.path.join(CSRC, "q4k_mfma.hip"),
-           os.path.join(CSRC, "q4k_api.hip")]
+SOURCES = [os.path.join(CSRC, "q4k_kernels.hip"), os.path.join(CSRC, "q4k_dpp.hip"),
+           os.path.join(CSRC, "q4k_mfma.hip"), os.path.join(CSRC, "q4k_api.hip")]
 HEADERS = [os.path.join(CSRC, "q4k_kernels.h"), os.path.join(CSRC, "q4k_device.h"),
-           os.path.join(os.path.dirname(PKG), "include", "q4k.h")]
+           os.path.join(CSRC, "q4k_lines.h"), os.path.join(os.path.dirname(PKG), "include", "q4k.h")]
 ARCH = "gfx950"
 
 
@@ -44,14 +44,18 @@ def compile_flags() -> list[str]:
 def build(verbose: bool = False) -> str:
     """Compile every source into a fresh libq4k.so (always rebuilds)."""
     objs = []
+    procs = []
     cc = hipcc()
-    for src in SOURCES:
+    for src in SOURCES:     # the sources compile in parallel
         obj = os.path.join(CSRC, os.path.splitext(os.path.basename(src))[0] + ".o")
         cmd = [cc] + compile_flags() + ["-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
-        subprocess.run(cmd, check=True)
+        procs.append((subprocess.Popen(cmd), cmd))
         objs.append(obj)
+    failed = [cmd for proc, cmd in procs if proc.wait() != 0]
+    if failed:
+        raise subprocess.CalledProcessError(1, failed[0])
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [cc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:

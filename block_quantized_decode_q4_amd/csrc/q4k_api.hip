@@ -143,10 +143,10 @@ int make_plan_mfma(int64_t n, int64_t k, int kernel, const q4k_launch* o, GemvPl
 }
 
 // Plan of the line-streamed kernels (k a multiple of 2048, weights 128-byte
-// aligned, m <= 8): kernel 5 (one MFMA group per vector) and kernel 6 (one
-// MFMA per sub-block and quad of vectors).  A task is a 16-row tile times a
-// group of slabs of eight superblock columns; x (every vector) is staged
-// whole.
+// aligned, m <= 8): kernel 7 (m = 1, integer dot products on the vector
+// ALU), kernel 5 (one MFMA group per vector) and kernel 6 (one MFMA per
+// sub-block and quad of vectors).  A task is a 16-row tile times a group of
+// slabs of eight superblock columns; x (every vector) is staged whole.
 int make_plan_lines(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t lds_max,
                     GemvPlan* p, int kernel = 5)
 {
@@ -172,6 +172,9 @@ int make_plan_lines(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t
     if ((m > 1 || kernel == 6) && (nw != 8 || ring != 3)) {
         return Q4K_ERR_UNSUPPORTED;    // several vectors: eight waves, three lines in flight
     }
+    if (kernel == 7 && (m != 1 || S * 16 > 4 * 64 * nw)) {
+        return Q4K_ERR_UNSUPPORTED;    // one vector; x in at most four groups per lane
+    }
     const int64_t ntiles = (n + 15) / 16;
     int64_t spt = 1;
     if (o && o->cols_per_task) {
@@ -188,7 +191,9 @@ int make_plan_lines(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t
         // all of x, which costs as much as decoding a few tiles
         rpb = 16 * ((ntiles + 255) / 256);
     }
-    const size_t lds_x = kernel == 6 ? q4k::sub_lds_bytes(S, (int)m) : q4k::lines_lds_bytes(S, (int)m, nw);
+    const size_t lds_x = kernel == 6   ? q4k::sub_lds_bytes(S, (int)m)
+                         : kernel == 7 ? q4k::dot4_lds_bytes(S, nw)
+                                       : q4k::lines_lds_bytes(S, (int)m, nw);
     if (!(o && o->cols_per_task)) {
         // whole rows per task when there are at least four tiles per CU of a
         // 256-CU part (no row sums to combine), else one slab per task for
@@ -234,10 +239,11 @@ int make_plan_lines(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t
 // aligned and their LDS (x of every vector, the line rings) fits.  m > 1:
 // the sub-block kernel (m >= 3) or the per-vector line-streamed kernel
 // (m = 2), the other one if only it fits, else the x-stager kernel.  m = 1:
-// the line-streamed kernel where it applies and the weights take at least
-// 16 MiB, else the streaming kernel, whose shorter start wins on smaller
-// matrices.  Options other than `kernel` keep the earlier families:
-// streaming for m = 1, x-stager otherwise.
+// the line-streamed vector-ALU kernel (7) where it applies and the weights
+// take at least 16 MiB, else the streaming kernel, whose shorter start wins
+// on smaller matrices; m = 1 never takes the matrix cores unless asked to.
+// Options other than `kernel` keep the earlier families: streaming for
+// m = 1, x-stager otherwise.
 bool any_option(const q4k_launch* o)
 {
     return o && (o->variant || o->spans_per_chunk || o->rows_per_block || o->rows_per_wave ||
@@ -268,8 +274,8 @@ int auto_kernel(int64_t n, int64_t k, int64_t m, const q4k_launch* o, bool w_ali
     }
     const int64_t bytes = n * (k / q4k::kQK) * q4k::kBlockBytes;
     if (w_aligned128 && bytes >= ((int64_t)16 << 20) &&
-        make_plan_lines(n, k, 1, nullptr, lds_max, &lp) == Q4K_OK && lp.lds_bytes <= lds_max) {
-        return 5;
+        make_plan_lines(n, k, 1, nullptr, lds_max, &lp, 7) == Q4K_OK && lp.lds_bytes <= lds_max) {
+        return 7;
     }
     return 2;
 }
@@ -300,7 +306,7 @@ int make_plan(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t lds_m
     const int nchunks = (nspans + spc - 1) / spc;
 
     const int kernel = (o && o->kernel) ? o->kernel : auto_kernel(n, k, m, o, w_aligned128, lds_max);
-    if (kernel < 1 || kernel > 6 || (kernel >= 2 && kernel <= 4 && m != 1)) {
+    if (kernel < 1 || kernel > 7 || (((kernel >= 2 && kernel <= 4) || kernel == 7) && m != 1)) {
         return Q4K_ERR_UNSUPPORTED;
     }
     if (kernel >= 5) {

@@ -1,6 +1,7 @@
 // q4k_device.h -- device helpers shared by the GEMV kernels (q4k_kernels.hip,
-// q4k_mfma.hip): fp16 half access, the eight-code fma_mix dot, the
-// superblock header decode, loads and wave reductions.  Internal.
+// q4k_mfma.hip, q4k_dpp.hip): fp16 half access, the eight-code fma_mix dot,
+// the superblock header decode, loads, DPP moves and wave reductions.
+// Internal.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -78,6 +79,14 @@ __device__ __forceinline__ ChunkScales decode_header(const uint4& h, int c)
     s.m_lo = (float)(mm & 0xFFu);
     s.m_hi = (float)((mm >> 8) & 0xFFu);
     return s;
+}
+
+// v of another lane of the wave, chosen by the DPP control CTRL (all rows
+// and banks enabled)
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v)
+{
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
 }
 
 __device__ __forceinline__ float wave_sum(float v)

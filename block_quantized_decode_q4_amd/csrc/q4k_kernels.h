@@ -1,5 +1,6 @@
 // q4k_kernels.h -- internal interface between the C-ABI layer (q4k_api.hip)
-// and the kernels (q4k_kernels.hip).  Not installed, not part of the ABI.
+// and the kernels (q4k_kernels.hip, q4k_dpp.hip, q4k_mfma.hip).  Not
+// installed, not part of the ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -28,7 +29,8 @@ struct GemvPlan {
     int grid;
     size_t lds_bytes;
     int kernel;            // 1: x-stager, 2: streaming, 3: f16 matrix-core, 4: int8 matrix-core,
-                           // 5: line-streamed int8 matrix-core, 6: sub-block int8 matrix-core
+                           // 5: line-streamed int8 matrix-core, 6: sub-block int8 matrix-core,
+                           // 7: line-streamed int8 dot products (vector ALU)
     int ring_depth;        // kernels 2, 3: loads in flight per wave
     int rows_per_task;     // streaming kernel: rows per wave task
     int cols_per_task;     // matrix-core kernel: superblock columns per task
@@ -44,6 +46,9 @@ size_t mfma_col_bytes(int kernel);
 size_t mfma_lds_bytes(int kernel, int cols_chunk);
 size_t lines_lds_bytes(int S, int m, int waves);
 size_t sub_lds_bytes(int S, int m);
+hipError_t launch_gemv_dot4(const GemvPlan& p, const void* w, const float* x, float* y,
+                            hipStream_t stream);
+size_t dot4_lds_bytes(int S, int waves);
 hipError_t launch_dequant(const void* w, float* out, int64_t nsb, hipStream_t stream);
 hipError_t launch_read(const void* buf, size_t n16, float* out, hipStream_t stream);
 

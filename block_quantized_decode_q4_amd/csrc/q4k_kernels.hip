@@ -669,6 +669,9 @@ hipError_t launch_gemv(const GemvPlan& p, const void* w, const float* x, float* 
                        hipStream_t stream)
 {
     const uint8_t* wb = static_cast<const uint8_t*>(w);
+    if (p.kernel == 7) {
+        return launch_gemv_dot4(p, w, x, y, stream);
+    }
     if (p.kernel >= 3) {
         return launch_gemv_mfma(p, w, x, y, stream);
     }

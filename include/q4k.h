@@ -101,15 +101,15 @@ const char* q4k_status_string(int rc);
 
 /* ---------------------------------------------------------------------
  * Launch options for q4k_gemv_ex (tests and tuning).  q4k_gemv is
- * q4k_gemv_ex with every field 0 (automatic).  The line-streamed
- * matrix-core kernel applies when k % 2048 == 0, w is 128-byte aligned and
- * the staged x of all m vectors (960 bytes per 256 elements per vector) plus
- * its line rings fit the LDS.  m = 1: that kernel when it applies and the
- * weights take at least 16 MiB, else the streaming kernel.  m > 1: the
- * sub-block kernel (6) for m >= 3, the line-streamed kernel (5) for m = 2,
- * the other of the two if only it fits, else the x-stager kernel.  With
- * kernel = 0 and another field set, m = 1 uses the streaming kernel and
- * m > 1 the x-stager.
+ * q4k_gemv_ex with every field 0 (automatic).  The line-streamed kernels
+ * (5, 6, 7) apply when k % 2048 == 0, w is 128-byte aligned and their staged
+ * x plus line rings fit the LDS.  m = 1: the line-streamed vector-ALU kernel
+ * (7; k <= 32768) when it applies and the weights take at least 16 MiB, else
+ * the streaming kernel; the matrix cores only when asked for.  m > 1: the
+ * sub-block kernel (6) for m >= 3, the line-streamed matrix-core kernel (5)
+ * for m = 2, the other of the two if only it fits, else the x-stager
+ * kernel.  With kernel = 0 and another field set, m = 1 uses the streaming
+ * kernel and m > 1 the x-stager.
  *
  * x is staged in LDS in spans of 4096 elements per vector.  The single-stage
  * variant holds all of x at once; the K-chunked variant stages
@@ -131,8 +131,10 @@ typedef struct q4k_launch {
                                  kernel (m = 1), 5 line-streamed int8 matrix-core
                                  kernel (m <= 8, k % 2048 == 0, w 128-byte aligned;
                                  m > 1: 8 waves and 3 lines in flight), 6 sub-block
-                                 int8 matrix-core kernel (as 5; 8 waves, 3 lines)    */
-    int32_t ring_depth;       /* kernels 2-5: loads in flight per wave, 0 auto;
+                                 int8 matrix-core kernel (as 5; 8 waves, 3 lines),
+                                 7 line-streamed vector-ALU kernel (m = 1, int8 dot
+                                 products; otherwise as 5)                          */
+    int32_t ring_depth;       /* kernels 2-5, 7: loads in flight per wave, 0 auto;
                                  streaming 1..4 rows; f16 matrix-core 1, 2 or 4
                                  steps; int8 matrix-core 1..3 columns; line-streamed
                                  3 or 9 lines                                        */

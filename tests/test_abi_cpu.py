@@ -105,8 +105,13 @@ def test_launch_struct_matches_header():
 def test_gemv_ex_kernel_option_refusals(lib):
     """Options that no kernel can honour are refused before any HIP call."""
     cases = [
-        (dict(kernel=7), 16, 2048, 1),
+        (dict(kernel=8), 16, 2048, 1),
         (dict(kernel=6), 16, 1024, 1),                       # k not a multiple of 2048
+        (dict(kernel=7), 16, 4096, 2),                       # vector-ALU lines: one vector
+        (dict(kernel=7), 16, 1024, 1),                       # k not a multiple of 2048
+        (dict(kernel=7, waves_per_block=16, ring_depth=9), 16, 4096, 1),
+        (dict(kernel=7, waves_per_block=8), 16, 65536, 1),   # x: four groups per lane at most
+        (dict(kernel=7, tiles_per_task=2), 16, 4096, 1),
         (dict(kernel=6, waves_per_block=4), 16, 4096, 2),    # eight waves only
         (dict(kernel=6, ring_depth=9), 16, 4096, 2),         # three lines in flight only
         (dict(kernel=-1), 16, 2048, 1),

@@ -339,6 +339,112 @@ def test_sub_kernel_workload(oracle_mod):
     assert_within(y, y_ref, bound, "sub-block workload 4")
 
 
+# line-streamed vector-ALU kernel (m = 1, k a multiple of 2048): integer dot
+# products with x broadcast across the tile's rows by DPP.  Its sums run in
+# the same order for every launch geometry with the same column grouping, so
+# those launches are bit-identical.
+DOT4_VARIANTS = [
+    dict(kernel=7),
+    dict(kernel=7, cols_per_task=8),
+    dict(kernel=7, waves_per_block=4, rows_per_block=48),
+    dict(kernel=7, waves_per_block=16, rows_per_block=320, cols_per_task=8),
+    dict(kernel=7, rows_per_block=40),
+    dict(kernel=7, waves_per_block=4, rows_per_block=16),
+    dict(kernel=7, ring_depth=9),
+    dict(kernel=7, ring_depth=9, cols_per_task=8, rows_per_block=16),
+    dict(kernel=7, ring_depth=9, waves_per_block=4, rows_per_block=80),
+]
+
+
+def _dot4_auto_cols(n, k, opts):
+    """Automatic column grouping of the vector-ALU line-streamed kernel:
+    whole rows for at least 1024 tiles or when the per-slab row sums do not
+    fit the LDS, else one slab of 8 columns."""
+    S = k // 256
+    ntiles = (n + 15) // 16
+    rpb = opts.get("rows_per_block") or 16 * ((ntiles + 255) // 256)
+    nw = opts.get("waves_per_block", 8)
+    fits = S * 1088 + nw * 4352 + (S // 8) * rpb * 4 <= 160 * 1024
+    return S if (ntiles >= 1024 or not fits) else 8
+
+
+def _dot4_check(w_d, x, n, k, y_ref, bound, what):
+    S = k // 256
+    firsts = {}
+    for opts in DOT4_VARIANTS:
+        _say("%s vector-ALU line-streamed %r" % (what, opts))
+        nw = opts.get("waves_per_block", 8)
+        try:
+            y = run_gemv(w_d, x, n, k, 1, **opts)
+        except q4k.Q4KError as e:
+            # refused: a task's column group must divide the slabs of a row,
+            # the staged x (1088 bytes per superblock column) plus the line
+            # rings (4352 bytes per wave) must fit the 160 KiB LDS, and x
+            # takes at most four 16-element groups per lane
+            bad_group = "cols_per_task" in opts and (S // 8) % (opts["cols_per_task"] // 8) != 0
+            too_big = S * 1088 + nw * 4352 > 160 * 1024 or S * 16 > 4 * 64 * nw
+            assert e.rc == q4k.Q4K_ERR_UNSUPPORTED and (bad_group or too_big), opts
+            continue
+        assert_within(y, y_ref, bound, "%s vector-ALU line-streamed %r" % (what, opts))
+        cpt = opts.get("cols_per_task") or _dot4_auto_cols(n, k, opts)
+        if cpt in firsts:
+            assert np.array_equal(y.view(np.uint32), firsts[cpt].view(np.uint32)), opts
+        else:
+            firsts[cpt] = y
+
+
+@pytest.mark.parametrize("i", [1, 2, 3])
+def test_dot4_kernel_workloads(oracle_mod, i):
+    wl, w, x, y_ref, bound = workload(i, oracle_mod)
+    _dot4_check(dev(w), x, wl.n, wl.k, y_ref, bound, "workload %d" % i)
+
+
+@pytest.mark.parametrize("n,k", [(1, 2048), (17, 4096), (130, 14336), (3, 65536), (257, 2048),
+                                 (33, 18432), (20, 24576)])
+def test_dot4_kernel_shapes(oracle_mod, n, k):
+    w, x = synth.make_inputs(n, k, 1, seed=n + 13 * k)
+    y_ref, bound = oracle_mod.gemv(w, x, n)
+    _dot4_check(dev(w), x, n, k, y_ref, bound, "n=%d k=%d" % (n, k))
+
+
+@pytest.mark.parametrize("n,k", [(64, 2048), (33, 4096)])
+def test_dot4_kernel_x_dynamic_range(oracle_mod, n, k):
+    rng = np.random.default_rng(n * k + 1)
+    w, _ = synth.make_inputs(n, k, 1, seed=n + k + 1)
+    xs = _x_cases(rng, k)
+    w_d = dev(w)
+    for b in range(xs.shape[0]):
+        x = xs[b:b + 1]
+        y_ref, bound = oracle_mod.gemv(w, x, n)
+        for opts in DOT4_VARIANTS[:2]:
+            _say("vector-ALU dynamic range n=%d k=%d case %d %r" % (n, k, b, opts))
+            y = run_gemv(w_d, x, n, k, 1, **opts)
+            assert_within(y, y_ref, bound, "vector-ALU x case %d %r" % (b, opts))
+
+
+def test_dot4_kernel_refusals():
+    """Shapes the vector-ALU line-streamed kernel cannot take are refused
+    without launching: several vectors, k not a multiple of 2048, rows not
+    128-byte aligned, x larger than four groups of 16 per lane."""
+    n = 8
+    w, x = synth.make_inputs(n, 2048, 2, seed=8)
+    y_d = torch.zeros((2, n), dtype=torch.float32, device="cuda")
+    with pytest.raises(q4k.Q4KError) as e:
+        q4k.q4k_gemv_ex(dev(w), dev(x), y_d, n, 2048, 2, kernel=7)
+    assert e.value.rc == q4k.Q4K_ERR_UNSUPPORTED
+    w_d = torch.zeros(w.size + 128, dtype=torch.uint8, device="cuda")
+    w_d[16:16 + w.size] = torch.from_numpy(w).cuda()
+    with pytest.raises(q4k.Q4KError) as e:
+        q4k.q4k_gemv_ex(w_d.data_ptr() + 16, dev(x[:1]), y_d, n, 2048, 1, kernel=7)
+    assert e.value.rc == q4k.Q4K_ERR_UNSUPPORTED
+    w2, x2 = synth.make_inputs(n, 65536, 1, seed=9)
+    with pytest.raises(q4k.Q4KError) as e:
+        q4k.q4k_gemv_ex(dev(w2), dev(x2), y_d, n, 65536, 1, kernel=7, waves_per_block=8)
+    assert e.value.rc == q4k.Q4K_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(y_d).item() == 0
+
+
 def test_sub_kernel_x_dynamic_range(oracle_mod):
     n, k = 40, 4096
     rng = np.random.default_rng(99)
