@@ -75,80 +75,13 @@ int device_lds_max(size_t* out)
     return Q4K_OK;
 }
 
-// Plan of the matrix-core kernel (m = 1).  A task is a group of superblock
-// columns times 1, 2 or 4 tiles of 16 rows; the automatic choice makes about
-// 4096 tasks (16 per CU of a 256-CU part) and gives every wave of a workgroup
-// one task per x stage.
-int make_plan_mfma(int64_t n, int64_t k, int kernel, const q4k_launch* o, GemvPlan* p)
-{
-    const int S = (int)(k / q4k::kQK);
-    const int nw = (o && o->waves_per_block) ? o->waves_per_block : 8;
-    const int tpt = (o && o->tiles_per_task) ? o->tiles_per_task : 1;
-    // ring: f16 kernel 1, 2 or 4 steps; int8 kernel 1, 2 or 3 columns in flight
-    const int ring = (o && o->ring_depth) ? o->ring_depth : 2;
-    const bool ring_ok = kernel == 4 ? (ring >= 1 && ring <= 3) : (ring == 1 || ring == 2 || ring == 4);
-    if ((nw != 4 && nw != 8) || (tpt != 1 && tpt != 2 && tpt != 4) || !ring_ok) {
-        return Q4K_ERR_UNSUPPORTED;
-    }
-    if (o && (o->cols_per_task < 0 || o->cols_per_chunk < 0 || o->rows_per_block < 0 ||
-              o->variant != 0 || o->spans_per_chunk != 0 || o->rows_per_wave != 0 ||
-              o->x_in_registers != 0 || o->rows_per_task != 0)) {
-        return Q4K_ERR_UNSUPPORTED;
-    }
-    const int64_t ntiles = (n + 15) / 16;
-    const int64_t ntg = (ntiles + tpt - 1) / tpt;
-    int64_t cpt = (o && o->cols_per_task) ? o->cols_per_task : ((int64_t)S * ntg + 4095) / 4096;
-    cpt = cpt < 1 ? 1 : cpt > S ? S : cpt;
-    const int64_t ncg = (S + cpt - 1) / cpt;
-    // x stage: the requested columns (whole tasks), else about 64 KiB
-    int64_t chunk_cols = (o && o->cols_per_chunk) ? o->cols_per_chunk
-                                                  : (64 * 1024) / (int64_t)q4k::mfma_col_bytes(kernel);
-    int64_t gpc = chunk_cols / cpt;
-    gpc = gpc < 1 ? 1 : gpc > ncg ? ncg : gpc;
-    int64_t rpb;
-    if (o && o->rows_per_block > 0) {
-        rpb = o->rows_per_block;
-    } else {
-        const int64_t tile_groups = nw > ncg ? nw / ncg : 1;
-        rpb = tile_groups * tpt * 16;
-    }
-    if (rpb > kInt32Max / (ncg > 1 ? ncg : 1)) {
-        return Q4K_ERR_SHAPE;
-    }
-    const int64_t grid = (n + rpb - 1) / rpb;
-    const int64_t cols_chunk = gpc * cpt < S ? gpc * cpt : S;
-    const size_t lds = q4k::mfma_lds_bytes(kernel, (int)cols_chunk) +
-                       (ncg > 1 ? (size_t)ncg * rpb * 4 : 0);
-
-    p->n = (int)n;
-    p->k = (int)k;
-    p->S = S;
-    p->m = 1;
-    p->nspans = (S + q4k::kSpanSB - 1) / q4k::kSpanSB;
-    p->spans_per_chunk = 0;
-    p->nchunks = (int)((ncg + gpc - 1) / gpc);
-    p->rows_per_block = (int)rpb;
-    p->rows_per_wave = 0;
-    p->waves_per_block = nw;
-    p->x_in_registers = 0;
-    p->grid = (int)grid;
-    p->lds_bytes = lds;
-    p->kernel = kernel;
-    p->ring_depth = ring;
-    p->rows_per_task = 0;
-    p->cols_per_task = (int)cpt;
-    p->tiles_per_task = tpt;
-    p->groups_per_chunk = (int)gpc;
-    return Q4K_OK;
-}
-
 // Plan of the line-streamed kernels (k a multiple of 2048, weights 128-byte
-// aligned, m <= 8): kernel 7 (m = 1, integer dot products on the vector
-// ALU), kernel 5 (one MFMA group per vector) and kernel 6 (one MFMA per
+// aligned, m <= 8): kernel 3 (m = 1, integer dot products on the vector
+// ALU), kernel 4 (one MFMA group per vector) and kernel 5 (one MFMA per
 // sub-block and quad of vectors).  A task is a 16-row tile times a group of
 // slabs of eight superblock columns; x (every vector) is staged whole.
 int make_plan_lines(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t lds_max,
-                    GemvPlan* p, int kernel = 5)
+                    GemvPlan* p, int kernel)
 {
     const int S = (int)(k / q4k::kQK);
     if (S % 8 != 0) {
@@ -161,7 +94,7 @@ int make_plan_lines(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t
     }
     if (o && (o->cols_per_task < 0 || o->rows_per_block < 0 || o->variant != 0 ||
               o->spans_per_chunk != 0 || o->rows_per_wave != 0 || o->x_in_registers != 0 ||
-              o->rows_per_task != 0 || o->tiles_per_task != 0 || o->cols_per_chunk != 0 ||
+              o->rows_per_task != 0 ||
               (o->ring_depth != 0 && o->ring_depth != 3 && o->ring_depth != 9))) {
         return Q4K_ERR_UNSUPPORTED;
     }
@@ -169,10 +102,10 @@ int make_plan_lines(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t
     if (nw == 16 && ring == 9) {
         return Q4K_ERR_UNSUPPORTED;    // 1024-lane workgroups cap a lane at 128 VGPRs
     }
-    if ((m > 1 || kernel == 6) && (nw != 8 || ring != 3)) {
+    if ((m > 1 || kernel == 5) && (nw != 8 || ring != 3)) {
         return Q4K_ERR_UNSUPPORTED;    // several vectors: eight waves, three lines in flight
     }
-    if (kernel == 7 && (m != 1 || S * 16 > 4 * 64 * nw)) {
+    if (kernel == 3 && (m != 1 || S * 16 > 4 * 64 * nw)) {
         return Q4K_ERR_UNSUPPORTED;    // one vector; x in at most four groups per lane
     }
     const int64_t ntiles = (n + 15) / 16;
@@ -191,8 +124,8 @@ int make_plan_lines(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t
         // all of x, which costs as much as decoding a few tiles
         rpb = 16 * ((ntiles + 255) / 256);
     }
-    const size_t lds_x = kernel == 6   ? q4k::sub_lds_bytes(S, (int)m)
-                         : kernel == 7 ? q4k::dot4_lds_bytes(S, nw)
+    const size_t lds_x = kernel == 5   ? q4k::sub_lds_bytes(S, (int)m)
+                         : kernel == 3 ? q4k::dot4_lds_bytes(S, nw)
                                        : q4k::lines_lds_bytes(S, (int)m, nw);
     if (!(o && o->cols_per_task)) {
         // whole rows per task when there are at least four tiles per CU of a
@@ -226,8 +159,6 @@ int make_plan_lines(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t
     p->ring_depth = ring;
     p->rows_per_task = 0;
     p->cols_per_task = (int)(spt * 8);
-    p->tiles_per_task = 1;
-    p->groups_per_chunk = 1;
     return Q4K_OK;
 }
 
@@ -237,18 +168,19 @@ int make_plan_lines(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t
 // The automatic kernel (choices measured on MI355X).  The line-streamed
 // kernels apply when k is a multiple of 2048, the weights are 128-byte
 // aligned and their LDS (x of every vector, the line rings) fits.  m > 1:
-// the sub-block kernel (m >= 3) or the per-vector line-streamed kernel
-// (m = 2), the other one if only it fits, else the x-stager kernel.  m = 1:
-// the line-streamed vector-ALU kernel (7) where it applies and the weights
-// take at least 16 MiB, else the streaming kernel, whose shorter start wins
-// on smaller matrices; m = 1 never takes the matrix cores unless asked to.
+// the sub-block kernel (5, m >= 3) or the per-vector line-streamed kernel
+// (4, m = 2), the other one if only it fits, else the x-stager kernel.
+// m = 1: the line-streamed vector-ALU kernel (3) where it applies and the
+// weights take at least 16 MiB, else the streaming kernel, whose shorter
+// start wins on smaller matrices; m = 1 takes the matrix cores only when
+// asked to.
 // Options other than `kernel` keep the earlier families: streaming for
 // m = 1, x-stager otherwise.
 bool any_option(const q4k_launch* o)
 {
     return o && (o->variant || o->spans_per_chunk || o->rows_per_block || o->rows_per_wave ||
                  o->waves_per_block || o->x_in_registers || o->ring_depth || o->rows_per_task ||
-                 o->cols_per_task || o->tiles_per_task || o->cols_per_chunk);
+                 o->cols_per_task);
 }
 
 int auto_kernel(int64_t n, int64_t k, int64_t m, const q4k_launch* o, bool w_aligned128,
@@ -259,8 +191,8 @@ int auto_kernel(int64_t n, int64_t k, int64_t m, const q4k_launch* o, bool w_ali
         // several vectors: a line-streamed kernel whenever one applies; the
         // sub-block kernel from three vectors on
         if (!any_option(o) && w_aligned128) {
-            const int first = m >= 3 ? 6 : 5;
-            for (int kern : {first, 11 - first}) {
+            const int first = m >= 3 ? 5 : 4;
+            for (int kern : {first, 9 - first}) {
                 if (make_plan_lines(n, k, m, nullptr, lds_max, &lp, kern) == Q4K_OK &&
                     lp.lds_bytes <= lds_max) {
                     return kern;
@@ -274,8 +206,8 @@ int auto_kernel(int64_t n, int64_t k, int64_t m, const q4k_launch* o, bool w_ali
     }
     const int64_t bytes = n * (k / q4k::kQK) * q4k::kBlockBytes;
     if (w_aligned128 && bytes >= ((int64_t)16 << 20) &&
-        make_plan_lines(n, k, 1, nullptr, lds_max, &lp, 7) == Q4K_OK && lp.lds_bytes <= lds_max) {
-        return 7;
+        make_plan_lines(n, k, 1, nullptr, lds_max, &lp, 3) == Q4K_OK && lp.lds_bytes <= lds_max) {
+        return 3;
     }
     return 2;
 }
@@ -306,17 +238,14 @@ int make_plan(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t lds_m
     const int nchunks = (nspans + spc - 1) / spc;
 
     const int kernel = (o && o->kernel) ? o->kernel : auto_kernel(n, k, m, o, w_aligned128, lds_max);
-    if (kernel < 1 || kernel > 7 || (((kernel >= 2 && kernel <= 4) || kernel == 7) && m != 1)) {
+    if (kernel < 1 || kernel > 5 || ((kernel == 2 || kernel == 3) && m != 1)) {
         return Q4K_ERR_UNSUPPORTED;
     }
-    if (kernel >= 5) {
+    if (kernel >= 3) {
         return make_plan_lines(n, k, m, o, lds_max, p, kernel);
     }
-    if (kernel >= 3) {
-        return make_plan_mfma(n, k, kernel, o, p);
-    }
-    if (o && (o->cols_per_task || o->tiles_per_task || o->cols_per_chunk)) {
-        return Q4K_ERR_UNSUPPORTED;   // matrix-core options only
+    if (o && o->cols_per_task) {
+        return Q4K_ERR_UNSUPPORTED;   // line-streamed kernels only
     }
     int nw = (o && o->waves_per_block) ? o->waves_per_block
                                        : (kernel == 2 ? (nspans > 8 ? 16 : 8) : 8);
@@ -421,8 +350,6 @@ int make_plan(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t lds_m
     p->ring_depth = ring_depth;
     p->rows_per_task = (int)rows_per_task;
     p->cols_per_task = 0;
-    p->tiles_per_task = 0;
-    p->groups_per_chunk = 0;
     return Q4K_OK;
 }
 
@@ -465,7 +392,7 @@ int gemv_checked(const void* w, const float* x, float* y, int64_t n, int64_t k, 
     if (plan.lds_bytes > lds_max) {
         return Q4K_ERR_UNSUPPORTED;
     }
-    if (plan.kernel >= 5 && (reinterpret_cast<uintptr_t>(w) & 127u) != 0) {
+    if (plan.kernel >= 3 && (reinterpret_cast<uintptr_t>(w) & 127u) != 0) {
         return Q4K_ERR_UNSUPPORTED;    // whole-line reads need 128-byte aligned rows
     }
     return hip_status(q4k::launch_gemv(plan, w, x, y, static_cast<hipStream_t>(stream)));

@@ -28,22 +28,18 @@ struct GemvPlan {
     int x_in_registers;    // 1: x kept in VGPRs (single span, m = 1)
     int grid;
     size_t lds_bytes;
-    int kernel;            // 1: x-stager, 2: streaming, 3: f16 matrix-core, 4: int8 matrix-core,
-                           // 5: line-streamed int8 matrix-core, 6: sub-block int8 matrix-core,
-                           // 7: line-streamed int8 dot products (vector ALU)
-    int ring_depth;        // kernels 2, 3: loads in flight per wave
+    int kernel;            // 1: x-stager, 2: streaming, 3: line-streamed int8 dot products
+                           // (vector ALU), 4: line-streamed int8 matrix-core,
+                           // 5: sub-block int8 matrix-core
+    int ring_depth;        // kernel 2: rows in flight per wave; 3-5: lines in flight
     int rows_per_task;     // streaming kernel: rows per wave task
-    int cols_per_task;     // matrix-core kernel: superblock columns per task
-    int tiles_per_task;    // matrix-core kernel: 16-row tiles per task (1, 2, 4)
-    int groups_per_chunk;  // matrix-core kernel: column groups per x stage
+    int cols_per_task;     // line-streamed kernels: superblock columns per task
 };
 
 hipError_t launch_gemv(const GemvPlan& p, const void* w, const float* x, float* y,
                        hipStream_t stream);
 hipError_t launch_gemv_mfma(const GemvPlan& p, const void* w, const float* x, float* y,
                             hipStream_t stream);
-size_t mfma_col_bytes(int kernel);
-size_t mfma_lds_bytes(int kernel, int cols_chunk);
 size_t lines_lds_bytes(int S, int m, int waves);
 size_t sub_lds_bytes(int S, int m);
 hipError_t launch_gemv_dot4(const GemvPlan& p, const void* w, const float* x, float* y,

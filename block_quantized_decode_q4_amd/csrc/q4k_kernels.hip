@@ -669,10 +669,10 @@ hipError_t launch_gemv(const GemvPlan& p, const void* w, const float* x, float* 
                        hipStream_t stream)
 {
     const uint8_t* wb = static_cast<const uint8_t*>(w);
-    if (p.kernel == 7) {
+    if (p.kernel == 3) {
         return launch_gemv_dot4(p, w, x, y, stream);
     }
-    if (p.kernel >= 3) {
+    if (p.kernel >= 4) {
         return launch_gemv_mfma(p, w, x, y, stream);
     }
     if (p.kernel == 2) {

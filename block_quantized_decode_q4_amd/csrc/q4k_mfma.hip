@@ -1,39 +1,16 @@
-// q4k_mfma.hip -- Q4_K GEMV on the CDNA4 matrix cores (v_mfma_f32_16x16x32_f16).
+// q4k_mfma.hip -- Q4_K GEMV for a small batch of vectors (m <= 8) on the
+// CDNA4 int8 matrix cores, fed by the line stream of q4k_lines.h.
 //
-// The multiply of the decode moves from the vector ALU to MFMA, which leaves
-// the VALU with the nibble unpack, the header decode and the per-superblock
-// scaling (about 1.3 lane-ops per weight instead of about 2.3).
-//
-// Operands of one MFMA (16 x 16 x 32): lane l = 16 g + j holds
-//   A[i = j][k = 8g .. 8g+7]  (8 halves),   B[k = 8g .. 8g+7][j]  (8 halves),
-//   D[i = 4g + r][j], r = 0..3.
-//
-//  * B = the 4-bit codes of 16 weight rows (j = row of the tile) for one
-//    32-element sub-block.  A code masked into mantissa bits 4..7 of an fp16
-//    is the subnormal q * 2^-20, exactly; the matrix core keeps these inputs
-//    (checked on MI355X: errors at f32-accumulation level; codes in bits 0..3
-//    lose precision there, so bits 4..7 are used for both nibbles).  Lane
-//    group g takes bytes 8g .. 8g+7 of each 32-byte chunk, so the k order of a
-//    sub-block is 8g + {0,2,1,3,4,6,5,7}; x is staged in the same order.
-//  * A = x, split into two fp16 halves x_hi + x_lo (about 22 bits), after a
-//    power-of-two scaling per 256-element column that maps the column's
-//    largest |x| into [2^13, 2^14).  For one vector, row i = 2s + v of A holds
-//    variant v of sub-block s and every other row is zero, so the eight MFMAs
-//    of a superblock accumulate into ONE D whose rows 4g..4g+3 are sub-blocks
-//    2g and 2g+1 (hi and lo parts) of row j -- exactly the sub-blocks whose
-//    scales lane (g, j) decodes (chunk g of the header).  The scaling is then
-//    lane-local:
-//      acc += d * 2^(20-sigma) * (sc_lo*(D0+D1) + sc_hi*(D2+D3))
-//             - dmin * (m_lo*X_lo + m_hi*X_hi)
-//    with X the f32 x sums of the two sub-blocks (staged once per x).
-//  * At the end of a task the four lane groups of a row are added (two
-//    cross-lane shuffles) and lanes 0..15 hold the 16 row totals.
-//
-// Work split: a task is (column group of cols_per_task superblock columns,
-// TPT tiles of 16 rows); waves take tasks round-robin; the x stage holds a
-// K-chunk of columns; per-column-group row sums meet in LDS when a row has
-// several column groups.  Loads of the next P (column, tile) steps are in
-// flight while a step is decoded.
+// With several vectors the same decoded weights meet m different x, which
+// makes the multiply a real (small) contraction: the matrix cores take it,
+// and the vector ALU keeps the nibble unpack, the header decode and the
+// per-superblock scaling.  Two kernels:
+//  * gemv_i8_lines_kernel<NW, P, XC, M>: four v_mfma_i32_16x16x64_i8 per
+//    superblock and vector (one 16-row tile, one vector per MFMA group);
+//    automatic for m = 2.  With m = 1 it runs only when asked for, as the
+//    measured matrix-core counterpart of the vector-ALU kernel (q4k_dpp.hip).
+//  * gemv_i8_sub_kernel<NW, XC, NQ>: one v_mfma_i32_16x16x32_i8 per
+//    32-element sub-block and quad of vectors; automatic for m >= 3.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -43,93 +20,6 @@
 #include "q4k_lines.h"
 
 namespace q4k {
-
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-// Bytes of the staged x per superblock column: x_hi and x_lo (256 halves
-// each), eight sub-block sums and one scale.
-constexpr int kMfmaColBytes = 256 * 2 * 2 + 8 * 4 + 4;
-
-struct TileCodes {
-    uint4 h;        // the lane's row header
-    uint2 q[4];     // bytes 8g .. 8g+7 of chunk c, c = 0..3
-};
-
-__device__ __forceinline__ TileCodes load_tile(const uint8_t* p, int g)
-{
-    TileCodes t;
-    t.h = *reinterpret_cast<const uint4*>(p);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        t.q[c] = *reinterpret_cast<const uint2*>(p + 16 + 32 * c + 8 * g);
-    }
-    return t;
-}
-
-__device__ __forceinline__ float wave_max_all(float v)
-{
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        v = fmaxf(v, __shfl_xor(v, off, 64));
-    }
-    return v;
-}
-
-// Stage superblock columns [col0, col0 + nc) of x: one wave per column, lane
-// l takes elements 4l .. 4l+3.  Writes x_hi / x_lo (quads in order
-// 0,2,1,3), the eight sub-block sums (f32, unscaled) and 2^(20-sigma).
-__device__ __forceinline__ void stage_x_mfma(const float* __restrict__ x, int S, int col0, int nc,
-                                             _Float16* xh, _Float16* xl, float* xsum,
-                                             float* xscale, int lane, int wave, int nw)
-{
-    for (int cl = wave; cl < nc; cl += nw) {
-        const int col = col0 + cl;
-        float4 g = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (col < S) {
-            g = *reinterpret_cast<const float4*>(x + (size_t)col * 256 + 4 * lane);
-        }
-        float m = fmaxf(fmaxf(fabsf(g.x), fabsf(g.y)), fmaxf(fabsf(g.z), fabsf(g.w)));
-        m = wave_max_all(m);
-        // sigma: the column maximum lands in [2^13, 2^14); a zero column keeps
-        // 0.  The clamp keeps 2^sigma and 2^(20-sigma) finite f32 values, so
-        // columns whose largest |x| is 2^120 or more overflow the f16 halves.
-        int sigma = 0;
-        if (m > 0.f) {
-            int e = 0;
-            (void)frexpf(m, &e);                 // m = f * 2^e, f in [0.5, 1)
-            sigma = 14 - e;
-            sigma = sigma < -106 ? -106 : sigma > 126 ? 126 : sigma;
-        }
-        const float up = ldexpf(1.0f, sigma);
-        const float vals[4] = {g.x, g.z, g.y, g.w};
-        half4_t hi, lo;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const float v = vals[t] * up;
-            const _Float16 h = (_Float16)v;
-            hi[t] = h;
-            lo[t] = (_Float16)(v - (float)h);
-        }
-        *reinterpret_cast<half4_t*>(xh + cl * 256 + 4 * lane) = hi;
-        *reinterpret_cast<half4_t*>(xl + cl * 256 + 4 * lane) = lo;
-        // sum of each 32-element sub-block = 8 lanes
-        float s4 = (g.x + g.y) + (g.z + g.w);
-        s4 += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                  0, __builtin_bit_cast(int, s4), 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
-        s4 += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                  0, __builtin_bit_cast(int, s4), 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
-        s4 += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                  0, __builtin_bit_cast(int, s4), 0x141, 0xF, 0xF, false));  // row_half_mirror
-        if ((lane & 7) == 0) {
-            xsum[cl * 8 + (lane >> 3)] = s4;
-        }
-        if (lane == 0) {
-            xscale[cl] = ldexpf(1.0f, 20 - sigma);
-        }
-    }
-}
 
 // Scales of chunk g (sub-blocks 2g, 2g+1) of a header; d unscaled.
 struct ChunkScalesD {
@@ -156,174 +46,8 @@ __device__ __forceinline__ ChunkScalesD decode_chunk(const uint4& h, uint32_t sh
     return s;
 }
 
-// The eight MFMAs of one (tile, column) step; returns the lane's partial.
-__device__ __forceinline__ float mfma_step(const TileCodes& cur, const half8_t* A, float xsc,
-                                           float X_lo, float X_hi, uint32_t sh, uint32_t sel)
-{
-    f32x4_t D = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const uint32_t d0 = cur.q[c].x;
-        const uint32_t d1 = cur.q[c].y;
-        const u32x4_t lo = {(d0 << 4) & 0x00F000F0u, (d0 >> 4) & 0x00F000F0u,
-                            (d1 << 4) & 0x00F000F0u, (d1 >> 4) & 0x00F000F0u};
-        const u32x4_t hi = {d0 & 0x00F000F0u, (d0 >> 8) & 0x00F000F0u,
-                            d1 & 0x00F000F0u, (d1 >> 8) & 0x00F000F0u};
-        D = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[2 * c], __builtin_bit_cast(half8_t, lo), D,
-                                                   0, 0, 0);
-        D = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[2 * c + 1], __builtin_bit_cast(half8_t, hi),
-                                                   D, 0, 0, 0);
-    }
-    const ChunkScalesD s = decode_chunk(cur.h, sh, sel);
-    float t1 = s.sc_lo * (D[0] + D[1]);
-    t1 = __builtin_fmaf(s.sc_hi, D[2] + D[3], t1);
-    float t2 = s.m_lo * X_lo;
-    t2 = __builtin_fmaf(s.m_hi, X_hi, t2);
-    const float acc = (s.d * xsc) * t1;
-    return __builtin_fmaf(-s.dmin, t2, acc);
-}
-
-template <int NW, int TPT, int P>
-__global__ void __launch_bounds__(NW * 64)
-gemv_mfma1_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
-                  float* __restrict__ y, int n, int S, int rows_per_block, int cols_per_task,
-                  int groups_per_chunk)
-{
-    static_assert(P == 1 || P == 2 || P == 4, "prefetch depth");
-    static_assert(TPT == 1 || TPT == 2 || TPT == 4, "tiles per task");
-    constexpr int UC = P > TPT ? P / TPT : 1;          // columns per unrolled block
-    static_assert((UC * TPT) % P == 0, "prefetch slots must repeat per block");
-
-    extern __shared__ __align__(16) unsigned char smem[];
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int g = lane >> 4;
-    const int j = lane & 15;
-    const int s_l = j >> 1;        // sub-block whose A row this lane feeds
-    const int v_l = j & 1;         // 0: x_hi, 1: x_lo
-    const uint32_t sh = (uint32_t)(g & 1) * 16u;
-    const uint32_t sel = g < 2 ? 0xFFFFFFFFu : 0u;
-
-    const int row0 = blockIdx.x * rows_per_block;
-    const int rows_here = min(rows_per_block, n - row0);
-    const int ntiles = (rows_here + 15) >> 4;
-    const int ntg = (ntiles + TPT - 1) / TPT;
-    const int ncg_total = (S + cols_per_task - 1) / cols_per_task;
-    const int nchunks = (ncg_total + groups_per_chunk - 1) / groups_per_chunk;
-    const int cols_chunk = min(groups_per_chunk * cols_per_task, S);
-    const size_t row_bytes = (size_t)S * 144;
-
-    _Float16* xh = reinterpret_cast<_Float16*>(smem);
-    _Float16* xl = xh + cols_chunk * 256;
-    float* xsum = reinterpret_cast<float*>(xl + cols_chunk * 256);
-    float* xscale = xsum + cols_chunk * 8;
-    float* ypart = xscale + ((cols_chunk + 3) & ~3);
-
-    for (int ch = 0; ch < nchunks; ++ch) {
-        const int cg0 = ch * groups_per_chunk;
-        const int ncg = min(groups_per_chunk, ncg_total - cg0);
-        const int col0 = cg0 * cols_per_task;
-        const int ncols = min(ncg * cols_per_task, S - col0);
-        const int ntasks = ncg * ntg;
-        if (ch > 0) {
-            __syncthreads();
-        }
-        stage_x_mfma(x, S, col0, ncols, xh, xl, xsum, xscale, lane, wave, NW);
-        __syncthreads();
-
-        for (int task = wave; task < ntasks; task += NW) {
-            const int cgl = task % ncg;
-            const int tile0 = (task / ncg) * TPT;
-            const int c_begin = col0 + cgl * cols_per_task;
-            const int c_end = min(c_begin + cols_per_task, S);
-
-            // row of each tile this lane loads (clamped into the block)
-            const uint8_t* rowp[TPT];
-#pragma unroll
-            for (int t = 0; t < TPT; ++t) {
-                const int r = min((tile0 + t) * 16 + j, rows_here - 1);
-                rowp[t] = w + (size_t)(row0 + r) * row_bytes;
-            }
-            // step s of a task is (column c_begin + s / TPT, tile s % TPT);
-            // prefetches past the last column re-read the last one
-            TileCodes buf[P];
-#pragma unroll
-            for (int p = 0; p < P; ++p) {
-                const int col = min(c_begin + p / TPT, c_end - 1);
-                buf[p] = load_tile(rowp[p % TPT] + (size_t)col * 144, g);
-            }
-            float acc[TPT];
-#pragma unroll
-            for (int t = 0; t < TPT; ++t) {
-                acc[t] = 0.f;
-            }
-            half8_t A[8];
-#pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                A[s] = half8_t{0, 0, 0, 0, 0, 0, 0, 0};
-            }
-
-            for (int col = c_begin; col < c_end; col += UC) {
-#pragma unroll
-                for (int uc = 0; uc < UC; ++uc) {
-                    const int cc = col + uc;
-                    const bool live = cc < c_end;
-                    const int cl = min(cc, c_end - 1) - col0;
-                    // A rows for this column: lane feeds row 2 s_l + v_l only
-                    const _Float16* src = (v_l ? xl : xh) + cl * 256 + 32 * s_l + 8 * g;
-                    const half8_t xa = *reinterpret_cast<const half8_t*>(src);
-#pragma unroll
-                    for (int s = 0; s < 8; ++s) {
-                        A[s] = s_l == s ? xa : half8_t{0, 0, 0, 0, 0, 0, 0, 0};
-                    }
-                    const float2 X = *reinterpret_cast<const float2*>(xsum + cl * 8 + 2 * g);
-                    const float xsc = xscale[cl];
-#pragma unroll
-                    for (int t = 0; t < TPT; ++t) {
-                        const int slot = (uc * TPT + t) % P;
-                        const float part = mfma_step(buf[slot], A, xsc, X.x, X.y, sh, sel);
-                        acc[t] += live ? part : 0.f;
-                        // the slot is refilled only after its last use, so the
-                        // load lands in the same registers (no copy that would
-                        // wait for it) and stays in flight for P - 1 steps
-                        __builtin_amdgcn_sched_barrier(0);
-                        const int pcol = min(cc + (t + P) / TPT, c_end - 1);
-                        buf[slot] = load_tile(rowp[(t + P) % TPT] + (size_t)pcol * 144, g);
-                    }
-                }
-            }
-            // the four lane groups of a row, then lanes 0..15 store the tile
-#pragma unroll
-            for (int t = 0; t < TPT; ++t) {
-                float v = acc[t];
-                v += __shfl_xor(v, 16, 64);
-                v += __shfl_xor(v, 32, 64);
-                const int r = (tile0 + t) * 16 + j;
-                if (g == 0 && r < rows_here) {
-                    if (ncg_total == 1) {
-                        y[row0 + r] = v;
-                    } else {
-                        ypart[(cg0 + cgl) * rows_per_block + r] = v;
-                    }
-                }
-            }
-        }
-    }
-    if (ncg_total > 1) {
-        __syncthreads();
-        for (int r = tid; r < rows_here; r += NW * 64) {
-            float acc = 0.f;
-            for (int cg = 0; cg < ncg_total; ++cg) {
-                acc += ypart[cg * rows_per_block + r];
-            }
-            y[row0 + r] = acc;
-        }
-    }
-}
-
 // ---------------------------------------------------------------------------
-// int8 matrix-core kernel (v_mfma_i32_16x16x64_i8).
+// int8 matrix-core decode (v_mfma_i32_16x16x64_i8).
 //
 // Operands of one MFMA (16 x 16 x 64): lane l = 16 g + j holds
 //   A[i = j][k = 16g .. 16g+15] (16 bytes), B[k = 16g .. 16g+15][j], D[4g + r][j].
@@ -362,108 +86,14 @@ constexpr int kI8ColA = 4 * kI8MuBytes;         // four MFMA operands per column
 constexpr int kI8ColConst = 4 * 32;             // eight floats per lane group
 constexpr int kI8ColBytes = kI8ColA + kI8ColConst;
 
-// Reductions over aligned groups of 8 lanes (one sub-block of x): DPP
-// quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror.
-__device__ __forceinline__ float max8(float v)
-{
-    v = fmaxf(v, __builtin_bit_cast(float, dpp_i<0xB1>(__builtin_bit_cast(int, v))));
-    v = fmaxf(v, __builtin_bit_cast(float, dpp_i<0x4E>(__builtin_bit_cast(int, v))));
-    return fmaxf(v, __builtin_bit_cast(float, dpp_i<0x141>(__builtin_bit_cast(int, v))));
-}
-
-__device__ __forceinline__ float sum8(float v)
-{
-    v += __builtin_bit_cast(float, dpp_i<0xB1>(__builtin_bit_cast(int, v)));
-    v += __builtin_bit_cast(float, dpp_i<0x4E>(__builtin_bit_cast(int, v)));
-    return v + __builtin_bit_cast(float, dpp_i<0x141>(__builtin_bit_cast(int, v)));
-}
-
-__device__ __forceinline__ uint32_t sum8(uint32_t v)
-{
-    v += (uint32_t)dpp_i<0xB1>((int)v);
-    v += (uint32_t)dpp_i<0x4E>((int)v);
-    return v + (uint32_t)dpp_i<0x141>((int)v);
-}
-
-__device__ __forceinline__ int sum8(int v)
-{
-    v += dpp_i<0xB1>(v);
-    v += dpp_i<0x4E>(v);
-    return v + dpp_i<0x141>(v);
-}
-
-// Convert one superblock column of x (lane l holds elements 4l .. 4l+3,
-// sub-block l / 8) into its matrix-core operands and constants at `col`.
-__device__ __forceinline__ void convert_col_i8(const float4& v, unsigned char* col, int lane)
-{
-    const int s = lane >> 3;                  // sub-block
-    const int e_in = 4 * (lane & 7);          // first element within it
-    const int g = s >> 1;
-    const int mu = 2 * (s & 1) + (e_in >= 16 ? 1 : 0);
-    const float m = max8(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)),
-                               fmaxf(fabsf(v.z), fabsf(v.w))));
-    // sigma puts the sub-block's largest |x| in [2^21, 2^22); a zero
-    // sub-block keeps 0.  2^sigma and 2^-sigma stay normal f32 values.
-    int sigma = 0;
-    if (m > 0.f) {
-        sigma = 22 - __builtin_amdgcn_frexp_expf(m);   // m = f * 2^e, f in [0.5, 1)
-        sigma = sigma < -126 ? -126 : sigma > 126 ? 126 : sigma;
-    }
-    const float scale = __builtin_bit_cast(float, (uint32_t)(sigma + 127) << 23);
-    // xi = rint(x * 2^sigma), |xi| <= 2^22: the product is exact and
-    // adding 1.5 * 2^23 in the same fused operation rounds it to an
-    // integer once; the low bits of the sum hold xi + 2^22 + 2^23.
-    // u = xi + 0x808080 then has the base-256 digits d_l + 128 of the
-    // balanced digits d_l in [-128, 127] of xi, so byte l of u, with
-    // its top bit flipped, is digit l as a signed byte.
-    const float vals[4] = {v.x, v.y, v.z, v.w};
-    uint32_t u[4];
-    uint32_t usum = 0;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        u[t] = __builtin_bit_cast(uint32_t, __builtin_fmaf(vals[t], scale, 12582912.0f)) -
-               0x4ABF7F80u;
-        usum += u[t];
-    }
-    // byte planes: plane l holds byte l of u[0..3]
-    const uint32_t lo01 = __builtin_amdgcn_perm(u[1], u[0], 0x05010400u);  // u0b0 u1b0 u0b1 u1b1
-    const uint32_t lo23 = __builtin_amdgcn_perm(u[3], u[2], 0x05010400u);
-    const uint32_t hi01 = __builtin_amdgcn_perm(u[1], u[0], 0x07030602u);  // u0b2 u1b2 u0b3 u1b3
-    const uint32_t hi23 = __builtin_amdgcn_perm(u[3], u[2], 0x07030602u);
-    const uint32_t dig0 = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u) ^ 0x80808080u;
-    const uint32_t dig1 = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u) ^ 0x80808080u;
-    const uint32_t dig2 = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u) ^ 0x80808080u;
-    unsigned char* slot = col + mu * kI8MuBytes + g * 48 + (e_in & 15);
-    *reinterpret_cast<uint32_t*>(slot) = dig0;
-    *reinterpret_cast<uint32_t*>(slot + 16) = dig1;
-    *reinterpret_cast<uint32_t*>(slot + 32) = dig2;
-    if (lane < 4) {
-        *reinterpret_cast<uint4*>(col + lane * kI8MuBytes + kI8ZeroSlot) =
-            make_uint4(0, 0, 0, 0);
-    }
-    // integer x sum of the sub-block (32 elements, below 2^29)
-    const int XI = (int)sum8(usum) - 32 * 0x808080;
-    if ((lane & 7) == 0) {
-        float* c = reinterpret_cast<float*>(col + kI8ColA + g * 32);
-        const float inv = __builtin_bit_cast(float, (uint32_t)(127 - sigma) << 23);
-        const float xq = inv * (float)XI;         // sum of the quantized x
-        if ((s & 1) == 0) {
-            c[0] = inv;
-            c[3] = xq;
-        } else {
-            c[1] = inv * 0.0625f;
-            c[2] = 8.0f * xq;
-            c[4] = xq;
-        }
-    }
-}
-
 // Convert four (column, vector) pairs at once, one per 16-lane group: lane
 // l takes elements 16 (l % 16) .. 16 (l % 16) + 15 of its pair, half of a
 // sub-block, so each lane writes three whole 16-byte digit slots and the
 // per-lane costs (largest |x|, scale, sums) are shared by 16 elements.
-// `col` is the LDS slot of the lane's pair.  Produces exactly the bytes and
-// constants of convert_col_i8.
+// `col` is the LDS slot of the lane's pair: 12 digit slots of 16 bytes per
+// MFMA operand mu (digit l of the 16 elements of k-group g at slot 3 g + l,
+// a zero slot after them) and the constants {2^-s, 2^-s / 16, 8 X, X_lo,
+// X_hi} of each lane group's two sub-blocks.
 __device__ __forceinline__ void convert4_i8(const float4 (&v)[4], unsigned char* col, int lane)
 {
     const int le = lane & 15;
@@ -542,48 +172,10 @@ __device__ __forceinline__ void load_x_quarter(const float* __restrict__ x, int 
     }
 }
 
-__device__ __forceinline__ float4 load_x_col(const float* __restrict__ x, int col, int lane)
-{
-    return *reinterpret_cast<const float4*>(x + (size_t)col * 256 + 4 * lane);
-}
-
-// Stage superblock columns [col0, col0 + nc) of x: one wave per column; the
-// x loads of up to MAXC of the wave's columns go out before the first is
-// converted.
-template <int MAXC>
-__device__ __forceinline__ void stage_x_i8(const float* __restrict__ x, int col0, int nc,
-                                           unsigned char* lds, int lane, int wave, int nw)
-{
-    for (int cl0 = wave; cl0 < nc; cl0 += nw * MAXC) {
-        float4 v[MAXC];
-#pragma unroll
-        for (int i = 0; i < MAXC; ++i) {
-            v[i] = load_x_col(x, col0 + min(cl0 + i * nw, nc - 1), lane);
-        }
-#pragma unroll
-        for (int i = 0; i < MAXC; ++i) {
-            const int cl = cl0 + i * nw;
-            if (cl >= nc) {
-                break;
-            }
-            convert_col_i8(v[i], lds + cl * kI8ColBytes, lane);
-        }
-    }
-}
-
 struct TileI8 {
     uint4 h;       // the lane's row header
     uint4 q0, q1;  // chunk g of the row: code bytes 0-15 and 16-31
 };
-
-__device__ __forceinline__ TileI8 load_tile_i8(const uint8_t* p, int g)
-{
-    TileI8 t;
-    t.h = *reinterpret_cast<const uint4*>(p);
-    t.q0 = *reinterpret_cast<const uint4*>(p + 16 + 32 * g);
-    t.q1 = *reinterpret_cast<const uint4*>(p + 32 + 32 * g);
-    return t;
-}
 
 struct ColI8 {
     i32x4_t a[4];     // MFMA A operands of the column
@@ -657,146 +249,6 @@ __device__ __forceinline__ float step_vector(const StepW& t, const ColI8& col)
     float t2 = t.s.m_lo * col.xlo;
     t2 = __builtin_fmaf(t.s.m_hi, col.xhi, t2);
     return __builtin_fmaf(-t.s.dmin, t2, t.s.d * t1);
-}
-
-// One (tile, column) step for one vector.
-__device__ __forceinline__ float i8_step(const TileI8& cur, const ColI8& col, uint32_t sh,
-                                         uint32_t sel)
-{
-    return step_vector(step_weights(cur, sh, sel), col);
-}
-
-// Tasks: (column group, TPT tiles of 16 rows).  A ring holds the tiles of
-// UC columns: each slot is decoded, then refilled with the same tiles UC
-// columns further on, so UC columns of loads stay in flight.  The first
-// task's loads go out before the x stage.
-template <int NW, int TPT, int UC>
-__global__ void __launch_bounds__(NW * 64)
-gemv_mfma_i8_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
-                    float* __restrict__ y, int n, int S, int rows_per_block, int cols_per_task,
-                    int groups_per_chunk)
-{
-    extern __shared__ __align__(16) unsigned char smem[];
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int g = lane >> 4;
-    const int j = lane & 15;
-    const bool active = (j >> 2) == g && (j & 3) < 3;
-    const uint32_t a_off = active ? (uint32_t)((g * 3 + (j & 3)) * 16) : (uint32_t)kI8ZeroSlot;
-    const uint32_t sh = (uint32_t)(g & 1) * 16u;
-    const uint32_t sel = g < 2 ? 0xFFFFFFFFu : 0u;
-
-    const int row0 = blockIdx.x * rows_per_block;
-    const int rows_here = min(rows_per_block, n - row0);
-    const int ntiles = (rows_here + 15) >> 4;
-    const int ntg = (ntiles + TPT - 1) / TPT;
-    const int ncg_total = (S + cols_per_task - 1) / cols_per_task;
-    const int nchunks = (ncg_total + groups_per_chunk - 1) / groups_per_chunk;
-    const int cols_chunk = min(groups_per_chunk * cols_per_task, S);
-    const size_t row_bytes = (size_t)S * 144;
-    float* ypart = reinterpret_cast<float*>(smem + (size_t)cols_chunk * kI8ColBytes);
-
-    for (int ch = 0; ch < nchunks; ++ch) {
-        const int cg0 = ch * groups_per_chunk;
-        const int ncg = min(groups_per_chunk, ncg_total - cg0);
-        const int col0 = cg0 * cols_per_task;
-        const int ncols = min(ncg * cols_per_task, S - col0);
-        const int ntasks = ncg * ntg;
-
-        TileI8 buf[UC][TPT];
-        int task = wave;
-        auto task_rows = [&](int tk, const uint8_t** rowp) {
-            const int tile0 = (tk / ncg) * TPT;
-#pragma unroll
-            for (int t = 0; t < TPT; ++t) {
-                const int r = min((tile0 + t) * 16 + j, rows_here - 1);
-                rowp[t] = w + (size_t)(row0 + r) * row_bytes;
-            }
-        };
-        auto fill = [&](const uint8_t* const* rowp, int c_begin, int c_end) {
-#pragma unroll
-            for (int u = 0; u < UC; ++u) {
-                const int cc = min(c_begin + u, c_end - 1);
-#pragma unroll
-                for (int t = 0; t < TPT; ++t) {
-                    buf[u][t] = load_tile_i8(rowp[t] + (size_t)cc * 144, g);
-                }
-            }
-        };
-        if (task < ntasks) {
-            const uint8_t* rowp[TPT];
-            task_rows(task, rowp);
-            const int c_begin = col0 + (task % ncg) * cols_per_task;
-            fill(rowp, c_begin, min(c_begin + cols_per_task, S));
-        }
-        if (ch > 0) {
-            __syncthreads();
-        }
-        stage_x_i8<4>(x, col0, ncols, smem, lane, wave, NW);
-        __syncthreads();
-
-        for (; task < ntasks; task += NW) {
-            const int cgl = task % ncg;
-            const int tile0 = (task / ncg) * TPT;
-            const int c_begin = col0 + cgl * cols_per_task;
-            const int c_end = min(c_begin + cols_per_task, S);
-            const uint8_t* rowp[TPT];
-            task_rows(task, rowp);
-            if (task != wave) {
-                fill(rowp, c_begin, c_end);
-            }
-            float acc[TPT];
-#pragma unroll
-            for (int t = 0; t < TPT; ++t) {
-                acc[t] = 0.f;
-            }
-            for (int c = c_begin; c < c_end; c += UC) {
-#pragma unroll
-                for (int u = 0; u < UC; ++u) {
-                    const int cc = min(c + u, c_end - 1);
-                    const bool live = c + u < c_end;
-                    const ColI8 col = read_col_i8(smem + (cc - col0) * kI8ColBytes, a_off, g);
-                    const int nc = min(c + u + UC, c_end - 1);
-#pragma unroll
-                    for (int t = 0; t < TPT; ++t) {
-                        const float part = i8_step(buf[u][t], col, sh, sel);
-                        acc[t] += live ? part : 0.f;
-                        // refill after the last use: the load lands in the
-                        // registers just read, so it needs no copy (which
-                        // would wait for it) and stays in flight for UC - 1
-                        // columns
-                        __builtin_amdgcn_sched_barrier(0);
-                        buf[u][t] = load_tile_i8(rowp[t] + (size_t)nc * 144, g);
-                    }
-                }
-            }
-#pragma unroll
-            for (int t = 0; t < TPT; ++t) {
-                float v = acc[t];
-                v += __shfl_xor(v, 16, 64);
-                v += __shfl_xor(v, 32, 64);
-                const int r = (tile0 + t) * 16 + j;
-                if (g == 0 && r < rows_here) {
-                    if (ncg_total == 1) {
-                        y[row0 + r] = v;
-                    } else {
-                        ypart[(cg0 + cgl) * rows_per_block + r] = v;
-                    }
-                }
-            }
-        }
-    }
-    if (ncg_total > 1) {
-        __syncthreads();
-        for (int r = tid; r < rows_here; r += NW * 64) {
-            float acc = 0.f;
-            for (int cg = 0; cg < ncg_total; ++cg) {
-                acc += ypart[cg * rows_per_block + r];
-            }
-            y[row0 + r] = acc;
-        }
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1241,96 +693,27 @@ static hipError_t launch_lines_m(const GemvPlan& p, const uint8_t* w, const floa
     return launch_lines_x<8, 3, 4, M>(p, w, x, y, stream);
 }
 
-template <int NW, int TPT, int UC>
-static hipError_t launch_i8(const GemvPlan& p, const uint8_t* w, const float* x, float* y,
-                            hipStream_t stream)
-{
-    hipLaunchKernelGGL((gemv_mfma_i8_kernel<NW, TPT, UC>), dim3(p.grid), dim3(NW * 64),
-                       p.lds_bytes, stream, w, x, y, p.n, p.S, p.rows_per_block,
-                       p.cols_per_task, p.groups_per_chunk);
-    return hipGetLastError();
-}
-
-template <int NW, int TPT>
-static hipError_t launch_i8_u(const GemvPlan& p, const uint8_t* w, const float* x, float* y,
-                              hipStream_t stream)
-{
-    if (p.ring_depth == 1) return launch_i8<NW, TPT, 1>(p, w, x, y, stream);
-    if (p.ring_depth == 2) return launch_i8<NW, TPT, 2>(p, w, x, y, stream);
-    return launch_i8<NW, TPT, 3>(p, w, x, y, stream);
-}
-
-template <int NW>
-static hipError_t launch_i8_t(const GemvPlan& p, const uint8_t* w, const float* x, float* y,
-                              hipStream_t stream)
-{
-    if (p.tiles_per_task == 1) return launch_i8_u<NW, 1>(p, w, x, y, stream);
-    if (p.tiles_per_task == 2) return launch_i8_u<NW, 2>(p, w, x, y, stream);
-    return launch_i8_u<NW, 4>(p, w, x, y, stream);
-}
-
-template <int NW, int TPT, int P>
-static hipError_t launch_mfma1(const GemvPlan& p, const uint8_t* w, const float* x, float* y,
-                               hipStream_t stream)
-{
-    hipLaunchKernelGGL((gemv_mfma1_kernel<NW, TPT, P>), dim3(p.grid), dim3(NW * 64),
-                       p.lds_bytes, stream, w, x, y, p.n, p.S, p.rows_per_block,
-                       p.cols_per_task, p.groups_per_chunk);
-    return hipGetLastError();
-}
-
-template <int NW, int TPT>
-static hipError_t launch_mfma1_p(const GemvPlan& p, const uint8_t* w, const float* x, float* y,
-                                 hipStream_t stream)
-{
-    if (p.ring_depth == 1) return launch_mfma1<NW, TPT, 1>(p, w, x, y, stream);
-    if (p.ring_depth == 2) return launch_mfma1<NW, TPT, 2>(p, w, x, y, stream);
-    return launch_mfma1<NW, TPT, 4>(p, w, x, y, stream);
-}
-
-template <int NW>
-static hipError_t launch_mfma1_t(const GemvPlan& p, const uint8_t* w, const float* x, float* y,
-                                 hipStream_t stream)
-{
-    if (p.tiles_per_task == 1) return launch_mfma1_p<NW, 1>(p, w, x, y, stream);
-    if (p.tiles_per_task == 2) return launch_mfma1_p<NW, 2>(p, w, x, y, stream);
-    return launch_mfma1_p<NW, 4>(p, w, x, y, stream);
-}
-
 hipError_t launch_gemv_mfma(const GemvPlan& p, const void* w, const float* x, float* y,
                             hipStream_t stream)
 {
     const uint8_t* wb = static_cast<const uint8_t*>(w);
-    if (p.kernel == 6) {
+    if (p.kernel == 5) {
         if (p.m > 4) return launch_sub<2>(p, wb, x, y, stream);
         return launch_sub<1>(p, wb, x, y, stream);
     }
-    if (p.kernel == 5) {
-        switch (p.m) {
-        case 1: break;
-        case 2: return launch_lines_m<2>(p, wb, x, y, stream);
-        case 3: return launch_lines_m<3>(p, wb, x, y, stream);
-        case 4: return launch_lines_m<4>(p, wb, x, y, stream);
-        case 5: return launch_lines_m<5>(p, wb, x, y, stream);
-        case 6: return launch_lines_m<6>(p, wb, x, y, stream);
-        case 7: return launch_lines_m<7>(p, wb, x, y, stream);
-        default: return launch_lines_m<8>(p, wb, x, y, stream);
-        }
-        if (p.waves_per_block == 8) return launch_lines<8>(p, wb, x, y, stream);
-        if (p.waves_per_block == 16) return launch_lines_p<16, 3>(p, wb, x, y, stream);
-        return launch_lines<4>(p, wb, x, y, stream);
+    switch (p.m) {
+    case 1: break;
+    case 2: return launch_lines_m<2>(p, wb, x, y, stream);
+    case 3: return launch_lines_m<3>(p, wb, x, y, stream);
+    case 4: return launch_lines_m<4>(p, wb, x, y, stream);
+    case 5: return launch_lines_m<5>(p, wb, x, y, stream);
+    case 6: return launch_lines_m<6>(p, wb, x, y, stream);
+    case 7: return launch_lines_m<7>(p, wb, x, y, stream);
+    default: return launch_lines_m<8>(p, wb, x, y, stream);
     }
-    if (p.kernel == 4) {
-        if (p.waves_per_block == 8) return launch_i8_t<8>(p, wb, x, y, stream);
-        return launch_i8_t<4>(p, wb, x, y, stream);
-    }
-    if (p.waves_per_block == 8) return launch_mfma1_t<8>(p, wb, x, y, stream);
-    return launch_mfma1_t<4>(p, wb, x, y, stream);
-}
-
-size_t mfma_col_bytes(int kernel)
-{
-    return kernel == 4 ? (size_t)kI8ColBytes : (size_t)kMfmaColBytes;
+    if (p.waves_per_block == 8) return launch_lines<8>(p, wb, x, y, stream);
+    if (p.waves_per_block == 16) return launch_lines_p<16, 3>(p, wb, x, y, stream);
+    return launch_lines<4>(p, wb, x, y, stream);
 }
 
 size_t sub_lds_bytes(int S, int m)
@@ -1342,14 +725,6 @@ size_t sub_lds_bytes(int S, int m)
 size_t lines_lds_bytes(int S, int m, int waves)
 {
     return (size_t)(S * m + 1) * kI8ColBytes + (size_t)waves * kRingWave;
-}
-
-size_t mfma_lds_bytes(int kernel, int cols_chunk)
-{
-    if (kernel == 4) {
-        return (size_t)cols_chunk * kI8ColBytes;
-    }
-    return (size_t)cols_chunk * (kMfmaColBytes - 4) + (size_t)((cols_chunk + 3) & ~3) * 4;
 }
 
 }  // namespace q4k

@@ -54,8 +54,6 @@ class q4k_launch(ctypes.Structure):
         ("ring_depth", ctypes.c_int32),
         ("rows_per_task", ctypes.c_int32),
         ("cols_per_task", ctypes.c_int32),
-        ("tiles_per_task", ctypes.c_int32),
-        ("cols_per_chunk", ctypes.c_int32),
     ]
 
 

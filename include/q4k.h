@@ -101,15 +101,21 @@ const char* q4k_status_string(int rc);
 
 /* ---------------------------------------------------------------------
  * Launch options for q4k_gemv_ex (tests and tuning).  q4k_gemv is
- * q4k_gemv_ex with every field 0 (automatic).  The line-streamed kernels
- * (5, 6, 7) apply when k % 2048 == 0, w is 128-byte aligned and their staged
- * x plus line rings fit the LDS.  m = 1: the line-streamed vector-ALU kernel
- * (7; k <= 32768) when it applies and the weights take at least 16 MiB, else
- * the streaming kernel; the matrix cores only when asked for.  m > 1: the
- * sub-block kernel (6) for m >= 3, the line-streamed matrix-core kernel (5)
- * for m = 2, the other of the two if only it fits, else the x-stager
- * kernel.  With kernel = 0 and another field set, m = 1 uses the streaming
- * kernel and m > 1 the x-stager.
+ * q4k_gemv_ex with every field 0 (automatic).  Kernels:
+ *   1  x-stager (any m): x staged in LDS (whole or in K-chunks), fp32 decode
+ *   2  streaming (m = 1): rows streamed with dwordx4 loads, fp32 decode
+ *   3  line-streamed vector-ALU (m = 1): whole 128-byte weight lines through
+ *      a per-wave LDS ring, int8 dot products with x broadcast by DPP
+ *   4  line-streamed int8 matrix-core (m <= 8), one MFMA group per vector
+ *   5  sub-block int8 matrix-core (m <= 8), one MFMA per sub-block and quad
+ *      of vectors
+ * Kernels 3-5 need k % 2048 == 0, w 128-byte aligned and their staged x plus
+ * line rings within the LDS (kernel 3 also k <= 4096 * waves_per_block).
+ * Automatic choice: m = 1 kernel 3 when it applies and the weights take at
+ * least 16 MiB, else kernel 2 (the matrix cores only when asked for); m > 1
+ * kernel 5 for m >= 3, kernel 4 for m = 2, the other of the two if only it
+ * fits, else kernel 1.  With kernel = 0 and another field set, m = 1 uses
+ * the streaming kernel and m > 1 the x-stager.
  *
  * x is staged in LDS in spans of 4096 elements per vector.  The single-stage
  * variant holds all of x at once; the K-chunked variant stages
@@ -124,25 +130,14 @@ typedef struct q4k_launch {
     int32_t spans_per_chunk;  /* K-chunked: spans per stage, >= 1 (0 = automatic)  */
     int32_t rows_per_block;   /* rows per workgroup (0 = automatic)                */
     int32_t rows_per_wave;    /* rows a wave decodes per pass: 0 auto, 1, 2 or 4   */
-    int32_t waves_per_block;  /* 0 auto, 4 or 8 (streaming kernel: also 16)        */
+    int32_t waves_per_block;  /* 0 auto, 4 or 8; 16 for kernels 2-4 at m = 1       */
     int32_t x_in_registers;   /* 0 auto, 1 keep x in VGPRs (one span, m = 1), 2 LDS */
-    int32_t kernel;           /* 0 auto, 1 x-stager kernel, 2 streaming kernel (m = 1),
-                                 3 f16 matrix-core kernel (m = 1), 4 int8 matrix-core
-                                 kernel (m = 1), 5 line-streamed int8 matrix-core
-                                 kernel (m <= 8, k % 2048 == 0, w 128-byte aligned;
-                                 m > 1: 8 waves and 3 lines in flight), 6 sub-block
-                                 int8 matrix-core kernel (as 5; 8 waves, 3 lines),
-                                 7 line-streamed vector-ALU kernel (m = 1, int8 dot
-                                 products; otherwise as 5)                          */
-    int32_t ring_depth;       /* kernels 2-5, 7: loads in flight per wave, 0 auto;
-                                 streaming 1..4 rows; f16 matrix-core 1, 2 or 4
-                                 steps; int8 matrix-core 1..3 columns; line-streamed
-                                 3 or 9 lines                                        */
-    int32_t rows_per_task;    /* streaming: rows per wave task, 0 auto, >= 1           */
-    int32_t cols_per_task;    /* matrix-core: superblock columns per task, 0 auto      */
-    int32_t tiles_per_task;   /* matrix-core: 16-row tiles per task, 0 auto, 1, 2, 4   */
-    int32_t cols_per_chunk;   /* matrix-core: superblock columns of x staged at once
-                                 (rounded down to whole tasks), 0 auto               */
+    int32_t kernel;           /* 0 auto, else 1-5 as listed above                  */
+    int32_t ring_depth;       /* loads in flight per wave, 0 auto: streaming 1..4
+                                 rows; line-streamed 3 or 9 lines                  */
+    int32_t rows_per_task;    /* streaming: rows per wave task, 0 auto, >= 1       */
+    int32_t cols_per_task;    /* line-streamed: superblock columns per task (whole
+                                 slabs of 8 dividing the row), 0 auto              */
 } q4k_launch;
 
 /* q4k_gemv with explicit launch options (NULL = automatic).  Options that do

@@ -105,31 +105,26 @@ def test_launch_struct_matches_header():
 def test_gemv_ex_kernel_option_refusals(lib):
     """Options that no kernel can honour are refused before any HIP call."""
     cases = [
-        (dict(kernel=8), 16, 2048, 1),
-        (dict(kernel=6), 16, 1024, 1),                       # k not a multiple of 2048
-        (dict(kernel=7), 16, 4096, 2),                       # vector-ALU lines: one vector
-        (dict(kernel=7), 16, 1024, 1),                       # k not a multiple of 2048
-        (dict(kernel=7, waves_per_block=16, ring_depth=9), 16, 4096, 1),
-        (dict(kernel=7, waves_per_block=8), 16, 65536, 1),   # x: four groups per lane at most
-        (dict(kernel=7, tiles_per_task=2), 16, 4096, 1),
-        (dict(kernel=6, waves_per_block=4), 16, 4096, 2),    # eight waves only
-        (dict(kernel=6, ring_depth=9), 16, 4096, 2),         # three lines in flight only
+        (dict(kernel=6), 16, 2048, 1),                       # kernels 1-5 only
         (dict(kernel=-1), 16, 2048, 1),
         (dict(kernel=2), 16, 2048, 2),                       # streaming: one vector
-        (dict(kernel=3), 16, 2048, 2),                       # f16 matrix cores: one vector
-        (dict(kernel=4), 16, 2048, 3),
-        (dict(kernel=4, tiles_per_task=3), 16, 2048, 1),
-        (dict(kernel=4, ring_depth=4), 16, 2048, 1),
-        (dict(kernel=3, ring_depth=3), 16, 2048, 1),
+        (dict(kernel=3), 16, 4096, 2),                       # vector-ALU lines: one vector
+        (dict(kernel=3), 16, 1024, 1),                       # k not a multiple of 2048
+        (dict(kernel=3, waves_per_block=16, ring_depth=9), 16, 4096, 1),
+        (dict(kernel=3, waves_per_block=8), 16, 65536, 1),   # x: four groups per lane at most
+        (dict(kernel=3, ring_depth=4), 16, 4096, 1),
+        (dict(kernel=4), 16, 1024, 1),                       # k not a multiple of 2048
+        (dict(kernel=4, cols_per_task=12), 16, 4096, 1),     # whole slabs only
+        (dict(kernel=4, cols_per_task=24), 16, 4096, 1),     # must divide the row's slabs
+        (dict(kernel=4, ring_depth=4), 16, 4096, 1),
+        (dict(kernel=4, waves_per_block=16, ring_depth=9), 16, 4096, 1),
+        (dict(kernel=4, waves_per_block=4), 16, 4096, 2),    # several vectors: 8 waves
+        (dict(kernel=4, rows_per_task=2), 16, 4096, 1),
         (dict(kernel=5), 16, 1024, 1),                       # k not a multiple of 2048
-        (dict(kernel=5, cols_per_task=12), 16, 4096, 1),     # whole slabs only
-        (dict(kernel=5, cols_per_task=24), 16, 4096, 1),     # must divide the row's slabs
-        (dict(kernel=5, ring_depth=4), 16, 4096, 1),
-        (dict(kernel=5, waves_per_block=16, ring_depth=9), 16, 4096, 1),
-        (dict(kernel=5, waves_per_block=4), 16, 4096, 2),    # several vectors: 8 waves
-        (dict(kernel=5, tiles_per_task=2), 16, 4096, 1),
-        (dict(kernel=1, cols_per_task=8), 16, 4096, 1),      # matrix-core options only
-        (dict(kernel=2, tiles_per_task=1), 16, 4096, 1),
+        (dict(kernel=5, waves_per_block=4), 16, 4096, 2),    # eight waves only
+        (dict(kernel=5, ring_depth=9), 16, 4096, 2),         # three lines in flight only
+        (dict(kernel=1, cols_per_task=8), 16, 4096, 1),      # line-streamed options only
+        (dict(kernel=2, cols_per_task=8), 16, 4096, 1),
     ]
     for o, n, k, m in cases:
         cfg = q4k.q4k_launch(**o)
