@@ -252,10 +252,28 @@ int make_plan(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t lds_m
     if (nw != 4 && nw != 8 && !(nw == 16 && kernel == 2)) {
         return Q4K_ERR_UNSUPPORTED;
     }
-    // streaming kernel: about 2048 wave tasks (8 per CU of a 256-CU part);
-    // measured best on MI355X for the 4096- to 32000-row shapes
+    // streaming kernel: about 2048 wave tasks (8 per CU of a 256-CU part),
+    // measured best on MI355X for the 4096- to 32000-row shapes; then, within
+    // a factor of two of that, the rows per task whose workgroups fill the
+    // 256 CUs in the fewest rounds for the least work per workgroup (342
+    // workgroups of 12 rows take two rounds where 256 of 16 take one:
+    // 4096 x 11008 14.7 -> 11.2 us)
     int64_t auto_rpt = ((int64_t)nspans * n + 2047) / 2048;
     auto_rpt = auto_rpt < 1 ? 1 : auto_rpt > 64 ? 64 : auto_rpt;
+    if (kernel == 2 && !(o && (o->rows_per_task || o->rows_per_block))) {
+        const int64_t groups = nw > nspans ? nw / nspans : 1;
+        // from the largest down, so ties keep the fewer workgroups
+        int64_t best = auto_rpt, best_cost = 0;
+        for (int64_t r = 2 * auto_rpt < 64 ? 2 * auto_rpt : 64; r >= (auto_rpt + 1) / 2; --r) {
+            const int64_t rpb_r = groups * r;
+            const int64_t cost = ((n + rpb_r - 1) / rpb_r + 255) / 256 * rpb_r;
+            if (best_cost == 0 || cost < best_cost) {
+                best = r;
+                best_cost = cost;
+            }
+        }
+        auto_rpt = best;
+    }
     const int64_t rows_per_task = (o && o->rows_per_task) ? o->rows_per_task : auto_rpt;
     const int ring_cap = nw == 16 ? 2 : 3;
     const int ring_depth = (o && o->ring_depth) ? o->ring_depth
