@@ -75,19 +75,20 @@ int device_lds_max(size_t* out)
     return Q4K_OK;
 }
 
-// Plan of the line-streamed kernels (k a multiple of 2048, weights 128-byte
-// aligned, m <= 8): kernel 3 (m = 1, integer dot products on the vector
-// ALU), kernel 4 (one MFMA group per vector) and kernel 5 (one MFMA per
-// sub-block and quad of vectors).  A task is a 16-row tile times a group of
-// slabs of eight superblock columns; x (every vector) is staged whole.
+// Plan of the line-streamed kernels (weights 128-byte aligned, m <= 8):
+// kernel 3 (m = 1, integer dot products on the vector ALU, any k), kernel 4
+// (one MFMA group per vector) and kernel 5 (one MFMA per sub-block and quad
+// of vectors), both for k a multiple of 2048.  A task is a 16-row tile
+// times a group of slabs of eight superblock columns (the last slab of a
+// row may be partial); x (every vector) is staged whole.
 int make_plan_lines(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t lds_max,
                     GemvPlan* p, int kernel)
 {
     const int S = (int)(k / q4k::kQK);
-    if (S % 8 != 0) {
-        return Q4K_ERR_UNSUPPORTED;
+    if (S % 8 != 0 && kernel != 3) {
+        return Q4K_ERR_UNSUPPORTED;    // rows of whole slabs (vector-ALU kernel: any rows)
     }
-    const int nslabs = S / 8;
+    const int nslabs = (S + 7) / 8;
     const int nw = (o && o->waves_per_block) ? o->waves_per_block : 8;
     if (nw != 4 && nw != 8 && nw != 16) {
         return Q4K_ERR_UNSUPPORTED;
@@ -105,8 +106,9 @@ int make_plan_lines(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t
     if ((m > 1 || kernel == 5) && (nw != 8 || ring != 3)) {
         return Q4K_ERR_UNSUPPORTED;    // several vectors: eight waves, three lines in flight
     }
-    if (kernel == 3 && (m != 1 || S * 16 > 4 * 64 * nw)) {
-        return Q4K_ERR_UNSUPPORTED;    // one vector; x in at most four groups per lane
+    if (kernel == 3 && (m != 1 || S * 16 > 4 * 64 * nw || (S % 8 != 0 && ring != 3))) {
+        return Q4K_ERR_UNSUPPORTED;    // one vector; x in at most four groups per lane;
+                                       // rows of any length: three lines in flight
     }
     const int64_t ntiles = (n + 15) / 16;
     int64_t spt = 1;
@@ -166,8 +168,9 @@ int make_plan_lines(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t
 // Plans needing more LDS than lds_max are returned as they are; the caller
 // refuses them.
 // The automatic kernel (choices measured on MI355X).  The line-streamed
-// kernels apply when k is a multiple of 2048, the weights are 128-byte
-// aligned and their LDS (x of every vector, the line rings) fits.  m > 1:
+// kernels apply when the weights are 128-byte aligned, their LDS (x of every
+// vector, the line rings) fits and, for the matrix-core ones, k is a
+// multiple of 2048.  m > 1:
 // the sub-block kernel (5, m >= 3) or the per-vector line-streamed kernel
 // (4, m = 2), the other one if only it fits, else the x-stager kernel.
 // m = 1: the line-streamed vector-ALU kernel (3) where it applies and the

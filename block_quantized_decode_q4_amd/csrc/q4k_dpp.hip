@@ -143,7 +143,9 @@ __device__ __forceinline__ void convert_group_dot(const float4 (&v)[4], int G, b
     }
 }
 
-template <int NW, int P, int XC>
+// ANY: rows of any whole number of superblocks (line_stream_any, four-line
+// rings, per-row start offsets); else S % 8 == 0 (line_stream).
+template <int NW, int P, int XC, bool ANY>
 __global__ void __launch_bounds__(NW * 64)
 gemv_dot4_lines_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
                        float* __restrict__ y, int n, int S, int rows_per_block, int slabs_per_task)
@@ -156,12 +158,16 @@ gemv_dot4_lines_kernel(const uint8_t* __restrict__ w, const float* __restrict__ 
     const int j = lane & 15;
     const int row0 = blockIdx.x * rows_per_block;
     const int rows_here = min(rows_per_block, n - row0);
-    const int ncg = (S >> 3) / slabs_per_task;
+    const int ncg = ((S + 7) >> 3) / slabs_per_task;
+    constexpr int kWaveRing = ANY ? kRing4Wave : kRingWave;
+    constexpr uint32_t kWindow = ANY ? 511u : 255u;        // ring window of a row, minus one
+    // byte offset of the lane's row within its first line (tiles start on a line)
+    const uint32_t loff = ANY ? (uint32_t)(j * 144 * S) & 127u : 0u;
 
     // LDS: staged x (S columns), the line rings, row sums of slab groups
     const size_t xbytes = (size_t)S * kDotCol;
-    unsigned char* ring = smem + xbytes + wave * kRingWave;
-    float* ypart = reinterpret_cast<float*>(smem + xbytes + NW * kRingWave);
+    unsigned char* ring = smem + xbytes + wave * kWaveRing;
+    float* ypart = reinterpret_cast<float*>(smem + xbytes + NW * kWaveRing);
 
     // XC groups of 16 x values per thread: all of x when S * 16 <= XC * 64 NW;
     // loads past the end are clamped, their results not stored
@@ -187,9 +193,10 @@ gemv_dot4_lines_kernel(const uint8_t* __restrict__ w, const float* __restrict__ 
 
     float acc = 0.f;
     auto step = [&](int c, const unsigned char* rr, uint32_t b0) {
-        const uint4 h = *reinterpret_cast<const uint4*>(rr + (b0 & 255u));
-        const uint4 q0 = *reinterpret_cast<const uint4*>(rr + ((b0 + 16u + 32u * (uint32_t)g) & 255u));
-        const uint4 q1 = *reinterpret_cast<const uint4*>(rr + ((b0 + 32u + 32u * (uint32_t)g) & 255u));
+        const uint32_t b = b0 + loff;
+        const uint4 h = *reinterpret_cast<const uint4*>(rr + (b & kWindow));
+        const uint4 q0 = *reinterpret_cast<const uint4*>(rr + ((b + 16u + 32u * (uint32_t)g) & kWindow));
+        const uint4 q1 = *reinterpret_cast<const uint4*>(rr + ((b + 32u + 32u * (uint32_t)g) & kWindow));
         const unsigned char* col = smem + (size_t)c * kDotCol;
         const uint4 xd = *reinterpret_cast<const uint4*>(col + g * 256 + j * 16);
         const float4 k4 = *reinterpret_cast<const float4*>(col + 1024 + g * 16);
@@ -227,8 +234,13 @@ gemv_dot4_lines_kernel(const uint8_t* __restrict__ w, const float* __restrict__ 
         }
         acc = 0.f;
     };
-    line_stream<NW, P>(w, x, n, S, rows_per_block, slabs_per_task, ring, issue_x, convert_x, step,
-                       task_end);
+    if constexpr (ANY) {
+        line_stream_any<NW>(w, x, n, S, rows_per_block, slabs_per_task, ring, issue_x, convert_x,
+                            step, task_end);
+    } else {
+        line_stream<NW, P>(w, x, n, S, rows_per_block, slabs_per_task, ring, issue_x, convert_x,
+                           step, task_end);
+    }
 
     if (ncg > 1) {
         __syncthreads();
@@ -246,7 +258,15 @@ template <int NW, int P, int XC>
 static hipError_t launch_dot4_x(const GemvPlan& p, const uint8_t* w, const float* x, float* y,
                                 hipStream_t stream)
 {
-    hipLaunchKernelGGL((gemv_dot4_lines_kernel<NW, P, XC>), dim3(p.grid), dim3(NW * 64),
+    if constexpr (P == 3) {
+        if (p.S % 8 != 0) {
+            hipLaunchKernelGGL((gemv_dot4_lines_kernel<NW, 3, XC, true>), dim3(p.grid),
+                               dim3(NW * 64), p.lds_bytes, stream, w, x, y, p.n, p.S,
+                               p.rows_per_block, p.cols_per_task / 8);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((gemv_dot4_lines_kernel<NW, P, XC, false>), dim3(p.grid), dim3(NW * 64),
                        p.lds_bytes, stream, w, x, y, p.n, p.S, p.rows_per_block,
                        p.cols_per_task / 8);
     return hipGetLastError();
@@ -287,7 +307,7 @@ hipError_t launch_gemv_dot4(const GemvPlan& p, const void* w, const float* x, fl
 
 size_t dot4_lds_bytes(int S, int waves)
 {
-    return (size_t)S * kDotCol + (size_t)waves * kRingWave;
+    return (size_t)S * kDotCol + (size_t)waves * (S % 8 != 0 ? kRing4Wave : kRingWave);
 }
 
 }  // namespace q4k

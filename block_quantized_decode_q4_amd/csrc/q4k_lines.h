@@ -20,6 +20,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace q4k {
 
 constexpr int kRingRow = 2 * 128 + 16;        // two lines per row, padded
@@ -146,6 +148,148 @@ __device__ __forceinline__ void line_stream(const uint8_t* __restrict__ w,
         if (sig % slabs_per_task == slabs_per_task - 1) {
             task_end(wave + (sig / slabs_per_task) * NW);
         }
+    }
+}
+
+constexpr int kRing4Row = 4 * 128 + 16;       // four lines per row, padded
+constexpr int kRing4Wave = 16 * kRing4Row;
+
+// The line stream for rows of any whole number of superblocks: S % 8 may be
+// non-zero, so a row starts on any 16-byte boundary of a line.  A 16-row
+// tile is 18 S lines, so tiles start on a line (w 128-byte aligned) and row
+// j of every tile starts (144 S j) mod 128 bytes into its first line.  Each
+// row has a four-line ring.  A task (tile, slabs_per_task slabs) streams
+// 9 slabs_per_task + 3 line indices per row: line 0, the nine further lines
+// each slab reaches (a superblock that starts 112 bytes into a line ends in
+// the next one, so the slab's reach is one line longer than when rows are
+// aligned), and two surplus indices that keep a line's register slot equal
+// to its index mod 3 from one task to the next.  A 16-byte piece past the
+// row's bytes of the task is not loaded (the wave's line of x instead), so
+// nothing beyond the matrix is read.  Superblock t of a task (t = 0 ..)
+// needs lines floor(144 t / 128) .. floor((255 + 144 t) / 128) at most,
+// three of the ring's four.  Calls as line_stream; step(c, rr, b0) gets
+// b0 = 144 t, the byte offset within the task's ring window of 512 bytes
+// before the lane adds its row's start offset, and runs only for the task's
+// superblocks (the last slab of a row may hold fewer than eight).
+template <int NW, typename IssueX, typename ConvertX, typename Step, typename TaskEnd>
+__device__ __forceinline__ void line_stream_any(const uint8_t* __restrict__ w,
+                                                const float* __restrict__ x, int n, int S,
+                                                int rows_per_block, int slabs_per_task,
+                                                unsigned char* ring, IssueX issue_x,
+                                                ConvertX convert_x, Step step, TaskEnd task_end)
+{
+    constexpr int P = 3;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int j = lane & 15;
+    const int lrow = lane >> 3;
+    const int lunit = lane & 7;
+
+    const int row0 = blockIdx.x * rows_per_block;
+    const int rows_here = min(rows_per_block, n - row0);
+    const int ntiles = (rows_here + 15) >> 4;
+    const int nslabs = (S + 7) >> 3;
+    const int ncg = nslabs / slabs_per_task;
+    const int ntasks = ntiles * ncg;
+    const int my_tasks = ntasks > wave ? (ntasks - wave + NW - 1) / NW : 0;
+    const int lpt = 9 * slabs_per_task + 3;          // line indices per task
+    const size_t row_bytes = (size_t)S * 144;
+    const int xlines = S * 8;
+    const uint64_t dx = (uint64_t)(reinterpret_cast<const uint8_t*>(x) - w) +
+                        (uint64_t)((blockIdx.x * NW + wave) % xlines) * 128u +
+                        16u * (uint32_t)lunit;
+
+    // task q of this wave (clamped into its tasks) -> (tile, column group,
+    // superblocks)
+    auto task_of = [&](int q, int& tile, int& cg, int& T) {
+        const int qc = max(0, min(q, my_tasks - 1));
+        const int task = min(wave + qc * NW, ntasks - 1);
+        tile = task / ncg;
+        cg = task % ncg;
+        T = min(8 * slabs_per_task, S - 8 * cg * slabs_per_task);
+    };
+    // the two piece addresses (rows lrow and 8 + lrow) of line L of task q;
+    // x past the wave's tasks or the row's bytes of the task (a mask on the
+    // byte offset from w, as in line_stream)
+    auto line_ptrs = [&](int q, int L, const uint8_t** p) {
+        int tile, cg, T;
+        task_of(q, tile, cg, T);
+        const bool past = q >= my_tasks;                             // wave-uniform
+        const uint32_t piece = 128u * (uint32_t)L + 16u * (uint32_t)lunit;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int r = min(tile * 16 + 8 * h + lrow, rows_here - 1);
+            const uint64_t start = (uint64_t)(row0 + r) * row_bytes;
+            const uint32_t off = (uint32_t)start & 127u;
+            const uint64_t at = start - off + (uint64_t)cg * slabs_per_task * 1152u + piece;
+            const bool need = !past && piece < off + 144u * (uint32_t)T;
+            const uint64_t mask = need ? 0ull : ~0ull;
+            p[h] = w + ((at & ~mask) | (dx & mask));
+        }
+    };
+    uint4 lines[P][2];
+    // write line L = 9 s2 + X of task q into the ring, refill its slot
+    // (X % 3) with the line three indices on
+    auto put = [&](int q, int s2, auto Xc) {
+        constexpr int X = decltype(Xc)::value;
+        constexpr int slot = X % P;
+        const int L = 9 * s2 + X;
+        const uint32_t lpos = ((uint32_t)L & 3u) * 128u + 16u * (uint32_t)lunit;
+        *reinterpret_cast<uint4*>(ring + lrow * kRing4Row + lpos) = lines[slot][0];
+        *reinterpret_cast<uint4*>(ring + (8 + lrow) * kRing4Row + lpos) = lines[slot][1];
+        __builtin_amdgcn_sched_barrier(0x000F);
+        const int ln = L + P;
+        const uint8_t* p[2];
+        line_ptrs(ln >= lpt ? q + 1 : q, ln >= lpt ? ln - lpt : ln, p);
+        lines[slot][0] = load_line_nt(p[0]);
+        lines[slot][1] = load_line_nt(p[1]);
+    };
+
+    issue_x();
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int l = 0; l < P; ++l) {
+        const uint8_t* p[2];
+        line_ptrs(0, l, p);
+        lines[l][0] = load_line_nt(p[0]);
+        lines[l][1] = load_line_nt(p[1]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    convert_x();
+    __syncthreads();
+
+    for (int q = 0; q < my_tasks; ++q) {
+        int tile, cg, T;
+        task_of(q, tile, cg, T);
+        const int c0 = 8 * cg * slabs_per_task;
+        put(q, 0, std::integral_constant<int, 0>());
+        for (int s2 = 0; s2 < slabs_per_task; ++s2) {
+            // lines 9 s2 + 1 .. 9 s2 + 9: two before superblock 1 of the slab,
+            // one before each other
+            put(q, s2, std::integral_constant<int, 1>());
+            if (8 * s2 < T) step(c0 + 8 * s2, ring + j * kRing4Row, 1152u * (uint32_t)s2);
+            put(q, s2, std::integral_constant<int, 2>());
+            put(q, s2, std::integral_constant<int, 3>());
+            if (8 * s2 + 1 < T) step(c0 + 8 * s2 + 1, ring + j * kRing4Row, 1152u * (uint32_t)s2 + 144u);
+            put(q, s2, std::integral_constant<int, 4>());
+            if (8 * s2 + 2 < T) step(c0 + 8 * s2 + 2, ring + j * kRing4Row, 1152u * (uint32_t)s2 + 288u);
+            put(q, s2, std::integral_constant<int, 5>());
+            if (8 * s2 + 3 < T) step(c0 + 8 * s2 + 3, ring + j * kRing4Row, 1152u * (uint32_t)s2 + 432u);
+            put(q, s2, std::integral_constant<int, 6>());
+            if (8 * s2 + 4 < T) step(c0 + 8 * s2 + 4, ring + j * kRing4Row, 1152u * (uint32_t)s2 + 576u);
+            put(q, s2, std::integral_constant<int, 7>());
+            if (8 * s2 + 5 < T) step(c0 + 8 * s2 + 5, ring + j * kRing4Row, 1152u * (uint32_t)s2 + 720u);
+            put(q, s2, std::integral_constant<int, 8>());
+            if (8 * s2 + 6 < T) step(c0 + 8 * s2 + 6, ring + j * kRing4Row, 1152u * (uint32_t)s2 + 864u);
+            put(q, s2, std::integral_constant<int, 9>());
+            if (8 * s2 + 7 < T) step(c0 + 8 * s2 + 7, ring + j * kRing4Row, 1152u * (uint32_t)s2 + 1008u);
+        }
+        // the two surplus indices of the task
+        put(q, slabs_per_task, std::integral_constant<int, 1>());
+        put(q, slabs_per_task, std::integral_constant<int, 2>());
+        task_end(wave + q * NW);
     }
 }
 

@@ -109,8 +109,10 @@ const char* q4k_status_string(int rc);
  *   4  line-streamed int8 matrix-core (m <= 8), one MFMA group per vector
  *   5  sub-block int8 matrix-core (m <= 8), one MFMA per sub-block and quad
  *      of vectors
- * Kernels 3-5 need k % 2048 == 0, w 128-byte aligned and their staged x plus
- * line rings within the LDS (kernel 3 also k <= 4096 * waves_per_block).
+ * Kernels 3-5 need w 128-byte aligned and their staged x plus line rings
+ * within the LDS; kernels 4 and 5 also k % 2048 == 0 (rows of whole 8-
+ * superblock slabs), kernel 3 takes any k up to 4096 * waves_per_block (rows
+ * of partial slabs with four-line rings and three lines in flight).
  * Automatic choice: m = 1 kernel 3 when it applies and the weights take at
  * least 16 MiB, else kernel 2 (the matrix cores only when asked for); m > 1
  * kernel 5 for m >= 3, kernel 4 for m = 2, the other of the two if only it

@@ -109,7 +109,7 @@ def test_gemv_ex_kernel_option_refusals(lib):
         (dict(kernel=-1), 16, 2048, 1),
         (dict(kernel=2), 16, 2048, 2),                       # streaming: one vector
         (dict(kernel=3), 16, 4096, 2),                       # vector-ALU lines: one vector
-        (dict(kernel=3), 16, 1024, 1),                       # k not a multiple of 2048
+        (dict(kernel=3, ring_depth=9), 16, 1024, 1),         # partial slabs: three lines
         (dict(kernel=3, waves_per_block=16, ring_depth=9), 16, 4096, 1),
         (dict(kernel=3, waves_per_block=8), 16, 65536, 1),   # x: four groups per lane at most
         (dict(kernel=3, ring_depth=4), 16, 4096, 1),

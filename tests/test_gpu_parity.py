@@ -285,10 +285,11 @@ def test_sub_kernel_workload(oracle_mod):
     assert_within(y, y_ref, bound, "sub-block workload 4")
 
 
-# line-streamed vector-ALU kernel (m = 1, k a multiple of 2048): integer dot
-# products with x broadcast across the tile's rows by DPP.  Its sums run in
-# the same order for every launch geometry with the same column grouping, so
-# those launches are bit-identical.
+# line-streamed vector-ALU kernel (m = 1, any k): integer dot products with x
+# broadcast across the tile's rows by DPP; rows of a whole number of slabs
+# (k a multiple of 2048) take the two-line rings, other rows four-line rings
+# and per-row start offsets.  Its sums run in the same order for every launch
+# geometry with the same column grouping, so those launches are bit-identical.
 DOT4_VARIANTS = [
     dict(kernel=3),
     dict(kernel=3, cols_per_task=8),
@@ -307,15 +308,23 @@ def _dot4_auto_cols(n, k, opts):
     whole rows for at least 1024 tiles or when the per-slab row sums do not
     fit the LDS, else one slab of 8 columns."""
     S = k // 256
+    nslabs = (S + 7) // 8
     ntiles = (n + 15) // 16
     rpb = opts.get("rows_per_block") or 16 * ((ntiles + 255) // 256)
     nw = opts.get("waves_per_block", 8)
-    fits = S * 1088 + nw * 4352 + (S // 8) * rpb * 4 <= 160 * 1024
-    return S if (ntiles >= 1024 or not fits) else 8
+    fits = S * 1088 + nw * _dot4_ring(S) + nslabs * rpb * 4 <= 160 * 1024
+    return 8 * nslabs if (ntiles >= 1024 or not fits) else 8
+
+
+def _dot4_ring(S):
+    """LDS bytes of one wave's line rings: two lines per row for rows of
+    whole slabs, four otherwise (16 rows, 16 bytes of padding per row)."""
+    return 16 * (2 * 128 + 16) if S % 8 == 0 else 16 * (4 * 128 + 16)
 
 
 def _dot4_check(w_d, x, n, k, y_ref, bound, what):
     S = k // 256
+    nslabs = (S + 7) // 8
     firsts = {}
     for opts in DOT4_VARIANTS:
         _say("%s vector-ALU line-streamed %r" % (what, opts))
@@ -325,11 +334,13 @@ def _dot4_check(w_d, x, n, k, y_ref, bound, what):
         except q4k.Q4KError as e:
             # refused: a task's column group must divide the slabs of a row,
             # the staged x (1088 bytes per superblock column) plus the line
-            # rings (4352 bytes per wave) must fit the 160 KiB LDS, and x
-            # takes at most four 16-element groups per lane
-            bad_group = "cols_per_task" in opts and (S // 8) % (opts["cols_per_task"] // 8) != 0
-            too_big = S * 1088 + nw * 4352 > 160 * 1024 or S * 16 > 4 * 64 * nw
-            assert e.rc == q4k.Q4K_ERR_UNSUPPORTED and (bad_group or too_big), opts
+            # rings must fit the 160 KiB LDS, x takes at most four
+            # 16-element groups per lane, rows of partial slabs keep three
+            # lines in flight
+            bad_group = "cols_per_task" in opts and nslabs % (opts["cols_per_task"] // 8) != 0
+            too_big = S * 1088 + nw * _dot4_ring(S) > 160 * 1024 or S * 16 > 4 * 64 * nw
+            bad_ring = S % 8 != 0 and opts.get("ring_depth", 3) != 3
+            assert e.rc == q4k.Q4K_ERR_UNSUPPORTED and (bad_group or too_big or bad_ring), opts
             continue
         assert_within(y, y_ref, bound, "%s vector-ALU line-streamed %r" % (what, opts))
         cpt = opts.get("cols_per_task") or _dot4_auto_cols(n, k, opts)
@@ -339,21 +350,24 @@ def _dot4_check(w_d, x, n, k, y_ref, bound, what):
             firsts[cpt] = y
 
 
-@pytest.mark.parametrize("i", [1, 2, 3])
+@pytest.mark.parametrize("i", [0, 1, 2, 3])
 def test_dot4_kernel_workloads(oracle_mod, i):
     wl, w, x, y_ref, bound = workload(i, oracle_mod)
     _dot4_check(dev(w), x, wl.n, wl.k, y_ref, bound, "workload %d" % i)
 
 
 @pytest.mark.parametrize("n,k", [(1, 2048), (17, 4096), (130, 14336), (3, 65536), (257, 2048),
-                                 (33, 18432), (20, 24576)])
+                                 (33, 18432), (20, 24576),
+                                 # rows of partial slabs: any start offset in a line
+                                 (1, 256), (5, 768), (17, 1280), (33, 4352), (130, 11008),
+                                 (257, 5120), (16, 2304), (48, 13824), (300, 3328)])
 def test_dot4_kernel_shapes(oracle_mod, n, k):
     w, x = synth.make_inputs(n, k, 1, seed=n + 13 * k)
     y_ref, bound = oracle_mod.gemv(w, x, n)
     _dot4_check(dev(w), x, n, k, y_ref, bound, "n=%d k=%d" % (n, k))
 
 
-@pytest.mark.parametrize("n,k", [(64, 2048), (33, 4096)])
+@pytest.mark.parametrize("n,k", [(64, 2048), (33, 4096), (40, 1280)])
 def test_dot4_kernel_x_dynamic_range(oracle_mod, n, k):
     rng = np.random.default_rng(n * k + 1)
     w, _ = synth.make_inputs(n, k, 1, seed=n + k + 1)
@@ -370,8 +384,8 @@ def test_dot4_kernel_x_dynamic_range(oracle_mod, n, k):
 
 def test_dot4_kernel_refusals():
     """Shapes the vector-ALU line-streamed kernel cannot take are refused
-    without launching: several vectors, k not a multiple of 2048, rows not
-    128-byte aligned, x larger than four groups of 16 per lane."""
+    without launching: several vectors, rows not 128-byte aligned, x larger
+    than four groups of 16 per lane."""
     n = 8
     w, x = synth.make_inputs(n, 2048, 2, seed=8)
     y_d = torch.zeros((2, n), dtype=torch.float32, device="cuda")
