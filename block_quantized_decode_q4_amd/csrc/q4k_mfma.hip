@@ -254,10 +254,10 @@ __device__ __forceinline__ float step_vector(const StepW& t, const ColI8& col)
 // ---------------------------------------------------------------------------
 // Line-streamed int8 matrix-core kernel (rows of whole 128-byte lines).
 //
-// The same operands and arithmetic as gemv_mfma_i8_kernel, but the weights
-// reach the matrix-core lanes through the line stream of q4k_lines.h: whole
-// 128-byte lines per row into a per-wave LDS ring, from which the lanes read
-// the tile layout of the matrix cores.
+// The operands and arithmetic above, fed by the line stream of q4k_lines.h:
+// whole 128-byte lines per row into a per-wave LDS ring, from which the
+// lanes read the tile layout of the matrix cores; M vectors share the
+// weight side (codes, scales) of each step.
 // ---------------------------------------------------------------------------
 
 template <int NW, int P, int XC, int M>
