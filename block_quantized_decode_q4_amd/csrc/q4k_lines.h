@@ -76,26 +76,43 @@ __device__ __forceinline__ void line_stream(const uint8_t* __restrict__ w,
         tile = task / ncg;
         slab = (task % ncg) * slabs_per_task + sig % slabs_per_task;
     };
-    // the two global addresses (rows lrow and 8 + lrow) of line l of slab
-    // sig; past the wave's last slab the prefetch reads a 128-byte line of x
-    // instead (cached, so the surplus loads cost no HBM traffic; each wave
+    // the byte offsets from w of line 0 of slab sig for rows lrow and
+    // 8 + lrow (the lane's 16 bytes of them), and the line stride; past the
+    // wave's last slab the prefetch reads a 128-byte line of x instead, with
+    // stride 0 (cached, so the surplus loads cost no HBM traffic; each wave
     // takes its own line, or the tails of all waves would queue on one L2
     // channel).  The choice is a mask on the byte offset from w: a select of
     // two pointers makes the compiler branch around the address arithmetic,
-    // which costs registers across the unrolled slab.
+    // which costs registers across the unrolled slab.  Computed once per
+    // slab, so a line costs one 64-bit add per row.
     const int xlines = S * 8;                        // 128-byte lines of one x vector
     const uint64_t dx = (uint64_t)(reinterpret_cast<const uint8_t*>(x) - w) +
-                        (uint64_t)((blockIdx.x * NW + wave) % xlines) * 128u;
-    auto line_ptrs = [&](int sig, int l, const uint8_t** p) {
+                        (uint64_t)((blockIdx.x * NW + wave) % xlines) * 128u +
+                        16u * (uint32_t)lunit;
+    struct SlabBase {
+        uint64_t b[2];
+        uint32_t stride;
+    };
+    auto slab_base = [&](int sig) {
         int tile, slab;
         slab_of(sig, tile, slab);
-        const uint64_t mask = sig >= my_slabs ? ~0ull : 0ull;     // wave-uniform
-        const uint64_t off = (uint64_t)(9 * slab + l) * 128;
+        const bool past = sig >= my_slabs;                          // wave-uniform
+        const uint64_t mask = past ? ~0ull : 0ull;
+        SlabBase sb;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int r = min(tile * 16 + 8 * h + lrow, rows_here - 1);
-            const uint64_t full = (uint64_t)(row0 + r) * row_bytes + off;
-            p[h] = w + (((full & ~mask) | (dx & mask)) + 16 * lunit);
+            const uint64_t full = (uint64_t)(row0 + r) * row_bytes + (uint64_t)slab * 1152u +
+                                  16u * (uint32_t)lunit;
+            sb.b[h] = (full & ~mask) | (dx & mask);
+        }
+        sb.stride = past ? 0u : 128u;
+        return sb;
+    };
+    auto line_ptrs = [&](const SlabBase& sb, int l, const uint8_t** p) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            p[h] = w + sb.b[h] + (uint64_t)(sb.stride * (uint32_t)l);
         }
     };
 
@@ -109,12 +126,15 @@ __device__ __forceinline__ void line_stream(const uint8_t* __restrict__ w,
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     uint4 lines[P][2];
+    {
+        const SlabBase sb0 = slab_base(0);
 #pragma unroll
-    for (int l = 0; l < P; ++l) {
-        const uint8_t* p[2];
-        line_ptrs(0, l, p);
-        lines[l][0] = load_line_nt(p[0]);
-        lines[l][1] = load_line_nt(p[1]);
+        for (int l = 0; l < P; ++l) {
+            const uint8_t* p[2];
+            line_ptrs(sb0, l, p);
+            lines[l][0] = load_line_nt(p[0]);
+            lines[l][1] = load_line_nt(p[1]);
+        }
     }
     __builtin_amdgcn_sched_barrier(0);
     convert_x();
@@ -124,6 +144,8 @@ __device__ __forceinline__ void line_stream(const uint8_t* __restrict__ w,
         int tile, slab;
         slab_of(sig, tile, slab);
         const uint32_t par = (uint32_t)slab & 1u;      // parity of line 9*slab
+        const SlabBase cur = slab_base(sig);
+        const SlabBase nxt = slab_base(sig + 1);
 #pragma unroll
         for (int cp = 0; cp < 8; ++cp) {
             // lines written before superblock cp: 0 and 1 first, then cp + 1
@@ -138,7 +160,7 @@ __device__ __forceinline__ void line_stream(const uint8_t* __restrict__ w,
                 __builtin_amdgcn_sched_barrier(0x000F);
                 const int ln = l + P;              // refill: P lines ahead
                 const uint8_t* p[2];
-                line_ptrs(ln >= 9 ? sig + 1 : sig, ln >= 9 ? ln - 9 : ln, p);
+                line_ptrs(ln >= 9 ? nxt : cur, ln >= 9 ? ln - 9 : ln, p);
                 lines[slot][0] = load_line_nt(p[0]);
                 lines[slot][1] = load_line_nt(p[1]);
             }
@@ -208,29 +230,43 @@ __device__ __forceinline__ void line_stream_any(const uint8_t* __restrict__ w,
         cg = task % ncg;
         T = min(8 * slabs_per_task, S - 8 * cg * slabs_per_task);
     };
-    // the two piece addresses (rows lrow and 8 + lrow) of line L of task q;
+    // per task q and row (lrow, 8 + lrow): the byte offset from w of the
+    // lane's 16 bytes of line 0, and the bound below which a line's piece
+    // holds bytes of the row's task (128 L < lim); computed once per task.
     // x past the wave's tasks or the row's bytes of the task (a mask on the
     // byte offset from w, as in line_stream)
-    auto line_ptrs = [&](int q, int L, const uint8_t** p) {
+    struct TaskBase {
+        uint64_t b[2];
+        int lim[2];
+    };
+    auto task_base = [&](int q) {
         int tile, cg, T;
         task_of(q, tile, cg, T);
         const bool past = q >= my_tasks;                             // wave-uniform
-        const uint32_t piece = 128u * (uint32_t)L + 16u * (uint32_t)lunit;
+        TaskBase tb;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int r = min(tile * 16 + 8 * h + lrow, rows_here - 1);
             const uint64_t start = (uint64_t)(row0 + r) * row_bytes;
-            const uint32_t off = (uint32_t)start & 127u;
-            const uint64_t at = start - off + (uint64_t)cg * slabs_per_task * 1152u + piece;
-            const bool need = !past && piece < off + 144u * (uint32_t)T;
-            const uint64_t mask = need ? 0ull : ~0ull;
-            p[h] = w + ((at & ~mask) | (dx & mask));
+            const int off = (int)((uint32_t)start & 127u);
+            tb.b[h] = start - (uint64_t)off + (uint64_t)cg * slabs_per_task * 1152u +
+                      16u * (uint32_t)lunit;
+            tb.lim[h] = past ? 0 : off + 144 * T - 16 * lunit;
+        }
+        return tb;
+    };
+    auto line_ptrs = [&](const TaskBase& tb, int L, const uint8_t** p) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint64_t mask = 128 * L < tb.lim[h] ? 0ull : ~0ull;
+            p[h] = w + (((tb.b[h] + 128u * (uint32_t)L) & ~mask) | (dx & mask));
         }
     };
     uint4 lines[P][2];
-    // write line L = 9 s2 + X of task q into the ring, refill its slot
-    // (X % 3) with the line three indices on
-    auto put = [&](int q, int s2, auto Xc) {
+    // write line L = 9 s2 + X of the current task (bases cur, next task's
+    // nxt) into the ring, refill its slot (X % 3) with the line three
+    // indices on
+    auto put = [&](const TaskBase& cur, const TaskBase& nxt, int s2, auto Xc) {
         constexpr int X = decltype(Xc)::value;
         constexpr int slot = X % P;
         const int L = 9 * s2 + X;
@@ -240,7 +276,7 @@ __device__ __forceinline__ void line_stream_any(const uint8_t* __restrict__ w,
         __builtin_amdgcn_sched_barrier(0x000F);
         const int ln = L + P;
         const uint8_t* p[2];
-        line_ptrs(ln >= lpt ? q + 1 : q, ln >= lpt ? ln - lpt : ln, p);
+        line_ptrs(ln >= lpt ? nxt : cur, ln >= lpt ? ln - lpt : ln, p);
         lines[slot][0] = load_line_nt(p[0]);
         lines[slot][1] = load_line_nt(p[1]);
     };
@@ -249,12 +285,15 @@ __device__ __forceinline__ void line_stream_any(const uint8_t* __restrict__ w,
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
+    {
+        const TaskBase tb0 = task_base(0);
 #pragma unroll
-    for (int l = 0; l < P; ++l) {
-        const uint8_t* p[2];
-        line_ptrs(0, l, p);
-        lines[l][0] = load_line_nt(p[0]);
-        lines[l][1] = load_line_nt(p[1]);
+        for (int l = 0; l < P; ++l) {
+            const uint8_t* p[2];
+            line_ptrs(tb0, l, p);
+            lines[l][0] = load_line_nt(p[0]);
+            lines[l][1] = load_line_nt(p[1]);
+        }
     }
     __builtin_amdgcn_sched_barrier(0);
     convert_x();
@@ -264,31 +303,33 @@ __device__ __forceinline__ void line_stream_any(const uint8_t* __restrict__ w,
         int tile, cg, T;
         task_of(q, tile, cg, T);
         const int c0 = 8 * cg * slabs_per_task;
-        put(q, 0, std::integral_constant<int, 0>());
+        const TaskBase cur = task_base(q);
+        const TaskBase nxt = task_base(q + 1);
+        put(cur, nxt, 0, std::integral_constant<int, 0>());
         for (int s2 = 0; s2 < slabs_per_task; ++s2) {
             // lines 9 s2 + 1 .. 9 s2 + 9: two before superblock 1 of the slab,
             // one before each other
-            put(q, s2, std::integral_constant<int, 1>());
+            put(cur, nxt, s2, std::integral_constant<int, 1>());
             if (8 * s2 < T) step(c0 + 8 * s2, ring + j * kRing4Row, 1152u * (uint32_t)s2);
-            put(q, s2, std::integral_constant<int, 2>());
-            put(q, s2, std::integral_constant<int, 3>());
+            put(cur, nxt, s2, std::integral_constant<int, 2>());
+            put(cur, nxt, s2, std::integral_constant<int, 3>());
             if (8 * s2 + 1 < T) step(c0 + 8 * s2 + 1, ring + j * kRing4Row, 1152u * (uint32_t)s2 + 144u);
-            put(q, s2, std::integral_constant<int, 4>());
+            put(cur, nxt, s2, std::integral_constant<int, 4>());
             if (8 * s2 + 2 < T) step(c0 + 8 * s2 + 2, ring + j * kRing4Row, 1152u * (uint32_t)s2 + 288u);
-            put(q, s2, std::integral_constant<int, 5>());
+            put(cur, nxt, s2, std::integral_constant<int, 5>());
             if (8 * s2 + 3 < T) step(c0 + 8 * s2 + 3, ring + j * kRing4Row, 1152u * (uint32_t)s2 + 432u);
-            put(q, s2, std::integral_constant<int, 6>());
+            put(cur, nxt, s2, std::integral_constant<int, 6>());
             if (8 * s2 + 4 < T) step(c0 + 8 * s2 + 4, ring + j * kRing4Row, 1152u * (uint32_t)s2 + 576u);
-            put(q, s2, std::integral_constant<int, 7>());
+            put(cur, nxt, s2, std::integral_constant<int, 7>());
             if (8 * s2 + 5 < T) step(c0 + 8 * s2 + 5, ring + j * kRing4Row, 1152u * (uint32_t)s2 + 720u);
-            put(q, s2, std::integral_constant<int, 8>());
+            put(cur, nxt, s2, std::integral_constant<int, 8>());
             if (8 * s2 + 6 < T) step(c0 + 8 * s2 + 6, ring + j * kRing4Row, 1152u * (uint32_t)s2 + 864u);
-            put(q, s2, std::integral_constant<int, 9>());
+            put(cur, nxt, s2, std::integral_constant<int, 9>());
             if (8 * s2 + 7 < T) step(c0 + 8 * s2 + 7, ring + j * kRing4Row, 1152u * (uint32_t)s2 + 1008u);
         }
         // the two surplus indices of the task
-        put(q, slabs_per_task, std::integral_constant<int, 1>());
-        put(q, slabs_per_task, std::integral_constant<int, 2>());
+        put(cur, nxt, slabs_per_task, std::integral_constant<int, 1>());
+        put(cur, nxt, slabs_per_task, std::integral_constant<int, 2>());
         task_end(wave + q * NW);
     }
 }
