@@ -46,7 +46,7 @@ __device__ __forceinline__ void dot8(uint32_t D, const float4& xl, const float4&
 }
 
 struct ChunkScales {
-    float d24;    // d * 2^24
+    float d24;    // d * dscale (2^24 for the fma_mix codes, whose values are q * 2^-24)
     float dmin;
     float sc_lo, sc_hi, m_lo, m_hi;
 };
@@ -58,11 +58,12 @@ struct ChunkScales {
 //           m_j  = (s[j+4] >> 4) | (s[j]   >> 6) << 4
 // Both forms take bytes 2(c&1), 2(c&1)+1 of their dwords, so one shift
 // serves both; the lane picks its form with a select.
-__device__ __forceinline__ ChunkScales decode_header(const uint4& h, int c)
+__device__ __forceinline__ ChunkScales decode_header(const uint4& h, int c,
+                                                     float dscale = 16777216.0f)
 {
     ChunkScales s;
     const half2_t dd = __builtin_bit_cast(half2_t, h.x);
-    s.d24 = (float)dd.x * 16777216.0f;
+    s.d24 = (float)dd.x * dscale;
     s.dmin = (float)dd.y;
     const uint32_t sh = (uint32_t)(c & 1) * 16u;
     const uint32_t y = h.y >> sh;
@@ -74,6 +75,32 @@ __device__ __forceinline__ ChunkScales decode_header(const uint4& h, int c)
     const uint32_t m_b = ((wv >> 4) & 0x0F0Fu) | ((z >> 2) & 0x3030u);
     const uint32_t sc = c < 2 ? sc_a : sc_b;
     const uint32_t mm = c < 2 ? m_a : m_b;
+    s.sc_lo = (float)(sc & 0xFFu);
+    s.sc_hi = (float)((sc >> 8) & 0xFFu);
+    s.m_lo = (float)(mm & 0xFFu);
+    s.m_hi = (float)((mm >> 8) & 0xFFu);
+    return s;
+}
+
+// Scales of chunk g (sub-blocks 2g, 2g+1) of a header, d unscaled; sh =
+// 16 (g & 1) and sel = all ones for g < 2, else 0 (lane constants).
+struct ChunkScalesD {
+    float d, dmin, sc_lo, sc_hi, m_lo, m_hi;
+};
+
+__device__ __forceinline__ ChunkScalesD decode_chunk(const uint4& h, uint32_t sh, uint32_t sel)
+{
+    ChunkScalesD s;
+    const half2_t dd = __builtin_bit_cast(half2_t, h.x);
+    s.d = (float)dd.x;
+    s.dmin = (float)dd.y;
+    const uint32_t y = h.y >> sh;
+    const uint32_t z = h.z >> sh;
+    const uint32_t wv = h.w >> sh;
+    const uint32_t sc_b = (wv & 0x0F0Fu) | ((y >> 2) & 0x3030u);
+    const uint32_t m_b = ((wv >> 4) & 0x0F0Fu) | ((z >> 2) & 0x3030u);
+    const uint32_t sc = ((y & 0x3F3Fu) & sel) | (sc_b & ~sel);
+    const uint32_t mm = ((z & 0x3F3Fu) & sel) | (m_b & ~sel);
     s.sc_lo = (float)(sc & 0xFFu);
     s.sc_hi = (float)((sc >> 8) & 0xFFu);
     s.m_lo = (float)(mm & 0xFFu);

@@ -200,7 +200,7 @@ gemv_dot4_lines_kernel(const uint8_t* __restrict__ w, const float* __restrict__ 
         const unsigned char* col = smem + (size_t)c * kDotCol;
         const uint4 xd = *reinterpret_cast<const uint4*>(col + g * 256 + j * 16);
         const float4 k4 = *reinterpret_cast<const float4*>(col + 1024 + g * 16);
-        const ChunkScales cs = decode_header(h, g);
+        const ChunkScales cs = decode_header(h, g, 1.0f);            // d unscaled
         const uint32_t D[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
         int cl[8], ch[8];
 #pragma unroll
@@ -210,13 +210,15 @@ gemv_dot4_lines_kernel(const uint8_t* __restrict__ w, const float* __restrict__ 
         }
         int t[6] = {0, 0, 0, 0, 0, 0};
         dot_step(xd, cl, ch, t);
-        // T_2 * 65536 is exact in f32 (|T_2| < 2^19); 256 T_1 + T_0 < 2^27
-        const float tlo = __builtin_fmaf((float)t[2], 65536.0f, (float)(t[1] * 256 + t[0]));
+        // low codes q <= 15 and digits |D2| <= 64, |D1|, |D0| <= 128 over 32
+        // elements: |T_0 + 256 T_1 + 65536 T_2| < 2^31, exact in int32.  High
+        // codes 16 q - 128 take the sum in f32 (T_2 * 65536 exact, |T_2| < 2^19;
+        // 256 T_1 + T_0 < 2^27).
+        const float tlo = (float)(t[2] * 65536 + t[1] * 256 + t[0]);
         const float thi = __builtin_fmaf((float)t[5], 65536.0f, (float)(t[4] * 256 + t[3]));
         const float ulo = k4.x * tlo;                         // sum q x, low sub-block
         const float uhi = __builtin_fmaf(k4.z, thi, k4.w);    // sum q x, high sub-block
-        const float d = cs.d24 * (1.0f / 16777216.0f);
-        acc = __builtin_fmaf(d, __builtin_fmaf(cs.sc_lo, ulo, cs.sc_hi * uhi), acc);
+        acc = __builtin_fmaf(cs.d24, __builtin_fmaf(cs.sc_lo, ulo, cs.sc_hi * uhi), acc);
         acc = __builtin_fmaf(-cs.dmin, __builtin_fmaf(cs.m_lo, k4.y, cs.m_hi * (k4.w * 0.125f)),
                              acc);
     };

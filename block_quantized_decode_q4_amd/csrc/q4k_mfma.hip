@@ -21,30 +21,6 @@
 
 namespace q4k {
 
-// Scales of chunk g (sub-blocks 2g, 2g+1) of a header; d unscaled.
-struct ChunkScalesD {
-    float d, dmin, sc_lo, sc_hi, m_lo, m_hi;
-};
-
-__device__ __forceinline__ ChunkScalesD decode_chunk(const uint4& h, uint32_t sh, uint32_t sel)
-{
-    ChunkScalesD s;
-    const half2_t dd = __builtin_bit_cast(half2_t, h.x);
-    s.d = (float)dd.x;
-    s.dmin = (float)dd.y;
-    const uint32_t y = h.y >> sh;
-    const uint32_t z = h.z >> sh;
-    const uint32_t wv = h.w >> sh;
-    const uint32_t sc_b = (wv & 0x0F0Fu) | ((y >> 2) & 0x3030u);
-    const uint32_t m_b = ((wv >> 4) & 0x0F0Fu) | ((z >> 2) & 0x3030u);
-    const uint32_t sc = ((y & 0x3F3Fu) & sel) | (sc_b & ~sel);
-    const uint32_t mm = ((z & 0x3F3Fu) & sel) | (m_b & ~sel);
-    s.sc_lo = (float)(sc & 0xFFu);
-    s.sc_hi = (float)((sc >> 8) & 0xFFu);
-    s.m_lo = (float)(mm & 0xFFu);
-    s.m_hi = (float)((mm >> 8) & 0xFFu);
-    return s;
-}
 
 // ---------------------------------------------------------------------------
 // int8 matrix-core decode (v_mfma_i32_16x16x64_i8).
