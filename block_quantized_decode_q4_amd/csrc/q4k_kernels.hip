@@ -1,5 +1,7 @@
 // q4k_kernels.hip -- HIP kernels for the Q4_K fused dequantize-and-multiply
-// GEMV on CDNA4 (gfx950, wave64).  Launchers are in q4k_api.hip.
+// GEMV on CDNA4 (gfx950, wave64): the fp32 kernels 1 (x-stager) and 2
+// (streaming), the dequantizer and the read calibration; launch plans are
+// made in q4k_api.hip.
 //
 // Problem (see include/q4k.h for the page citations): y[b][r] =
 // sum_c W[r][c] * x[b][c], W stored as GGUF Q4_K superblocks of 144 bytes /
