@@ -360,7 +360,9 @@ def test_dot4_kernel_workloads(oracle_mod, i):
                                  (33, 18432), (20, 24576),
                                  # rows of partial slabs: any start offset in a line
                                  (1, 256), (5, 768), (17, 1280), (33, 4352), (130, 11008),
-                                 (257, 5120), (16, 2304), (48, 13824), (300, 3328)])
+                                 (257, 5120), (16, 2304), (48, 13824), (300, 3328),
+                                 # at least 1024 tiles: whole rows per task
+                                 (16400, 1280), (16480, 2560)])
 def test_dot4_kernel_shapes(oracle_mod, n, k):
     w, x = synth.make_inputs(n, k, 1, seed=n + 13 * k)
     y_ref, bound = oracle_mod.gemv(w, x, n)
