@@ -31,7 +31,7 @@
 //
 // Staged x per superblock column (kDotCol bytes): four chunks of sixteen
 // 16-byte slots (D0, D1, D2, 0) in the lane order above, then eight
-// {2^-s, X} pairs (high sub-blocks keep 2^-s / 16 and 8 X).
+// {2^-s, 8 X} pairs (high sub-blocks keep 2^-s / 16).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -80,6 +80,39 @@ __device__ __forceinline__ void dot_step(const uint4& xd, const int (&cl)[8], co
 
 #undef Q4K_DOTU
 #undef Q4K_DOTB
+
+// Scales of chunk g (sub-blocks j = 2g, 2g+1) by two byte gathers with lane
+// constants.  With e = 2 (g & 1), P = (s[e], s[e+1], s[e+4], s[e+5]) and
+// Q = (s[e+8], s[e+9], s[e+8], s[e+9]):
+//   g < 2 : (sc_j, sc_j+1, m_j, m_j+1) = P & 63 (bytewise)
+//   g >= 2: the same four from the low and high nibbles of Q (bits 0-3)
+//           and bits 6-7 of P (bits 4-5)
+// (the 6-bit packing of get_scale_min_k4 in the Q4_K format description).
+struct ScaleGather {
+    uint32_t selp, selq, ma, mb, mc, md;
+};
+
+__device__ __forceinline__ ScaleGather scale_gather(int g)
+{
+    const uint32_t e = 2u * (uint32_t)(g & 1);
+    const bool lo = g < 2;
+    ScaleGather s;
+    s.selp = e | (e + 1u) << 8 | (e + 4u) << 16 | (e + 5u) << 24;
+    s.selq = e | (e + 1u) << 8 | e << 16 | (e + 1u) << 24;
+    s.ma = lo ? 0x3F3F3F3Fu : 0u;
+    s.mb = lo ? 0u : 0x30303030u;
+    s.mc = lo ? 0u : 0x00000F0Fu;
+    s.md = lo ? 0u : 0x0F0F0000u;
+    return s;
+}
+
+// bytes (sc_lo, sc_hi, m_lo, m_hi) of the lane's chunk of header h
+__device__ __forceinline__ uint32_t gather_scales(const uint4& h, const ScaleGather& s)
+{
+    const uint32_t p = __builtin_amdgcn_perm(h.z, h.y, s.selp);   // bytes 0-3: h.y, 4-7: h.z
+    const uint32_t q = __builtin_amdgcn_perm(h.w, h.w, s.selq);
+    return (p & s.ma) | ((p >> 2) & s.mb) | (q & s.mc) | ((q >> 4) & s.md);
+}
 
 // Convert 16 consecutive x values (group G of 16: column G / 16, elements
 // 16 (G % 16) ..) into digit slots; lanes G and G ^ 1 hold one sub-block and
@@ -137,8 +170,7 @@ __device__ __forceinline__ void convert_group_dot(const float4 (&v)[4], int G, b
             const float inv = __builtin_bit_cast(float, (uint32_t)(127 - sigma) << 23);
             const int sb = (G & 15) >> 1;
             *reinterpret_cast<float2*>(col + 1024 + sb * 8) =
-                (sb & 1) ? make_float2(inv * 0.0625f, 8.0f * inv * (float)XI)
-                         : make_float2(inv, inv * (float)XI);
+                make_float2((sb & 1) ? inv * 0.0625f : inv, 8.0f * inv * (float)XI);
         }
     }
 }
@@ -160,9 +192,6 @@ gemv_dot4_lines_kernel(const uint8_t* __restrict__ w, const float* __restrict__ 
     const int rows_here = min(rows_per_block, n - row0);
     const int ncg = ((S + 7) >> 3) / slabs_per_task;
     constexpr int kWaveRing = ANY ? kRing4Wave : kRingWave;
-    constexpr uint32_t kWindow = ANY ? 511u : 255u;        // ring window of a row, minus one
-    // byte offset of the lane's row within its first line (tiles start on a line)
-    const uint32_t loff = ANY ? (uint32_t)(j * 144 * S) & 127u : 0u;
 
     // LDS: staged x (S columns), the line rings, row sums of slab groups
     const size_t xbytes = (size_t)S * kDotCol;
@@ -191,16 +220,12 @@ gemv_dot4_lines_kernel(const uint8_t* __restrict__ w, const float* __restrict__ 
         }
     };
 
-    float acc = 0.f;
-    auto step = [&](int c, const unsigned char* rr, uint32_t b0) {
-        const uint32_t b = b0 + loff;
-        const uint4 h = *reinterpret_cast<const uint4*>(rr + (b & kWindow));
-        const uint4 q0 = *reinterpret_cast<const uint4*>(rr + ((b + 16u + 32u * (uint32_t)g) & kWindow));
-        const uint4 q1 = *reinterpret_cast<const uint4*>(rr + ((b + 32u + 32u * (uint32_t)g) & kWindow));
-        const unsigned char* col = smem + (size_t)c * kDotCol;
+    // d terms and 8 x the dmin terms of the lane's (row, chunk) sum
+    float acc = 0.f, accm = 0.f;
+    const ScaleGather sg = scale_gather(g);
+    auto dot_math = [&](const uint4& h, const uint4& q0, const uint4& q1, const unsigned char* col) {
         const uint4 xd = *reinterpret_cast<const uint4*>(col + g * 256 + j * 16);
         const float4 k4 = *reinterpret_cast<const float4*>(col + 1024 + g * 16);
-        const ChunkScales cs = decode_header(h, g, 1.0f);            // d unscaled
         const uint32_t D[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
         int cl[8], ch[8];
 #pragma unroll
@@ -210,21 +235,28 @@ gemv_dot4_lines_kernel(const uint8_t* __restrict__ w, const float* __restrict__ 
         }
         int t[6] = {0, 0, 0, 0, 0, 0};
         dot_step(xd, cl, ch, t);
+        const uint32_t sm = gather_scales(h, sg);
+        const half2_t dd = __builtin_bit_cast(half2_t, h.x);
         // low codes q <= 15 and digits |D2| <= 64, |D1|, |D0| <= 128 over 32
         // elements: |T_0 + 256 T_1 + 65536 T_2| < 2^31, exact in int32.  High
         // codes 16 q - 128 take the sum in f32 (T_2 * 65536 exact, |T_2| < 2^19;
         // 256 T_1 + T_0 < 2^27).
-        const float tlo = (float)(t[2] * 65536 + t[1] * 256 + t[0]);
+        const float tlo = (float)(((t[2] << 8) + t[1]) * 256 + t[0]);
         const float thi = __builtin_fmaf((float)t[5], 65536.0f, (float)(t[4] * 256 + t[3]));
         const float ulo = k4.x * tlo;                         // sum q x, low sub-block
         const float uhi = __builtin_fmaf(k4.z, thi, k4.w);    // sum q x, high sub-block
-        acc = __builtin_fmaf(cs.d24, __builtin_fmaf(cs.sc_lo, ulo, cs.sc_hi * uhi), acc);
-        acc = __builtin_fmaf(-cs.dmin, __builtin_fmaf(cs.m_lo, k4.y, cs.m_hi * (k4.w * 0.125f)),
+        acc = __builtin_fmaf((float)dd.x,
+                             __builtin_fmaf((float)(sm & 0xFFu), ulo,
+                                            (float)((sm >> 8) & 0xFFu) * uhi),
                              acc);
+        accm = __builtin_fmaf((float)dd.y,
+                              __builtin_fmaf((float)((sm >> 16) & 0xFFu), k4.y,
+                                             (float)(sm >> 24) * k4.w),
+                              accm);
     };
     auto task_end = [&](int task) {
         const int r = (task / ncg) * 16 + j;
-        float v = acc;
+        float v = __builtin_fmaf(-0.125f, accm, acc);
         v += __shfl_xor(v, 16, 64);
         v += __shfl_xor(v, 32, 64);
         if (g == 0 && r < rows_here) {
@@ -235,11 +267,42 @@ gemv_dot4_lines_kernel(const uint8_t* __restrict__ w, const float* __restrict__ 
             }
         }
         acc = 0.f;
+        accm = 0.f;
     };
     if constexpr (ANY) {
+        // row j starts loff bytes into its first line (tiles start on a
+        // line); pieces wrap in the row's four-line window individually
+        constexpr uint32_t kWindow = 511u;
+        const uint32_t loff = (uint32_t)(j * 144 * S) & 127u;
+        auto step = [&](int c, const unsigned char* rr, uint32_t b0) {
+            const uint32_t b = b0 + loff;
+            const uint4 h = *reinterpret_cast<const uint4*>(rr + (b & kWindow));
+            const uint4 q0 =
+                *reinterpret_cast<const uint4*>(rr + ((b + 16u + 32u * (uint32_t)g) & kWindow));
+            const uint4 q1 =
+                *reinterpret_cast<const uint4*>(rr + ((b + 32u + 32u * (uint32_t)g) & kWindow));
+            dot_math(h, q0, q1, smem + (size_t)c * kDotCol);
+        };
         line_stream_any<NW>(w, x, n, S, rows_per_block, slabs_per_task, ring, issue_x, convert_x,
                             step, task_end);
     } else {
+        // superblock c' of a slab starts at 144 c' mod 256 in the two-line
+        // window of its ring row: the header at that compile-time offset, the
+        // lane's 32 code bytes 16 + 32 g further, mod 256 (both 16-byte
+        // halves on the same side of the wrap), so their eight addresses are
+        // lane constants
+        const unsigned char* qa[8];
+#pragma unroll
+        for (int cp = 0; cp < 8; ++cp) {
+            qa[cp] = ring + j * kRingRow + ((144u * (uint32_t)cp + 16u + 32u * (uint32_t)g) & 255u);
+        }
+        auto step = [&](int c, const unsigned char* rr, uint32_t b0) {
+            const int cp = (int)(b0 / 144u);         // b0 = 144 cp
+            const uint4 h = *reinterpret_cast<const uint4*>(rr + (b0 & 255u));
+            const uint4 q0 = *reinterpret_cast<const uint4*>(qa[cp]);
+            const uint4 q1 = *reinterpret_cast<const uint4*>(qa[cp] + 16);
+            dot_math(h, q0, q1, smem + (size_t)c * kDotCol);
+        };
         line_stream<NW, P>(w, x, n, S, rows_per_block, slabs_per_task, ring, issue_x, convert_x,
                            step, task_end);
     }

@@ -40,9 +40,12 @@ __device__ __forceinline__ uint4 load_line_nt(const uint8_t* p)
 // w + NW, ...  Calls, in order: issue_x() (the x loads), the first P lines
 // of weights go out, convert_x() (x into LDS), a workgroup barrier, then
 // step(c, rr, b0) for every superblock column c of the wave's tasks in order
-// (rr: the ring row of the lane's tile row j, b0: the superblock's byte
-// offset in that row's two-line ring window, mod 256) and task_end(task)
-// after each task's last slab.
+// (rr: the ring row of the lane's tile row j, b0 = 144 (c mod 8): the
+// superblock's byte offset in that row's two-line ring window, mod 256; a
+// compile-time constant) and task_end(task) after each task's last slab.
+// Line l of every slab goes to ring slot l mod 2: the previous slab's last
+// line (slot 0) is dead once its last superblock has been read, and the
+// wave's LDS accesses complete in order.
 template <int NW, int P, typename IssueX, typename ConvertX, typename Step, typename TaskEnd>
 __device__ __forceinline__ void line_stream(const uint8_t* __restrict__ w,
                                             const float* __restrict__ x, int n, int S,
@@ -143,7 +146,6 @@ __device__ __forceinline__ void line_stream(const uint8_t* __restrict__ w,
     for (int sig = 0; sig < my_slabs; ++sig) {
         int tile, slab;
         slab_of(sig, tile, slab);
-        const uint32_t par = (uint32_t)slab & 1u;      // parity of line 9*slab
         const SlabBase cur = slab_base(sig);
         const SlabBase nxt = slab_base(sig + 1);
 #pragma unroll
@@ -152,7 +154,7 @@ __device__ __forceinline__ void line_stream(const uint8_t* __restrict__ w,
 #pragma unroll
             for (int l = (cp == 0 ? 0 : cp + 1); l <= cp + 1; ++l) {
                 const int slot = l % P;
-                const uint32_t lpos = ((par + (uint32_t)l) & 1u) * 128u + 16u * (uint32_t)lunit;
+                const uint32_t lpos = (uint32_t)(l & 1) * 128u + 16u * (uint32_t)lunit;
                 *reinterpret_cast<uint4*>(ring + lrow * kRingRow + lpos) = lines[slot][0];
                 *reinterpret_cast<uint4*>(ring + (8 + lrow) * kRingRow + lpos) = lines[slot][1];
                 // memory operations stay in order here (the refill after the
@@ -165,7 +167,7 @@ __device__ __forceinline__ void line_stream(const uint8_t* __restrict__ w,
                 lines[slot][1] = load_line_nt(p[1]);
             }
             // superblock c = 8 slab + cp, in the ring of tile row j
-            step(8 * slab + cp, ring + j * kRingRow, (uint32_t)(144 * cp) + par * 128u);
+            step(8 * slab + cp, ring + j * kRingRow, (uint32_t)(144 * cp));
         }
         if (sig % slabs_per_task == slabs_per_task - 1) {
             task_end(wave + (sig / slabs_per_task) * NW);
