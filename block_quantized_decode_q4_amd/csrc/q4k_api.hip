@@ -130,12 +130,13 @@ int make_plan_lines(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t
                          : kernel == 3 ? q4k::dot4_lds_bytes(S, nw)
                                        : q4k::lines_lds_bytes(S, (int)m, nw);
     if (!(o && o->cols_per_task)) {
-        // whole rows per task when there are at least four tiles per CU of a
-        // 256-CU part (no row sums to combine), else one slab per task for
-        // more parallel tasks; whole rows too when the per-slab row sums do
-        // not fit the LDS (choices measured on MI355X)
+        // whole rows per task when the workgroup has a tile for every wave
+        // (no row sums to combine), else one slab per task, so that every
+        // wave streams; whole rows too when the per-slab row sums do not fit
+        // the LDS (choices measured on MI355X: with fewer tiles than waves,
+        // whole rows leave waves idle, 0.3-0.8 us on 16384-28672-row shapes)
         const bool fits = lds_x + (size_t)nslabs * rpb * 4 * m <= lds_max;
-        spt = (ntiles >= 1024 || !fits) ? nslabs : 1;
+        spt = (rpb / 16 >= nw || !fits) ? nslabs : 1;
     }
     const int64_t ncg = nslabs / spt;
     if (rpb > kInt32Max / (ncg * m)) {

@@ -179,15 +179,15 @@ LINES_VARIANTS = [
 
 
 def _lines_auto_cols(n, k, m, opts):
-    """The line-streamed kernel's automatic column grouping: whole rows for
-    at least 1024 tiles of 16 rows or when the per-slab row sums do not fit
-    the LDS, else one slab of 8 columns."""
+    """The line-streamed kernel's automatic column grouping: whole rows when
+    the workgroup has a 16-row tile for every wave or when the per-slab row
+    sums do not fit the LDS, else one slab of 8 columns."""
     S = k // 256
     ntiles = (n + 15) // 16
     rpb = opts.get("rows_per_block") or 16 * ((ntiles + 255) // 256)
     nw = opts.get("waves_per_block", 8)
     fits = (S * m + 1) * 960 + nw * 4352 + (S // 8) * rpb * 4 * m <= 160 * 1024
-    return S if (ntiles >= 1024 or not fits) else 8
+    return S if (rpb // 16 >= nw or not fits) else 8
 
 
 def _lines_check(w_d, w, x, n, k, y_ref, bound, what):
@@ -305,15 +305,15 @@ DOT4_VARIANTS = [
 
 def _dot4_auto_cols(n, k, opts):
     """Automatic column grouping of the vector-ALU line-streamed kernel:
-    whole rows for at least 1024 tiles or when the per-slab row sums do not
-    fit the LDS, else one slab of 8 columns."""
+    whole rows when the workgroup has a tile for every wave or when the
+    per-slab row sums do not fit the LDS, else one slab of 8 columns."""
     S = k // 256
     nslabs = (S + 7) // 8
     ntiles = (n + 15) // 16
     rpb = opts.get("rows_per_block") or 16 * ((ntiles + 255) // 256)
     nw = opts.get("waves_per_block", 8)
     fits = S * 1088 + nw * _dot4_ring(S) + nslabs * rpb * 4 <= 160 * 1024
-    return 8 * nslabs if (ntiles >= 1024 or not fits) else 8
+    return 8 * nslabs if (rpb // 16 >= nw or not fits) else 8
 
 
 def _dot4_ring(S):
@@ -361,8 +361,9 @@ def test_dot4_kernel_workloads(oracle_mod, i):
                                  # rows of partial slabs: any start offset in a line
                                  (1, 256), (5, 768), (17, 1280), (33, 4352), (130, 11008),
                                  (257, 5120), (16, 2304), (48, 13824), (300, 3328),
-                                 # at least 1024 tiles: whole rows per task
-                                 (16400, 1280), (16480, 2560)])
+                                 # a 16-row tile for each of the 8 waves of a
+                                 # workgroup: whole rows per task
+                                 (28688, 1280), (28720, 2560)])
 def test_dot4_kernel_shapes(oracle_mod, n, k):
     w, x = synth.make_inputs(n, k, 1, seed=n + 13 * k)
     y_ref, bound = oracle_mod.gemv(w, x, n)
