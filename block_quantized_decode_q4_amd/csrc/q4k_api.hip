@@ -77,10 +77,11 @@ int device_lds_max(size_t* out)
 
 // Plan of the line-streamed kernels (weights 128-byte aligned, m <= 8):
 // kernel 3 (m = 1, integer dot products on the vector ALU, any k), kernel 4
-// (one MFMA group per vector) and kernel 5 (one MFMA per sub-block and quad
-// of vectors), both for k a multiple of 2048.  A task is a 16-row tile
-// times a group of slabs of eight superblock columns (the last slab of a
-// row may be partial); x (every vector) is staged whole.
+// (one MFMA group per vector), kernel 5 (one MFMA per sub-block and quad
+// of vectors) and kernel 6 (kernel 5 with x converted per column by each
+// wave), all three for k a multiple of 2048.  A task is a 16-row tile times
+// a group of slabs of eight superblock columns (the last slab of a row may
+// be partial); x (every vector) is staged whole, except for kernel 6.
 int make_plan_lines(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t lds_max,
                     GemvPlan* p, int kernel)
 {
@@ -103,7 +104,7 @@ int make_plan_lines(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t
     if (nw == 16 && ring == 9) {
         return Q4K_ERR_UNSUPPORTED;    // 1024-lane workgroups cap a lane at 128 VGPRs
     }
-    if ((m > 1 || kernel == 5) && (nw != 8 || ring != 3)) {
+    if ((m > 1 || kernel >= 5) && (nw != 8 || ring != 3)) {
         return Q4K_ERR_UNSUPPORTED;    // several vectors: eight waves, three lines in flight
     }
     if (kernel == 3 && (m != 1 || S * 16 > 4 * 64 * nw || (S % 8 != 0 && ring != 3))) {
@@ -126,7 +127,8 @@ int make_plan_lines(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t
         // all of x, which costs as much as decoding a few tiles
         rpb = 16 * ((ntiles + 255) / 256);
     }
-    const size_t lds_x = kernel == 5   ? q4k::sub_lds_bytes(S, (int)m)
+    const size_t lds_x = kernel == 6   ? q4k::jit_lds_bytes((int)m)
+                         : kernel == 5 ? q4k::sub_lds_bytes(S, (int)m)
                          : kernel == 3 ? q4k::dot4_lds_bytes(S, nw)
                                        : q4k::lines_lds_bytes(S, (int)m, nw);
     if (!(o && o->cols_per_task)) {
@@ -193,10 +195,11 @@ int auto_kernel(int64_t n, int64_t k, int64_t m, const q4k_launch* o, bool w_ali
     GemvPlan lp;
     if (m != 1) {
         // several vectors: a line-streamed kernel whenever one applies; the
-        // sub-block kernel from three vectors on
+        // sub-block kernel from three vectors on; per-wave x conversion when
+        // no whole x stage fits the LDS
         if (!any_option(o) && w_aligned128) {
             const int first = m >= 3 ? 5 : 4;
-            for (int kern : {first, 9 - first}) {
+            for (int kern : {first, 9 - first, 6}) {
                 if (make_plan_lines(n, k, m, nullptr, lds_max, &lp, kern) == Q4K_OK &&
                     lp.lds_bytes <= lds_max) {
                     return kern;
@@ -242,7 +245,7 @@ int make_plan(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t lds_m
     const int nchunks = (nspans + spc - 1) / spc;
 
     const int kernel = (o && o->kernel) ? o->kernel : auto_kernel(n, k, m, o, w_aligned128, lds_max);
-    if (kernel < 1 || kernel > 5 || ((kernel == 2 || kernel == 3) && m != 1)) {
+    if (kernel < 1 || kernel > 6 || ((kernel == 2 || kernel == 3) && m != 1)) {
         return Q4K_ERR_UNSUPPORTED;
     }
     if (kernel >= 3) {

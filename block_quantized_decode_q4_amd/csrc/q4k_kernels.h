@@ -30,8 +30,9 @@ struct GemvPlan {
     size_t lds_bytes;
     int kernel;            // 1: x-stager, 2: streaming, 3: line-streamed int8 dot products
                            // (vector ALU), 4: line-streamed int8 matrix-core,
-                           // 5: sub-block int8 matrix-core
-    int ring_depth;        // kernel 2: rows in flight per wave; 3-5: lines in flight
+                           // 5: sub-block int8 matrix-core, 6: the same with x
+                           // converted per column by each wave
+    int ring_depth;        // kernel 2: rows in flight per wave; 3-6: lines in flight
     int rows_per_task;     // streaming kernel: rows per wave task
     int cols_per_task;     // line-streamed kernels: superblock columns per task
 };
@@ -42,6 +43,7 @@ hipError_t launch_gemv_mfma(const GemvPlan& p, const void* w, const float* x, fl
                             hipStream_t stream);
 size_t lines_lds_bytes(int S, int m, int waves);
 size_t sub_lds_bytes(int S, int m);
+size_t jit_lds_bytes(int m);
 hipError_t launch_gemv_dot4(const GemvPlan& p, const void* w, const float* x, float* y,
                             hipStream_t stream);
 size_t dot4_lds_bytes(int S, int waves);

@@ -43,6 +43,8 @@ __device__ __forceinline__ uint4 load_line_nt(const uint8_t* p)
 // (rr: the ring row of the lane's tile row j, b0 = 144 (c mod 8): the
 // superblock's byte offset in that row's two-line ring window, mod 256; a
 // compile-time constant) and task_end(task) after each task's last slab.
+// A step taking (c, cn, rr, b0) also gets cn, the first column of the
+// wave's next slab (of its last slab after the last one).
 // Line l of every slab goes to ring slot l mod 2: the previous slab's last
 // line (slot 0) is dead once its last superblock has been read, and the
 // wave's LDS accesses complete in order.
@@ -144,8 +146,9 @@ __device__ __forceinline__ void line_stream(const uint8_t* __restrict__ w,
     __syncthreads();
 
     for (int sig = 0; sig < my_slabs; ++sig) {
-        int tile, slab;
+        int tile, slab, tile_n, slab_n;
         slab_of(sig, tile, slab);
+        slab_of(sig + 1, tile_n, slab_n);      // clamped: the last slab again at the end
         const SlabBase cur = slab_base(sig);
         const SlabBase nxt = slab_base(sig + 1);
 #pragma unroll
@@ -166,8 +169,13 @@ __device__ __forceinline__ void line_stream(const uint8_t* __restrict__ w,
                 lines[slot][0] = load_line_nt(p[0]);
                 lines[slot][1] = load_line_nt(p[1]);
             }
-            // superblock c = 8 slab + cp, in the ring of tile row j
-            step(8 * slab + cp, ring + j * kRingRow, (uint32_t)(144 * cp));
+            // superblock c = 8 slab + cp, in the ring of tile row j (and, for
+            // a step that looks ahead, the first column of the next slab)
+            if constexpr (std::is_invocable_v<Step&, int, int, unsigned char*, uint32_t>) {
+                step(8 * slab + cp, 8 * slab_n, ring + j * kRingRow, (uint32_t)(144 * cp));
+            } else {
+                step(8 * slab + cp, ring + j * kRingRow, (uint32_t)(144 * cp));
+            }
         }
         if (sig % slabs_per_task == slabs_per_task - 1) {
             task_end(wave + (sig / slabs_per_task) * NW);

@@ -9,8 +9,12 @@
 //    superblock and vector (one 16-row tile, one vector per MFMA group);
 //    automatic for m = 2.  With m = 1 it runs only when asked for, as the
 //    measured matrix-core counterpart of the vector-ALU kernel (q4k_dpp.hip).
-//  * gemv_i8_sub_kernel<NW, XC, NQ>: one v_mfma_i32_16x16x32_i8 per
-//    32-element sub-block and quad of vectors; automatic for m >= 3.
+//  * gemv_i8_sub_kernel<NW, XC, NQ, false> (kernel 5): one
+//    v_mfma_i32_16x16x32_i8 per 32-element sub-block and quad of vectors;
+//    automatic for m >= 3.
+//  * gemv_i8_sub_kernel<NW, XC, NQ, true> (kernel 6): the same decode with
+//    x converted per column by each wave for itself, for batches whose x
+//    does not fit the LDS as one stage (m k large).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -421,16 +425,15 @@ __device__ __forceinline__ void convert4_sb(const float4 (&v)[4], unsigned char*
                 make_uint2(dig[l][2 * h], dig[l][2 * h + 1]);
         }
     }
-    if (bq == 0 && half == 0) {
-        *reinterpret_cast<uint2*>(blk + kSbZero) = make_uint2(0, 0);
-    }
+    // the zero slot and the sub-block constants: every lane of a pair holds
+    // the same values (pair max and sum by DPP), so both store them -- no
+    // branch inside the callers' unrolled loops
+    *reinterpret_cast<uint2*>(blk + kSbZero) = make_uint2(0, 0);
     const uint32_t us2 = usum + (uint32_t)dpp_i<0xB1>((int)usum);
     const int XI = (int)us2 - 32 * 0x808080;
-    if (half == 0) {
-        const float inv = __builtin_bit_cast(float, (uint32_t)(127 - sigma) << 23);
-        *reinterpret_cast<float2*>(grp + kSbQuad + bq * kSbConst + s * 8) =
-            make_float2((s & 1) ? inv * 0.0625f : inv, inv * (float)XI);
-    }
+    const float inv = __builtin_bit_cast(float, (uint32_t)(127 - sigma) << 23);
+    *reinterpret_cast<float2*>(grp + kSbQuad + bq * kSbConst + s * 8) =
+        make_float2((s & 1) ? inv * 0.0625f : inv, inv * (float)XI);
 }
 
 // The eight sub-block scales and mins of a header as floats.
@@ -459,7 +462,21 @@ __device__ __forceinline__ RowScales decode_row(const uint4& h)
     return r;
 }
 
-template <int NW, int XC, int NQ>
+// Columns of x a wave of kernel 6 holds in registers ahead of its step: with
+// four, waiting for a column's x (loads complete in order) never waits for
+// a weight line before the line stream itself would (the lines are three
+// ahead); two vector quads take two, as 4 x 32 registers do not fit.
+template <int NQ>
+constexpr int jit_ahead()
+{
+    return NQ == 1 ? 4 : 2;
+}
+
+// JIT = false (kernel 5): x staged whole in LDS before the stream.  JIT =
+// true (kernel 6): each wave converts the x column of each of its steps for
+// itself into its own LDS groups, from registers loaded jit_ahead columns
+// earlier -- for batches whose whole x stage does not fit the LDS.
+template <int NW, int XC, int NQ, bool JIT>
 __global__ void __launch_bounds__(NW * 64)
 gemv_i8_sub_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
                    float* __restrict__ y, int n, int S, int m, int rows_per_block,
@@ -479,10 +496,11 @@ gemv_i8_sub_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
     const int ncg = (S >> 3) / slabs_per_task;
     const int k = S * 256;
 
-    // LDS: staged x (S columns x NQ quads and a spare group), the line
-    // rings, row sums
+    // LDS: staged x (S columns x NQ quads and a spare group; JIT: NQ groups
+    // per wave), the line rings, row sums
     const int ngroups = S * NQ;
-    const size_t xbytes = (size_t)(ngroups + 1) * kSbGroup;
+    const size_t xbytes = JIT ? (size_t)NW * NQ * kSbGroup : (size_t)(ngroups + 1) * kSbGroup;
+    unsigned char* xw = smem + (JIT ? (size_t)wave * NQ * kSbGroup : 0);
     unsigned char* ring = smem + xbytes + wave * kRingWave;
     float* ypart = reinterpret_cast<float*>(smem + xbytes + NW * kRingWave);
 
@@ -499,19 +517,39 @@ gemv_i8_sub_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
         }
     };
     auto zero_past = [&](int q0, float4 (&v)[4]) {
-        const bool past = 4 * (min(q0, ngroups - 1) % NQ) + (lane >> 4) >= m;
+        const uint32_t keep = 4 * (min(q0, ngroups - 1) % NQ) + (lane >> 4) >= m ? 0u : ~0u;
+        auto z = [&](float f) { return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, f) & keep); };
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            v[i] = past ? make_float4(0.f, 0.f, 0.f, 0.f) : v[i];
+            v[i] = make_float4(z(v[i].x), z(v[i].y), z(v[i].z), z(v[i].w));
         }
     };
+    // JIT: slot a holds the x of a column with c mod kA = a (first column
+    // of the wave's first slab: c_first)
+    constexpr int kA = JIT ? jit_ahead<NQ>() : 1;
+    float4 xa[kA][NQ][4];
+    const int ntasks = ((rows_here + 15) >> 4) * ncg;
+    const int c_first = 8 * ((min(wave, ntasks - 1) % ncg) * slabs_per_task);
     auto issue_x = [&]() {
+        if constexpr (JIT) {
+#pragma unroll
+            for (int a = 0; a < kA; ++a) {
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) {
+                    load_group((c_first + a) * NQ + q, xa[a][q]);
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < XC; ++i) {
             load_group(wave + i * NW, xv[i]);
         }
     };
     auto convert_x = [&]() {
+        if constexpr (JIT) {
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < XC; ++i) {
             const int q0 = wave + i * NW;
@@ -531,7 +569,9 @@ gemv_i8_sub_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
     for (int q = 0; q < NQ; ++q) {
         acc[q] = 0.f;
     }
-    auto step = [&](int c, const unsigned char* rr, uint32_t b0) {
+    // one superblock of the lane's tile (ring row rr, offset b0) against
+    // the x groups of its column at grp0, grp0 + kSbGroup, ...
+    auto decode = [&](const unsigned char* rr, uint32_t b0, const unsigned char* grp0) {
         const uint4 hdr = *reinterpret_cast<const uint4*>(rr + (b0 & 255u));
         uint2 raw[4];
 #pragma unroll
@@ -550,7 +590,7 @@ gemv_i8_sub_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
         const RowScales rs = decode_row(hdr);
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
-            const unsigned char* grp = smem + (size_t)(c * NQ + q) * kSbGroup;
+            const unsigned char* grp = grp0 + (size_t)q * kSbGroup;
             const float4* cst = reinterpret_cast<const float4*>(grp + kSbQuad + g * kSbConst);
             float t1 = 0.f, t2 = 0.f;
 #pragma unroll
@@ -574,6 +614,30 @@ gemv_i8_sub_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
             acc[q] = __builtin_fmaf(-rs.dmin, t2, acc[q]);
         }
     };
+    auto step = [&](int c, const unsigned char* rr, uint32_t b0) {
+        decode(rr, b0, smem + (size_t)c * NQ * kSbGroup);
+    };
+    // JIT: convert column c (slot c mod kA) into the wave's groups, refill
+    // the slot with the column kA on (cn: first column of the next slab),
+    // then decode; the groups are rewritten only after this step's reads of
+    // them (the wave's LDS accesses complete in order)
+    auto step_jit = [&](int c, int cn, const unsigned char* rr, uint32_t b0) {
+        const int cp = (int)(b0 / 144u);                 // b0 = 144 cp
+        float4 (&v)[NQ][4] = xa[JIT ? cp % kA : 0];
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            zero_past(c * NQ + q, v[q]);
+            convert4_sb(v[q], xw + (size_t)q * kSbGroup, lane);
+        }
+        const int ca = cp + kA < 8 ? c + kA : cn + cp + kA - 8;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            load_group(ca * NQ + q, v[q]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        decode(rr, b0, xw);
+    };
     auto task_end = [&](int task) {
         const int r = (task / ncg) * 16 + j;
 #pragma unroll
@@ -589,8 +653,13 @@ gemv_i8_sub_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
             acc[q] = 0.f;
         }
     };
-    line_stream<NW, 3>(w, x, n, S, rows_per_block, slabs_per_task, ring, issue_x, convert_x, step,
-                       task_end);
+    if constexpr (JIT) {
+        line_stream<NW, 3>(w, x, n, S, rows_per_block, slabs_per_task, ring, issue_x, convert_x,
+                           step_jit, task_end);
+    } else {
+        line_stream<NW, 3>(w, x, n, S, rows_per_block, slabs_per_task, ring, issue_x, convert_x,
+                           step, task_end);
+    }
 
     if (ncg > 1) {
         __syncthreads();
@@ -606,12 +675,13 @@ gemv_i8_sub_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
     }
 }
 
-template <int XC, int NQ>
+template <int XC, int NQ, bool JIT = false>
 static hipError_t launch_sub_x(const GemvPlan& p, const uint8_t* w, const float* x, float* y,
                                hipStream_t stream)
 {
-    hipLaunchKernelGGL((gemv_i8_sub_kernel<8, XC, NQ>), dim3(p.grid), dim3(512), p.lds_bytes,
-                       stream, w, x, y, p.n, p.S, p.m, p.rows_per_block, p.cols_per_task / 8);
+    hipLaunchKernelGGL((gemv_i8_sub_kernel<8, XC, NQ, JIT>), dim3(p.grid), dim3(512),
+                       p.lds_bytes, stream, w, x, y, p.n, p.S, p.m, p.rows_per_block,
+                       p.cols_per_task / 8);
     return hipGetLastError();
 }
 
@@ -677,6 +747,10 @@ hipError_t launch_gemv_mfma(const GemvPlan& p, const void* w, const float* x, fl
         if (p.m > 4) return launch_sub<2>(p, wb, x, y, stream);
         return launch_sub<1>(p, wb, x, y, stream);
     }
+    if (p.kernel == 6) {
+        if (p.m > 4) return launch_sub_x<1, 2, true>(p, wb, x, y, stream);
+        return launch_sub_x<1, 1, true>(p, wb, x, y, stream);
+    }
     switch (p.m) {
     case 1: break;
     case 2: return launch_lines_m<2>(p, wb, x, y, stream);
@@ -696,6 +770,12 @@ size_t sub_lds_bytes(int S, int m)
 {
     const int nq = (m + 3) / 4;
     return (size_t)(S * nq + 1) * kSbGroup + (size_t)8 * kRingWave;
+}
+
+size_t jit_lds_bytes(int m)
+{
+    const int nq = (m + 3) / 4;
+    return (size_t)8 * nq * kSbGroup + (size_t)8 * kRingWave;
 }
 
 size_t lines_lds_bytes(int S, int m, int waves)

@@ -109,15 +109,18 @@ const char* q4k_status_string(int rc);
  *   4  line-streamed int8 matrix-core (m <= 8), one MFMA group per vector
  *   5  sub-block int8 matrix-core (m <= 8), one MFMA per sub-block and quad
  *      of vectors
- * Kernels 3-5 need w 128-byte aligned and their staged x plus line rings
- * within the LDS; kernels 4 and 5 also k % 2048 == 0 (rows of whole 8-
+ *   6  kernel 5 with x converted one superblock column at a time by each
+ *      wave for itself (no whole x stage: any k)
+ * Kernels 3-6 need w 128-byte aligned and their staged x plus line rings
+ * within the LDS; kernels 4-6 also k % 2048 == 0 (rows of whole 8-
  * superblock slabs), kernel 3 takes any k up to 4096 * waves_per_block (rows
  * of partial slabs with four-line rings and three lines in flight).
  * Automatic choice: m = 1 kernel 3 when it applies and the weights take at
  * least 16 MiB, else kernel 2 (the matrix cores only when asked for); m > 1
  * kernel 5 for m >= 3, kernel 4 for m = 2, the other of the two if only it
- * fits, else kernel 1.  With kernel = 0 and another field set, m = 1 uses
- * the streaming kernel and m > 1 the x-stager.
+ * fits, else kernel 6 when it fits, else kernel 1.  With kernel = 0 and
+ * another field set, m = 1 uses the streaming kernel and m > 1 the
+ * x-stager.
  *
  * x is staged in LDS in spans of 4096 elements per vector.  The single-stage
  * variant holds all of x at once; the K-chunked variant stages
@@ -134,7 +137,7 @@ typedef struct q4k_launch {
     int32_t rows_per_wave;    /* rows a wave decodes per pass: 0 auto, 1, 2 or 4   */
     int32_t waves_per_block;  /* 0 auto, 4 or 8; 16 for kernels 2-4 at m = 1       */
     int32_t x_in_registers;   /* 0 auto, 1 keep x in VGPRs (one span, m = 1), 2 LDS */
-    int32_t kernel;           /* 0 auto, else 1-5 as listed above                  */
+    int32_t kernel;           /* 0 auto, else 1-6 as listed above                  */
     int32_t ring_depth;       /* loads in flight per wave, 0 auto: streaming 1..4
                                  rows; line-streamed 3 or 9 lines                  */
     int32_t rows_per_task;    /* streaming: rows per wave task, 0 auto, >= 1       */

@@ -105,7 +105,7 @@ def test_launch_struct_matches_header():
 def test_gemv_ex_kernel_option_refusals(lib):
     """Options that no kernel can honour are refused before any HIP call."""
     cases = [
-        (dict(kernel=6), 16, 2048, 1),                       # kernels 1-5 only
+        (dict(kernel=7), 16, 2048, 1),                       # kernels 1-6 only
         (dict(kernel=-1), 16, 2048, 1),
         (dict(kernel=2), 16, 2048, 2),                       # streaming: one vector
         (dict(kernel=3), 16, 4096, 2),                       # vector-ALU lines: one vector
@@ -123,6 +123,9 @@ def test_gemv_ex_kernel_option_refusals(lib):
         (dict(kernel=5), 16, 1024, 1),                       # k not a multiple of 2048
         (dict(kernel=5, waves_per_block=4), 16, 4096, 2),    # eight waves only
         (dict(kernel=5, ring_depth=9), 16, 4096, 2),         # three lines in flight only
+        (dict(kernel=6), 16, 1024, 2),                       # k not a multiple of 2048
+        (dict(kernel=6, waves_per_block=16), 16, 4096, 2),   # eight waves only
+        (dict(kernel=6, ring_depth=9), 16, 4096, 8),         # three lines in flight only
         (dict(kernel=1, cols_per_task=8), 16, 4096, 1),      # line-streamed options only
         (dict(kernel=2, cols_per_task=8), 16, 4096, 1),
     ]

@@ -285,6 +285,61 @@ def test_sub_kernel_workload(oracle_mod):
     assert_within(y, y_ref, bound, "sub-block workload 4")
 
 
+# kernel 6: the sub-block decode with x converted one superblock column at a
+# time by each wave for itself (no whole x stage), automatic for batches
+# whose whole x stage does not fit the LDS.  Its digits, MFMAs and sums are
+# those of kernel 5 in the same order, so where both run with the same
+# column grouping they give bit-identical y.
+@pytest.mark.parametrize("n,k,m", [(300, 4096, 2), (17, 2048, 3), (130, 4096, 8), (64, 4096, 5),
+                                   (33, 2048, 8), (40, 8192, 4), (1, 2048, 6), (64, 4096, 1),
+                                   # no whole x stage fits: automatic kernel 6
+                                   (130, 14336, 8), (48, 28672, 3), (257, 16384, 4),
+                                   (20, 22528, 7)])
+def test_jit_kernel(oracle_mod, n, k, m):
+    w, x = synth.make_inputs(n, k, m, seed=n * 29 + k + 5 * m)
+    y_ref, bound = oracle_mod.gemv(w, x, n)
+    w_d = dev(w)
+    _say("per-wave x kernel n=%d k=%d m=%d" % (n, k, m))
+    y = run_gemv(w_d, x, n, k, m, kernel=6, cols_per_task=8)
+    assert_within(y, y_ref, bound, "per-wave x m=%d" % m)
+    try:
+        y5 = run_gemv(w_d, x, n, k, m, kernel=5, cols_per_task=8)
+    except q4k.Q4KError as e:
+        assert e.rc == q4k.Q4K_ERR_UNSUPPORTED
+    else:
+        assert np.array_equal(y5.view(np.uint32), y.view(np.uint32))
+    for opts in (dict(rows_per_block=48, cols_per_task=8), dict(rows_per_block=16, cols_per_task=8),
+                 dict(rows_per_block=200, cols_per_task=8)):
+        y2 = run_gemv(w_d, x, n, k, m, kernel=6, **opts)
+        assert np.array_equal(y2.view(np.uint32), y.view(np.uint32)), opts
+    y3 = run_gemv(w_d, x, n, k, m, kernel=6, cols_per_task=k // 256)
+    assert_within(y3, y_ref, bound, "per-wave x whole rows m=%d" % m)
+    if m > 1:
+        y4 = run_gemv(w_d, x, n, k, m)         # automatic kernel
+        assert_within(y4, y_ref, bound, "automatic m=%d k=%d" % (m, k))
+
+
+def test_jit_kernel_ffn_down_batch8(oracle_mod):
+    """The FFN-down shape (4096 x 14336) with eight vectors: the automatic
+    plan (kernel 6, no whole x stage fits) against the oracle."""
+    n, k, m = 4096, 14336, 8
+    w, x = synth.make_inputs(n, k, m, seed=4096 + 14336 + 8)
+    y_ref, bound = oracle_mod.gemv(w, x, n)
+    _say("automatic n=%d k=%d m=%d" % (n, k, m))
+    y = run_gemv(dev(w), x, n, k, m)
+    assert_within(y, y_ref, bound, "automatic FFN-down m=8")
+
+
+def test_jit_kernel_x_dynamic_range(oracle_mod):
+    n, k = 40, 4096
+    rng = np.random.default_rng(77)
+    w, _ = synth.make_inputs(n, k, 1, seed=321)
+    xs = _x_cases(rng, k)
+    y_ref, bound = oracle_mod.gemv(w, xs, n)
+    y = run_gemv(dev(w), xs, n, k, 2, kernel=6)
+    assert_within(y, y_ref, bound, "per-wave x dynamic-range x")
+
+
 # line-streamed vector-ALU kernel (m = 1, any k): integer dot products with x
 # broadcast across the tile's rows by DPP; rows of a whole number of slabs
 # (k a multiple of 2048) take the two-line rings, other rows four-line rings
