@@ -505,7 +505,9 @@ gemv_i8_sub_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
     float* ypart = reinterpret_cast<float*>(smem + xbytes + NW * kRingWave);
 
     // group q0 = column q0 / NQ, quad q0 % NQ; 16-lane group l / 16 takes
-    // vector 4 (q0 % NQ) + l / 16 (zero past the last vector)
+    // vector 4 (q0 % NQ) + l / 16 (past the last vector the last vector
+    // again: its digits reach only the D rows of lanes whose sums are never
+    // stored, so they need no zeroing)
     float4 xv[XC][4];
     auto load_group = [&](int q0, float4 (&v)[4]) {
         const int qc = min(q0, ngroups - 1);
@@ -514,14 +516,6 @@ gemv_i8_sub_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             v[i] = reinterpret_cast<const float4*>(src)[i];
-        }
-    };
-    auto zero_past = [&](int q0, float4 (&v)[4]) {
-        const uint32_t keep = 4 * (min(q0, ngroups - 1) % NQ) + (lane >> 4) >= m ? 0u : ~0u;
-        auto z = [&](float f) { return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, f) & keep); };
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            v[i] = make_float4(z(v[i].x), z(v[i].y), z(v[i].z), z(v[i].w));
         }
     };
     // JIT: slot a holds the x of a column with c mod kA = a (first column
@@ -553,13 +547,11 @@ gemv_i8_sub_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
 #pragma unroll
         for (int i = 0; i < XC; ++i) {
             const int q0 = wave + i * NW;
-            zero_past(q0, xv[i]);
             convert4_sb(xv[i], smem + (size_t)min(q0, ngroups) * kSbGroup, lane);
         }
         for (int q0 = XC * NW + wave; q0 < ngroups; q0 += NW) {
             float4 v[4];
             load_group(q0, v);
-            zero_past(q0, v);
             convert4_sb(v, smem + (size_t)q0 * kSbGroup, lane);
         }
     };
@@ -627,7 +619,6 @@ gemv_i8_sub_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
-            zero_past(c * NQ + q, v[q]);
             convert4_sb(v[q], xw + (size_t)q * kSbGroup, lane);
         }
         const int ca = cp + kA < 8 ? c + kA : cn + cp + kA - 8;
