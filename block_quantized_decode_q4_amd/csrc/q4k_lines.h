@@ -145,6 +145,18 @@ __device__ __forceinline__ void line_stream(const uint8_t* __restrict__ w,
     convert_x();
     __syncthreads();
 
+    // Waves w and w + 4 of an 8-wave workgroup share a SIMD, and with equal
+    // priority the older (w) wins every issue arbitration: with equal work
+    // the younger ends about 1 us later (wave timestamps, LM head), and the
+    // SIMD finishes on one wave.  With equal work of at least two slabs the
+    // younger raises its priority for the stream (the older has got ahead
+    // during the x stage), which evens out the end times (LM head -0.2 us,
+    // 128256 x 4096 -0.35 us; one slab each: no gain, so left alone).  Set
+    // once, outside the stream, so the stream's code is unchanged.
+    if (NW == 8 && wave >= 4 && my_slabs >= 2 &&
+        (ntasks - (wave - 4) + NW - 1) / NW == my_tasks) {
+        __builtin_amdgcn_s_setprio(1);
+    }
     for (int sig = 0; sig < my_slabs; ++sig) {
         int tile, slab, tile_n, slab_n;
         slab_of(sig, tile, slab);
