@@ -77,17 +77,17 @@ int device_lds_max(size_t* out)
 
 // Plan of the line-streamed kernels (weights 128-byte aligned, m <= 8):
 // kernel 3 (m = 1, integer dot products on the vector ALU, any k), kernel 4
-// (one MFMA group per vector), kernel 5 (one MFMA per sub-block and quad
-// of vectors) and kernel 6 (kernel 5 with x converted per column by each
-// wave), all three for k a multiple of 2048.  A task is a 16-row tile times
-// a group of slabs of eight superblock columns (the last slab of a row may
-// be partial); x (every vector) is staged whole, except for kernel 6.
+// (one MFMA group per vector; k a multiple of 2048), kernel 5 (one MFMA per
+// sub-block and quad of vectors) and kernel 6 (kernel 5 with x converted per
+// column by each wave).  A task is a 16-row tile times a group of slabs of
+// eight superblock columns (the last slab of a row may be partial); x
+// (every vector) is staged whole, except for kernel 6.
 int make_plan_lines(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t lds_max,
                     GemvPlan* p, int kernel)
 {
     const int S = (int)(k / q4k::kQK);
-    if (S % 8 != 0 && kernel != 3) {
-        return Q4K_ERR_UNSUPPORTED;    // rows of whole slabs (vector-ALU kernel: any rows)
+    if (S % 8 != 0 && kernel == 4) {
+        return Q4K_ERR_UNSUPPORTED;    // rows of whole slabs (kernels 3, 5, 6: any rows)
     }
     const int nslabs = (S + 7) / 8;
     const int nw = (o && o->waves_per_block) ? o->waves_per_block : 8;
@@ -127,7 +127,7 @@ int make_plan_lines(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t
         // all of x, which costs as much as decoding a few tiles
         rpb = 16 * ((ntiles + 255) / 256);
     }
-    const size_t lds_x = kernel == 6   ? q4k::jit_lds_bytes((int)m)
+    const size_t lds_x = kernel == 6   ? q4k::jit_lds_bytes(S, (int)m)
                          : kernel == 5 ? q4k::sub_lds_bytes(S, (int)m)
                          : kernel == 3 ? q4k::dot4_lds_bytes(S, nw)
                                        : q4k::lines_lds_bytes(S, (int)m, nw);

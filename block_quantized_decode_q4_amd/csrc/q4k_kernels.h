@@ -43,7 +43,7 @@ hipError_t launch_gemv_mfma(const GemvPlan& p, const void* w, const float* x, fl
                             hipStream_t stream);
 size_t lines_lds_bytes(int S, int m, int waves);
 size_t sub_lds_bytes(int S, int m);
-size_t jit_lds_bytes(int m);
+size_t jit_lds_bytes(int S, int m);
 hipError_t launch_gemv_dot4(const GemvPlan& p, const void* w, const float* x, float* y,
                             hipStream_t stream);
 size_t dot4_lds_bytes(int S, int waves);

@@ -25,6 +25,11 @@
 namespace q4k {
 
 constexpr int kRingRow = 2 * 128 + 16;        // two lines per row, padded
+
+// a step that takes (c, cend, cn, rr, b0, cp, valid): see line_stream
+template <typename Step>
+constexpr bool kLookAhead =
+    std::is_invocable_v<Step&, int, int, int, unsigned char*, uint32_t, int, bool>;
 constexpr int kRingWave = 16 * kRingRow;
 
 __device__ __forceinline__ uint4 load_line_nt(const uint8_t* p)
@@ -43,8 +48,12 @@ __device__ __forceinline__ uint4 load_line_nt(const uint8_t* p)
 // (rr: the ring row of the lane's tile row j, b0 = 144 (c mod 8): the
 // superblock's byte offset in that row's two-line ring window, mod 256; a
 // compile-time constant) and task_end(task) after each task's last slab.
-// A step taking (c, cn, rr, b0) also gets cn, the first column of the
-// wave's next slab (of its last slab after the last one).
+// A look-ahead step, step(c, cend, cn, rr, b0, cp, valid), also gets the
+// end cend of the columns of c's slab (or task), the first column cn of the
+// wave's next slab (task; its last one again after the last), c's position
+// cp in its slab and whether c is a column of the row at all (rows of
+// partial slabs: the positions past the row's end are passed too, invalid,
+// so that a step can keep state that cycles with cp).
 // Line l of every slab goes to ring slot l mod 2: the previous slab's last
 // line (slot 0) is dead once its last superblock has been read, and the
 // wave's LDS accesses complete in order.
@@ -182,9 +191,11 @@ __device__ __forceinline__ void line_stream(const uint8_t* __restrict__ w,
                 lines[slot][1] = load_line_nt(p[1]);
             }
             // superblock c = 8 slab + cp, in the ring of tile row j (and, for
-            // a step that looks ahead, the first column of the next slab)
-            if constexpr (std::is_invocable_v<Step&, int, int, unsigned char*, uint32_t>) {
-                step(8 * slab + cp, 8 * slab_n, ring + j * kRingRow, (uint32_t)(144 * cp));
+            // a step that looks ahead, the end of this slab's columns and the
+            // first column of the next slab)
+            if constexpr (kLookAhead<Step>) {
+                step(8 * slab + cp, 8 * slab + 8, 8 * slab_n, ring + j * kRingRow,
+                     (uint32_t)(144 * cp), cp, true);
             } else {
                 step(8 * slab + cp, ring + j * kRingRow, (uint32_t)(144 * cp));
             }
@@ -322,32 +333,44 @@ __device__ __forceinline__ void line_stream_any(const uint8_t* __restrict__ w,
     __syncthreads();
 
     for (int q = 0; q < my_tasks; ++q) {
-        int tile, cg, T;
+        int tile, cg, T, tile_n, cg_n, T_n;
         task_of(q, tile, cg, T);
+        task_of(q + 1, tile_n, cg_n, T_n);     // clamped: the last task again at the end
         const int c0 = 8 * cg * slabs_per_task;
+        const int cn = 8 * cg_n * slabs_per_task;
         const TaskBase cur = task_base(q);
         const TaskBase nxt = task_base(q + 1);
+        // superblock cp of slab s2 of the task, if the row has it
+        auto stp = [&](int s2, int cp) {
+            const int c = c0 + 8 * s2 + cp;
+            const uint32_t b0 = 1152u * (uint32_t)s2 + 144u * (uint32_t)cp;
+            if constexpr (kLookAhead<Step>) {
+                step(c, c0 + 8 * slabs_per_task, cn, ring + j * kRing4Row, b0, cp, 8 * s2 + cp < T);
+            } else {
+                if (8 * s2 + cp < T) step(c, ring + j * kRing4Row, b0);
+            }
+        };
         put(cur, nxt, 0, std::integral_constant<int, 0>());
         for (int s2 = 0; s2 < slabs_per_task; ++s2) {
             // lines 9 s2 + 1 .. 9 s2 + 9: two before superblock 1 of the slab,
             // one before each other
             put(cur, nxt, s2, std::integral_constant<int, 1>());
-            if (8 * s2 < T) step(c0 + 8 * s2, ring + j * kRing4Row, 1152u * (uint32_t)s2);
+            stp(s2, 0);
             put(cur, nxt, s2, std::integral_constant<int, 2>());
             put(cur, nxt, s2, std::integral_constant<int, 3>());
-            if (8 * s2 + 1 < T) step(c0 + 8 * s2 + 1, ring + j * kRing4Row, 1152u * (uint32_t)s2 + 144u);
+            stp(s2, 1);
             put(cur, nxt, s2, std::integral_constant<int, 4>());
-            if (8 * s2 + 2 < T) step(c0 + 8 * s2 + 2, ring + j * kRing4Row, 1152u * (uint32_t)s2 + 288u);
+            stp(s2, 2);
             put(cur, nxt, s2, std::integral_constant<int, 5>());
-            if (8 * s2 + 3 < T) step(c0 + 8 * s2 + 3, ring + j * kRing4Row, 1152u * (uint32_t)s2 + 432u);
+            stp(s2, 3);
             put(cur, nxt, s2, std::integral_constant<int, 6>());
-            if (8 * s2 + 4 < T) step(c0 + 8 * s2 + 4, ring + j * kRing4Row, 1152u * (uint32_t)s2 + 576u);
+            stp(s2, 4);
             put(cur, nxt, s2, std::integral_constant<int, 7>());
-            if (8 * s2 + 5 < T) step(c0 + 8 * s2 + 5, ring + j * kRing4Row, 1152u * (uint32_t)s2 + 720u);
+            stp(s2, 5);
             put(cur, nxt, s2, std::integral_constant<int, 8>());
-            if (8 * s2 + 6 < T) step(c0 + 8 * s2 + 6, ring + j * kRing4Row, 1152u * (uint32_t)s2 + 864u);
+            stp(s2, 6);
             put(cur, nxt, s2, std::integral_constant<int, 9>());
-            if (8 * s2 + 7 < T) step(c0 + 8 * s2 + 7, ring + j * kRing4Row, 1152u * (uint32_t)s2 + 1008u);
+            stp(s2, 7);
         }
         // the two surplus indices of the task
         put(cur, nxt, slabs_per_task, std::integral_constant<int, 1>());

@@ -476,7 +476,9 @@ constexpr int jit_ahead()
 // true (kernel 6): each wave converts the x column of each of its steps for
 // itself into its own LDS groups, from registers loaded jit_ahead columns
 // earlier -- for batches whose whole x stage does not fit the LDS.
-template <int NW, int XC, int NQ, bool JIT>
+// ANY: rows of any whole number of superblocks (line_stream_any: four-line
+// rings, per-row start offsets); else S % 8 == 0 (line_stream).
+template <int NW, int XC, int NQ, bool JIT, bool ANY>
 __global__ void __launch_bounds__(NW * 64)
 gemv_i8_sub_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
                    float* __restrict__ y, int n, int S, int m, int rows_per_block,
@@ -493,16 +495,20 @@ gemv_i8_sub_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
                                        : (uint32_t)kSbZero;
     const int row0 = blockIdx.x * rows_per_block;
     const int rows_here = min(rows_per_block, n - row0);
-    const int ncg = (S >> 3) / slabs_per_task;
+    const int ncg = ((S + 7) >> 3) / slabs_per_task;
     const int k = S * 256;
+    constexpr int kWaveRing = ANY ? kRing4Wave : kRingWave;
+    constexpr uint32_t kWindow = ANY ? 511u : 255u;        // ring window of a row, minus one
+    // byte offset of the lane's row within its first line (tiles start on a line)
+    const uint32_t loff = ANY ? (uint32_t)(j * 144 * S) & 127u : 0u;
 
     // LDS: staged x (S columns x NQ quads and a spare group; JIT: NQ groups
     // per wave), the line rings, row sums
     const int ngroups = S * NQ;
     const size_t xbytes = JIT ? (size_t)NW * NQ * kSbGroup : (size_t)(ngroups + 1) * kSbGroup;
     unsigned char* xw = smem + (JIT ? (size_t)wave * NQ * kSbGroup : 0);
-    unsigned char* ring = smem + xbytes + wave * kRingWave;
-    float* ypart = reinterpret_cast<float*>(smem + xbytes + NW * kRingWave);
+    unsigned char* ring = smem + xbytes + wave * kWaveRing;
+    float* ypart = reinterpret_cast<float*>(smem + xbytes + NW * kWaveRing);
 
     // group q0 = column q0 / NQ, quad q0 % NQ; 16-lane group l / 16 takes
     // vector 4 (q0 % NQ) + l / 16 (past the last vector the last vector
@@ -564,11 +570,12 @@ gemv_i8_sub_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
     // one superblock of the lane's tile (ring row rr, offset b0) against
     // the x groups of its column at grp0, grp0 + kSbGroup, ...
     auto decode = [&](const unsigned char* rr, uint32_t b0, const unsigned char* grp0) {
-        const uint4 hdr = *reinterpret_cast<const uint4*>(rr + (b0 & 255u));
+        const uint32_t b = b0 + loff;
+        const uint4 hdr = *reinterpret_cast<const uint4*>(rr + (b & kWindow));
         uint2 raw[4];
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) {
-            raw[cc] = *reinterpret_cast<const uint2*>(rr + ((b0 + 16u + 32u * cc + 8u * g) & 255u));
+            raw[cc] = *reinterpret_cast<const uint2*>(rr + ((b + 16u + 32u * cc + 8u * g) & kWindow));
         }
         long codes[8];
 #pragma unroll
@@ -609,25 +616,30 @@ gemv_i8_sub_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
     auto step = [&](int c, const unsigned char* rr, uint32_t b0) {
         decode(rr, b0, smem + (size_t)c * NQ * kSbGroup);
     };
-    // JIT: convert column c (slot c mod kA) into the wave's groups, refill
-    // the slot with the column kA on (cn: first column of the next slab),
-    // then decode; the groups are rewritten only after this step's reads of
-    // them (the wave's LDS accesses complete in order)
-    auto step_jit = [&](int c, int cn, const unsigned char* rr, uint32_t b0) {
-        const int cp = (int)(b0 / 144u);                 // b0 = 144 cp
+    // JIT: convert column c (slot cp mod kA) into the wave's groups, refill
+    // the slot with the column kA positions on (past cend: the next slab's or
+    // task's, from cn), then decode; the groups are rewritten only after this
+    // step's reads of them (the wave's LDS accesses complete in order).
+    // Positions past a partial slab's end (invalid) keep the slots cycling.
+    auto step_jit = [&](int c, int cend, int cn, const unsigned char* rr, uint32_t b0, int cp,
+                        bool valid) {
         float4 (&v)[NQ][4] = xa[JIT ? cp % kA : 0];
         __builtin_amdgcn_sched_barrier(0);
+        if (valid) {
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-            convert4_sb(v[q], xw + (size_t)q * kSbGroup, lane);
+            for (int q = 0; q < NQ; ++q) {
+                convert4_sb(v[q], xw + (size_t)q * kSbGroup, lane);
+            }
         }
-        const int ca = cp + kA < 8 ? c + kA : cn + cp + kA - 8;
+        const int ca = c + kA < cend ? c + kA : cn + (c + kA - cend);
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
             load_group(ca * NQ + q, v[q]);
         }
         __builtin_amdgcn_sched_barrier(0);
-        decode(rr, b0, xw);
+        if (valid) {
+            decode(rr, b0, xw);
+        }
     };
     auto task_end = [&](int task) {
         const int r = (task / ncg) * 16 + j;
@@ -644,9 +656,15 @@ gemv_i8_sub_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
             acc[q] = 0.f;
         }
     };
-    if constexpr (JIT) {
+    if constexpr (JIT && ANY) {
+        line_stream_any<NW>(w, x, n, S, rows_per_block, slabs_per_task, ring, issue_x, convert_x,
+                            step_jit, task_end);
+    } else if constexpr (JIT) {
         line_stream<NW, 3>(w, x, n, S, rows_per_block, slabs_per_task, ring, issue_x, convert_x,
                            step_jit, task_end);
+    } else if constexpr (ANY) {
+        line_stream_any<NW>(w, x, n, S, rows_per_block, slabs_per_task, ring, issue_x, convert_x,
+                            step, task_end);
     } else {
         line_stream<NW, 3>(w, x, n, S, rows_per_block, slabs_per_task, ring, issue_x, convert_x,
                            step, task_end);
@@ -670,9 +688,15 @@ template <int XC, int NQ, bool JIT = false>
 static hipError_t launch_sub_x(const GemvPlan& p, const uint8_t* w, const float* x, float* y,
                                hipStream_t stream)
 {
-    hipLaunchKernelGGL((gemv_i8_sub_kernel<8, XC, NQ, JIT>), dim3(p.grid), dim3(512),
-                       p.lds_bytes, stream, w, x, y, p.n, p.S, p.m, p.rows_per_block,
-                       p.cols_per_task / 8);
+    if (p.S % 8 != 0) {
+        hipLaunchKernelGGL((gemv_i8_sub_kernel<8, XC, NQ, JIT, true>), dim3(p.grid), dim3(512),
+                           p.lds_bytes, stream, w, x, y, p.n, p.S, p.m, p.rows_per_block,
+                           p.cols_per_task / 8);
+    } else {
+        hipLaunchKernelGGL((gemv_i8_sub_kernel<8, XC, NQ, JIT, false>), dim3(p.grid), dim3(512),
+                           p.lds_bytes, stream, w, x, y, p.n, p.S, p.m, p.rows_per_block,
+                           p.cols_per_task / 8);
+    }
     return hipGetLastError();
 }
 
@@ -760,13 +784,13 @@ hipError_t launch_gemv_mfma(const GemvPlan& p, const void* w, const float* x, fl
 size_t sub_lds_bytes(int S, int m)
 {
     const int nq = (m + 3) / 4;
-    return (size_t)(S * nq + 1) * kSbGroup + (size_t)8 * kRingWave;
+    return (size_t)(S * nq + 1) * kSbGroup + (size_t)8 * (S % 8 != 0 ? kRing4Wave : kRingWave);
 }
 
-size_t jit_lds_bytes(int m)
+size_t jit_lds_bytes(int S, int m)
 {
     const int nq = (m + 3) / 4;
-    return (size_t)8 * nq * kSbGroup + (size_t)8 * kRingWave;
+    return (size_t)8 * nq * kSbGroup + (size_t)8 * (S % 8 != 0 ? kRing4Wave : kRingWave);
 }
 
 size_t lines_lds_bytes(int S, int m, int waves)

@@ -110,11 +110,11 @@ const char* q4k_status_string(int rc);
  *   5  sub-block int8 matrix-core (m <= 8), one MFMA per sub-block and quad
  *      of vectors
  *   6  kernel 5 with x converted one superblock column at a time by each
- *      wave for itself (no whole x stage: any k)
+ *      wave for itself (no whole x stage: any k and m)
  * Kernels 3-6 need w 128-byte aligned and their staged x plus line rings
- * within the LDS; kernels 4-6 also k % 2048 == 0 (rows of whole 8-
- * superblock slabs), kernel 3 takes any k up to 4096 * waves_per_block (rows
- * of partial slabs with four-line rings and three lines in flight).
+ * within the LDS; kernel 4 also k % 2048 == 0 (rows of whole 8-superblock
+ * slabs); kernels 3, 5 and 6 take rows of partial slabs too (four-line
+ * rings, three lines in flight), kernel 3 up to k = 4096 * waves_per_block.
  * Automatic choice: m = 1 kernel 3 when it applies and the weights take at
  * least 16 MiB, else kernel 2 (the matrix cores only when asked for); m > 1
  * kernel 5 for m >= 3, kernel 4 for m = 2, the other of the two if only it

@@ -120,10 +120,8 @@ def test_gemv_ex_kernel_option_refusals(lib):
         (dict(kernel=4, waves_per_block=16, ring_depth=9), 16, 4096, 1),
         (dict(kernel=4, waves_per_block=4), 16, 4096, 2),    # several vectors: 8 waves
         (dict(kernel=4, rows_per_task=2), 16, 4096, 1),
-        (dict(kernel=5), 16, 1024, 1),                       # k not a multiple of 2048
         (dict(kernel=5, waves_per_block=4), 16, 4096, 2),    # eight waves only
         (dict(kernel=5, ring_depth=9), 16, 4096, 2),         # three lines in flight only
-        (dict(kernel=6), 16, 1024, 2),                       # k not a multiple of 2048
         (dict(kernel=6, waves_per_block=16), 16, 4096, 2),   # eight waves only
         (dict(kernel=6, ring_depth=9), 16, 4096, 8),         # three lines in flight only
         (dict(kernel=1, cols_per_task=8), 16, 4096, 1),      # line-streamed options only

@@ -319,6 +319,33 @@ def test_jit_kernel(oracle_mod, n, k, m):
         assert_within(y4, y_ref, bound, "automatic m=%d k=%d" % (m, k))
 
 
+@pytest.mark.parametrize("n,k,m", [(17, 1280, 3), (130, 11008, 8), (33, 4352, 2), (257, 5120, 5),
+                                   (48, 13824, 4), (5, 768, 6), (16, 2304, 7), (1, 256, 2),
+                                   (300, 3328, 8)])
+def test_sub_kernels_partial_slabs(oracle_mod, n, k, m):
+    """Kernels 5 and 6 on rows of partial slabs (k not a multiple of 2048:
+    four-line rings, per-row start offsets): within tolerance, bit-identical
+    to each other with the same column grouping, and the automatic plan."""
+    w, x = synth.make_inputs(n, k, m, seed=n * 31 + k + 7 * m)
+    y_ref, bound = oracle_mod.gemv(w, x, n)
+    w_d = dev(w)
+    _say("partial-slab sub-block kernels n=%d k=%d m=%d" % (n, k, m))
+    y6 = run_gemv(w_d, x, n, k, m, kernel=6, cols_per_task=8)
+    assert_within(y6, y_ref, bound, "per-wave x partial slabs m=%d" % m)
+    try:
+        y5 = run_gemv(w_d, x, n, k, m, kernel=5, cols_per_task=8)
+    except q4k.Q4KError as e:
+        assert e.rc == q4k.Q4K_ERR_UNSUPPORTED
+    else:
+        assert np.array_equal(y5.view(np.uint32), y6.view(np.uint32))
+    nslabs = (k // 256 + 7) // 8
+    for opts in (dict(rows_per_block=48), dict(cols_per_task=8 * nslabs)):
+        y2 = run_gemv(w_d, x, n, k, m, kernel=6, **opts)
+        assert_within(y2, y_ref, bound, "per-wave x partial slabs %r" % opts)
+    y4 = run_gemv(w_d, x, n, k, m)             # automatic kernel
+    assert_within(y4, y_ref, bound, "automatic partial slabs m=%d k=%d" % (m, k))
+
+
 def test_jit_kernel_ffn_down_batch8(oracle_mod):
     """The FFN-down shape (4096 x 14336) with eight vectors: the automatic
     plan (kernel 6, no whole x stage fits) against the oracle."""
