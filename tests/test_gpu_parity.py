@@ -302,6 +302,9 @@ def test_jit_kernel(oracle_mod, n, k, m):
     _say("per-wave x kernel n=%d k=%d m=%d" % (n, k, m))
     y = run_gemv(w_d, x, n, k, m, kernel=6, cols_per_task=8)
     assert_within(y, y_ref, bound, "per-wave x m=%d" % m)
+    for b in range(m):                          # batched == m single-vector launches
+        y1 = run_gemv(w_d, x[b:b + 1], n, k, 1, kernel=6, cols_per_task=8)
+        assert np.array_equal(y1[0].view(np.uint32), y[b].view(np.uint32)), b
     try:
         y5 = run_gemv(w_d, x, n, k, m, kernel=5, cols_per_task=8)
     except q4k.Q4KError as e:
@@ -332,6 +335,9 @@ def test_sub_kernels_partial_slabs(oracle_mod, n, k, m):
     _say("partial-slab sub-block kernels n=%d k=%d m=%d" % (n, k, m))
     y6 = run_gemv(w_d, x, n, k, m, kernel=6, cols_per_task=8)
     assert_within(y6, y_ref, bound, "per-wave x partial slabs m=%d" % m)
+    for b in range(m):                          # batched == m single-vector launches
+        y1 = run_gemv(w_d, x[b:b + 1], n, k, 1, kernel=6, cols_per_task=8)
+        assert np.array_equal(y1[0].view(np.uint32), y6[b].view(np.uint32)), b
     try:
         y5 = run_gemv(w_d, x, n, k, m, kernel=5, cols_per_task=8)
     except q4k.Q4KError as e:
