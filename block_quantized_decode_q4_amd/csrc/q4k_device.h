@@ -46,7 +46,7 @@ __device__ __forceinline__ void dot8(uint32_t D, const float4& xl, const float4&
 }
 
 struct ChunkScales {
-    float d24;    // d * dscale (2^24 for the fma_mix codes, whose values are q * 2^-24)
+    float d24;    // d * 2^24 (the fma_mix codes' values are q * 2^-24)
     float dmin;
     float sc_lo, sc_hi, m_lo, m_hi;
 };
@@ -58,12 +58,11 @@ struct ChunkScales {
 //           m_j  = (s[j+4] >> 4) | (s[j]   >> 6) << 4
 // Both forms take bytes 2(c&1), 2(c&1)+1 of their dwords, so one shift
 // serves both; the lane picks its form with a select.
-__device__ __forceinline__ ChunkScales decode_header(const uint4& h, int c,
-                                                     float dscale = 16777216.0f)
+__device__ __forceinline__ ChunkScales decode_header(const uint4& h, int c)
 {
     ChunkScales s;
     const half2_t dd = __builtin_bit_cast(half2_t, h.x);
-    s.d24 = (float)dd.x * dscale;
+    s.d24 = (float)dd.x * 16777216.0f;
     s.dmin = (float)dd.y;
     const uint32_t sh = (uint32_t)(c & 1) * 16u;
     const uint32_t y = h.y >> sh;
