@@ -16,8 +16,9 @@
 //    T_d = sum q * D_d.  sum q xi = T_0 + 256 T_1 + 65536 T_2 for the low
 //    sub-block; the high one adds 128 * XI (XI = sum xi) and divides by 16.
 //  * Superblock scales: fp16 d and dmin and the 6-bit (sc, m) pairs of the
-//    lane's two sub-blocks (decode_header), applied in f32 once per
-//    superblock and lane; the x sums X = 2^-s XI give the min term.
+//    lane's two sub-blocks (two byte permutes, gather_scales), applied in
+//    f32 once per superblock and lane; the x sums X = 2^-s XI give the min
+//    terms, which collect in a second accumulator.
 //
 // Lane layout of a 16-row tile step (one superblock column): lane l = 16 g +
 // j takes row j, chunk g (bytes 16 + 32 g .. of the superblock: elements
