@@ -118,3 +118,73 @@ def test_line_stream_any_model(n, S):
                 # every superblock column of every 16-row tile, once
                 tiles = sum((min(rpb, n - b) + 15) // 16 for b in range(0, n, rpb))
                 assert steps == tiles * S
+
+
+def lookahead_columns(n, S, NW, rpb, spt, kA, aligned):
+    """Replay kernel 6's per-wave x look-ahead (gemv_i8_sub_kernel<..., true,
+    ANY> in csrc/q4k_mfma.hip) over the columns the streams step through:
+    register slot cp % kA must hold column c whenever step (c, cp) is
+    valid.  The streams pass cend (end of the slab's or task's columns) and
+    cn (first column of the wave's next slab or task, clamped to its last)."""
+    nslabs = (S + 7) // 8
+    ncg = nslabs // spt
+    grid = (n + rpb - 1) // rpb
+    checked = 0
+    for blk in range(grid):
+        rows_here = min(rpb, n - blk * rpb)
+        ntasks = ((rows_here + 15) // 16) * ncg
+        for wave in range(NW):
+            my_tasks = (ntasks - wave + NW - 1) // NW if ntasks > wave else 0
+            # steps as the stream issues them: (c, cend, cn, cp, valid)
+            seq = []
+            if aligned:
+                my_slabs = my_tasks * spt
+
+                def slab_of(sig):
+                    sig = max(0, min(sig, my_slabs - 1))
+                    task = min(wave + (sig // spt) * NW, ntasks - 1)
+                    return (task % ncg) * spt + sig % spt
+                for sig in range(my_slabs):
+                    slab, slab_n = slab_of(sig), slab_of(sig + 1)
+                    for cp in range(8):
+                        seq.append((8 * slab + cp, 8 * slab + 8, 8 * slab_n, cp, True))
+            else:
+                def task_of(q):
+                    qc = max(0, min(q, my_tasks - 1))
+                    task = min(wave + qc * NW, ntasks - 1)
+                    cg = task % ncg
+                    return cg, min(8 * spt, S - 8 * cg * spt)
+                for q in range(my_tasks):
+                    cg, T = task_of(q)
+                    cg_n, _ = task_of(q + 1)
+                    c0, cn = 8 * cg * spt, 8 * cg_n * spt
+                    for s2 in range(spt):
+                        for cp in range(8):
+                            seq.append((c0 + 8 * s2 + cp, c0 + 8 * spt, cn, cp, 8 * s2 + cp < T))
+            # the kernel: prologue loads columns c_first + a into slot a
+            task0 = min(wave, ntasks - 1) if ntasks else 0
+            c_first = 8 * ((task0 % ncg) * spt) if ntasks else 0
+            slots = {a: c_first + a for a in range(kA)}
+            for c, cend, cn, cp, valid in seq:
+                if valid:
+                    assert slots[cp % kA] == c, (blk, wave, c, slots)
+                    assert 0 <= c < S
+                    checked += 1
+                ca = c + kA if c + kA < cend else cn + (c + kA - cend)
+                slots[cp % kA] = min(ca, S - 1)      # loads clamp to the last column
+    return checked
+
+
+@pytest.mark.parametrize("n,S,spt,aligned", [
+    (4096, 56, 1, True), (130, 16, 2, True), (300, 32, 1, True), (48, 112, 2, True),
+    (4096, 43, 1, False), (130, 5, 1, False), (257, 20, 3, False), (17, 54, 1, False),
+    (300, 13, 2, False), (1, 1, 1, False),
+])
+@pytest.mark.parametrize("kA", [2, 4])
+def test_jit_lookahead_columns(n, S, spt, aligned, kA):
+    nslabs = (S + 7) // 8
+    if nslabs % spt:
+        pytest.skip("column groups must divide the slabs")
+    for rpb in (16, 48, 128):
+        checked = lookahead_columns(n, S, 8, rpb, spt, kA, aligned)
+        assert checked == ((n + 15) // 16) * S      # every tile's columns, once each
