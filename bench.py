@@ -116,7 +116,7 @@ def main() -> int:
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build measures one GPU only (the GEMV runs on one MI355X; "
+        print("bench.py: measures one GPU only (the GEMV runs on one MI355X; "
               "--gpus %d is not supported)" % args.gpus, file=sys.stderr)
         return 2
 

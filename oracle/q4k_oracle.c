@@ -19,7 +19,8 @@
  *    `batched_q4k_gemv_into`: weights are N x K/256 superblocks shared by the
  *    batch; the input is M x K row-major and the output M x N row-major.
  *  - The superblock field layout inside the 144 bytes is not printed on the
- *    pages.  It is fixed by the problem statement this build implements:
+ *    pages.  It is the GGUF Q4_K layout (the format the pages' listings
+ *    decode, by name):
  *    fp16 d at byte 0, fp16 dmin at byte 2, twelve bytes of packed 6-bit
  *    (scale, min) pairs for the eight 32-element sub-blocks at byte 4, and 128
  *    bytes of 4-bit quants at byte 16 where, in each 64-element chunk c, byte i
