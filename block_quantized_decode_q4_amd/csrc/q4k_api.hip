@@ -378,6 +378,46 @@ int make_plan(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t lds_m
     return Q4K_OK;
 }
 
+// The plan gemv_checked would launch, for a given LDS budget; shape and
+// option checks in the same order.
+int plan_checked(int64_t n, int64_t k, int64_t m, const q4k_launch* opts, bool w128,
+                 size_t lds_max, GemvPlan* plan)
+{
+    int rc = check_nk(n, k);
+    if (rc != Q4K_OK) {
+        return rc;
+    }
+    if (m < 1) {
+        return Q4K_ERR_SHAPE;
+    }
+    if (m > q4k::kMaxM) {
+        return Q4K_ERR_UNSUPPORTED;
+    }
+    // options are validated before the first HIP call (unbounded LDS), then
+    // planned for the LDS size
+    rc = make_plan(n, k, m, opts, SIZE_MAX, plan, w128);
+    if (rc != Q4K_OK) {
+        return rc;
+    }
+    if (lds_max == 0) {
+        rc = device_lds_max(&lds_max);
+        if (rc != Q4K_OK) {
+            return rc;
+        }
+    }
+    rc = make_plan(n, k, m, opts, lds_max, plan, w128);
+    if (rc != Q4K_OK) {
+        return rc;
+    }
+    if (plan->lds_bytes > lds_max) {
+        return Q4K_ERR_UNSUPPORTED;
+    }
+    if (plan->kernel >= 3 && !w128) {
+        return Q4K_ERR_UNSUPPORTED;    // whole-line reads need 128-byte aligned rows
+    }
+    return Q4K_OK;
+}
+
 int gemv_checked(const void* w, const float* x, float* y, int64_t n, int64_t k, int64_t m,
                  const q4k_launch* opts, void* stream)
 {
@@ -397,28 +437,11 @@ int gemv_checked(const void* w, const float* x, float* y, int64_t n, int64_t k, 
     if (!aligned16(w) || !aligned16(x) || !aligned16(y)) {
         return Q4K_ERR_ALIGN;
     }
-    // options are validated before the first HIP call (unbounded LDS), then
-    // planned for the device's LDS size
     const bool w128 = (reinterpret_cast<uintptr_t>(w) & 127u) == 0;
     GemvPlan plan;
-    rc = make_plan(n, k, m, opts, SIZE_MAX, &plan, w128);
+    rc = plan_checked(n, k, m, opts, w128, 0, &plan);
     if (rc != Q4K_OK) {
         return rc;
-    }
-    size_t lds_max = 0;
-    rc = device_lds_max(&lds_max);
-    if (rc != Q4K_OK) {
-        return rc;
-    }
-    rc = make_plan(n, k, m, opts, lds_max, &plan, w128);
-    if (rc != Q4K_OK) {
-        return rc;
-    }
-    if (plan.lds_bytes > lds_max) {
-        return Q4K_ERR_UNSUPPORTED;
-    }
-    if (plan.kernel >= 3 && (reinterpret_cast<uintptr_t>(w) & 127u) != 0) {
-        return Q4K_ERR_UNSUPPORTED;    // whole-line reads need 128-byte aligned rows
     }
     return hip_status(q4k::launch_gemv(plan, w, x, y, static_cast<hipStream_t>(stream)));
 }
@@ -470,6 +493,28 @@ int q4k_gemv_ex(const void* w, const float* x, float* y, int64_t n, int64_t k, i
                 const q4k_launch* opts, void* stream)
 {
     return gemv_checked(w, x, y, n, k, m, opts, stream);
+}
+
+int q4k_plan(int64_t n, int64_t k, int64_t m, const q4k_launch* opts, int w_aligned128,
+             size_t lds_max, q4k_plan_info* out)
+{
+    if (!out) {
+        return Q4K_ERR_NULL;
+    }
+    GemvPlan plan;
+    const int rc = plan_checked(n, k, m, opts, w_aligned128 != 0, lds_max, &plan);
+    if (rc != Q4K_OK) {
+        return rc;
+    }
+    out->kernel = plan.kernel;
+    out->grid = plan.grid;
+    out->threads = plan.waves_per_block * 64;
+    out->lds_bytes = (int32_t)plan.lds_bytes;
+    out->rows_per_block = plan.rows_per_block;
+    out->cols_per_task = plan.kernel >= 3 ? plan.cols_per_task : 0;
+    out->ring_depth = plan.ring_depth;
+    out->spans_per_chunk = plan.kernel <= 2 ? plan.spans_per_chunk : 0;
+    return Q4K_OK;
 }
 
 int q4k_dequantize(const void* w, float* out, int64_t n, int64_t k, void* stream)

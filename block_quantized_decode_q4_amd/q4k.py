@@ -33,6 +33,7 @@ EXPORTED = (
     "q4k_gemv_ex",
     "q4k_read_calibrate",
     "q4k_read_calibrate_blocks",
+    "q4k_plan",
 )
 
 
@@ -54,6 +55,19 @@ class q4k_launch(ctypes.Structure):
         ("ring_depth", ctypes.c_int32),
         ("rows_per_task", ctypes.c_int32),
         ("cols_per_task", ctypes.c_int32),
+    ]
+
+
+class q4k_plan_info(ctypes.Structure):
+    _fields_ = [
+        ("kernel", ctypes.c_int32),
+        ("grid", ctypes.c_int32),
+        ("threads", ctypes.c_int32),
+        ("lds_bytes", ctypes.c_int32),
+        ("rows_per_block", ctypes.c_int32),
+        ("cols_per_task", ctypes.c_int32),
+        ("ring_depth", ctypes.c_int32),
+        ("spans_per_chunk", ctypes.c_int32),
     ]
 
 
@@ -93,6 +107,9 @@ def load_library():
         lib.q4k_read_calibrate.restype = ctypes.c_int
         lib.q4k_read_calibrate_blocks.argtypes = []
         lib.q4k_read_calibrate_blocks.restype = ctypes.c_int
+        lib.q4k_plan.argtypes = [i64, i64, i64, ctypes.POINTER(q4k_launch), ctypes.c_int,
+                                 ctypes.c_size_t, ctypes.POINTER(q4k_plan_info)]
+        lib.q4k_plan.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -166,6 +183,18 @@ def q4k_dequantize(w, out, n: int, k: int, stream=None) -> None:
     """out[r*k + c] = W[r][c] in f32 (bit-exact); asynchronous on stream."""
     _check(load_library().q4k_dequantize(_addr(w), _addr(out), int(n), int(k), _stream(stream)),
            "q4k_dequantize")
+
+
+def q4k_plan(n: int, k: int, m: int = 1, w_aligned128: bool = True, lds_max: int = 0,
+             **opts) -> q4k_plan_info:
+    """The launch q4k_gemv_ex would make (no launch).  lds_max = 0 asks the
+    current device; a nonzero value needs no GPU."""
+    cfg = q4k_launch(**opts) if opts else None
+    out = q4k_plan_info()
+    _check(load_library().q4k_plan(int(n), int(k), int(m), ctypes.byref(cfg) if cfg else None,
+                                   1 if w_aligned128 else 0, int(lds_max), ctypes.byref(out)),
+           "q4k_plan")
+    return out
 
 
 def q4k_read_calibrate_blocks() -> int:

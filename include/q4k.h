@@ -152,6 +152,33 @@ int q4k_gemv_ex(const void* w, const float* x, float* y,
                 int64_t n, int64_t k, int64_t m,
                 const q4k_launch* opts, void* stream);
 
+/* The launch q4k_gemv_ex(w, x, y, n, k, m, opts, stream) would make,
+ * without launching (introspection for tests and tuning).
+ *   w_aligned128 : nonzero if the weights' address is 128-byte aligned (the
+ *                  line-streamed kernels 3-6 need it)
+ *   lds_max      : LDS bytes a workgroup may use; 0 = ask the current HIP
+ *                  device (163840 on MI355X), so with a nonzero value no
+ *                  HIP call is made and this runs without a GPU
+ *   out          : host, filled on Q4K_OK
+ * Returns what q4k_gemv_ex would return for the shape and options before
+ * launching (Q4K_ERR_SHAPE, Q4K_ERR_UNSUPPORTED, ...); pointers and their
+ * 16-byte alignment are not checked here. */
+typedef struct q4k_plan_info {
+    int32_t kernel;          /* 1-6 as listed above                           */
+    int32_t grid;            /* workgroups                                     */
+    int32_t threads;         /* per workgroup                                  */
+    int32_t lds_bytes;       /* dynamic LDS per workgroup                      */
+    int32_t rows_per_block;  /* weight rows per workgroup                      */
+    int32_t cols_per_task;   /* line-streamed: superblock columns per task;
+                                else 0                                          */
+    int32_t ring_depth;      /* streaming: rows in flight; line-streamed: lines */
+    int32_t spans_per_chunk; /* kernels 1, 2: 4096-element spans per x stage;
+                                else 0                                          */
+} q4k_plan_info;
+
+int q4k_plan(int64_t n, int64_t k, int64_t m, const q4k_launch* opts, int w_aligned128,
+             size_t lds_max, q4k_plan_info* out);
+
 /* Read `bytes` (a multiple of 16) of device memory at `buf` (16-byte
  * aligned) with coalesced 16-byte loads and write a checksum per workgroup
  * to `out` (device, q4k_read_calibrate_blocks() floats).  Benchmark

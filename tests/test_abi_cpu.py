@@ -165,3 +165,71 @@ def test_binding_raises_with_status():
     with pytest.raises(q4k.Q4KError) as ei:
         q4k.q4k_gemv(A, A, A, 16, 256, 9, stream=0)
     assert ei.value.rc == q4k.Q4K_ERR_UNSUPPORTED
+
+
+MI355X_LDS = 163840   # LDS bytes per workgroup on gfx950
+
+
+def test_plan_info_struct_matches_header():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    body = re.search(r"typedef struct q4k_plan_info \{(.*?)\} q4k_plan_info;", text, re.S).group(1)
+    fields = re.findall(r"int32_t\s+([a-z_0-9]+)\s*;", body)
+    assert fields == [f for f, _ in q4k.q4k_plan_info._fields_]
+    assert all(t is ctypes.c_int32 for _, t in q4k.q4k_plan_info._fields_)
+
+
+@pytest.mark.parametrize("n,k,m,aligned,kernel,grid,cols", [
+    (32000, 4096, 1, True, 3, 250, 16),     # LM head: 64 MiB of weights, 128 rows a block
+    (4096, 14336, 1, True, 3, 256, 8),      # FFN down: 16 rows a block, slab tasks
+    (16384, 16384, 1, True, 3, 256, 8),
+    (4096, 4096, 1, True, 2, 256, 0),       # 9 MiB: below the line-stream threshold
+    (256, 1024, 1, True, 2, 32, 0),
+    (32000, 4096, 1, False, 2, None, 0),    # weights not 128-byte aligned
+    (32000, 4096, 2, True, 4, 250, 16),     # m = 2: line MFMA
+    (14336, 4096, 8, True, 5, 224, 8),      # m >= 3: sub-block MFMA, x staged whole
+    (4096, 14336, 8, True, 6, 256, 8),      # x of 8 columns does not fit: per-wave x
+    (4096, 11008, 8, True, 6, 256, 8),      # partial slab (43 superblocks)
+    (14336, 4096, 8, False, 1, None, 0),
+])
+def test_plan_automatic_choice(n, k, m, aligned, kernel, grid, cols):
+    """The automatic rule of q4k_gemv_ex, asked without a GPU."""
+    p = q4k.q4k_plan(n, k, m, w_aligned128=aligned, lds_max=MI355X_LDS)
+    assert p.kernel == kernel
+    if grid is not None:
+        assert p.grid == grid
+    assert p.cols_per_task == cols
+    assert p.threads % 64 == 0 and 64 <= p.threads <= 1024
+    assert 0 < p.lds_bytes <= MI355X_LDS
+    assert p.grid * p.rows_per_block >= n
+    assert (p.grid - 1) * p.rows_per_block < n
+    if kernel <= 2:
+        assert p.spans_per_chunk >= 1
+    else:
+        assert p.spans_per_chunk == 0 and p.ring_depth == 3
+
+
+def test_plan_follows_options_and_lds_limit():
+    p = q4k.q4k_plan(32000, 4096, 1, lds_max=MI355X_LDS, kernel=4)
+    assert p.kernel == 4
+    p = q4k.q4k_plan(32000, 4096, 1, lds_max=MI355X_LDS, kernel=3, cols_per_task=8)
+    assert p.kernel == 3 and p.cols_per_task == 8
+    # the whole-x stage of kernel 5 (150848 bytes here) does not fit in 64 KiB:
+    # the automatic choice moves on to per-wave x
+    p = q4k.q4k_plan(14336, 4096, 8, lds_max=MI355X_LDS)
+    assert p.kernel == 5 and p.lds_bytes == 150848
+    p = q4k.q4k_plan(14336, 4096, 4, lds_max=65536)
+    assert p.kernel == 6 and p.lds_bytes <= 65536
+    with pytest.raises(q4k.Q4KError) as ei:
+        q4k.q4k_plan(14336, 4096, 8, lds_max=65536, kernel=5)
+    assert ei.value.rc == q4k.Q4K_ERR_UNSUPPORTED
+
+
+def test_plan_refusals(lib):
+    out = q4k.q4k_plan_info()
+    assert lib.q4k_plan(4096, 4096, 1, None, 1, MI355X_LDS, None) == q4k.Q4K_ERR_NULL
+    assert lib.q4k_plan(16, 100, 1, None, 1, MI355X_LDS, ctypes.byref(out)) == q4k.Q4K_ERR_SHAPE
+    assert lib.q4k_plan(16, 256, 9, None, 1, MI355X_LDS, ctypes.byref(out)) == q4k.Q4K_ERR_UNSUPPORTED
+    cfg = q4k.q4k_launch(kernel=3)
+    assert lib.q4k_plan(32000, 4096, 2, ctypes.byref(cfg), 1, MI355X_LDS,
+                        ctypes.byref(out)) == q4k.Q4K_ERR_UNSUPPORTED

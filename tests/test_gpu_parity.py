@@ -722,3 +722,13 @@ def test_nonzero_stream_and_overwrite(oracle_mod):
         q4k.q4k_gemv(w_d, x_d, y_d, wl.n, wl.k, wl.m, stream=s)
     s.synchronize()
     assert_within(y_d.cpu().numpy(), y_ref, bound, "side stream")
+
+
+def test_plan_query_on_device():
+    """q4k_plan asking the device for its LDS size plans as it does with
+    gfx950's 160 KiB given explicitly."""
+    for shp in [(32000, 4096, 1), (4096, 14336, 1), (4096, 4096, 1), (14336, 4096, 8),
+                (4096, 14336, 8), (32000, 4096, 2)]:
+        a = q4k.q4k_plan(*shp, lds_max=0)
+        b = q4k.q4k_plan(*shp, lds_max=163840)
+        assert [getattr(a, f) for f, _ in a._fields_] == [getattr(b, f) for f, _ in b._fields_]
