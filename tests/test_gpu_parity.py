@@ -732,3 +732,37 @@ def test_plan_query_on_device():
         a = q4k.q4k_plan(*shp, lds_max=0)
         b = q4k.q4k_plan(*shp, lds_max=163840)
         assert [getattr(a, f) for f, _ in a._fields_] == [getattr(b, f) for f, _ in b._fields_]
+
+
+def _random_cases(count, seed):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(count):
+        m = int(rng.choice([1, 1, 1, 2, 3, 4, 5, 6, 7, 8]))
+        if m == 1 and rng.random() < 0.5:
+            n = int(rng.integers(2000, 9000))
+            S = int(rng.choice([16, 24, 32, 40, 43, 56]))
+        else:
+            n = int(rng.integers(1, 1500))
+            S = int(rng.integers(1, 80))
+        off = int(rng.choice([0, 0, 16, 48]))
+        cases.append((n, 256 * S, m, off))
+    return cases
+
+
+@pytest.mark.parametrize("n,k,m,off", _random_cases(24, 2026))
+def test_random_shapes_automatic_plan(oracle_mod, n, k, m, off):
+    """Seeded random shapes, batch sizes and weight-buffer offsets (16-byte
+    aligned, not always 128-byte aligned) through q4k_gemv's automatic plan."""
+    p = q4k.q4k_plan(n, k, m, w_aligned128=(off == 0))
+    _say("random n=%d k=%d m=%d off=%d -> kernel %d" % (n, k, m, off, p.kernel))
+    if off:
+        assert p.kernel <= 2   # the line-streamed kernels need 128-byte aligned rows
+    w, x = synth.make_inputs(n, k, m, seed=n * 131 + k + m)
+    y_ref, bound = oracle_mod.gemv(w, x, n)
+    buf = torch.empty(w.size + off, dtype=torch.uint8, device="cuda")
+    buf[off:].copy_(torch.from_numpy(w))
+    w_d = buf[off:]
+    assert w_d.data_ptr() % 128 == off % 128
+    y = run_gemv(w_d, x, n, k, m)
+    assert_within(y, y_ref, bound, "n=%d k=%d m=%d off=%d" % (n, k, m, off))
