@@ -110,6 +110,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20000)
     ap.add_argument("--warmup", type=int, default=20000)
     ap.add_argument("--workload", type=int, default=DEFAULT_WORKLOAD)
+    ap.add_argument("--shape", default=None, metavar="N:K:M",
+                    help="time this shape (seeded synthetic inputs) instead of --workload")
     ap.add_argument("--rotate-gib", type=float, default=1.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -131,7 +133,12 @@ def main() -> int:
     q4k.load_library()           # raises if libq4k.so is missing: no fallback
     torch.cuda.set_device(0)
 
-    wl, w, x = synth.workload_inputs(args.workload)
+    if args.shape:
+        n_, k_, m_ = (int(t) for t in args.shape.split(":"))
+        wl = synth.Workload(-1, "q4k_gemv_n%d_k%d_m%d" % (n_, k_, m_), n_, k_, m_)
+        w, x = synth.make_inputs(n_, k_, m_, seed=n_ + k_ + m_)
+    else:
+        wl, w, x = synth.workload_inputs(args.workload)
     n, k, m = wl.n, wl.k, wl.m
     wb = wl.weight_bytes
     copies = max(4, math.ceil(args.rotate_gib * (1 << 30) / wb))

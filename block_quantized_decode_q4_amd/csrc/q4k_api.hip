@@ -89,6 +89,9 @@ int make_plan_lines(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t
     if (S % 8 != 0 && kernel == 4) {
         return Q4K_ERR_UNSUPPORTED;    // rows of whole slabs (kernels 3, 5, 6: any rows)
     }
+    if (m > q4k::kMaxM && kernel < 5) {
+        return Q4K_ERR_UNSUPPORTED;    // 9-16 vectors: the sub-block kernels only
+    }
     const int nslabs = (S + 7) / 8;
     const int nw = (o && o->waves_per_block) ? o->waves_per_block : 8;
     if (nw != 4 && nw != 8 && nw != 16) {
@@ -171,11 +174,12 @@ int make_plan_lines(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t
 // Plans needing more LDS than lds_max are returned as they are; the caller
 // refuses them.
 // The automatic kernel (choices measured on MI355X).  The line-streamed
-// kernels apply when the weights are 128-byte aligned, their LDS (x of every
-// vector, the line rings) fits and, for the matrix-core ones, k is a
-// multiple of 2048.  m > 1:
+// kernels apply when the weights are 128-byte aligned and their LDS (staged
+// x, the line rings) fits; kernel 4 also needs k a multiple of 2048.  m > 1:
 // the sub-block kernel (5, m >= 3) or the per-vector line-streamed kernel
-// (4, m = 2), the other one if only it fits, else the x-stager kernel.
+// (4, m = 2), the other one if only it fits, then the sub-block kernel with
+// per-wave x (6), else the x-stager kernel (1, m <= 8; 9-16 vectors are
+// refused there).
 // m = 1: the line-streamed vector-ALU kernel (3) where it applies and the
 // weights take at least 16 MiB, else the streaming kernel, whose shorter
 // start wins on smaller matrices; m = 1 takes the matrix cores only when
@@ -245,7 +249,8 @@ int make_plan(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t lds_m
     const int nchunks = (nspans + spc - 1) / spc;
 
     const int kernel = (o && o->kernel) ? o->kernel : auto_kernel(n, k, m, o, w_aligned128, lds_max);
-    if (kernel < 1 || kernel > 6 || ((kernel == 2 || kernel == 3) && m != 1)) {
+    if (kernel < 1 || kernel > 6 || ((kernel == 2 || kernel == 3) && m != 1) ||
+        (kernel == 1 && m > q4k::kMaxM)) {
         return Q4K_ERR_UNSUPPORTED;
     }
     if (kernel >= 3) {
@@ -378,10 +383,37 @@ int make_plan(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t lds_m
     return Q4K_OK;
 }
 
+// 9-16 vectors, automatic plan: one pass of the sub-block kernels over the
+// weights where their whole x stage fits or where eight vectors would take
+// kernel 6 anyway; else two launches (vectors 0-7, then the rest).  Measured
+// on MI355X, two launches of eight against one pass of sixteen: 4096 x 14336
+// 2 x 21.0 against 34.0 us; 14336 x 4096 28.7 against 33.8 and 32000 x 4096
+// 43.9 against 61.1 us (with four vector quads kernel 6 holds only one x
+// column in registers ahead of its step, where kernel 5 of eight vectors
+// stages x whole).  Two launches also serve weights that are not 128-byte
+// aligned and rows whose sixteen-vector plan does not fit the LDS.
+bool split_wide(int64_t n, int64_t k, int64_t m, const q4k_launch* o, bool w128, size_t lds_max)
+{
+    if (m <= q4k::kMaxM || (o && (o->kernel || any_option(o)))) {
+        return false;
+    }
+    GemvPlan pw, p8;
+    if (make_plan(n, k, m, nullptr, lds_max, &pw, w128) != Q4K_OK || pw.kernel < 5 ||
+        pw.lds_bytes > lds_max) {
+        return true;
+    }
+    if (pw.kernel == 5) {
+        return false;
+    }
+    return make_plan(n, k, q4k::kMaxM, nullptr, lds_max, &p8, w128) != Q4K_OK || p8.kernel != 6;
+}
+
 // The plan gemv_checked would launch, for a given LDS budget; shape and
-// option checks in the same order.
+// option checks in the same order.  *split (may be NULL: then never): the
+// automatic plan of 9-16 vectors is two launches, `plan` the first (vectors
+// 0-7), plan_checked(m - 8) the second.
 int plan_checked(int64_t n, int64_t k, int64_t m, const q4k_launch* opts, bool w128,
-                 size_t lds_max, GemvPlan* plan)
+                 size_t lds_max, GemvPlan* plan, bool* split = nullptr)
 {
     int rc = check_nk(n, k);
     if (rc != Q4K_OK) {
@@ -390,8 +422,23 @@ int plan_checked(int64_t n, int64_t k, int64_t m, const q4k_launch* opts, bool w
     if (m < 1) {
         return Q4K_ERR_SHAPE;
     }
-    if (m > q4k::kMaxM) {
+    if (m > q4k::kMaxMWide) {
         return Q4K_ERR_UNSUPPORTED;
+    }
+    if (split) {
+        *split = false;
+        if (m > q4k::kMaxM && !(opts && (opts->kernel || any_option(opts)))) {
+            if (lds_max == 0) {
+                rc = device_lds_max(&lds_max);
+                if (rc != Q4K_OK) {
+                    return rc;
+                }
+            }
+            if (split_wide(n, k, m, opts, w128, lds_max)) {
+                *split = true;
+                return plan_checked(n, k, q4k::kMaxM, opts, w128, lds_max, plan);
+            }
+        }
     }
     // options are validated before the first HIP call (unbounded LDS), then
     // planned for the LDS size
@@ -431,7 +478,7 @@ int gemv_checked(const void* w, const float* x, float* y, int64_t n, int64_t k, 
     if (m < 1) {
         return Q4K_ERR_SHAPE;
     }
-    if (m > q4k::kMaxM) {
+    if (m > q4k::kMaxMWide) {
         return Q4K_ERR_UNSUPPORTED;
     }
     if (!aligned16(w) || !aligned16(x) || !aligned16(y)) {
@@ -439,11 +486,27 @@ int gemv_checked(const void* w, const float* x, float* y, int64_t n, int64_t k, 
     }
     const bool w128 = (reinterpret_cast<uintptr_t>(w) & 127u) == 0;
     GemvPlan plan;
-    rc = plan_checked(n, k, m, opts, w128, 0, &plan);
+    bool split = false;
+    rc = plan_checked(n, k, m, opts, w128, 0, &plan, &split);
     if (rc != Q4K_OK) {
         return rc;
     }
-    return hip_status(q4k::launch_gemv(plan, w, x, y, static_cast<hipStream_t>(stream)));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (split) {
+        // both launches planned before the first goes out
+        GemvPlan rest;
+        rc = plan_checked(n, k, m - q4k::kMaxM, opts, w128, 0, &rest);
+        if (rc != Q4K_OK) {
+            return rc;
+        }
+        rc = hip_status(q4k::launch_gemv(plan, w, x, y, s));
+        if (rc != Q4K_OK) {
+            return rc;
+        }
+        return hip_status(q4k::launch_gemv(rest, w, x + (size_t)q4k::kMaxM * (size_t)k,
+                                           y + (size_t)q4k::kMaxM * (size_t)n, s));
+    }
+    return hip_status(q4k::launch_gemv(plan, w, x, y, s));
 }
 
 }  // namespace
@@ -501,11 +564,16 @@ int q4k_plan(int64_t n, int64_t k, int64_t m, const q4k_launch* opts, int w_alig
     if (!out) {
         return Q4K_ERR_NULL;
     }
-    GemvPlan plan;
-    const int rc = plan_checked(n, k, m, opts, w_aligned128 != 0, lds_max, &plan);
+    GemvPlan plan, rest;
+    bool split = false;
+    int rc = plan_checked(n, k, m, opts, w_aligned128 != 0, lds_max, &plan, &split);
+    if (rc == Q4K_OK && split) {
+        rc = plan_checked(n, k, m - q4k::kMaxM, opts, w_aligned128 != 0, lds_max, &rest);
+    }
     if (rc != Q4K_OK) {
         return rc;
     }
+    out->launches = split ? 2 : 1;
     out->kernel = plan.kernel;
     out->grid = plan.grid;
     out->threads = plan.waves_per_block * 64;
@@ -544,7 +612,9 @@ const char* q4k_status_string(int rc)
     case Q4K_ERR_SHAPE: return "bad shape: need 1 <= n, 256 <= k, k % 256 == 0, 1 <= m, n and k below 2^31";
     case Q4K_ERR_SIZE: return "byte count does not match n*(k/256)*144";
     case Q4K_ERR_ALIGN: return "a pointer is not 16-byte aligned";
-    case Q4K_ERR_UNSUPPORTED: return "unsupported: m > 8, or launch options that do not fit the shape or the device";
+    case Q4K_ERR_UNSUPPORTED:
+        return "unsupported: m > 16, or launch options that do not fit the shape, m or the "
+               "device";
     default: break;
     }
     if (rc >= Q4K_ERR_HIP) {

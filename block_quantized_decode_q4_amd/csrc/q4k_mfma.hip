@@ -1,5 +1,6 @@
-// q4k_mfma.hip -- Q4_K GEMV for a small batch of vectors (m <= 8) on the
-// CDNA4 int8 matrix cores, fed by the line stream of q4k_lines.h.
+// q4k_mfma.hip -- Q4_K GEMV for a small batch of vectors (m <= 8; kernels 5
+// and 6 up to 16) on the CDNA4 int8 matrix cores, fed by the line stream of
+// q4k_lines.h.
 //
 // With several vectors the same decoded weights meet m different x, which
 // makes the multiply a real (small) contraction: the matrix cores take it,
@@ -10,7 +11,8 @@
 //    automatic for m = 2.  With m = 1 it runs only when asked for, as the
 //    measured matrix-core counterpart of the vector-ALU kernel (q4k_dpp.hip).
 //  * gemv_i8_sub_kernel<NW, XC, NQ, false> (kernel 5): one
-//    v_mfma_i32_16x16x32_i8 per 32-element sub-block and quad of vectors;
+//    v_mfma_i32_16x16x32_i8 per 32-element sub-block and quad of vectors
+//    (up to four quads: one pass over the weights for 16 vectors);
 //    automatic for m >= 3.
 //  * gemv_i8_sub_kernel<NW, XC, NQ, true> (kernel 6): the same decode with
 //    x converted per column by each wave for itself, for batches whose x
@@ -465,11 +467,12 @@ __device__ __forceinline__ RowScales decode_row(const uint4& h)
 // Columns of x a wave of kernel 6 holds in registers ahead of its step: with
 // four, waiting for a column's x (loads complete in order) never waits for
 // a weight line before the line stream itself would (the lines are three
-// ahead); two vector quads take two, as 4 x 32 registers do not fit.
+// ahead); two vector quads take two, as 4 x 32 registers do not fit, and
+// four quads one (64 registers).
 template <int NQ>
 constexpr int jit_ahead()
 {
-    return NQ == 1 ? 4 : 2;
+    return NQ == 1 ? 4 : NQ == 2 ? 2 : 1;
 }
 
 // JIT = false (kernel 5): x staged whole in LDS before the stream.  JIT =
@@ -754,16 +757,25 @@ static hipError_t launch_lines_m(const GemvPlan& p, const uint8_t* w, const floa
     return launch_lines_x<8, 3, 4, M>(p, w, x, y, stream);
 }
 
+// vector quads of the sub-block kernels' launch for m vectors (1, 2 or 4)
+static int sub_quads(int m)
+{
+    return m > 8 ? 4 : m > 4 ? 2 : 1;
+}
+
 hipError_t launch_gemv_mfma(const GemvPlan& p, const void* w, const float* x, float* y,
                             hipStream_t stream)
 {
     const uint8_t* wb = static_cast<const uint8_t*>(w);
-    if (p.kernel == 5) {
-        if (p.m > 4) return launch_sub<2>(p, wb, x, y, stream);
-        return launch_sub<1>(p, wb, x, y, stream);
-    }
-    if (p.kernel == 6) {
-        if (p.m > 4) return launch_sub_x<1, 2, true>(p, wb, x, y, stream);
+    if (p.kernel == 5 || p.kernel == 6) {
+        const int nq = sub_quads(p.m);         // the quads sub_lds_bytes, jit_lds_bytes size
+        if (p.kernel == 5) {
+            if (nq == 4) return launch_sub<4>(p, wb, x, y, stream);
+            if (nq == 2) return launch_sub<2>(p, wb, x, y, stream);
+            return launch_sub<1>(p, wb, x, y, stream);
+        }
+        if (nq == 4) return launch_sub_x<1, 4, true>(p, wb, x, y, stream);
+        if (nq == 2) return launch_sub_x<1, 2, true>(p, wb, x, y, stream);
         return launch_sub_x<1, 1, true>(p, wb, x, y, stream);
     }
     switch (p.m) {
@@ -783,13 +795,13 @@ hipError_t launch_gemv_mfma(const GemvPlan& p, const void* w, const float* x, fl
 
 size_t sub_lds_bytes(int S, int m)
 {
-    const int nq = (m + 3) / 4;
+    const int nq = sub_quads(m);
     return (size_t)(S * nq + 1) * kSbGroup + (size_t)8 * (S % 8 != 0 ? kRing4Wave : kRingWave);
 }
 
 size_t jit_lds_bytes(int S, int m)
 {
-    const int nq = (m + 3) / 4;
+    const int nq = sub_quads(m);
     return (size_t)8 * nq * kSbGroup + (size_t)8 * (S % 8 != 0 ? kRing4Wave : kRingWave);
 }
 

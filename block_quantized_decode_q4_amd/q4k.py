@@ -68,6 +68,7 @@ class q4k_plan_info(ctypes.Structure):
         ("cols_per_task", ctypes.c_int32),
         ("ring_depth", ctypes.c_int32),
         ("spans_per_chunk", ctypes.c_int32),
+        ("launches", ctypes.c_int32),
     ]
 
 

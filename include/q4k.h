@@ -60,7 +60,8 @@ enum q4k_status {
     Q4K_ERR_SHAPE = 2,       /* n < 1, k < 256, k % 256 != 0, m < 1, or too big  */
     Q4K_ERR_SIZE = 3,        /* byte count does not match n*(k/256)*144          */
     Q4K_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                 */
-    Q4K_ERR_UNSUPPORTED = 5, /* m > 8, or a launch option that cannot be honoured*/
+    Q4K_ERR_UNSUPPORTED = 5, /* m > 16, or a launch option that cannot be
+                                honoured (m > 8: kernels 5 and 6 only)          */
     Q4K_ERR_HIP = 1000       /* + hipError_t                                     */
 };
 
@@ -82,6 +83,11 @@ int q4k_load(void* w_dev, const void* src_host, size_t src_bytes,
  *  x : device, m*k f32, 16-byte aligned
  *  y : device, m*n f32, 16-byte aligned, fully overwritten (no accumulate)
  *  1 <= n <= 2^31-1, 256 <= k <= 2^31-1 with k % 256 == 0, 1 <= m <= 8.
+ *  9 <= m <= 16: one pass over the weights for all m vectors on the
+ *  sub-block matrix-core kernels (5, 6) where their whole x stage fits or
+ *  eight vectors would need kernel 6 as well; otherwise two launches on
+ *  `stream`, vectors 0-7 and then the rest (so any alignment and k).
+ *  m > 16: Q4K_ERR_UNSUPPORTED.
  * Asynchronous on `stream`; allocates nothing.  Results agree with the exact
  * dot product of the dequantized weights within 1e-5 * sum|w||x| per output
  * on the workloads' value distributions.  Dequantization happens in
@@ -107,7 +113,7 @@ const char* q4k_status_string(int rc);
  *   3  line-streamed vector-ALU (m = 1): whole 128-byte weight lines through
  *      a per-wave LDS ring, int8 dot products with x broadcast by DPP
  *   4  line-streamed int8 matrix-core (m <= 8), one MFMA group per vector
- *   5  sub-block int8 matrix-core (m <= 8), one MFMA per sub-block and quad
+ *   5  sub-block int8 matrix-core (m <= 16), one MFMA per sub-block and quad
  *      of vectors
  *   6  kernel 5 with x converted one superblock column at a time by each
  *      wave for itself (no whole x stage: any k and m)
@@ -118,7 +124,7 @@ const char* q4k_status_string(int rc);
  * Automatic choice: m = 1 kernel 3 when it applies and the weights take at
  * least 16 MiB, else kernel 2 (the matrix cores only when asked for); m > 1
  * kernel 5 for m >= 3, kernel 4 for m = 2, the other of the two if only it
- * fits, else kernel 6 when it fits, else kernel 1.  With kernel = 0 and
+ * fits, else kernel 6 when it fits, else kernel 1 (m <= 8).  With kernel = 0 and
  * another field set, m = 1 uses the streaming kernel and m > 1 the
  * x-stager.
  *
@@ -174,6 +180,9 @@ typedef struct q4k_plan_info {
     int32_t ring_depth;      /* streaming: rows in flight; line-streamed: lines */
     int32_t spans_per_chunk; /* kernels 1, 2: 4096-element spans per x stage;
                                 else 0                                          */
+    int32_t launches;        /* 1; 2 when an automatic plan of 9-16 vectors
+                                launches vectors 0-7, then the rest (the fields
+                                above describe the first launch)               */
 } q4k_plan_info;
 
 int q4k_plan(int64_t n, int64_t k, int64_t m, const q4k_launch* opts, int w_aligned128,

@@ -67,7 +67,7 @@ def test_gemv_refusals(lib):
     for n, k, m in ((0, 256, 1), (-1, 256, 1), (16, 255, 1), (16, 0, 1), (16, 384, 1),
                     (16, 256, 0), (16, 256, -3), (2 ** 31, 256, 1), (16, 2 ** 31 + 256, 1)):
         assert raw_gemv(lib, A, A, A, n, k, m) == q4k.Q4K_ERR_SHAPE, (n, k, m)
-    for m in (9, 16, 32):
+    for m in (17, 32):
         assert raw_gemv(lib, A, A, A, 16, 256, m) == q4k.Q4K_ERR_UNSUPPORTED
     assert raw_gemv(lib, MIS, A, A, 16, 256, 1) == q4k.Q4K_ERR_ALIGN
     assert raw_gemv(lib, A, MIS, A, 16, 256, 1) == q4k.Q4K_ERR_ALIGN
@@ -163,7 +163,7 @@ def test_binding_raises_with_status():
         q4k.q4k_gemv(0, A, A, 16, 256, 1, stream=0)
     assert ei.value.rc == q4k.Q4K_ERR_NULL
     with pytest.raises(q4k.Q4KError) as ei:
-        q4k.q4k_gemv(A, A, A, 16, 256, 9, stream=0)
+        q4k.q4k_gemv(A, A, A, 16, 256, 17, stream=0)
     assert ei.value.rc == q4k.Q4K_ERR_UNSUPPORTED
 
 
@@ -229,7 +229,49 @@ def test_plan_refusals(lib):
     out = q4k.q4k_plan_info()
     assert lib.q4k_plan(4096, 4096, 1, None, 1, MI355X_LDS, None) == q4k.Q4K_ERR_NULL
     assert lib.q4k_plan(16, 100, 1, None, 1, MI355X_LDS, ctypes.byref(out)) == q4k.Q4K_ERR_SHAPE
-    assert lib.q4k_plan(16, 256, 9, None, 1, MI355X_LDS, ctypes.byref(out)) == q4k.Q4K_ERR_UNSUPPORTED
+    assert lib.q4k_plan(16, 256, 17, None, 1, MI355X_LDS, ctypes.byref(out)) == q4k.Q4K_ERR_UNSUPPORTED
+    assert lib.q4k_plan(16, 256, 9, None, 0, MI355X_LDS, ctypes.byref(out)) == q4k.Q4K_OK
+    assert out.launches == 2 and out.kernel == 1     # unaligned: two x-stager launches
     cfg = q4k.q4k_launch(kernel=3)
     assert lib.q4k_plan(32000, 4096, 2, ctypes.byref(cfg), 1, MI355X_LDS,
                         ctypes.byref(out)) == q4k.Q4K_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("n,k,m,aligned,launches,kernel", [
+    (4096, 14336, 16, True, 1, 6),     # eight vectors take kernel 6 too: one pass
+    (300, 2048, 12, True, 1, 5),       # sixteen vectors' x fits one stage
+    (17, 1280, 13, True, 1, 5),        # partial slab, whole stage
+    (5, 256, 16, True, 1, 5),
+    (14336, 4096, 16, True, 2, 5),     # eight vectors stage x whole: two launches
+    (14336, 4096, 9, True, 2, 5),
+    (32000, 4096, 16, True, 2, 5),
+    (130, 11008, 16, True, 2, 6),      # sixteen vectors' plan exceeds the LDS
+    (14336, 4096, 9, False, 2, 1),     # weights not 128-byte aligned
+])
+def test_plan_wide_batches(n, k, m, aligned, launches, kernel):
+    """9-16 vectors: one pass over the weights, or two launches of at most
+    eight vectors (the fields describe the first)."""
+    p = q4k.q4k_plan(n, k, m, w_aligned128=aligned, lds_max=MI355X_LDS)
+    assert (p.launches, p.kernel) == (launches, kernel)
+    assert p.lds_bytes <= MI355X_LDS
+    if launches == 2:
+        first = q4k.q4k_plan(n, k, 8, w_aligned128=aligned, lds_max=MI355X_LDS)
+        assert [getattr(p, f) for f, _ in p._fields_][:-1] == \
+            [getattr(first, f) for f, _ in first._fields_][:-1]
+    for m1 in range(1, 9):
+        assert q4k.q4k_plan(n, k, m1, w_aligned128=aligned, lds_max=MI355X_LDS).launches == 1
+
+
+def test_plan_wide_batch_refusals():
+    for opts in (dict(kernel=1), dict(kernel=4), dict(rows_per_block=64)):
+        with pytest.raises(q4k.Q4KError) as ei:
+            q4k.q4k_plan(14336, 4096, 9, lds_max=MI355X_LDS, **opts)
+        assert ei.value.rc == q4k.Q4K_ERR_UNSUPPORTED
+    # rows of partial slabs whose x of 16 vectors does not fit one stage:
+    # kernel 6's four-line rings and four quads exceed the LDS
+    with pytest.raises(q4k.Q4KError) as ei:
+        q4k.q4k_plan(130, 11008, 16, lds_max=MI355X_LDS, kernel=6)
+    assert ei.value.rc == q4k.Q4K_ERR_UNSUPPORTED
+    # a forced kernel is one launch
+    p = q4k.q4k_plan(14336, 4096, 16, lds_max=MI355X_LDS, kernel=6)
+    assert (p.launches, p.kernel) == (1, 6)

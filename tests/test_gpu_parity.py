@@ -766,3 +766,78 @@ def test_random_shapes_automatic_plan(oracle_mod, n, k, m, off):
     assert w_d.data_ptr() % 128 == off % 128
     y = run_gemv(w_d, x, n, k, m)
     assert_within(y, y_ref, bound, "n=%d k=%d m=%d off=%d" % (n, k, m, off))
+
+
+# 9-16 vectors: one pass over the weights for up to four quads of vectors on
+# the sub-block kernels.  Per vector the digits, MFMAs and sums are those of
+# a single-vector launch of the same kernel and column grouping.
+@pytest.mark.parametrize("n,k,m", [(300, 4096, 16), (130, 4096, 9), (17, 2048, 12), (64, 8192, 13),
+                                   (33, 2048, 15), (1, 2048, 10), (257, 16384, 16),
+                                   (40, 14336, 11),
+                                   # rows of partial slabs: kernel 5's whole x stage
+                                   (17, 1280, 13), (5, 768, 16), (70, 1536, 9)])
+def test_wide_batch(oracle_mod, n, k, m):
+    w, x = synth.make_inputs(n, k, m, seed=n * 37 + k + 11 * m)
+    y_ref, bound = oracle_mod.gemv(w, x, n)
+    w_d = dev(w)
+    _say("wide batch n=%d k=%d m=%d" % (n, k, m))
+    y = run_gemv(w_d, x, n, k, m)               # automatic kernel
+    assert_within(y, y_ref, bound, "wide batch automatic m=%d" % m)
+    ran = []
+    for kern in (5, 6):
+        try:
+            yk = run_gemv(w_d, x, n, k, m, kernel=kern, cols_per_task=8)
+        except q4k.Q4KError as e:
+            assert e.rc == q4k.Q4K_ERR_UNSUPPORTED
+            continue
+        ran.append(kern)
+        assert_within(yk, y_ref, bound, "wide batch kernel %d m=%d" % (kern, m))
+        for b in range(m):                      # batched == m single-vector launches
+            y1 = run_gemv(w_d, x[b:b + 1], n, k, 1, kernel=kern, cols_per_task=8)
+            assert np.array_equal(y1[0].view(np.uint32), yk[b].view(np.uint32)), (kern, b)
+    assert ran
+
+
+def test_wide_batch_full_size(oracle_mod):
+    """14336 x 4096 with sixteen vectors (automatic: kernel 6) against the
+    oracle, and against two calls of eight vectors (same kernel and column
+    grouping: bit-identical)."""
+    n, k, m = 14336, 4096, 16
+    w, x = synth.make_inputs(n, k, m, seed=14336 + 4096 + 16)
+    y_ref, bound = oracle_mod.gemv(w, x, n)
+    w_d = dev(w)
+    _say("wide batch automatic n=%d k=%d m=%d" % (n, k, m))
+    y = run_gemv(w_d, x, n, k, m)
+    assert_within(y, y_ref, bound, "14336 x 4096 m=16")
+    y16 = run_gemv(w_d, x, n, k, m, kernel=6, cols_per_task=8)
+    assert_within(y16, y_ref, bound, "14336 x 4096 m=16 one pass")
+    for h in range(2):
+        y8 = run_gemv(w_d, x[8 * h:8 * h + 8], n, k, 8, kernel=6, cols_per_task=8)
+        assert np.array_equal(y8.view(np.uint32), y16[8 * h:8 * h + 8].view(np.uint32)), h
+    # the automatic plan here is two launches: exactly two calls of eight
+    assert q4k.q4k_plan(n, k, m).launches == 2
+    for h in range(2):
+        y8 = run_gemv(w_d, x[8 * h:8 * h + 8], n, k, 8)
+        assert np.array_equal(y8.view(np.uint32), y[8 * h:8 * h + 8].view(np.uint32)), h
+
+
+@pytest.mark.parametrize("n,k,m,off", [(300, 4096, 12, 16), (130, 11008, 16, 0), (33, 2304, 9, 48),
+                                       (4096, 14336, 16, 0)])
+def test_wide_batch_automatic(oracle_mod, n, k, m, off):
+    """Automatic plans of 9-16 vectors (one pass, or two launches on
+    unaligned weights and on rows whose sixteen-vector plan exceeds the
+    LDS) against the oracle, and a two-launch plan against its two calls."""
+    p = q4k.q4k_plan(n, k, m, w_aligned128=(off == 0))
+    _say("wide batch automatic n=%d k=%d m=%d off=%d -> %d launch(es), kernel %d"
+         % (n, k, m, off, p.launches, p.kernel))
+    w, x = synth.make_inputs(n, k, m, seed=n * 41 + k + 13 * m)
+    y_ref, bound = oracle_mod.gemv(w, x, n)
+    buf = torch.empty(w.size + off, dtype=torch.uint8, device="cuda")
+    buf[off:].copy_(torch.from_numpy(w))
+    w_d = buf[off:]
+    y = run_gemv(w_d, x, n, k, m)
+    assert_within(y, y_ref, bound, "n=%d k=%d m=%d off=%d" % (n, k, m, off))
+    if p.launches == 2:
+        ya = run_gemv(w_d, x[:8], n, k, 8)
+        yb = run_gemv(w_d, x[8:], n, k, m - 8)
+        assert np.array_equal(np.concatenate([ya, yb]).view(np.uint32), y.view(np.uint32))
