@@ -75,7 +75,8 @@ int device_lds_max(size_t* out)
     return Q4K_OK;
 }
 
-// Plan of the line-streamed kernels (weights 128-byte aligned, m <= 8):
+// Plan of the line-streamed kernels (weights 128-byte aligned; m <= 8, kernels
+// 5 and 6 m <= 16):
 // kernel 3 (m = 1, integer dot products on the vector ALU, any k), kernel 4
 // (one MFMA group per vector; k a multiple of 2048), kernel 5 (one MFMA per
 // sub-block and quad of vectors) and kernel 6 (kernel 5 with x converted per

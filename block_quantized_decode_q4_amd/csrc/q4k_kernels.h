@@ -13,7 +13,7 @@ constexpr int kQK = 256;          // weights per superblock
 constexpr int kBlockBytes = 144;  // bytes per superblock
 constexpr int kSpanSB = 16;       // superblocks per wave pass (4 lanes each)
 constexpr int kSpan = kSpanSB * kQK;
-constexpr int kMaxM = 8;         // vectors per call: every kernel
+constexpr int kMaxM = 8;         // vectors per launch that every kernel takes
 constexpr int kMaxMWide = 16;    // the sub-block matrix-core kernels 5 and 6
 constexpr int kReadBlocks = 4096;
 
