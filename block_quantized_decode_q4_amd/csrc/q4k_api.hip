@@ -384,37 +384,13 @@ int make_plan(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t lds_m
     return Q4K_OK;
 }
 
-// 9-16 vectors, automatic plan: one pass of the sub-block kernels over the
-// weights where their whole x stage fits or where eight vectors would take
-// kernel 6 anyway; else two launches (vectors 0-7, then the rest).  Measured
-// on MI355X, two launches of eight against one pass of sixteen: 4096 x 14336
-// 2 x 21.0 against 34.0 us; 14336 x 4096 28.7 against 33.8 and 32000 x 4096
-// 43.9 against 61.1 us (with four vector quads kernel 6 holds only one x
-// column in registers ahead of its step, where kernel 5 of eight vectors
-// stages x whole).  Two launches also serve weights that are not 128-byte
-// aligned and rows whose sixteen-vector plan does not fit the LDS.
-bool split_wide(int64_t n, int64_t k, int64_t m, const q4k_launch* o, bool w128, size_t lds_max)
-{
-    if (m <= q4k::kMaxM || (o && (o->kernel || any_option(o)))) {
-        return false;
-    }
-    GemvPlan pw, p8;
-    if (make_plan(n, k, m, nullptr, lds_max, &pw, w128) != Q4K_OK || pw.kernel < 5 ||
-        pw.lds_bytes > lds_max) {
-        return true;
-    }
-    if (pw.kernel == 5) {
-        return false;
-    }
-    return make_plan(n, k, q4k::kMaxM, nullptr, lds_max, &p8, w128) != Q4K_OK || p8.kernel != 6;
-}
-
 // The plan gemv_checked would launch, for a given LDS budget; shape and
-// option checks in the same order.  *split (may be NULL: then never): the
-// automatic plan of 9-16 vectors is two launches, `plan` the first (vectors
-// 0-7), plan_checked(m - 8) the second.
+// option checks in the same order.  9-16 vectors run in one pass over the
+// weights on the sub-block kernels (5, 6) or are refused: a batch is never
+// split into several launches (turbospark-runtime 0.1.0,
+// real_forward_dispatch.rs: doc of `encode_gemm_any`).
 int plan_checked(int64_t n, int64_t k, int64_t m, const q4k_launch* opts, bool w128,
-                 size_t lds_max, GemvPlan* plan, bool* split = nullptr)
+                 size_t lds_max, GemvPlan* plan)
 {
     int rc = check_nk(n, k);
     if (rc != Q4K_OK) {
@@ -425,21 +401,6 @@ int plan_checked(int64_t n, int64_t k, int64_t m, const q4k_launch* opts, bool w
     }
     if (m > q4k::kMaxMWide) {
         return Q4K_ERR_UNSUPPORTED;
-    }
-    if (split) {
-        *split = false;
-        if (m > q4k::kMaxM && !(opts && (opts->kernel || any_option(opts)))) {
-            if (lds_max == 0) {
-                rc = device_lds_max(&lds_max);
-                if (rc != Q4K_OK) {
-                    return rc;
-                }
-            }
-            if (split_wide(n, k, m, opts, w128, lds_max)) {
-                *split = true;
-                return plan_checked(n, k, q4k::kMaxM, opts, w128, lds_max, plan);
-            }
-        }
     }
     // options are validated before the first HIP call (unbounded LDS), then
     // planned for the LDS size
@@ -462,6 +423,9 @@ int plan_checked(int64_t n, int64_t k, int64_t m, const q4k_launch* opts, bool w
     }
     if (plan->kernel >= 3 && !w128) {
         return Q4K_ERR_UNSUPPORTED;    // whole-line reads need 128-byte aligned rows
+    }
+    if (m > q4k::kMaxM && plan->kernel < 5) {
+        return Q4K_ERR_UNSUPPORTED;    // 9-16 vectors: the sub-block kernels only
     }
     return Q4K_OK;
 }
@@ -487,26 +451,11 @@ int gemv_checked(const void* w, const float* x, float* y, int64_t n, int64_t k, 
     }
     const bool w128 = (reinterpret_cast<uintptr_t>(w) & 127u) == 0;
     GemvPlan plan;
-    bool split = false;
-    rc = plan_checked(n, k, m, opts, w128, 0, &plan, &split);
+    rc = plan_checked(n, k, m, opts, w128, 0, &plan);
     if (rc != Q4K_OK) {
         return rc;
     }
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    if (split) {
-        // both launches planned before the first goes out
-        GemvPlan rest;
-        rc = plan_checked(n, k, m - q4k::kMaxM, opts, w128, 0, &rest);
-        if (rc != Q4K_OK) {
-            return rc;
-        }
-        rc = hip_status(q4k::launch_gemv(plan, w, x, y, s));
-        if (rc != Q4K_OK) {
-            return rc;
-        }
-        return hip_status(q4k::launch_gemv(rest, w, x + (size_t)q4k::kMaxM * (size_t)k,
-                                           y + (size_t)q4k::kMaxM * (size_t)n, s));
-    }
     return hip_status(q4k::launch_gemv(plan, w, x, y, s));
 }
 
@@ -565,16 +514,11 @@ int q4k_plan(int64_t n, int64_t k, int64_t m, const q4k_launch* opts, int w_alig
     if (!out) {
         return Q4K_ERR_NULL;
     }
-    GemvPlan plan, rest;
-    bool split = false;
-    int rc = plan_checked(n, k, m, opts, w_aligned128 != 0, lds_max, &plan, &split);
-    if (rc == Q4K_OK && split) {
-        rc = plan_checked(n, k, m - q4k::kMaxM, opts, w_aligned128 != 0, lds_max, &rest);
-    }
+    GemvPlan plan;
+    const int rc = plan_checked(n, k, m, opts, w_aligned128 != 0, lds_max, &plan);
     if (rc != Q4K_OK) {
         return rc;
     }
-    out->launches = split ? 2 : 1;
     out->kernel = plan.kernel;
     out->grid = plan.grid;
     out->threads = plan.waves_per_block * 64;

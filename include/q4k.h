@@ -18,8 +18,10 @@
  *    occupies x[b*k .. b*k+k-1] and y[b*n .. b*n+n-1] (realizar 0.8.5,
  *    uses.rs: memory-layout doc of `batched_q4k_gemv_into`; turbospark-
  *    runtime 0.1.0, real_forward_dispatch.rs: doc of `encode_gemm_any`).
- *    At most 8 vectors per call (uses.rs: `batched_q4k_gemv_into`, "max 8");
- *    more are refused by name, never looped (real_forward_dispatch.rs: doc of
+ *    The pages batch at most 8 vectors per call (uses.rs:
+ *    `batched_q4k_gemv_into`, "max 8"); here 9-16 also run, in one pass over
+ *    the weights, where the kernels that can hold them apply.  Anything else
+ *    is refused by name, never looped (real_forward_dispatch.rs: doc of
  *    `encode_gemm_any`).
  *  - Weights are uploaded once and reused by every call (realizar 0.8.5,
  *    q4k_gemv_cached.rs: doc of `q4k_gemv_cached`); the launch is
@@ -60,8 +62,9 @@ enum q4k_status {
     Q4K_ERR_SHAPE = 2,       /* n < 1, k < 256, k % 256 != 0, m < 1, or too big  */
     Q4K_ERR_SIZE = 3,        /* byte count does not match n*(k/256)*144          */
     Q4K_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                 */
-    Q4K_ERR_UNSUPPORTED = 5, /* m > 16, or a launch option that cannot be
-                                honoured (m > 8: kernels 5 and 6 only)          */
+    Q4K_ERR_UNSUPPORTED = 5, /* m > 16; 9-16 vectors where the one-pass
+                                kernels 5 and 6 do not apply; or a launch
+                                option that cannot be honoured                  */
     Q4K_ERR_HIP = 1000       /* + hipError_t                                     */
 };
 
@@ -83,11 +86,10 @@ int q4k_load(void* w_dev, const void* src_host, size_t src_bytes,
  *  x : device, m*k f32, 16-byte aligned
  *  y : device, m*n f32, 16-byte aligned, fully overwritten (no accumulate)
  *  1 <= n <= 2^31-1, 256 <= k <= 2^31-1 with k % 256 == 0, 1 <= m <= 8.
- *  9 <= m <= 16: one pass over the weights for all m vectors on the
- *  sub-block matrix-core kernels (5, 6) where their whole x stage fits or
- *  eight vectors would need kernel 6 as well; otherwise two launches on
- *  `stream`, vectors 0-7 and then the rest (so any alignment and k).
- *  m > 16: Q4K_ERR_UNSUPPORTED.
+ *  9 <= m <= 16 (beyond the pages' batch of 8): one pass over the weights on
+ *  the sub-block matrix-core kernels (5, 6) when w is 128-byte aligned and
+ *  their LDS fits; otherwise Q4K_ERR_UNSUPPORTED.  m > 16:
+ *  Q4K_ERR_UNSUPPORTED.  A batch is never split into several launches.
  * Asynchronous on `stream`; allocates nothing.  Results agree with the exact
  * dot product of the dequantized weights within 1e-5 * sum|w||x| per output
  * on the workloads' value distributions.  Dequantization happens in
@@ -96,7 +98,10 @@ int q4k_gemv(const void* w, const float* x, float* y,
              int64_t n, int64_t k, int64_t m, void* stream);
 
 /* out[r*k + c] = W[r][c] as f32 (bit-exact: one round-to-nearest-even of
- * d*sc_j*q - dmin*m_j, whose products are exact in f32).
+ * d*sc_j*q - dmin*m_j, whose products are exact in f32).  The f32 twin of the
+ * pages' Q4_K dequantizer (memra-engine 0.83.1, src/f16_ffi.rs: doc comment
+ * of `memra_q4_K_dequant_f16`, which writes the same weights as fp16 for a
+ * mirror of the matrix).
  *  w   : device, as for q4k_gemv
  *  out : device, n*k f32, 16-byte aligned.
  * Asynchronous on `stream`. */
@@ -180,9 +185,6 @@ typedef struct q4k_plan_info {
     int32_t ring_depth;      /* streaming: rows in flight; line-streamed: lines */
     int32_t spans_per_chunk; /* kernels 1, 2: 4096-element spans per x stage;
                                 else 0                                          */
-    int32_t launches;        /* 1; 2 when an automatic plan of 9-16 vectors
-                                launches vectors 0-7, then the rest (the fields
-                                above describe the first launch)               */
 } q4k_plan_info;
 
 int q4k_plan(int64_t n, int64_t k, int64_t m, const q4k_launch* opts, int w_aligned128,

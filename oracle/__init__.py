@@ -13,7 +13,6 @@ Functions (names follow the problem's notation: d, dmin, sc_j, m_j, q):
   pack_scales(sc, m)          the inverse, written from the same bit table
   dequant(w, n, k)            f32 weights [n, k], one rounding per weight
   gemv(w, x)                  y and sum|w||x| in f64, x is [m, k]
-  gemv_rows(w, x, rows)       the same for listed rows only
   quantize_rows(x)            simple reference quantizer -> Q4_K bytes
 """
 from __future__ import annotations
@@ -60,7 +59,6 @@ def _load():
         u8p = ctypes.POINTER(ctypes.c_uint8)
         f32p = ctypes.POINTER(ctypes.c_float)
         f64p = ctypes.POINTER(ctypes.c_double)
-        i64p = ctypes.POINTER(ctypes.c_int64)
         i64 = ctypes.c_int64
         lib.oq_f16_to_f32.argtypes = [ctypes.c_uint16]
         lib.oq_f16_to_f32.restype = ctypes.c_float
@@ -76,8 +74,6 @@ def _load():
         lib.oq_dequant.restype = ctypes.c_int
         lib.oq_gemv.argtypes = [u8p, f32p, i64, i64, i64, f64p, f64p]
         lib.oq_gemv.restype = ctypes.c_int
-        lib.oq_gemv_rows.argtypes = [u8p, f32p, i64, i64, i64, i64p, i64, f64p, f64p]
-        lib.oq_gemv_rows.restype = ctypes.c_int
         lib.oq_quantize_row.argtypes = [f32p, i64, u8p]
         lib.oq_quantize_row.restype = ctypes.c_int
         lib.oq_num_threads.argtypes = []
@@ -185,26 +181,6 @@ def gemv(w, x, n: int) -> tuple[np.ndarray, np.ndarray]:
                      _ptr(y, ctypes.c_double), _ptr(bound, ctypes.c_double))
     if rc != 0:
         raise RuntimeError("oq_gemv rc=%d" % rc)
-    return y, bound
-
-
-def gemv_rows(w, x, n: int, rows) -> tuple[np.ndarray, np.ndarray]:
-    """The oracle on listed rows only: y[b, t], bound[b, t] for row rows[t]."""
-    lib = _load()
-    xa = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
-    if xa.ndim == 1:
-        xa = xa.reshape(1, -1)
-    m, k = xa.shape
-    wb = _u8(w)
-    _check_shape(wb, n, k)
-    r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1))
-    y = np.empty((m, r.size), dtype=np.float64)
-    bound = np.empty((m, r.size), dtype=np.float64)
-    rc = lib.oq_gemv_rows(_ptr(wb, ctypes.c_uint8), _ptr(xa, ctypes.c_float), n, k, m,
-                          _ptr(r, ctypes.c_int64), r.size,
-                          _ptr(y, ctypes.c_double), _ptr(bound, ctypes.c_double))
-    if rc != 0:
-        raise RuntimeError("oq_gemv_rows rc=%d" % rc)
     return y, bound
 
 

@@ -256,36 +256,6 @@ int oq_gemv(const uint8_t* w, const float* x, int64_t n, int64_t k, int64_t m,
     return bad ? -2 : 0;
 }
 
-/* The same for a list of rows: y[b][t], bound[b][t] for the t-th listed row. */
-int oq_gemv_rows(const uint8_t* w, const float* x, int64_t n, int64_t k, int64_t m,
-                 const int64_t* rows, int64_t nrows, double* y, double* bound)
-{
-    if (!oq_shape_ok(n, k) || m < 1) {
-        return -1;
-    }
-    for (int64_t t = 0; t < nrows; ++t) {
-        if (rows[t] < 0 || rows[t] >= n) {
-            return -1;
-        }
-    }
-    int bad = 0;
-#pragma omp parallel
-    {
-        float* wrow = (float*)malloc((size_t)k * sizeof(float));
-        if (!wrow) {
-#pragma omp atomic write
-            bad = 1;
-        } else {
-#pragma omp for schedule(static)
-            for (int64_t t = 0; t < nrows; ++t) {
-                oq_row(w, x, k, m, rows[t], wrow, y + t, bound ? bound + t : NULL, nrows);
-            }
-            free(wrow);
-        }
-    }
-    return bad ? -2 : 0;
-}
-
 /* ---------------------------------------------------------------------------
  * Simple reference quantizer (tests only): one row of k floats -> k/256
  * superblocks.  Per 32-element sub-block j: lo_j = min(0, min x), hi_j =

@@ -230,36 +230,44 @@ def test_plan_refusals(lib):
     assert lib.q4k_plan(4096, 4096, 1, None, 1, MI355X_LDS, None) == q4k.Q4K_ERR_NULL
     assert lib.q4k_plan(16, 100, 1, None, 1, MI355X_LDS, ctypes.byref(out)) == q4k.Q4K_ERR_SHAPE
     assert lib.q4k_plan(16, 256, 17, None, 1, MI355X_LDS, ctypes.byref(out)) == q4k.Q4K_ERR_UNSUPPORTED
-    assert lib.q4k_plan(16, 256, 9, None, 0, MI355X_LDS, ctypes.byref(out)) == q4k.Q4K_OK
-    assert out.launches == 2 and out.kernel == 1     # unaligned: two x-stager launches
+    # 9-16 vectors need the one-pass sub-block kernels, which need 128-byte
+    # aligned weights: refused, never split into two launches
+    assert lib.q4k_plan(16, 256, 9, None, 0, MI355X_LDS, ctypes.byref(out)) == \
+        q4k.Q4K_ERR_UNSUPPORTED
     cfg = q4k.q4k_launch(kernel=3)
     assert lib.q4k_plan(32000, 4096, 2, ctypes.byref(cfg), 1, MI355X_LDS,
                         ctypes.byref(out)) == q4k.Q4K_ERR_UNSUPPORTED
 
 
-@pytest.mark.parametrize("n,k,m,aligned,launches,kernel", [
-    (4096, 14336, 16, True, 1, 6),     # eight vectors take kernel 6 too: one pass
-    (300, 2048, 12, True, 1, 5),       # sixteen vectors' x fits one stage
-    (17, 1280, 13, True, 1, 5),        # partial slab, whole stage
-    (5, 256, 16, True, 1, 5),
-    (14336, 4096, 16, True, 2, 5),     # eight vectors stage x whole: two launches
-    (14336, 4096, 9, True, 2, 5),
-    (32000, 4096, 16, True, 2, 5),
-    (130, 11008, 16, True, 2, 6),      # sixteen vectors' plan exceeds the LDS
-    (14336, 4096, 9, False, 2, 1),     # weights not 128-byte aligned
+@pytest.mark.parametrize("n,k,m,kernel", [
+    (4096, 14336, 16, 6),     # x per column per wave
+    (300, 2048, 12, 5),       # sixteen vectors' x fits one stage
+    (17, 1280, 13, 5),        # partial slab, whole stage
+    (5, 256, 16, 5),
+    (14336, 4096, 16, 6),
+    (14336, 4096, 9, 6),
+    (32000, 4096, 16, 6),
 ])
-def test_plan_wide_batches(n, k, m, aligned, launches, kernel):
-    """9-16 vectors: one pass over the weights, or two launches of at most
-    eight vectors (the fields describe the first)."""
-    p = q4k.q4k_plan(n, k, m, w_aligned128=aligned, lds_max=MI355X_LDS)
-    assert (p.launches, p.kernel) == (launches, kernel)
+def test_plan_wide_batches(n, k, m, kernel):
+    """9-16 vectors: one pass over the weights on a sub-block kernel."""
+    p = q4k.q4k_plan(n, k, m, lds_max=MI355X_LDS)
+    assert p.kernel == kernel
     assert p.lds_bytes <= MI355X_LDS
-    if launches == 2:
-        first = q4k.q4k_plan(n, k, 8, w_aligned128=aligned, lds_max=MI355X_LDS)
-        assert [getattr(p, f) for f, _ in p._fields_][:-1] == \
-            [getattr(first, f) for f, _ in first._fields_][:-1]
-    for m1 in range(1, 9):
-        assert q4k.q4k_plan(n, k, m1, w_aligned128=aligned, lds_max=MI355X_LDS).launches == 1
+
+
+@pytest.mark.parametrize("n,k,m,aligned", [
+    (130, 11008, 16, True),   # the sixteen-vector plan exceeds the LDS
+    (14336, 4096, 9, False),  # weights not 128-byte aligned
+    (64, 4096, 12, False),
+])
+def test_plan_wide_batches_refused(n, k, m, aligned):
+    """9-16 vectors where no one-pass kernel applies: refused by name, not
+    split into launches of at most eight (turbospark-runtime 0.1.0,
+    real_forward_dispatch.rs: doc of `encode_gemm_any`); eight still run."""
+    with pytest.raises(q4k.Q4KError) as ei:
+        q4k.q4k_plan(n, k, m, w_aligned128=aligned, lds_max=MI355X_LDS)
+    assert ei.value.rc == q4k.Q4K_ERR_UNSUPPORTED
+    q4k.q4k_plan(n, k, 8, w_aligned128=aligned, lds_max=MI355X_LDS)
 
 
 def test_plan_wide_batch_refusals():
@@ -272,6 +280,5 @@ def test_plan_wide_batch_refusals():
     with pytest.raises(q4k.Q4KError) as ei:
         q4k.q4k_plan(130, 11008, 16, lds_max=MI355X_LDS, kernel=6)
     assert ei.value.rc == q4k.Q4K_ERR_UNSUPPORTED
-    # a forced kernel is one launch
     p = q4k.q4k_plan(14336, 4096, 16, lds_max=MI355X_LDS, kernel=6)
-    assert (p.launches, p.kernel) == (1, 6)
+    assert p.kernel == 6

@@ -799,14 +799,15 @@ def test_wide_batch(oracle_mod, n, k, m):
 
 
 def test_wide_batch_full_size(oracle_mod):
-    """14336 x 4096 with sixteen vectors (automatic: kernel 6) against the
-    oracle, and against two calls of eight vectors (same kernel and column
-    grouping: bit-identical)."""
+    """14336 x 4096 with sixteen vectors (automatic: one pass on kernel 6)
+    against the oracle, and against two calls of eight vectors on the same
+    kernel and column grouping (bit-identical)."""
     n, k, m = 14336, 4096, 16
     w, x = synth.make_inputs(n, k, m, seed=14336 + 4096 + 16)
     y_ref, bound = oracle_mod.gemv(w, x, n)
     w_d = dev(w)
     _say("wide batch automatic n=%d k=%d m=%d" % (n, k, m))
+    assert q4k.q4k_plan(n, k, m).kernel == 6
     y = run_gemv(w_d, x, n, k, m)
     assert_within(y, y_ref, bound, "14336 x 4096 m=16")
     y16 = run_gemv(w_d, x, n, k, m, kernel=6, cols_per_task=8)
@@ -814,30 +815,33 @@ def test_wide_batch_full_size(oracle_mod):
     for h in range(2):
         y8 = run_gemv(w_d, x[8 * h:8 * h + 8], n, k, 8, kernel=6, cols_per_task=8)
         assert np.array_equal(y8.view(np.uint32), y16[8 * h:8 * h + 8].view(np.uint32)), h
-    # the automatic plan here is two launches: exactly two calls of eight
-    assert q4k.q4k_plan(n, k, m).launches == 2
-    for h in range(2):
-        y8 = run_gemv(w_d, x[8 * h:8 * h + 8], n, k, 8)
-        assert np.array_equal(y8.view(np.uint32), y[8 * h:8 * h + 8].view(np.uint32)), h
 
 
-@pytest.mark.parametrize("n,k,m,off", [(300, 4096, 12, 16), (130, 11008, 16, 0), (33, 2304, 9, 48),
+@pytest.mark.parametrize("n,k,m,off", [(300, 4096, 12, 0), (130, 11008, 16, 0), (33, 2304, 9, 48),
                                        (4096, 14336, 16, 0)])
 def test_wide_batch_automatic(oracle_mod, n, k, m, off):
-    """Automatic plans of 9-16 vectors (one pass, or two launches on
-    unaligned weights and on rows whose sixteen-vector plan exceeds the
-    LDS) against the oracle, and a two-launch plan against its two calls."""
-    p = q4k.q4k_plan(n, k, m, w_aligned128=(off == 0))
-    _say("wide batch automatic n=%d k=%d m=%d off=%d -> %d launch(es), kernel %d"
-         % (n, k, m, off, p.launches, p.kernel))
+    """Automatic plans of 9-16 vectors: one pass against the oracle, or a
+    refusal (unaligned weights; rows whose sixteen-vector plan exceeds the
+    LDS) that launches nothing and leaves y untouched."""
     w, x = synth.make_inputs(n, k, m, seed=n * 41 + k + 13 * m)
-    y_ref, bound = oracle_mod.gemv(w, x, n)
     buf = torch.empty(w.size + off, dtype=torch.uint8, device="cuda")
     buf[off:].copy_(torch.from_numpy(w))
     w_d = buf[off:]
+    try:
+        p = q4k.q4k_plan(n, k, m, w_aligned128=(off == 0))
+    except q4k.Q4KError as e:
+        assert e.rc == q4k.Q4K_ERR_UNSUPPORTED
+        _say("wide batch automatic n=%d k=%d m=%d off=%d -> refused" % (n, k, m, off))
+        x_d = dev(x)
+        y_d = torch.full((m, n), 7.0, dtype=torch.float32, device="cuda")
+        with pytest.raises(q4k.Q4KError) as ei:
+            q4k.q4k_gemv(w_d, x_d, y_d, n, k, m)
+        assert ei.value.rc == q4k.Q4K_ERR_UNSUPPORTED
+        torch.cuda.synchronize()
+        assert bool((y_d == 7.0).all())
+        return
+    _say("wide batch automatic n=%d k=%d m=%d off=%d -> kernel %d" % (n, k, m, off, p.kernel))
+    assert p.kernel in (5, 6)
+    y_ref, bound = oracle_mod.gemv(w, x, n)
     y = run_gemv(w_d, x, n, k, m)
     assert_within(y, y_ref, bound, "n=%d k=%d m=%d off=%d" % (n, k, m, off))
-    if p.launches == 2:
-        ya = run_gemv(w_d, x[:8], n, k, 8)
-        yb = run_gemv(w_d, x[8:], n, k, m - 8)
-        assert np.array_equal(np.concatenate([ya, yb]).view(np.uint32), y.view(np.uint32))
