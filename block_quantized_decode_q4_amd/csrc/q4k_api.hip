@@ -28,7 +28,6 @@ constexpr int64_t kInt32Max = 2147483647;
 // i.e. three 4096-element spans of one vector.
 constexpr int64_t kSingleStageBytes = 48 * 1024;
 constexpr int64_t kSpanBytes = (int64_t)q4k::kSpan * 4;          // 16 KiB per vector
-constexpr int64_t kSpanSumBytes = 64 * 8;                        // per vector
 constexpr int kMaxDevices = 64;
 
 std::atomic<int> g_lds_max[kMaxDevices];  // 0 = not queried yet
@@ -93,8 +92,13 @@ int make_plan_lines(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t
     if (m > q4k::kMaxM && kernel < 5) {
         return Q4K_ERR_UNSUPPORTED;    // 9-16 vectors: the sub-block kernels only
     }
+    if (kernel == 4 && m > 2) {
+        return Q4K_ERR_UNSUPPORTED;    // one MFMA group per vector: one or two vectors
+    }
     const int nslabs = (S + 7) / 8;
-    const int nw = (o && o->waves_per_block) ? o->waves_per_block : 8;
+    // kernel 6 with more than eight vectors: four waves (see jit_waves)
+    const int nw_multi = kernel == 6 ? q4k::jit_waves((int)m) : 8;
+    const int nw = (o && o->waves_per_block) ? o->waves_per_block : (m > 1 || kernel >= 5 ? nw_multi : 8);
     if (nw != 4 && nw != 8 && nw != 16) {
         return Q4K_ERR_UNSUPPORTED;
     }
@@ -105,11 +109,13 @@ int make_plan_lines(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t
         return Q4K_ERR_UNSUPPORTED;
     }
     const int ring = (o && o->ring_depth) ? o->ring_depth : 3;
-    if (nw == 16 && ring == 9) {
-        return Q4K_ERR_UNSUPPORTED;    // 1024-lane workgroups cap a lane at 128 VGPRs
+    if ((m > 1 || kernel >= 5) && (nw != nw_multi || ring != 3)) {
+        return Q4K_ERR_UNSUPPORTED;    // several vectors: eight waves (kernel 6 with more
+                                       // than eight: four), three lines in flight
     }
-    if ((m > 1 || kernel >= 5) && (nw != 8 || ring != 3)) {
-        return Q4K_ERR_UNSUPPORTED;    // several vectors: eight waves, three lines in flight
+    if (nw == 16) {
+        return Q4K_ERR_UNSUPPORTED;    // 1024-lane workgroups cap a lane at 128 VGPRs,
+                                       // below what the exact x terms need
     }
     if (kernel == 3 && (m != 1 || S * 16 > 4 * 64 * nw || (S % 8 != 0 && ring != 3))) {
         return Q4K_ERR_UNSUPPORTED;    // one vector; x in at most four groups per lane;
@@ -141,7 +147,7 @@ int make_plan_lines(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t
         // wave streams; whole rows too when the per-slab row sums do not fit
         // the LDS (choices measured on MI355X: with fewer tiles than waves,
         // whole rows leave waves idle, 0.3-0.8 us on 16384-28672-row shapes)
-        const bool fits = lds_x + (size_t)nslabs * rpb * 4 * m <= lds_max;
+        const bool fits = lds_x + (size_t)nslabs * rpb * 8 * m <= lds_max;
         spt = (rpb / 16 >= nw || !fits) ? nslabs : 1;
     }
     const int64_t ncg = nslabs / spt;
@@ -149,7 +155,8 @@ int make_plan_lines(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t
         return Q4K_ERR_SHAPE;
     }
     const int64_t grid = (n + rpb - 1) / rpb;
-    const size_t lds = lds_x + (ncg > 1 ? (size_t)ncg * rpb * 4 * m : 0);
+    // row sums of the slab groups: f64
+    const size_t lds = lds_x + (ncg > 1 ? (size_t)ncg * rpb * 8 * m : 0);
 
     p->n = (int)n;
     p->k = (int)k;
@@ -260,9 +267,10 @@ int make_plan(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t lds_m
     if (o && o->cols_per_task) {
         return Q4K_ERR_UNSUPPORTED;   // line-streamed kernels only
     }
-    int nw = (o && o->waves_per_block) ? o->waves_per_block
-                                       : (kernel == 2 ? (nspans > 8 ? 16 : 8) : 8);
-    if (nw != 4 && nw != 8 && !(nw == 16 && kernel == 2)) {
+    // four or eight waves: the f64 x of the streaming kernel (128 VGPRs a
+    // lane) leaves no room in 1024-lane workgroups
+    int nw = (o && o->waves_per_block) ? o->waves_per_block : 8;
+    if (nw != 4 && nw != 8) {
         return Q4K_ERR_UNSUPPORTED;
     }
     // streaming kernel: about 2048 wave tasks (8 per CU of a 256-CU part),
@@ -288,12 +296,9 @@ int make_plan(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t lds_m
         auto_rpt = best;
     }
     const int64_t rows_per_task = (o && o->rows_per_task) ? o->rows_per_task : auto_rpt;
-    const int ring_cap = nw == 16 ? 2 : 3;
-    const int ring_depth = (o && o->ring_depth) ? o->ring_depth
-                                                : (rows_per_task >= 8 ? ring_cap : 1);
-    // 16-wave workgroups cap a lane at 128 VGPRs: at most 2 rows in flight there
+    const int ring_depth = (o && o->ring_depth) ? o->ring_depth : (rows_per_task >= 8 ? 3 : 1);
     if (kernel == 2 && (ring_depth < 1 || ring_depth > 4 || rows_per_task < 1 ||
-                        rows_per_task > kInt32Max || (nw == 16 && ring_depth > 2))) {
+                        rows_per_task > kInt32Max)) {
         return Q4K_ERR_UNSUPPORTED;
     }
     int R = (o && o->rows_per_wave) ? o->rows_per_wave : 2;
@@ -333,8 +338,8 @@ int make_plan(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t lds_m
     if (rpb > kInt32Max) {
         rpb = kInt32Max;
     }
-    const size_t lds_x = (size_t)m * spc * (kSpanBytes + kSpanSumBytes);
-    const size_t lds_row = kernel == 2 ? 0 : nchunks > 1 ? (size_t)m * 64 * 4 : 0;   // parked lane partials
+    const size_t lds_x = (size_t)m * spc * kSpanBytes;
+    const size_t lds_row = kernel == 2 ? 0 : nchunks > 1 ? (size_t)m * 64 * 8 : 0;   // parked lane partials (f64)
     if (lds_row && !(o && o->rows_per_block > 0) && lds_x + (size_t)rpb * lds_row > lds_max) {
         // automatic row blocks shrink to whole row groups that fit the LDS;
         // an automatic row count per wave, then wave count, shrinks first
@@ -357,8 +362,8 @@ int make_plan(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t lds_m
     }
     size_t lds;
     if (kernel == 2) {
-        // x chunk (no LDS sums: each wave sums its own x) + per-span row sums
-        lds = (size_t)spc * kSpanBytes + (nspans > 1 ? (size_t)nspans * rpb * 4 : 0);
+        // x chunk + per-span row sums (f64)
+        lds = (size_t)spc * kSpanBytes + (nspans > 1 ? (size_t)nspans * rpb * 8 : 0);
     } else {
         // partial sums are parked per row group, so round the rows up to whole groups
         lds = lds_x + (size_t)((rpb + R - 1) / R) * R * lds_row;

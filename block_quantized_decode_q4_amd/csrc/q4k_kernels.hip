@@ -14,24 +14,21 @@
 //    nibbles).  One wave pass covers 16 superblocks = 4096 elements (a
 //    "span").  Per superblock and row each lane issues three dwordx4 loads:
 //    the 16-byte header (d, dmin, scales) and its 32 quant bytes.
-//  * Nibble decode without conversions.  A 4-bit code placed in the low
+//  * Exact weights, exact products.  A 4-bit code placed in the low
 //    mantissa bits of an fp16 is the subnormal q*2^-24 (or q*2^-20 for a
 //    high nibble masked in place), exactly.  One AND turns a dword of
-//    codes into two such fp16 values, and v_fma_mix_f32 multiplies an fp16
-//    half of a register by an f32 x and accumulates in f32.  Eight weights
-//    cost 5 integer ops + 8 fma_mix.  The 2^-24 is folded into d, and the
-//    high-nibble 16 into x (x of high-nibble elements is staged as x/16, an
-//    exact power-of-two scaling).
-//  * Scales factored out.  Per lane and superblock:
-//      acc += d*2^24 * (sc_lo*A_lo + sc_hi*A_hi) - dmin*(m_lo*X_lo + m_hi*X_hi)
-//    with A = sum q*x over the lane's 32 elements of each sub-block and X =
-//    sum x over the same elements.  X depends only on x, so the x stager
-//    computes it once per workgroup: the min term costs nothing per weight.
+//    codes into two such fp16 values, and one v_fma_mix_f32 gives the
+//    weight fl32(d*sc*q - dmin*m) rounded once, as the format defines it
+//    (d*sc*2^24, or 2^20, and dmin*m are exact f32 factors per sub-block).
+//    Each weight times its x is exact in f64 and added in f64, so the only
+//    error before the final rounding of y to f32 is f64 rounding, for any
+//    finite x and weights (no f32 range limit on the products), and inf and
+//    NaN propagate as in IEEE arithmetic.
 //  * x stager (LDS).  A workgroup stages x (or a K-chunk of it) into LDS in
 //    lane order -- [vector][span][v = 0..15][lane] float4 -- so every
 //    ds_read_b128 of a wave reads 1 KiB of consecutive LDS (no bank
-//    conflicts), plus X per lane.  With one span and one vector, x is then
-//    held in 64 VGPRs per lane for the whole row loop.
+//    conflicts).  With one span and one vector, x is then held in 64 VGPRs
+//    per lane for the whole row loop.
 //  * K-chunked path.  When x does not fit the single-stage LDS budget, it is
 //    staged spans_per_chunk spans at a time; each lane's partial sums are
 //    parked in LDS between chunks, so the accumulation order -- and the
@@ -39,8 +36,9 @@
 //  * Multi-output scheduling.  A workgroup owns rows_per_block consecutive
 //    rows; its waves take groups of R rows round-robin and decode R rows per
 //    pass against one read of x, and the row loop streams each row once.
-//  * Per-row reduction: 64 lane partials -> one value with a butterfly of
-//    cross-lane adds; y is written once per row (overwrite).
+//  * Per-row reduction: 64 f64 lane partials -> one value with a butterfly
+//    of cross-lane adds, rounded once to f32; y is written once per row
+//    (overwrite).
 //  * m-batched (m <= 8): each decoded code feeds m accumulators.
 
 #include <hip/hip_runtime.h>
@@ -52,14 +50,14 @@
 namespace q4k {
 
 // ------------------------------------------------------------ x stager
-// Stage spans [span0, span0 + nsp) of every vector into LDS in lane order
-// and compute the per-lane sums X.  Slot ((b*nsp + sp)*16 + v)*64 + lane
-// holds, for superblock sb = (span0+sp)*16 + lane/4, chunk c = lane%4,
-// u = v/2, h = v%2: x[b][sb*256 + 64c + 32h + 4u + {0,2,1,3}] (times 1/16
-// when h = 1).  Superblocks past the row end stage zeros.
+// Stage spans [span0, span0 + nsp) of every vector into LDS in lane order.
+// Slot ((b*nsp + sp)*16 + v)*64 + lane holds, for superblock sb =
+// (span0+sp)*16 + lane/4, chunk c = lane%4, u = v/2, h = v%2:
+// x[b][sb*256 + 64c + 32h + 4u + {0,2,1,3}].  Superblocks past the row end
+// stage zeros.
 template <int M>
 __device__ __forceinline__ void stage_x(const float* __restrict__ x, int k, int S, int span0,
-                                        int nsp, float4* xs, float2* sums, int tid, int nthreads)
+                                        int nsp, float4* xs, int tid, int nthreads)
 {
     const int per_vec = nsp * 1024;
     const int total = M * per_vec;
@@ -86,25 +84,9 @@ __device__ __forceinline__ void stage_x(const float* __restrict__ x, int k, int 
         for (int i = 0; i < 4; ++i) {
             const int slot = base + i * nthreads;
             if (slot < total) {
-                const float sc = (((slot - (slot / per_vec) * per_vec) >> 6) & 1) ? 0.0625f : 1.0f;
-                xs[slot] = make_float4(g[i].x * sc, g[i].z * sc, g[i].y * sc, g[i].w * sc);
+                xs[slot] = make_float4(g[i].x, g[i].z, g[i].y, g[i].w);
             }
         }
-    }
-    __syncthreads();
-    for (int t = tid; t < M * nsp * 64; t += nthreads) {
-        const int bsp = t >> 6;
-        const int ln = t & 63;
-        const float4* base = xs + bsp * 1024 + ln;
-        float lo = 0.f, hi = 0.f;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const float4 a = base[(2 * u) * 64];
-            const float4 q = base[(2 * u + 1) * 64];
-            lo += (a.x + a.y) + (a.z + a.w);
-            hi += (q.x + q.y) + (q.z + q.w);
-        }
-        sums[t] = make_float2(lo, hi * 16.0f);   // undo the exact 1/16 scaling
     }
     __syncthreads();
 }
@@ -126,8 +108,9 @@ gemv_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x, float* _
     const int chunk_spans = spans_per_chunk < nspans ? spans_per_chunk : nspans;
     const int nchunks = (nspans + chunk_spans - 1) / chunk_spans;
     float4* xs = reinterpret_cast<float4*>(smem);
-    float2* sums = reinterpret_cast<float2*>(xs + M * chunk_spans * 1024);
-    float* partial = reinterpret_cast<float*>(sums + M * chunk_spans * 64);
+    double* partial = reinterpret_cast<double*>(xs + M * chunk_spans * 1024);
+    const uint32_t shift = (uint32_t)(c & 1) * 16u;
+    const uint32_t sel = c < 2 ? 0xFFFFFFFFu : 0u;
 
     const int row0 = blockIdx.x * rows_per_block;
     const int rows_here = min(rows_per_block, n - row0);
@@ -140,25 +123,23 @@ gemv_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x, float* _
         if (ch > 0) {
             __syncthreads();            // every wave is done with the previous chunk
         }
-        stage_x<M>(x, k, S, span0, nsp, xs, sums, tid, NW * 64);
+        stage_x<M>(x, k, S, span0, nsp, xs, tid, NW * 64);
 
         float4 xr[XREG ? 16 : 1];
-        float2 Xr = make_float2(0.f, 0.f);
         if constexpr (XREG) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 xr[v] = xs[v * 64 + lane];
             }
-            Xr = sums[lane];
         }
 
         for (int g = wave; g < ngroups; g += NW) {
-            float acc[R][M];
+            double acc[R][M];
 #pragma unroll
             for (int i = 0; i < R; ++i) {
 #pragma unroll
                 for (int b = 0; b < M; ++b) {
-                    acc[i][b] = ch == 0 ? 0.f : partial[((g * R + i) * M + b) * 64 + lane];
+                    acc[i][b] = ch == 0 ? 0.0 : partial[((g * R + i) * M + b) * 64 + lane];
                 }
             }
             for (int sp = 0; sp < nsp; ++sp) {
@@ -179,13 +160,19 @@ gemv_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x, float* _
                         qb[i] = make_uint4(0u, 0u, 0u, 0u);
                     }
                 }
-                float alo[R][M], ahi[R][M];
+                ChunkScales cs[R];
+#pragma unroll
+                for (int i = 0; i < R; ++i) {
+                    cs[i] = decode_header(hd[i], shift, sel);
+                }
+                // low and high sub-block sums apart: two chains per row and vector
+                double alo[R][M], ahi[R][M];
 #pragma unroll
                 for (int i = 0; i < R; ++i) {
 #pragma unroll
                     for (int b = 0; b < M; ++b) {
-                        alo[i][b] = 0.f;
-                        ahi[i][b] = 0.f;
+                        alo[i][b] = acc[i][b];
+                        ahi[i][b] = 0.0;
                     }
                 }
 #pragma unroll
@@ -209,30 +196,16 @@ gemv_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x, float* _
                         const uint32_t D = uu == 0 ? q4.x : uu == 1 ? q4.y : uu == 2 ? q4.z : q4.w;
 #pragma unroll
                         for (int b = 0; b < M; ++b) {
-                            dot8(D, xl[b], xh[b], alo[i][b], ahi[i][b]);
+                            dot8_exact(D, xl[b], xh[b], cs[i].sl, cs[i].sh, cs[i].ml, cs[i].mh,
+                                       alo[i][b], ahi[i][b]);
                         }
-                    }
-                }
-                float2 X[M];
-                if constexpr (XREG) {
-                    X[0] = Xr;
-                } else {
-#pragma unroll
-                    for (int b = 0; b < M; ++b) {
-                        X[b] = sums[(b * nsp + sp) * 64 + lane];
                     }
                 }
 #pragma unroll
                 for (int i = 0; i < R; ++i) {
-                    const ChunkScales s = decode_header(hd[i], c);
 #pragma unroll
                     for (int b = 0; b < M; ++b) {
-                        float t1 = s.sc_lo * alo[i][b];
-                        t1 = __builtin_fmaf(s.sc_hi, ahi[i][b], t1);
-                        float t2 = s.m_lo * X[b].x;
-                        t2 = __builtin_fmaf(s.m_hi, X[b].y, t2);
-                        acc[i][b] = __builtin_fmaf(s.d24, t1, acc[i][b]);
-                        acc[i][b] = __builtin_fmaf(-s.dmin, t2, acc[i][b]);
+                        acc[i][b] = alo[i][b] + ahi[i][b];
                     }
                 }
             }
@@ -241,10 +214,10 @@ gemv_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x, float* _
                 for (int i = 0; i < R; ++i) {
 #pragma unroll
                     for (int b = 0; b < M; ++b) {
-                        const float v = wave_sum(acc[i][b]);
+                        const double v = wave_sum(acc[i][b]);
                         const int rl = g * R + i;
                         if (lane == 0 && rl < rows_here) {
-                            y[(size_t)b * n + row0 + rl] = v;
+                            y[(size_t)b * n + row0 + rl] = (float)v;
                         }
                     }
                 }
@@ -289,8 +262,7 @@ __device__ __forceinline__ void stage_x_batched(const float* __restrict__ x, int
         for (int i = 0; i < 4; ++i) {
             const int slot = base + i * NT;
             if (slot < total) {
-                const float sc = ((slot >> 6) & 1) ? 0.0625f : 1.0f;
-                xs[slot] = make_float4(g[i].x * sc, g[i].z * sc, g[i].y * sc, g[i].w * sc);
+                xs[slot] = make_float4(g[i].x, g[i].z, g[i].y, g[i].w);
             }
         }
     }
@@ -333,22 +305,27 @@ __device__ __forceinline__ RowData load_row(const uint8_t* p, int c)
     return r;
 }
 
-// Sum over the 64 lanes with DPP (quad, half-row, row, row broadcasts);
-// the total lands in lane 63.
-__device__ __forceinline__ float dpp_sum_to_lane63(float v)
+// v of another lane chosen by DPP (CTRL, row mask RM), for an f64 value:
+// the two halves move alike; lanes outside the rows get 0.0
+template <int CTRL, int RM>
+__device__ __forceinline__ double dpp_f64(double v)
 {
-    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-             0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));    // quad_perm 1,0,3,2
-    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-             0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));    // quad_perm 2,3,0,1
-    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-             0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));   // row_half_mirror
-    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-             0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));   // row_mirror
-    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-             0, __builtin_bit_cast(int, v), 0x142, 0xA, 0xF, false));   // row_bcast:15
-    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-             0, __builtin_bit_cast(int, v), 0x143, 0xC, 0xF, false));   // row_bcast:31
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, RM, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, RM, 0xF, false);
+    return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+// Sum over the 64 lanes with DPP (quad, half-row, row, row broadcasts), in
+// f64; the total lands in lane 63.
+__device__ __forceinline__ double dpp_sum_to_lane63(double v)
+{
+    v += dpp_f64<0xB1, 0xF>(v);     // quad_perm 1,0,3,2
+    v += dpp_f64<0x4E, 0xF>(v);     // quad_perm 2,3,0,1
+    v += dpp_f64<0x141, 0xF>(v);    // row_half_mirror
+    v += dpp_f64<0x140, 0xF>(v);    // row_mirror
+    v += dpp_f64<0x142, 0xA>(v);    // row_bcast:15
+    v += dpp_f64<0x143, 0xC>(v);    // row_bcast:31
     return v;
 }
 
@@ -358,34 +335,22 @@ struct LaneDecode {
     uint32_t sel;    // all ones for c < 2 (j < 4 form), zero otherwise
 };
 
-// One row's partial dot for this lane: 64 weights of chunk c.
-__device__ __forceinline__ float row_partial(const RowData& q, const float4* xr, float Xl, float Xh,
-                                             const LaneDecode& ld)
+// One row's partial dot for this lane: the 64 weights of chunk c, exact
+// weights times x exactly, in f64 (dot8_exact).
+__device__ __forceinline__ double row_partial(const RowData& q, const X4D* xr,
+                                              const LaneDecode& ld)
 {
-    float alo = 0.f, ahi = 0.f;
-    dot8(q.a.x, xr[0], xr[1], alo, ahi);
-    dot8(q.a.y, xr[2], xr[3], alo, ahi);
-    dot8(q.a.z, xr[4], xr[5], alo, ahi);
-    dot8(q.a.w, xr[6], xr[7], alo, ahi);
-    dot8(q.b.x, xr[8], xr[9], alo, ahi);
-    dot8(q.b.y, xr[10], xr[11], alo, ahi);
-    dot8(q.b.z, xr[12], xr[13], alo, ahi);
-    dot8(q.b.w, xr[14], xr[15], alo, ahi);
-    const half2_t dd = __builtin_bit_cast(half2_t, q.h.x);
-    const uint32_t y = q.h.y >> ld.sh;
-    const uint32_t z = q.h.z >> ld.sh;
-    const uint32_t wv = q.h.w >> ld.sh;
-    const uint32_t sc_b = (wv & 0x0F0Fu) | ((y >> 2) & 0x3030u);
-    const uint32_t m_b = ((wv >> 4) & 0x0F0Fu) | ((z >> 2) & 0x3030u);
-    // select without a branch: (a & sel) | (b & ~sel)
-    const uint32_t sc = ((y & 0x3F3Fu) & ld.sel) | (sc_b & ~ld.sel);
-    const uint32_t mm = ((z & 0x3F3Fu) & ld.sel) | (m_b & ~ld.sel);
-    float t1 = (float)(sc & 0xFFu) * alo;
-    t1 = __builtin_fmaf((float)((sc >> 8) & 0xFFu), ahi, t1);
-    float t2 = (float)(mm & 0xFFu) * Xl;
-    t2 = __builtin_fmaf((float)((mm >> 8) & 0xFFu), Xh, t2);
-    float acc = ((float)dd.x * 16777216.0f) * t1;
-    return __builtin_fmaf(-(float)dd.y, t2, acc);
+    const ChunkScales s = decode_header(q.h, ld.sh, ld.sel);
+    double alo = 0.0, ahi = 0.0;
+    dot8_exact(q.a.x, xr[0], xr[1], s.sl, s.sh, s.ml, s.mh, alo, ahi);
+    dot8_exact(q.a.y, xr[2], xr[3], s.sl, s.sh, s.ml, s.mh, alo, ahi);
+    dot8_exact(q.a.z, xr[4], xr[5], s.sl, s.sh, s.ml, s.mh, alo, ahi);
+    dot8_exact(q.a.w, xr[6], xr[7], s.sl, s.sh, s.ml, s.mh, alo, ahi);
+    dot8_exact(q.b.x, xr[8], xr[9], s.sl, s.sh, s.ml, s.mh, alo, ahi);
+    dot8_exact(q.b.y, xr[10], xr[11], s.sl, s.sh, s.ml, s.mh, alo, ahi);
+    dot8_exact(q.b.z, xr[12], xr[13], s.sl, s.sh, s.ml, s.mh, alo, ahi);
+    dot8_exact(q.b.w, xr[14], xr[15], s.sl, s.sh, s.ml, s.mh, alo, ahi);
+    return alo + ahi;
 }
 
 template <int NW, int P>
@@ -413,7 +378,7 @@ gemv_stream_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
     const size_t row_bytes = (size_t)S * 144;
 
     float4* xs = reinterpret_cast<float4*>(smem);
-    float* ypart = reinterpret_cast<float*>(xs + chunk_spans * 1024);
+    double* ypart = reinterpret_cast<double*>(xs + chunk_spans * 1024);
 
     for (int ch = 0; ch < nchunks; ++ch) {
         const int span0 = ch * chunk_spans;
@@ -453,24 +418,18 @@ gemv_stream_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
                     buf[j] = load_row(base + (size_t)min(j, T - 1) * row_bytes, c);
                 }
             }
-            float4 xr[16];
+            // the lane's 64 x of the span, in f64 once per task (128 VGPRs)
+            X4D xr[16];
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                xr[v] = xs[(sp * 16 + v) * 64 + lane];
+                const float4 t4 = xs[(sp * 16 + v) * 64 + lane];
+                xr[v] = X4D{(double)t4.x, (double)t4.y, (double)t4.z, (double)t4.w};
             }
-            float Xl = 0.f, Xh = 0.f;
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                Xl += (xr[2 * u].x + xr[2 * u].y) + (xr[2 * u].z + xr[2 * u].w);
-                Xh += (xr[2 * u + 1].x + xr[2 * u + 1].y) + (xr[2 * u + 1].z + xr[2 * u + 1].w);
-            }
-            Xh *= 16.0f;                    // exact: undoes the 1/16 of the stage
-
             // y (global) or the per-span row sums (LDS): two typed pointers, so
             // that neither store becomes a flat access, which would make the
             // compiler drain the prefetched loads at every row
             float* yout = y + row0 + rb;
-            float* pout = ypart + span * rows_per_block + rb;
+            double* pout = ypart + span * rows_per_block + rb;
             const bool direct = nspans == 1;
             int t = 0;
             for (; t + P <= T; t += P) {
@@ -478,10 +437,10 @@ gemv_stream_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
                 for (int j = 0; j < P; ++j) {
                     const RowData q = buf[j];
                     buf[j] = load_row(base + (size_t)min(t + j + P, T - 1) * row_bytes, c);
-                    const float v = dpp_sum_to_lane63(row_partial(q, xr, Xl, Xh, ld));
+                    const double v = dpp_sum_to_lane63(row_partial(q, xr, ld));
                     if (lane == 63) {
                         if (direct) {
-                            yout[t + j] = v;
+                            yout[t + j] = (float)v;
                         } else {
                             pout[t + j] = v;
                         }
@@ -491,10 +450,10 @@ gemv_stream_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
 #pragma unroll
             for (int j = 0; j < P; ++j) {
                 if (t + j < T) {
-                    const float v = dpp_sum_to_lane63(row_partial(buf[j], xr, Xl, Xh, ld));
+                    const double v = dpp_sum_to_lane63(row_partial(buf[j], xr, ld));
                     if (lane == 63) {
                         if (direct) {
-                            yout[t + j] = v;
+                            yout[t + j] = (float)v;
                         } else {
                             pout[t + j] = v;
                         }
@@ -506,11 +465,11 @@ gemv_stream_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
     if (nspans > 1) {
         __syncthreads();
         for (int r = tid; r < rows_here; r += NW * 64) {
-            float acc = 0.f;
+            double acc = 0.0;
             for (int sp = 0; sp < nspans; ++sp) {
                 acc += ypart[sp * rows_per_block + r];
             }
-            y[row0 + r] = acc;
+            y[row0 + r] = (float)acc;
         }
     }
 }
@@ -657,14 +616,9 @@ static hipError_t launch_stream_nw(const GemvPlan& p, const uint8_t* w, const fl
                                    hipStream_t stream)
 {
     if (p.ring_depth == 1) return launch_stream<NW, 1>(p, w, x, y, stream);
-    if constexpr (NW == 16) {
-        // 1024-thread workgroups leave 128 VGPRs per lane: two rows in flight
-        return launch_stream<NW, 2>(p, w, x, y, stream);
-    } else {
-        if (p.ring_depth == 2) return launch_stream<NW, 2>(p, w, x, y, stream);
-        if (p.ring_depth == 3) return launch_stream<NW, 3>(p, w, x, y, stream);
-        return launch_stream<NW, 4>(p, w, x, y, stream);
-    }
+    if (p.ring_depth == 2) return launch_stream<NW, 2>(p, w, x, y, stream);
+    if (p.ring_depth == 3) return launch_stream<NW, 3>(p, w, x, y, stream);
+    return launch_stream<NW, 4>(p, w, x, y, stream);
 }
 
 hipError_t launch_gemv(const GemvPlan& p, const void* w, const float* x, float* y,
@@ -678,7 +632,6 @@ hipError_t launch_gemv(const GemvPlan& p, const void* w, const float* x, float* 
         return launch_gemv_mfma(p, w, x, y, stream);
     }
     if (p.kernel == 2) {
-        if (p.waves_per_block == 16) return launch_stream_nw<16>(p, wb, x, y, stream);
         if (p.waves_per_block == 8) return launch_stream_nw<8>(p, wb, x, y, stream);
         return launch_stream_nw<4>(p, wb, x, y, stream);
     }

@@ -21,6 +21,7 @@
 #include <stdint.h>
 
 #include <type_traits>
+#include <utility>
 
 namespace q4k {
 
@@ -31,6 +32,31 @@ template <typename Step>
 constexpr bool kLookAhead =
     std::is_invocable_v<Step&, int, int, int, unsigned char*, uint32_t, int, bool>;
 constexpr int kRingWave = 16 * kRingRow;
+
+// a step that takes (c, rr, b0, corr) with corr a std::integral_constant:
+// the stream calls it with true only for slabs whose slab_flag is set, so a
+// step keeps a rarely taken path out of the other slabs' code
+template <typename Step>
+constexpr bool kFlagged =
+    std::is_invocable_v<Step&, int, unsigned char*, uint32_t, std::true_type>;
+
+struct NoSlabFlag {
+    __device__ bool operator()(int) const { return false; }
+};
+
+// f(std::integral_constant<int, i>()) for i = 0 .. N-1, each call inlined:
+// a loop whose body must see its index as a constant, whatever its size
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>)
+{
+    (f(std::integral_constant<int, I>()), ...);
+}
+
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f)
+{
+    static_for_impl(f, std::make_integer_sequence<int, N>());
+}
 
 __device__ __forceinline__ uint4 load_line_nt(const uint8_t* p)
 {
@@ -57,12 +83,14 @@ __device__ __forceinline__ uint4 load_line_nt(const uint8_t* p)
 // Line l of every slab goes to ring slot l mod 2: the previous slab's last
 // line (slot 0) is dead once its last superblock has been read, and the
 // wave's LDS accesses complete in order.
-template <int NW, int P, typename IssueX, typename ConvertX, typename Step, typename TaskEnd>
+template <int NW, int P, typename IssueX, typename ConvertX, typename Step, typename TaskEnd,
+          typename SlabFlag = NoSlabFlag>
 __device__ __forceinline__ void line_stream(const uint8_t* __restrict__ w,
                                             const float* __restrict__ x, int n, int S,
                                             int rows_per_block, int slabs_per_task,
                                             unsigned char* ring, IssueX issue_x,
-                                            ConvertX convert_x, Step step, TaskEnd task_end)
+                                            ConvertX convert_x, Step step, TaskEnd task_end,
+                                            SlabFlag slab_flag = SlabFlag())
 {
     static_assert(P == 3 || P == 9, "line slots must divide the nine lines of a slab");
     const int lane = threadIdx.x & 63;
@@ -84,7 +112,7 @@ __device__ __forceinline__ void line_stream(const uint8_t* __restrict__ w,
     // slab sig of this wave -> (tile, absolute slab); clamped into the
     // wave's slabs (and into the block's tasks for a wave without any), so
     // every prefetch address is valid and no load sits behind a branch
-    auto slab_of = [&](int sig, int& tile, int& slab) {
+    auto slab_of = [&](int sig, int& tile, int& slab) __attribute__((always_inline)) {
         sig = max(0, min(sig, my_slabs - 1));
         const int task = min(wave + (sig / slabs_per_task) * NW, ntasks - 1);
         tile = task / ncg;
@@ -107,7 +135,7 @@ __device__ __forceinline__ void line_stream(const uint8_t* __restrict__ w,
         uint64_t b[2];
         uint32_t stride;
     };
-    auto slab_base = [&](int sig) {
+    auto slab_base = [&](int sig) __attribute__((always_inline)) {
         int tile, slab;
         slab_of(sig, tile, slab);
         const bool past = sig >= my_slabs;                          // wave-uniform
@@ -123,7 +151,7 @@ __device__ __forceinline__ void line_stream(const uint8_t* __restrict__ w,
         sb.stride = past ? 0u : 128u;
         return sb;
     };
-    auto line_ptrs = [&](const SlabBase& sb, int l, const uint8_t** p) {
+    auto line_ptrs = [&](const SlabBase& sb, int l, const uint8_t** p) __attribute__((always_inline)) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             p[h] = w + sb.b[h] + (uint64_t)(sb.stride * (uint32_t)l);
@@ -172,33 +200,54 @@ __device__ __forceinline__ void line_stream(const uint8_t* __restrict__ w,
         slab_of(sig + 1, tile_n, slab_n);      // clamped: the last slab again at the end
         const SlabBase cur = slab_base(sig);
         const SlabBase nxt = slab_base(sig + 1);
-#pragma unroll
-        for (int cp = 0; cp < 8; ++cp) {
-            // lines written before superblock cp: 0 and 1 first, then cp + 1
-#pragma unroll
-            for (int l = (cp == 0 ? 0 : cp + 1); l <= cp + 1; ++l) {
-                const int slot = l % P;
-                const uint32_t lpos = (uint32_t)(l & 1) * 128u + 16u * (uint32_t)lunit;
-                *reinterpret_cast<uint4*>(ring + lrow * kRingRow + lpos) = lines[slot][0];
-                *reinterpret_cast<uint4*>(ring + (8 + lrow) * kRingRow + lpos) = lines[slot][1];
-                // memory operations stay in order here (the refill after the
-                // write of its slot); arithmetic may move across
-                __builtin_amdgcn_sched_barrier(0x000F);
-                const int ln = l + P;              // refill: P lines ahead
-                const uint8_t* p[2];
-                line_ptrs(ln >= 9 ? nxt : cur, ln >= 9 ? ln - 9 : ln, p);
-                lines[slot][0] = load_line_nt(p[0]);
-                lines[slot][1] = load_line_nt(p[1]);
-            }
-            // superblock c = 8 slab + cp, in the ring of tile row j (and, for
-            // a step that looks ahead, the end of this slab's columns and the
-            // first column of the next slab)
-            if constexpr (kLookAhead<Step>) {
-                step(8 * slab + cp, 8 * slab + 8, 8 * slab_n, ring + j * kRingRow,
-                     (uint32_t)(144 * cp), cp, true);
+        // line l (compile-time) of the slab into the ring, and its slot
+        // refilled with line l + P
+        auto put = [&](auto lc) __attribute__((always_inline)) {
+            constexpr int l = decltype(lc)::value;
+            constexpr int slot = l % P;
+            const uint32_t lpos = (uint32_t)(l & 1) * 128u + 16u * (uint32_t)lunit;
+            *reinterpret_cast<uint4*>(ring + lrow * kRingRow + lpos) = lines[slot][0];
+            *reinterpret_cast<uint4*>(ring + (8 + lrow) * kRingRow + lpos) = lines[slot][1];
+            // memory operations stay in order here (the refill after the
+            // write of its slot); arithmetic may move across
+            __builtin_amdgcn_sched_barrier(0x000F);
+            constexpr int ln = l + P;                  // refill: P lines ahead
+            const uint8_t* p[2];
+            line_ptrs(ln >= 9 ? nxt : cur, ln >= 9 ? ln - 9 : ln, p);
+            lines[slot][0] = load_line_nt(p[0]);
+            lines[slot][1] = load_line_nt(p[1]);
+        };
+        // superblock cp (compile-time) of the slab: lines 0 and 1 before
+        // the first, then line cp + 1; then the step on the ring of tile row
+        // j (and, for a step that looks ahead, the end of this slab's columns
+        // and the first column of the next slab).  Compile-time positions
+        // keep every index into the line registers constant, however large
+        // the step's body.
+        auto slab_body = [&](auto corr) __attribute__((always_inline)) {
+            static_for<8>([&](auto cpc) __attribute__((always_inline)) {
+                constexpr int cp = decltype(cpc)::value;
+                if constexpr (cp == 0) {
+                    put(std::integral_constant<int, 0>());
+                }
+                put(std::integral_constant<int, cp + 1>());
+                if constexpr (kLookAhead<Step>) {
+                    step(8 * slab + cp, 8 * slab + 8, 8 * slab_n, ring + j * kRingRow,
+                         (uint32_t)(144 * cp), cp, true);
+                } else if constexpr (kFlagged<Step>) {
+                    step(8 * slab + cp, ring + j * kRingRow, (uint32_t)(144 * cp), corr);
+                } else {
+                    step(8 * slab + cp, ring + j * kRingRow, (uint32_t)(144 * cp));
+                }
+            });
+        };
+        if constexpr (kFlagged<Step>) {
+            if (slab_flag(slab)) {
+                slab_body(std::true_type());
             } else {
-                step(8 * slab + cp, ring + j * kRingRow, (uint32_t)(144 * cp));
+                slab_body(std::false_type());
             }
+        } else {
+            slab_body(std::false_type());
         }
         if (sig % slabs_per_task == slabs_per_task - 1) {
             task_end(wave + (sig / slabs_per_task) * NW);
@@ -226,12 +275,14 @@ constexpr int kRing4Wave = 16 * kRing4Row;
 // b0 = 144 t, the byte offset within the task's ring window of 512 bytes
 // before the lane adds its row's start offset, and runs only for the task's
 // superblocks (the last slab of a row may hold fewer than eight).
-template <int NW, typename IssueX, typename ConvertX, typename Step, typename TaskEnd>
+template <int NW, typename IssueX, typename ConvertX, typename Step, typename TaskEnd,
+          typename SlabFlag = NoSlabFlag>
 __device__ __forceinline__ void line_stream_any(const uint8_t* __restrict__ w,
                                                 const float* __restrict__ x, int n, int S,
                                                 int rows_per_block, int slabs_per_task,
                                                 unsigned char* ring, IssueX issue_x,
-                                                ConvertX convert_x, Step step, TaskEnd task_end)
+                                                ConvertX convert_x, Step step, TaskEnd task_end,
+                                                SlabFlag slab_flag = SlabFlag())
 {
     constexpr int P = 3;
     const int lane = threadIdx.x & 63;
@@ -256,7 +307,7 @@ __device__ __forceinline__ void line_stream_any(const uint8_t* __restrict__ w,
 
     // task q of this wave (clamped into its tasks) -> (tile, column group,
     // superblocks)
-    auto task_of = [&](int q, int& tile, int& cg, int& T) {
+    auto task_of = [&](int q, int& tile, int& cg, int& T) __attribute__((always_inline)) {
         const int qc = max(0, min(q, my_tasks - 1));
         const int task = min(wave + qc * NW, ntasks - 1);
         tile = task / ncg;
@@ -272,7 +323,7 @@ __device__ __forceinline__ void line_stream_any(const uint8_t* __restrict__ w,
         uint64_t b[2];
         int lim[2];
     };
-    auto task_base = [&](int q) {
+    auto task_base = [&](int q) __attribute__((always_inline)) {
         int tile, cg, T;
         task_of(q, tile, cg, T);
         const bool past = q >= my_tasks;                             // wave-uniform
@@ -288,7 +339,7 @@ __device__ __forceinline__ void line_stream_any(const uint8_t* __restrict__ w,
         }
         return tb;
     };
-    auto line_ptrs = [&](const TaskBase& tb, int L, const uint8_t** p) {
+    auto line_ptrs = [&](const TaskBase& tb, int L, const uint8_t** p) __attribute__((always_inline)) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const uint64_t mask = 128 * L < tb.lim[h] ? 0ull : ~0ull;
@@ -299,7 +350,7 @@ __device__ __forceinline__ void line_stream_any(const uint8_t* __restrict__ w,
     // write line L = 9 s2 + X of the current task (bases cur, next task's
     // nxt) into the ring, refill its slot (X % 3) with the line three
     // indices on
-    auto put = [&](const TaskBase& cur, const TaskBase& nxt, int s2, auto Xc) {
+    auto put = [&](const TaskBase& cur, const TaskBase& nxt, int s2, auto Xc) __attribute__((always_inline)) {
         constexpr int X = decltype(Xc)::value;
         constexpr int slot = X % P;
         const int L = 9 * s2 + X;
@@ -341,36 +392,49 @@ __device__ __forceinline__ void line_stream_any(const uint8_t* __restrict__ w,
         const TaskBase cur = task_base(q);
         const TaskBase nxt = task_base(q + 1);
         // superblock cp of slab s2 of the task, if the row has it
-        auto stp = [&](int s2, int cp) {
+        auto stp = [&](int s2, int cp, auto corr) __attribute__((always_inline)) {
             const int c = c0 + 8 * s2 + cp;
             const uint32_t b0 = 1152u * (uint32_t)s2 + 144u * (uint32_t)cp;
             if constexpr (kLookAhead<Step>) {
                 step(c, c0 + 8 * slabs_per_task, cn, ring + j * kRing4Row, b0, cp, 8 * s2 + cp < T);
+            } else if constexpr (kFlagged<Step>) {
+                if (8 * s2 + cp < T) step(c, ring + j * kRing4Row, b0, corr);
             } else {
                 if (8 * s2 + cp < T) step(c, ring + j * kRing4Row, b0);
             }
         };
-        put(cur, nxt, 0, std::integral_constant<int, 0>());
-        for (int s2 = 0; s2 < slabs_per_task; ++s2) {
+        auto slab_body = [&](int s2, auto corr) __attribute__((always_inline)) {
             // lines 9 s2 + 1 .. 9 s2 + 9: two before superblock 1 of the slab,
             // one before each other
             put(cur, nxt, s2, std::integral_constant<int, 1>());
-            stp(s2, 0);
+            stp(s2, 0, corr);
             put(cur, nxt, s2, std::integral_constant<int, 2>());
             put(cur, nxt, s2, std::integral_constant<int, 3>());
-            stp(s2, 1);
+            stp(s2, 1, corr);
             put(cur, nxt, s2, std::integral_constant<int, 4>());
-            stp(s2, 2);
+            stp(s2, 2, corr);
             put(cur, nxt, s2, std::integral_constant<int, 5>());
-            stp(s2, 3);
+            stp(s2, 3, corr);
             put(cur, nxt, s2, std::integral_constant<int, 6>());
-            stp(s2, 4);
+            stp(s2, 4, corr);
             put(cur, nxt, s2, std::integral_constant<int, 7>());
-            stp(s2, 5);
+            stp(s2, 5, corr);
             put(cur, nxt, s2, std::integral_constant<int, 8>());
-            stp(s2, 6);
+            stp(s2, 6, corr);
             put(cur, nxt, s2, std::integral_constant<int, 9>());
-            stp(s2, 7);
+            stp(s2, 7, corr);
+        };
+        put(cur, nxt, 0, std::integral_constant<int, 0>());
+        for (int s2 = 0; s2 < slabs_per_task; ++s2) {
+            if constexpr (kFlagged<Step>) {
+                if (slab_flag(cg * slabs_per_task + s2)) {
+                    slab_body(s2, std::true_type());
+                } else {
+                    slab_body(s2, std::false_type());
+                }
+            } else {
+                slab_body(s2, std::false_type());
+            }
         }
         // the two surplus indices of the task
         put(cur, nxt, slabs_per_task, std::integral_constant<int, 1>());

@@ -24,12 +24,14 @@
 #include "q4k_device.h"
 #include "q4k_kernels.h"
 #include "q4k_lines.h"
+#include "q4k_xrep.h"
 
 namespace q4k {
 
 
 // ---------------------------------------------------------------------------
-// int8 matrix-core decode (v_mfma_i32_16x16x64_i8).
+// Line-streamed int8 matrix-core kernel, one MFMA group per vector
+// (v_mfma_i32_16x16x64_i8).
 //
 // Operands of one MFMA (16 x 16 x 64): lane l = 16 g + j holds
 //   A[i = j][k = 16g .. 16g+15] (16 bytes), B[k = 16g .. 16g+15][j], D[4g + r][j].
@@ -38,147 +40,33 @@ namespace q4k {
 //    row (32 code bytes: sub-block 2g in the low nibbles, 2g+1 in the high
 //    ones).  Low codes: byte & 0x0F (one AND per four codes).  High codes:
 //    (byte & 0xF0) ^ 0x80 = 16 q - 128 as a signed byte (one three-input
-//    bit operation per four codes); the -128 is undone with the sub-block's
-//    integer x sum.  Four MFMAs per superblock: bytes 0-15 and 16-31 of the
-//    chunk, low and high codes.
-//  * A = x as a 23-bit integer per element, xi = rint(x * 2^sigma_s) with one
-//    power of two per 32-element sub-block s (largest |x| in [2^21, 2^22)),
-//    split into three signed base-256 digits xi = l0 + 256 l1 + 65536 l2.
-//    Row i = 4g' + l of A holds digit l of sub-block 2g' (low MFMAs) or
-//    2g'+1 (high MFMAs) in k-group g', zero elsewhere, so D rows 4g..4g+2 of
-//    lane (g, j) are the three digit dot products of exactly the two
-//    sub-blocks whose scales lane (g, j) decodes.  The zero rows cost
-//    nothing: inactive lanes read a zero slot of the stage.
-//  * Per step and lane: T = D0 + 256 D1 + 65536 D2 (exact in int32 up to the
-//    last f32 rounding), then
-//      acc += d * (sc_lo * 2^-sigma_lo * T_lo
-//                  + sc_hi * (2^-sigma_hi / 16 * T_hi + 8 * X_hi))
-//             - dmin * (m_lo * X_lo + m_hi * X_hi)
-//    with X = 2^-sigma * XI the sum of the quantized x of a sub-block (XI
-//    its integer sum).
-//  * Quantizing x to 23 bits per sub-block bounds the error of a product by
-//    2^-22 of the sub-block's largest |x| times |w|.
+//    bit operation per four codes).  Four MFMAs per superblock and vector:
+//    bytes 0-15 and 16-31 of the chunk (mu = 0, 1: low codes; 2, 3: high).
+//  * A = x on the grid of q4k_xrep.h, four signed digits per element.  Row
+//    i = 4g' + l of A holds digit l of the 16 elements of chunk g' that
+//    operand mu covers, in k-group g', and zero elsewhere, so D rows
+//    4g .. 4g+3 of lane (g, j) are the four digit sums of exactly the
+//    sub-block whose scales lane (g, j) decodes.  Inactive lanes read a zero
+//    slot of the stage.
+//  * Per step, vector and lane: the same exact sums and f64 scaling as the
+//    vector-ALU kernel (q4k_dpp.hip), and the same exact terms for the
+//    column's uncertified elements (the lane holds chunk g of row j, as
+//    there).
+//
+// Staged x per (column, vector) pair (kK4Pair bytes): four operand blocks of
+// sixteen 16-byte digit slots (slot 4 g + l: digit l of chunk g's sixteen
+// elements) and a zero slot, eight {2^-s, XI} f64 pairs, the count of the
+// pair's uncertified elements and the first kCorr of them.
 // ---------------------------------------------------------------------------
 
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kI8MuBytes = 208;                 // 12 digit slots of 16 B + a zero slot
-constexpr int kI8ZeroSlot = 192;
-constexpr int kI8ColA = 4 * kI8MuBytes;         // four MFMA operands per column
-constexpr int kI8ColConst = 4 * 32;             // eight floats per lane group
-constexpr int kI8ColBytes = kI8ColA + kI8ColConst;
-
-// Convert four (column, vector) pairs at once, one per 16-lane group: lane
-// l takes elements 16 (l % 16) .. 16 (l % 16) + 15 of its pair, half of a
-// sub-block, so each lane writes three whole 16-byte digit slots and the
-// per-lane costs (largest |x|, scale, sums) are shared by 16 elements.
-// `col` is the LDS slot of the lane's pair: 12 digit slots of 16 bytes per
-// MFMA operand mu (digit l of the 16 elements of k-group g at slot 3 g + l,
-// a zero slot after them) and the constants {2^-s, 2^-s / 16, 8 X, X_lo,
-// X_hi} of each lane group's two sub-blocks.
-__device__ __forceinline__ void convert4_i8(const float4 (&v)[4], unsigned char* col, int lane)
-{
-    const int le = lane & 15;
-    const int s = le >> 1;                    // sub-block
-    const int half = le & 1;                  // its elements 0-15 or 16-31
-    const int g = s >> 1;
-    const int mu = 2 * (s & 1) + half;
-    float m = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        m = fmaxf(m, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
-    }
-    m = fmaxf(m, __builtin_bit_cast(float, dpp_i<0xB1>(__builtin_bit_cast(int, m))));  // lane l ^ 1
-    int sigma = 0;
-    if (m > 0.f) {
-        sigma = 22 - __builtin_amdgcn_frexp_expf(m);
-        sigma = sigma < -126 ? -126 : sigma > 126 ? 126 : sigma;
-    }
-    const float scale = __builtin_bit_cast(float, (uint32_t)(sigma + 127) << 23);
-    uint32_t usum = 0;
-    uint4 dig[3];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float vals[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-        uint32_t u[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            u[t] = __builtin_bit_cast(uint32_t, __builtin_fmaf(vals[t], scale, 12582912.0f)) -
-                   0x4ABF7F80u;
-            usum += u[t];
-        }
-        const uint32_t lo01 = __builtin_amdgcn_perm(u[1], u[0], 0x05010400u);
-        const uint32_t lo23 = __builtin_amdgcn_perm(u[3], u[2], 0x05010400u);
-        const uint32_t hi01 = __builtin_amdgcn_perm(u[1], u[0], 0x07030602u);
-        const uint32_t hi23 = __builtin_amdgcn_perm(u[3], u[2], 0x07030602u);
-        const uint32_t d0 = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u) ^ 0x80808080u;
-        const uint32_t d1 = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u) ^ 0x80808080u;
-        const uint32_t d2 = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u) ^ 0x80808080u;
-        (&dig[0].x)[i] = d0;
-        (&dig[1].x)[i] = d1;
-        (&dig[2].x)[i] = d2;
-    }
-    unsigned char* slot = col + mu * kI8MuBytes + g * 48;
-    *reinterpret_cast<uint4*>(slot) = dig[0];
-    *reinterpret_cast<uint4*>(slot + 16) = dig[1];
-    *reinterpret_cast<uint4*>(slot + 32) = dig[2];
-    if (le < 4) {
-        *reinterpret_cast<uint4*>(col + le * kI8MuBytes + kI8ZeroSlot) = make_uint4(0, 0, 0, 0);
-    }
-    const uint32_t us2 = usum + (uint32_t)dpp_i<0xB1>((int)usum);
-    const int XI = (int)us2 - 32 * 0x808080;
-    if (half == 0) {
-        float* c = reinterpret_cast<float*>(col + kI8ColA + g * 32);
-        const float inv = __builtin_bit_cast(float, (uint32_t)(127 - sigma) << 23);
-        const float xq = inv * (float)XI;
-        if ((s & 1) == 0) {
-            c[0] = inv;
-            c[3] = xq;
-        } else {
-            c[1] = inv * 0.0625f;
-            c[2] = 8.0f * xq;
-            c[4] = xq;
-        }
-    }
-}
-
-// The 16 x elements lane l converts in convert4_i8, of pair p (column p / m
-// of vector p % m).
-__device__ __forceinline__ void load_x_quarter(const float* __restrict__ x, int k, int m, int p,
-                                               int lane, float4 (&v)[4])
-{
-    const float* src = x + (size_t)(p % m) * k + (size_t)(p / m) * 256 + 16 * (lane & 15);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        v[i] = reinterpret_cast<const float4*>(src)[i];
-    }
-}
-
-struct TileI8 {
-    uint4 h;       // the lane's row header
-    uint4 q0, q1;  // chunk g of the row: code bytes 0-15 and 16-31
-};
-
-struct ColI8 {
-    i32x4_t a[4];     // MFMA A operands of the column
-    float c0, c1, c2, xlo, xhi;
-};
-
-__device__ __forceinline__ ColI8 read_col_i8(const unsigned char* col, uint32_t a_off, int g)
-{
-    ColI8 c;
-#pragma unroll
-    for (int mu = 0; mu < 4; ++mu) {
-        c.a[mu] = *reinterpret_cast<const i32x4_t*>(col + a_off + mu * kI8MuBytes);
-    }
-    const float4 k = *reinterpret_cast<const float4*>(col + kI8ColA + g * 32);
-    c.c0 = k.x;
-    c.c1 = k.y;
-    c.c2 = k.z;
-    c.xlo = k.w;
-    c.xhi = *reinterpret_cast<const float*>(col + kI8ColA + g * 32 + 16);
-    return c;
-}
+constexpr int kK4Mu = 17 * 16;                  // 16 digit slots + a zero slot
+constexpr int kK4Zero = 16 * 16;
+constexpr int kK4Const = 4 * kK4Mu;
+constexpr int kK4Word = kK4Const + 8 * 16;
+constexpr int kK4List = kK4Word + 16;
+constexpr int kK4Pair = kK4List + kCorr * 8;
 
 __device__ __forceinline__ i32x4_t lo_codes(const uint4& q)
 {
@@ -192,55 +80,49 @@ __device__ __forceinline__ i32x4_t hi_codes(const uint4& q)
                    (int)((q.z & 0xF0F0F0F0u) ^ 0x80808080u), (int)((q.w & 0xF0F0F0F0u) ^ 0x80808080u)};
 }
 
-__device__ __forceinline__ float digits_value(const i32x4_t& D)
+// Convert the 16 elements lane l holds of a (column, vector) pair: elements
+// 16 (l % 16) .. of the column, which operand mu = (l % 16) % 4 of chunk
+// (l % 16) / 4 covers.  The 16 lanes of a DPP row hold one pair.
+__device__ __forceinline__ void convert_pair_k4(const float4 (&v)[4], unsigned char* pair, int lane,
+                                                bool store)
 {
-    return __builtin_fmaf((float)D[2], 65536.0f, (float)(D[1] * 256 + D[0]));
+    const float e[16] = {v[0].x, v[0].y, v[0].z, v[0].w, v[1].x, v[1].y, v[1].z, v[1].w,
+                         v[2].x, v[2].y, v[2].z, v[2].w, v[3].x, v[3].y, v[3].z, v[3].w};
+    const Conv16 cv = convert16(e);
+    if (!store) {
+        return;
+    }
+    const int t = lane & 15;
+    const int mu = t & 3;
+    const int g = t >> 2;
+#pragma unroll
+    for (int l = 0; l < 4; ++l) {
+        *reinterpret_cast<uint4*>(pair + mu * kK4Mu + (4 * g + l) * 16) =
+            make_uint4(cv.plane[l][0], cv.plane[l][1], cv.plane[l][2], cv.plane[l][3]);
+    }
+    if (t < 4) {
+        *reinterpret_cast<uint4*>(pair + t * kK4Mu + kK4Zero) = make_uint4(0u, 0u, 0u, 0u);
+    }
+    if ((t & 1) == 0) {
+        *reinterpret_cast<double2*>(pair + kK4Const + (t >> 1) * 16) =
+            make_double2(grid_scale(cv.sigma), cv.xsum);
+    }
+    if (t == 0) {
+        *reinterpret_cast<uint32_t*>(pair + kK4Word) = (uint32_t)cv.total;
+    }
+    store_corrections(pair + kK4List, cv, e, 16 * t);
 }
 
-// The weight side of one (tile, column) step: unpacked codes and the
-// lane's chunk scales, shared by every vector.
-struct StepW {
-    i32x4_t lo0, lo1, hi0, hi1;
-    ChunkScalesD s;
-};
-
-__device__ __forceinline__ StepW step_weights(const TileI8& cur, uint32_t sh, uint32_t sel)
+// The 16 x elements lane l converts, of pair p (column p / m of vector p % m).
+__device__ __forceinline__ void load_x_quarter(const float* __restrict__ x, int k, int m, int p,
+                                               int lane, float4 (&v)[4])
 {
-    StepW t;
-    t.lo0 = lo_codes(cur.q0);
-    t.lo1 = lo_codes(cur.q1);
-    t.hi0 = hi_codes(cur.q0);
-    t.hi1 = hi_codes(cur.q1);
-    t.s = decode_chunk(cur.h, sh, sel);
-    return t;
+    const float* src = x + (size_t)(p % m) * k + (size_t)(p / m) * 256 + 16 * (lane & 15);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[i] = reinterpret_cast<const float4*>(src)[i];
+    }
 }
-
-// One vector's part of a step: four MFMAs and the scaling; the lane's
-// partial of its row.
-__device__ __forceinline__ float step_vector(const StepW& t, const ColI8& col)
-{
-    const i32x4_t zero = {0, 0, 0, 0};
-    i32x4_t Dl = __builtin_amdgcn_mfma_i32_16x16x64_i8(col.a[0], t.lo0, zero, 0, 0, 0);
-    Dl = __builtin_amdgcn_mfma_i32_16x16x64_i8(col.a[1], t.lo1, Dl, 0, 0, 0);
-    i32x4_t Dh = __builtin_amdgcn_mfma_i32_16x16x64_i8(col.a[2], t.hi0, zero, 0, 0, 0);
-    Dh = __builtin_amdgcn_mfma_i32_16x16x64_i8(col.a[3], t.hi1, Dh, 0, 0, 0);
-    const float u_lo = col.c0 * digits_value(Dl);
-    const float u_hi = __builtin_fmaf(col.c1, digits_value(Dh), col.c2);
-    float t1 = t.s.sc_lo * u_lo;
-    t1 = __builtin_fmaf(t.s.sc_hi, u_hi, t1);
-    float t2 = t.s.m_lo * col.xlo;
-    t2 = __builtin_fmaf(t.s.m_hi, col.xhi, t2);
-    return __builtin_fmaf(-t.s.dmin, t2, t.s.d * t1);
-}
-
-// ---------------------------------------------------------------------------
-// Line-streamed int8 matrix-core kernel (rows of whole 128-byte lines).
-//
-// The operands and arithmetic above, fed by the line stream of q4k_lines.h:
-// whole 128-byte lines per row into a per-wave LDS ring, from which the
-// lanes read the tile layout of the matrix cores; M vectors share the
-// weight side (codes, scales) of each step.
-// ---------------------------------------------------------------------------
 
 template <int NW, int P, int XC, int M>
 __global__ void __launch_bounds__(NW * 64)
@@ -253,98 +135,136 @@ gemv_i8_lines_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4;
     const int j = lane & 15;
-    const bool active = (j >> 2) == g && (j & 3) < 3;
-    const uint32_t a_off = active ? (uint32_t)((g * 3 + (j & 3)) * 16) : (uint32_t)kI8ZeroSlot;
-    const uint32_t sh = (uint32_t)(g & 1) * 16u;
-    const uint32_t sel = g < 2 ? 0xFFFFFFFFu : 0u;
+    const uint32_t a_off =
+        (j >> 2) == g ? (uint32_t)((g * 4 + (j & 3)) * 16) : (uint32_t)kK4Zero;
     const int row0 = blockIdx.x * rows_per_block;
     const int rows_here = min(rows_per_block, n - row0);
     const int ncg = (S >> 3) / slabs_per_task;
 
     // LDS: staged x (S columns of M vectors, column-major, and a spare
-    // slot), the line rings, row sums
+    // pair), the line rings, row sums (f64)
     const int npairs = S * M;
-    const size_t xbytes = (size_t)(npairs + 1) * kI8ColBytes;
+    const size_t xbytes = (size_t)(npairs + 1) * kK4Pair;
     unsigned char* ring = smem + xbytes + wave * kRingWave;
-    float* ypart = reinterpret_cast<float*>(smem + xbytes + NW * kRingWave);
+    double* ypart = reinterpret_cast<double*>(smem + xbytes + NW * kRingWave);
     const int k = S * 256;
 
     // XC groups of four (column, vector) pairs of x per wave, one pair per
     // 16-lane group: all of them when S * M <= 4 * XC * NW; pair p is column
     // p / M of vector p % M
     float4 xv[XC][4];
-    auto issue_x = [&]() {
+    auto issue_x = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < XC; ++i) {
             const int pr = min(4 * (wave + i * NW) + (lane >> 4), npairs - 1);
             load_x_quarter(x, k, M, pr, lane, xv[i]);
         }
     };
-    // unconditional conversions (a load feeding a conditional use would be
-    // sunk into the branch and wait for every load before it); pairs past
-    // the last go to a spare slot
-    auto convert_x = [&]() {
+    // every lane converts (the conversion exchanges values between lanes);
+    // pairs past the last are not stored
+    auto convert_x = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < XC; ++i) {
-            const int pr = min(4 * (wave + i * NW) + (lane >> 4), npairs);
-            convert4_i8(xv[i], smem + (size_t)pr * kI8ColBytes, lane);
+            const int pr = 4 * (wave + i * NW) + (lane >> 4);
+            convert_pair_k4(xv[i], smem + (size_t)min(pr, npairs) * kK4Pair, lane, pr < npairs);
         }
         for (int q = XC * NW + wave; 4 * q < npairs; q += NW) {
-            const int pr = min(4 * q + (lane >> 4), npairs - 1);
+            const int pr = 4 * q + (lane >> 4);
             float4 v[4];
-            load_x_quarter(x, k, M, pr, lane, v);
-            convert4_i8(v, smem + (size_t)(4 * q + (lane >> 4) < npairs ? pr : npairs) * kI8ColBytes,
-                        lane);
+            load_x_quarter(x, k, M, min(pr, npairs - 1), lane, v);
+            convert_pair_k4(v, smem + (size_t)min(pr, npairs) * kK4Pair, lane, pr < npairs);
         }
     };
 
-    float acc[M];
+    double acc[M];
 #pragma unroll
     for (int b = 0; b < M; ++b) {
-        acc[b] = 0.f;
+        acc[b] = 0.0;
     }
-    auto step = [&](int c, const unsigned char* rr, uint32_t b0) {
-        TileI8 t;
-        t.h = *reinterpret_cast<const uint4*>(rr + (b0 & 255u));
-        t.q0 = *reinterpret_cast<const uint4*>(rr + ((b0 + 16u + 32u * (uint32_t)g) & 255u));
-        t.q1 = *reinterpret_cast<const uint4*>(rr + ((b0 + 32u + 32u * (uint32_t)g) & 255u));
-        const StepW sw = step_weights(t, sh, sel);
+    const ScaleGather sg = scale_gather(g);
+    auto step = [&](int c, const unsigned char* rr, uint32_t b0, auto corr) __attribute__((always_inline)) {
+        const uint4 h = *reinterpret_cast<const uint4*>(rr + (b0 & 255u));
+        const uint4 q0 = *reinterpret_cast<const uint4*>(rr + ((b0 + 16u + 32u * (uint32_t)g) & 255u));
+        const uint4 q1 = *reinterpret_cast<const uint4*>(rr + ((b0 + 32u + 32u * (uint32_t)g) & 255u));
+        const uint32_t D[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+        const i32x4_t lo0 = lo_codes(q0), lo1 = lo_codes(q1);
+        const i32x4_t hi0 = hi_codes(q0), hi1 = hi_codes(q1);
+        const uint32_t sm = gather_scales(h, sg);
+        const half2_t dd = __builtin_bit_cast(half2_t, h.x);
+        const float d = (float)dd.x;
+        const float dmin = (float)dd.y;
+        const float Dlo = d * (float)(sm & 0xFFu);
+        const float Dhi = d * (float)((sm >> 8) & 0xFFu);
+        const float Mlo = dmin * (float)((sm >> 16) & 0xFFu);
+        const float Mhi = dmin * (float)(sm >> 24);
 #pragma unroll
         for (int b = 0; b < M; ++b) {
-            const ColI8 col = read_col_i8(smem + (size_t)(c * M + b) * kI8ColBytes, a_off, g);
-            acc[b] += step_vector(sw, col);
+            const unsigned char* pair = smem + (size_t)(c * M + b) * kK4Pair;
+            const i32x4_t a0 = *reinterpret_cast<const i32x4_t*>(pair + a_off);
+            const i32x4_t a1 = *reinterpret_cast<const i32x4_t*>(pair + kK4Mu + a_off);
+            const i32x4_t a2 = *reinterpret_cast<const i32x4_t*>(pair + 2 * kK4Mu + a_off);
+            const i32x4_t a3 = *reinterpret_cast<const i32x4_t*>(pair + 3 * kK4Mu + a_off);
+            const double2 klo = *reinterpret_cast<const double2*>(pair + kK4Const + g * 32);
+            const double2 khi = *reinterpret_cast<const double2*>(pair + kK4Const + g * 32 + 16);
+            const uint32_t cnt = *reinterpret_cast<const uint32_t*>(pair + kK4Word);
+            const i32x4_t zero = {0, 0, 0, 0};
+            i32x4_t Dl = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, lo0, zero, 0, 0, 0);
+            Dl = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, lo1, Dl, 0, 0, 0);
+            i32x4_t Dh = __builtin_amdgcn_mfma_i32_16x16x64_i8(a2, hi0, zero, 0, 0, 0);
+            Dh = __builtin_amdgcn_mfma_i32_16x16x64_i8(a3, hi1, Dh, 0, 0, 0);
+            const double Tlo = digits_exact(Dl[0], Dl[1], Dl[2], Dl[3]);
+            const double Thi16 = __builtin_fma(khi.y, 128.0, digits_exact(Dh[0], Dh[1], Dh[2], Dh[3]));
+            acc[b] = subblock_term(acc[b], Dlo, Tlo, Mlo, klo.y, klo.x);
+            acc[b] = subblock_term(acc[b], Dhi * 0.0625f, Thi16, Mhi, khi.y, khi.x);
+            if constexpr (decltype(corr)::value) {
+                const uint32_t ncorr = __builtin_amdgcn_readfirstlane(cnt);
+                if (ncorr != 0u) {
+                    acc[b] = column_corrections(acc[b], ncorr, pair + kK4List, D, g, Dlo, Dhi, Mlo,
+                                                Mhi, klo.x, khi.x, x + (size_t)b * k + (size_t)c * 256);
+                }
+            } else {
+                (void)cnt;
+            }
         }
     };
-    auto task_end = [&](int task) {
+    // whether slab sl has a (column, vector) pair with uncertified elements
+    auto slab_flag = [&](int sl) __attribute__((always_inline)) {
+        uint32_t f = 0;
+        for (int pr = 8 * sl * M; pr < 8 * (sl + 1) * M; ++pr) {
+            f |= *reinterpret_cast<const uint32_t*>(smem + (size_t)pr * kK4Pair + kK4Word);
+        }
+        return __builtin_amdgcn_readfirstlane(f) != 0u;
+    };
+    auto task_end = [&](int task) __attribute__((always_inline)) {
         const int r = (task / ncg) * 16 + j;
 #pragma unroll
         for (int b = 0; b < M; ++b) {
-            float v = acc[b];
+            double v = acc[b];
             v += __shfl_xor(v, 16, 64);
             v += __shfl_xor(v, 32, 64);
             if (g == 0 && r < rows_here) {
                 if (ncg == 1) {
-                    y[(size_t)b * n + row0 + r] = v;
+                    y[(size_t)b * n + row0 + r] = (float)v;
                 } else {
                     ypart[(b * ncg + task % ncg) * rows_per_block + r] = v;
                 }
             }
-            acc[b] = 0.f;
+            acc[b] = 0.0;
         }
     };
     line_stream<NW, P>(w, x, n, S, rows_per_block, slabs_per_task, ring, issue_x, convert_x, step,
-                       task_end);
+                       task_end, slab_flag);
 
     if (ncg > 1) {
         __syncthreads();
         for (int i = tid; i < rows_here * M; i += NW * 64) {
             const int b = i / rows_here;
             const int r = i - b * rows_here;
-            float a = 0.f;
+            double a = 0.0;
             for (int cg = 0; cg < ncg; ++cg) {
                 a += ypart[(b * ncg + cg) * rows_per_block + r];
             }
-            y[(size_t)b * n + row0 + r] = a;
+            y[(size_t)b * n + row0 + r] = (float)a;
         }
     }
 }
@@ -359,83 +279,61 @@ gemv_i8_lines_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
 // One MFMA covers one 32-element sub-block s for four vectors: B = the codes
 // of sub-block s of the 16 rows of the tile (lane group g: elements 8g ..
 // 8g+7, taken from bytes 8g .. 8g+7 of the chunk, low or high nibbles as in
-// the kernels above), A row 4 b' + l = digit l of vector b' of the quad (row
-// 4 b' + 3 zero).  A is dense, so a superblock costs eight small MFMAs per
-// quad of vectors instead of four large ones per vector, and lane (g, j) ends
-// with the three digit sums of vector g of the quad for row j: it needs no
-// other lane, but it scales all eight sub-blocks of its row:
-//   acc += d * sum_s sc_s * u_s - dmin * sum_s m_s * X_s,
-//   u_s = 2^-sigma_s * T_s (low sub-blocks), 2^-sigma_s / 16 * T_s + 8 X_s (high),
-// T = D0 + 256 D1 + 65536 D2, X_s the quantized x sum of the sub-block.
+// the kernels above), A row 4 b' + l = digit l of vector b' of the quad (x
+// on the grid of q4k_xrep.h).  A is dense, so a superblock costs eight
+// small MFMAs per quad of vectors instead of four large ones per vector, and
+// lane (g, j) ends with the four digit sums of vector g of the quad for row
+// j: it needs no other lane, but it scales all eight sub-blocks of its row,
+// each with the exact sums and the one-rounding f64 term of subblock_term.
+// A vector's uncertified elements are added exactly, per element, as in
+// the kernels above (their codes read again from the row's ring).
 // ---------------------------------------------------------------------------
 
-constexpr int kSbBlock = 49 * 8;              // 48 digit slots of 8 bytes and a zero slot
-constexpr int kSbZero = 48 * 8;
-constexpr int kSbQuad = 8 * kSbBlock;         // A operands of one column and vector quad
-constexpr int kSbConst = 8 * 8;               // {scale, X} of the eight sub-blocks of one vector
-constexpr int kSbGroup = kSbQuad + 4 * kSbConst;   // one column, one quad: A, then constants
+constexpr int kSbBlock = 4 * 4 * 4 * 8;       // k-group x vector x digit, 8 bytes each
+constexpr int kSbConst = 8 * kSbBlock;        // {2^-s, XI} per (vector, sub-block)
+constexpr int kSbWord = kSbConst + 4 * 8 * 16;   // uncertified elements per vector
+constexpr int kSbList = kSbWord + 16;         // the first kCorr of each vector
+constexpr int kSbGroup = kSbList + 4 * kCorr * 8;   // one column, one quad
+constexpr int kSbLists = kSbGroup - kSbWord;  // the counts and lists of a group
+constexpr int kSigmaFromX = 1 << 20;          // rescan_subblock: no exponent given
 
 // Convert one (column, vector quad): lane l takes vector l / 16 of the quad
 // and elements 16 (l % 16) .. +15 of the column (half of sub-block (l % 16) /
-// 2).  Digits as in convert4_i8; here digit l of elements 8g .. 8g+7 of
-// sub-block s of vector b' goes to slot (g, b', l) of block s.
-__device__ __forceinline__ void convert4_sb(const float4 (&v)[4], unsigned char* grp, int lane)
+// 2); digit l of elements 8 gk .. 8 gk + 7 of sub-block s of vector b' goes
+// to slot (gk, b', l) of block s.  Every lane calls this (the conversion
+// exchanges values between lanes).  The count of each vector's uncertified
+// elements and the first kCorr of them go to lists (kSbLists bytes: four
+// counts, then four lists).  Returns the lane's vector's count (the same in
+// its 16 lanes).
+__device__ __forceinline__ int convert_quad(const float4 (&v)[4], unsigned char* grp,
+                                            unsigned char* lists, int lane)
 {
-    const int le = lane & 15;
+    const float e[16] = {v[0].x, v[0].y, v[0].z, v[0].w, v[1].x, v[1].y, v[1].z, v[1].w,
+                         v[2].x, v[2].y, v[2].z, v[2].w, v[3].x, v[3].y, v[3].z, v[3].w};
+    const Conv16 cv = convert16(e);
+    const int t = lane & 15;
     const int bq = lane >> 4;                 // vector within the quad
-    const int s = le >> 1;                    // sub-block
-    const int half = le & 1;
-    float m = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        m = fmaxf(m, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
-    }
-    m = fmaxf(m, __builtin_bit_cast(float, dpp_i<0xB1>(__builtin_bit_cast(int, m))));  // lane l ^ 1
-    int sigma = 0;
-    if (m > 0.f) {
-        sigma = 22 - __builtin_amdgcn_frexp_expf(m);
-        sigma = sigma < -126 ? -126 : sigma > 126 ? 126 : sigma;
-    }
-    const float scale = __builtin_bit_cast(float, (uint32_t)(sigma + 127) << 23);
-    uint32_t usum = 0;
-    uint32_t dig[3][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float vals[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-        uint32_t u[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            u[t] = __builtin_bit_cast(uint32_t, __builtin_fmaf(vals[t], scale, 12582912.0f)) -
-                   0x4ABF7F80u;
-            usum += u[t];
-        }
-        const uint32_t lo01 = __builtin_amdgcn_perm(u[1], u[0], 0x05010400u);
-        const uint32_t lo23 = __builtin_amdgcn_perm(u[3], u[2], 0x05010400u);
-        const uint32_t hi01 = __builtin_amdgcn_perm(u[1], u[0], 0x07030602u);
-        const uint32_t hi23 = __builtin_amdgcn_perm(u[3], u[2], 0x07030602u);
-        dig[0][i] = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u) ^ 0x80808080u;
-        dig[1][i] = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u) ^ 0x80808080u;
-        dig[2][i] = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u) ^ 0x80808080u;
-    }
+    const int s = t >> 1;                     // sub-block
+    const int half = t & 1;
     unsigned char* blk = grp + s * kSbBlock;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int gk = 2 * half + h;          // k-group of these eight elements
 #pragma unroll
-        for (int l = 0; l < 3; ++l) {
-            *reinterpret_cast<uint2*>(blk + ((gk * 4 + bq) * 3 + l) * 8) =
-                make_uint2(dig[l][2 * h], dig[l][2 * h + 1]);
+        for (int l = 0; l < 4; ++l) {
+            *reinterpret_cast<uint2*>(blk + ((gk * 4 + bq) * 4 + l) * 8) =
+                make_uint2(cv.plane[l][2 * h], cv.plane[l][2 * h + 1]);
         }
     }
-    // the zero slot and the sub-block constants: every lane of a pair holds
-    // the same values (pair max and sum by DPP), so both store them -- no
-    // branch inside the callers' unrolled loops
-    *reinterpret_cast<uint2*>(blk + kSbZero) = make_uint2(0, 0);
-    const uint32_t us2 = usum + (uint32_t)dpp_i<0xB1>((int)usum);
-    const int XI = (int)us2 - 32 * 0x808080;
-    const float inv = __builtin_bit_cast(float, (uint32_t)(127 - sigma) << 23);
-    *reinterpret_cast<float2*>(grp + kSbQuad + bq * kSbConst + s * 8) =
-        make_float2((s & 1) ? inv * 0.0625f : inv, inv * (float)XI);
+    if (half == 0) {
+        *reinterpret_cast<double2*>(grp + kSbConst + (bq * 8 + s) * 16) =
+            make_double2(grid_scale(cv.sigma), cv.xsum);
+    }
+    if (t == 0) {
+        *reinterpret_cast<uint32_t*>(lists + bq * 4) = (uint32_t)cv.total;
+    }
+    store_corrections(lists + 16 + bq * (kCorr * 8), cv, e, 16 * t);
+    return cv.total;
 }
 
 // The eight sub-block scales and mins of a header as floats.
@@ -463,6 +361,135 @@ __device__ __forceinline__ RowScales decode_row(const uint4& h)
     }
     return r;
 }
+
+// v[s] for a per-lane s in 0..7, by masks (an indexed read would go through
+// scratch memory)
+__device__ __forceinline__ float pick8(const float (&v)[8], int s)
+{
+    uint32_t r = 0;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        r |= __builtin_bit_cast(uint32_t, v[t]) & (0u - (uint32_t)(s == t));
+    }
+    return __builtin_bit_cast(float, r);
+}
+
+// The exact terms of sub-block se's uncertified elements for the lane's row
+// (xs: the sub-block's 32 values of x, sigma: its grid exponent), each
+// element tested as the conversion tested it: fl32(d sc q - dmin m) * x in
+// f64, the oracle's own arithmetic.  Ds, Ms: d sc_j (/ 16 for odd j) and
+// dmin m_j of the row; its codes are read again from its ring (rr, b: the
+// superblock's first byte, window: the ring's size minus one).
+__device__ __forceinline__ double rescan_subblock(double acc, const float* __restrict__ xs, int se,
+                                                  int sigma, const float (&Ds)[8],
+                                                  const float (&Ms)[8], const unsigned char* rr,
+                                                  uint32_t b, uint32_t window)
+{
+    const float4* src = reinterpret_cast<const float4*>(xs);
+    float4 xv[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        xv[t] = src[t];
+    }
+    const uint32_t cb = b + 16u + 32u * (uint32_t)(se >> 1);
+    const uint4 c0 = *reinterpret_cast<const uint4*>(rr + (cb & window));
+    const uint4 c1 = *reinterpret_cast<const uint4*>(rr + ((cb + 16u) & window));
+    const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+    if (sigma == kSigmaFromX) {           // the conversion's own exponent, from x
+        float mx = 0.f;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            mx = fmaxf(mx, fminf(fabsf(xv[t].x), kF32Max));
+            mx = fmaxf(mx, fminf(fabsf(xv[t].y), kF32Max));
+            mx = fmaxf(mx, fminf(fabsf(xv[t].z), kF32Max));
+            mx = fmaxf(mx, fminf(fabsf(xv[t].w), kF32Max));
+        }
+        sigma = grid_sigma(mx);
+    }
+    const float Dw = pick8(Ds, se) * ((se & 1) ? 16.0f : 1.0f);
+    const float Mw = pick8(Ms, se);
+    const uint32_t sh = 4u * (uint32_t)(se & 1);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const float xe[4] = {xv[t].x, xv[t].y, xv[t].z, xv[t].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            uint32_t u;
+            int cert;
+            grid_element(xe[i], sigma, u, cert);
+            const uint32_t q = (cw[t] >> (8 * i + sh)) & 15u;
+            const float wv = __builtin_fmaf(Dw, (float)q, -Mw);
+            const double tv = (double)wv * (double)xe[i];
+            acc = cert ? acc : acc + tv;
+        }
+    }
+    return acc;
+}
+
+// The exact terms of one vector's uncertified elements in one column for
+// the lane's row: cnt of them, listed in `list` when cnt <= kCorr, else
+// found again by rescan_subblock (xg: the vector's 256 values of the column;
+// cst: its {2^-s, XI} per sub-block, or null: the exponents are found again
+// from x).  Arguments otherwise as there.
+__device__ __forceinline__ double vector_corrections(double acc, uint32_t cnt, const unsigned char* list,
+                                                     const double2* cst, const float* __restrict__ xg,
+                                                     const float (&Ds)[8], const float (&Ms)[8],
+                                                     const unsigned char* rr, uint32_t b,
+                                                     uint32_t window)
+{
+    if (cnt <= (uint32_t)kCorr) {
+        for (uint32_t k = 0; k < cnt; ++k) {
+            const Corr c = *reinterpret_cast<const Corr*>(list + k * 8);
+            const int se = (int)(c.e >> 5);              // sub-block 2 chunk + half
+            const uint32_t byte = rr[(b + 16u + 32u * (uint32_t)(se >> 1) + (c.e & 31u)) & window];
+            const uint32_t q = (se & 1) ? byte >> 4 : byte & 15u;
+            const float Dw = pick8(Ds, se) * ((se & 1) ? 16.0f : 1.0f);
+            const float Mw = pick8(Ms, se);
+            const float wv = __builtin_fmaf(Dw, (float)q, -Mw);
+            acc += (double)wv * (double)c.x;             // exact product
+        }
+        return acc;
+    }
+#pragma nounroll
+    for (int se = 0; se < 8; ++se) {
+        acc = rescan_subblock(acc, xg + 32 * se, se, cst ? grid_sigma_of(cst[se].x) : kSigmaFromX,
+                              Ds, Ms, rr, b, window);
+    }
+    return acc;
+}
+
+// The row sums of up to four vector quads as named values: the correction
+// loops pick a quad at run time, and an array indexed so would be kept in
+// scratch memory (the compiler turns a chain of selects over an array's
+// elements back into an indexed load).
+struct QuadAcc {
+    double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+
+    template <int Q>
+    __device__ __forceinline__ double& at()
+    {
+        if constexpr (Q == 0) {
+            return a0;
+        } else if constexpr (Q == 1) {
+            return a1;
+        } else if constexpr (Q == 2) {
+            return a2;
+        } else {
+            return a3;
+        }
+    }
+    __device__ __forceinline__ double get(int q) const
+    {
+        return q == 0 ? a0 : q == 1 ? a1 : q == 2 ? a2 : a3;
+    }
+    __device__ __forceinline__ void set(int q, double v)
+    {
+        a0 = q == 0 ? v : a0;
+        a1 = q == 1 ? v : a1;
+        a2 = q == 2 ? v : a2;
+        a3 = q == 3 ? v : a3;
+    }
+};
 
 // Columns of x a wave of kernel 6 holds in registers ahead of its step: with
 // four, waiting for a column's x (loads complete in order) never waits for
@@ -493,9 +520,8 @@ gemv_i8_sub_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4;
     const int j = lane & 15;
-    // A row of this lane: vector j / 4 of the quad, digit j % 4 (3: zero)
-    const uint32_t a_off = (j & 3) < 3 ? (uint32_t)(((g * 4 + (j >> 2)) * 3 + (j & 3)) * 8)
-                                       : (uint32_t)kSbZero;
+    // A row of this lane: vector j / 4 of the quad, digit j % 4
+    const uint32_t a_off = (uint32_t)(((g * 4 + (j >> 2)) * 4 + (j & 3)) * 8);
     const int row0 = blockIdx.x * rows_per_block;
     const int rows_here = min(rows_per_block, n - row0);
     const int ncg = ((S + 7) >> 3) / slabs_per_task;
@@ -505,20 +531,22 @@ gemv_i8_sub_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
     // byte offset of the lane's row within its first line (tiles start on a line)
     const uint32_t loff = ANY ? (uint32_t)(j * 144 * S) & 127u : 0u;
 
-    // LDS: staged x (S columns x NQ quads and a spare group; JIT: NQ groups
-    // per wave), the line rings, row sums
+    // LDS: staged x (S columns x NQ quads and a spare group; JIT: per wave
+    // the digits and constants of one group and the lists of NQ), the line
+    // rings, row sums (f64)
     const int ngroups = S * NQ;
-    const size_t xbytes = JIT ? (size_t)NW * NQ * kSbGroup : (size_t)(ngroups + 1) * kSbGroup;
-    unsigned char* xw = smem + (JIT ? (size_t)wave * NQ * kSbGroup : 0);
+    constexpr int kJitWave = kSbWord + NQ * kSbLists;
+    const size_t xbytes = JIT ? (size_t)NW * kJitWave : (size_t)(ngroups + 1) * kSbGroup;
+    unsigned char* xw = smem + (JIT ? (size_t)wave * kJitWave : 0);
+    unsigned char* xl = xw + kSbWord;            // JIT: the lists of quad q at xl + q kSbLists
     unsigned char* ring = smem + xbytes + wave * kWaveRing;
-    float* ypart = reinterpret_cast<float*>(smem + xbytes + NW * kWaveRing);
+    double* ypart = reinterpret_cast<double*>(smem + xbytes + NW * kWaveRing);
 
     // group q0 = column q0 / NQ, quad q0 % NQ; 16-lane group l / 16 takes
     // vector 4 (q0 % NQ) + l / 16 (past the last vector the last vector
-    // again: its digits reach only the D rows of lanes whose sums are never
-    // stored, so they need no zeroing)
+    // again: its sums reach only lanes whose results are never stored)
     float4 xv[XC][4];
-    auto load_group = [&](int q0, float4 (&v)[4]) {
+    auto load_group = [&](int q0, float4 (&v)[4]) __attribute__((always_inline)) {
         const int qc = min(q0, ngroups - 1);
         const int b = 4 * (qc % NQ) + (lane >> 4);
         const float* src = x + (size_t)min(b, m - 1) * k + (size_t)(qc / NQ) * 256 + 16 * (lane & 15);
@@ -533,7 +561,7 @@ gemv_i8_sub_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
     float4 xa[kA][NQ][4];
     const int ntasks = ((rows_here + 15) >> 4) * ncg;
     const int c_first = 8 * ((min(wave, ntasks - 1) % ncg) * slabs_per_task);
-    auto issue_x = [&]() {
+    auto issue_x = [&]() __attribute__((always_inline)) {
         if constexpr (JIT) {
 #pragma unroll
             for (int a = 0; a < kA; ++a) {
@@ -549,89 +577,140 @@ gemv_i8_sub_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
             load_group(wave + i * NW, xv[i]);
         }
     };
-    auto convert_x = [&]() {
+    auto convert_x = [&]() __attribute__((always_inline)) {
         if constexpr (JIT) {
             return;
         }
 #pragma unroll
         for (int i = 0; i < XC; ++i) {
             const int q0 = wave + i * NW;
-            convert4_sb(xv[i], smem + (size_t)min(q0, ngroups) * kSbGroup, lane);
+            unsigned char* grp = smem + (size_t)min(q0, ngroups) * kSbGroup;
+            convert_quad(xv[i], grp, grp + kSbWord, lane);
         }
         for (int q0 = XC * NW + wave; q0 < ngroups; q0 += NW) {
             float4 v[4];
             load_group(q0, v);
-            convert4_sb(v, smem + (size_t)q0 * kSbGroup, lane);
+            convert_quad(v, smem + (size_t)q0 * kSbGroup, smem + (size_t)q0 * kSbGroup + kSbWord, lane);
         }
     };
 
-    float acc[NQ];
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-        acc[q] = 0.f;
-    }
-    // one superblock of the lane's tile (ring row rr, offset b0) against
-    // the x groups of its column at grp0, grp0 + kSbGroup, ...
-    auto decode = [&](const unsigned char* rr, uint32_t b0, const unsigned char* grp0) {
-        const uint32_t b = b0 + loff;
-        const uint4 hdr = *reinterpret_cast<const uint4*>(rr + (b & kWindow));
+    QuadAcc acc;
+    // The lane's part of one superblock (column c) of its tile row (ring row
+    // rr, offset b0): its codes of the eight sub-blocks as MFMA B operands,
+    // and d sc_j (/ 16 for the high sub-blocks, whose digit sums carry 16 q)
+    // and dmin m_j, exact in f32.
+    struct Tile {
+        long codes[8];
+        float Ds[8], Ms[8];
+        uint32_t b;
+    };
+    auto prep = [&](const unsigned char* rr, uint32_t b0) __attribute__((always_inline)) {
+        Tile t;
+        t.b = b0 + loff;
+        const uint4 hdr = *reinterpret_cast<const uint4*>(rr + (t.b & kWindow));
         uint2 raw[4];
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) {
-            raw[cc] = *reinterpret_cast<const uint2*>(rr + ((b + 16u + 32u * cc + 8u * g) & kWindow));
+            raw[cc] = *reinterpret_cast<const uint2*>(rr + ((t.b + 16u + 32u * cc + 8u * g) & kWindow));
         }
-        long codes[8];
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) {
-            codes[2 * cc] = __builtin_bit_cast(long, make_uint2(raw[cc].x & 0x0F0F0F0Fu,
-                                                                 raw[cc].y & 0x0F0F0F0Fu));
-            codes[2 * cc + 1] = __builtin_bit_cast(
+            t.codes[2 * cc] = __builtin_bit_cast(long, make_uint2(raw[cc].x & 0x0F0F0F0Fu,
+                                                                   raw[cc].y & 0x0F0F0F0Fu));
+            t.codes[2 * cc + 1] = __builtin_bit_cast(
                 long, make_uint2((raw[cc].x & 0xF0F0F0F0u) ^ 0x80808080u,
                                  (raw[cc].y & 0xF0F0F0F0u) ^ 0x80808080u));
         }
         const RowScales rs = decode_row(hdr);
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-            const unsigned char* grp = grp0 + (size_t)q * kSbGroup;
-            const float4* cst = reinterpret_cast<const float4*>(grp + kSbQuad + g * kSbConst);
-            float t1 = 0.f, t2 = 0.f;
+        for (int sb = 0; sb < 8; ++sb) {
+            t.Ds[sb] = rs.d * rs.sc[sb] * ((sb & 1) ? 0.0625f : 1.0f);
+            t.Ms[sb] = rs.dmin * rs.m[sb];
+        }
+        return t;
+    };
+    // quad q of the tile against the x group grp: eight MFMAs, the exact
+    // sums scaled once per sub-block
+    auto quad = [&](const Tile& t, auto qc, const unsigned char* grp) __attribute__((always_inline)) {
+        constexpr int q = decltype(qc)::value;
+        const double2* cst = reinterpret_cast<const double2*>(grp + kSbConst + g * 128);
 #pragma unroll
-            for (int sp = 0; sp < 4; ++sp) {
-                const float4 k2 = cst[sp];        // {scale, X} of sub-blocks 2sp, 2sp+1
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int sb = 2 * sp + h;
-                    const long a = *reinterpret_cast<const long*>(grp + sb * kSbBlock + a_off);
-                    const i32x4_t zero = {0, 0, 0, 0};
-                    const i32x4_t D = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, codes[sb], zero, 0, 0, 0);
-                    const float T = digits_value(D);
-                    const float sca = h ? k2.z : k2.x;
-                    const float X = h ? k2.w : k2.y;
-                    const float u = h ? __builtin_fmaf(sca, T, 8.0f * X) : sca * T;
-                    t1 = __builtin_fmaf(rs.sc[sb], u, t1);
-                    t2 = __builtin_fmaf(rs.m[sb], X, t2);
-                }
+        for (int sb = 0; sb < 8; ++sb) {
+            const long a = *reinterpret_cast<const long*>(grp + sb * kSbBlock + a_off);
+            const double2 k2 = cst[sb];                   // {2^-s, XI}
+            const i32x4_t zero = {0, 0, 0, 0};
+            const i32x4_t D = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, t.codes[sb], zero, 0, 0, 0);
+            double T = digits_exact(D[0], D[1], D[2], D[3]);
+            if (sb & 1) {
+                T = __builtin_fma(k2.y, 128.0, T);
             }
-            acc[q] = __builtin_fmaf(rs.d, t1, acc[q]);
-            acc[q] = __builtin_fmaf(-rs.dmin, t2, acc[q]);
+            acc.at<q>() = subblock_term(acc.at<q>(), t.Ds[sb], T, t.Ms[sb], k2.y, k2.x);
         }
     };
-    auto step = [&](int c, const unsigned char* rr, uint32_t b0) {
-        decode(rr, b0, smem + (size_t)c * NQ * kSbGroup);
+    // kernel 5: the column's groups of the stage, one quad after the other
+    // (a quad's operands are dead before the next one's are read); in a
+    // flagged slab then the exact terms of the column's uncertified
+    // elements, quad by quad in a loop (one copy of that code per step)
+    auto step = [&](int c, const unsigned char* rr, uint32_t b0, auto corr) __attribute__((always_inline)) {
+        const Tile t = prep(rr, b0);
+        static_for<NQ>([&](auto qc) __attribute__((always_inline)) {
+            quad(t, qc, smem + (size_t)(c * NQ + decltype(qc)::value) * kSbGroup);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        if constexpr (decltype(corr)::value) {
+#pragma nounroll
+            for (int q = 0; q < NQ; ++q) {
+                const unsigned char* grp = smem + (size_t)(c * NQ + q) * kSbGroup;
+                const uint4 cnts = *reinterpret_cast<const uint4*>(grp + kSbWord);
+                const uint32_t any = __builtin_amdgcn_readfirstlane(cnts.x | cnts.y | cnts.z | cnts.w);
+                if (any != 0u) {
+                    const uint32_t cnt = g == 0 ? cnts.x : g == 1 ? cnts.y : g == 2 ? cnts.z : cnts.w;
+                    const int bv = min(4 * q + g, m - 1);
+                    const double a = vector_corrections(
+                        acc.get(q), cnt, grp + kSbList + g * (kCorr * 8),
+                        reinterpret_cast<const double2*>(grp + kSbConst + g * 128),
+                        x + (size_t)bv * k + (size_t)c * 256, t.Ds, t.Ms, rr, t.b, kWindow);
+                    acc.set(q, a);
+                }
+            }
+        }
     };
-    // JIT: convert column c (slot cp mod kA) into the wave's groups, refill
-    // the slot with the column kA positions on (past cend: the next slab's or
-    // task's, from cn), then decode; the groups are rewritten only after this
-    // step's reads of them (the wave's LDS accesses complete in order).
-    // Positions past a partial slab's end (invalid) keep the slots cycling.
+    // kernel 6: convert quad q of column c (registers of slot cp mod kA)
+    // into the wave's one group and decode it, quad after quad (the wave's
+    // LDS accesses complete in order, so a conversion overwrites the group
+    // only after the previous quad's reads); a quad of which some vector has
+    // uncertified elements in the column sets its bit in `dirty`, and those
+    // quads' exact terms follow, found again from x.  Then the slot is
+    // refilled with the column kA positions on (past cend: the next slab's
+    // or task's, from cn).  Positions past a partial slab's end (invalid)
+    // keep the slots cycling.
     auto step_jit = [&](int c, int cend, int cn, const unsigned char* rr, uint32_t b0, int cp,
-                        bool valid) {
+                        bool valid) __attribute__((always_inline)) {
         float4 (&v)[NQ][4] = xa[JIT ? cp % kA : 0];
         __builtin_amdgcn_sched_barrier(0);
         if (valid) {
-#pragma unroll
-            for (int q = 0; q < NQ; ++q) {
-                convert4_sb(v[q], xw + (size_t)q * kSbGroup, lane);
+            const Tile t = prep(rr, b0);
+            uint32_t dirty = 0;
+            static_for<NQ>([&](auto qc) __attribute__((always_inline)) {
+                constexpr int q = decltype(qc)::value;
+                const int total = convert_quad(v[q], xw, xl + q * kSbLists, lane);
+                dirty |= (total != 0 ? 1u : 0u) << q;
+                quad(t, qc, xw);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            if (__builtin_amdgcn_readfirstlane(__ballot(dirty != 0u) != 0 ? 1 : 0) != 0) {
+#pragma nounroll
+                for (int q = 0; q < NQ; ++q) {
+                    if ((dirty >> q) & 1u) {
+                        const unsigned char* lq = xl + q * kSbLists;
+                        const uint32_t cnt = *reinterpret_cast<const uint32_t*>(lq + g * 4);
+                        const int bv = min(4 * q + g, m - 1);
+                        const double a = vector_corrections(
+                            acc.get(q), cnt, lq + 16 + g * (kCorr * 8), nullptr,
+                            x + (size_t)bv * k + (size_t)c * 256, t.Ds, t.Ms, rr, t.b, kWindow);
+                        acc.set(q, a);
+                    }
+                }
             }
         }
         const int ca = c + kA < cend ? c + kA : cn + (c + kA - cend);
@@ -640,24 +719,50 @@ gemv_i8_sub_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
             load_group(ca * NQ + q, v[q]);
         }
         __builtin_amdgcn_sched_barrier(0);
-        if (valid) {
-            decode(rr, b0, xw);
-        }
     };
-    auto task_end = [&](int task) {
-        const int r = (task / ncg) * 16 + j;
+    // whether slab sl has a column with uncertified elements in any vector:
+    // one bit per column in scalar registers, gathered by a ballot on the
+    // first call (after the x stage)
+    uint64_t cmask[2] = {0, 0};
+    bool have_mask = false;
+    auto slab_flag = [&](int sl) __attribute__((always_inline)) {
+        if (!have_mask) {
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) {
+            for (int h = 0; h < 2; ++h) {
+                const int c = 64 * h + lane;
+                uint32_t f = 0;
+                if (c < S) {
+                    for (int q = 0; q < NQ; ++q) {
+                        const uint4 cn = *reinterpret_cast<const uint4*>(
+                            smem + (size_t)(c * NQ + q) * kSbGroup + kSbWord);
+                        f |= cn.x | cn.y | cn.z | cn.w;
+                    }
+                }
+                cmask[h] = __ballot(f != 0u);
+            }
+            have_mask = true;
+        }
+        const int c0 = 8 * sl;
+        if (c0 >= 128) {
+            return true;
+        }
+        const uint64_t bits = c0 < 64 ? cmask[0] >> c0 : cmask[1] >> (c0 - 64);
+        return (bits & 0xFFu) != 0u;
+    };
+    auto task_end = [&](int task) __attribute__((always_inline)) {
+        const int r = (task / ncg) * 16 + j;
+        static_for<NQ>([&](auto qc) __attribute__((always_inline)) {
+            constexpr int q = decltype(qc)::value;
             const int b = 4 * q + g;
             if (b < m && r < rows_here) {
                 if (ncg == 1) {
-                    y[(size_t)b * n + row0 + r] = acc[q];
+                    y[(size_t)b * n + row0 + r] = (float)acc.at<q>();
                 } else {
-                    ypart[(b * ncg + task % ncg) * rows_per_block + r] = acc[q];
+                    ypart[(b * ncg + task % ncg) * rows_per_block + r] = acc.at<q>();
                 }
             }
-            acc[q] = 0.f;
-        }
+            acc.at<q>() = 0.0;
+        });
     };
     if constexpr (JIT && ANY) {
         line_stream_any<NW>(w, x, n, S, rows_per_block, slabs_per_task, ring, issue_x, convert_x,
@@ -667,10 +772,10 @@ gemv_i8_sub_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
                            step_jit, task_end);
     } else if constexpr (ANY) {
         line_stream_any<NW>(w, x, n, S, rows_per_block, slabs_per_task, ring, issue_x, convert_x,
-                            step, task_end);
+                            step, task_end, slab_flag);
     } else {
         line_stream<NW, 3>(w, x, n, S, rows_per_block, slabs_per_task, ring, issue_x, convert_x,
-                           step, task_end);
+                           step, task_end, slab_flag);
     }
 
     if (ncg > 1) {
@@ -678,25 +783,28 @@ gemv_i8_sub_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
         for (int i = tid; i < rows_here * m; i += NW * 64) {
             const int b = i / rows_here;
             const int r = i - b * rows_here;
-            float a = 0.f;
+            double a = 0.0;
             for (int cg = 0; cg < ncg; ++cg) {
                 a += ypart[(b * ncg + cg) * rows_per_block + r];
             }
-            y[(size_t)b * n + row0 + r] = a;
+            y[(size_t)b * n + row0 + r] = (float)a;
         }
     }
 }
 
-template <int XC, int NQ, bool JIT = false>
+template <int XC, int NQ, bool JIT = false, int NW = 8>
 static hipError_t launch_sub_x(const GemvPlan& p, const uint8_t* w, const float* x, float* y,
                                hipStream_t stream)
 {
+    if (p.waves_per_block != NW) {
+        return hipErrorInvalidValue;
+    }
     if (p.S % 8 != 0) {
-        hipLaunchKernelGGL((gemv_i8_sub_kernel<8, XC, NQ, JIT, true>), dim3(p.grid), dim3(512),
+        hipLaunchKernelGGL((gemv_i8_sub_kernel<NW, XC, NQ, JIT, true>), dim3(p.grid), dim3(NW * 64),
                            p.lds_bytes, stream, w, x, y, p.n, p.S, p.m, p.rows_per_block,
                            p.cols_per_task / 8);
     } else {
-        hipLaunchKernelGGL((gemv_i8_sub_kernel<8, XC, NQ, JIT, false>), dim3(p.grid), dim3(512),
+        hipLaunchKernelGGL((gemv_i8_sub_kernel<NW, XC, NQ, JIT, false>), dim3(p.grid), dim3(NW * 64),
                            p.lds_bytes, stream, w, x, y, p.n, p.S, p.m, p.rows_per_block,
                            p.cols_per_task / 8);
     }
@@ -774,22 +882,19 @@ hipError_t launch_gemv_mfma(const GemvPlan& p, const void* w, const float* x, fl
             if (nq == 2) return launch_sub<2>(p, wb, x, y, stream);
             return launch_sub<1>(p, wb, x, y, stream);
         }
-        if (nq == 4) return launch_sub_x<1, 4, true>(p, wb, x, y, stream);
+        // four quads: four waves, whose lanes may hold 512 registers (the
+        // x of the next column takes 64 of them)
+        if (nq == 4) return launch_sub_x<1, 4, true, 4>(p, wb, x, y, stream);
         if (nq == 2) return launch_sub_x<1, 2, true>(p, wb, x, y, stream);
         return launch_sub_x<1, 1, true>(p, wb, x, y, stream);
     }
-    switch (p.m) {
-    case 1: break;
-    case 2: return launch_lines_m<2>(p, wb, x, y, stream);
-    case 3: return launch_lines_m<3>(p, wb, x, y, stream);
-    case 4: return launch_lines_m<4>(p, wb, x, y, stream);
-    case 5: return launch_lines_m<5>(p, wb, x, y, stream);
-    case 6: return launch_lines_m<6>(p, wb, x, y, stream);
-    case 7: return launch_lines_m<7>(p, wb, x, y, stream);
-    default: return launch_lines_m<8>(p, wb, x, y, stream);
+    if (p.m == 2) {
+        return launch_lines_m<2>(p, wb, x, y, stream);
+    }
+    if (p.m != 1) {
+        return hipErrorInvalidValue;   // one MFMA group per vector: one or two vectors
     }
     if (p.waves_per_block == 8) return launch_lines<8>(p, wb, x, y, stream);
-    if (p.waves_per_block == 16) return launch_lines_p<16, 3>(p, wb, x, y, stream);
     return launch_lines<4>(p, wb, x, y, stream);
 }
 
@@ -799,15 +904,21 @@ size_t sub_lds_bytes(int S, int m)
     return (size_t)(S * nq + 1) * kSbGroup + (size_t)8 * (S % 8 != 0 ? kRing4Wave : kRingWave);
 }
 
+int jit_waves(int m)
+{
+    return sub_quads(m) == 4 ? 4 : 8;
+}
+
 size_t jit_lds_bytes(int S, int m)
 {
-    const int nq = sub_quads(m);
-    return (size_t)8 * nq * kSbGroup + (size_t)8 * (S % 8 != 0 ? kRing4Wave : kRingWave);
+    const int nw = jit_waves(m);
+    return (size_t)nw * (kSbWord + sub_quads(m) * kSbLists) +
+           (size_t)nw * (S % 8 != 0 ? kRing4Wave : kRingWave);
 }
 
 size_t lines_lds_bytes(int S, int m, int waves)
 {
-    return (size_t)(S * m + 1) * kI8ColBytes + (size_t)waves * kRingWave;
+    return (size_t)(S * m + 1) * kK4Pair + (size_t)waves * kRingWave;
 }
 
 }  // namespace q4k

@@ -146,7 +146,7 @@ typedef struct q4k_launch {
     int32_t spans_per_chunk;  /* K-chunked: spans per stage, >= 1 (0 = automatic)  */
     int32_t rows_per_block;   /* rows per workgroup (0 = automatic)                */
     int32_t rows_per_wave;    /* rows a wave decodes per pass: 0 auto, 1, 2 or 4   */
-    int32_t waves_per_block;  /* 0 auto, 4 or 8; 16 for kernels 2-4 at m = 1       */
+    int32_t waves_per_block;  /* 0 auto, 4 or 8                                    */
     int32_t x_in_registers;   /* 0 auto, 1 keep x in VGPRs (one span, m = 1), 2 LDS */
     int32_t kernel;           /* 0 auto, else 1-6 as listed above                  */
     int32_t ring_depth;       /* loads in flight per wave, 0 auto: streaming 1..4

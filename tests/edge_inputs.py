@@ -190,7 +190,29 @@ def nonfinite_header(n=48, k=1024):
     return Case("inf and NaN as d or dmin", w, x, n, k, strict_kind=False)
 
 
+def wide_magnitudes(n=48, k=2048):
+    """x = N(0,1) * 2^u, u uniform on -40..40 per element: most elements sit
+    far below their sub-block's largest, so most columns hold many values
+    that need their exact terms (more than a short list holds)."""
+    rng = np.random.default_rng(521)
+    w = synth.pack(_fields(522, n, k // 256))
+    x = (rng.standard_normal((2, k)) * np.exp2(rng.integers(-40, 41, size=(2, k)))).astype(np.float32)
+    return Case("x N(0,1) * 2^(-40..40)", w, x, n, k)
+
+
+def few_small(n=48, k=2048):
+    """N(0,1) x where column c (of eight) holds c elements of size 1e-12:
+    zero up to seven values that the grid leaves out per column."""
+    rng = np.random.default_rng(523)
+    w = synth.pack(_fields(524, n, k // 256))
+    x = rng.standard_normal((2, k)).astype(np.float32)
+    for c in range(k // 256):
+        pos = rng.choice(256, size=c, replace=False)
+        x[:, 256 * c + pos] = np.float32(1e-12)
+    return Case("N(0,1) x with 0..7 tiny values per column", w, x, n, k)
+
+
 def all_cases():
     return [tiny_x(), subnormal_x(), huge_x(), overflow_y(), mixed_subblock(),
             mixed_subblock(rest="normal"), outliers(), outliers(big=3.0e9), zero_bound(),
-            near_zero_bound(), nonfinite_x(), nonfinite_header()]
+            near_zero_bound(), nonfinite_x(), nonfinite_header(), wide_magnitudes(), few_small()]

@@ -12,19 +12,20 @@ x representation, per 32-element sub-block of one vector:
   * v = x * 2^sigma (exact in f32 for every element that is not rounded to
     zero), xi = rint(v) (round to nearest even), |xi| < 2^30, written as four
     signed base-256 digits (the bytes of xi + 0x80808080, each minus 128);
-  * an element is certified when it is finite and either xi = 0 = x, or
-    xi != 0 and |v - xi| <= 2^-17 |v| (relative error of the representation
-    at most 2^-17); a sub-block with any uncertified element is "dirty";
+  * an element is certified when x = 0 or 2^16 <= |x 2^sigma| <= 2^30
+    (then |v - xi| <= 1/2 <= 2^-17 |v|); an uncertified element (a value
+    below 2^-13 of the sub-block's largest, inf, NaN) is left out of the
+    digits (xi := 0);
   * per sub-block constants: s = 2^-sigma (f64) and XI = sum xi (exact
-    integer), both 0 for a dirty sub-block.
+    integer, certified elements only).
 
 Per (row, sub-block) with D = d*sc_j and M = dmin*m_j (exact in f32):
-  * clean: T = sum q xi (exact integer from digit sums: low codes q, high
-    codes 16 q - 128 then T = (T' + 128 XI) / 16), then in f64
-    p1 = D*T, e1 = D*T - p1 (exact product error), p2 = M*XI (exact),
+  * T = sum q xi (exact integer from digit sums: low codes q, high codes
+    16 q - 128 then T = (T' + 128 XI) / 16), then in f64 p1 = D*T,
+    e1 = D*T - p1 (exact product error), p2 = M*XI (exact),
     r = (p1 - p2) + e1, contribution r * s;
-  * dirty: contribution sum_e fl32(D q_e - M) * x_e in f64 (the exact
-    weights against the exact x), and the clean formula contributes r * 0.
+  * every uncertified element adds fl32(D q_e - M) * x_e in f64 (its exact
+    weight against its exact x).
 A row's contributions add up in f64; y is that sum rounded once to f32.
 
 Error (finite inputs): each certified element's x error is at most
@@ -64,7 +65,7 @@ class XRep:
         xs = np.asarray(x, np.float32).reshape(-1, 32)
         self.x = xs
         finite = np.isfinite(xs)
-        a = np.where(finite, np.abs(xs), np.float32(0))
+        a = np.minimum(np.where(np.isnan(xs), np.float32(0), np.abs(xs)), np.float32(3.4028235e38))
         mx = a.max(axis=1)
         _, E = np.frexp(mx)
         self.sigma = np.where(mx > 0, 30 - E, 0).astype(np.int64)
@@ -72,14 +73,15 @@ class XRep:
             v = np.ldexp(np.where(finite, xs, np.float32(0)), self.sigma[:, None].astype(np.int32))
         v = v.astype(np.float32)
         xi = np.rint(v).astype(np.float32)
-        res = np.abs(v - xi)
-        cert = finite & np.where(xi == 0, xs == 0, res <= np.float32(CERT_REL) * np.abs(v))
-        self.xi = xi.astype(np.int64)
+        a = np.abs(np.ldexp(xs, self.sigma[:, None].astype(np.int32)).astype(np.float32))
+        cert = ((a >= 65536.0) & (a <= 2.0 ** 30)) | (xs == 0)
+        self.cert = cert
+        self.xi = np.where(cert, xi, 0).astype(np.int64)
         assert np.all(np.abs(self.xi) < 2 ** 30)
-        self.dirty = ~cert.all(axis=1)
+        self.dirty = ~cert.all(axis=1)          # sub-blocks with an uncertified element
         self.uncertified = int((~cert).sum())
-        self.XI = np.where(self.dirty, 0, self.xi.sum(axis=1))
-        self.s = np.where(self.dirty, 0.0, np.ldexp(1.0, -self.sigma))
+        self.XI = self.xi.sum(axis=1)
+        self.s = np.ldexp(1.0, -self.sigma)
         u = (self.xi + 0x80808080).astype(np.uint64)
         assert np.all(u < 2 ** 32)
         self.digits = np.stack([((u >> (8 * l)) & 0xFF).astype(np.int64) - 128
@@ -139,12 +141,12 @@ def gemv(w: np.ndarray, x: np.ndarray, n: int):
             p2 = M.astype(np.float64) * XI[None]
             r = (p1 - p2) + e1
             acc = (r * s[None]).sum(axis=(1, 2))
-            # dirty sub-blocks: exact weights against exact x
-            if rep.dirty.any():
+            # uncertified elements: exact weights against exact x
+            if rep.uncertified:
                 xs = rep.x.reshape(S, 8, 32)
-                ds = rep.dirty.reshape(S, 8)
+                unc = ~rep.cert.reshape(S, 8, 32)
                 w32 = (D[..., None] * qsb.astype(np.float32) - M[..., None]).astype(np.float32)
-                prod = w32.astype(np.float64) * xs[None].astype(np.float64)
-                acc = acc + np.where(ds[None, :, :, None], prod, 0.0).sum(axis=(1, 2, 3))
+                prod = w32.astype(np.float64) * np.where(unc, xs, 0)[None].astype(np.float64)
+                acc = acc + np.where(unc[None], prod, 0.0).sum(axis=(1, 2, 3))
         y[b] = acc.astype(np.float32)
     return y, dirty

@@ -187,7 +187,8 @@ def test_plan_info_struct_matches_header():
     (256, 1024, 1, True, 2, 32, 0),
     (32000, 4096, 1, False, 2, None, 0),    # weights not 128-byte aligned
     (32000, 4096, 2, True, 4, 250, 16),     # m = 2: line MFMA
-    (14336, 4096, 8, True, 5, 224, 8),      # m >= 3: sub-block MFMA, x staged whole
+    (14336, 4096, 4, True, 5, 224, 8),      # m >= 3: sub-block MFMA, x staged whole
+    (14336, 4096, 8, True, 6, 224, 8),      # x of 8 vectors does not fit one stage
     (4096, 14336, 8, True, 6, 256, 8),      # x of 8 columns does not fit: per-wave x
     (4096, 11008, 8, True, 6, 256, 8),      # partial slab (43 superblocks)
     (14336, 4096, 8, False, 1, None, 0),
@@ -214,14 +215,20 @@ def test_plan_follows_options_and_lds_limit():
     assert p.kernel == 4
     p = q4k.q4k_plan(32000, 4096, 1, lds_max=MI355X_LDS, kernel=3, cols_per_task=8)
     assert p.kernel == 3 and p.cols_per_task == 8
-    # the whole-x stage of kernel 5 (150848 bytes here) does not fit in 64 KiB:
-    # the automatic choice moves on to per-wave x
+    # the whole-x stage of kernel 5 for eight vectors (33 groups of 4752
+    # bytes and eight rings of 4352) exceeds the LDS: the automatic choice
+    # moves on to per-wave x (per wave one group's digits and constants, 4608
+    # bytes, and two quads' lists of 144; eight rings; f64 row sums of two
+    # slab groups of 64 rows)
     p = q4k.q4k_plan(14336, 4096, 8, lds_max=MI355X_LDS)
-    assert p.kernel == 5 and p.lds_bytes == 150848
-    p = q4k.q4k_plan(14336, 4096, 4, lds_max=65536)
-    assert p.kernel == 6 and p.lds_bytes <= 65536
+    assert p.kernel == 6 and p.lds_bytes == 8 * (4608 + 2 * 144) + 8 * 4352 + 2 * 64 * 8 * 8
+    # four vectors: 17 groups and the rings fit 160 KiB, not 96 KiB
+    p = q4k.q4k_plan(14336, 4096, 4, lds_max=MI355X_LDS)
+    assert p.kernel == 5
+    p = q4k.q4k_plan(14336, 4096, 4, lds_max=98304)
+    assert p.kernel == 6 and p.lds_bytes <= 98304
     with pytest.raises(q4k.Q4KError) as ei:
-        q4k.q4k_plan(14336, 4096, 8, lds_max=65536, kernel=5)
+        q4k.q4k_plan(14336, 4096, 8, lds_max=MI355X_LDS, kernel=5)
     assert ei.value.rc == q4k.Q4K_ERR_UNSUPPORTED
 
 
@@ -241,9 +248,11 @@ def test_plan_refusals(lib):
 
 @pytest.mark.parametrize("n,k,m,kernel", [
     (4096, 14336, 16, 6),     # x per column per wave
-    (300, 2048, 12, 5),       # sixteen vectors' x fits one stage
-    (17, 1280, 13, 5),        # partial slab, whole stage
-    (5, 256, 16, 5),
+    (300, 2048, 12, 6),
+    (17, 1280, 13, 6),        # partial slabs
+    (130, 11008, 16, 6),
+    (5, 256, 16, 5),          # sixteen vectors' x fits one stage
+    (3, 768, 9, 5),
     (14336, 4096, 16, 6),
     (14336, 4096, 9, 6),
     (32000, 4096, 16, 6),
@@ -256,7 +265,6 @@ def test_plan_wide_batches(n, k, m, kernel):
 
 
 @pytest.mark.parametrize("n,k,m,aligned", [
-    (130, 11008, 16, True),   # the sixteen-vector plan exceeds the LDS
     (14336, 4096, 9, False),  # weights not 128-byte aligned
     (64, 4096, 12, False),
 ])
@@ -275,10 +283,11 @@ def test_plan_wide_batch_refusals():
         with pytest.raises(q4k.Q4KError) as ei:
             q4k.q4k_plan(14336, 4096, 9, lds_max=MI355X_LDS, **opts)
         assert ei.value.rc == q4k.Q4K_ERR_UNSUPPORTED
-    # rows of partial slabs whose x of 16 vectors does not fit one stage:
-    # kernel 6's four-line rings and four quads exceed the LDS
+    # kernel 6 with more than eight vectors runs four waves only
     with pytest.raises(q4k.Q4KError) as ei:
-        q4k.q4k_plan(130, 11008, 16, lds_max=MI355X_LDS, kernel=6)
+        q4k.q4k_plan(14336, 4096, 16, lds_max=MI355X_LDS, kernel=6, waves_per_block=8)
     assert ei.value.rc == q4k.Q4K_ERR_UNSUPPORTED
     p = q4k.q4k_plan(14336, 4096, 16, lds_max=MI355X_LDS, kernel=6)
-    assert p.kernel == 6
+    assert p.kernel == 6 and p.threads == 256
+    p = q4k.q4k_plan(14336, 4096, 8, lds_max=MI355X_LDS, kernel=6)
+    assert p.threads == 512

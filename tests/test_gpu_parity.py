@@ -15,6 +15,8 @@ import pytest
 
 torch = pytest.importorskip("torch")
 
+import checks  # noqa: E402
+
 from block_quantized_decode_q4_amd import q4k, synth  # noqa: E402
 
 pytestmark = pytest.mark.gpu
@@ -50,16 +52,9 @@ def run_gemv(w_d, x_np, n, k, m, **opts):
 
 
 def assert_within(y, y_ref, bound, what):
-    assert y.shape == y_ref.shape
-    assert np.all(np.isfinite(y)), what
-    err = np.abs(y.astype(np.float64) - y_ref)
-    bad = err > TOL * bound
-    if np.any(bad):
-        i = np.argwhere(bad)[0]
-        raise AssertionError("%s: %d outputs out of tolerance, first %s: y=%r ref=%r bound=%r"
-                             % (what, int(bad.sum()), tuple(i), y[tuple(i)], y_ref[tuple(i)],
-                                bound[tuple(i)]))
-    return float((err / np.maximum(bound, 1e-300)).max())
+    """The rule of tests/checks.py: within 1e-5 * sum|w||x| of every finite
+    exact result (a NaN or infinity in y fails), non-finite where it is."""
+    return checks.assert_y(y, y_ref, bound, what)
 
 
 _cache = {}
@@ -124,10 +119,10 @@ VARIANTS = [
 STREAM_VARIANTS = [
     dict(kernel=2),
     dict(kernel=2, ring_depth=2, rows_per_task=7),
-    dict(kernel=2, ring_depth=2, rows_per_task=64, waves_per_block=16),
+    dict(kernel=2, ring_depth=2, rows_per_task=64, waves_per_block=4),
     dict(kernel=2, ring_depth=4, rows_per_task=16, waves_per_block=8),
     dict(kernel=2, ring_depth=3, rows_per_task=1, waves_per_block=4, rows_per_block=3),
-    dict(kernel=2, ring_depth=1, rows_per_task=3, waves_per_block=16),
+    dict(kernel=2, ring_depth=1, rows_per_task=3, waves_per_block=8),
     dict(kernel=2, variant=2, spans_per_chunk=1, rows_per_task=5, rows_per_block=37),
     dict(kernel=2, variant=1, rows_per_task=33, rows_per_block=200),
 ]
@@ -186,7 +181,7 @@ def _lines_auto_cols(n, k, m, opts):
     ntiles = (n + 15) // 16
     rpb = opts.get("rows_per_block") or 16 * ((ntiles + 255) // 256)
     nw = opts.get("waves_per_block", 8)
-    fits = (S * m + 1) * 960 + nw * 4352 + (S // 8) * rpb * 4 * m <= 160 * 1024
+    fits = (S * m + 1) * 1264 + nw * 4352 + (S // 8) * rpb * 8 * m <= 160 * 1024
     return S if (rpb // 16 >= nw or not fits) else 8
 
 
@@ -199,11 +194,15 @@ def _lines_check(w_d, w, x, n, k, y_ref, bound, what):
             y = run_gemv(w_d, x, n, k, 1, **opts)
         except q4k.Q4KError as e:
             # refused: a task's column group must divide the slabs of a row,
-            # and the whole staged x (960 bytes per superblock column) plus
-            # the line rings (4352 bytes per wave) must fit the 160 KiB LDS
+            # the whole staged x (1264 bytes per superblock column) plus the
+            # line rings (4352 bytes per wave) and row sums must fit the
+            # 160 KiB LDS; 16-wave workgroups are refused
             nw = opts.get("waves_per_block", 8)
             bad_group = "cols_per_task" in opts and (S // 8) % (opts["cols_per_task"] // 8) != 0
-            too_big = (S + 1) * 960 + nw * 4352 > 160 * 1024
+            ncg = (S // 8) // (opts["cols_per_task"] // 8) if "cols_per_task" in opts else 1
+            rpb = opts.get("rows_per_block", 16 * (((n + 15) // 16 + 255) // 256))
+            ysum = ncg * rpb * 8 if ncg > 1 else 0
+            too_big = (S + 1) * 1264 + nw * 4352 + ysum > 160 * 1024 or nw == 16
             assert e.rc == q4k.Q4K_ERR_UNSUPPORTED and (bad_group or too_big), opts
             continue
         assert_within(y, y_ref, bound, "%s line-streamed %r" % (what, opts))
@@ -228,10 +227,9 @@ def test_lines_kernel_shapes(oracle_mod, n, k):
     _lines_check(dev(w), w, x, n, k, y_ref, bound, "n=%d k=%d" % (n, k))
 
 
-@pytest.mark.parametrize("n,k,m", [(300, 4096, 2), (17, 2048, 3), (130, 4096, 8), (64, 4096, 5),
-                                   (33, 2048, 8), (40, 16384, 2)])
+@pytest.mark.parametrize("n,k,m", [(300, 4096, 2), (33, 2048, 2), (40, 8192, 2), (130, 6144, 2)])
 def test_lines_kernel_batched(oracle_mod, n, k, m):
-    """m vectors in one launch: within tolerance, and bit-identical to m
+    """Two vectors in one launch: within tolerance, and bit-identical to two
     single-vector launches of the same kernel (each vector's sums run in
     the same order)."""
     w, x = synth.make_inputs(n, k, m, seed=n * 31 + k + m)
@@ -246,18 +244,21 @@ def test_lines_kernel_batched(oracle_mod, n, k, m):
 
 
 def test_lines_kernel_batched_workload(oracle_mod):
+    """The batched workload's vectors two at a time on the per-vector
+    matrix-core kernel (one MFMA group per vector takes at most two)."""
     wl, w, x, y_ref, bound = workload(4, oracle_mod)
     w_d = dev(w)
-    _say("line-streamed batched workload 4")
-    y = run_gemv(w_d, x, wl.n, wl.k, wl.m, kernel=4)
-    assert_within(y, y_ref, bound, "line-streamed workload 4")
-    for b in range(wl.m):
-        y1 = run_gemv(w_d, x[b:b + 1], wl.n, wl.k, 1, kernel=4)
-        assert np.array_equal(y1[0].view(np.uint32), y[b].view(np.uint32)), b
+    _say("line-streamed batched workload 4, two vectors per launch")
+    with pytest.raises(q4k.Q4KError) as e:
+        run_gemv(w_d, x, wl.n, wl.k, wl.m, kernel=4)
+    assert e.value.rc == q4k.Q4K_ERR_UNSUPPORTED
+    for b in range(0, wl.m, 2):
+        y2 = run_gemv(w_d, x[b:b + 2], wl.n, wl.k, 2, kernel=4)
+        assert_within(y2, y_ref[b:b + 2], bound[b:b + 2], "line-streamed workload 4 pair %d" % b)
 
 
-@pytest.mark.parametrize("n,k,m", [(300, 4096, 1), (300, 4096, 2), (17, 2048, 3), (130, 4096, 8),
-                                   (64, 4096, 5), (33, 2048, 8), (40, 8192, 4), (1, 2048, 6)])
+@pytest.mark.parametrize("n,k,m", [(300, 4096, 1), (300, 4096, 2), (17, 2048, 3), (130, 2048, 8),
+                                   (64, 2048, 5), (33, 2048, 8), (40, 4096, 4), (1, 2048, 6)])
 def test_sub_kernel(oracle_mod, n, k, m):
     """The sub-block kernel: within tolerance, bit-identical to m
     single-vector launches of itself, and across workgroup shapes with the
@@ -279,10 +280,18 @@ def test_sub_kernel(oracle_mod, n, k, m):
 
 
 def test_sub_kernel_workload(oracle_mod):
+    """The batched workload (14336 x 4096, eight vectors): its whole x stage
+    (33 groups of 4752 bytes) and the rings exceed the LDS, so kernel 5 is
+    refused and the automatic plan takes kernel 6."""
     wl, w, x, y_ref, bound = workload(4, oracle_mod)
-    _say("sub-block kernel workload 4")
-    y = run_gemv(dev(w), x, wl.n, wl.k, wl.m, kernel=5)
-    assert_within(y, y_ref, bound, "sub-block workload 4")
+    _say("sub-block kernels workload 4")
+    with pytest.raises(q4k.Q4KError) as ei:
+        run_gemv(dev(w), x, wl.n, wl.k, wl.m, kernel=5)
+    assert ei.value.rc == q4k.Q4K_ERR_UNSUPPORTED
+    y = run_gemv(dev(w), x, wl.n, wl.k, wl.m)
+    assert_within(y, y_ref, bound, "automatic workload 4")
+    y6 = run_gemv(dev(w), x, wl.n, wl.k, wl.m, kernel=6)
+    assert np.array_equal(y6.view(np.uint32), y.view(np.uint32))
 
 
 # kernel 6: the sub-block decode with x converted one superblock column at a
@@ -312,7 +321,7 @@ def test_jit_kernel(oracle_mod, n, k, m):
     else:
         assert np.array_equal(y5.view(np.uint32), y.view(np.uint32))
     for opts in (dict(rows_per_block=48, cols_per_task=8), dict(rows_per_block=16, cols_per_task=8),
-                 dict(rows_per_block=200, cols_per_task=8)):
+                 dict(rows_per_block=100, cols_per_task=8)):
         y2 = run_gemv(w_d, x, n, k, m, kernel=6, **opts)
         assert np.array_equal(y2.view(np.uint32), y.view(np.uint32)), opts
     y3 = run_gemv(w_d, x, n, k, m, kernel=6, cols_per_task=k // 256)
@@ -400,7 +409,7 @@ def _dot4_auto_cols(n, k, opts):
     ntiles = (n + 15) // 16
     rpb = opts.get("rows_per_block") or 16 * ((ntiles + 255) // 256)
     nw = opts.get("waves_per_block", 8)
-    fits = S * 1088 + nw * _dot4_ring(S) + nslabs * rpb * 4 <= 160 * 1024
+    fits = S * 1200 + nw * _dot4_ring(S) + nslabs * rpb * 8 <= 160 * 1024
     return 8 * nslabs if (rpb // 16 >= nw or not fits) else 8
 
 
@@ -421,12 +430,18 @@ def _dot4_check(w_d, x, n, k, y_ref, bound, what):
             y = run_gemv(w_d, x, n, k, 1, **opts)
         except q4k.Q4KError as e:
             # refused: a task's column group must divide the slabs of a row,
-            # the staged x (1088 bytes per superblock column) plus the line
-            # rings must fit the 160 KiB LDS, x takes at most four
+            # the staged x (1200 bytes per superblock column) plus the line
+            # rings and row sums must fit the 160 KiB LDS, x takes at most four
+            # groups per lane, 16-wave workgroups are refused
             # 16-element groups per lane, rows of partial slabs keep three
             # lines in flight
             bad_group = "cols_per_task" in opts and nslabs % (opts["cols_per_task"] // 8) != 0
-            too_big = S * 1088 + nw * _dot4_ring(S) > 160 * 1024 or S * 16 > 4 * 64 * nw
+            # staged x: 1200 bytes per column; f64 row sums per slab group
+            ncg = nslabs // (opts["cols_per_task"] // 8) if "cols_per_task" in opts else 1
+            rpb = opts.get("rows_per_block", 16 * (((n + 15) // 16 + 255) // 256))
+            ysum = ncg * rpb * 8 if ncg > 1 else 0
+            too_big = (S * 1200 + nw * _dot4_ring(S) + ysum > 160 * 1024
+                       or S * 16 > 4 * 64 * nw or nw == 16)
             bad_ring = S % 8 != 0 and opts.get("ring_depth", 3) != 3
             assert e.rc == q4k.Q4K_ERR_UNSUPPORTED and (bad_group or too_big or bad_ring), opts
             continue
@@ -522,11 +537,16 @@ def test_lines_kernel_refusals():
     with pytest.raises(q4k.Q4KError) as e:
         q4k.q4k_gemv_ex(dev(w2), dev(x2), y_d, n, 1024, 1, kernel=4)
     assert e.value.rc == q4k.Q4K_ERR_UNSUPPORTED
-    # staged x of every vector must fit the LDS: 32 columns x 5 vectors do not
+    # at most two vectors, and the staged x of every vector must fit the
+    # LDS: 72 columns x 2 vectors do not
     w3, x3 = synth.make_inputs(n, 8192, 5, seed=7)
     y3 = torch.zeros((5, n), dtype=torch.float32, device="cuda")
     with pytest.raises(q4k.Q4KError) as e:
         q4k.q4k_gemv_ex(dev(w3), dev(x3), y3, n, 8192, 5, kernel=4)
+    assert e.value.rc == q4k.Q4K_ERR_UNSUPPORTED
+    w4, x4 = synth.make_inputs(n, 18432, 2, seed=8)
+    with pytest.raises(q4k.Q4KError) as e:
+        q4k.q4k_gemv_ex(dev(w4), dev(x4), y3, n, 18432, 2, kernel=4)
     assert e.value.rc == q4k.Q4K_ERR_UNSUPPORTED
     torch.cuda.synchronize()
     assert torch.count_nonzero(y3).item() == 0
@@ -603,13 +623,12 @@ def test_batched_equals_separate_calls(oracle_mod, m):
 
 
 def test_batched_workload_against_separate(oracle_mod):
-    """The batched workload: the automatic kernel (line-streamed) and the
-    x-stager kernel, each bit-identical to m single-vector launches of
-    itself."""
+    """The batched workload: the automatic kernel (sub-block, per-wave x)
+    and the x-stager kernel, each bit-identical to m single-vector launches
+    of itself."""
     wl, w, x, y_ref, bound = workload(4, oracle_mod)
     w_d = dev(w)
-    for opts, single in ((dict(), dict(kernel=5)), (dict(kernel=4), dict(kernel=4)),
-                         (dict(kernel=1), dict(kernel=1))):
+    for opts, single in ((dict(), dict(kernel=6)), (dict(kernel=1), dict(kernel=1))):
         _say("batched workload 4 %r" % opts)
         yb = run_gemv(w_d, x, wl.n, wl.k, wl.m, **opts)
         assert_within(yb, y_ref, bound, "batched workload %r" % opts)

@@ -27,20 +27,21 @@ def test_model_workload_distribution(oracle_mod, seed):
     worst = checks.assert_y(y, y_ref, bound, "workload distribution")
     assert worst < 1e-6
     # N(0,1) x: about 0.4 % of sub-blocks hold an element below 2^-14 of
-    # their largest |x| that the representation does not carry to 2^-17
+    # their largest |x| that the grid does not carry to 2^-17
     assert sum(dirty) <= 0.03 * m * k // 32
 
 
 def test_model_certification_is_needed(oracle_mod):
-    """Without the dirty sub-blocks' exact path (x rounded to the 31-bit grid
-    everywhere) the mixed-magnitude case breaks the bound: the check is what
-    carries the guarantee, not the digit count."""
+    """Without the exact terms of uncertified elements (x rounded to the
+    31-bit grid everywhere) the mixed-magnitude case breaks the bound: the
+    check is what carries the guarantee, not the digit count."""
     case = edge_inputs.mixed_subblock(rest="normal")
     y_ref, bound = oracle_mod.gemv(case.w, case.x, case.n)
     rep = kernel_model.XRep(case.x[0])
     assert rep.dirty[0] and rep.dirty.sum() == 1
-    # the grid value of every element, as a dirty-free kernel would use it
-    xg = (rep.xi * np.ldexp(1.0, -rep.sigma)[:, None]).reshape(-1).astype(np.float64)
+    # the grid value of every element, as a kernel without the check would use it
+    v = np.ldexp(case.x[0].reshape(-1, 32).astype(np.float64), rep.sigma[:, None])
+    xg = (np.rint(v) * np.ldexp(1.0, -rep.sigma)[:, None]).reshape(-1)
     wd = oracle_mod.dequant(case.w, case.n, case.k).astype(np.float64)
     err = np.abs(wd @ xg - y_ref[0])
     assert np.any(err > 1e-5 * bound[0])
@@ -55,6 +56,10 @@ def test_model_digits_and_grid():
     assert np.all(np.abs(rep.digits) <= 128)
     rebuilt = (rep.digits * (256 ** np.arange(4))).sum(axis=-1)
     assert np.array_equal(rebuilt, rep.xi)
-    top = np.abs(rep.xi).max(axis=1)
+    # the grid of each sub-block: its largest |x| (certified or not) lands in
+    # [2^29, 2^30); an uncertified element has xi = 0
+    assert np.all(rep.xi[~rep.cert] == 0)
+    v = np.ldexp(np.abs(rep.x).astype(np.float64), rep.sigma[:, None])
+    top = np.rint(np.where(np.isfinite(v), v, 0)).max(axis=1)
     nz = top > 0
     assert np.all((top[nz] >= 2 ** 29 - 1) & (top[nz] <= 2 ** 30))
