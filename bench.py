@@ -7,8 +7,8 @@ decode, dot, reduction and store all happen inside it) over one copy of the
 weights.  To measure HBM and not the 256 MB last-level cache, the weights are
 replicated into >= 1 GiB of distinct copies and the steps cycle through them.
 Inputs are resident in HBM before timing starts.  W untimed warm-up steps,
-then exactly K steps between two HIP events on the launch stream, bracketed
-by device synchronisation.  The defaults (20000 and 20000, about 0.3 s each
+then exactly K steps between HIP events on the launch stream (seven batches,
+events between them), bracketed by device synchronisation.  The defaults (20000 and 20000, about 0.3 s each
 on the LM head) let the GPU's clocks settle before the timed region: a few
 hundred warm-up steps leave the first milliseconds of the timed region 2-5 %
 slower on MI355X.
@@ -72,14 +72,26 @@ def committed_traffic(workload_name: str):
     return float(tb.group(1))
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, x, n, k, m, weight_bytes, y_gpu, target_s=12.0):
     """Time the CPU oracle on the whole workload, repeated for about
-    `target_s` seconds of CPU work (median run), and check the GPU output
-    against it."""
+    `target_s` seconds of CPU work after one warm-up run (median run), on
+    all the threads OpenMP takes, then once more on one thread; check the
+    GPU output against it."""
     import numpy as np
     import oracle
 
     threads = oracle.num_threads()
+    y_ref, bound = oracle.gemv(w, x, n)           # warm-up
     times = []
     t_total = time.time()
     while True:
@@ -91,17 +103,51 @@ def cpu_baseline(w, x, n, k, m, weight_bytes, y_gpu, target_s=12.0):
         if len(times) >= 5000:
             break
     t_med = sorted(times)[len(times) // 2]
+    # one thread: the same workload, median of three runs
+    oracle.set_num_threads(1)
+    try:
+        t1 = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            oracle.gemv(w, x, n)
+            t1.append(time.perf_counter() - t0)
+    finally:
+        oracle.set_num_threads(threads)
+    t1_med = sorted(t1)[1]
     err = np.abs(y_gpu.astype(np.float64) - y_ref) / np.maximum(bound, 1e-300)
     return {
         "value": weight_bytes / t_med / 1e9,
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": "whole workload (%d x %d, m=%d) repeated for %.1f s, median of %d runs, "
-                  "f32 dequant + f64 dot, OpenMP over rows" % (n, k, m, sum(times), len(times)),
+        "sample": "whole workload (%d x %d, m=%d) repeated for %.1f s after one warm-up run, "
+                  "median of %d runs, f32 dequant + f64 dot, OpenMP over rows"
+                  % (n, k, m, sum(times), len(times)),
+        "cpu_model": cpu_model(),
         "gemv_per_s": 1.0 / t_med,
+        "one_thread": {"value": weight_bytes / t1_med / 1e9, "unit": "GB/s",
+                       "gemv_per_s": 1.0 / t1_med, "sample": "the same workload, median of 3 runs"},
         "gpu_max_err_over_bound": float(err.max()),
     }
+
+
+KERNEL_NAMES = {1: "gemv_kernel", 2: "gemv_stream_kernel", 3: "gemv_dot4_lines_kernel",
+                4: "gemv_i8_lines_kernel", 5: "gemv_i8_sub_kernel (x staged)",
+                6: "gemv_i8_sub_kernel (x per wave)"}
+
+# The arithmetic each kernel computes in (the plan's kernel number)
+KERNEL_DTYPE = {
+    1: ("f32-x/f64", "x f32; each weight fl32(d sc q - dmin m) as the format defines it; "
+                     "products exact and sums in f64; y rounded once to f32"),
+    2: ("f32-x/f64", "as kernel 1 (streaming kernel)"),
+    3: ("i8x4-x/i32/f64", "x as four int8 digits of a per-32-element integer grid (values far "
+                          "below their sub-block's largest, inf and NaN added exactly); int32 "
+                          "dot4 sums; per sub-block D T - M XI rounded once in f64; y rounded "
+                          "once to f32"),
+    4: ("i8x4-x/i32/f64", "as kernel 3, digit sums on int8 matrix cores (16x16x64)"),
+    5: ("i8x4-x/i32/f64", "as kernel 3, digit sums on int8 matrix cores (16x16x32), x staged whole"),
+    6: ("i8x4-x/i32/f64", "as kernel 5, x converted per column by each wave"),
+}
 
 
 def main() -> int:
@@ -166,16 +212,23 @@ def main() -> int:
         step(i)
     torch.cuda.synchronize()
 
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
+    # the K timed steps in 7 batches: events between the batches, so that the
+    # median batch is reported beside the mean over the whole region
+    nb = 7 if args.steps >= 7 else 1
+    bounds = [round(i * args.steps / nb) for i in range(nb + 1)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(nb + 1)]
     torch.cuda.synchronize()
-    start.record(stream)
-    for i in range(args.steps):
-        step(args.warmup + i)
-    end.record(stream)
+    ev[0].record(stream)
+    for b in range(nb):
+        for i in range(bounds[b], bounds[b + 1]):
+            step(args.warmup + i)
+        ev[b + 1].record(stream)
     torch.cuda.synchronize()
-    ms = start.elapsed_time(end)
+    ms = ev[0].elapsed_time(ev[nb])
     t_launch = ms / 1e3 / args.steps
+    batch_us = sorted(ev[b].elapsed_time(ev[b + 1]) * 1e3 / (bounds[b + 1] - bounds[b])
+                      for b in range(nb))
+    t_median = batch_us[nb // 2] / 1e6
     y_last = y_d.cpu().numpy()
     log("bench: %.3f us per GEMV over %d steps" % (t_launch * 1e6, args.steps))
 
@@ -195,10 +248,26 @@ def main() -> int:
     c1.record(stream)
     torch.cuda.synchronize()
     read_gbps = total * reps / (c0.elapsed_time(c1) / 1e3) / 1e9
+    # the same read at the GEMV's size: one weight copy per launch, cycling
+    # through the copies as the steps do (the ceiling a launch of this size
+    # reaches with plain loads)
+    wbr = wb - wb % 16
+    one_reps = max(50, min(2000, args.steps))
+    for i in range(20):
+        q4k.q4k_read_calibrate(ptrs[i % copies], wbr, cal_out, stream=sp)
+    torch.cuda.synchronize()
+    c0.record(stream)
+    for i in range(one_reps):
+        q4k.q4k_read_calibrate(ptrs[i % copies], wbr, cal_out, stream=sp)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    one_us = c0.elapsed_time(c1) * 1e3 / one_reps
 
     alg_bytes = wb + 4 * k * m + 4 * n * m
     achieved = alg_bytes / t_launch / 1e9
     traffic = committed_traffic(wl.name)
+    plan = q4k.q4k_plan(n, k, m)
+    dtype, numerics = KERNEL_DTYPE[plan.kernel]
     out = {
         "metric": METRIC,
         "value": round(wb / t_launch / 1e9, 2),
@@ -210,7 +279,8 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": dtype,
+        "numerics": numerics,
         "data": "synthetic",
         "config": {
             "workload": wl.name,
@@ -223,7 +293,10 @@ def main() -> int:
         },
         "pct_of_hbm_peak": round(100.0 * wb / t_launch / 1e9 / HBM_PEAK_GBPS, 2),
         "gemv_per_s": 1.0 / t_launch,
+        "median_batch": {"us_per_step": round(t_median * 1e6, 3), "batches": nb,
+                         "value": round(wb / t_median / 1e9, 2)},
         "roofline": {
+            "kernel": KERNEL_NAMES.get(plan.kernel, str(plan.kernel)),
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
@@ -232,7 +305,9 @@ def main() -> int:
             "traffic": traffic,
         },
         "calibration": {"read_gbps": round(read_gbps, 2),
-                        "frac_of_peak": round(read_gbps / HBM_PEAK_GBPS, 4)},
+                        "frac_of_peak": round(read_gbps / HBM_PEAK_GBPS, 4),
+                        "read_one_copy_us": round(one_us, 3),
+                        "read_one_copy_gbps": round(wbr / one_us / 1e3, 2)},
     }
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle")

@@ -78,15 +78,17 @@ int device_lds_max(size_t* out)
 // 5 and 6 m <= 16):
 // kernel 3 (m = 1, integer dot products on the vector ALU, any k), kernel 4
 // (one MFMA group per vector; k a multiple of 2048), kernel 5 (one MFMA per
-// sub-block and quad of vectors) and kernel 6 (kernel 5 with x converted per
-// column by each wave).  A task is a 16-row tile times a group of slabs of
-// eight superblock columns (the last slab of a row may be partial); x
-// (every vector) is staged whole, except for kernel 6.
+// sub-block and quad of vectors), kernel 6 (kernel 5 with x converted per
+// column by each wave) and kernel 7 (kernel 5 with x converted by the
+// workgroup one column ahead into a two-column window of every slab; at most
+// one task of one slab per wave).  A task is a 16-row tile times a group of
+// slabs of eight superblock columns (the last slab of a row may be partial);
+// x (every vector) is staged whole, except for kernels 6 and 7.
 int make_plan_lines(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t lds_max,
                     GemvPlan* p, int kernel)
 {
     const int S = (int)(k / q4k::kQK);
-    if (S % 8 != 0 && kernel == 4) {
+    if (S % 8 != 0 && (kernel == 4 || kernel == 7)) {
         return Q4K_ERR_UNSUPPORTED;    // rows of whole slabs (kernels 3, 5, 6: any rows)
     }
     if (m > q4k::kMaxM && kernel < 5) {
@@ -121,6 +123,13 @@ int make_plan_lines(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t
         return Q4K_ERR_UNSUPPORTED;    // one vector; x in at most four groups per lane;
                                        // rows of any length: three lines in flight
     }
+    // kernel 7: at most one window pair (slab, vector quad) per wave; one
+    // slab per task and a task for at most every wave
+    const int quads = m > 8 ? 4 : m > 4 ? 2 : 1;
+    if (kernel == 7 && (nslabs * quads > nw || nslabs > nw ||
+                        (o && o->cols_per_task && o->cols_per_task != 8))) {
+        return Q4K_ERR_UNSUPPORTED;
+    }
     const int64_t ntiles = (n + 15) / 16;
     int64_t spt = 1;
     if (o && o->cols_per_task) {
@@ -132,16 +141,24 @@ int make_plan_lines(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t
     int64_t rpb;
     if (o && o->rows_per_block > 0) {
         rpb = o->rows_per_block;
+        if (kernel == 7 && (rpb + 15) / 16 * nslabs > nw) {
+            return Q4K_ERR_UNSUPPORTED;
+        }
+    } else if (kernel == 7) {
+        rpb = 16 * (nw / nslabs);            // a task for every wave
     } else {
         // at most about one workgroup per CU of a 256-CU part: each stages
         // all of x, which costs as much as decoding a few tiles
         rpb = 16 * ((ntiles + 255) / 256);
     }
-    const size_t lds_x = kernel == 6   ? q4k::jit_lds_bytes(S, (int)m)
+    const size_t lds_x = kernel == 7   ? q4k::win_lds_bytes(S, (int)m)
+                         : kernel == 6 ? q4k::jit_lds_bytes(S, (int)m)
                          : kernel == 5 ? q4k::sub_lds_bytes(S, (int)m)
                          : kernel == 3 ? q4k::dot4_lds_bytes(S, nw)
                                        : q4k::lines_lds_bytes(S, (int)m, nw);
-    if (!(o && o->cols_per_task)) {
+    if (kernel == 7) {
+        spt = 1;
+    } else if (!(o && o->cols_per_task)) {
         // whole rows per task when the workgroup has a tile for every wave
         // (no row sums to combine), else one slab per task, so that every
         // wave streams; whole rows too when the per-slab row sums do not fit
@@ -186,8 +203,8 @@ int make_plan_lines(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t
 // x, the line rings) fits; kernel 4 also needs k a multiple of 2048.  m > 1:
 // the sub-block kernel (5, m >= 3) or the per-vector line-streamed kernel
 // (4, m = 2), the other one if only it fits, then the sub-block kernel with
-// per-wave x (6), else the x-stager kernel (1, m <= 8; 9-16 vectors are
-// refused there).
+// a column window (7), then with per-wave x (6), else the x-stager kernel
+// (1, m <= 8; 9-16 vectors are refused there).
 // m = 1: the line-streamed vector-ALU kernel (3) where it applies and the
 // weights take at least 16 MiB, else the streaming kernel, whose shorter
 // start wins on smaller matrices; m = 1 takes the matrix cores only when
@@ -207,11 +224,11 @@ int auto_kernel(int64_t n, int64_t k, int64_t m, const q4k_launch* o, bool w_ali
     GemvPlan lp;
     if (m != 1) {
         // several vectors: a line-streamed kernel whenever one applies; the
-        // sub-block kernel from three vectors on; per-wave x conversion when
-        // no whole x stage fits the LDS
+        // sub-block kernel from three vectors on; when no whole x stage fits
+        // the LDS, the workgroup's column window, else per-wave x conversion
         if (!any_option(o) && w_aligned128) {
             const int first = m >= 3 ? 5 : 4;
-            for (int kern : {first, 9 - first, 6}) {
+            for (int kern : {first, 9 - first, 7, 6}) {
                 if (make_plan_lines(n, k, m, nullptr, lds_max, &lp, kern) == Q4K_OK &&
                     lp.lds_bytes <= lds_max) {
                     return kern;
@@ -257,7 +274,7 @@ int make_plan(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t lds_m
     const int nchunks = (nspans + spc - 1) / spc;
 
     const int kernel = (o && o->kernel) ? o->kernel : auto_kernel(n, k, m, o, w_aligned128, lds_max);
-    if (kernel < 1 || kernel > 6 || ((kernel == 2 || kernel == 3) && m != 1) ||
+    if (kernel < 1 || kernel > 7 || ((kernel == 2 || kernel == 3) && m != 1) ||
         (kernel == 1 && m > q4k::kMaxM)) {
         return Q4K_ERR_UNSUPPORTED;
     }

@@ -15,7 +15,7 @@ constexpr int kSpanSB = 16;       // superblocks per wave pass (4 lanes each)
 constexpr int kSpan = kSpanSB * kQK;
 constexpr int kMaxM = 8;         // vectors per launch that every kernel takes
 constexpr int kMaxMWide = 16;    // the sub-block matrix-core kernels 5 and 6
-constexpr int kReadBlocks = 4096;
+constexpr int kReadBlocks = 512;     // two 1024-lane workgroups per CU of a 256-CU part
 
 // One resolved launch of the GEMV kernel.
 struct GemvPlan {
@@ -46,6 +46,7 @@ size_t lines_lds_bytes(int S, int m, int waves);
 size_t sub_lds_bytes(int S, int m);
 size_t jit_lds_bytes(int S, int m);
 int jit_waves(int m);      // waves per workgroup of kernel 6 for m vectors
+size_t win_lds_bytes(int S, int m);
 hipError_t launch_gemv_dot4(const GemvPlan& p, const void* w, const float* x, float* y,
                             hipStream_t stream);
 size_t dot4_lds_bytes(int S, int waves);

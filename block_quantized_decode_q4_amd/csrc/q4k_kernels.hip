@@ -536,9 +536,19 @@ read_kernel(const u32x4_t* __restrict__ buf, size_t n16, float* __restrict__ out
     const size_t per = (n16 + gridDim.x - 1) / gridDim.x;
     const size_t b0 = (size_t)blockIdx.x * per;
     const size_t b1 = b0 + per < n16 ? b0 + per : n16;
-    for (size_t i = b0 + threadIdx.x; i < b1; i += blockDim.x) {
-        const u32x4_t a = __builtin_nontemporal_load(buf + i);
-        acc ^= a.x ^ a.y ^ a.z ^ a.w;
+    // eight independent loads per thread before any is used, so that a
+    // slice of a few hundred KiB is requested in one or two memory latencies
+    for (size_t i = b0 + threadIdx.x; i < b1; i += 8 * (size_t)blockDim.x) {
+        u32x4_t a[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const size_t j = i + (size_t)u * blockDim.x;
+            a[u] = j < b1 ? __builtin_nontemporal_load(buf + j) : u32x4_t{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            acc ^= a[u].x ^ a[u].y ^ a[u].z ^ a[u].w;
+        }
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {

@@ -399,10 +399,10 @@ __device__ __forceinline__ double rescan_subblock(double acc, const float* __res
         float mx = 0.f;
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-            mx = fmaxf(mx, fminf(fabsf(xv[t].x), kF32Max));
-            mx = fmaxf(mx, fminf(fabsf(xv[t].y), kF32Max));
-            mx = fmaxf(mx, fminf(fabsf(xv[t].z), kF32Max));
-            mx = fmaxf(mx, fminf(fabsf(xv[t].w), kF32Max));
+            mx = fmaxf(mx, fabsf(xv[t].x));
+            mx = fmaxf(mx, fabsf(xv[t].y));
+            mx = fmaxf(mx, fabsf(xv[t].z));
+            mx = fmaxf(mx, fabsf(xv[t].w));
         }
         sigma = grid_sigma(mx);
     }
@@ -502,18 +502,39 @@ constexpr int jit_ahead()
     return NQ == 1 ? 4 : NQ == 2 ? 2 : 1;
 }
 
-// JIT = false (kernel 5): x staged whole in LDS before the stream.  JIT =
-// true (kernel 6): each wave converts the x column of each of its steps for
-// itself into its own LDS groups, from registers loaded jit_ahead columns
+// The three ways the sub-block kernel gets x into LDS (the kernel numbers
+// of the launch options).
+constexpr int kModeStaged = 5;   // x staged whole before the stream
+constexpr int kModeJit = 6;      // each wave converts the column of each step for itself
+constexpr int kModeWindow = 7;   // the workgroup converts each column once, just ahead
+
+// Columns of x an owner of a window pair holds in registers ahead of its
+// conversion.
+constexpr int kWinAhead = 2;
+
+// MODE kModeStaged (kernel 5): x staged whole in LDS before the stream.
+// kModeJit (kernel 6): each wave converts the x column of each of its steps
+// for itself into its own LDS group, from registers loaded jit_ahead columns
 // earlier -- for batches whose whole x stage does not fit the LDS.
+// kModeWindow (kernel 7): every wave has at most one task of one slab, so
+// step s of every wave is superblock column 8 cg + s of its slab cg; the
+// LDS holds two columns of every slab (a double-buffered window), and at step
+// s the waves convert column s + 1 of every slab (pair (cg, q) of slab and
+// vector quad by wave (cg NQ + q) mod NW) while they decode column s: one
+// conversion per column and workgroup, with one LDS barrier per step.  Waves
+// without a task go through the same conversions and barriers.
 // ANY: rows of any whole number of superblocks (line_stream_any: four-line
-// rings, per-row start offsets); else S % 8 == 0 (line_stream).
-template <int NW, int XC, int NQ, bool JIT, bool ANY>
+// rings, per-row start offsets); else S % 8 == 0 (line_stream; always so
+// for kModeWindow).
+template <int NW, int XC, int NQ, int MODE, bool ANY>
 __global__ void __launch_bounds__(NW * 64)
 gemv_i8_sub_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
                    float* __restrict__ y, int n, int S, int m, int rows_per_block,
                    int slabs_per_task)
 {
+    static_assert(MODE != kModeWindow || !ANY, "the window needs whole slabs");
+    constexpr bool JIT = MODE == kModeJit;
+    constexpr bool WIN = MODE == kModeWindow;
     extern __shared__ __align__(16) unsigned char smem[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -532,11 +553,13 @@ gemv_i8_sub_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
     const uint32_t loff = ANY ? (uint32_t)(j * 144 * S) & 127u : 0u;
 
     // LDS: staged x (S columns x NQ quads and a spare group; JIT: per wave
-    // the digits and constants of one group and the lists of NQ), the line
-    // rings, row sums (f64)
+    // the digits and constants of one group and the lists of NQ; window: two
+    // columns of every slab), the line rings, row sums (f64)
     const int ngroups = S * NQ;
     constexpr int kJitWave = kSbWord + NQ * kSbLists;
-    const size_t xbytes = JIT ? (size_t)NW * kJitWave : (size_t)(ngroups + 1) * kSbGroup;
+    const size_t xbytes = JIT   ? (size_t)NW * kJitWave
+                          : WIN ? (size_t)ncg * 2 * NQ * kSbGroup
+                                : (size_t)(ngroups + 1) * kSbGroup;
     unsigned char* xw = smem + (JIT ? (size_t)wave * kJitWave : 0);
     unsigned char* xl = xw + kSbWord;            // JIT: the lists of quad q at xl + q kSbLists
     unsigned char* ring = smem + xbytes + wave * kWaveRing;
@@ -561,7 +584,40 @@ gemv_i8_sub_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
     float4 xa[kA][NQ][4];
     const int ntasks = ((rows_here + 15) >> 4) * ncg;
     const int c_first = 8 * ((min(wave, ntasks - 1) % ncg) * slabs_per_task);
+    // window: group of quad q of the column in slot sl (column parity) of slab cg
+    auto win = [&](int cg, int sl, int q) __attribute__((always_inline)) {
+        return smem + (size_t)((cg * 2 + sl) * NQ + q) * kSbGroup;
+    };
+    // window: the wave's pairs (cg, q) = p / NQ, p % NQ for p = wave + i NW,
+    // and the x of columns s, s + 1 of its slab in slot s mod 2
+    const int npairs = ncg * NQ;
+    float4 xp[WIN ? XC : 1][kWinAhead][4];
+    auto pair_load = [&](int i, int s) __attribute__((always_inline)) {
+        const int pr = min(wave + i * NW, npairs - 1);
+        load_group((8 * (pr / NQ) + min(s, 7)) * NQ + pr % NQ, xp[i][s % kWinAhead]);
+    };
+    auto pair_convert = [&](int s) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < XC; ++i) {
+            const int pr = wave + i * NW;
+            if (pr < npairs) {                    // wave-uniform
+                unsigned char* grp = win(pr / NQ, s & 1, pr % NQ);
+                convert_quad(xp[i][s % kWinAhead], grp, grp + kSbWord, lane);
+                pair_load(i, s + kWinAhead);
+            }
+        }
+    };
     auto issue_x = [&]() __attribute__((always_inline)) {
+        if constexpr (WIN) {
+#pragma unroll
+            for (int i = 0; i < XC; ++i) {
+#pragma unroll
+                for (int a = 0; a < kWinAhead; ++a) {
+                    pair_load(i, a);
+                }
+            }
+            return;
+        }
         if constexpr (JIT) {
 #pragma unroll
             for (int a = 0; a < kA; ++a) {
@@ -579,6 +635,10 @@ gemv_i8_sub_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
     };
     auto convert_x = [&]() __attribute__((always_inline)) {
         if constexpr (JIT) {
+            return;
+        }
+        if constexpr (WIN) {
+            pair_convert(0);
             return;
         }
 #pragma unroll
@@ -720,6 +780,48 @@ gemv_i8_sub_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
         }
         __builtin_amdgcn_sched_barrier(0);
     };
+    // window: all LDS accesses of this wave done, then every wave at the
+    // same point (LDS only: the line loads in flight are not waited for)
+    auto lds_barrier = [&]() __attribute__((always_inline)) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    };
+    // window step s = c mod 8: after the barrier, column s is in slot s mod 2
+    // of every slab and column s - 1's slot is free: convert column s + 1
+    // into it, then decode column c (quads one after the other, the exact
+    // terms of a quad with uncertified elements in a loop after them)
+    auto step_win = [&](int c, const unsigned char* rr, uint32_t b0) __attribute__((always_inline)) {
+        const int sidx = (int)(b0 / 144u);         // c mod 8, a compile-time constant
+        if (sidx > 0) {
+            lds_barrier();
+        }
+        if (sidx < 7) {
+            pair_convert(sidx + 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        const Tile t = prep(rr, b0);
+        const int cg = c >> 3;
+        static_for<NQ>([&](auto qc) __attribute__((always_inline)) {
+            quad(t, qc, win(cg, sidx & 1, decltype(qc)::value));
+            __builtin_amdgcn_sched_barrier(0);
+        });
+#pragma nounroll
+        for (int q = 0; q < NQ; ++q) {
+            const unsigned char* grp = win(cg, sidx & 1, q);
+            const uint4 cnts = *reinterpret_cast<const uint4*>(grp + kSbWord);
+            const uint32_t any = __builtin_amdgcn_readfirstlane(cnts.x | cnts.y | cnts.z | cnts.w);
+            if (any != 0u) {
+                const uint32_t cnt = g == 0 ? cnts.x : g == 1 ? cnts.y : g == 2 ? cnts.z : cnts.w;
+                const int bv = min(4 * q + g, m - 1);
+                const double a = vector_corrections(
+                    acc.get(q), cnt, grp + kSbList + g * (kCorr * 8),
+                    reinterpret_cast<const double2*>(grp + kSbConst + g * 128),
+                    x + (size_t)bv * k + (size_t)c * 256, t.Ds, t.Ms, rr, t.b, kWindow);
+                acc.set(q, a);
+            }
+        }
+    };
     // whether slab sl has a column with uncertified elements in any vector:
     // one bit per column in scalar registers, gathered by a ballot on the
     // first call (after the x stage)
@@ -764,7 +866,23 @@ gemv_i8_sub_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
             acc.at<q>() = 0.0;
         });
     };
-    if constexpr (JIT && ANY) {
+    if constexpr (WIN) {
+        line_stream<NW, 3>(w, x, n, S, rows_per_block, slabs_per_task, ring, issue_x, convert_x,
+                           step_win, task_end);
+        // a wave without a task: the same conversions and barriers as the
+        // eight steps of a slab
+        if (wave >= ntasks) {
+            static_for<8>([&](auto sc) __attribute__((always_inline)) {
+                constexpr int sidx = decltype(sc)::value;
+                if constexpr (sidx > 0) {
+                    lds_barrier();
+                }
+                if constexpr (sidx < 7) {
+                    pair_convert(sidx + 1);
+                }
+            });
+        }
+    } else if constexpr (JIT && ANY) {
         line_stream_any<NW>(w, x, n, S, rows_per_block, slabs_per_task, ring, issue_x, convert_x,
                             step_jit, task_end);
     } else if constexpr (JIT) {
@@ -792,19 +910,31 @@ gemv_i8_sub_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
     }
 }
 
-template <int XC, int NQ, bool JIT = false, int NW = 8>
+template <int XC, int NQ, int MODE = kModeStaged, int NW = 8>
 static hipError_t launch_sub_x(const GemvPlan& p, const uint8_t* w, const float* x, float* y,
                                hipStream_t stream)
 {
     if (p.waves_per_block != NW) {
         return hipErrorInvalidValue;
     }
-    if (p.S % 8 != 0) {
-        hipLaunchKernelGGL((gemv_i8_sub_kernel<NW, XC, NQ, JIT, true>), dim3(p.grid), dim3(NW * 64),
+    if constexpr (MODE == kModeWindow) {
+        // one slab per task, a task for at most every wave, pairs within XC
+        // per wave: the plan ensures it; refused here too, as a wave with two
+        // tasks would not meet the others at the barriers
+        const int ncg = p.S / 8;
+        if (p.S % 8 != 0 || p.cols_per_task != 8 || ((p.rows_per_block + 15) / 16) * ncg > NW ||
+            ncg * NQ > XC * NW) {
+            return hipErrorInvalidValue;
+        }
+        hipLaunchKernelGGL((gemv_i8_sub_kernel<NW, XC, NQ, MODE, false>), dim3(p.grid),
+                           dim3(NW * 64), p.lds_bytes, stream, w, x, y, p.n, p.S, p.m,
+                           p.rows_per_block, 1);
+    } else if (p.S % 8 != 0) {
+        hipLaunchKernelGGL((gemv_i8_sub_kernel<NW, XC, NQ, MODE, true>), dim3(p.grid), dim3(NW * 64),
                            p.lds_bytes, stream, w, x, y, p.n, p.S, p.m, p.rows_per_block,
                            p.cols_per_task / 8);
     } else {
-        hipLaunchKernelGGL((gemv_i8_sub_kernel<NW, XC, NQ, JIT, false>), dim3(p.grid), dim3(NW * 64),
+        hipLaunchKernelGGL((gemv_i8_sub_kernel<NW, XC, NQ, MODE, false>), dim3(p.grid), dim3(NW * 64),
                            p.lds_bytes, stream, w, x, y, p.n, p.S, p.m, p.rows_per_block,
                            p.cols_per_task / 8);
     }
@@ -875,18 +1005,24 @@ hipError_t launch_gemv_mfma(const GemvPlan& p, const void* w, const float* x, fl
                             hipStream_t stream)
 {
     const uint8_t* wb = static_cast<const uint8_t*>(w);
-    if (p.kernel == 5 || p.kernel == 6) {
-        const int nq = sub_quads(p.m);         // the quads sub_lds_bytes, jit_lds_bytes size
+    if (p.kernel >= 5) {
+        const int nq = sub_quads(p.m);         // the quads the LDS sizes count
         if (p.kernel == 5) {
             if (nq == 4) return launch_sub<4>(p, wb, x, y, stream);
             if (nq == 2) return launch_sub<2>(p, wb, x, y, stream);
             return launch_sub<1>(p, wb, x, y, stream);
         }
+        if (p.kernel == 7) {
+            // one pair of the window per wave
+            if (nq == 4) return launch_sub_x<1, 4, kModeWindow>(p, wb, x, y, stream);
+            if (nq == 2) return launch_sub_x<1, 2, kModeWindow>(p, wb, x, y, stream);
+            return launch_sub_x<1, 1, kModeWindow>(p, wb, x, y, stream);
+        }
         // four quads: four waves, whose lanes may hold 512 registers (the
         // x of the next column takes 64 of them)
-        if (nq == 4) return launch_sub_x<1, 4, true, 4>(p, wb, x, y, stream);
-        if (nq == 2) return launch_sub_x<1, 2, true>(p, wb, x, y, stream);
-        return launch_sub_x<1, 1, true>(p, wb, x, y, stream);
+        if (nq == 4) return launch_sub_x<1, 4, kModeJit, 4>(p, wb, x, y, stream);
+        if (nq == 2) return launch_sub_x<1, 2, kModeJit>(p, wb, x, y, stream);
+        return launch_sub_x<1, 1, kModeJit>(p, wb, x, y, stream);
     }
     if (p.m == 2) {
         return launch_lines_m<2>(p, wb, x, y, stream);
@@ -914,6 +1050,12 @@ size_t jit_lds_bytes(int S, int m)
     const int nw = jit_waves(m);
     return (size_t)nw * (kSbWord + sub_quads(m) * kSbLists) +
            (size_t)nw * (S % 8 != 0 ? kRing4Wave : kRingWave);
+}
+
+// the window kernel: two columns of every slab (S % 8 == 0), eight rings
+size_t win_lds_bytes(int S, int m)
+{
+    return (size_t)(S / 8) * 2 * sub_quads(m) * kSbGroup + (size_t)8 * kRingWave;
 }
 
 size_t lines_lds_bytes(int S, int m, int waves)

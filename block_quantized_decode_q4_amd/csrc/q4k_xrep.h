@@ -4,10 +4,11 @@
 //
 // Per 32-element sub-block of one vector (the unit that shares d*sc_j and
 // dmin*m_j in the Q4_K format):
-//  * mx = the largest |x| over the finite elements, sigma = 30 - E for
-//    mx = f * 2^E with f in [1/2, 1), so that mx * 2^sigma lies in
-//    [2^29, 2^30) (sigma = 0 when mx = 0).  sigma spans -98 .. 178, so the
-//    scale 2^-sigma is kept in f64 and no range is clamped;
+//  * mx = the largest |x| (NaN left out), sigma = 30 - E for mx = f * 2^E
+//    with f in [1/2, 1), so that mx * 2^sigma lies in [2^29, 2^30) (sigma =
+//    0 when mx = 0, 30 when mx is infinite: frexp gives it exponent 0).
+//    sigma spans -98 .. 178, so the scale 2^-sigma is kept in f64 and no
+//    range is clamped;
 //  * v = x * 2^sigma (exact for every element that does not round to
 //    zero), xi = rint(v) with |xi| < 2^30, written as four signed base-256
 //    digits (the bytes of xi + 0x80808080, each minus 128), so that int8
@@ -34,14 +35,6 @@ namespace q4k {
 
 constexpr float kCertRel = 0x1p-17f;
 constexpr int kCorr = 4;             // exact corrections listed per column
-constexpr float kF32Max = 3.40282347e38f;
-
-// |x| for finite x, else 0
-__device__ __forceinline__ float finite_abs(float x)
-{
-    const float a = fabsf(x);
-    return a <= kF32Max ? a : 0.f;
-}
 
 // grid exponent of a sub-block from its largest finite |x|
 __device__ __forceinline__ int grid_sigma(float mx)
@@ -133,17 +126,16 @@ __device__ __forceinline__ double digits_exact(int t0, int t1, int t2, int t3)
 }
 
 // Exclusive prefix sum and total of v over the 16 lanes of a DPP row
-// (every lane of the wave active).
+// (every lane of the wave active): a Hillis-Steele scan by row_shr (lanes
+// shifted in from outside the row read 0), the total by row_share:15.
 __device__ __forceinline__ int row16_scan(int v, int& total)
 {
-    const int lane = (int)(threadIdx.x & 15);
     int incl = v;
-#pragma unroll
-    for (int d = 1; d < 16; d <<= 1) {
-        const int o = __shfl_up(incl, (unsigned)d, 16);
-        incl += lane >= d ? o : 0;
-    }
-    total = __shfl(incl, 15, 16);
+    incl += __builtin_amdgcn_update_dpp(0, incl, 0x111, 0xF, 0xF, true);   // row_shr:1
+    incl += __builtin_amdgcn_update_dpp(0, incl, 0x112, 0xF, 0xF, true);   // row_shr:2
+    incl += __builtin_amdgcn_update_dpp(0, incl, 0x114, 0xF, 0xF, true);   // row_shr:4
+    incl += __builtin_amdgcn_update_dpp(0, incl, 0x118, 0xF, 0xF, true);   // row_shr:8
+    total = __builtin_amdgcn_update_dpp(0, incl, 0x15F, 0xF, 0xF, false);  // row_share:15
     return incl - v;
 }
 
@@ -163,13 +155,14 @@ struct Conv16 {
 __device__ __forceinline__ Conv16 convert16(const float (&e)[16])
 {
     Conv16 c;
-    // largest |x| over the finite elements (an infinity counts as the
-    // largest finite value, NaN not at all: either leaves its sub-block on a
-    // grid that still carries every finite element it certifies)
+    // largest |x| (NaN left out by the IEEE max; an infinity makes mx
+    // infinite, whose frexp exponent is 0: sigma = 30, a grid that still
+    // carries every element it certifies, the sub-block's other large
+    // values going to the exact terms)
     float mx = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        mx = fmaxf(mx, fminf(fabsf(e[i]), kF32Max));
+        mx = fmaxf(mx, fabsf(e[i]));
     }
     mx = fmaxf(mx, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
                        0, __builtin_bit_cast(int, mx), 0xB1, 0xF, 0xF, false)));   // lane ^ 1

@@ -87,13 +87,15 @@ int q4k_load(void* w_dev, const void* src_host, size_t src_bytes,
  *  y : device, m*n f32, 16-byte aligned, fully overwritten (no accumulate)
  *  1 <= n <= 2^31-1, 256 <= k <= 2^31-1 with k % 256 == 0, 1 <= m <= 8.
  *  9 <= m <= 16 (beyond the pages' batch of 8): one pass over the weights on
- *  the sub-block matrix-core kernels (5, 6) when w is 128-byte aligned and
+ *  the sub-block matrix-core kernels (5-7) when w is 128-byte aligned and
  *  their LDS fits; otherwise Q4K_ERR_UNSUPPORTED.  m > 16:
  *  Q4K_ERR_UNSUPPORTED.  A batch is never split into several launches.
  * Asynchronous on `stream`; allocates nothing.  Results agree with the exact
  * dot product of the dequantized weights within 1e-5 * sum|w||x| per output
- * on the workloads' value distributions.  Dequantization happens in
- * registers; the weights are read exactly once from HBM. */
+ * for every input whose exact result is finite (the tolerance the problem
+ * states); where the exact result is an infinity or NaN, so is y.
+ * Dequantization happens in registers; the weights are read exactly once
+ * from HBM. */
 int q4k_gemv(const void* w, const float* x, float* y,
              int64_t n, int64_t k, int64_t m, void* stream);
 
@@ -122,14 +124,21 @@ const char* q4k_status_string(int rc);
  *      of vectors
  *   6  kernel 5 with x converted one superblock column at a time by each
  *      wave for itself (no whole x stage: any k and m)
- * Kernels 3-6 need w 128-byte aligned and their staged x plus line rings
- * within the LDS; kernel 4 also k % 2048 == 0 (rows of whole 8-superblock
- * slabs); kernels 3, 5 and 6 take rows of partial slabs too (four-line
- * rings, three lines in flight), kernel 3 up to k = 4096 * waves_per_block.
+ *   7  kernel 5 with x converted once per workgroup, one column ahead, into
+ *      a two-column window of every slab (one slab per task, eight waves;
+ *      limits below; 16 * (8 / slabs) rows per workgroup by default)
+ * Kernels 3-7 need w 128-byte aligned and their staged x plus line rings
+ * within the LDS; kernels 4 and 7 also k % 2048 == 0 (rows of whole
+ * 8-superblock slabs); kernels 3, 5 and 6 take rows of partial slabs too
+ * (four-line rings, three lines in flight), kernel 3 up to k = 4096 *
+ * waves_per_block.  Kernel 7: k / 2048 slabs times the vector quads (one
+ * per four vectors) at most 8, slabs times the tiles of 16 rows of a
+ * workgroup at most 8.
  * Automatic choice: m = 1 kernel 3 when it applies and the weights take at
  * least 16 MiB, else kernel 2 (the matrix cores only when asked for); m > 1
  * kernel 5 for m >= 3, kernel 4 for m = 2, the other of the two if only it
- * fits, else kernel 6 when it fits, else kernel 1 (m <= 8).  With kernel = 0 and
+ * fits, else kernel 7, else kernel 6 when it fits, else kernel 1 (m <= 8).
+ * With kernel = 0 and
  * another field set, m = 1 uses the streaming kernel and m > 1 the
  * x-stager.
  *
@@ -148,7 +157,7 @@ typedef struct q4k_launch {
     int32_t rows_per_wave;    /* rows a wave decodes per pass: 0 auto, 1, 2 or 4   */
     int32_t waves_per_block;  /* 0 auto, 4 or 8                                    */
     int32_t x_in_registers;   /* 0 auto, 1 keep x in VGPRs (one span, m = 1), 2 LDS */
-    int32_t kernel;           /* 0 auto, else 1-6 as listed above                  */
+    int32_t kernel;           /* 0 auto, else 1-7 as listed above                  */
     int32_t ring_depth;       /* loads in flight per wave, 0 auto: streaming 1..4
                                  rows; line-streamed 3 or 9 lines                  */
     int32_t rows_per_task;    /* streaming: rows per wave task, 0 auto, >= 1       */
@@ -175,7 +184,7 @@ int q4k_gemv_ex(const void* w, const float* x, float* y,
  * launching (Q4K_ERR_SHAPE, Q4K_ERR_UNSUPPORTED, ...); pointers and their
  * 16-byte alignment are not checked here. */
 typedef struct q4k_plan_info {
-    int32_t kernel;          /* 1-6 as listed above                           */
+    int32_t kernel;          /* 1-7 as listed above                           */
     int32_t grid;            /* workgroups                                     */
     int32_t threads;         /* per workgroup                                  */
     int32_t lds_bytes;       /* dynamic LDS per workgroup                      */

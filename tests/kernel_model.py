@@ -6,9 +6,9 @@ on inputs the workloads never produce.  It models the kernels, not the
 method: the oracle stays the reference.
 
 x representation, per 32-element sub-block of one vector:
-  * mx = largest |x| over the finite elements; sigma = 30 - E for
-    mx = f * 2^E, f in [1/2, 1) (so mx * 2^sigma lies in [2^29, 2^30)), 0 when
-    mx = 0;
+  * mx = largest |x| (NaN left out); sigma = 30 - E for mx = f * 2^E, f in
+    [1/2, 1) (so mx * 2^sigma lies in [2^29, 2^30)), 0 when mx = 0, 30 when
+    mx is infinite (frexp gives it exponent 0);
   * v = x * 2^sigma (exact in f32 for every element that is not rounded to
     zero), xi = rint(v) (round to nearest even), |xi| < 2^30, written as four
     signed base-256 digits (the bytes of xi + 0x80808080, each minus 128);
@@ -65,9 +65,9 @@ class XRep:
         xs = np.asarray(x, np.float32).reshape(-1, 32)
         self.x = xs
         finite = np.isfinite(xs)
-        a = np.minimum(np.where(np.isnan(xs), np.float32(0), np.abs(xs)), np.float32(3.4028235e38))
+        a = np.where(np.isnan(xs), np.float32(0), np.abs(xs))
         mx = a.max(axis=1)
-        _, E = np.frexp(mx)
+        _, E = np.frexp(mx)             # an infinite mx: exponent 0, sigma = 30
         self.sigma = np.where(mx > 0, 30 - E, 0).astype(np.int64)
         with np.errstate(invalid="ignore", over="ignore"):
             v = np.ldexp(np.where(finite, xs, np.float32(0)), self.sigma[:, None].astype(np.int32))

@@ -105,7 +105,10 @@ def test_launch_struct_matches_header():
 def test_gemv_ex_kernel_option_refusals(lib):
     """Options that no kernel can honour are refused before any HIP call."""
     cases = [
-        (dict(kernel=7), 16, 2048, 1),                       # kernels 1-6 only
+        (dict(kernel=8), 16, 2048, 1),                       # kernels 1-7 only
+        (dict(kernel=7), 16, 1280, 2),                       # window: whole slabs only
+        (dict(kernel=7, ring_depth=9), 16, 4096, 8),         # three lines in flight only
+        (dict(kernel=7, rows_per_block=80), 16, 4096, 8),    # 5 tiles x 2 slabs > 8 waves
         (dict(kernel=-1), 16, 2048, 1),
         (dict(kernel=2), 16, 2048, 2),                       # streaming: one vector
         (dict(kernel=3), 16, 4096, 2),                       # vector-ALU lines: one vector
@@ -188,8 +191,9 @@ def test_plan_info_struct_matches_header():
     (32000, 4096, 1, False, 2, None, 0),    # weights not 128-byte aligned
     (32000, 4096, 2, True, 4, 250, 16),     # m = 2: line MFMA
     (14336, 4096, 4, True, 5, 224, 8),      # m >= 3: sub-block MFMA, x staged whole
-    (14336, 4096, 8, True, 6, 224, 8),      # x of 8 vectors does not fit one stage
-    (4096, 14336, 8, True, 6, 256, 8),      # x of 8 columns does not fit: per-wave x
+    (14336, 4096, 8, True, 7, 224, 8),      # x of 8 vectors does not fit one stage: window
+    (14336, 8192, 8, True, 7, 448, 8),      # four slabs: 32 rows a workgroup
+    (4096, 14336, 8, True, 6, 256, 8),      # 7 slabs x 2 quads: no window; per-wave x
     (4096, 11008, 8, True, 6, 256, 8),      # partial slab (43 superblocks)
     (14336, 4096, 8, False, 1, None, 0),
 ])
@@ -217,16 +221,20 @@ def test_plan_follows_options_and_lds_limit():
     assert p.kernel == 3 and p.cols_per_task == 8
     # the whole-x stage of kernel 5 for eight vectors (33 groups of 4752
     # bytes and eight rings of 4352) exceeds the LDS: the automatic choice
-    # moves on to per-wave x (per wave one group's digits and constants, 4608
-    # bytes, and two quads' lists of 144; eight rings; f64 row sums of two
-    # slab groups of 64 rows)
+    # moves on to the column window (two columns of each of two slabs for
+    # two quads; eight rings; f64 row sums of two slab groups of 64 rows)
     p = q4k.q4k_plan(14336, 4096, 8, lds_max=MI355X_LDS)
-    assert p.kernel == 6 and p.lds_bytes == 8 * (4608 + 2 * 144) + 8 * 4352 + 2 * 64 * 8 * 8
+    assert p.kernel == 7 and p.lds_bytes == 2 * 2 * 2 * 4752 + 8 * 4352 + 2 * 64 * 8 * 8
+    assert p.rows_per_block == 64 and p.cols_per_task == 8
+    # per-wave x: one group's digits and constants (4608 bytes) and two
+    # quads' lists (144 each) per wave
+    p = q4k.q4k_plan(14336, 4096, 8, lds_max=MI355X_LDS, kernel=6)
+    assert p.lds_bytes == 8 * (4608 + 2 * 144) + 8 * 4352 + 2 * 64 * 8 * 8
     # four vectors: 17 groups and the rings fit 160 KiB, not 96 KiB
     p = q4k.q4k_plan(14336, 4096, 4, lds_max=MI355X_LDS)
     assert p.kernel == 5
     p = q4k.q4k_plan(14336, 4096, 4, lds_max=98304)
-    assert p.kernel == 6 and p.lds_bytes <= 98304
+    assert p.kernel == 7 and p.lds_bytes <= 98304
     with pytest.raises(q4k.Q4KError) as ei:
         q4k.q4k_plan(14336, 4096, 8, lds_max=MI355X_LDS, kernel=5)
     assert ei.value.rc == q4k.Q4K_ERR_UNSUPPORTED
@@ -248,14 +256,15 @@ def test_plan_refusals(lib):
 
 @pytest.mark.parametrize("n,k,m,kernel", [
     (4096, 14336, 16, 6),     # x per column per wave
-    (300, 2048, 12, 6),
+    (300, 2048, 12, 7),       # one slab x four quads: the window
     (17, 1280, 13, 6),        # partial slabs
     (130, 11008, 16, 6),
     (5, 256, 16, 5),          # sixteen vectors' x fits one stage
     (3, 768, 9, 5),
-    (14336, 4096, 16, 6),
-    (14336, 4096, 9, 6),
-    (32000, 4096, 16, 6),
+    (14336, 4096, 16, 7),     # two slabs x four quads: the window
+    (14336, 4096, 9, 7),
+    (32000, 4096, 16, 7),
+    (14336, 8192, 16, 6),     # four slabs x four quads: per-wave x
 ])
 def test_plan_wide_batches(n, k, m, kernel):
     """9-16 vectors: one pass over the weights on a sub-block kernel."""
@@ -291,3 +300,29 @@ def test_plan_wide_batch_refusals():
     assert p.kernel == 6 and p.threads == 256
     p = q4k.q4k_plan(14336, 4096, 8, lds_max=MI355X_LDS, kernel=6)
     assert p.threads == 512
+
+
+@pytest.mark.parametrize("n,k,m,opts", [
+    (300, 1280, 4, {}),                        # partial slab: no window
+    (4096, 14336, 8, {}),                      # 7 slabs x 2 quads > 8 waves
+    (4096, 20480, 1, {}),                      # 10 slabs > 8 waves
+    (14336, 4096, 8, dict(rows_per_block=80)),  # 5 tiles x 2 slabs > 8 tasks
+    (14336, 4096, 8, dict(cols_per_task=16)),  # one slab per task only
+    (14336, 4096, 8, dict(waves_per_block=4)),
+])
+def test_plan_window_refusals(n, k, m, opts):
+    """Kernel 7 (the workgroup's column window) only where every wave has at
+    most one task of one slab and one window pair: anything else would make
+    a wave meet the others' barriers a different number of times."""
+    with pytest.raises(q4k.Q4KError) as ei:
+        q4k.q4k_plan(n, k, m, lds_max=MI355X_LDS, kernel=7, **opts)
+    assert ei.value.rc == q4k.Q4K_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("n,k,m,rpb", [(14336, 4096, 8, 64), (300, 4096, 3, 64), (33, 2048, 2, 128),
+                                       (1, 16384, 1, 16), (14336, 4096, 16, 64), (64, 8192, 5, 32)])
+def test_plan_window(n, k, m, rpb):
+    p = q4k.q4k_plan(n, k, m, lds_max=MI355X_LDS, kernel=7)
+    assert p.kernel == 7 and p.cols_per_task == 8 and p.threads == 512
+    assert p.rows_per_block == rpb
+    assert (rpb + 15) // 16 * (k // 2048) <= 8

@@ -21,8 +21,8 @@ from block_quantized_decode_q4_amd import q4k  # noqa: E402
 pytestmark = pytest.mark.gpu
 
 # kernels and the vectors one call of each takes
-KERNELS = [1, 2, 3, 4, 5, 6]
-MAX_M = {1: 8, 2: 1, 3: 1, 4: 2, 5: 16, 6: 16}
+KERNELS = [1, 2, 3, 4, 5, 6, 7]
+MAX_M = {1: 8, 2: 1, 3: 1, 4: 2, 5: 16, 6: 16, 7: 16}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -50,8 +50,8 @@ def _run(w_d, x, n, k, kernel):
 def test_edge_inputs(oracle_mod, case, kernel):
     print("edge input '%s' n=%d k=%d m=%d kernel %d" % (case.name, case.n, case.k, case.m, kernel),
           flush=True)
-    if kernel == 4 and case.k % 2048 != 0:
-        pytest.skip("kernel 4 takes rows of whole 8-superblock slabs only (k % 2048 == 0)")
+    if kernel in (4, 7) and case.k % 2048 != 0:
+        pytest.skip("kernels 4 and 7 take rows of whole 8-superblock slabs only (k % 2048 == 0)")
     y_ref, bound = oracle_mod.gemv(case.w, case.x, case.n)
     w_d = torch.from_numpy(case.w).cuda()
     step = MAX_M[kernel]

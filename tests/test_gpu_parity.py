@@ -282,7 +282,8 @@ def test_sub_kernel(oracle_mod, n, k, m):
 def test_sub_kernel_workload(oracle_mod):
     """The batched workload (14336 x 4096, eight vectors): its whole x stage
     (33 groups of 4752 bytes) and the rings exceed the LDS, so kernel 5 is
-    refused and the automatic plan takes kernel 6."""
+    refused; the automatic plan (the column window, kernel 7) and kernel 6
+    agree bit for bit."""
     wl, w, x, y_ref, bound = workload(4, oracle_mod)
     _say("sub-block kernels workload 4")
     with pytest.raises(q4k.Q4KError) as ei:
@@ -359,6 +360,51 @@ def test_sub_kernels_partial_slabs(oracle_mod, n, k, m):
         assert_within(y2, y_ref, bound, "per-wave x partial slabs %r" % opts)
     y4 = run_gemv(w_d, x, n, k, m)             # automatic kernel
     assert_within(y4, y_ref, bound, "automatic partial slabs m=%d k=%d" % (m, k))
+
+
+# kernel 7: the sub-block decode with x converted once per workgroup, one
+# column ahead, into a two-column window of every slab (waves in step, one
+# LDS barrier per column).  Per column and vector its digits, MFMAs and sums
+# are those of kernels 5 and 6, so with one slab per task the three agree
+# bit for bit.  Small n leaves waves without a task: they still convert and
+# meet the barriers.
+@pytest.mark.parametrize("n,k,m", [(300, 4096, 8), (130, 4096, 4), (64, 8192, 2), (17, 2048, 3),
+                                   (1, 4096, 16), (257, 16384, 1), (40, 4096, 12), (3, 6144, 5),
+                                   (1000, 8192, 6)])
+def test_window_kernel(oracle_mod, n, k, m):
+    w, x = synth.make_inputs(n, k, m, seed=n * 43 + k + 3 * m)
+    y_ref, bound = oracle_mod.gemv(w, x, n)
+    w_d = dev(w)
+    _say("window kernel n=%d k=%d m=%d" % (n, k, m))
+    y = run_gemv(w_d, x, n, k, m, kernel=7)
+    assert_within(y, y_ref, bound, "window m=%d" % m)
+    for b in range(m):                          # batched == m single-vector launches
+        y1 = run_gemv(w_d, x[b:b + 1], n, k, 1, kernel=7)
+        assert np.array_equal(y1[0].view(np.uint32), y[b].view(np.uint32)), b
+    y6 = run_gemv(w_d, x, n, k, m, kernel=6, cols_per_task=8)
+    assert np.array_equal(y6.view(np.uint32), y.view(np.uint32))
+    try:
+        y5 = run_gemv(w_d, x, n, k, m, kernel=5, cols_per_task=8)
+    except q4k.Q4KError as e:
+        assert e.rc == q4k.Q4K_ERR_UNSUPPORTED
+    else:
+        assert np.array_equal(y5.view(np.uint32), y.view(np.uint32))
+    ncg = k // 2048
+    for rpb in (16, 32, 48):
+        if (rpb + 15) // 16 * ncg > 8:
+            continue
+        y2 = run_gemv(w_d, x, n, k, m, kernel=7, rows_per_block=rpb)
+        assert np.array_equal(y2.view(np.uint32), y.view(np.uint32)), rpb
+
+
+def test_window_kernel_workload(oracle_mod):
+    """The batched workload (14336 x 4096, eight vectors) on its automatic
+    plan, the column window."""
+    wl, w, x, y_ref, bound = workload(4, oracle_mod)
+    assert q4k.q4k_plan(wl.n, wl.k, wl.m).kernel == 7
+    _say("window kernel workload 4")
+    y = run_gemv(dev(w), x, wl.n, wl.k, wl.m)
+    assert_within(y, y_ref, bound, "window workload 4")
 
 
 def test_jit_kernel_ffn_down_batch8(oracle_mod):
@@ -623,9 +669,9 @@ def test_batched_equals_separate_calls(oracle_mod, m):
 
 
 def test_batched_workload_against_separate(oracle_mod):
-    """The batched workload: the automatic kernel (sub-block, per-wave x)
-    and the x-stager kernel, each bit-identical to m single-vector launches
-    of itself."""
+    """The batched workload: the automatic kernel (sub-block, column window;
+    its single-vector counterpart: per-wave x, the same sums) and the
+    x-stager kernel, each bit-identical to m single-vector launches."""
     wl, w, x, y_ref, bound = workload(4, oracle_mod)
     w_d = dev(w)
     for opts, single in ((dict(), dict(kernel=6)), (dict(kernel=1), dict(kernel=1))):
@@ -818,7 +864,7 @@ def test_wide_batch(oracle_mod, n, k, m):
 
 
 def test_wide_batch_full_size(oracle_mod):
-    """14336 x 4096 with sixteen vectors (automatic: one pass on kernel 6)
+    """14336 x 4096 with sixteen vectors (automatic: one pass on kernel 7)
     against the oracle, and against two calls of eight vectors on the same
     kernel and column grouping (bit-identical)."""
     n, k, m = 14336, 4096, 16
@@ -826,11 +872,12 @@ def test_wide_batch_full_size(oracle_mod):
     y_ref, bound = oracle_mod.gemv(w, x, n)
     w_d = dev(w)
     _say("wide batch automatic n=%d k=%d m=%d" % (n, k, m))
-    assert q4k.q4k_plan(n, k, m).kernel == 6
+    assert q4k.q4k_plan(n, k, m).kernel == 7
     y = run_gemv(w_d, x, n, k, m)
     assert_within(y, y_ref, bound, "14336 x 4096 m=16")
     y16 = run_gemv(w_d, x, n, k, m, kernel=6, cols_per_task=8)
     assert_within(y16, y_ref, bound, "14336 x 4096 m=16 one pass")
+    assert np.array_equal(y16.view(np.uint32), y.view(np.uint32))
     for h in range(2):
         y8 = run_gemv(w_d, x[8 * h:8 * h + 8], n, k, 8, kernel=6, cols_per_task=8)
         assert np.array_equal(y8.view(np.uint32), y16[8 * h:8 * h + 8].view(np.uint32)), h
@@ -860,7 +907,7 @@ def test_wide_batch_automatic(oracle_mod, n, k, m, off):
         assert bool((y_d == 7.0).all())
         return
     _say("wide batch automatic n=%d k=%d m=%d off=%d -> kernel %d" % (n, k, m, off, p.kernel))
-    assert p.kernel in (5, 6)
+    assert p.kernel in (5, 6, 7)
     y_ref, bound = oracle_mod.gemv(w, x, n)
     y = run_gemv(w_d, x, n, k, m)
     assert_within(y, y_ref, bound, "n=%d k=%d m=%d off=%d" % (n, k, m, off))
