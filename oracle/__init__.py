@@ -76,6 +76,11 @@ def _load():
         lib.oq_gemv.restype = ctypes.c_int
         lib.oq_quantize_row.argtypes = [f32p, i64, u8p]
         lib.oq_quantize_row.restype = ctypes.c_int
+        i8p = ctypes.POINTER(ctypes.c_int8)
+        lib.oq_quantize_q8.argtypes = [f32p, i64, i8p, f32p]
+        lib.oq_quantize_q8.restype = ctypes.c_int
+        lib.oq_gemv_q8.argtypes = [u8p, i8p, f32p, i64, i64, i64, f64p, f64p]
+        lib.oq_gemv_q8.restype = ctypes.c_int
         lib.oq_num_threads.argtypes = []
         lib.oq_num_threads.restype = ctypes.c_int
         lib.oq_set_num_threads.argtypes = [ctypes.c_int]
@@ -202,3 +207,46 @@ def quantize_rows(x) -> np.ndarray:
         if rc != 0:
             raise RuntimeError("oq_quantize_row rc=%d" % rc)
     return out
+
+
+def quantize_q8(x) -> tuple[np.ndarray, np.ndarray]:
+    """Q8 activations: float32 [m, k] -> codes int8 [m, k] and scales
+    float32 [m, k/32] (blocks of 32, d = amax/127, nearest-even codes)."""
+    lib = _load()
+    xa = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    if xa.ndim == 1:
+        xa = xa.reshape(1, -1)
+    m, k = xa.shape
+    if k % 32 != 0:
+        raise ValueError("k must be a multiple of 32")
+    q = np.empty((m, k), dtype=np.int8)
+    d = np.empty((m, k // 32), dtype=np.float32)
+    for b in range(m):
+        row = np.ascontiguousarray(xa[b])
+        qb = q[b]
+        db = d[b]
+        rc = lib.oq_quantize_q8(_ptr(row, ctypes.c_float), k, _ptr(qb, ctypes.c_int8),
+                                _ptr(db, ctypes.c_float))
+        if rc != 0:
+            raise RuntimeError("oq_quantize_q8 rc=%d" % rc)
+    return q, d
+
+
+def gemv_q8(w, q, d, n: int) -> tuple[np.ndarray, np.ndarray]:
+    """y[b, r] = sum_c w[r, c] * d[b, c/32] * q[b, c] and its bound
+    sum |w| |d q|, float64 [m, n]."""
+    lib = _load()
+    qa = np.ascontiguousarray(np.asarray(q, dtype=np.int8))
+    if qa.ndim == 1:
+        qa = qa.reshape(1, -1)
+    m, k = qa.shape
+    da = np.ascontiguousarray(np.asarray(d, dtype=np.float32).reshape(m, k // 32))
+    wb = _u8(w)
+    _check_shape(wb, n, k)
+    y = np.empty((m, n), dtype=np.float64)
+    bound = np.empty((m, n), dtype=np.float64)
+    rc = lib.oq_gemv_q8(_ptr(wb, ctypes.c_uint8), _ptr(qa, ctypes.c_int8), _ptr(da, ctypes.c_float),
+                        n, k, m, _ptr(y, ctypes.c_double), _ptr(bound, ctypes.c_double))
+    if rc != 0:
+        raise RuntimeError("oq_gemv_q8 rc=%d" % rc)
+    return y, bound

@@ -35,7 +35,10 @@
  * Pins (tests/, CPU only): exhaustive binary16 decode against numpy's
  * float16 conversion; exhaustive scale pack/unpack; one-hot layout brute
  * force; hand-computed golden superblocks; closed forms; exact dyadic dots;
- * quantizer round-trip.
+ * quantizer round-trip; for the Q8 activations: exact round trips of
+ * dyadic blocks, constant, zero, one-hot and mirrored blocks, the rounding
+ * bound, non-finite blocks, and the Q8 GEMV against the f32 GEMV where the
+ * quantized x is x itself.
  */
 #include <math.h>
 #include <stdint.h>
@@ -329,6 +332,90 @@ int oq_quantize_row(const float* x, int64_t k, uint8_t* out)
         }
     }
     return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Q8 activations, for the pages' integer-dot variant (realizar 0.8.5,
+ * src/cuda/executor/layers/modules_utilities.rs, `preload_hw_dp4a_modules`:
+ * a Q8 quantize kernel for every GEMV input length, feeding the DP4A Q4_K
+ * GEMV).  The pages name the kernels only; the block format is the reading
+ * taken: blocks of 32 consecutive elements (one Q4_K sub-block), one f32
+ * scale d = amax / 127 with amax the largest |x| of the block (NaN when the
+ * block holds a NaN), and codes q = the nearest-even integer of x * (127 /
+ * amax), that product and quotient rounded to f32; q = 0 where amax is 0 or
+ * not a number, or where the product is not finite.
+ * ------------------------------------------------------------------------- */
+int oq_quantize_q8(const float* x, int64_t k, int8_t* q, float* d)
+{
+    if (k <= 0 || k % 32 != 0) {
+        return -1;
+    }
+    for (int64_t b = 0; b < k / 32; ++b) {
+        const float* xb = x + 32 * b;
+        float amax = 0.0f;
+        int has_nan = 0;
+        for (int t = 0; t < 32; ++t) {
+            const float a = fabsf(xb[t]);
+            if (a != a) {
+                has_nan = 1;
+            } else if (a > amax) {
+                amax = a;
+            }
+        }
+        if (has_nan) {
+            amax = NAN;
+        }
+        const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
+        d[b] = amax / 127.0f;
+        for (int t = 0; t < 32; ++t) {
+            const float v = xb[t] * inv;
+            q[32 * b + t] = (int8_t)(isfinite(v) ? (int)rintf(v) : 0);
+        }
+    }
+    return 0;
+}
+
+/* The GEMV against Q8 activations: y[b][r] = sum_c w[r][c] * xq[b][c] and
+ * bound[b][r] = sum_c |w[r][c]| |xq[b][c]| in f64, where xq = d * q (exact
+ * in f64) for the block of c.  q: m x k codes, d: m x k/32 scales. */
+int oq_gemv_q8(const uint8_t* w, const int8_t* q, const float* d, int64_t n, int64_t k,
+               int64_t m, double* y, double* bound)
+{
+    if (!oq_shape_ok(n, k) || m < 1) {
+        return -1;
+    }
+    int bad = 0;
+#pragma omp parallel
+    {
+        float* wrow = (float*)malloc((size_t)k * sizeof(float));
+        if (!wrow) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+            const int64_t S = k / OQ_QK;
+#pragma omp for schedule(static)
+            for (int64_t r = 0; r < n; ++r) {
+                for (int64_t s = 0; s < S; ++s) {
+                    oq_dequant_superblock(w + (r * S + s) * OQ_SB, wrow + s * OQ_QK);
+                }
+                for (int64_t b = 0; b < m; ++b) {
+                    double acc = 0.0, mag = 0.0;
+                    for (int64_t c = 0; c < k; ++c) {
+                        const double wv = (double)wrow[c];
+                        const double xv = (double)d[b * (k / 32) + c / 32] * (double)q[b * k + c];
+                        acc += wv * xv;
+                        mag += fabs(wv) * fabs(xv);
+                    }
+                    y[b * n + r] = acc;
+                    if (bound) {
+                        bound[b * n + r] = mag;
+                    }
+                }
+            }
+            free(wrow);
+        }
+    }
+    return bad ? -2 : 0;
 }
 
 int oq_num_threads(void)

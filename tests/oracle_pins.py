@@ -416,6 +416,95 @@ def check_shape_errors(oracle_mod):
     assert y.shape == (1, 0)
 
 
+# ------------------------------------------------- Q8 activations (variant)
+# The Q8 block format is a reading (see oracle/q4k_oracle.c): blocks of 32,
+# d = amax/127, codes the nearest-even integer of x*(127/amax).  Pinned by
+# facts that hold whatever the implementation: exact round trips of dyadic
+# blocks, closed forms of constant, zero, one-hot and mirrored blocks, the
+# rounding bound, non-finite blocks, and the Q8 GEMV equal to the pinned
+# f32 GEMV where the quantized x is x itself.
+
+def _dyadic_q8_blocks(rng, m, nblk):
+    """x = j * 2^e, integer j in [-127, 127] with one |j| = 127 per block,
+    e per block in -60..60: amax = 127 * 2^e, so d = 2^e and the codes are j."""
+    j = rng.integers(-127, 128, size=(m, nblk, 32))
+    pos = rng.integers(0, 32, size=(m, nblk))
+    sign = rng.choice([-1, 1], size=(m, nblk))
+    for b in range(m):
+        for t in range(nblk):
+            j[b, t, pos[b, t]] = 127 * sign[b, t]
+    e = rng.integers(-60, 61, size=(m, nblk))
+    x = (j * np.exp2(e)[:, :, None]).astype(np.float32).reshape(m, nblk * 32)
+    return x, j.reshape(m, nblk * 32).astype(np.int8), np.exp2(e).astype(np.float32)
+
+
+def check_q8_dyadic_round_trip(oracle_mod):
+    rng = np.random.default_rng(901)
+    x, j, d = _dyadic_q8_blocks(rng, 3, 40)
+    q, dq = oracle_mod.quantize_q8(x)
+    assert np.array_equal(q, j)
+    assert np.array_equal(dq.view(np.uint32), d.view(np.uint32))
+
+
+def check_q8_closed_forms(oracle_mod):
+    # constant positive block: all codes 127, d = c / 127 (f32); zero block:
+    # d = 0, codes 0; one nonzero element: its code +-127, the rest 0;
+    # the mirrored block: codes negated, the same scale
+    rng = np.random.default_rng(902)
+    c = np.float32(rng.uniform(0.5, 3.0))
+    x = np.zeros((1, 128), np.float32)
+    x[0, :32] = c
+    x[0, 64 + 5] = -np.float32(7.25)
+    x[0, 96:] = rng.standard_normal(32).astype(np.float32)
+    q, d = oracle_mod.quantize_q8(x)
+    assert np.all(q[0, :32] == 127) and d[0, 0] == np.float32(c / np.float32(127.0))
+    assert np.all(q[0, 32:64] == 0) and d[0, 1] == 0.0
+    assert q[0, 64 + 5] == -127 and np.count_nonzero(q[0, 64:96]) == 1
+    assert d[0, 2] == np.float32(np.float32(7.25) / np.float32(127.0))
+    qn, dn = oracle_mod.quantize_q8(-x)
+    assert np.array_equal(qn, -q) and np.array_equal(dn, d)
+
+
+def check_q8_rounding_bound(oracle_mod):
+    # |x - d q| <= d/2 (1 + 2^-20) + 2^-21 |x| and |q| <= 127, x spread over
+    # many binades
+    rng = np.random.default_rng(903)
+    x = (rng.standard_normal((4, 2048)) * np.exp2(rng.integers(-30, 31, size=(4, 64, 1))).repeat(
+        32, axis=2).reshape(4, 2048)).astype(np.float32)
+    q, d = oracle_mod.quantize_q8(x)
+    assert np.all(np.abs(q.astype(int)) <= 127)
+    dd = np.repeat(d.astype(np.float64), 32, axis=1)
+    err = np.abs(x.astype(np.float64) - dd * q)
+    assert np.all(err <= dd / 2 * (1 + 2.0 ** -20) + 2.0 ** -21 * np.abs(x.astype(np.float64)))
+    # the largest element of each block takes code +-127
+    amax = np.abs(x).reshape(4, 64, 32).max(axis=2)
+    qmax = np.abs(q.astype(int)).reshape(4, 64, 32).max(axis=2)
+    assert np.all(qmax[amax > 0] == 127)
+
+
+def check_q8_non_finite_blocks(oracle_mod):
+    x = np.ones((1, 96), np.float32)
+    x[0, 3] = np.nan
+    x[0, 40] = np.inf
+    q, d = oracle_mod.quantize_q8(x)
+    assert np.isnan(d[0, 0]) and np.all(q[0, :32] == 0)
+    assert np.isinf(d[0, 1]) and np.all(q[0, 32:64] == 0)
+    assert d[0, 2] == np.float32(1.0 / np.float32(127.0)) and np.all(q[0, 64:] == 127)
+
+
+def check_q8_gemv_equals_f32_gemv_on_dyadic_x(oracle_mod):
+    # where d q = x exactly (dyadic blocks), the Q8 GEMV is the pinned f32 GEMV
+    rng = np.random.default_rng(904)
+    n, k, m = 7, 512, 2
+    w = synth.pack(synth.draw_fields(np.random.default_rng(905), n, k // 256))
+    x, j, d = _dyadic_q8_blocks(rng, m, k // 32)
+    x = (x * np.float32(2.0 ** -70)).astype(np.float32)     # products well inside f64
+    d = (d * np.float32(2.0 ** -70)).astype(np.float32)
+    y, bound = oracle_mod.gemv(w, x, n)
+    yq, bq = oracle_mod.gemv_q8(w, j, d, n)
+    assert np.array_equal(y, yq) and np.array_equal(bound, bq)
+
+
 # fastest first: the mutation test stops at the first failing check
 ALL_CHECKS = (
     check_golden_handbuilt_superblock,
@@ -435,4 +524,9 @@ ALL_CHECKS = (
     check_quantizer_round_trip,
     check_f16_encode_rne_matches_numpy,
     check_scale_pack_unpack_exhaustive,
+    check_q8_dyadic_round_trip,
+    check_q8_closed_forms,
+    check_q8_rounding_bound,
+    check_q8_non_finite_blocks,
+    check_q8_gemv_equals_f32_gemv_on_dyadic_x,
 )

@@ -44,6 +44,11 @@ MUTANTS = {
     "encoder_truncates": ("double sig = nearbyint(ldexp(fr, 11));", "double sig = floor(ldexp(fr, 11));"),
     "quantizer_min_sign": ("q = oq_clampi(nearbyint(((double)xs[e] + dm) / dsc), 0, 15);",
                            "q = oq_clampi(nearbyint(((double)xs[e] - dm) / dsc), 0, 15);"),
+    "q8_truncates": ("(int)rintf(v)", "(int)truncf(v)"),
+    "q8_scale_128": ("d[b] = amax / 127.0f;", "d[b] = amax / 128.0f;"),
+    "q8_nan_ignored": ("            amax = NAN;\n", "            amax = amax;\n"),
+    "q8_block_scale_index": ("(double)d[b * (k / 32) + c / 32]", "(double)d[b * (k / 32) + c / 64]"),
+    "q8_codes_of_vector_0": ("(double)q[b * k + c]", "(double)q[c]"),
 }
 
 
