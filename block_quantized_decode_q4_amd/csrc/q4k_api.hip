@@ -119,7 +119,8 @@ int make_plan_lines(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t
         return Q4K_ERR_UNSUPPORTED;    // 1024-lane workgroups cap a lane at 128 VGPRs,
                                        // below what the exact x terms need
     }
-    if (kernel == 3 && (m != 1 || S * 16 > 4 * 64 * nw || (S % 8 != 0 && ring != 3))) {
+    if ((kernel == 3 || kernel == 8) &&
+        (m != 1 || S * 16 > 4 * 64 * nw || (S % 8 != 0 && ring != 3))) {
         return Q4K_ERR_UNSUPPORTED;    // one vector; x in at most four groups per lane;
                                        // rows of any length: three lines in flight
     }
@@ -151,7 +152,8 @@ int make_plan_lines(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t
         // all of x, which costs as much as decoding a few tiles
         rpb = 16 * ((ntiles + 255) / 256);
     }
-    const size_t lds_x = kernel == 7   ? q4k::win_lds_bytes(S, (int)m)
+    const size_t lds_x = kernel == 8   ? q4k::q8_lds_bytes(S, nw)
+                         : kernel == 7 ? q4k::win_lds_bytes(S, (int)m)
                          : kernel == 6 ? q4k::jit_lds_bytes(S, (int)m)
                          : kernel == 5 ? q4k::sub_lds_bytes(S, (int)m)
                          : kernel == 3 ? q4k::dot4_lds_bytes(S, nw)
@@ -569,6 +571,66 @@ int q4k_dequantize(const void* w, float* out, int64_t n, int64_t k, void* stream
         return Q4K_ERR_SHAPE;
     }
     return hip_status(q4k::launch_dequant(w, out, nsb, static_cast<hipStream_t>(stream)));
+}
+
+int q4k_gemv_q8(const void* w, const float* x, float* y, int64_t n, int64_t k, int64_t m,
+                void* stream)
+{
+    if (!w || !x || !y) {
+        return Q4K_ERR_NULL;
+    }
+    int rc = check_nk(n, k);
+    if (rc != Q4K_OK) {
+        return rc;
+    }
+    if (m < 1) {
+        return Q4K_ERR_SHAPE;
+    }
+    if (m != 1) {
+        return Q4K_ERR_UNSUPPORTED;    // one vector (the pages' decode GEMV)
+    }
+    if (!aligned16(w) || !aligned16(x) || !aligned16(y)) {
+        return Q4K_ERR_ALIGN;
+    }
+    if ((reinterpret_cast<uintptr_t>(w) & 127u) != 0) {
+        return Q4K_ERR_UNSUPPORTED;    // whole-line reads need 128-byte aligned rows
+    }
+    GemvPlan plan;
+    rc = make_plan_lines(n, k, 1, nullptr, SIZE_MAX, &plan, 8);
+    if (rc != Q4K_OK) {
+        return rc;
+    }
+    size_t lds_max = 0;
+    rc = device_lds_max(&lds_max);
+    if (rc != Q4K_OK) {
+        return rc;
+    }
+    rc = make_plan_lines(n, k, 1, nullptr, lds_max, &plan, 8);
+    if (rc != Q4K_OK) {
+        return rc;
+    }
+    if (plan.lds_bytes > lds_max) {
+        return Q4K_ERR_UNSUPPORTED;
+    }
+    return hip_status(q4k::launch_gemv_q8(plan, w, x, y, static_cast<hipStream_t>(stream)));
+}
+
+int q4k_quantize_q8(const float* x, int8_t* q, float* d, int64_t k, int64_t m, void* stream)
+{
+    if (!x || !q || !d) {
+        return Q4K_ERR_NULL;
+    }
+    if (k < 32 || k % 32 != 0 || m < 1 || k > kInt32Max || m > kInt32Max) {
+        return Q4K_ERR_SHAPE;
+    }
+    if (!aligned16(x) || !aligned16(q) || !aligned16(d)) {
+        return Q4K_ERR_ALIGN;
+    }
+    const int64_t nblocks = m * (k / 32);
+    if ((nblocks + 255) / 256 > kInt32Max) {
+        return Q4K_ERR_SHAPE;
+    }
+    return hip_status(q4k::launch_quantize_q8(x, q, d, nblocks, static_cast<hipStream_t>(stream)));
 }
 
 const char* q4k_status_string(int rc)

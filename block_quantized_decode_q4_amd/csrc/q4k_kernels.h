@@ -51,6 +51,12 @@ hipError_t launch_gemv_dot4(const GemvPlan& p, const void* w, const float* x, fl
                             hipStream_t stream);
 size_t dot4_lds_bytes(int S, int waves);
 hipError_t launch_dequant(const void* w, float* out, int64_t nsb, hipStream_t stream);
+// the integer-dot variant with x quantized to Q8 (q4k_q8.hip)
+hipError_t launch_gemv_q8(const GemvPlan& p, const void* w, const float* x, float* y,
+                          hipStream_t stream);
+hipError_t launch_quantize_q8(const float* x, int8_t* q, float* d, int64_t nblocks,
+                              hipStream_t stream);
+size_t q8_lds_bytes(int S, int waves);
 hipError_t launch_read(const void* buf, size_t n16, float* out, hipStream_t stream);
 
 }  // namespace q4k

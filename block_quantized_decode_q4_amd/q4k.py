@@ -34,6 +34,8 @@ EXPORTED = (
     "q4k_read_calibrate",
     "q4k_read_calibrate_blocks",
     "q4k_plan",
+    "q4k_gemv_q8",
+    "q4k_quantize_q8",
 )
 
 
@@ -101,6 +103,10 @@ def load_library():
         lib.q4k_gemv_ex.restype = ctypes.c_int
         lib.q4k_dequantize.argtypes = [vp, vp, i64, i64, vp]
         lib.q4k_dequantize.restype = ctypes.c_int
+        lib.q4k_gemv_q8.argtypes = [vp, vp, vp, i64, i64, i64, vp]
+        lib.q4k_gemv_q8.restype = ctypes.c_int
+        lib.q4k_quantize_q8.argtypes = [vp, vp, vp, i64, i64, vp]
+        lib.q4k_quantize_q8.restype = ctypes.c_int
         lib.q4k_status_string.argtypes = [ctypes.c_int]
         lib.q4k_status_string.restype = ctypes.c_char_p
         lib.q4k_read_calibrate.argtypes = [vp, ctypes.c_size_t, vp, vp]
@@ -183,6 +189,20 @@ def q4k_dequantize(w, out, n: int, k: int, stream=None) -> None:
     """out[r*k + c] = W[r][c] in f32 (bit-exact); asynchronous on stream."""
     _check(load_library().q4k_dequantize(_addr(w), _addr(out), int(n), int(k), _stream(stream)),
            "q4k_dequantize")
+
+
+def q4k_gemv_q8(w, x, y, n: int, k: int, m: int = 1, stream=None) -> None:
+    """y = W x with x quantized to Q8 inside the kernel (the integer-dot
+    variant, its own tolerance: see include/q4k.h); asynchronous."""
+    _check(load_library().q4k_gemv_q8(_addr(w), _addr(x), _addr(y), int(n), int(k), int(m),
+                                      _stream(stream)), "q4k_gemv_q8")
+
+
+def q4k_quantize_q8(x, q, d, k: int, m: int = 1, stream=None) -> None:
+    """The Q8 codes (int8, m x k) and scales (f32, m x k/32) of x (f32, m x k)
+    that q4k_gemv_q8 uses; asynchronous."""
+    _check(load_library().q4k_quantize_q8(_addr(x), _addr(q), _addr(d), int(k), int(m),
+                                          _stream(stream)), "q4k_quantize_q8")
 
 
 def q4k_plan(n: int, k: int, m: int = 1, w_aligned128: bool = True, lds_max: int = 0,

@@ -109,6 +109,36 @@ int q4k_gemv(const void* w, const float* x, float* y,
  * Asynchronous on `stream`. */
 int q4k_dequantize(const void* w, float* out, int64_t n, int64_t k, void* stream);
 
+/* The integer-dot variant: the Q8 quantize kernel and the DP4A Q4_K GEMV
+ * that realizar 0.8.5 preloads together (src/cuda/executor/layers/
+ * modules_utilities.rs, `preload_hw_dp4a_modules`), fused into one launch.
+ * x is quantized inside the kernel in blocks of 32 consecutive elements
+ * (one Q4_K sub-block; the block format is a reading, the pages name the
+ * kernels only): d = amax/127 in f32, amax the largest |x| of the block (NaN
+ * when the block holds a NaN), int8 codes q = nearest-even integer of
+ * x * (127/amax) (quotient and product rounded to f32; 0 where amax is 0
+ * or NaN, or the product is not finite) -- exactly what q4k_quantize_q8
+ * writes.  Then y = sum_c w * d * q with exact int32 code sums, each
+ * sub-block rounded once in f64 at its scale d, and y rounded once to f32.
+ *  w : device, as for q4k_gemv, 128-byte aligned (whole-line reads)
+ *  x : device, k f32, 16-byte aligned;  y : device, n f32, 16-byte aligned,
+ *  overwritten.  m must be 1 (Q4K_ERR_UNSUPPORTED otherwise); k as for
+ *  q4k_gemv, at most 4096 * 4 * 8 (x staged whole).
+ * Its own tolerance (not q4k_gemv's): |y - y_ref| <= sum_e |w_e| (d_b(e)/2 *
+ * (1 + 2^-19) + 2^-20 |x_e|) + 2^-23 |y_ref|, y_ref the exact GEMV with the
+ * f32 x (a code carries its x to within d/2 (1 + 2^-20) + 2^-21 |x|);
+ * against the exact GEMV of the quantized x (d*q) it is within
+ * 2^-23 |y| + 1e-9 sum|w||d q|.  Non-finite x make y NaN.  Asynchronous on
+ * `stream`; allocates nothing. */
+int q4k_gemv_q8(const void* w, const float* x, float* y, int64_t n, int64_t k, int64_t m,
+                void* stream);
+
+/* The Q8 quantization of q4k_gemv_q8 on its own (tests, and callers that
+ * keep x in Q8): q[b*k + c] int8 codes and d[b*(k/32) + c/32] f32 scales of
+ * the m vectors of x (m x k f32).  All three pointers device and 16-byte
+ * aligned; k a positive multiple of 32.  Asynchronous on `stream`. */
+int q4k_quantize_q8(const float* x, int8_t* q, float* d, int64_t k, int64_t m, void* stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char* q4k_status_string(int rc);
 

@@ -326,3 +326,19 @@ def test_plan_window(n, k, m, rpb):
     assert p.kernel == 7 and p.cols_per_task == 8 and p.threads == 512
     assert p.rows_per_block == rpb
     assert (rpb + 15) // 16 * (k // 2048) <= 8
+
+
+def test_q8_refusals(lib):
+    """The Q8 variant's argument checks, before any HIP call."""
+    assert lib.q4k_gemv_q8(None, A, A, 16, 256, 1, None) == q4k.Q4K_ERR_NULL
+    assert lib.q4k_gemv_q8(A, A, A, 16, 300, 1, None) == q4k.Q4K_ERR_SHAPE
+    assert lib.q4k_gemv_q8(A, A, A, 0, 256, 1, None) == q4k.Q4K_ERR_SHAPE
+    assert lib.q4k_gemv_q8(A, A, A, 16, 256, 0, None) == q4k.Q4K_ERR_SHAPE
+    assert lib.q4k_gemv_q8(A, A, A, 16, 256, 2, None) == q4k.Q4K_ERR_UNSUPPORTED   # one vector
+    assert lib.q4k_gemv_q8(A, MIS, A, 16, 256, 1, None) == q4k.Q4K_ERR_ALIGN
+    assert lib.q4k_gemv_q8(A + 16, A, A, 16, 256, 1, None) == q4k.Q4K_ERR_UNSUPPORTED  # not 128-B aligned
+    assert lib.q4k_quantize_q8(None, A, A, 64, 1, None) == q4k.Q4K_ERR_NULL
+    assert lib.q4k_quantize_q8(A, A, A, 48, 1, None) == q4k.Q4K_ERR_SHAPE
+    assert lib.q4k_quantize_q8(A, A, A, 0, 1, None) == q4k.Q4K_ERR_SHAPE
+    assert lib.q4k_quantize_q8(A, A, A, 64, 0, None) == q4k.Q4K_ERR_SHAPE
+    assert lib.q4k_quantize_q8(A, A, MIS, 64, 1, None) == q4k.Q4K_ERR_ALIGN
