@@ -133,7 +133,7 @@ def cpu_baseline(w, x, n, k, m, weight_bytes, y_gpu, target_s=12.0):
 
 KERNEL_NAMES = {1: "gemv_kernel", 2: "gemv_stream_kernel", 3: "gemv_dot4_lines_kernel",
                 4: "gemv_i8_lines_kernel", 5: "gemv_i8_sub_kernel (x staged)",
-                6: "gemv_i8_sub_kernel (x per wave)"}
+                6: "gemv_i8_sub_kernel (x per wave)", 7: "gemv_i8_sub_kernel (x window)"}
 
 # The arithmetic each kernel computes in (the plan's kernel number)
 KERNEL_DTYPE = {
@@ -147,6 +147,8 @@ KERNEL_DTYPE = {
     4: ("i8x4-x/i32/f64", "as kernel 3, digit sums on int8 matrix cores (16x16x64)"),
     5: ("i8x4-x/i32/f64", "as kernel 3, digit sums on int8 matrix cores (16x16x32), x staged whole"),
     6: ("i8x4-x/i32/f64", "as kernel 5, x converted per column by each wave"),
+    7: ("i8x4-x/i32/f64", "as kernel 5, x converted once per workgroup into a two-column "
+                          "window of every slab"),
 }
 
 
@@ -263,6 +265,31 @@ def main() -> int:
     torch.cuda.synchronize()
     one_us = c0.elapsed_time(c1) * 1e3 / one_reps
 
+    # the integer-dot variant with Q8 activations (m = 1 only; its own
+    # tolerance): the same rotation, after the headline measurement
+    q8 = None
+    if m == 1 and (ptrs[0] % 128) == 0:
+        def step_q8(i):
+            rc = lib.q4k_gemv_q8(ptrs[i % copies], xp, yp, n, k, 1, sp)
+            if rc != 0:
+                raise q4k.Q4KError(rc, "q4k_gemv_q8")
+        q8_steps = max(100, min(args.steps, 5000))
+        for i in range(min(args.warmup, 5000)):
+            step_q8(i)
+        torch.cuda.synchronize()
+        c0.record(stream)
+        for i in range(q8_steps):
+            step_q8(i)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        q8_us = c0.elapsed_time(c1) * 1e3 / q8_steps
+        q8 = {"entry": "q4k_gemv_q8", "us_per_step": round(q8_us, 3), "steps": q8_steps,
+              "value": round(wb / q8_us / 1e3, 2), "unit": "GB/s",
+              "frac_of_hbm_peak": round((wb + 4 * k + 4 * n) / q8_us / 1e3 / HBM_PEAK_GBPS, 4),
+              "numerics": "x as Q8 (int8 codes, one f32 scale per 32 elements), int32 dot4, "
+                          "f64 scaling; its own tolerance sum|w|(d/2(1+2^-19) + 2^-20|x|) + "
+                          "2^-23|y_ref|"}
+
     alg_bytes = wb + 4 * k * m + 4 * n * m
     achieved = alg_bytes / t_launch / 1e9
     traffic = committed_traffic(wl.name)
@@ -309,6 +336,8 @@ def main() -> int:
                         "read_one_copy_us": round(one_us, 3),
                         "read_one_copy_gbps": round(wbr / one_us / 1e3, 2)},
     }
+    if q8 is not None:
+        out["q8_variant"] = q8
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline(w, x, n, k, m, wb, y_last)

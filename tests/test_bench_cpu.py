@@ -51,3 +51,15 @@ def test_kernel_source_hash_follows_the_sources(tmp_path, monkeypatch):
     (src / "b.h").rename(src / "c.h")
     h4 = bench.kernel_source_hash()
     assert len({h1, h2, h3, h4}) == 4
+
+
+def test_every_kernel_has_a_dtype_and_name():
+    """bench.py names the arithmetic of whatever kernel the plan picks."""
+    import importlib.util
+    import os
+    spec = importlib.util.spec_from_file_location(
+        "bench_mod", os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                                  "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    assert set(mod.KERNEL_DTYPE) == set(range(1, 8)) == set(mod.KERNEL_NAMES)
