@@ -14,6 +14,10 @@ Functions (names follow the problem's notation: d, dmin, sc_j, m_j, q):
   dequant(w, n, k)            f32 weights [n, k], one rounding per weight
   gemv(w, x)                  y and sum|w||x| in f64, x is [m, k]
   quantize_rows(x)            simple reference quantizer -> Q4_K bytes
+  quantize_q8(x), gemv_q8     Q8 activations and the GEMV over them
+  q6k_dequant_superblock(b)   one 210-byte Q6_K superblock -> 256 f32
+  q6k_dequant(w, n, k)        Q6_K weights [n, k] (exact products)
+  q6k_gemv(w, x, n)           the same GEMV over Q6_K weights
 """
 from __future__ import annotations
 
@@ -81,6 +85,12 @@ def _load():
         lib.oq_quantize_q8.restype = ctypes.c_int
         lib.oq_gemv_q8.argtypes = [u8p, i8p, f32p, i64, i64, i64, f64p, f64p]
         lib.oq_gemv_q8.restype = ctypes.c_int
+        lib.oq6_dequant_superblock.argtypes = [u8p, f32p]
+        lib.oq6_dequant_superblock.restype = None
+        lib.oq6_dequant.argtypes = [u8p, i64, i64, i64, f32p]
+        lib.oq6_dequant.restype = ctypes.c_int
+        lib.oq6_gemv.argtypes = [u8p, f32p, i64, i64, i64, i64, f64p, f64p]
+        lib.oq6_gemv.restype = ctypes.c_int
         lib.oq_num_threads.argtypes = []
         lib.oq_num_threads.restype = ctypes.c_int
         lib.oq_set_num_threads.argtypes = [ctypes.c_int]
@@ -249,4 +259,64 @@ def gemv_q8(w, q, d, n: int) -> tuple[np.ndarray, np.ndarray]:
                         n, k, m, _ptr(y, ctypes.c_double), _ptr(bound, ctypes.c_double))
     if rc != 0:
         raise RuntimeError("oq_gemv_q8 rc=%d" % rc)
+    return y, bound
+
+
+Q6K_SB_BYTES = 210
+
+
+def _q6k_stride(w: np.ndarray, n: int, k: int, row_stride: int) -> int:
+    if k <= 0 or k % QK != 0 or n < 0:
+        raise ValueError("bad shape n=%d k=%d" % (n, k))
+    dense = (k // QK) * Q6K_SB_BYTES
+    stride = dense if row_stride == 0 else int(row_stride)
+    if stride < dense:
+        raise ValueError("row_stride %d below the %d bytes of a row" % (stride, dense))
+    if n > 0 and w.size < (n - 1) * stride + dense:
+        raise ValueError("weight bytes %d too few for n=%d rows of stride %d" % (w.size, n, stride))
+    return stride
+
+
+def q6k_dequant_superblock(blk) -> np.ndarray:
+    lib = _load()
+    b = _u8(blk)
+    assert b.size == Q6K_SB_BYTES
+    out = np.empty(QK, dtype=np.float32)
+    lib.oq6_dequant_superblock(_ptr(b, ctypes.c_uint8), _ptr(out, ctypes.c_float))
+    return out
+
+
+def q6k_dequant(w, n: int, k: int, row_stride: int = 0) -> np.ndarray:
+    """Q6_K weights as f32 [n, k]; row r starts at byte r * row_stride
+    (0: rows packed densely, 210 k / 256 bytes each)."""
+    lib = _load()
+    wb = _u8(w)
+    stride = _q6k_stride(wb, n, k, row_stride)
+    out = np.empty((n, k), dtype=np.float32)
+    if n == 0:
+        return out
+    rc = lib.oq6_dequant(_ptr(wb, ctypes.c_uint8), n, k, stride, _ptr(out, ctypes.c_float))
+    if rc != 0:
+        raise RuntimeError("oq6_dequant rc=%d" % rc)
+    return out
+
+
+def q6k_gemv(w, x, n: int, row_stride: int = 0) -> tuple[np.ndarray, np.ndarray]:
+    """y[b, r] and bound[b, r] = sum_c |w[r,c]| |x[b,c]| over Q6_K weights,
+    both float64 [m, n]."""
+    lib = _load()
+    xa = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    if xa.ndim == 1:
+        xa = xa.reshape(1, -1)
+    m, k = xa.shape
+    wb = _u8(w)
+    stride = _q6k_stride(wb, n, k, row_stride)
+    y = np.empty((m, n), dtype=np.float64)
+    bound = np.empty((m, n), dtype=np.float64)
+    if n == 0:
+        return y, bound
+    rc = lib.oq6_gemv(_ptr(wb, ctypes.c_uint8), _ptr(xa, ctypes.c_float), n, k, stride, m,
+                      _ptr(y, ctypes.c_double), _ptr(bound, ctypes.c_double))
+    if rc != 0:
+        raise RuntimeError("oq6_gemv rc=%d" % rc)
     return y, bound

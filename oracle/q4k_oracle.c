@@ -38,7 +38,10 @@
  * quantizer round-trip; for the Q8 activations: exact round trips of
  * dyadic blocks, constant, zero, one-hot and mirrored blocks, the rounding
  * bound, non-finite blocks, and the Q8 GEMV against the f32 GEMV where the
- * quantized x is x itself.
+ * quantized x is x itself; for Q6_K: a hand-computed golden superblock,
+ * one-hot brute force over every element and code bit against an
+ * independently written packer, every weight equal to the exact product of
+ * its fields, closed forms, exact dyadic dots, special d, row strides.
  */
 #include <math.h>
 #include <stdint.h>
@@ -403,6 +406,123 @@ int oq_gemv_q8(const uint8_t* w, const int8_t* q, const float* d, int64_t n, int
                     for (int64_t c = 0; c < k; ++c) {
                         const double wv = (double)wrow[c];
                         const double xv = (double)d[b * (k / 32) + c / 32] * (double)q[b * k + c];
+                        acc += wv * xv;
+                        mag += fabs(wv) * fabs(xv);
+                    }
+                    y[b * n + r] = acc;
+                    if (bound) {
+                        bound[b * n + r] = mag;
+                    }
+                }
+            }
+            free(wrow);
+        }
+    }
+    return bad ? -2 : 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Q6_K, the other block format of the decode loop (realizar 0.8.5,
+ * q4k_gemv_cached.rs, doc of `q6k_gemv_cached_async`: the same GEMV over
+ * Q6_K weights, used for an LM head stored as Q6_K; memra-engine 0.83.1,
+ * src/f16_ffi.rs, doc of `memra_q6_K_dequant_f16` and `ensure_f16_mirror`:
+ * 210-byte superblocks of 256 weights, in_f / 256 of them per row).
+ * The field layout inside the 210 bytes is not printed on the pages; the
+ * reading taken is the GGUF Q6_K layout:
+ *   bytes   0..127  ql: the low four bits of the codes,
+ *   bytes 128..191  qh: the high two bits,
+ *   bytes 192..207  sixteen signed 8-bit scales, scale s for elements
+ *                   16 s .. 16 s + 15,
+ *   bytes 208..209  fp16 d (little-endian).
+ * Element e = 128 h + 32 t + l (h = 0, 1; t = 0..3; l = 0..31) takes its low
+ * bits from ql byte 64 h + 32 (t % 2) + l (the low nibble for t < 2, the high
+ * one for t >= 2) and its high bits from bits 2 t, 2 t + 1 of qh byte
+ * 32 h + l; its code q is 0..63 and its weight w = d * sc * (q - 32).
+ * ------------------------------------------------------------------------- */
+#define OQ6_SB 210
+
+/* code (0..63) and scale index of element e (0..255) of a Q6_K superblock */
+static void oq6_element_code(const uint8_t* blk, int e, int* s, int* q)
+{
+    const int h = e / 128;
+    const int t = (e % 128) / 32;
+    const int l = e % 32;
+    const uint8_t lo_byte = blk[64 * h + 32 * (t % 2) + l];
+    const uint8_t hi_byte = blk[128 + 32 * h + l];
+    const int lo = (t < 2) ? (lo_byte % 16) : (lo_byte / 16);
+    const int hi = (hi_byte >> (2 * t)) % 4;
+    *q = lo + 16 * hi;
+    *s = e / 16;
+}
+
+/* Dequantize one 210-byte superblock to 256 floats: w = (d * sc) * (q - 32).
+ * d has at most 11 significant bits, |sc| <= 128 and |q - 32| <= 32, so both
+ * products are exact in binary32 (at most 11 + 7 + 5 significant bits, far
+ * from overflow and underflow): every weight is the exact value of its
+ * fields, with no rounding at all. */
+void oq6_dequant_superblock(const uint8_t* blk, float* out)
+{
+    const float d = oq_f16_to_f32((uint16_t)(blk[208] | (blk[209] << 8)));
+    for (int e = 0; e < OQ_QK; ++e) {
+        int s, q;
+        oq6_element_code(blk, e, &s, &q);
+        const float sc = (float)(int8_t)blk[192 + s];
+        const float dsc = d * sc;
+        out[e] = dsc * (float)(q - 32);
+    }
+}
+
+/* Rows of k / 256 superblocks, row r starting at byte r * row_stride
+ * (row_stride >= 210 k / 256).  Returns 0, or -1 on a bad shape. */
+static int oq6_shape_ok(int64_t n, int64_t k, int64_t row_stride)
+{
+    return oq_shape_ok(n, k) && row_stride >= (k / OQ_QK) * OQ6_SB;
+}
+
+/* out[r][c] for r < n, c < k. */
+int oq6_dequant(const uint8_t* w, int64_t n, int64_t k, int64_t row_stride, float* out)
+{
+    if (!oq6_shape_ok(n, k, row_stride)) {
+        return -1;
+    }
+    const int64_t S = k / OQ_QK;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; ++r) {
+        for (int64_t s = 0; s < S; ++s) {
+            oq6_dequant_superblock(w + r * row_stride + s * OQ6_SB, out + r * k + s * OQ_QK);
+        }
+    }
+    return 0;
+}
+
+/* y[b][r] = sum_c W[r][c] x[b][c] and bound[b][r] = sum_c |W[r][c]| |x[b][c]|,
+ * in f64 over the f32 weights, for b < m (both m x n, row-major). */
+int oq6_gemv(const uint8_t* w, const float* x, int64_t n, int64_t k, int64_t row_stride,
+             int64_t m, double* y, double* bound)
+{
+    if (!oq6_shape_ok(n, k, row_stride) || m < 1) {
+        return -1;
+    }
+    int bad = 0;
+#pragma omp parallel
+    {
+        float* wrow = (float*)malloc((size_t)k * sizeof(float));
+        if (!wrow) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+            const int64_t S = k / OQ_QK;
+#pragma omp for schedule(static)
+            for (int64_t r = 0; r < n; ++r) {
+                for (int64_t s = 0; s < S; ++s) {
+                    oq6_dequant_superblock(w + r * row_stride + s * OQ6_SB, wrow + s * OQ_QK);
+                }
+                for (int64_t b = 0; b < m; ++b) {
+                    const float* xb = x + b * k;
+                    double acc = 0.0, mag = 0.0;
+                    for (int64_t c = 0; c < k; ++c) {
+                        const double wv = (double)wrow[c];
+                        const double xv = (double)xb[c];
                         acc += wv * xv;
                         mag += fabs(wv) * fabs(xv);
                     }

@@ -505,6 +505,208 @@ def check_q8_gemv_equals_f32_gemv_on_dyadic_x(oracle_mod):
     assert np.array_equal(y, yq) and np.array_equal(bound, bq)
 
 
+# ------------------------------------------------------------------ Q6_K
+# The Q6_K field layout is a reading (GGUF Q6_K; see oracle/q4k_oracle.c).
+# Pinned by a hand-computed superblock, by bytes placed element by element
+# from the layout table here (an inverse written apart from the oracle's
+# decode and from the generator's vectorized packer), by exact products of
+# the fields, closed forms, exact dyadic dots and IEEE special values.
+
+def load_q6k_golden():
+    fields = {"ql": [], "qh": [], "scales": [], "d": []}
+    w = []
+    with open(os.path.join(GOLDEN, "q6k_superblock_handbuilt.txt")) as fh:
+        for line in fh:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            if line.startswith("w "):
+                _, e, v = line.split()
+                w.append((int(e), float(v)))
+                continue
+            key, val = line.split(":", 1)
+            fields[key] += [int(t, 16) for t in val.split()]
+    blk = np.array(fields["ql"] + fields["qh"] + fields["scales"] + fields["d"], dtype=np.uint8)
+    assert blk.size == 210
+    return blk, w
+
+
+def q6k_place(codes, scales, d_bits):
+    """One 210-byte superblock from 256 codes (0..63), 16 int8 scales and the
+    fp16 bits of d, each code's bits placed one element at a time."""
+    b = np.zeros(210, dtype=np.uint8)
+    for e in range(256):
+        h, t, l = e // 128, (e % 128) // 32, e % 32
+        q = int(codes[e])
+        lo, hi = q & 15, q >> 4
+        i = 64 * h + 32 * (t % 2) + l
+        b[i] |= lo if t < 2 else lo << 4
+        b[128 + 32 * h + l] |= hi << (2 * t)
+    b[192:208] = np.asarray(scales, dtype=np.int8).view(np.uint8)
+    b[208] = d_bits & 0xFF
+    b[209] = d_bits >> 8
+    return b
+
+
+def check_q6k_golden_handbuilt_superblock(oracle_mod):
+    blk, w = load_q6k_golden()
+    out = oracle_mod.q6k_dequant_superblock(blk)
+    for e, v in w:
+        assert out[e] == np.float32(v), (e, out[e], v)
+
+
+def check_q6k_golden_through_gemv(oracle_mod):
+    """x = e_i picks out weight i, through the GEMV with two vectors."""
+    blk, w = load_q6k_golden()
+    x = np.zeros((len(w), 256), np.float32)
+    for t, (e, _) in enumerate(w):
+        x[t, e] = 1.0
+    y, bound = oracle_mod.q6k_gemv(blk, x, n=1)
+    for t, (e, v) in enumerate(w):
+        assert y[t, 0] == v and bound[t, 0] == abs(v)
+
+
+def check_q6k_onehot_every_element_and_bit(oracle_mod):
+    """All codes 32 (weight 0) but element e, whose code is 32 with bit b
+    flipped: the one nonzero weight sits at e and equals d sc[e/16] (q - 32)
+    with distinct scales per group.  Every element, every code bit, one
+    superblock per row, in one call."""
+    scales = np.array([3, -5, 7, -11, 13, -17, 19, -23, 29, -31, 37, -41, 43, -47, 53, -59],
+                      np.int8)
+    rows = []
+    expect = []
+    for e in range(256):
+        for bit in range(6):
+            codes = np.full(256, 32, np.int64)
+            codes[e] = 32 ^ (1 << bit)
+            rows.append(q6k_place(codes, scales, F16_ONE))
+            ex = np.zeros(256, np.float32)
+            ex[e] = float(scales[e // 16]) * float(codes[e] - 32)
+            expect.append(ex)
+    w = np.concatenate(rows)
+    out = oracle_mod.q6k_dequant(w, len(rows), 256)
+    assert np.array_equal(out, np.array(expect))
+
+
+def check_q6k_generator_layout_agrees(oracle_mod):
+    """The generator's vectorized packer and the element-wise placement here
+    give the same bytes; decoded, every weight is the exact product of its
+    fields (d has 11 significant bits, |sc| <= 128, |q - 32| <= 32: exact in
+    f32), checked with rational arithmetic."""
+    rng = np.random.default_rng(611)
+    f = synth.draw_q6k_fields(rng, 3, 2)
+    # the extremes of every field in the first superblock
+    f.q[0, 0, :4] = [0, 63, 32, 31]
+    f.sc[0, 0, :2] = [-128, 127]
+    f.d_bits[0, 0] = 0x7BFF                       # largest finite binary16
+    f.d_bits[1, 0] = 0x0001                       # smallest subnormal
+    w = synth.pack_q6k(f)
+    by_hand = np.concatenate([q6k_place(f.q[r, s], f.sc[r, s], int(f.d_bits[r, s]))
+                              for r in range(3) for s in range(2)])
+    assert np.array_equal(w, by_hand)
+    out = oracle_mod.q6k_dequant(w, 3, 512)
+    d = f.d_bits.view(np.float16)
+    for r in range(3):
+        for s in range(2):
+            dv = Fraction(float(d[r, s]))
+            for e in range(256):
+                exact = dv * int(f.sc[r, s, e // 16]) * (int(f.q[r, s, e]) - 32)
+                assert Fraction(float(out[r, 256 * s + e])) == exact, (r, s, e)
+
+
+def check_q6k_closed_forms(oracle_mod):
+    """Codes all 32: W = 0, y = 0 and bound 0.  Uniform code c and scale s,
+    d = 1/2: every weight is s (c - 32) / 2, so y = s (c - 32) / 2 * sum x,
+    exactly for dyadic x."""
+    n, k = 3, 768
+    zero = np.concatenate([q6k_place(np.full(256, 32), np.arange(1, 17), F16_HALF)
+                           for _ in range(n * k // 256)])
+    x = np.random.default_rng(612).standard_normal((2, k)).astype(np.float32)
+    y, bound = oracle_mod.q6k_gemv(zero, x, n)
+    assert np.all(y == 0.0) and np.all(bound == 0.0)
+    c, sv = 45, -9
+    uni = np.concatenate([q6k_place(np.full(256, c), np.full(16, sv), F16_HALF)
+                          for _ in range(n * k // 256)])
+    xd = (np.random.default_rng(613).integers(-64, 65, size=(2, k)) / 8.0).astype(np.float32)
+    y, bound = oracle_mod.q6k_gemv(uni, xd, n)
+    wv = Fraction(sv * (c - 32), 2)
+    for b in range(2):
+        sx = sum(Fraction(float(v)) for v in xd[b])
+        sa = sum(abs(Fraction(float(v))) for v in xd[b])
+        assert all(Fraction(float(v)) == wv * sx for v in y[b])
+        assert all(Fraction(float(v)) == abs(wv) * sa for v in bound[b])
+
+
+def check_q6k_exact_dyadic_dot(oracle_mod):
+    """d = 2^-10, random codes and scales, integer x: every product and sum is
+    exact in f64, so y equals the dot product in integers."""
+    rng = np.random.default_rng(614)
+    n, k = 5, 512
+    codes = rng.integers(0, 64, size=(n, k // 256, 256))
+    scales = rng.integers(-128, 128, size=(n, k // 256, 16))
+    w = np.concatenate([q6k_place(codes[r, s], scales[r, s], 0x1400)      # 2^-10
+                        for r in range(n) for s in range(k // 256)])
+    x = rng.integers(-1000, 1001, size=(3, k)).astype(np.float32)
+    y, _ = oracle_mod.q6k_gemv(w, x, n)
+    for r in range(n):
+        wr = [int(scales[r, c // 256, (c % 256) // 16]) * (int(codes[r, c // 256, c % 256]) - 32)
+              for c in range(k)]
+        for b in range(3):
+            exact = Fraction(sum(wv * int(xv) for wv, xv in zip(wr, x[b])), 1024)
+            assert Fraction(float(y[b, r])) == exact, (r, b)
+
+
+def check_q6k_special_d(oracle_mod):
+    """d = +-0, +-inf, NaN: weights follow IEEE products (inf * 0 is NaN: a
+    zero scale or a code of 32)."""
+    codes = np.arange(256) % 64
+    scales = np.array([0, 1, -1, 5, -128, 127, 2, -2, 0, 3, -3, 4, -4, 7, -7, 1], np.int8)
+    for bits in (0x0000, 0x8000, 0x7C00, 0xFC00, 0x7E00, 0x3C01):
+        out = oracle_mod.q6k_dequant_superblock(q6k_place(codes, scales, bits))
+        d = np.array([bits], np.uint16).view(np.float16).astype(np.float32)[0]
+        with np.errstate(invalid="ignore"):
+            expect = (d * scales.astype(np.float32).repeat(16)) * (codes - 32).astype(np.float32)
+        assert np.array_equal(out.view(np.uint32), expect.astype(np.float32).view(np.uint32)) or (
+            np.array_equal(np.isnan(out), np.isnan(expect))
+            and np.array_equal(out[~np.isnan(out)].view(np.uint32),
+                               expect[~np.isnan(expect)].astype(np.float32).view(np.uint32))), bits
+
+
+def check_q6k_row_stride(oracle_mod):
+    """Rows at a stride above 210 k / 256 bytes decode as the dense rows;
+    the padding bytes (here 0xff) are never read."""
+    rng = np.random.default_rng(615)
+    n, k = 4, 1024
+    f = synth.draw_q6k_fields(rng, n, k // 256)
+    dense = synth.pack_q6k(f)
+    stride = 896
+    padded = synth.pack_q6k(f, stride).reshape(n, stride)
+    padded[:, 840:] = 0xFF
+    padded = padded.reshape(-1)
+    assert np.array_equal(oracle_mod.q6k_dequant(padded, n, k, stride),
+                          oracle_mod.q6k_dequant(dense, n, k))
+    x = rng.standard_normal((2, k)).astype(np.float32)
+    y0, b0 = oracle_mod.q6k_gemv(dense, x, n)
+    y1, b1 = oracle_mod.q6k_gemv(padded, x, n, stride)
+    assert np.array_equal(y0, y1) and np.array_equal(b0, b1)
+
+
+def check_q6k_shape_errors(oracle_mod):
+    for args in ((np.zeros(210, np.uint8), 1, 255), (np.zeros(209, np.uint8), 1, 256)):
+        try:
+            oracle_mod.q6k_dequant(*args)
+        except ValueError:
+            pass
+        else:
+            raise AssertionError("bad shape accepted")
+    try:
+        oracle_mod.q6k_dequant(np.zeros(420, np.uint8), 2, 256, 200)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("row stride below the row accepted")
+
+
 # fastest first: the mutation test stops at the first failing check
 ALL_CHECKS = (
     check_golden_handbuilt_superblock,
@@ -529,4 +731,13 @@ ALL_CHECKS = (
     check_q8_rounding_bound,
     check_q8_non_finite_blocks,
     check_q8_gemv_equals_f32_gemv_on_dyadic_x,
+    check_q6k_golden_handbuilt_superblock,
+    check_q6k_golden_through_gemv,
+    check_q6k_shape_errors,
+    check_q6k_special_d,
+    check_q6k_row_stride,
+    check_q6k_closed_forms,
+    check_q6k_exact_dyadic_dot,
+    check_q6k_generator_layout_agrees,
+    check_q6k_onehot_every_element_and_bit,
 )

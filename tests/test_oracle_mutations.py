@@ -49,6 +49,21 @@ MUTANTS = {
     "q8_nan_ignored": ("            amax = NAN;\n", "            amax = amax;\n"),
     "q8_block_scale_index": ("(double)d[b * (k / 32) + c / 32]", "(double)d[b * (k / 32) + c / 64]"),
     "q8_codes_of_vector_0": ("(double)q[b * k + c]", "(double)q[c]"),
+    "q6_ql_half_stride": ("blk[64 * h + 32 * (t % 2) + l]", "blk[32 * h + 32 * (t % 2) + l]"),
+    "q6_ql_nibble_select": ("(t < 2) ? (lo_byte % 16) : (lo_byte / 16)",
+                            "(t % 2 == 0) ? (lo_byte % 16) : (lo_byte / 16)"),
+    "q6_qh_shift": ("(hi_byte >> (2 * t)) % 4", "(hi_byte >> t) % 4"),
+    "q6_qh_byte": ("blk[128 + 32 * h + l]", "blk[128 + h + 2 * l]"),
+    "q6_high_bits_weight": ("*q = lo + 16 * hi;", "*q = lo + 32 * hi;"),
+    "q6_scale_index": ("*s = e / 16;", "*s = e / 32;"),
+    "q6_offset_dropped": ("out[e] = dsc * (float)(q - 32);", "out[e] = dsc * (float)q;"),
+    "q6_scale_unsigned": ("(float)(int8_t)blk[192 + s]", "(float)blk[192 + s]"),
+    "q6_d_offset": ("oq_f16_to_f32((uint16_t)(blk[208] | (blk[209] << 8)))",
+                    "oq_f16_to_f32((uint16_t)(blk[192] | (blk[193] << 8)))"),
+    "q6_row_stride_ignored": ("oq6_dequant_superblock(w + r * row_stride + s * OQ6_SB, out",
+                              "oq6_dequant_superblock(w + r * S * OQ6_SB + s * OQ6_SB, out"),
+    "q6_gemv_x_vector_ignored": ("                    const float* xb = x + b * k;",
+                                 "                    const float* xb = x;"),
 }
 
 
