@@ -483,6 +483,126 @@ int gemv_checked(const void* w, const float* x, float* y, int64_t n, int64_t k, 
     return hip_status(q4k::launch_gemv(plan, w, x, y, s));
 }
 
+// ------------------------------------------------------------------ Q6_K
+constexpr int64_t kQ6Bytes = 210;
+
+// The row stride in bytes (0: dense), checked against the row and the
+// 16-byte rule.
+int q6k_stride(int64_t k, int64_t row_stride, int64_t* out)
+{
+    const int64_t dense = (k / q4k::kQK) * kQ6Bytes;
+    const int64_t stride = row_stride == 0 ? dense : row_stride;
+    if (stride < dense || stride > ((int64_t)1 << 40)) {
+        return Q4K_ERR_SHAPE;
+    }
+    if (stride % 16 != 0) {
+        return Q4K_ERR_ALIGN;
+    }
+    *out = stride;
+    return Q4K_OK;
+}
+
+// Tiles of 16 rows; about one workgroup of NW waves per CU: a workgroup
+// takes ceil(tiles / 256) tiles and, when that leaves waves idle, splits each
+// tile's columns into up to eight groups (powers of two, at most S).
+int make_q6k_plan(int64_t n, int64_t k, int64_t stride, bool w128, const q6k_launch* o,
+                  size_t lds_max, q4k::Q6kPlan* p)
+{
+    int rc = check_nk(n, k);
+    if (rc != Q4K_OK) {
+        return rc;
+    }
+    const int S = (int)(k / q4k::kQK);
+    const int64_t tiles = (n + 15) / 16;
+    p->n = (int)n;
+    p->k = (int)k;
+    p->S = S;
+    p->row_stride = stride;
+    const bool lines = w128 && stride % 128 == 0;
+    const int unit = o ? o->unit_bytes : 0;
+    if (unit == 0) {
+        p->unit = lines ? 128 : 64;
+    } else if (unit == 64 || (unit == 128 && lines)) {
+        p->unit = unit;
+    } else {
+        return Q4K_ERR_UNSUPPORTED;
+    }
+    const int nw = o ? o->waves_per_block : 0;
+    if (nw != 0 && nw != 4 && nw != 8) {
+        return Q4K_ERR_UNSUPPORTED;
+    }
+    p->waves_per_block = nw == 0 ? 8 : nw;
+    if (S * 16 > 4 * p->waves_per_block * 64) {
+        return Q4K_ERR_UNSUPPORTED;      // at most four groups of 16 x values per thread
+    }
+    int64_t tpb = o && o->tiles_per_block ? o->tiles_per_block : (tiles + 255) / 256;
+    if (tpb < 1 || tpb * 16 > kInt32Max / 64) {
+        return Q4K_ERR_UNSUPPORTED;
+    }
+    tpb = tpb > tiles ? tiles : tpb;
+    int ncg = o ? o->column_groups : 0;
+    if (ncg == 0) {
+        ncg = 1;
+        while (ncg * 2 <= 8 && ncg * 2 <= S && tpb * ncg < p->waves_per_block) {
+            ncg *= 2;
+        }
+    } else if (ncg < 1 || ncg > 16 || ncg > S) {
+        return Q4K_ERR_UNSUPPORTED;
+    }
+    p->ncg = ncg;
+    p->rows_per_block = (int)(16 * tpb);
+    const int64_t grid = (tiles + tpb - 1) / tpb;
+    if (grid > kInt32Max) {
+        return Q4K_ERR_SHAPE;
+    }
+    p->grid = (int)grid;
+    p->lds_bytes = q4k::q6k_lds_bytes(S, p->waves_per_block, p->rows_per_block, ncg);
+    if (p->lds_bytes > lds_max) {
+        return Q4K_ERR_UNSUPPORTED;
+    }
+    return Q4K_OK;
+}
+
+int q6k_gemv_checked(const void* w, const float* x, float* y, int64_t n, int64_t k,
+                     int64_t row_stride, const q6k_launch* opts, void* stream)
+{
+    if (!w || !x || !y) {
+        return Q4K_ERR_NULL;
+    }
+    int rc = check_nk(n, k);
+    if (rc != Q4K_OK) {
+        return rc;
+    }
+    int64_t stride = 0;
+    rc = q6k_stride(k, row_stride, &stride);
+    if (rc != Q4K_OK) {
+        return rc;
+    }
+    if (n > INT64_MAX / stride) {
+        return Q4K_ERR_SHAPE;
+    }
+    if (!aligned16(w) || !aligned16(x) || !aligned16(y)) {
+        return Q4K_ERR_ALIGN;
+    }
+    // options and shape first (no HIP call), then the device's LDS limit
+    const bool w128 = (reinterpret_cast<uintptr_t>(w) & 127u) == 0;
+    q4k::Q6kPlan plan;
+    rc = make_q6k_plan(n, k, stride, w128, opts, SIZE_MAX, &plan);
+    if (rc != Q4K_OK) {
+        return rc;
+    }
+    size_t lds_max = 0;
+    rc = device_lds_max(&lds_max);
+    if (rc != Q4K_OK) {
+        return rc;
+    }
+    rc = make_q6k_plan(n, k, stride, w128, opts, lds_max, &plan);
+    if (rc != Q4K_OK) {
+        return rc;
+    }
+    return hip_status(q4k::launch_q6k_gemv(plan, w, x, y, static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -633,14 +753,127 @@ int q4k_quantize_q8(const float* x, int8_t* q, float* d, int64_t k, int64_t m, v
     return hip_status(q4k::launch_quantize_q8(x, q, d, nblocks, static_cast<hipStream_t>(stream)));
 }
 
+size_t q6k_row_bytes(int64_t k)
+{
+    if (k < q4k::kQK || k % q4k::kQK != 0) {
+        return 0;
+    }
+    return (size_t)(k / q4k::kQK) * (size_t)kQ6Bytes;
+}
+
+int q6k_load(void* w_dev, const void* src_host, size_t src_bytes, int64_t n, int64_t k,
+             int64_t row_stride, void* stream)
+{
+    if (!w_dev || !src_host) {
+        return Q4K_ERR_NULL;
+    }
+    int rc = check_nk(n, k);
+    if (rc != Q4K_OK) {
+        return rc;
+    }
+    int64_t stride = 0;
+    rc = q6k_stride(k, row_stride, &stride);
+    if (rc != Q4K_OK) {
+        return rc;
+    }
+    const size_t row = q6k_row_bytes(k);
+    if ((size_t)n > SIZE_MAX / row || (size_t)n * row != src_bytes ||
+        (size_t)n > SIZE_MAX / (size_t)stride) {
+        return Q4K_ERR_SIZE;
+    }
+    if (!aligned16(w_dev)) {
+        return Q4K_ERR_ALIGN;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpy2DAsync(w_dev, (size_t)stride, src_host, row, row, (size_t)n,
+                                    hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) {
+        e = hipStreamSynchronize(s);
+    }
+    return hip_status(e);
+}
+
+int q6k_gemv(const void* w, const float* x, float* y, int64_t n, int64_t k, int64_t row_stride,
+             void* stream)
+{
+    return q6k_gemv_checked(w, x, y, n, k, row_stride, nullptr, stream);
+}
+
+int q6k_gemv_ex(const void* w, const float* x, float* y, int64_t n, int64_t k,
+                int64_t row_stride, const q6k_launch* opts, void* stream)
+{
+    return q6k_gemv_checked(w, x, y, n, k, row_stride, opts, stream);
+}
+
+int q6k_plan(int64_t n, int64_t k, int64_t row_stride, int w_aligned128, const q6k_launch* opts,
+             size_t lds_max, q6k_plan_info* out)
+{
+    if (!out) {
+        return Q4K_ERR_NULL;
+    }
+    int rc = check_nk(n, k);
+    if (rc != Q4K_OK) {
+        return rc;
+    }
+    int64_t stride = 0;
+    rc = q6k_stride(k, row_stride, &stride);
+    if (rc != Q4K_OK) {
+        return rc;
+    }
+    if (lds_max == 0) {
+        rc = device_lds_max(&lds_max);
+        if (rc != Q4K_OK) {
+            return rc;
+        }
+    }
+    q4k::Q6kPlan plan;
+    rc = make_q6k_plan(n, k, stride, w_aligned128 != 0, opts, lds_max, &plan);
+    if (rc != Q4K_OK) {
+        return rc;
+    }
+    out->unit_bytes = plan.unit;
+    out->waves_per_block = plan.waves_per_block;
+    out->column_groups = plan.ncg;
+    out->rows_per_block = plan.rows_per_block;
+    out->grid = plan.grid;
+    out->lds_bytes = (int32_t)plan.lds_bytes;
+    return Q4K_OK;
+}
+
+int q6k_dequantize(const void* w, float* out, int64_t n, int64_t k, int64_t row_stride,
+                   void* stream)
+{
+    if (!w || !out) {
+        return Q4K_ERR_NULL;
+    }
+    int rc = check_nk(n, k);
+    if (rc != Q4K_OK) {
+        return rc;
+    }
+    int64_t stride = 0;
+    rc = q6k_stride(k, row_stride, &stride);
+    if (rc != Q4K_OK) {
+        return rc;
+    }
+    if (!aligned16(out)) {
+        return Q4K_ERR_ALIGN;
+    }
+    const int64_t groups = n * (k / q4k::kQK) * 16;
+    if ((groups + 255) / 256 > kInt32Max || n > INT64_MAX / stride) {
+        return Q4K_ERR_SHAPE;
+    }
+    return hip_status(q4k::launch_q6k_dequant(w, out, n, (int)(k / q4k::kQK), stride,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 const char* q4k_status_string(int rc)
 {
     switch (rc) {
     case Q4K_OK: return "ok";
     case Q4K_ERR_NULL: return "a required pointer is NULL";
     case Q4K_ERR_SHAPE: return "bad shape: need 1 <= n, 256 <= k, k % 256 == 0, 1 <= m, n and k below 2^31";
-    case Q4K_ERR_SIZE: return "byte count does not match n*(k/256)*144";
-    case Q4K_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case Q4K_ERR_SIZE: return "byte count does not match n rows of the format (144 or 210 bytes per 256 weights)";
+    case Q4K_ERR_ALIGN: return "a pointer, or a Q6_K row stride, is not 16-byte aligned";
     case Q4K_ERR_UNSUPPORTED:
         return "unsupported: m > 16, or launch options that do not fit the shape, m or the "
                "device";

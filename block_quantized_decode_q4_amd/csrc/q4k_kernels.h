@@ -1,6 +1,6 @@
 // q4k_kernels.h -- internal interface between the C-ABI layer (q4k_api.hip)
-// and the kernels (q4k_kernels.hip, q4k_dpp.hip, q4k_mfma.hip).  Not
-// installed, not part of the ABI.
+// and the kernels (q4k_kernels.hip, q4k_dpp.hip, q4k_mfma.hip, q4k_q8.hip,
+// q4k_q6k.hip).  Not installed, not part of the ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -58,5 +58,23 @@ hipError_t launch_quantize_q8(const float* x, int8_t* q, float* d, int64_t nbloc
                               hipStream_t stream);
 size_t q8_lds_bytes(int S, int waves);
 hipError_t launch_read(const void* buf, size_t n16, float* out, hipStream_t stream);
+
+// The GEMV over Q6_K weights (q4k_q6k.hip), one vector.
+struct Q6kPlan {
+    int n, k, S;
+    int64_t row_stride;    // bytes from one row to the next (a multiple of 16)
+    int unit;              // bytes of a row one load instruction reads: 64, or 128
+                           // (rows and w 128-byte aligned)
+    int waves_per_block;   // 8, or 4 when the LDS cannot hold eight rings
+    int rows_per_block;    // 16 per tile
+    int ncg;               // column groups per tile (the tasks of one tile)
+    int grid;
+    size_t lds_bytes;
+};
+hipError_t launch_q6k_gemv(const Q6kPlan& p, const void* w, const float* x, float* y,
+                           hipStream_t stream);
+hipError_t launch_q6k_dequant(const void* w, float* out, int64_t n, int S, int64_t row_stride,
+                              hipStream_t stream);
+size_t q6k_lds_bytes(int S, int waves, int rows_per_block, int ncg);
 
 }  // namespace q4k

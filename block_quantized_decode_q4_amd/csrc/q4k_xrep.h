@@ -146,6 +146,7 @@ __device__ __forceinline__ int row16_scan(int v, int& total)
 struct Conv16 {
     uint32_t plane[4][4];   // plane[l][t]: digit l of elements 4t .. 4t+3, signed bytes
     double xsum;            // XI of the lane's sub-block (certified elements)
+    double xsum16;          // XI of the lane's own 16 elements
     int sigma;              // the sub-block's grid exponent
     uint32_t uncmask;       // bit i: element i is uncertified
     int first;              // its index among the column's uncertified elements
@@ -185,6 +186,7 @@ __device__ __forceinline__ Conv16 convert16(const float (&e)[16])
             ps[l] = __builtin_amdgcn_sdot4((int)d[l], 0x01010101, ps[l], false);
         }
     }
+    c.xsum16 = digits_exact(ps[0], ps[1], ps[2], ps[3]);
     // the sub-block's plane sums (pair by DPP), |sum| <= 32 * 128: XI exactly
 #pragma unroll
     for (int l = 0; l < 4; ++l) {

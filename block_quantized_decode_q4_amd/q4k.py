@@ -36,6 +36,12 @@ EXPORTED = (
     "q4k_plan",
     "q4k_gemv_q8",
     "q4k_quantize_q8",
+    "q6k_row_bytes",
+    "q6k_load",
+    "q6k_gemv",
+    "q6k_gemv_ex",
+    "q6k_plan",
+    "q6k_dequantize",
 )
 
 
@@ -73,6 +79,26 @@ class q4k_plan_info(ctypes.Structure):
     ]
 
 
+class q6k_launch(ctypes.Structure):
+    _fields_ = [
+        ("unit_bytes", ctypes.c_int32),
+        ("waves_per_block", ctypes.c_int32),
+        ("column_groups", ctypes.c_int32),
+        ("tiles_per_block", ctypes.c_int32),
+    ]
+
+
+class q6k_plan_info(ctypes.Structure):
+    _fields_ = [
+        ("unit_bytes", ctypes.c_int32),
+        ("waves_per_block", ctypes.c_int32),
+        ("column_groups", ctypes.c_int32),
+        ("rows_per_block", ctypes.c_int32),
+        ("grid", ctypes.c_int32),
+        ("lds_bytes", ctypes.c_int32),
+    ]
+
+
 VARIANT_AUTO = 0
 VARIANT_SINGLE = 1
 VARIANT_CHUNKED = 2
@@ -107,6 +133,19 @@ def load_library():
         lib.q4k_gemv_q8.restype = ctypes.c_int
         lib.q4k_quantize_q8.argtypes = [vp, vp, vp, i64, i64, vp]
         lib.q4k_quantize_q8.restype = ctypes.c_int
+        lib.q6k_row_bytes.argtypes = [i64]
+        lib.q6k_row_bytes.restype = ctypes.c_size_t
+        lib.q6k_load.argtypes = [vp, vp, ctypes.c_size_t, i64, i64, i64, vp]
+        lib.q6k_load.restype = ctypes.c_int
+        lib.q6k_gemv.argtypes = [vp, vp, vp, i64, i64, i64, vp]
+        lib.q6k_gemv.restype = ctypes.c_int
+        lib.q6k_gemv_ex.argtypes = [vp, vp, vp, i64, i64, i64, ctypes.POINTER(q6k_launch), vp]
+        lib.q6k_gemv_ex.restype = ctypes.c_int
+        lib.q6k_plan.argtypes = [i64, i64, i64, ctypes.c_int, ctypes.POINTER(q6k_launch),
+                                 ctypes.c_size_t, ctypes.POINTER(q6k_plan_info)]
+        lib.q6k_plan.restype = ctypes.c_int
+        lib.q6k_dequantize.argtypes = [vp, vp, i64, i64, i64, vp]
+        lib.q6k_dequantize.restype = ctypes.c_int
         lib.q4k_status_string.argtypes = [ctypes.c_int]
         lib.q4k_status_string.restype = ctypes.c_char_p
         lib.q4k_read_calibrate.argtypes = [vp, ctypes.c_size_t, vp, vp]
@@ -215,6 +254,55 @@ def q4k_plan(n: int, k: int, m: int = 1, w_aligned128: bool = True, lds_max: int
                                    1 if w_aligned128 else 0, int(lds_max), ctypes.byref(out)),
            "q4k_plan")
     return out
+
+
+def q6k_row_bytes(k: int) -> int:
+    return int(load_library().q6k_row_bytes(int(k)))
+
+
+def q6k_load(w_dev, src_host, n: int, k: int, row_stride: int = 0, stream=None,
+             src_bytes: int | None = None) -> None:
+    """Copy dense Q6_K rows from host memory into w_dev at row_stride
+    (synchronous on stream)."""
+    if src_bytes is None:
+        src_bytes = src_host.nbytes if hasattr(src_host, "nbytes") else len(src_host)
+    _check(load_library().q6k_load(_addr(w_dev), _addr(src_host), int(src_bytes), int(n), int(k),
+                                   int(row_stride), _stream(stream)), "q6k_load")
+
+
+def q6k_gemv(w, x, y, n: int, k: int, row_stride: int = 0, stream=None) -> None:
+    """y[r] = sum_c W[r][c] x[c] over Q6_K rows; asynchronous on stream."""
+    _check(load_library().q6k_gemv(_addr(w), _addr(x), _addr(y), int(n), int(k), int(row_stride),
+                                   _stream(stream)), "q6k_gemv")
+
+
+def q6k_gemv_ex(w, x, y, n: int, k: int, row_stride: int = 0, stream=None, **opts) -> None:
+    """q6k_gemv with explicit launch options (fields of q6k_launch)."""
+    unknown = set(opts) - {f for f, _ in q6k_launch._fields_}
+    if unknown:
+        raise TypeError("unknown launch options %s" % sorted(unknown))
+    cfg = q6k_launch(**{f: int(opts.get(f, 0)) for f, _ in q6k_launch._fields_})
+    _check(load_library().q6k_gemv_ex(_addr(w), _addr(x), _addr(y), int(n), int(k),
+                                      int(row_stride), ctypes.byref(cfg), _stream(stream)),
+           "q6k_gemv_ex")
+
+
+def q6k_plan(n: int, k: int, row_stride: int = 0, w_aligned128: bool = True, lds_max: int = 0,
+             **opts) -> q6k_plan_info:
+    """The launch q6k_gemv_ex would make (no launch); lds_max = 0 asks the
+    current device, a nonzero value needs no GPU."""
+    cfg = q6k_launch(**opts) if opts else None
+    out = q6k_plan_info()
+    _check(load_library().q6k_plan(int(n), int(k), int(row_stride), 1 if w_aligned128 else 0,
+                                   ctypes.byref(cfg) if cfg else None, int(lds_max),
+                                   ctypes.byref(out)), "q6k_plan")
+    return out
+
+
+def q6k_dequantize(w, out, n: int, k: int, row_stride: int = 0, stream=None) -> None:
+    """out[r*k + c] = W[r][c] in f32 (bit-exact); asynchronous on stream."""
+    _check(load_library().q6k_dequantize(_addr(w), _addr(out), int(n), int(k), int(row_stride),
+                                         _stream(stream)), "q6k_dequantize")
 
 
 def q4k_read_calibrate_blocks() -> int:

@@ -60,8 +60,9 @@ enum q4k_status {
     Q4K_OK = 0,
     Q4K_ERR_NULL = 1,        /* a required pointer is NULL                       */
     Q4K_ERR_SHAPE = 2,       /* n < 1, k < 256, k % 256 != 0, m < 1, or too big  */
-    Q4K_ERR_SIZE = 3,        /* byte count does not match n*(k/256)*144          */
-    Q4K_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                 */
+    Q4K_ERR_SIZE = 3,        /* byte count does not match n rows of the format   */
+    Q4K_ERR_ALIGN = 4,       /* a pointer (or a Q6_K row stride) is not 16-byte
+                                aligned                                         */
     Q4K_ERR_UNSUPPORTED = 5, /* m > 16; 9-16 vectors where the one-pass
                                 kernels 5 and 6 do not apply; or a launch
                                 option that cannot be honoured                  */
@@ -228,6 +229,89 @@ typedef struct q4k_plan_info {
 
 int q4k_plan(int64_t n, int64_t k, int64_t m, const q4k_launch* opts, int w_aligned128,
              size_t lds_max, q4k_plan_info* out);
+
+/* ---------------------------------------------------------------------
+ * Q6_K: the same GEMV over the other block format of the decode loop, one
+ * vector (realizar 0.8.5, q4k_gemv_cached.rs: doc of
+ * `q6k_gemv_cached_async`, the Q6_K GEMV used for an LM head stored as
+ * Q6_K; memra-engine 0.83.1, src/f16_ffi.rs: doc of `memra_q6_K_dequant_f16`
+ * and the row-size check in `ensure_f16_mirror`: 210-byte superblocks of
+ * 256 weights, k / 256 of them per row).
+ *  - Superblock layout (GGUF Q6_K; not printed on the pages): bytes 0-127
+ *    ql, the low four bits of the codes; 128-191 qh, the high two bits;
+ *    192-207 sixteen signed 8-bit scales, scale s for elements 16s..16s+15;
+ *    208-209 fp16 d (little-endian).  Element e = 128h + 32t + l (h < 2,
+ *    t < 4, l < 32) keeps its low bits in ql byte 64h + 32(t%2) + l (low
+ *    nibble for t < 2, high nibble for t >= 2) and its high bits in bits
+ *    2t, 2t+1 of qh byte 32h + l; its weight is w = d*sc*(q - 32), an exact
+ *    product in f32.
+ *  - Row r starts at byte r*row_stride of w; row_stride = 0 means the dense
+ *    q6k_row_bytes(k).  row_stride must be a multiple of 16 and at least
+ *    q6k_row_bytes(k) (Q4K_ERR_SHAPE below it, Q4K_ERR_ALIGN when it is not
+ *    a multiple of 16: dense rows qualify when k % 2048 == 0), and w must
+ *    hold n*row_stride bytes (the last row's padding included).  A stride
+ *    that is a multiple of 128 with w 128-byte aligned lets the kernel read
+ *    whole 128-byte lines per row.
+ * ------------------------------------------------------------------- */
+
+/* Bytes of one dense Q6_K row of k weights: (k/256)*210, or 0 when k < 256
+ * or k % 256 != 0. */
+size_t q6k_row_bytes(int64_t k);
+
+/* Copy n dense rows of GGUF Q6_K bytes (src_bytes == n*q6k_row_bytes(k))
+ * from host memory into the device buffer w_dev at row_stride (0 = dense),
+ * leaving the padding bytes of each row untouched.  Synchronous on
+ * `stream`.  Errors as q4k_load, and the row_stride rules above. */
+int q6k_load(void* w_dev, const void* src_host, size_t src_bytes, int64_t n, int64_t k,
+             int64_t row_stride, void* stream);
+
+/* y[r] = sum_c W[r][c] * x[c] for r < n, W in Q6_K rows.
+ *  w : device, 16-byte aligned, rows as above
+ *  x : device, k f32, 16-byte aligned
+ *  y : device, n f32, 16-byte aligned, fully overwritten
+ *  1 <= n <= 2^31-1, 256 <= k with k % 256 == 0; x is staged whole in LDS
+ *  beside eight waves' rings, so k <= 18432 on MI355X (160 KiB of LDS);
+ *  beyond: Q4K_ERR_UNSUPPORTED.
+ * Asynchronous on `stream`; allocates nothing.  Tolerance as q4k_gemv:
+ * within 1e-5 * sum|w||x| of the exact dot product of the f32 weights for
+ * every input whose exact result is finite; inf and NaN propagate. */
+int q6k_gemv(const void* w, const float* x, float* y, int64_t n, int64_t k,
+             int64_t row_stride, void* stream);
+
+/* Launch options of q6k_gemv_ex (tests and tuning; every field 0 =
+ * automatic). */
+typedef struct q6k_launch {
+    int32_t unit_bytes;       /* bytes of a row per load instruction: 64, or 128
+                                 (row_stride % 128 == 0, w 128-byte aligned)  */
+    int32_t waves_per_block;  /* 4 or 8 (4: k <= 16384)                        */
+    int32_t column_groups;    /* tasks per 16-row tile, splitting its columns:
+                                 1 .. min(16, k/256)                           */
+    int32_t tiles_per_block;  /* 16-row tiles per workgroup, >= 1              */
+} q6k_launch;
+
+int q6k_gemv_ex(const void* w, const float* x, float* y, int64_t n, int64_t k,
+                int64_t row_stride, const q6k_launch* opts, void* stream);
+
+/* The launch q6k_gemv_ex would make, without launching: lds_max as for
+ * q4k_plan (0 = ask the device), w_aligned128 as for q4k_plan. */
+typedef struct q6k_plan_info {
+    int32_t unit_bytes;
+    int32_t waves_per_block;
+    int32_t column_groups;
+    int32_t rows_per_block;
+    int32_t grid;
+    int32_t lds_bytes;
+} q6k_plan_info;
+
+int q6k_plan(int64_t n, int64_t k, int64_t row_stride, int w_aligned128, const q6k_launch* opts,
+             size_t lds_max, q6k_plan_info* out);
+
+/* out[r*k + c] = W[r][c] as f32, bit-exact (every Q6_K weight is exact in
+ * f32): the f32 twin of `memra_q6_K_dequant_f16` (memra-engine 0.83.1,
+ * src/f16_ffi.rs).  w as for q6k_gemv; out device, n*k f32, 16-byte
+ * aligned.  Asynchronous on `stream`. */
+int q6k_dequantize(const void* w, float* out, int64_t n, int64_t k, int64_t row_stride,
+                   void* stream);
 
 /* Read `bytes` (a multiple of 16) of device memory at `buf` (16-byte
  * aligned) with coalesced 16-byte loads and write a checksum per workgroup

@@ -26,7 +26,7 @@ MIS = 0x100004        # misaligned
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(q4k_[a-z0-9_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(q[46]k_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -342,3 +342,87 @@ def test_q8_refusals(lib):
     assert lib.q4k_quantize_q8(A, A, A, 0, 1, None) == q4k.Q4K_ERR_SHAPE
     assert lib.q4k_quantize_q8(A, A, A, 64, 0, None) == q4k.Q4K_ERR_SHAPE
     assert lib.q4k_quantize_q8(A, A, MIS, 64, 1, None) == q4k.Q4K_ERR_ALIGN
+
+
+# ------------------------------------------------------------------ Q6_K
+def test_q6k_row_bytes():
+    assert q4k.q6k_row_bytes(256) == 210
+    assert q4k.q6k_row_bytes(4096) == 16 * 210
+    assert q4k.q6k_row_bytes(14336) == 56 * 210
+    for bad in (0, -256, 255, 257):
+        assert q4k.q6k_row_bytes(bad) == 0
+
+
+def test_q6k_structs_match_header():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    for name, cls in (("q6k_launch", q4k.q6k_launch), ("q6k_plan_info", q4k.q6k_plan_info)):
+        body = re.search(r"typedef struct %s \{(.*?)\} %s;" % (name, name), text, re.S).group(1)
+        fields = re.findall(r"int32_t\s+([a-z_0-9]+)\s*;", body)
+        assert fields == [f for f, _ in cls._fields_], name
+        assert all(t is ctypes.c_int32 for _, t in cls._fields_)
+
+
+def test_q6k_refusals(lib):
+    """Argument checks of the Q6_K entry points, before any HIP call."""
+    g = lib.q6k_gemv
+    assert g(None, A, A, 16, 4096, 0, None) == q4k.Q4K_ERR_NULL
+    assert g(A, None, A, 16, 4096, 0, None) == q4k.Q4K_ERR_NULL
+    assert g(A, A, None, 16, 4096, 0, None) == q4k.Q4K_ERR_NULL
+    for n, k in ((0, 2048), (16, 300), (16, 0), (2 ** 31, 2048)):
+        assert g(A, A, A, n, k, 0, None) == q4k.Q4K_ERR_SHAPE, (n, k)
+    assert g(A, A, A, 16, 2048, 1679, None) == q4k.Q4K_ERR_SHAPE       # below the row's bytes
+    assert g(A, A, A, 16, 2048, 1688, None) == q4k.Q4K_ERR_ALIGN       # not a multiple of 16
+    assert g(A, A, A, 16, 1024, 0, None) == q4k.Q4K_ERR_ALIGN          # dense 840-byte rows
+    assert g(MIS, A, A, 16, 2048, 0, None) == q4k.Q4K_ERR_ALIGN
+    assert g(A, MIS, A, 16, 2048, 0, None) == q4k.Q4K_ERR_ALIGN
+    assert g(A, A, MIS, 16, 2048, 0, None) == q4k.Q4K_ERR_ALIGN
+    for o in (dict(unit_bytes=32), dict(waves_per_block=2), dict(column_groups=9),
+              dict(column_groups=-1), dict(tiles_per_block=-2)):
+        cfg = q4k.q6k_launch(**o)
+        assert lib.q6k_gemv_ex(A, A, A, 16, 2048, 0, ctypes.byref(cfg), None) == \
+            q4k.Q4K_ERR_UNSUPPORTED, o
+    # whole-line units need a stride that is a multiple of 128 and w aligned to 128
+    cfg = q4k.q6k_launch(unit_bytes=128)
+    assert lib.q6k_gemv_ex(A, A, A, 16, 4096, 0, ctypes.byref(cfg), None) == q4k.Q4K_ERR_UNSUPPORTED
+    assert lib.q6k_gemv_ex(A + 16, A, A, 16, 4096, 3456, ctypes.byref(cfg), None) == \
+        q4k.Q4K_ERR_UNSUPPORTED
+    d = lib.q6k_dequantize
+    assert d(None, A, 16, 2048, 0, None) == q4k.Q4K_ERR_NULL
+    assert d(A, A, 16, 300, 0, None) == q4k.Q4K_ERR_SHAPE
+    assert d(A, MIS, 16, 2048, 0, None) == q4k.Q4K_ERR_ALIGN
+    assert d(A, A, 16, 2048, 1000, None) == q4k.Q4K_ERR_SHAPE
+    buf = np.zeros(4 * 1680, np.uint8)
+    assert lib.q6k_load(A, buf.ctypes.data, buf.nbytes - 1, 4, 2048, 0, None) == q4k.Q4K_ERR_SIZE
+    assert lib.q6k_load(None, buf.ctypes.data, buf.nbytes, 4, 2048, 0, None) == q4k.Q4K_ERR_NULL
+    assert lib.q6k_load(A, buf.ctypes.data, buf.nbytes, 4, 2048, 1688, None) == q4k.Q4K_ERR_ALIGN
+    assert lib.q6k_load(A, buf.ctypes.data, buf.nbytes, 4, 2048, 1664, None) == q4k.Q4K_ERR_SHAPE
+
+
+@pytest.mark.parametrize("n,k,stride,aligned,unit,groups,rpb,grid", [
+    (32000, 4096, 0, True, 64, 1, 128, 250),      # dense LM head: 3360-byte rows
+    (32000, 4096, 3456, True, 128, 1, 128, 250),  # rows padded to whole lines
+    (32000, 4096, 3456, False, 64, 1, 128, 250),  # w not 128-byte aligned
+    (4096, 14336, 0, True, 64, 8, 16, 256),       # FFN down: one tile a workgroup, 8 groups
+    (256, 1024, 848, True, 64, 4, 16, 16),        # four superblocks: four groups at most
+    (128256, 4096, 0, True, 64, 1, 512, 251),     # four tiles a wave
+    (17, 2048, 0, True, 64, 8, 16, 2),
+])
+def test_q6k_plan_automatic(n, k, stride, aligned, unit, groups, rpb, grid):
+    p = q4k.q6k_plan(n, k, stride, aligned, lds_max=163840)
+    assert (p.unit_bytes, p.column_groups, p.rows_per_block, p.grid, p.waves_per_block) == \
+        (unit, groups, rpb, grid, 8)
+    # x (1264 bytes a column) + eight rings of 16 x 560 bytes + the group sums
+    assert p.lds_bytes == (k // 256) * 1264 + 8 * 16 * 560 + (rpb * groups * 8 if groups > 1 else 0)
+
+
+def test_q6k_plan_lds_limit():
+    assert q4k.q6k_plan(64, 18432, 0, True, lds_max=163840).lds_bytes <= 163840
+    with pytest.raises(q4k.Q4KError) as e:
+        q4k.q6k_plan(64, 18432 + 2048, 0, True, lds_max=163840)
+    assert e.value.rc == q4k.Q4K_ERR_UNSUPPORTED
+    p = q4k.q6k_plan(64, 16384, 0, True, lds_max=163840, waves_per_block=4)
+    assert p.waves_per_block == 4 and p.lds_bytes == 64 * 1264 + 4 * 16 * 560 + (
+        p.rows_per_block * p.column_groups * 8 if p.column_groups > 1 else 0)
+    with pytest.raises(q4k.Q4KError):
+        q4k.q6k_plan(64, 18432, 0, True, lds_max=163840, waves_per_block=4)   # x per thread

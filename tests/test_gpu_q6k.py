@@ -1,0 +1,186 @@
+"""GPU parity of the Q6_K GEMV and dequantization (q6k_gemv, q6k_gemv_ex,
+q6k_dequantize; realizar 0.8.5, q4k_gemv_cached.rs, `q6k_gemv_cached_async`;
+memra-engine 0.83.1, src/f16_ffi.rs, `memra_q6_K_dequant_f16`).
+
+Every y is held to the rule of tests/checks.py against the oracle
+(oracle.q6k_gemv: f64 dot of the f32 weights), |y - y_ref| <= 1e-5 sum|w||x|
+per output; dequantized weights must equal the oracle's bit for bit.  Shapes
+span several tiles and column groups with ragged row counts, dense and
+padded row strides (16-byte pieces, or whole 128-byte lines), every launch
+geometry the options allow, the edge inputs of tests/edge_inputs.py (x
+values) with Q6_K weights, special d, and the full-size LM-head and
+FFN-down workloads.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from block_quantized_decode_q4_amd import q4k, synth  # noqa: E402
+
+import checks  # noqa: E402
+import edge_inputs  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    q4k.load_library()
+    yield
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _dev_weights(w, align=256):
+    """Device copy of the bytes at an address aligned to `align` (128 for
+    line units) but not to twice that (so alignment is what the test says)."""
+    buf = torch.zeros(w.size + 2 * align, dtype=torch.uint8, device="cuda")
+    base = buf.data_ptr()
+    off = (-base) % align
+    if (base + off) % (2 * align) == 0:
+        off += align
+    view = buf[off:off + w.size]
+    view.copy_(torch.from_numpy(w))
+    return buf, view
+
+
+def _run(w_view, x, n, k, stride=0, **opts):
+    x_d = torch.from_numpy(np.ascontiguousarray(x.reshape(-1))).cuda()
+    y_d = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
+    if opts:
+        q4k.q6k_gemv_ex(w_view, x_d, y_d, n, k, stride, **opts)
+    else:
+        q4k.q6k_gemv(w_view, x_d, y_d, n, k, stride)
+    torch.cuda.synchronize()
+    return y_d.cpu().numpy()
+
+
+def _check(oracle_mod, w, x, n, k, stride=0, what="", strict_kind=True, align=256, **opts):
+    _say("q6k %s n=%d k=%d stride=%d opts=%s" % (what, n, k, stride, opts))
+    _, view = _dev_weights(w, align)
+    y = _run(view, x, n, k, stride, **opts)
+    y_ref, bound = oracle_mod.q6k_gemv(w, x.reshape(1, k), n, stride)
+    return y, checks.assert_y(y[None, :], y_ref, bound, what, strict_kind)
+
+
+SHAPES = [
+    # n, k, stride (0 dense): one row; ragged tiles; dense rows of 16 and
+    # 56 superblocks; strides padded to 16 bytes and to whole lines
+    (1, 256, 256),
+    (17, 2048, 0),
+    (256, 1024, 848),
+    (256, 1024, 896),
+    (300, 4096, 0),
+    (300, 4096, 3456),
+    (129, 14336, 0),
+    (40, 18432, 0),
+    (1000, 4096, 3376),
+]
+
+
+@pytest.mark.parametrize("n,k,stride", SHAPES)
+def test_q6k_gemv_shapes(oracle_mod, n, k, stride):
+    w, x = synth.make_q6k_inputs(n, k, 1, seed=3000 + n + k, row_stride=stride)
+    plan = q4k.q6k_plan(n, k, stride, True)
+    _say("plan unit=%d waves=%d groups=%d rows/block=%d grid=%d lds=%d" % (
+        plan.unit_bytes, plan.waves_per_block, plan.column_groups, plan.rows_per_block,
+        plan.grid, plan.lds_bytes))
+    _check(oracle_mod, w, x[0], n, k, stride, "shape")
+
+
+def test_q6k_unit_64_when_not_line_aligned(oracle_mod):
+    n, k, stride = 64, 4096, 3456
+    w, x = synth.make_q6k_inputs(n, k, 1, seed=3101, row_stride=stride)
+    assert q4k.q6k_plan(n, k, stride, False).unit_bytes == 64
+    _check(oracle_mod, w, x[0], n, k, stride, "16-byte aligned w", align=16)
+
+
+GEOMETRIES = [
+    dict(unit_bytes=64), dict(unit_bytes=128), dict(waves_per_block=4),
+    dict(column_groups=1), dict(column_groups=3), dict(column_groups=5), dict(column_groups=16),
+    dict(tiles_per_block=1), dict(tiles_per_block=3, column_groups=2),
+    dict(waves_per_block=4, tiles_per_block=5, column_groups=7, unit_bytes=128),
+]
+
+
+@pytest.mark.parametrize("opts", GEOMETRIES, ids=lambda o: ",".join("%s=%d" % kv for kv in o.items()))
+def test_q6k_launch_geometries(oracle_mod, opts):
+    n, k, stride = 333, 4096, 3456
+    w, x = synth.make_q6k_inputs(n, k, 1, seed=3201, row_stride=stride)
+    _check(oracle_mod, w, x[0], n, k, stride, "geometry", **opts)
+
+
+def test_q6k_same_groups_same_bits(oracle_mod):
+    """With the same column groups, unit size, waves and tiles per workgroup
+    change only who computes a sum, not its order: y is bit-identical."""
+    n, k, stride = 200, 4096, 3456
+    w, x = synth.make_q6k_inputs(n, k, 1, seed=3301, row_stride=stride)
+    _, view = _dev_weights(w)
+    ys = [_run(view, x[0], n, k, stride, column_groups=4, **o)
+          for o in (dict(unit_bytes=64), dict(unit_bytes=128), dict(waves_per_block=4),
+                    dict(tiles_per_block=3))]
+    for y in ys[1:]:
+        assert np.array_equal(y.view(np.uint32), ys[0].view(np.uint32))
+
+
+def test_q6k_dequantize_bit_exact(oracle_mod):
+    for n, k, stride in ((37, 2048, 0), (64, 1024, 896), (5, 4096, 3360)):
+        w, _ = synth.make_q6k_inputs(n, k, 1, seed=3401 + n, row_stride=stride)
+        _say("q6k dequant n=%d k=%d stride=%d" % (n, k, stride))
+        _, view = _dev_weights(w)
+        out = torch.full((n, k), float("nan"), dtype=torch.float32, device="cuda")
+        q4k.q6k_dequantize(view, out, n, k, stride)
+        torch.cuda.synchronize()
+        ref = oracle_mod.q6k_dequant(w, n, k, stride)
+        assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("case", edge_inputs.all_cases(), ids=lambda c: c.name)
+def test_q6k_edge_x(oracle_mod, case):
+    """The x of every edge case (tiny, subnormal, huge, overflowing y,
+    outliers, inf and NaN, many values the grid leaves out) against Q6_K
+    weights of the same shape: dense rows when k % 2048 == 0, else rows
+    padded to whole lines."""
+    stride = 0 if case.k % 2048 == 0 else -(-(case.k // 256 * 210) // 128) * 128
+    f = synth.draw_q6k_fields(np.random.default_rng(3500 + case.n), case.n, case.k // 256)
+    w = synth.pack_q6k(f, stride)
+    for b in range(case.m):
+        _check(oracle_mod, w, case.x[b], case.n, case.k, stride,
+               "%s (vector %d)" % (case.name, b))
+
+
+def test_q6k_special_d_and_zero_weights(oracle_mod):
+    """d = +-inf, NaN, +-0 in some superblocks, zero scales under an
+    infinite d, all codes 32 (weights exactly 0) in whole rows, and a row of
+    weights +-7d only: kinds of non-finite y may differ where d is not
+    finite."""
+    n, k = 48, 4096
+    f = synth.draw_q6k_fields(np.random.default_rng(3701), n, k // 256)
+    for i, sp in enumerate((0x7C00, 0xFC00, 0x7E00, 0x0000, 0x8000)):
+        f.d_bits[i, 3] = sp
+    f.sc[0, 3, :] = 0                    # inf * 0 inside d * sc
+    f.q[10:14] = 32                      # zero weights: y exactly 0, bound 0
+    f.q[20, :, :128] = 33                # weights +7 d and -7 d
+    f.q[20, :, 128:] = 31
+    f.sc[20] = 7
+    w = synth.pack_q6k(f)
+    x = np.random.default_rng(3702).standard_normal(k).astype(np.float32)
+    y, _ = _check(oracle_mod, w, x, n, k, 0, "special d", strict_kind=False)
+    assert np.all(y[10:14] == 0.0)
+
+
+@pytest.mark.parametrize("index", [1, 2])
+def test_q6k_workload_full_size(oracle_mod, index):
+    """The LM head (32000 x 4096, dense rows and rows padded to lines) and
+    FFN-down (4096 x 14336) at full size, every output against the oracle."""
+    wl = synth.Q6K_WORKLOADS[index]
+    strides = (0, 3456) if index == 1 else (0,)
+    for stride in strides:
+        _, w, x = synth.q6k_workload_inputs(index, row_stride=stride)
+        _, worst = _check(oracle_mod, w, x[0], wl.n, wl.k, stride, wl.name)
+        _say("  worst |err|/bound %.3g" % worst)
