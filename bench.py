@@ -152,6 +152,62 @@ KERNEL_DTYPE = {
 }
 
 
+def time_q6k(q4k, synth, torch, lib, n, k, x_d, y_d, sp, stream, args):
+    """Time q6k_gemv on seeded Q6_K weights of shape n x k (the same x):
+    dense rows (when their bytes are a multiple of 16) and rows padded to
+    whole lines.  Returns a list of results, one per layout."""
+    dense = q4k.q6k_row_bytes(k)
+    layouts = [s for s in (0 if dense % 16 == 0 else None, -(-dense // 128) * 128)
+               if s is not None]
+    res = []
+    for stride in dict.fromkeys(layouts):
+        st = stride or dense
+        w6, _ = synth.make_q6k_inputs(n, k, 1, seed=2000 + n + k, row_stride=stride)
+        nbytes = w6.size                              # n * st
+        copies = max(4, math.ceil(args.rotate_gib * (1 << 30) / nbytes))
+        pool = torch.empty((copies, nbytes + 128), dtype=torch.uint8, device="cuda")
+        base = pool.data_ptr()
+        # every copy at a 128-byte-aligned address (the row pitch is nbytes + 128)
+        offs = [(-(base + c * (nbytes + 128))) % 128 for c in range(copies)]
+        src = torch.from_numpy(w6).cuda()
+        for c in range(copies):
+            pool[c, offs[c]:offs[c] + nbytes].copy_(src)
+        del src
+        ptrs = [base + c * (nbytes + 128) + offs[c] for c in range(copies)]
+        xp, yp = x_d.data_ptr(), y_d.data_ptr()
+
+        def step6(i):
+            rc = lib.q6k_gemv(ptrs[i % copies], xp, yp, n, k, stride, sp)
+            if rc != 0:
+                raise q4k.Q4KError(rc, "q6k_gemv")
+        steps = max(100, min(args.steps, 5000))
+        for i in range(min(args.warmup, 5000)):
+            step6(i)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(steps):
+            step6(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        wbytes = n * dense
+        plan = q4k.q6k_plan(n, k, stride, True)
+        res.append({"entry": "q6k_gemv",
+                    "workload": "q6k_gemv_n%d_k%d_m1" % (n, k),
+                    "row_stride": st, "unit_bytes": plan.unit_bytes,
+                    "column_groups": plan.column_groups,
+                    "us_per_step": round(us, 3), "steps": steps,
+                    "value": round(wbytes / us / 1e3, 2), "unit": "GB/s",
+                    "frac_of_hbm_peak": round((wbytes + 4 * k + 4 * n) / us / 1e3
+                                              / HBM_PEAK_GBPS, 4)})
+        log("bench: q6k_gemv n=%d k=%d stride=%d: %.3f us" % (n, k, st, us))
+        del pool
+        torch.cuda.empty_cache()
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -290,6 +346,15 @@ def main() -> int:
                           "f64 scaling; its own tolerance sum|w|(d/2(1+2^-19) + 2^-20|x|) + "
                           "2^-23|y_ref|"}
 
+    # the Q6_K GEMV over a Q6_K matrix of the same shape (m = 1; the pages'
+    # Q6_K LM head): dense rows and rows padded to whole 128-byte lines, each
+    # cycling through >= rotate-gib of copies
+    q6 = None
+    if m == 1 and k % 256 == 0 and q4k.q6k_row_bytes(k) * n > 0:
+        del pool
+        torch.cuda.empty_cache()
+        q6 = time_q6k(q4k, synth, torch, lib, n, k, x_d, y_d, sp, stream, args)
+
     alg_bytes = wb + 4 * k * m + 4 * n * m
     achieved = alg_bytes / t_launch / 1e9
     traffic = committed_traffic(wl.name)
@@ -338,6 +403,8 @@ def main() -> int:
     }
     if q8 is not None:
         out["q8_variant"] = q8
+    if q6:
+        out["q6k"] = q6
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline(w, x, n, k, m, wb, y_last)

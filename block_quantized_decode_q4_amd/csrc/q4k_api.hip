@@ -518,12 +518,21 @@ int make_q6k_plan(int64_t n, int64_t k, int64_t stride, bool w128, const q6k_lau
     p->k = (int)k;
     p->S = S;
     p->row_stride = stride;
-    const bool lines = w128 && stride % 128 == 0;
+    const bool lines = w128;       // whole lines: any 16-byte row stride, w 128-byte aligned
     const int unit = o ? o->unit_bytes : 0;
     if (unit == 0) {
         p->unit = lines ? 128 : 64;
     } else if (unit == 64 || (unit == 128 && lines)) {
         p->unit = unit;
+    } else {
+        return Q4K_ERR_UNSUPPORTED;
+    }
+    const bool no_phase = p->unit == 64 || stride % 128 == 0;
+    const int batch = o ? o->batch_bytes : 0;
+    if (batch == 0) {
+        p->batch = no_phase ? 256 : 128;
+    } else if ((batch == 128 && p->unit == 128) || (batch == 256 && no_phase)) {
+        p->batch = batch;
     } else {
         return Q4K_ERR_UNSUPPORTED;
     }
@@ -832,6 +841,7 @@ int q6k_plan(int64_t n, int64_t k, int64_t row_stride, int w_aligned128, const q
         return rc;
     }
     out->unit_bytes = plan.unit;
+    out->batch_bytes = plan.batch;
     out->waves_per_block = plan.waves_per_block;
     out->column_groups = plan.ncg;
     out->rows_per_block = plan.rows_per_block;

@@ -64,7 +64,10 @@ struct Q6kPlan {
     int n, k, S;
     int64_t row_stride;    // bytes from one row to the next (a multiple of 16)
     int unit;              // bytes of a row one load instruction reads: 64, or 128
-                           // (rows and w 128-byte aligned)
+                           // (whole lines; w 128-byte aligned)
+    int batch;             // bytes of a row per batch: 256 (no row has a phase within
+                           // its line: unit 64, or a row stride that is a multiple
+                           // of 128) or 128
     int waves_per_block;   // 8, or 4 when the LDS cannot hold eight rings
     int rows_per_block;    // 16 per tile
     int ncg;               // column groups per tile (the tasks of one tile)

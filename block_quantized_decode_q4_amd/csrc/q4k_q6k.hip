@@ -30,16 +30,19 @@
 // for j = 4 t + u, broadcast to the row by row_newbcast folded into the dot
 // instruction (as in q4k_dpp.hip).
 //
-// Stream: rows start on 16-byte boundaries (row_stride % 16 == 0), not on
-// lines, and a superblock column sits 210 c bytes into its row, so the
-// bytes of a column are at the same offset in every row of a tile.  Each
-// wave streams its tile's rows in batches of 256 bytes per row (four load
-// instructions of 64 x 16 bytes: 16 rows x 64 bytes, or 8 rows x one
-// 128-byte line when rows are line-aligned) into a ring of 512 bytes per row
-// in LDS (two batches), two batches in flight in registers; after each batch
-// it computes the columns whose 210 bytes are all in the ring.  A field of a
-// column starts at 210 c mod 4 = 0 or 2 bytes into a dword: the lanes read
-// five aligned dwords and shift them by that wave-uniform amount.  The ring
+// Stream: rows start on 16-byte boundaries (row_stride % 16 == 0), and a
+// superblock column sits 210 c bytes into its row.  Each wave streams its
+// tile's 16 rows in batches of BB bytes per row into a 512-byte ring per
+// row in LDS, 512 bytes per row in flight in registers.  A load instruction
+// reads 16 rows x 64 bytes, or, with w 128-byte aligned, 8 rows x one whole
+// 128-byte line: a row's batches then start on the line holding its first
+// byte, the row's bytes `phase` (a multiple of 16, below 128) into them.
+// Where no row has a phase (64-byte pieces, or a row stride that is a
+// multiple of 128) a batch is 256 bytes (two lines of a row back to back),
+// else 128.  After each batch the wave computes the columns whose 210 bytes
+// are in the ring for every row.  A field of a column starts 210 c mod 4 = 0
+// or 2 bytes into a dword (the same for every row): the lanes read five
+// aligned dwords and shift them by that wave-uniform amount.  The ring
 // repeats its first 32 bytes after its end, so no field read wraps.
 
 #include <hip/hip_runtime.h>
@@ -166,15 +169,17 @@ __device__ __forceinline__ uint32_t pick_q6_code(const int (&c)[4][4], int t, in
     return r;
 }
 
-// NW waves; UB = 64 (rows 16-byte aligned) or 128 (rows line-aligned): the
-// bytes of a row one load instruction reads; XC groups of 16 x per thread.
-template <int NW, int UB, int XC>
+// NW waves; UB = 64 or 128 (w 128-byte aligned: whole lines): the bytes of
+// a row one load instruction reads; BB = 128 or 256: the bytes of a row per
+// batch (256 only where no row has a phase); XC groups of 16 x per thread.
+template <int NW, int UB, int BB, int XC>
 __global__ void __launch_bounds__(NW * 64)
 q6k_gemv_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
                 float* __restrict__ y, int n, int S, long long row_stride, int rows_per_block,
                 int ncg)
 {
     static_assert(UB == 64 || UB == 128, "unit");
+    static_assert(BB == 128 || BB == 256, "batch");
     extern __shared__ __align__(16) unsigned char smem[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -193,18 +198,30 @@ q6k_gemv_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
     unsigned char* ring = smem + xbytes + wave * kQ6Wave;
     double* ypart = reinterpret_cast<double*>(smem + xbytes + NW * kQ6Wave);
 
-    // load role: LPR lanes per row and instruction
+    // load role: LPR lanes per row and instruction; a batch is BB bytes of
+    // each of the tile's 16 rows, NI instructions
     constexpr int LPR = UB / 16;
+    constexpr int NI = BB / 64;
     const int lrow = lane / LPR;
     const int lpiece = lane % LPR;
-    // instruction i (0..3) of a batch: the row it reads (of the tile) and its
-    // byte offset within the batch's 256 bytes
+    // instruction i (< NI) of a batch: the tile row it reads (the lane's
+    // first or second row, i & 1, for line units) and its byte offset
+    // within the batch
     auto ins_row = [&](int i) __attribute__((always_inline)) {
         return UB == 64 ? lrow : 8 * (i & 1) + lrow;
     };
     auto ins_off = [&](int i) __attribute__((always_inline)) {
         return UB == 64 ? 64 * i + 16 * lpiece : 128 * (i >> 1) + 16 * lpiece;
     };
+    // a row's batches start on a line (UB = 128; w is 128-byte aligned) or
+    // on its first 16-byte piece: the row's bytes sit `phase` bytes into
+    // its ring, at most kPhaseMax.  When the row stride is a multiple of
+    // kAlign every row starts on a line, and a task's origin B0 is aligned
+    // down to one too, so no row has a phase
+    constexpr uint32_t kAlign = UB == 128 ? 128u : 16u;
+    const bool aligned_rows = ((uint64_t)row_stride & (kAlign - 1u)) == 0;
+    const uint32_t kPhaseMax = aligned_rows ? 0u : kAlign - 16u;
+    const uint32_t kOriginMask = aligned_rows ? ~(kAlign - 1u) : ~15u;
 
     // x: all of it converted into LDS, the first batches of weights already
     // in flight
@@ -231,41 +248,55 @@ q6k_gemv_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
         c0 = (int)((long long)cg * S / ncg);
         c1 = (int)((long long)(cg + 1) * S / ncg);
     };
-    // per task: row base offsets (two rows for line units), the byte origin
-    // B0 (a unit boundary at or before column c0) and the last 16-byte piece
-    // of the task's bytes; loads past it re-read that piece
+    // per task: for the two rows the lane loads, the byte offset from w of
+    // its batch 0 (the row's bytes from the task's origin B0 at or before
+    // column c0, aligned down to kAlign) and of the last 16-byte piece of the task's
+    // bytes (loads past it re-read that piece); the phase of the lane's
+    // compute row j
     struct TaskGeo {
-        uint64_t rb[2];
-        uint32_t B0, last;
+        uint64_t a[2], lim[2];
+        uint32_t B0, pj;
     };
     auto task_geo = [&](int q) __attribute__((always_inline)) {
         int tile, c0, c1;
         task_cols(q, tile, c0, c1);
         TaskGeo g;
+        g.B0 = (210u * (uint32_t)c0) & kOriginMask;
+        const uint32_t last = (210u * (uint32_t)c1 - 1u) & ~15u;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int r = min(tile * 16 + ins_row(h), rows_here - 1);
-            g.rb[h] = (uint64_t)(row0 + r) * (uint64_t)row_stride;
+            const uint64_t rb = (uint64_t)(row0 + r) * (uint64_t)row_stride;
+            g.a[h] = (rb + g.B0) & ~(uint64_t)(kAlign - 1u);
+            g.lim[h] = rb + last;
         }
-        g.B0 = (210u * (uint32_t)c0) & ~(uint32_t)(UB - 1);
-        g.last = (210u * (uint32_t)c1 - 1u) & ~15u;
+        const int rj = min(tile * 16 + j, rows_here - 1);
+        g.pj = (uint32_t)(((uint64_t)(row0 + rj) * (uint64_t)row_stride + g.B0) &
+                          (uint64_t)(kAlign - 1u));
         return g;
     };
-    uint4 regs[2][4];
-    auto issue = [&](const TaskGeo& g, int b, int P) __attribute__((always_inline)) {
+    constexpr int kNBF = 512 / BB;           // batches in flight per wave (and ring slots)
+    uint4 regs[kNBF][NI];
+    auto issue = [&](const TaskGeo& g, int b, int slot) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t off = min(g.B0 + 256u * (uint32_t)b + (uint32_t)ins_off(i), g.last);
-            regs[P][i] = load_line_nt(w + g.rb[i & 1] + off);
+        for (int i = 0; i < NI; ++i) {
+            const uint64_t off = min(g.a[i & 1] + (uint32_t)BB * (uint32_t)b + (uint32_t)ins_off(i),
+                                     g.lim[i & 1]);
+            regs[slot][i] = load_line_nt(w + off);
         }
     };
-    // the first two batches of the wave's first task go out before the
-    // conversion (a wave without tasks loads from its clamped task)
+    auto issue_first = [&](const TaskGeo& g) __attribute__((always_inline)) {
+        static_for<kNBF>([&](auto I) __attribute__((always_inline)) {
+            issue(g, decltype(I)::value, decltype(I)::value);
+        });
+    };
+    // the first batches of the wave's first task go out before the
+    // conversion.  No load sits behind a branch (a wave without tasks loads
+    // from its clamped task too): the compiler's counter waits then let
+    // the conversion wait for x alone, and the stream keep every batch in
+    // flight
     TaskGeo geo = task_geo(0);
-    if (my_tasks > 0) {
-        issue(geo, 0, 0);
-        issue(geo, 1, 1);
-    }
+    issue_first(geo);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < XC; ++i) {
@@ -276,9 +307,11 @@ q6k_gemv_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
 
     unsigned char* rr = ring + j * kQ6Row;      // the lane's row in the ring (compute role)
     double acc = 0.0;
+    uint64_t flags[2] = {0, 0};                 // columns of the task with exact terms (S <= 128)
 
-    // column c of the task (origin B0): its 210 bytes are in the ring
-    auto column = [&](int c, uint32_t B0) __attribute__((always_inline)) {
+    // column c of the task (origin B0, the lane's row at phase pj): its 210
+    // bytes are in the ring
+    auto column = [&](int c, uint32_t B0, uint32_t pj) __attribute__((always_inline)) {
         const unsigned char* col = smem + (size_t)c * kQ6Col;
         const uint4 xd = *reinterpret_cast<const uint4*>(col + kQ6Digits + quad * 256 + j * 16);
         const double2 xi01 = *reinterpret_cast<const double2*>(col + kQ6Sum + quad * 32);
@@ -286,8 +319,9 @@ q6k_gemv_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
         const double2 s01 = *reinterpret_cast<const double2*>(col + kQ6Scale + hq * 32);
         const double2 s23 = *reinterpret_cast<const double2*>(col + kQ6Scale + hq * 32 + 16);
         const uint32_t cnt = *reinterpret_cast<const uint32_t*>(col + kQ6Word);
-        const uint32_t r0 = (210u * (uint32_t)c - B0) & (uint32_t)(kQ6Ring - 1);
-        const uint32_t sh = r0 & 3u;                 // wave-uniform: 0 or 2
+        const uint32_t rel = 210u * (uint32_t)c - B0;
+        const uint32_t r0 = (pj + rel) & (uint32_t)(kQ6Ring - 1);
+        const uint32_t sh = rel & 3u;                // wave-uniform (pj % 16 == 0): 0 or 2
         auto at = [&](uint32_t f) __attribute__((always_inline)) {
             return rr + ((r0 + f) & (uint32_t)(kQ6Ring - 4));
         };
@@ -333,51 +367,93 @@ q6k_gemv_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
         acc = subblock_term(acc, D[1], T1, 32.0f * D[1], XI[1], SC[1]);
         acc = subblock_term(acc, D[2], T2, 32.0f * D[2], XI[2], SC[2]);
         acc = subblock_term(acc, D[3], T3, 32.0f * D[3], XI[3], SC[3]);
-        // elements the digits leave out: fl32(d sc (q - 32)) x, exact in f64
+        // a column with elements the digits leave out: its exact terms come
+        // after the stream (correct_column), so this code stays small
         const uint32_t ncorr = __builtin_amdgcn_readfirstlane(cnt);
         if (ncorr != 0u) {
-            if (ncorr <= (uint32_t)kCorr) {
-                for (uint32_t k = 0; k < ncorr; ++k) {
-                    const Corr cr = *reinterpret_cast<const Corr*>(col + kQ6List + k * 8);
-                    const int e = __builtin_amdgcn_readfirstlane((int)cr.e);
-                    const float xe = __builtin_bit_cast(
-                        float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, cr.x)));
-                    const int te = (e >> 5) & 3;
-                    const int ie = e & 15;
-                    const uint32_t q = (pick_q6_code(cq, te, ie >> 2) >> (8 * (ie & 3))) & 63u;
-                    const float De = te == 0 ? D[0] : te == 1 ? D[1] : te == 2 ? D[2] : D[3];
-                    const float wv = De * (float)((int)q - 32);
-                    const double tv = (double)wv * (double)xe;
-                    const bool mine = (e >> 7) == hq && ((e >> 4) & 1) == aq;
-                    acc = mine ? acc + tv : acc;
-                }
-            } else {
-                const float* xg = x + (size_t)c * 256 + 128 * hq + 16 * aq;
+            flags[c >> 6] |= 1ull << (c & 63);
+        }
+    };
+
+    // the exact terms fl32(d sc (q - 32)) x (in f64, the oracle's arithmetic)
+    // of the elements of column c that the digits leave out, for the lane's
+    // row of `tile`: the column's bytes read again from global memory (five
+    // aligned dwords per 16-byte field, shifted; d by a 16-bit load)
+    auto correct_column = [&](int c, int tile) __attribute__((always_inline)) {
+        const unsigned char* col = smem + (size_t)c * kQ6Col;
+        const uint32_t ncorr =
+            __builtin_amdgcn_readfirstlane(*reinterpret_cast<const uint32_t*>(col + kQ6Word));
+        const double2 s01 = *reinterpret_cast<const double2*>(col + kQ6Scale + hq * 32);
+        const double2 s23 = *reinterpret_cast<const double2*>(col + kQ6Scale + hq * 32 + 16);
+        const double SC[4] = {s01.x, s01.y, s23.x, s23.y};
+        const int rj = min(tile * 16 + j, rows_here - 1);
+        const uint8_t* sb = w + (uint64_t)(row0 + rj) * (uint64_t)row_stride + 210u * (uint32_t)c;
+        const uint32_t sh = (210u * (uint32_t)c) & 3u;
+        const uint8_t* sb4 = sb - sh;                   // 4-byte aligned
+        uint32_t A[4], B[4], H[4];
+        read16_shifted(sb4 + 64u * hq + 16u * aq, sh, A);
+        read16_shifted(sb4 + 64u * hq + 32u + 16u * aq, sh, B);
+        read16_shifted(sb4 + 128u + 32u * hq + 16u * aq, sh, H);
+        const uint32_t* sp = reinterpret_cast<const uint32_t*>(sb4 + 192u + 8u * hq);
+        const uint32_t sw0 = __builtin_amdgcn_alignbyte(sp[1], sp[0], sh);
+        const uint32_t sw1 = __builtin_amdgcn_alignbyte(sp[2], sp[1], sh);
+        const uint16_t dbits = *reinterpret_cast<const uint16_t*>(sb + 208);
+        const float d = (float)__builtin_bit_cast(_Float16, dbits);
+        int cq[4][4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            cq[0][u] = (int)((A[u] & 0x0F0F0F0Fu) | ((H[u] << 4) & 0x30303030u));
+            cq[1][u] = (int)((B[u] & 0x0F0F0F0Fu) | ((H[u] << 2) & 0x30303030u));
+            cq[2][u] = (int)(((A[u] >> 4) & 0x0F0F0F0Fu) | (H[u] & 0x30303030u));
+            cq[3][u] = (int)(((B[u] >> 4) & 0x0F0F0F0Fu) | ((H[u] >> 2) & 0x30303030u));
+        }
+        const uint32_t sa = 8u * (uint32_t)aq;
+        float D[4];
+        D[0] = d * (float)(int)(int8_t)(uint8_t)(sw0 >> sa);
+        D[1] = d * (float)(int)(int8_t)(uint8_t)(sw0 >> (sa + 16u));
+        D[2] = d * (float)(int)(int8_t)(uint8_t)(sw1 >> sa);
+        D[3] = d * (float)(int)(int8_t)(uint8_t)(sw1 >> (sa + 16u));
+        if (ncorr <= (uint32_t)kCorr) {
+            for (uint32_t k = 0; k < ncorr; ++k) {
+                const Corr cr = *reinterpret_cast<const Corr*>(col + kQ6List + k * 8);
+                const int e = __builtin_amdgcn_readfirstlane((int)cr.e);
+                const float xe = __builtin_bit_cast(
+                    float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, cr.x)));
+                const int te = (e >> 5) & 3;
+                const int ie = e & 15;
+                const uint32_t q = (pick_q6_code(cq, te, ie >> 2) >> (8 * (ie & 3))) & 63u;
+                const float De = te == 0 ? D[0] : te == 1 ? D[1] : te == 2 ? D[2] : D[3];
+                const float wv = De * (float)((int)q - 32);
+                const double tv = (double)wv * (double)xe;
+                const bool mine = (e >> 7) == hq && ((e >> 4) & 1) == aq;
+                acc = mine ? acc + tv : acc;
+            }
+        } else {
+            const float* xg = x + (size_t)c * 256 + 128 * hq + 16 * aq;
 #pragma nounroll
-                for (int te = 0; te < 4; ++te) {
-                    const float4* src = reinterpret_cast<const float4*>(xg + 32 * te);
-                    float4 xe4[4];
+            for (int te = 0; te < 4; ++te) {
+                const float4* src = reinterpret_cast<const float4*>(xg + 32 * te);
+                float4 xe4[4];
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        xe4[u] = src[u];
-                    }
-                    const int sigma = grid_sigma_of(te == 0 ? SC[0] : te == 1 ? SC[1]
-                                                    : te == 2 ? SC[2] : SC[3]);
-                    const float De = te == 0 ? D[0] : te == 1 ? D[1] : te == 2 ? D[2] : D[3];
+                for (int u = 0; u < 4; ++u) {
+                    xe4[u] = src[u];
+                }
+                const int sigma = grid_sigma_of(te == 0 ? SC[0] : te == 1 ? SC[1]
+                                                : te == 2 ? SC[2] : SC[3]);
+                const float De = te == 0 ? D[0] : te == 1 ? D[1] : te == 2 ? D[2] : D[3];
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const uint32_t cw = pick_q6_code(cq, te, u);
-                        const float xs4[4] = {xe4[u].x, xe4[u].y, xe4[u].z, xe4[u].w};
+                for (int u = 0; u < 4; ++u) {
+                    const uint32_t cw = pick_q6_code(cq, te, u);
+                    const float xs4[4] = {xe4[u].x, xe4[u].y, xe4[u].z, xe4[u].w};
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            uint32_t uu;
-                            int cert;
-                            grid_element(xs4[i], sigma, uu, cert);
-                            const int q = (int)((cw >> (8 * i)) & 63u);
-                            const float wv = De * (float)(q - 32);
-                            const double tv = (double)wv * (double)xs4[i];
-                            acc = cert ? acc : acc + tv;
-                        }
+                    for (int i = 0; i < 4; ++i) {
+                        uint32_t uu;
+                        int cert;
+                        grid_element(xs4[i], sigma, uu, cert);
+                        const int q = (int)((cw >> (8 * i)) & 63u);
+                        const float wv = De * (float)(q - 32);
+                        const double tv = (double)wv * (double)xs4[i];
+                        acc = cert ? acc : acc + tv;
                     }
                 }
             }
@@ -387,39 +463,54 @@ q6k_gemv_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
     for (int q = 0; q < my_tasks; ++q) {
         int tile, c0, c1;
         task_cols(q, tile, c0, c1);
-        if (q > 0) {
-            geo = task_geo(q);
-            issue(geo, 0, 0);
-            issue(geo, 1, 1);
-        }
         const uint32_t B0 = geo.B0;
-        const int nb = (int)((210u * (uint32_t)c1 - B0 + 255u) / 256u);
+        // batches, in whole groups of kNBF (the surplus ones re-read the
+        // task's last piece and complete no column)
+        const int nb = (int)((210u * (uint32_t)c1 - B0 + kPhaseMax + BB - 1u) / (uint32_t)BB);
+        const int nbr = (nb + kNBF - 1) / kNBF * kNBF;
         int c = c0;
-        // batch b (register half P = b % 2, ring half P): into the ring,
-        // batch b + 2 out, then every column whose bytes are all in
-        auto consume = [&](int b, auto Pc) __attribute__((always_inline)) {
-            constexpr int P = decltype(Pc)::value;
+        // batch b (register and ring slot b % kNBF) into the ring, batch
+        // b + kNBF out into its registers, then every column whose bytes
+        // are in the ring for every row of the tile.  The slot written next
+        // holds none of a column not yet computed: with BB = 128 (four
+        // slots) such a column starts past 128 (b + 1) - 210 - 112, beyond
+        // batch b - 3; with BB = 256 (two slots; no row has a phase) past
+        // 256 (b + 1) - 210, inside batch b.
+        auto consume = [&](int b, auto sc) __attribute__((always_inline)) {
+            constexpr int sl = decltype(sc)::value;
+            constexpr int rs = sl;                 // ring slot (kNBF slots of BB bytes)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int o = P * 256 + ins_off(i);
+            for (int i = 0; i < NI; ++i) {
+                const int o = rs * BB + ins_off(i);
                 unsigned char* wr = ring + ins_row(i) * kQ6Row;
-                *reinterpret_cast<uint4*>(wr + o) = regs[P][i];
-                if (P == 0 && o < 32) {
-                    *reinterpret_cast<uint4*>(wr + kQ6Ring + o) = regs[P][i];
+                *reinterpret_cast<uint4*>(wr + o) = regs[sl][i];
+                if (rs == 0 && o < 32) {
+                    *reinterpret_cast<uint4*>(wr + kQ6Ring + o) = regs[sl][i];
                 }
             }
             __builtin_amdgcn_sched_barrier(0x000F);
-            issue(geo, b + 2, P);
-            const uint32_t have = 256u * (uint32_t)(b + 1);
-            while (c < c1 && 210u * (uint32_t)(c + 1) - B0 <= have) {
-                column(c, B0);
+            issue(geo, b + kNBF, sl);
+            const uint32_t have = (uint32_t)BB * (uint32_t)(b + 1);
+            while (c < c1 && 210u * (uint32_t)(c + 1) - B0 + kPhaseMax <= have) {
+                column(c, B0, geo.pj);
                 ++c;
             }
         };
-        for (int b = 0; b < nb; b += 2) {
-            consume(b, std::integral_constant<int, 0>());
-            if (b + 1 < nb) {
-                consume(b + 1, std::integral_constant<int, 1>());
+        for (int b = 0; b < nbr; b += kNBF) {
+            static_for<kNBF>([&](auto I) __attribute__((always_inline)) {
+                consume(b + decltype(I)::value, I);
+            });
+        }
+        // the next task's first batches (the last task's again after the
+        // last: clamped, harmless)
+        geo = task_geo(q + 1);
+        issue_first(geo);
+        // the task's columns with elements the digits leave out
+        for (int h = 0; h < 2; ++h) {
+            while (flags[h] != 0u) {
+                const int cf = 64 * h + __builtin_ctzll(flags[h]);
+                flags[h] &= flags[h] - 1u;
+                correct_column(cf, tile);
             }
         }
         // the rows of the task: four quadrant lanes per row
@@ -490,15 +581,15 @@ q6k_dequant_kernel(const uint8_t* __restrict__ w, float* __restrict__ out, int64
     }
 }
 
-template <int NW, int UB>
+template <int NW, int UB, int BB>
 static hipError_t launch_q6k_u(const Q6kPlan& p, const uint8_t* w, const float* x, float* y,
                                hipStream_t stream)
 {
     const int per = (p.S * 16 + NW * 64 - 1) / (NW * 64);
 #define Q6K_LAUNCH(XC)                                                                       \
-    hipLaunchKernelGGL((q6k_gemv_kernel<NW, UB, XC>), dim3(p.grid), dim3(NW * 64), p.lds_bytes, \
-                       stream, w, x, y, p.n, p.S, (long long)p.row_stride, p.rows_per_block,  \
-                       p.ncg)
+    hipLaunchKernelGGL((q6k_gemv_kernel<NW, UB, BB, XC>), dim3(p.grid), dim3(NW * 64),         \
+                       p.lds_bytes, stream, w, x, y, p.n, p.S, (long long)p.row_stride,        \
+                       p.rows_per_block, p.ncg)
     if (per <= 1) {
         Q6K_LAUNCH(1);
     } else if (per <= 2) {
@@ -512,17 +603,29 @@ static hipError_t launch_q6k_u(const Q6kPlan& p, const uint8_t* w, const float* 
     return hipGetLastError();
 }
 
+template <int NW>
+static hipError_t launch_q6k_w(const Q6kPlan& p, const uint8_t* w, const float* x, float* y,
+                               hipStream_t stream)
+{
+    if (p.unit == 64) {
+        return launch_q6k_u<NW, 64, 256>(p, w, x, y, stream);
+    }
+    return p.batch == 256 ? launch_q6k_u<NW, 128, 256>(p, w, x, y, stream)
+                          : launch_q6k_u<NW, 128, 128>(p, w, x, y, stream);
+}
+
 hipError_t launch_q6k_gemv(const Q6kPlan& p, const void* w, const float* x, float* y,
                            hipStream_t stream)
 {
     const uint8_t* wb = static_cast<const uint8_t*>(w);
+    if (p.unit == 64 && p.batch != 256) {
+        return hipErrorInvalidValue;
+    }
     if (p.waves_per_block == 8) {
-        return p.unit == 128 ? launch_q6k_u<8, 128>(p, wb, x, y, stream)
-                             : launch_q6k_u<8, 64>(p, wb, x, y, stream);
+        return launch_q6k_w<8>(p, wb, x, y, stream);
     }
     if (p.waves_per_block == 4) {
-        return p.unit == 128 ? launch_q6k_u<4, 128>(p, wb, x, y, stream)
-                             : launch_q6k_u<4, 64>(p, wb, x, y, stream);
+        return launch_q6k_w<4>(p, wb, x, y, stream);
     }
     return hipErrorInvalidValue;
 }

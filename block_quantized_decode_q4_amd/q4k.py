@@ -82,6 +82,7 @@ class q4k_plan_info(ctypes.Structure):
 class q6k_launch(ctypes.Structure):
     _fields_ = [
         ("unit_bytes", ctypes.c_int32),
+        ("batch_bytes", ctypes.c_int32),
         ("waves_per_block", ctypes.c_int32),
         ("column_groups", ctypes.c_int32),
         ("tiles_per_block", ctypes.c_int32),
@@ -91,6 +92,7 @@ class q6k_launch(ctypes.Structure):
 class q6k_plan_info(ctypes.Structure):
     _fields_ = [
         ("unit_bytes", ctypes.c_int32),
+        ("batch_bytes", ctypes.c_int32),
         ("waves_per_block", ctypes.c_int32),
         ("column_groups", ctypes.c_int32),
         ("rows_per_block", ctypes.c_int32),

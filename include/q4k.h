@@ -249,9 +249,9 @@ int q4k_plan(int64_t n, int64_t k, int64_t m, const q4k_launch* opts, int w_alig
  *    q6k_row_bytes(k).  row_stride must be a multiple of 16 and at least
  *    q6k_row_bytes(k) (Q4K_ERR_SHAPE below it, Q4K_ERR_ALIGN when it is not
  *    a multiple of 16: dense rows qualify when k % 2048 == 0), and w must
- *    hold n*row_stride bytes (the last row's padding included).  A stride
- *    that is a multiple of 128 with w 128-byte aligned lets the kernel read
- *    whole 128-byte lines per row.
+ *    hold n*row_stride bytes (the last row's padding included).  With w
+ *    128-byte aligned the kernel reads whole 128-byte lines of each row
+ *    (from the line holding its first byte), else 64-byte pieces.
  * ------------------------------------------------------------------- */
 
 /* Bytes of one dense Q6_K row of k weights: (k/256)*210, or 0 when k < 256
@@ -282,7 +282,9 @@ int q6k_gemv(const void* w, const float* x, float* y, int64_t n, int64_t k,
  * automatic). */
 typedef struct q6k_launch {
     int32_t unit_bytes;       /* bytes of a row per load instruction: 64, or 128
-                                 (row_stride % 128 == 0, w 128-byte aligned)  */
+                                 (whole lines; w 128-byte aligned)             */
+    int32_t batch_bytes;      /* bytes of each row per batch: 128 (unit 128), or
+                                 256 (unit 64, or row_stride % 128 == 0)        */
     int32_t waves_per_block;  /* 4 or 8 (4: k <= 16384)                        */
     int32_t column_groups;    /* tasks per 16-row tile, splitting its columns:
                                  1 .. min(16, k/256)                           */
@@ -296,6 +298,7 @@ int q6k_gemv_ex(const void* w, const float* x, float* y, int64_t n, int64_t k,
  * q4k_plan (0 = ask the device), w_aligned128 as for q4k_plan. */
 typedef struct q6k_plan_info {
     int32_t unit_bytes;
+    int32_t batch_bytes;
     int32_t waves_per_block;
     int32_t column_groups;
     int32_t rows_per_block;

@@ -378,14 +378,18 @@ def test_q6k_refusals(lib):
     assert g(A, MIS, A, 16, 2048, 0, None) == q4k.Q4K_ERR_ALIGN
     assert g(A, A, MIS, 16, 2048, 0, None) == q4k.Q4K_ERR_ALIGN
     for o in (dict(unit_bytes=32), dict(waves_per_block=2), dict(column_groups=9),
-              dict(column_groups=-1), dict(tiles_per_block=-2)):
+              dict(column_groups=-1), dict(tiles_per_block=-2), dict(batch_bytes=64),
+              dict(unit_bytes=64, batch_bytes=128)):
         cfg = q4k.q6k_launch(**o)
         assert lib.q6k_gemv_ex(A, A, A, 16, 2048, 0, ctypes.byref(cfg), None) == \
             q4k.Q4K_ERR_UNSUPPORTED, o
-    # whole-line units need a stride that is a multiple of 128 and w aligned to 128
+    # whole-line units need w aligned to 128 bytes; 256-byte batches need rows
+    # without a phase (a stride that is a multiple of 128, with lines)
     cfg = q4k.q6k_launch(unit_bytes=128)
-    assert lib.q6k_gemv_ex(A, A, A, 16, 4096, 0, ctypes.byref(cfg), None) == q4k.Q4K_ERR_UNSUPPORTED
     assert lib.q6k_gemv_ex(A + 16, A, A, 16, 4096, 3456, ctypes.byref(cfg), None) == \
+        q4k.Q4K_ERR_UNSUPPORTED
+    cfg = q4k.q6k_launch(batch_bytes=256)
+    assert lib.q6k_gemv_ex(A, A, A, 16, 4096, 0, ctypes.byref(cfg), None) == \
         q4k.Q4K_ERR_UNSUPPORTED
     d = lib.q6k_dequantize
     assert d(None, A, 16, 2048, 0, None) == q4k.Q4K_ERR_NULL
@@ -399,19 +403,19 @@ def test_q6k_refusals(lib):
     assert lib.q6k_load(A, buf.ctypes.data, buf.nbytes, 4, 2048, 1664, None) == q4k.Q4K_ERR_SHAPE
 
 
-@pytest.mark.parametrize("n,k,stride,aligned,unit,groups,rpb,grid", [
-    (32000, 4096, 0, True, 64, 1, 128, 250),      # dense LM head: 3360-byte rows
-    (32000, 4096, 3456, True, 128, 1, 128, 250),  # rows padded to whole lines
-    (32000, 4096, 3456, False, 64, 1, 128, 250),  # w not 128-byte aligned
-    (4096, 14336, 0, True, 64, 8, 16, 256),       # FFN down: one tile a workgroup, 8 groups
-    (256, 1024, 848, True, 64, 4, 16, 16),        # four superblocks: four groups at most
-    (128256, 4096, 0, True, 64, 1, 512, 251),     # four tiles a wave
-    (17, 2048, 0, True, 64, 8, 16, 2),
+@pytest.mark.parametrize("n,k,stride,aligned,unit,batch,groups,rpb,grid", [
+    (32000, 4096, 0, True, 128, 128, 1, 128, 250),     # dense LM head: 3360-byte rows, lines
+    (32000, 4096, 3456, True, 128, 256, 1, 128, 250),  # rows padded to whole lines
+    (32000, 4096, 3456, False, 64, 256, 1, 128, 250),  # w not 128-byte aligned: 64-byte pieces
+    (4096, 14336, 0, True, 128, 128, 8, 16, 256),      # FFN down: one tile a workgroup, 8 groups
+    (256, 1024, 848, True, 128, 128, 4, 16, 16),       # four superblocks: four groups at most
+    (128256, 4096, 0, True, 128, 128, 1, 512, 251),    # four tiles a wave
+    (17, 2048, 0, False, 64, 256, 8, 16, 2),
 ])
-def test_q6k_plan_automatic(n, k, stride, aligned, unit, groups, rpb, grid):
+def test_q6k_plan_automatic(n, k, stride, aligned, unit, batch, groups, rpb, grid):
     p = q4k.q6k_plan(n, k, stride, aligned, lds_max=163840)
-    assert (p.unit_bytes, p.column_groups, p.rows_per_block, p.grid, p.waves_per_block) == \
-        (unit, groups, rpb, grid, 8)
+    assert (p.unit_bytes, p.batch_bytes, p.column_groups, p.rows_per_block, p.grid,
+            p.waves_per_block) == (unit, batch, groups, rpb, grid, 8)
     # x (1264 bytes a column) + eight rings of 16 x 560 bytes + the group sums
     assert p.lds_bytes == (k // 256) * 1264 + 8 * 16 * 560 + (rpb * groups * 8 if groups > 1 else 0)
 

@@ -101,7 +101,7 @@ def test_q6k_unit_64_when_not_line_aligned(oracle_mod):
 
 
 GEOMETRIES = [
-    dict(unit_bytes=64), dict(unit_bytes=128), dict(waves_per_block=4),
+    dict(unit_bytes=64), dict(unit_bytes=128), dict(batch_bytes=128), dict(waves_per_block=4),
     dict(column_groups=1), dict(column_groups=3), dict(column_groups=5), dict(column_groups=16),
     dict(tiles_per_block=1), dict(tiles_per_block=3, column_groups=2),
     dict(waves_per_block=4, tiles_per_block=5, column_groups=7, unit_bytes=128),
@@ -122,8 +122,8 @@ def test_q6k_same_groups_same_bits(oracle_mod):
     w, x = synth.make_q6k_inputs(n, k, 1, seed=3301, row_stride=stride)
     _, view = _dev_weights(w)
     ys = [_run(view, x[0], n, k, stride, column_groups=4, **o)
-          for o in (dict(unit_bytes=64), dict(unit_bytes=128), dict(waves_per_block=4),
-                    dict(tiles_per_block=3))]
+          for o in (dict(unit_bytes=64), dict(unit_bytes=128), dict(batch_bytes=128),
+                    dict(waves_per_block=4), dict(tiles_per_block=3))]
     for y in ys[1:]:
         assert np.array_equal(y.view(np.uint32), ys[0].view(np.uint32))
 
