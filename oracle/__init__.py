@@ -18,6 +18,9 @@ Functions (names follow the problem's notation: d, dmin, sc_j, m_j, q):
   q6k_dequant_superblock(b)   one 210-byte Q6_K superblock -> 256 f32
   q6k_dequant(w, n, k)        Q6_K weights [n, k] (exact products)
   q6k_gemv(w, x, n)           the same GEMV over Q6_K weights
+  f16_cvt(x)                  f32 -> binary16 bits, nearest even
+  mirror_f16(w, fmt, n, k)    fp16 mirror of Q4_K (fmt 4) or Q6_K (fmt 6) rows
+  f16_gemm(w16, x16)          y = x16 @ w16^T exactly in f64, and its bound
 """
 from __future__ import annotations
 
@@ -91,6 +94,13 @@ def _load():
         lib.oq6_dequant.restype = ctypes.c_int
         lib.oq6_gemv.argtypes = [u8p, f32p, i64, i64, i64, i64, f64p, f64p]
         lib.oq6_gemv.restype = ctypes.c_int
+        u16p = ctypes.POINTER(ctypes.c_uint16)
+        lib.oq_f16_cvt.argtypes = [f32p, i64, u16p]
+        lib.oq_f16_cvt.restype = None
+        lib.oq_mirror_f16.argtypes = [u8p, ctypes.c_int, i64, i64, i64, u16p]
+        lib.oq_mirror_f16.restype = ctypes.c_int
+        lib.oq_f16_gemm.argtypes = [u16p, u16p, i64, i64, i64, f64p, f64p]
+        lib.oq_f16_gemm.restype = ctypes.c_int
         lib.oq_num_threads.argtypes = []
         lib.oq_num_threads.restype = ctypes.c_int
         lib.oq_set_num_threads.argtypes = [ctypes.c_int]
@@ -319,4 +329,53 @@ def q6k_gemv(w, x, n: int, row_stride: int = 0) -> tuple[np.ndarray, np.ndarray]
                       _ptr(y, ctypes.c_double), _ptr(bound, ctypes.c_double))
     if rc != 0:
         raise RuntimeError("oq6_gemv rc=%d" % rc)
+    return y, bound
+
+
+def f16_cvt(x) -> np.ndarray:
+    """binary16 bits (uint16) of float32 values, round to nearest even."""
+    lib = _load()
+    xa = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    out = np.empty(xa.shape, dtype=np.uint16)
+    lib.oq_f16_cvt(_ptr(xa, ctypes.c_float), xa.size, _ptr(out, ctypes.c_uint16))
+    return out
+
+
+def mirror_f16(w, fmt: int, n: int, k: int, row_stride: int = 0) -> np.ndarray:
+    """fp16 mirror (binary16 bits, uint16 [n, k]) of Q4_K rows (fmt 4, dense)
+    or Q6_K rows (fmt 6, at row_stride; 0 = dense)."""
+    lib = _load()
+    wb = _u8(w)
+    if fmt == 4:
+        _check_shape(wb, n, k)
+        stride = 0
+    elif fmt == 6:
+        stride = _q6k_stride(wb, n, k, row_stride)
+    else:
+        raise ValueError("fmt must be 4 or 6")
+    out = np.empty((n, k), dtype=np.uint16)
+    rc = lib.oq_mirror_f16(_ptr(wb, ctypes.c_uint8), fmt, n, k, stride, _ptr(out, ctypes.c_uint16))
+    if rc != 0:
+        raise RuntimeError("oq_mirror_f16 rc=%d" % rc)
+    return out
+
+
+def f16_gemm(w16, x16) -> tuple[np.ndarray, np.ndarray]:
+    """y[b, r] = sum_c w16[r, c] x16[b, c] exactly (f64) and its bound
+    sum |w16||x16|; w16 [n, k], x16 [m, k] binary16 bits (uint16)."""
+    lib = _load()
+    wa = np.ascontiguousarray(np.asarray(w16, dtype=np.uint16))
+    xa = np.ascontiguousarray(np.asarray(x16, dtype=np.uint16))
+    if xa.ndim == 1:
+        xa = xa.reshape(1, -1)
+    n, k = wa.shape
+    m, k2 = xa.shape
+    if k != k2:
+        raise ValueError("k mismatch")
+    y = np.empty((m, n), dtype=np.float64)
+    bound = np.empty((m, n), dtype=np.float64)
+    rc = lib.oq_f16_gemm(_ptr(wa, ctypes.c_uint16), _ptr(xa, ctypes.c_uint16), m, n, k,
+                         _ptr(y, ctypes.c_double), _ptr(bound, ctypes.c_double))
+    if rc != 0:
+        raise RuntimeError("oq_f16_gemm rc=%d" % rc)
     return y, bound

@@ -41,7 +41,9 @@
  * quantized x is x itself; for Q6_K: a hand-computed golden superblock,
  * one-hot brute force over every element and code bit against an
  * independently written packer, every weight equal to the exact product of
- * its fields, closed forms, exact dyadic dots, special d, row strides.
+ * its fields, closed forms, exact dyadic dots, special d, row strides; for
+ * the fp16 mirror and GEMM: numpy's binary16 cast of the pinned weights,
+ * integer-valued operands against exact integer products.
  */
 #include <math.h>
 #include <stdint.h>
@@ -536,6 +538,94 @@ int oq6_gemv(const uint8_t* w, const float* x, int64_t n, int64_t k, int64_t row
         }
     }
     return bad ? -2 : 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * The fp16 mirror and the prefill GEMM beside the decode path (memra-engine
+ * 0.83.1, src/f16_ffi.rs: docs of `memra_q4_K_dequant_f16` and
+ * `memra_q6_K_dequant_f16` -- GGUF superblocks to a row-major fp16 mirror
+ * built at load time; `memra_f16_cvt` -- the f32 activations to fp16;
+ * `memra_f16_pp_gemm` / `try_f16_gemm` -- y[m, out] = x[m, in] @ (fp16 W)^T
+ * with f32 accumulation).  The reading taken: a mirror element is the f32
+ * weight (as oq_dequant / oq6_dequant give it) rounded to binary16 to
+ * nearest-even (oq_f32_to_f16_rne), an activation likewise; the reference
+ * GEMM is the exact dot product of the two binary16 operands, in f64.
+ * ------------------------------------------------------------------------- */
+
+/* out[i] = binary16 bits of x[i], round to nearest even. */
+void oq_f16_cvt(const float* x, int64_t count, uint16_t* out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; ++i) {
+        out[i] = oq_f32_to_f16_rne(x[i]);
+    }
+}
+
+/* The fp16 mirror of n rows of Q4_K (fmt 4, dense rows) or Q6_K (fmt 6,
+ * rows at row_stride bytes): out[r*k + c] = binary16 of W[r][c]. */
+int oq_mirror_f16(const uint8_t* w, int fmt, int64_t n, int64_t k, int64_t row_stride,
+                  uint16_t* out)
+{
+    if (!oq_shape_ok(n, k) || (fmt != 4 && fmt != 6)) {
+        return -1;
+    }
+    if (fmt == 6 && row_stride < (k / OQ_QK) * OQ6_SB) {
+        return -1;
+    }
+    const int64_t S = k / OQ_QK;
+    int bad = 0;
+#pragma omp parallel
+    {
+        float* wrow = (float*)malloc((size_t)k * sizeof(float));
+        if (!wrow) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t r = 0; r < n; ++r) {
+                for (int64_t s = 0; s < S; ++s) {
+                    if (fmt == 4) {
+                        oq_dequant_superblock(w + (r * S + s) * OQ_SB, wrow + s * OQ_QK);
+                    } else {
+                        oq6_dequant_superblock(w + r * row_stride + s * OQ6_SB, wrow + s * OQ_QK);
+                    }
+                }
+                for (int64_t c = 0; c < k; ++c) {
+                    out[r * k + c] = oq_f32_to_f16_rne(wrow[c]);
+                }
+            }
+            free(wrow);
+        }
+    }
+    return bad ? -2 : 0;
+}
+
+/* y[b][r] = sum_c W16[r][c] * X16[b][c] and bound[b][r] = sum_c |W16||X16|,
+ * exactly in f64 (each product of two binary16 values is exact), for the
+ * fp16 mirror w16 (n x k) and fp16 activations x16 (m x k). */
+int oq_f16_gemm(const uint16_t* w16, const uint16_t* x16, int64_t m, int64_t n, int64_t k,
+                double* y, double* bound)
+{
+    if (m < 1 || n < 1 || k < 1) {
+        return -1;
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; ++r) {
+        for (int64_t b = 0; b < m; ++b) {
+            double acc = 0.0, mag = 0.0;
+            for (int64_t c = 0; c < k; ++c) {
+                const double wv = (double)oq_f16_to_f32(w16[r * k + c]);
+                const double xv = (double)oq_f16_to_f32(x16[b * k + c]);
+                acc += wv * xv;
+                mag += fabs(wv) * fabs(xv);
+            }
+            y[b * n + r] = acc;
+            if (bound) {
+                bound[b * n + r] = mag;
+            }
+        }
+    }
+    return 0;
 }
 
 int oq_num_threads(void)

@@ -707,6 +707,65 @@ def check_q6k_shape_errors(oracle_mod):
         raise AssertionError("row stride below the row accepted")
 
 
+# ----------------------------------------------------- fp16 mirror and GEMM
+# The mirror element is the pinned f32 weight rounded to binary16; numpy's
+# float16 cast (round to nearest even, written apart from the oracle) must
+# agree bit for bit.  The GEMM is pinned by integer-valued operands, whose
+# products and sums are exact, against integer matrix products, and by
+# one-hot rows that pick out one activation each (orientation).
+
+def _f16_bits(a):
+    return np.asarray(a, np.float32).astype(np.float16).view(np.uint16)
+
+
+def check_mirror_f16_is_the_rounded_weight(oracle_mod):
+    rng = np.random.default_rng(701)
+    n, k = 6, 1024
+    f = synth.draw_fields(rng, n, k // 256)
+    f.d_bits[0, 0] = 0x7800          # d = 32768: weights beyond the binary16 range -> inf
+    f.d_bits[1, 1] = 0x0001          # smallest subnormal d
+    w4 = synth.pack(f)
+    m4 = oracle_mod.mirror_f16(w4, 4, n, k)
+    assert np.array_equal(m4, _f16_bits(oracle_mod.dequant(w4, n, k)))
+    assert np.any(m4 == 0x7C00) or np.any(m4 == 0xFC00)
+    f6 = synth.draw_q6k_fields(rng, n, k // 256)
+    f6.d_bits[2, 0] = 0x7BFF         # largest finite d
+    w6 = synth.pack_q6k(f6, 896)
+    m6 = oracle_mod.mirror_f16(w6, 6, n, k, 896)
+    assert np.array_equal(m6, _f16_bits(oracle_mod.q6k_dequant(w6, n, k, 896)))
+
+
+def check_f16_cvt_matches_numpy(oracle_mod):
+    rng = np.random.default_rng(702)
+    x = (rng.standard_normal(20000) * np.exp2(rng.integers(-30, 20, size=20000))).astype(np.float32)
+    x[:6] = [0.0, -0.0, 65504.0, 65520.0, -1e-8, 6.0e-8]
+    assert np.array_equal(oracle_mod.f16_cvt(x), _f16_bits(x))
+
+
+def check_f16_gemm_integer_exact(oracle_mod):
+    rng = np.random.default_rng(703)
+    m, n, k = 5, 7, 300
+    wi = rng.integers(-64, 65, size=(n, k))
+    xi = rng.integers(-64, 65, size=(m, k))
+    y, bound = oracle_mod.f16_gemm(_f16_bits(wi), _f16_bits(xi))
+    assert np.array_equal(y, (xi @ wi.T).astype(np.float64))
+    assert np.array_equal(bound, (np.abs(xi) @ np.abs(wi).T).astype(np.float64))
+
+
+def check_f16_gemm_orientation(oracle_mod):
+    """Row r of W is one-hot at column (3 r + 1) mod k: y[b, r] is x[b] at
+    that column."""
+    rng = np.random.default_rng(704)
+    m, n, k = 3, 11, 37
+    w = np.zeros((n, k), np.float32)
+    for r in range(n):
+        w[r, (3 * r + 1) % k] = 1.0
+    x = rng.standard_normal((m, k)).astype(np.float16).astype(np.float32)
+    y, _ = oracle_mod.f16_gemm(_f16_bits(w), _f16_bits(x))
+    for r in range(n):
+        assert np.array_equal(y[:, r], x[:, (3 * r + 1) % k].astype(np.float64))
+
+
 # fastest first: the mutation test stops at the first failing check
 ALL_CHECKS = (
     check_golden_handbuilt_superblock,
@@ -740,4 +799,8 @@ ALL_CHECKS = (
     check_q6k_exact_dyadic_dot,
     check_q6k_generator_layout_agrees,
     check_q6k_onehot_every_element_and_bit,
+    check_f16_gemm_orientation,
+    check_f16_gemm_integer_exact,
+    check_f16_cvt_matches_numpy,
+    check_mirror_f16_is_the_rounded_weight,
 )

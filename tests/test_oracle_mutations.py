@@ -64,6 +64,12 @@ MUTANTS = {
                               "oq6_dequant_superblock(w + r * S * OQ6_SB + s * OQ6_SB, out"),
     "q6_gemv_x_vector_ignored": ("                    const float* xb = x + b * k;",
                                  "                    const float* xb = x;"),
+    "f16_gemm_transposed": ("(double)oq_f16_to_f32(w16[r * k + c])", "(double)oq_f16_to_f32(w16[c * n + r])"),
+    "f16_gemm_x_row_0": ("(double)oq_f16_to_f32(x16[b * k + c])", "(double)oq_f16_to_f32(x16[c])"),
+    "mirror_drops_lsb": ("out[r * k + c] = oq_f32_to_f16_rne(wrow[c]);",
+                         "out[r * k + c] = (uint16_t)(oq_f32_to_f16_rne(wrow[c]) & 0xFFFEu);"),
+    "mirror_q6_stride": ("oq6_dequant_superblock(w + r * row_stride + s * OQ6_SB, wrow + s * OQ_QK);\n                    }\n                }\n                for (int64_t c",
+                         "oq6_dequant_superblock(w + r * S * OQ6_SB + s * OQ6_SB, wrow + s * OQ_QK);\n                    }\n                }\n                for (int64_t c"),
 }
 
 
