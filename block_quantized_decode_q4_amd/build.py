@@ -18,7 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libq4k.so")
 SOURCES = [os.path.join(CSRC, "q4k_kernels.hip"), os.path.join(CSRC, "q4k_dpp.hip"),
            os.path.join(CSRC, "q4k_mfma.hip"), os.path.join(CSRC, "q4k_q8.hip"),
-           os.path.join(CSRC, "q4k_q6k.hip"), os.path.join(CSRC, "q4k_api.hip")]
+           os.path.join(CSRC, "q4k_q6k.hip"), os.path.join(CSRC, "q4k_f16.hip"),
+           os.path.join(CSRC, "q4k_api.hip")]
 HEADERS = [os.path.join(CSRC, "q4k_kernels.h"), os.path.join(CSRC, "q4k_device.h"),
            os.path.join(CSRC, "q4k_lines.h"), os.path.join(CSRC, "q4k_xrep.h"),
            os.path.join(os.path.dirname(PKG), "include", "q4k.h")]

@@ -612,6 +612,28 @@ int q6k_gemv_checked(const void* w, const float* x, float* y, int64_t n, int64_t
     return hip_status(q4k::launch_q6k_gemv(plan, w, x, y, static_cast<hipStream_t>(stream)));
 }
 
+// Arguments of the prefill GEMM (before any HIP call).
+int f16_gemm_checks(const void* w16, const void* x16, const float* y, int64_t m, int64_t n,
+                    int64_t k)
+{
+    if (!w16 || !x16 || !y) {
+        return Q4K_ERR_NULL;
+    }
+    if (m < 1 || n < 1 || k < 1 || m > kInt32Max || n > kInt32Max || k > kInt32Max) {
+        return Q4K_ERR_SHAPE;
+    }
+    if (k % 64 != 0) {
+        return Q4K_ERR_UNSUPPORTED;      // the k step of the tile
+    }
+    if (!aligned16(w16) || !aligned16(x16) || !aligned16(y)) {
+        return Q4K_ERR_ALIGN;
+    }
+    if (q4k::f16_gemm_grid(m, n) > kInt32Max) {
+        return Q4K_ERR_SHAPE;
+    }
+    return Q4K_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -874,6 +896,101 @@ int q6k_dequantize(const void* w, float* out, int64_t n, int64_t k, int64_t row_
     }
     return hip_status(q4k::launch_q6k_dequant(w, out, n, (int)(k / q4k::kQK), stride,
                                               static_cast<hipStream_t>(stream)));
+}
+
+int q4k_mirror_f16(const void* w, void* w16, int64_t n, int64_t k, void* stream)
+{
+    if (!w || !w16) {
+        return Q4K_ERR_NULL;
+    }
+    const int rc = check_nk(n, k);
+    if (rc != Q4K_OK) {
+        return rc;
+    }
+    if (!aligned16(w) || !aligned16(w16)) {
+        return Q4K_ERR_ALIGN;
+    }
+    const int64_t nsb = n * (k / q4k::kQK);
+    if ((nsb * 32 + 255) / 256 > kInt32Max) {
+        return Q4K_ERR_SHAPE;
+    }
+    return hip_status(q4k::launch_dequant_f16(w, w16, nsb, static_cast<hipStream_t>(stream)));
+}
+
+int q6k_mirror_f16(const void* w, void* w16, int64_t n, int64_t k, int64_t row_stride,
+                   void* stream)
+{
+    if (!w || !w16) {
+        return Q4K_ERR_NULL;
+    }
+    int rc = check_nk(n, k);
+    if (rc != Q4K_OK) {
+        return rc;
+    }
+    int64_t stride = 0;
+    rc = q6k_stride(k, row_stride, &stride);
+    if (rc != Q4K_OK) {
+        return rc;
+    }
+    if (!aligned16(w16)) {
+        return Q4K_ERR_ALIGN;
+    }
+    const int64_t groups = n * (k / q4k::kQK) * 16;
+    if ((groups + 255) / 256 > kInt32Max || n > INT64_MAX / stride) {
+        return Q4K_ERR_SHAPE;
+    }
+    return hip_status(q4k::launch_q6k_dequant_f16(w, w16, n, (int)(k / q4k::kQK), stride,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
+int q4k_f16_cvt(const float* x, void* x16, int64_t count, void* stream)
+{
+    if (!x || !x16) {
+        return Q4K_ERR_NULL;
+    }
+    if (count < 1 || (count + 1023) / 1024 > kInt32Max) {
+        return Q4K_ERR_SHAPE;
+    }
+    if (!aligned16(x) || !aligned16(x16)) {
+        return Q4K_ERR_ALIGN;
+    }
+    return hip_status(q4k::launch_f16_cvt(x, x16, count, static_cast<hipStream_t>(stream)));
+}
+
+
+int q4k_f16_gemm(const void* w16, const void* x16, float* y, int64_t m, int64_t n, int64_t k,
+                 void* stream)
+{
+    const int rc = f16_gemm_checks(w16, x16, y, m, n, k);
+    if (rc != Q4K_OK) {
+        return rc;
+    }
+    return hip_status(q4k::launch_f16_gemm(w16, x16, y, (int)m, (int)n, (int)k,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int q4k_f16_gemm_f32x(const void* w16, const float* x, void* xh, float* y, int64_t m,
+                      int64_t n, int64_t k, void* stream)
+{
+    if (!x || !xh) {
+        return Q4K_ERR_NULL;
+    }
+    int rc = f16_gemm_checks(w16, xh, y, m, n, k);
+    if (rc != Q4K_OK) {
+        return rc;
+    }
+    if (!aligned16(x)) {
+        return Q4K_ERR_ALIGN;
+    }
+    if ((m * k + 1023) / 1024 > kInt32Max) {
+        return Q4K_ERR_SHAPE;
+    }
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    rc = hip_status(q4k::launch_f16_cvt(x, xh, m * k, s));
+    if (rc != Q4K_OK) {
+        return rc;
+    }
+    return hip_status(q4k::launch_f16_gemm(w16, xh, y, (int)m, (int)n, (int)k, s));
 }
 
 const char* q4k_status_string(int rc)

@@ -1,0 +1,208 @@
+// q4k_f16.hip -- the prefill step beside the decode GEMV: a row-major fp16
+// mirror of the weights (built by the dequant kernels of q4k_kernels.hip and
+// q4k_q6k.hip) times fp16 activations on the matrix cores, f32 accumulation
+// (memra-engine 0.83.1, src/f16_ffi.rs: `memra_f16_cvt`, the f32 -> fp16
+// activation convert; `memra_f16_pp_gemm` / `try_f16_gemm`,
+// y[m, n] = x[m, k] @ (fp16 W)^T, f32 accumulate, for prefill batches).
+//
+// GEMM: a 256-thread workgroup computes a 128 x 128 tile of y (128 vectors x
+// 128 weight rows) over k in steps of 64: both operands are k-contiguous
+// (x rows and mirror rows), staged through LDS in rows of 64 halves padded
+// to 144 bytes (consecutive rows start 16 bytes apart in the banks), two
+// stages so the next step's global loads overlap this step's MFMAs.  Wave
+// (wm, wn) of the 2 x 2 layout holds a 64 x 64 sub-tile as 4 x 4
+// v_mfma_f32_16x16x32_f16 accumulators: lane l = 16 g + j holds
+// A[i = j][k = 8 g .. 8 g + 7] (an x row), B[k = 8 g .. 8 g + 7][j] (a
+// mirror row) and D[4 g + r][j].  Workgroups that share a block of mirror
+// rows run on the same XCD one after another (its L2 serves the repeats):
+// the mirror, the large operand, is read from HBM about once.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "q4k_kernels.h"
+
+namespace q4k {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t v4u_t __attribute__((ext_vector_type(4)));
+
+constexpr int kGB = 128;                 // tile rows of x and of the mirror
+constexpr int kGK = 64;                  // k per step
+constexpr int kGRow = kGK * 2 + 16;      // LDS bytes per staged row (padded)
+constexpr int kGTile = kGB * kGRow;      // one operand tile
+constexpr int kGXcd = 8;                 // XCDs: workgroups go round-robin over them
+
+// f32 -> fp16, round to nearest even (inf beyond the fp16 range, NaN kept).
+__global__ void __launch_bounds__(256)
+f16_cvt_kernel(const float* __restrict__ x, _Float16* __restrict__ out, int64_t count)
+{
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i + 4 <= count) {
+        const float4 v = *reinterpret_cast<const float4*>(x + i);
+        typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+        const h4_t h = {(_Float16)v.x, (_Float16)v.y, (_Float16)v.z, (_Float16)v.w};
+        *reinterpret_cast<h4_t*>(out + i) = h;
+    } else {
+        for (int64_t t = i; t < count; ++t) {
+            out[t] = (_Float16)x[t];
+        }
+    }
+}
+
+// y[b * n + r] = sum_c w16[r * k + c] x16[b * k + c] (f32 accumulation).
+// Grid: kGXcd * ceil(NT / kGXcd) * MT workgroups (MT, NT: tiles of x rows
+// and of mirror rows); k % 64 == 0.
+__global__ void __launch_bounds__(256)
+f16_gemm_kernel(const _Float16* __restrict__ w16, const _Float16* __restrict__ x16,
+                float* __restrict__ y, int m, int n, int k, int MT, int NT)
+{
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    // XCD-aware tile order: workgroup b runs on XCD b % 8; within an XCD
+    // the x tiles of one mirror tile follow each other
+    const int bid = blockIdx.x;
+    const int xcd = bid % kGXcd;
+    const int local = bid / kGXcd;
+    const int tm = local % MT;
+    const int tn = (local / MT) * kGXcd + xcd;
+    if (tn >= NT) {
+        return;
+    }
+    const int row_x0 = tm * kGB;
+    const int row_w0 = tn * kGB;
+
+    // load role: 4 x 16 bytes of each operand tile per thread per step
+    // (tile row idx / 8, 16-byte chunk idx % 8 of its 128 bytes)
+    const _Float16* xsrc[4];
+    const _Float16* wsrc[4];
+    int lds_off[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int idx = tid + 256 * i;
+        const int r = idx >> 3;
+        const int ch = idx & 7;
+        xsrc[i] = x16 + (int64_t)min(row_x0 + r, m - 1) * k + ch * 8;
+        wsrc[i] = w16 + (int64_t)min(row_w0 + r, n - 1) * k + ch * 8;
+        lds_off[i] = r * kGRow + ch * 16;
+    }
+    v4u_t xa[4], wa[4];
+    auto load = [&](int kb) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            xa[i] = *reinterpret_cast<const v4u_t*>(xsrc[i] + kb * kGK);
+            wa[i] = *reinterpret_cast<const v4u_t*>(wsrc[i] + kb * kGK);
+        }
+    };
+    auto stage = [&](int st) __attribute__((always_inline)) {
+        unsigned char* xs = smem + st * 2 * kGTile;
+        unsigned char* ws = xs + kGTile;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            *reinterpret_cast<v4u_t*>(xs + lds_off[i]) = xa[i];
+            *reinterpret_cast<v4u_t*>(ws + lds_off[i]) = wa[i];
+        }
+    };
+
+    // compute role: wave (wm, wn), lane (g, j)
+    const int wm = wave & 1;
+    const int wn = wave >> 1;
+    const int g = lane >> 4;
+    const int j = lane & 15;
+    f32x4_t acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    const int KB = k / kGK;
+    load(0);
+    stage(0);
+    __syncthreads();
+    for (int kb = 0; kb < KB; ++kb) {
+        const int st = kb & 1;
+        // the next step's tiles (the last step loads and stages its own
+        // again, into the stage nobody reads any more: no branch around it)
+        load(min(kb + 1, KB - 1));
+        const unsigned char* xs = smem + st * 2 * kGTile;
+        const unsigned char* ws = xs + kGTile;
+#pragma unroll
+        for (int s = 0; s < kGK / 32; ++s) {
+            half8_t av[4], bv[4];
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                av[a] = *reinterpret_cast<const half8_t*>(
+                    xs + (64 * wm + 16 * a + j) * kGRow + (32 * s + 8 * g) * 2);
+                bv[a] = *reinterpret_cast<const half8_t*>(
+                    ws + (64 * wn + 16 * a + j) * kGRow + (32 * s + 8 * g) * 2);
+            }
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[a], bv[b], acc[a][b],
+                                                                       0, 0, 0);
+                }
+            }
+        }
+        stage(st ^ 1);
+        __syncthreads();
+    }
+    // D[4 g + r][j] of block (a, b): x row 64 wm + 16 a + 4 g + r, mirror
+    // row 64 wn + 16 b + j
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int xr = row_x0 + 64 * wm + 16 * a + 4 * g + r;
+            if (xr < m) {
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const int wr = row_w0 + 64 * wn + 16 * b + j;
+                    if (wr < n) {
+                        y[(int64_t)xr * n + wr] = acc[a][b][r];
+                    }
+                }
+            }
+        }
+    }
+}
+
+hipError_t launch_f16_cvt(const float* x, void* out, int64_t count, hipStream_t stream)
+{
+    const int64_t blocks = (count + 1023) / 1024;
+    hipLaunchKernelGGL(f16_cvt_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x,
+                       static_cast<_Float16*>(out), count);
+    return hipGetLastError();
+}
+
+size_t f16_gemm_lds_bytes()
+{
+    return (size_t)4 * kGTile;
+}
+
+int64_t f16_gemm_grid(int64_t m, int64_t n)
+{
+    const int64_t MT = (m + kGB - 1) / kGB;
+    const int64_t NT = (n + kGB - 1) / kGB;
+    return kGXcd * ((NT + kGXcd - 1) / kGXcd) * MT;
+}
+
+hipError_t launch_f16_gemm(const void* w16, const void* x16, float* y, int m, int n, int k,
+                           hipStream_t stream)
+{
+    const int MT = (m + kGB - 1) / kGB;
+    const int NT = (n + kGB - 1) / kGB;
+    const int64_t grid = f16_gemm_grid(m, n);
+    hipLaunchKernelGGL(f16_gemm_kernel, dim3((unsigned)grid), dim3(256), f16_gemm_lds_bytes(),
+                       stream, static_cast<const _Float16*>(w16), static_cast<const _Float16*>(x16),
+                       y, m, n, k, MT, NT);
+    return hipGetLastError();
+}
+
+}  // namespace q4k

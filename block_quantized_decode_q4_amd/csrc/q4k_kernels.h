@@ -1,6 +1,6 @@
 // q4k_kernels.h -- internal interface between the C-ABI layer (q4k_api.hip)
 // and the kernels (q4k_kernels.hip, q4k_dpp.hip, q4k_mfma.hip, q4k_q8.hip,
-// q4k_q6k.hip).  Not installed, not part of the ABI.
+// q4k_q6k.hip, q4k_f16.hip).  Not installed, not part of the ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -79,5 +79,16 @@ hipError_t launch_q6k_gemv(const Q6kPlan& p, const void* w, const float* x, floa
 hipError_t launch_q6k_dequant(const void* w, float* out, int64_t n, int S, int64_t row_stride,
                               hipStream_t stream);
 size_t q6k_lds_bytes(int S, int waves, int rows_per_block, int ncg);
+
+// The fp16 mirror and the prefill GEMM (q4k_f16.hip; mirror builds in
+// q4k_kernels.hip and q4k_q6k.hip).
+hipError_t launch_dequant_f16(const void* w, void* out, int64_t nsb, hipStream_t stream);
+hipError_t launch_q6k_dequant_f16(const void* w, void* out, int64_t n, int S, int64_t row_stride,
+                                  hipStream_t stream);
+hipError_t launch_f16_cvt(const float* x, void* out, int64_t count, hipStream_t stream);
+hipError_t launch_f16_gemm(const void* w16, const void* x16, float* y, int m, int n, int k,
+                           hipStream_t stream);
+size_t f16_gemm_lds_bytes();
+int64_t f16_gemm_grid(int64_t m, int64_t n);
 
 }  // namespace q4k

@@ -476,11 +476,28 @@ gemv_stream_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
 
 // ------------------------------------------------------------- dequant
 // One thread per (superblock, chunk c, dword u): decodes 8 weights and
-// writes them as two float4.  w = fma(d*sc, q, -dmin*m); d*sc and dmin*m
-// are exact in f32 and so is d*sc*q, so the fma's single rounding is the
-// rounding of the exact value.
+// writes them as two groups of four (f32, or the fp16 mirror: the f32
+// weight rounded to nearest even).  w = fma(d*sc, q, -dmin*m); d*sc and
+// dmin*m are exact in f32 and so is d*sc*q, so the fma's single rounding is
+// the rounding of the exact value.
+template <typename T>
+__device__ __forceinline__ void store4(T* o, const float4& v);
+template <>
+__device__ __forceinline__ void store4<float>(float* o, const float4& v)
+{
+    *reinterpret_cast<float4*>(o) = v;
+}
+template <>
+__device__ __forceinline__ void store4<_Float16>(_Float16* o, const float4& v)
+{
+    typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+    const h4_t h = {(_Float16)v.x, (_Float16)v.y, (_Float16)v.z, (_Float16)v.w};
+    *reinterpret_cast<h4_t*>(o) = h;
+}
+
+template <typename T>
 __global__ void __launch_bounds__(256)
-dequant_kernel(const uint8_t* __restrict__ w, float* __restrict__ out, int64_t nsb)
+dequant_kernel(const uint8_t* __restrict__ w, T* __restrict__ out, int64_t nsb)
 {
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t sb = t >> 5;
@@ -515,9 +532,9 @@ dequant_kernel(const uint8_t* __restrict__ w, float* __restrict__ out, int64_t n
     hi.y = __builtin_fmaf(dsc_hi, (float)((D >> 12) & 15u), -dm_hi);
     hi.z = __builtin_fmaf(dsc_hi, (float)((D >> 20) & 15u), -dm_hi);
     hi.w = __builtin_fmaf(dsc_hi, (float)(D >> 28), -dm_hi);
-    float* o = out + sb * 256 + 64 * c + 4 * u;
-    *reinterpret_cast<float4*>(o) = lo;
-    *reinterpret_cast<float4*>(o + 32) = hi;
+    T* o = out + sb * 256 + 64 * c + 4 * u;
+    store4<T>(o, lo);
+    store4<T>(o + 32, hi);
 }
 
 // --------------------------------------------------------- calibration
@@ -662,8 +679,17 @@ hipError_t launch_dequant(const void* w, float* out, int64_t nsb, hipStream_t st
 {
     const int64_t threads = nsb * 32;
     const int64_t blocks = (threads + 255) / 256;
-    hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+    hipLaunchKernelGGL(dequant_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, stream,
                        static_cast<const uint8_t*>(w), out, nsb);
+    return hipGetLastError();
+}
+
+hipError_t launch_dequant_f16(const void* w, void* out, int64_t nsb, hipStream_t stream)
+{
+    const int64_t threads = nsb * 32;
+    const int64_t blocks = (threads + 255) / 256;
+    hipLaunchKernelGGL(dequant_kernel<_Float16>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       static_cast<const uint8_t*>(w), static_cast<_Float16*>(out), nsb);
     return hipGetLastError();
 }
 

@@ -545,9 +545,11 @@ q6k_gemv_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
 }
 
 // Dequantize: one thread per 16 weights (one scale); w = d sc (q - 32),
-// exact in f32.
+// exact in f32 (T = float), or that weight rounded to fp16 to nearest even
+// (T = _Float16: the mirror).
+template <typename T>
 __global__ void __launch_bounds__(256)
-q6k_dequant_kernel(const uint8_t* __restrict__ w, float* __restrict__ out, int64_t n, int S,
+q6k_dequant_kernel(const uint8_t* __restrict__ w, T* __restrict__ out, int64_t n, int S,
                    long long row_stride)
 {
     const int64_t gidx = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -574,10 +576,10 @@ q6k_dequant_kernel(const uint8_t* __restrict__ w, float* __restrict__ out, int64
         const int hi = (hb >> (2 * t)) & 3;
         o[i] = D * (float)(lo + 16 * hi - 32);
     }
-    float4* dst = reinterpret_cast<float4*>(out + r * (int64_t)S * 256 + (int64_t)s * 256 + 16 * g);
+    T* dst = out + r * (int64_t)S * 256 + (int64_t)s * 256 + 16 * g;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        dst[i] = make_float4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+    for (int i = 0; i < 16; ++i) {
+        dst[i] = (T)o[i];
     }
 }
 
@@ -635,8 +637,19 @@ hipError_t launch_q6k_dequant(const void* w, float* out, int64_t n, int S, int64
 {
     const int64_t total = n * (int64_t)S * 16;
     const int64_t blocks = (total + 255) / 256;
-    hipLaunchKernelGGL(q6k_dequant_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+    hipLaunchKernelGGL(q6k_dequant_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, stream,
                        static_cast<const uint8_t*>(w), out, n, S, (long long)row_stride);
+    return hipGetLastError();
+}
+
+hipError_t launch_q6k_dequant_f16(const void* w, void* out, int64_t n, int S, int64_t row_stride,
+                                  hipStream_t stream)
+{
+    const int64_t total = n * (int64_t)S * 16;
+    const int64_t blocks = (total + 255) / 256;
+    hipLaunchKernelGGL(q6k_dequant_kernel<_Float16>, dim3((unsigned)blocks), dim3(256), 0,
+                       stream, static_cast<const uint8_t*>(w), static_cast<_Float16*>(out), n, S,
+                       (long long)row_stride);
     return hipGetLastError();
 }
 

@@ -42,6 +42,11 @@ EXPORTED = (
     "q6k_gemv_ex",
     "q6k_plan",
     "q6k_dequantize",
+    "q4k_mirror_f16",
+    "q6k_mirror_f16",
+    "q4k_f16_cvt",
+    "q4k_f16_gemm",
+    "q4k_f16_gemm_f32x",
 )
 
 
@@ -148,6 +153,16 @@ def load_library():
         lib.q6k_plan.restype = ctypes.c_int
         lib.q6k_dequantize.argtypes = [vp, vp, i64, i64, i64, vp]
         lib.q6k_dequantize.restype = ctypes.c_int
+        lib.q4k_mirror_f16.argtypes = [vp, vp, i64, i64, vp]
+        lib.q4k_mirror_f16.restype = ctypes.c_int
+        lib.q6k_mirror_f16.argtypes = [vp, vp, i64, i64, i64, vp]
+        lib.q6k_mirror_f16.restype = ctypes.c_int
+        lib.q4k_f16_cvt.argtypes = [vp, vp, i64, vp]
+        lib.q4k_f16_cvt.restype = ctypes.c_int
+        lib.q4k_f16_gemm.argtypes = [vp, vp, vp, i64, i64, i64, vp]
+        lib.q4k_f16_gemm.restype = ctypes.c_int
+        lib.q4k_f16_gemm_f32x.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
+        lib.q4k_f16_gemm_f32x.restype = ctypes.c_int
         lib.q4k_status_string.argtypes = [ctypes.c_int]
         lib.q4k_status_string.restype = ctypes.c_char_p
         lib.q4k_read_calibrate.argtypes = [vp, ctypes.c_size_t, vp, vp]
@@ -305,6 +320,37 @@ def q6k_dequantize(w, out, n: int, k: int, row_stride: int = 0, stream=None) -> 
     """out[r*k + c] = W[r][c] in f32 (bit-exact); asynchronous on stream."""
     _check(load_library().q6k_dequantize(_addr(w), _addr(out), int(n), int(k), int(row_stride),
                                          _stream(stream)), "q6k_dequantize")
+
+
+def q4k_mirror_f16(w, w16, n: int, k: int, stream=None) -> None:
+    """The fp16 mirror (n x k halves) of dense Q4_K rows; asynchronous."""
+    _check(load_library().q4k_mirror_f16(_addr(w), _addr(w16), int(n), int(k), _stream(stream)),
+           "q4k_mirror_f16")
+
+
+def q6k_mirror_f16(w, w16, n: int, k: int, row_stride: int = 0, stream=None) -> None:
+    """The fp16 mirror (n x k halves) of Q6_K rows; asynchronous."""
+    _check(load_library().q6k_mirror_f16(_addr(w), _addr(w16), int(n), int(k), int(row_stride),
+                                         _stream(stream)), "q6k_mirror_f16")
+
+
+def q4k_f16_cvt(x, x16, count: int, stream=None) -> None:
+    """x16 = binary16 of x (nearest even); asynchronous."""
+    _check(load_library().q4k_f16_cvt(_addr(x), _addr(x16), int(count), _stream(stream)),
+           "q4k_f16_cvt")
+
+
+def q4k_f16_gemm(w16, x16, y, m: int, n: int, k: int, stream=None) -> None:
+    """y (m x n, f32) = x16 (m x k) @ w16 (n x k)^T on the matrix cores."""
+    _check(load_library().q4k_f16_gemm(_addr(w16), _addr(x16), _addr(y), int(m), int(n), int(k),
+                                       _stream(stream)), "q4k_f16_gemm")
+
+
+def q4k_f16_gemm_f32x(w16, x, xh, y, m: int, n: int, k: int, stream=None) -> None:
+    """Convert x (f32, m x k) into the scratch xh, then q4k_f16_gemm."""
+    _check(load_library().q4k_f16_gemm_f32x(_addr(w16), _addr(x), _addr(xh), _addr(y), int(m),
+                                            int(n), int(k), _stream(stream)),
+           "q4k_f16_gemm_f32x")
 
 
 def q4k_read_calibrate_blocks() -> int:

@@ -316,6 +316,54 @@ int q6k_plan(int64_t n, int64_t k, int64_t row_stride, int w_aligned128, const q
 int q6k_dequantize(const void* w, float* out, int64_t n, int64_t k, int64_t row_stride,
                    void* stream);
 
+/* ---------------------------------------------------------------------
+ * Prefill beside the decode path: a row-major fp16 mirror of the weights
+ * and an fp16 GEMM on the matrix cores for batches of many vectors
+ * (memra-engine 0.83.1, src/f16_ffi.rs: `memra_q4_K_dequant_f16` and
+ * `memra_q6_K_dequant_f16` build the mirror at load time, `memra_f16_cvt`
+ * converts the f32 activations, `memra_f16_pp_gemm` runs
+ * y[m, n] = x[m, k] @ (fp16 W)^T with f32 accumulation).
+ *  - A mirror element is the f32 weight (as q4k_dequantize / q6k_dequantize
+ *    give it) rounded to binary16, nearest even (beyond 65504: infinity);
+ *    activations are rounded the same way.  The mirror takes 2 bytes per
+ *    weight.
+ *  - The GEMM's products of two binary16 values are exact in f32; its sums
+ *    are f32, so y is within k * 2^-23 * sum|w16||x16| of the exact dot
+ *    product of the fp16 operands (the bound of an f32 sum of k terms in any
+ *    order, with a factor of 2 to spare).  Against the f32 weights and
+ *    activations the fp16 roundings add up to 2^-10 sum|w||x| more: this is
+ *    the numeric class of the pages' fp16 prefill lane, not q4k_gemv's.
+ * ------------------------------------------------------------------- */
+
+/* The fp16 mirror of n dense Q4_K rows: w16[r*k + c] = binary16 of W[r][c].
+ * w device (16-byte aligned), w16 device, n*k halves, 16-byte aligned.
+ * Asynchronous on `stream`. */
+int q4k_mirror_f16(const void* w, void* w16, int64_t n, int64_t k, void* stream);
+
+/* The fp16 mirror of n Q6_K rows at row_stride (0 = dense; the rules of
+ * q6k_gemv). */
+int q6k_mirror_f16(const void* w, void* w16, int64_t n, int64_t k, int64_t row_stride,
+                   void* stream);
+
+/* x16[i] = binary16 of x[i] (nearest even) for i < count: f32 in, fp16 out,
+ * both device and 16-byte aligned.  Asynchronous. */
+int q4k_f16_cvt(const float* x, void* x16, int64_t count, void* stream);
+
+/* y[b*n + r] = sum_c w16[r*k + c] * x16[b*k + c] for b < m, r < n: the fp16
+ * mirror w16 (n x k), fp16 activations x16 (m x k), y f32 (m x n, fully
+ * overwritten).  All device, 16-byte aligned; m, n >= 1; k >= 64 with
+ * k % 64 == 0 (Q4K_ERR_UNSUPPORTED otherwise).  Matrix cores
+ * (v_mfma_f32_16x16x32_f16), f32 accumulation; asynchronous; allocates
+ * nothing. */
+int q4k_f16_gemm(const void* w16, const void* x16, float* y, int64_t m, int64_t n, int64_t k,
+                 void* stream);
+
+/* q4k_f16_cvt of the f32 activations x (m x k) into the caller's scratch xh
+ * (m*k halves, 16-byte aligned), then q4k_f16_gemm: the pages' one-call
+ * prefill GEMM (`memra_f16_pp_gemm`).  Asynchronous; allocates nothing. */
+int q4k_f16_gemm_f32x(const void* w16, const float* x, void* xh, float* y, int64_t m,
+                      int64_t n, int64_t k, void* stream);
+
 /* Read `bytes` (a multiple of 16) of device memory at `buf` (16-byte
  * aligned) with coalesced 16-byte loads and write a checksum per workgroup
  * to `out` (device, q4k_read_calibrate_blocks() floats).  Benchmark

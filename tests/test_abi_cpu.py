@@ -430,3 +430,31 @@ def test_q6k_plan_lds_limit():
         p.rows_per_block * p.column_groups * 8 if p.column_groups > 1 else 0)
     with pytest.raises(q4k.Q4KError):
         q4k.q6k_plan(64, 18432, 0, True, lds_max=163840, waves_per_block=4)   # x per thread
+
+
+# ------------------------------------------------ fp16 mirror and prefill
+def test_f16_refusals(lib):
+    """Argument checks of the mirror, convert and GEMM entry points, before
+    any HIP call."""
+    assert lib.q4k_mirror_f16(None, A, 16, 256, None) == q4k.Q4K_ERR_NULL
+    assert lib.q4k_mirror_f16(A, A, 16, 300, None) == q4k.Q4K_ERR_SHAPE
+    assert lib.q4k_mirror_f16(A, MIS, 16, 256, None) == q4k.Q4K_ERR_ALIGN
+    assert lib.q6k_mirror_f16(A, None, 16, 2048, 0, None) == q4k.Q4K_ERR_NULL
+    assert lib.q6k_mirror_f16(A, A, 16, 2048, 1000, None) == q4k.Q4K_ERR_SHAPE
+    assert lib.q6k_mirror_f16(A, A, 16, 1024, 0, None) == q4k.Q4K_ERR_ALIGN   # 840-byte rows
+    assert lib.q4k_f16_cvt(None, A, 16, None) == q4k.Q4K_ERR_NULL
+    assert lib.q4k_f16_cvt(A, A, 0, None) == q4k.Q4K_ERR_SHAPE
+    assert lib.q4k_f16_cvt(A, MIS, 16, None) == q4k.Q4K_ERR_ALIGN
+    g = lib.q4k_f16_gemm
+    assert g(None, A, A, 8, 8, 64, None) == q4k.Q4K_ERR_NULL
+    assert g(A, A, None, 8, 8, 64, None) == q4k.Q4K_ERR_NULL
+    for m, n, k in ((0, 8, 64), (8, 0, 64), (8, 8, 0), (2 ** 31, 8, 64)):
+        assert g(A, A, A, m, n, k, None) == q4k.Q4K_ERR_SHAPE, (m, n, k)
+    assert g(A, A, A, 8, 8, 96, None) == q4k.Q4K_ERR_UNSUPPORTED      # k % 64
+    assert g(MIS, A, A, 8, 8, 64, None) == q4k.Q4K_ERR_ALIGN
+    assert g(A, A, MIS, 8, 8, 64, None) == q4k.Q4K_ERR_ALIGN
+    f = lib.q4k_f16_gemm_f32x
+    assert f(A, None, A, A, 8, 8, 64, None) == q4k.Q4K_ERR_NULL
+    assert f(A, A, None, A, 8, 8, 64, None) == q4k.Q4K_ERR_NULL
+    assert f(A, MIS, A, A, 8, 8, 64, None) == q4k.Q4K_ERR_ALIGN
+    assert f(A, A, A, A, 8, 8, 100, None) == q4k.Q4K_ERR_UNSUPPORTED
