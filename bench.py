@@ -42,6 +42,7 @@ if ROOT not in sys.path:
 
 METRIC = "Q4_K GEMV weight-stream GB/s and % of HBM peak (n×k, m=1)"
 HBM_PEAK_GBPS = 8000.0
+FP16_PEAK_TFLOPS = 2500.0       # dense fp16 matrix-core peak of MI355X
 DEFAULT_WORKLOAD = 3
 
 
@@ -208,6 +209,45 @@ def time_q6k(q4k, synth, torch, lib, n, k, x_d, y_d, sp, stream, args):
     return res
 
 
+def time_prefill(q4k, torch, sp, stream, args, m=512, shapes=((14336, 4096), (4096, 14336))):
+    """Time q4k_f16_gemm (fp16 mirror x fp16 activations, f32 accumulation)
+    at the prefill batch m on mirrors of the given (n, k) shapes (random
+    fp16 values; the time does not depend on them).  TFLOP/s against the
+    dense fp16 matrix-core peak."""
+    res = []
+    for n, k in shapes:
+        g = torch.Generator(device="cuda").manual_seed(n + k)
+        w16 = (torch.randn((n, k), device="cuda", generator=g) * 0.05).to(torch.float16)
+        x16 = torch.randn((m, k), device="cuda", generator=g).to(torch.float16)
+        y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+        lib = q4k.load_library()
+
+        def step():
+            rc = lib.q4k_f16_gemm(w16.data_ptr(), x16.data_ptr(), y.data_ptr(), m, n, k, sp)
+            if rc != 0:
+                raise q4k.Q4KError(rc, "q4k_f16_gemm")
+        reps = max(20, min(args.steps // 20, 500))
+        for _ in range(min(reps, 50)):
+            step()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        tflops = 2.0 * m * n * k / us / 1e6
+        res.append({"entry": "q4k_f16_gemm", "m": m, "n": n, "k": k, "us_per_gemm": round(us, 2),
+                    "reps": reps, "value": round(tflops, 1), "unit": "TFLOP/s",
+                    "frac_of_fp16_peak": round(tflops / FP16_PEAK_TFLOPS, 4)})
+        log("bench: q4k_f16_gemm m=%d n=%d k=%d: %.2f us, %.1f TFLOP/s" % (m, n, k, us, tflops))
+        del w16, x16, y
+    torch.cuda.empty_cache()
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -355,6 +395,9 @@ def main() -> int:
         torch.cuda.empty_cache()
         q6 = time_q6k(q4k, synth, torch, lib, n, k, x_d, y_d, sp, stream, args)
 
+    # the prefill GEMM beside the decode path (fp16 mirror, m = 512)
+    prefill = time_prefill(q4k, torch, sp, stream, args)
+
     alg_bytes = wb + 4 * k * m + 4 * n * m
     achieved = alg_bytes / t_launch / 1e9
     traffic = committed_traffic(wl.name)
@@ -405,6 +448,7 @@ def main() -> int:
         out["q8_variant"] = q8
     if q6:
         out["q6k"] = q6
+    out["prefill_f16"] = prefill
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline(w, x, n, k, m, wb, y_last)
