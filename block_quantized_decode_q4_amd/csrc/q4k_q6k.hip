@@ -250,9 +250,8 @@ q6k_gemv_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
     };
     // per task: for the two rows the lane loads, the byte offset from w of
     // its batch 0 (the row's bytes from the task's origin B0 at or before
-    // column c0, aligned down to kAlign) and of the last 16-byte piece of the task's
-    // bytes (loads past it re-read that piece); the phase of the lane's
-    // compute row j
+    // column c0, aligned down to kAlign) and the end of the 16-byte pieces
+    // holding the task's bytes; the phase of the lane's compute row j
     struct TaskGeo {
         uint64_t a[2], lim[2];
         uint32_t B0, pj;
@@ -263,12 +262,13 @@ q6k_gemv_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
         TaskGeo g;
         g.B0 = (210u * (uint32_t)c0) & kOriginMask;
         const uint32_t last = (210u * (uint32_t)c1 - 1u) & ~15u;
+        const bool past = q >= my_tasks;        // the prefetch after the wave's last task
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int r = min(tile * 16 + ins_row(h), rows_here - 1);
             const uint64_t rb = (uint64_t)(row0 + r) * (uint64_t)row_stride;
             g.a[h] = (rb + g.B0) & ~(uint64_t)(kAlign - 1u);
-            g.lim[h] = rb + last;
+            g.lim[h] = past ? 0u : rb + last + 16u;     // pieces below it are the task's
         }
         const int rj = min(tile * 16 + j, rows_here - 1);
         g.pj = (uint32_t)(((uint64_t)(row0 + rj) * (uint64_t)row_stride + g.B0) &
@@ -277,11 +277,15 @@ q6k_gemv_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
     };
     constexpr int kNBF = 512 / BB;           // batches in flight per wave (and ring slots)
     uint4 regs[kNBF][NI];
+    // a piece past the task's bytes (the surplus batches, the prefetch after
+    // the last task) reads 16 bytes of x instead: cached, so it costs no HBM
+    // traffic (x holds k * 4 >= 1024 bytes; a select, not a branch)
+    const uint64_t dx = (uint64_t)(reinterpret_cast<const uint8_t*>(x) - w) + 16u * (uint32_t)lane;
     auto issue = [&](const TaskGeo& g, int b, int slot) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-            const uint64_t off = min(g.a[i & 1] + (uint32_t)BB * (uint32_t)b + (uint32_t)ins_off(i),
-                                     g.lim[i & 1]);
+            const uint64_t o = g.a[i & 1] + (uint32_t)BB * (uint32_t)b + (uint32_t)ins_off(i);
+            const uint64_t off = o < g.lim[i & 1] ? o : dx;
             regs[slot][i] = load_line_nt(w + off);
         }
     };
@@ -464,8 +468,8 @@ q6k_gemv_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
         int tile, c0, c1;
         task_cols(q, tile, c0, c1);
         const uint32_t B0 = geo.B0;
-        // batches, in whole groups of kNBF (the surplus ones re-read the
-        // task's last piece and complete no column)
+        // batches, in whole groups of kNBF (the surplus ones read x and
+        // complete no column)
         const int nb = (int)((210u * (uint32_t)c1 - B0 + kPhaseMax + BB - 1u) / (uint32_t)BB);
         const int nbr = (nb + kNBF - 1) / kNBF * kNBF;
         int c = c0;
@@ -501,8 +505,7 @@ q6k_gemv_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
                 consume(b + decltype(I)::value, I);
             });
         }
-        // the next task's first batches (the last task's again after the
-        // last: clamped, harmless)
+        // the next task's first batches (after the last task: x)
         geo = task_geo(q + 1);
         issue_first(geo);
         // the task's columns with elements the digits leave out
