@@ -6,12 +6,13 @@
 // y[m, n] = x[m, k] @ (fp16 W)^T, f32 accumulate, for prefill batches).
 //
 // GEMM: a 256-thread workgroup computes a 128 x 128 tile of y (128 vectors x
-// 128 weight rows) over k in steps of 64: both operands are k-contiguous
+// 128 weight rows; 64 x 128 or 64 x 64 when that gives too few tiles to
+// fill the chip) over k in steps of 64: both operands are k-contiguous
 // (x rows and mirror rows), staged through LDS in rows of 64 halves padded
 // to 144 bytes (consecutive rows start 16 bytes apart in the banks), two
 // stages so the next step's global loads overlap this step's MFMAs.  Wave
-// (wm, wn) of the 2 x 2 layout holds a 64 x 64 sub-tile as 4 x 4
-// v_mfma_f32_16x16x32_f16 accumulators: lane l = 16 g + j holds
+// (wm, wn) of the 2 x 2 layout holds a quarter of the tile (64 x 64 for
+// 128 x 128) as 16 x 16 blocks of v_mfma_f32_16x16x32_f16 accumulators: lane l = 16 g + j holds
 // A[i = j][k = 8 g .. 8 g + 7] (an x row), B[k = 8 g .. 8 g + 7][j] (a
 // mirror row) and D[4 g + r][j].  Workgroups that share a block of mirror
 // rows run on the same XCD one after another (its L2 serves the repeats):
@@ -28,10 +29,8 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t v4u_t __attribute__((ext_vector_type(4)));
 
-constexpr int kGB = 128;                 // tile rows of x and of the mirror
 constexpr int kGK = 64;                  // k per step
 constexpr int kGRow = kGK * 2 + 16;      // LDS bytes per staged row (padded)
-constexpr int kGTile = kGB * kGRow;      // one operand tile
 constexpr int kGXcd = 8;                 // XCDs: workgroups go round-robin over them
 
 // f32 -> fp16, round to nearest even (inf beyond the fp16 range, NaN kept).
@@ -52,12 +51,22 @@ f16_cvt_kernel(const float* __restrict__ x, _Float16* __restrict__ out, int64_t 
 }
 
 // y[b * n + r] = sum_c w16[r * k + c] x16[b * k + c] (f32 accumulation).
+// Tiles of BM x rows by BN mirror rows (64 or 128 each); four waves in a
+// 2 x 2 layout, each with (BM / 32) x (BN / 32) MFMA blocks of 16 x 16.
 // Grid: kGXcd * ceil(NT / kGXcd) * MT workgroups (MT, NT: tiles of x rows
 // and of mirror rows); k % 64 == 0.
+template <int BM, int BN>
 __global__ void __launch_bounds__(256)
 f16_gemm_kernel(const _Float16* __restrict__ w16, const _Float16* __restrict__ x16,
                 float* __restrict__ y, int m, int n, int k, int MT, int NT)
 {
+    static_assert((BM == 64 || BM == 128) && (BN == 64 || BN == 128), "tile");
+    constexpr int LA = BM / 32;              // 16-byte loads of the x tile per thread and step
+    constexpr int LB = BN / 32;
+    constexpr int FA = BM / 32;              // 16-row MFMA blocks per wave
+    constexpr int FB = BN / 32;
+    constexpr int kXs = BM * kGRow;          // LDS bytes of one x tile
+    constexpr int kStage = (BM + BN) * kGRow;
     extern __shared__ __align__(16) unsigned char smem[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -72,38 +81,46 @@ f16_gemm_kernel(const _Float16* __restrict__ w16, const _Float16* __restrict__ x
     if (tn >= NT) {
         return;
     }
-    const int row_x0 = tm * kGB;
-    const int row_w0 = tn * kGB;
+    const int row_x0 = tm * BM;
+    const int row_w0 = tn * BN;
 
-    // load role: 4 x 16 bytes of each operand tile per thread per step
-    // (tile row idx / 8, 16-byte chunk idx % 8 of its 128 bytes)
-    const _Float16* xsrc[4];
-    const _Float16* wsrc[4];
-    int lds_off[4];
+    // load role: 16 bytes of a tile row per thread and load (tile row
+    // idx / 8, 16-byte chunk idx % 8 of its 128 bytes)
+    const _Float16* xsrc[LA];
+    const _Float16* wsrc[LB];
+    int xoff[LA], woff[LB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < LA; ++i) {
         const int idx = tid + 256 * i;
-        const int r = idx >> 3;
-        const int ch = idx & 7;
-        xsrc[i] = x16 + (int64_t)min(row_x0 + r, m - 1) * k + ch * 8;
-        wsrc[i] = w16 + (int64_t)min(row_w0 + r, n - 1) * k + ch * 8;
-        lds_off[i] = r * kGRow + ch * 16;
+        xsrc[i] = x16 + (int64_t)min(row_x0 + (idx >> 3), m - 1) * k + (idx & 7) * 8;
+        xoff[i] = (idx >> 3) * kGRow + (idx & 7) * 16;
     }
-    v4u_t xa[4], wa[4];
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+        const int idx = tid + 256 * i;
+        wsrc[i] = w16 + (int64_t)min(row_w0 + (idx >> 3), n - 1) * k + (idx & 7) * 8;
+        woff[i] = kXs + (idx >> 3) * kGRow + (idx & 7) * 16;
+    }
+    v4u_t xa[LA], wa[LB];
     auto load = [&](int kb) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < LA; ++i) {
             xa[i] = *reinterpret_cast<const v4u_t*>(xsrc[i] + kb * kGK);
+        }
+#pragma unroll
+        for (int i = 0; i < LB; ++i) {
             wa[i] = *reinterpret_cast<const v4u_t*>(wsrc[i] + kb * kGK);
         }
     };
     auto stage = [&](int st) __attribute__((always_inline)) {
-        unsigned char* xs = smem + st * 2 * kGTile;
-        unsigned char* ws = xs + kGTile;
+        unsigned char* base = smem + st * kStage;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            *reinterpret_cast<v4u_t*>(xs + lds_off[i]) = xa[i];
-            *reinterpret_cast<v4u_t*>(ws + lds_off[i]) = wa[i];
+        for (int i = 0; i < LA; ++i) {
+            *reinterpret_cast<v4u_t*>(base + xoff[i]) = xa[i];
+        }
+#pragma unroll
+        for (int i = 0; i < LB; ++i) {
+            *reinterpret_cast<v4u_t*>(base + woff[i]) = wa[i];
         }
     };
 
@@ -112,11 +129,11 @@ f16_gemm_kernel(const _Float16* __restrict__ w16, const _Float16* __restrict__ x
     const int wn = wave >> 1;
     const int g = lane >> 4;
     const int j = lane & 15;
-    f32x4_t acc[4][4];
+    f32x4_t acc[FA][FB];
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
+    for (int a = 0; a < FA; ++a) {
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
+        for (int b = 0; b < FB; ++b) {
             acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
     }
@@ -129,22 +146,25 @@ f16_gemm_kernel(const _Float16* __restrict__ w16, const _Float16* __restrict__ x
         // the next step's tiles (the last step loads and stages its own
         // again, into the stage nobody reads any more: no branch around it)
         load(min(kb + 1, KB - 1));
-        const unsigned char* xs = smem + st * 2 * kGTile;
-        const unsigned char* ws = xs + kGTile;
+        const unsigned char* xs = smem + st * kStage;
+        const unsigned char* ws = xs + kXs;
 #pragma unroll
         for (int s = 0; s < kGK / 32; ++s) {
-            half8_t av[4], bv[4];
+            half8_t av[FA], bv[FB];
 #pragma unroll
-            for (int a = 0; a < 4; ++a) {
+            for (int a = 0; a < FA; ++a) {
                 av[a] = *reinterpret_cast<const half8_t*>(
-                    xs + (64 * wm + 16 * a + j) * kGRow + (32 * s + 8 * g) * 2);
-                bv[a] = *reinterpret_cast<const half8_t*>(
-                    ws + (64 * wn + 16 * a + j) * kGRow + (32 * s + 8 * g) * 2);
+                    xs + ((BM / 2) * wm + 16 * a + j) * kGRow + (32 * s + 8 * g) * 2);
             }
 #pragma unroll
-            for (int a = 0; a < 4; ++a) {
+            for (int b = 0; b < FB; ++b) {
+                bv[b] = *reinterpret_cast<const half8_t*>(
+                    ws + ((BN / 2) * wn + 16 * b + j) * kGRow + (32 * s + 8 * g) * 2);
+            }
 #pragma unroll
-                for (int b = 0; b < 4; ++b) {
+            for (int a = 0; a < FA; ++a) {
+#pragma unroll
+                for (int b = 0; b < FB; ++b) {
                     acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[a], bv[b], acc[a][b],
                                                                        0, 0, 0);
                 }
@@ -153,17 +173,17 @@ f16_gemm_kernel(const _Float16* __restrict__ w16, const _Float16* __restrict__ x
         stage(st ^ 1);
         __syncthreads();
     }
-    // D[4 g + r][j] of block (a, b): x row 64 wm + 16 a + 4 g + r, mirror
-    // row 64 wn + 16 b + j
+    // D[4 g + r][j] of block (a, b): x row (BM / 2) wm + 16 a + 4 g + r,
+    // mirror row (BN / 2) wn + 16 b + j
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
+    for (int a = 0; a < FA; ++a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int xr = row_x0 + 64 * wm + 16 * a + 4 * g + r;
+            const int xr = row_x0 + (BM / 2) * wm + 16 * a + 4 * g + r;
             if (xr < m) {
 #pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const int wr = row_w0 + 64 * wn + 16 * b + j;
+                for (int b = 0; b < FB; ++b) {
+                    const int wr = row_w0 + (BN / 2) * wn + 16 * b + j;
                     if (wr < n) {
                         y[(int64_t)xr * n + wr] = acc[a][b][r];
                     }
@@ -181,28 +201,60 @@ hipError_t launch_f16_cvt(const float* x, void* out, int64_t count, hipStream_t 
     return hipGetLastError();
 }
 
-size_t f16_gemm_lds_bytes()
+// The tile: 128 x 128 while that gives at least 384 tiles (about 1.5 per
+// CU), else 64 x 128, else 64 x 64 (more, smaller tiles for short m or n
+// with long k).
+void f16_gemm_tile(int64_t m, int64_t n, int* bm, int* bn)
 {
-    return (size_t)4 * kGTile;
+    auto tiles = [&](int a, int b) { return ((m + a - 1) / a) * ((n + b - 1) / b); };
+    if (tiles(128, 128) >= 384) {
+        *bm = 128; *bn = 128;
+    } else if (tiles(64, 128) >= 384) {
+        *bm = 64; *bn = 128;
+    } else {
+        *bm = 64; *bn = 64;
+    }
+}
+
+size_t f16_gemm_lds_bytes(int bm, int bn)
+{
+    return (size_t)2 * (bm + bn) * kGRow;
 }
 
 int64_t f16_gemm_grid(int64_t m, int64_t n)
 {
-    const int64_t MT = (m + kGB - 1) / kGB;
-    const int64_t NT = (n + kGB - 1) / kGB;
+    int bm, bn;
+    f16_gemm_tile(m, n, &bm, &bn);
+    const int64_t MT = (m + bm - 1) / bm;
+    const int64_t NT = (n + bn - 1) / bn;
     return kGXcd * ((NT + kGXcd - 1) / kGXcd) * MT;
+}
+
+template <int BM, int BN>
+static hipError_t launch_f16_gemm_t(const void* w16, const void* x16, float* y, int m, int n,
+                                    int k, hipStream_t stream)
+{
+    const int MT = (m + BM - 1) / BM;
+    const int NT = (n + BN - 1) / BN;
+    const int64_t grid = kGXcd * ((int64_t)(NT + kGXcd - 1) / kGXcd) * MT;
+    hipLaunchKernelGGL((f16_gemm_kernel<BM, BN>), dim3((unsigned)grid), dim3(256),
+                       f16_gemm_lds_bytes(BM, BN), stream, static_cast<const _Float16*>(w16),
+                       static_cast<const _Float16*>(x16), y, m, n, k, MT, NT);
+    return hipGetLastError();
 }
 
 hipError_t launch_f16_gemm(const void* w16, const void* x16, float* y, int m, int n, int k,
                            hipStream_t stream)
 {
-    const int MT = (m + kGB - 1) / kGB;
-    const int NT = (n + kGB - 1) / kGB;
-    const int64_t grid = f16_gemm_grid(m, n);
-    hipLaunchKernelGGL(f16_gemm_kernel, dim3((unsigned)grid), dim3(256), f16_gemm_lds_bytes(),
-                       stream, static_cast<const _Float16*>(w16), static_cast<const _Float16*>(x16),
-                       y, m, n, k, MT, NT);
-    return hipGetLastError();
+    int bm, bn;
+    f16_gemm_tile(m, n, &bm, &bn);
+    if (bm == 128) {
+        return launch_f16_gemm_t<128, 128>(w16, x16, y, m, n, k, stream);
+    }
+    if (bn == 128) {
+        return launch_f16_gemm_t<64, 128>(w16, x16, y, m, n, k, stream);
+    }
+    return launch_f16_gemm_t<64, 64>(w16, x16, y, m, n, k, stream);
 }
 
 }  // namespace q4k

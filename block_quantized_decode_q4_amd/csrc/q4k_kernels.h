@@ -88,7 +88,8 @@ hipError_t launch_q6k_dequant_f16(const void* w, void* out, int64_t n, int S, in
 hipError_t launch_f16_cvt(const float* x, void* out, int64_t count, hipStream_t stream);
 hipError_t launch_f16_gemm(const void* w16, const void* x16, float* y, int m, int n, int k,
                            hipStream_t stream);
-size_t f16_gemm_lds_bytes();
+void f16_gemm_tile(int64_t m, int64_t n, int* bm, int* bn);
+size_t f16_gemm_lds_bytes(int bm, int bn);
 int64_t f16_gemm_grid(int64_t m, int64_t n);
 
 }  // namespace q4k

@@ -117,6 +117,23 @@ def test_f16_gemm_shapes(oracle_mod, m, n, k):
     _check_gemm(y, y_ref, bound, k, "m=%d n=%d k=%d" % (m, n, k))
 
 
+@pytest.mark.parametrize("m,n,k,tile", [(512, 14336, 128, "128 x 128"), (512, 6144, 128, "64 x 128"),
+                                        (500, 4100, 192, "64 x 64")])
+def test_f16_gemm_tile_variants(oracle_mod, m, n, k, tile):
+    """Shapes whose tile count selects each tile size (at least 384 tiles of
+    128 x 128, else of 64 x 128, else 64 x 64), ragged where possible;
+    outputs checked on sampled blocks, the tile edges among them."""
+    rng = np.random.default_rng(4600 + n)
+    w16 = oracle_mod.f16_cvt((rng.standard_normal((n, k)) * 0.05).astype(np.float32))
+    x16 = oracle_mod.f16_cvt(rng.standard_normal((m, k)).astype(np.float32))
+    _say("f16 gemm m=%d n=%d k=%d (%s tiles)" % (m, n, k, tile))
+    y = _gemm_gpu(w16, x16, m, n, k)
+    rows = np.r_[0:70, n // 2 - 70:n // 2 + 70, n - 70:n]
+    vecs = np.r_[0:70, m - 70:m]
+    y_ref, bound = oracle_mod.f16_gemm(w16[rows], x16[vecs])
+    _check_gemm(y[np.ix_(vecs, rows)], y_ref, bound, k, "%s sample" % tile)
+
+
 def test_f16_gemm_integer_operands_exact(oracle_mod):
     """Small integers: every partial sum is an integer below 2^24, so the
     f32 accumulation is exact and y must equal the integer product."""
