@@ -993,6 +993,37 @@ int q4k_f16_gemm_f32x(const void* w16, const float* x, void* xh, float* y, int64
     return hip_status(q4k::launch_f16_gemm(w16, xh, y, (int)m, (int)n, (int)k, s));
 }
 
+int q4k_f16_gemm_f32x_noalloc(const void* w16, const float* x, float* y, int64_t m, int64_t n,
+                              int64_t k, void* stream)
+{
+    if (!x) {
+        return Q4K_ERR_NULL;
+    }
+    // the checks of q4k_f16_gemm with the scratch standing in for xh (any
+    // non-null, aligned value: the array is 256-byte aligned)
+    int rc = f16_gemm_checks(w16, reinterpret_cast<const void*>(uintptr_t{256}), y, m, n, k);
+    if (rc != Q4K_OK) {
+        return rc;
+    }
+    if (!aligned16(x)) {
+        return Q4K_ERR_ALIGN;
+    }
+    if (m * k > q4k::kScratchHalves) {
+        return Q4K_ERR_UNSUPPORTED;      // beyond the static scratch (4 Mi halves)
+    }
+    void* xh = nullptr;
+    rc = hip_status(q4k::f16_scratch(&xh));
+    if (rc != Q4K_OK) {
+        return rc;
+    }
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    rc = hip_status(q4k::launch_f16_cvt(x, xh, m * k, s));
+    if (rc != Q4K_OK) {
+        return rc;
+    }
+    return hip_status(q4k::launch_f16_gemm(w16, xh, y, (int)m, (int)n, (int)k, s));
+}
+
 const char* q4k_status_string(int rc)
 {
     switch (rc) {

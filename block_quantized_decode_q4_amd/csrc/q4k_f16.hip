@@ -21,6 +21,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "q4k_kernels.h"
 
 namespace q4k {
@@ -255,6 +258,45 @@ hipError_t launch_f16_gemm(const void* w16, const void* x16, float* y, int m, in
         return launch_f16_gemm_t<64, 128>(w16, x16, y, m, n, k, stream);
     }
     return launch_f16_gemm_t<64, 64>(w16, x16, y, m, n, k, stream);
+}
+
+// ------------------------------------------------- allocation-free variant
+// The fp16 activations of q4k_f16_gemm_f32x_noalloc live in this array, one
+// copy per device, kept until the process ends.  In host code `scratch` is
+// only a stand-in for the symbol: its device address comes from
+// hipGetSymbolAddress, looked up once per device with that device current.
+static __device__ __align__(256) _Float16 scratch[kScratchHalves];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::atomic<void*> g_scratch[kScratchDevices];
+std::mutex g_scratch_lock;
+}  // namespace
+
+hipError_t f16_scratch(void** out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        return e;
+    }
+    if (dev < 0 || dev >= kScratchDevices) {
+        return hipErrorInvalidDevice;
+    }
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lk(g_scratch_lock);
+        p = g_scratch[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) {
+                return e;
+            }
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return hipSuccess;
 }
 
 }  // namespace q4k

@@ -89,6 +89,10 @@ hipError_t launch_f16_cvt(const float* x, void* out, int64_t count, hipStream_t 
 hipError_t launch_f16_gemm(const void* w16, const void* x16, float* y, int m, int n, int k,
                            hipStream_t stream);
 void f16_gemm_tile(int64_t m, int64_t n, int* bm, int* bn);
+// the static scratch of q4k_f16_gemm_f32x_noalloc: 4 Mi halves (8 MiB) per
+// device; f16_scratch gives its device address on the current device
+constexpr int64_t kScratchHalves = (int64_t)4 << 20;
+hipError_t f16_scratch(void** out);
 size_t f16_gemm_lds_bytes(int bm, int bn);
 int64_t f16_gemm_grid(int64_t m, int64_t n);
 

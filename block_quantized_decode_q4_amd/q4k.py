@@ -47,6 +47,7 @@ EXPORTED = (
     "q4k_f16_cvt",
     "q4k_f16_gemm",
     "q4k_f16_gemm_f32x",
+    "q4k_f16_gemm_f32x_noalloc",
 )
 
 
@@ -163,6 +164,8 @@ def load_library():
         lib.q4k_f16_gemm.restype = ctypes.c_int
         lib.q4k_f16_gemm_f32x.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
         lib.q4k_f16_gemm_f32x.restype = ctypes.c_int
+        lib.q4k_f16_gemm_f32x_noalloc.argtypes = [vp, vp, vp, i64, i64, i64, vp]
+        lib.q4k_f16_gemm_f32x_noalloc.restype = ctypes.c_int
         lib.q4k_status_string.argtypes = [ctypes.c_int]
         lib.q4k_status_string.restype = ctypes.c_char_p
         lib.q4k_read_calibrate.argtypes = [vp, ctypes.c_size_t, vp, vp]
@@ -351,6 +354,14 @@ def q4k_f16_gemm_f32x(w16, x, xh, y, m: int, n: int, k: int, stream=None) -> Non
     _check(load_library().q4k_f16_gemm_f32x(_addr(w16), _addr(x), _addr(xh), _addr(y), int(m),
                                             int(n), int(k), _stream(stream)),
            "q4k_f16_gemm_f32x")
+
+
+def q4k_f16_gemm_f32x_noalloc(w16, x, y, m: int, n: int, k: int, stream=None) -> None:
+    """q4k_f16_gemm_f32x with the library's static scratch (m*k <= 4 Mi);
+    calls on one GPU must not overlap."""
+    _check(load_library().q4k_f16_gemm_f32x_noalloc(_addr(w16), _addr(x), _addr(y), int(m),
+                                                    int(n), int(k), _stream(stream)),
+           "q4k_f16_gemm_f32x_noalloc")
 
 
 def q4k_read_calibrate_blocks() -> int:

@@ -364,6 +364,18 @@ int q4k_f16_gemm(const void* w16, const void* x16, float* y, int64_t m, int64_t 
 int q4k_f16_gemm_f32x(const void* w16, const float* x, void* xh, float* y, int64_t m,
                       int64_t n, int64_t k, void* stream);
 
+/* q4k_f16_gemm_f32x without the scratch argument, for callers that cannot
+ * allocate (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the fp16 activations go to a static device array
+ * of the library, 4 Mi halves (8 MiB) on each device it runs on, held until
+ * the process ends.  m*k above 4 * 2^20 returns Q4K_ERR_UNSUPPORTED before
+ * any HIP call.  Nothing is allocated; the first call on a device looks the
+ * array's address up (hipGetSymbolAddress).  Calls on one device share the
+ * array: calls that overlap on one GPU (other streams, other threads) race
+ * and must be serialised by the caller.  Asynchronous on `stream`. */
+int q4k_f16_gemm_f32x_noalloc(const void* w16, const float* x, float* y, int64_t m, int64_t n,
+                              int64_t k, void* stream);
+
 /* Read `bytes` (a multiple of 16) of device memory at `buf` (16-byte
  * aligned) with coalesced 16-byte loads and write a checksum per workgroup
  * to `out` (device, q4k_read_calibrate_blocks() floats).  Benchmark
