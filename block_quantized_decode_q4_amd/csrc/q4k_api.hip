@@ -75,7 +75,7 @@ int device_lds_max(size_t* out)
 }
 
 // Plan of the line-streamed kernels (weights 128-byte aligned; m <= 8, kernels
-// 5 and 6 m <= 16):
+// 5 and 7 m <= 16, kernel 6 m <= 32):
 // kernel 3 (m = 1, integer dot products on the vector ALU, any k), kernel 4
 // (one MFMA group per vector; k a multiple of 2048), kernel 5 (one MFMA per
 // sub-block and quad of vectors), kernel 6 (kernel 5 with x converted per
@@ -92,7 +92,10 @@ int make_plan_lines(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t
         return Q4K_ERR_UNSUPPORTED;    // rows of whole slabs (kernels 3, 5, 6: any rows)
     }
     if (m > q4k::kMaxM && kernel < 5) {
-        return Q4K_ERR_UNSUPPORTED;    // 9-16 vectors: the sub-block kernels only
+        return Q4K_ERR_UNSUPPORTED;    // 9-32 vectors: the sub-block kernels only
+    }
+    if (m > q4k::kMaxMStaged && kernel != 6) {
+        return Q4K_ERR_UNSUPPORTED;    // 17-32 vectors: eight quads, x per wave (kernel 6)
     }
     if (kernel == 4 && m > 2) {
         return Q4K_ERR_UNSUPPORTED;    // one MFMA group per vector: one or two vectors
@@ -206,7 +209,8 @@ int make_plan_lines(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t
 // the sub-block kernel (5, m >= 3) or the per-vector line-streamed kernel
 // (4, m = 2), the other one if only it fits, then the sub-block kernel with
 // a column window (7), then with per-wave x (6), else the x-stager kernel
-// (1, m <= 8; 9-16 vectors are refused there).
+// (1, m <= 8; 9-32 vectors are refused there).  17-32 vectors: kernel 6
+// only.
 // m = 1: the line-streamed vector-ALU kernel (3) where it applies and the
 // weights take at least 16 MiB, else the streaming kernel, whose shorter
 // start wins on smaller matrices; m = 1 takes the matrix cores only when
@@ -409,8 +413,8 @@ int make_plan(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t lds_m
 }
 
 // The plan gemv_checked would launch, for a given LDS budget; shape and
-// option checks in the same order.  9-16 vectors run in one pass over the
-// weights on the sub-block kernels (5, 6) or are refused: a batch is never
+// option checks in the same order.  9-32 vectors run in one pass over the
+// weights on the sub-block kernels (5-7; 6 beyond 16) or are refused: a batch is never
 // split into several launches (turbospark-runtime 0.1.0,
 // real_forward_dispatch.rs: doc of `encode_gemm_any`).
 int plan_checked(int64_t n, int64_t k, int64_t m, const q4k_launch* opts, bool w128,
@@ -449,7 +453,7 @@ int plan_checked(int64_t n, int64_t k, int64_t m, const q4k_launch* opts, bool w
         return Q4K_ERR_UNSUPPORTED;    // whole-line reads need 128-byte aligned rows
     }
     if (m > q4k::kMaxM && plan->kernel < 5) {
-        return Q4K_ERR_UNSUPPORTED;    // 9-16 vectors: the sub-block kernels only
+        return Q4K_ERR_UNSUPPORTED;    // 9-32 vectors: the sub-block kernels only
     }
     return Q4K_OK;
 }
@@ -1033,7 +1037,7 @@ const char* q4k_status_string(int rc)
     case Q4K_ERR_SIZE: return "byte count does not match n rows of the format (144 or 210 bytes per 256 weights)";
     case Q4K_ERR_ALIGN: return "a pointer, or a Q6_K row stride, is not 16-byte aligned";
     case Q4K_ERR_UNSUPPORTED:
-        return "unsupported: m > 16, or launch options that do not fit the shape, m or the "
+        return "unsupported: m > 32, or launch options that do not fit the shape, m or the "
                "device";
     default: break;
     }

@@ -14,7 +14,8 @@ constexpr int kBlockBytes = 144;  // bytes per superblock
 constexpr int kSpanSB = 16;       // superblocks per wave pass (4 lanes each)
 constexpr int kSpan = kSpanSB * kQK;
 constexpr int kMaxM = 8;         // vectors per launch that every kernel takes
-constexpr int kMaxMWide = 16;    // the sub-block matrix-core kernels 5 and 6
+constexpr int kMaxMStaged = 16;  // kernels 5 and 7: x of at most four vector quads in LDS
+constexpr int kMaxMWide = 32;    // kernel 6 (eight quads, x per wave and column)
 constexpr int kReadBlocks = 512;     // two 1024-lane workgroups per CU of a 256-CU part
 
 // One resolved launch of the GEMV kernel.

@@ -458,29 +458,45 @@ __device__ __forceinline__ double vector_corrections(double acc, uint32_t cnt, c
     return acc;
 }
 
-// The row sums of up to four vector quads as named values: the correction
+// The row sums of up to eight vector quads as named values: the correction
 // loops pick a quad at run time, and an array indexed so would be kept in
 // scratch memory (the compiler turns a chain of selects over an array's
 // elements back into an indexed load).
 struct QuadAcc {
-    double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+    double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0, a4 = 0.0, a5 = 0.0, a6 = 0.0, a7 = 0.0;
 
     template <int Q>
     __device__ __forceinline__ double& at()
     {
+        static_assert(Q >= 0 && Q < 8, "eight quads at most");
         if constexpr (Q == 0) {
             return a0;
         } else if constexpr (Q == 1) {
             return a1;
         } else if constexpr (Q == 2) {
             return a2;
-        } else {
+        } else if constexpr (Q == 3) {
             return a3;
+        } else if constexpr (Q == 4) {
+            return a4;
+        } else if constexpr (Q == 5) {
+            return a5;
+        } else if constexpr (Q == 6) {
+            return a6;
+        } else {
+            return a7;
         }
     }
     __device__ __forceinline__ double get(int q) const
     {
-        return q == 0 ? a0 : q == 1 ? a1 : q == 2 ? a2 : a3;
+        return q == 0   ? a0
+               : q == 1 ? a1
+               : q == 2 ? a2
+               : q == 3 ? a3
+               : q == 4 ? a4
+               : q == 5 ? a5
+               : q == 6 ? a6
+                        : a7;
     }
     __device__ __forceinline__ void set(int q, double v)
     {
@@ -488,14 +504,18 @@ struct QuadAcc {
         a1 = q == 1 ? v : a1;
         a2 = q == 2 ? v : a2;
         a3 = q == 3 ? v : a3;
+        a4 = q == 4 ? v : a4;
+        a5 = q == 5 ? v : a5;
+        a6 = q == 6 ? v : a6;
+        a7 = q == 7 ? v : a7;
     }
 };
 
 // Columns of x a wave of kernel 6 holds in registers ahead of its step: with
 // four, waiting for a column's x (loads complete in order) never waits for
 // a weight line before the line stream itself would (the lines are three
-// ahead); two vector quads take two, as 4 x 32 registers do not fit, and
-// four quads one (64 registers).
+// ahead); two vector quads take two, as 4 x 32 registers do not fit, four
+// quads one (64 registers), eight quads one (128).
 template <int NQ>
 constexpr int jit_ahead()
 {
@@ -570,7 +590,13 @@ gemv_i8_sub_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
     // again: its sums reach only lanes whose results are never stored)
     float4 xv[XC][4];
     auto load_group = [&](int q0, float4 (&v)[4]) __attribute__((always_inline)) {
-        const int qc = min(q0, ngroups - 1);
+        int qc = min(q0, ngroups - 1);
+        if constexpr (NQ > 4) {
+            // eight quads: each address from the group index at its use (the
+            // compiler would otherwise keep all eight quads' pointers, and
+            // more, live across the stream and spill them)
+            asm volatile("" : "+s"(qc));
+        }
         const int b = 4 * (qc % NQ) + (lane >> 4);
         const float* src = x + (size_t)min(b, m - 1) * k + (size_t)(qc / NQ) * 256 + 16 * (lane & 15);
 #pragma unroll
@@ -579,9 +605,12 @@ gemv_i8_sub_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
         }
     };
     // JIT: slot a holds the x of a column with c mod kA = a (first column
-    // of the wave's first slab: c_first)
+    // of the wave's first slab: c_first); with eight quads a slot holds
+    // four of them (kXQ), and each quad's registers are refilled with the
+    // quad four on as soon as it is converted
     constexpr int kA = JIT ? jit_ahead<NQ>() : 1;
-    float4 xa[kA][NQ][4];
+    constexpr int kXQ = NQ > 4 ? 4 : NQ;
+    float4 xa[kA][kXQ][4];
     const int ntasks = ((rows_here + 15) >> 4) * ncg;
     const int c_first = 8 * ((min(wave, ntasks - 1) % ncg) * slabs_per_task);
     // window: group of quad q of the column in slot sl (column parity) of slab cg
@@ -622,7 +651,7 @@ gemv_i8_sub_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
 #pragma unroll
             for (int a = 0; a < kA; ++a) {
 #pragma unroll
-                for (int q = 0; q < NQ; ++q) {
+                for (int q = 0; q < kXQ; ++q) {
                     load_group((c_first + a) * NQ + q, xa[a][q]);
                 }
             }
@@ -705,6 +734,12 @@ gemv_i8_sub_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
                 T = __builtin_fma(k2.y, 128.0, T);
             }
             acc.at<q>() = subblock_term(acc.at<q>(), t.Ds[sb], T, t.Ms[sb], k2.y, k2.x);
+            if constexpr (NQ > 4) {
+                // eight quads: the sum is formed here, not sunk towards its
+                // use at the task's end (which keeps every quad's MFMA
+                // results live and spills)
+                asm volatile("" : "+v"(acc.at<q>()));
+            }
         }
     };
     // kernel 5: the column's groups of the stage, one quad after the other
@@ -741,19 +776,30 @@ gemv_i8_sub_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
     // only after the previous quad's reads); a quad of which some vector has
     // uncertified elements in the column sets its bit in `dirty`, and those
     // quads' exact terms follow, found again from x.  Then the slot is
-    // refilled with the column kA positions on (past cend: the next slab's
-    // or task's, from cn).  Positions past a partial slab's end (invalid)
+    // refilled with the column kA positions on (ca: past cend, the next
+    // slab's or task's, from cn); with eight quads each quad's registers are
+    // refilled right after its conversion, with the quad four on (of this
+    // column, then of ca).  Positions past a partial slab's end (invalid)
     // keep the slots cycling.
     auto step_jit = [&](int c, int cend, int cn, const unsigned char* rr, uint32_t b0, int cp,
                         bool valid) __attribute__((always_inline)) {
-        float4 (&v)[NQ][4] = xa[JIT ? cp % kA : 0];
+        float4 (&v)[kXQ][4] = xa[JIT ? cp % kA : 0];
+        const int ca = c + kA < cend ? c + kA : cn + (c + kA - cend);
         __builtin_amdgcn_sched_barrier(0);
         if (valid) {
             const Tile t = prep(rr, b0);
             uint32_t dirty = 0;
             static_for<NQ>([&](auto qc) __attribute__((always_inline)) {
                 constexpr int q = decltype(qc)::value;
-                const int total = convert_quad(v[q], xw, xl + q * kSbLists, lane);
+                int lo = q * kSbLists;
+                if constexpr (NQ > 4) {
+                    asm volatile("" : "+s"(lo));
+                }
+                const int total = convert_quad(v[q % kXQ], xw, xl + lo, lane);
+                if constexpr (NQ > kXQ) {
+                    load_group(q + kXQ < NQ ? c * NQ + q + kXQ : ca * NQ + q + kXQ - NQ,
+                               v[q % kXQ]);
+                }
                 dirty |= (total != 0 ? 1u : 0u) << q;
                 quad(t, qc, xw);
                 __builtin_amdgcn_sched_barrier(0);
@@ -773,10 +819,11 @@ gemv_i8_sub_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
                 }
             }
         }
-        const int ca = c + kA < cend ? c + kA : cn + (c + kA - cend);
+        if (NQ <= kXQ || !valid) {
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-            load_group(ca * NQ + q, v[q]);
+            for (int q = 0; q < kXQ; ++q) {
+                load_group(ca * NQ + q, v[q]);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -855,7 +902,11 @@ gemv_i8_sub_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
         const int r = (task / ncg) * 16 + j;
         static_for<NQ>([&](auto qc) __attribute__((always_inline)) {
             constexpr int q = decltype(qc)::value;
-            const int b = 4 * q + g;
+            int b4 = 4 * q;
+            if constexpr (NQ > 4) {
+                asm volatile("" : "+s"(b4));     // the row's address at its use, as above
+            }
+            const int b = b4 + g;
             if (b < m && r < rows_here) {
                 if (ncg == 1) {
                     y[(size_t)b * n + row0 + r] = (float)acc.at<q>();
@@ -995,10 +1046,10 @@ static hipError_t launch_lines_m(const GemvPlan& p, const uint8_t* w, const floa
     return launch_lines_x<8, 3, 4, M>(p, w, x, y, stream);
 }
 
-// vector quads of the sub-block kernels' launch for m vectors (1, 2 or 4)
+// vector quads of the sub-block kernels' launch for m vectors (1, 2, 4 or 8)
 static int sub_quads(int m)
 {
-    return m > 8 ? 4 : m > 4 ? 2 : 1;
+    return m > kMaxMStaged ? 8 : m > 8 ? 4 : m > 4 ? 2 : 1;
 }
 
 hipError_t launch_gemv_mfma(const GemvPlan& p, const void* w, const float* x, float* y,
@@ -1007,6 +1058,9 @@ hipError_t launch_gemv_mfma(const GemvPlan& p, const void* w, const float* x, fl
     const uint8_t* wb = static_cast<const uint8_t*>(w);
     if (p.kernel >= 5) {
         const int nq = sub_quads(p.m);         // the quads the LDS sizes count
+        if (nq == 8 && p.kernel != 6) {
+            return hipErrorInvalidValue;   // eight quads: per-wave x only
+        }
         if (p.kernel == 5) {
             if (nq == 4) return launch_sub<4>(p, wb, x, y, stream);
             if (nq == 2) return launch_sub<2>(p, wb, x, y, stream);
@@ -1018,8 +1072,9 @@ hipError_t launch_gemv_mfma(const GemvPlan& p, const void* w, const float* x, fl
             if (nq == 2) return launch_sub_x<1, 2, kModeWindow>(p, wb, x, y, stream);
             return launch_sub_x<1, 1, kModeWindow>(p, wb, x, y, stream);
         }
-        // four quads: four waves, whose lanes may hold 512 registers (the
-        // x of the next column takes 64 of them)
+        // four or eight quads: four waves, whose lanes may hold 512
+        // registers (the x of the next column takes 64 or 128 of them)
+        if (nq == 8) return launch_sub_x<1, 8, kModeJit, 4>(p, wb, x, y, stream);
         if (nq == 4) return launch_sub_x<1, 4, kModeJit, 4>(p, wb, x, y, stream);
         if (nq == 2) return launch_sub_x<1, 2, kModeJit>(p, wb, x, y, stream);
         return launch_sub_x<1, 1, kModeJit>(p, wb, x, y, stream);
@@ -1042,7 +1097,7 @@ size_t sub_lds_bytes(int S, int m)
 
 int jit_waves(int m)
 {
-    return sub_quads(m) == 4 ? 4 : 8;
+    return sub_quads(m) >= 4 ? 4 : 8;
 }
 
 size_t jit_lds_bytes(int S, int m)

@@ -67,7 +67,7 @@ def test_gemv_refusals(lib):
     for n, k, m in ((0, 256, 1), (-1, 256, 1), (16, 255, 1), (16, 0, 1), (16, 384, 1),
                     (16, 256, 0), (16, 256, -3), (2 ** 31, 256, 1), (16, 2 ** 31 + 256, 1)):
         assert raw_gemv(lib, A, A, A, n, k, m) == q4k.Q4K_ERR_SHAPE, (n, k, m)
-    for m in (17, 32):
+    for m in (33, 64):
         assert raw_gemv(lib, A, A, A, 16, 256, m) == q4k.Q4K_ERR_UNSUPPORTED
     assert raw_gemv(lib, MIS, A, A, 16, 256, 1) == q4k.Q4K_ERR_ALIGN
     assert raw_gemv(lib, A, MIS, A, 16, 256, 1) == q4k.Q4K_ERR_ALIGN
@@ -166,7 +166,7 @@ def test_binding_raises_with_status():
         q4k.q4k_gemv(0, A, A, 16, 256, 1, stream=0)
     assert ei.value.rc == q4k.Q4K_ERR_NULL
     with pytest.raises(q4k.Q4KError) as ei:
-        q4k.q4k_gemv(A, A, A, 16, 256, 17, stream=0)
+        q4k.q4k_gemv(A, A, A, 16, 256, 33, stream=0)
     assert ei.value.rc == q4k.Q4K_ERR_UNSUPPORTED
 
 
@@ -244,8 +244,8 @@ def test_plan_refusals(lib):
     out = q4k.q4k_plan_info()
     assert lib.q4k_plan(4096, 4096, 1, None, 1, MI355X_LDS, None) == q4k.Q4K_ERR_NULL
     assert lib.q4k_plan(16, 100, 1, None, 1, MI355X_LDS, ctypes.byref(out)) == q4k.Q4K_ERR_SHAPE
-    assert lib.q4k_plan(16, 256, 17, None, 1, MI355X_LDS, ctypes.byref(out)) == q4k.Q4K_ERR_UNSUPPORTED
-    # 9-16 vectors need the one-pass sub-block kernels, which need 128-byte
+    assert lib.q4k_plan(16, 256, 33, None, 1, MI355X_LDS, ctypes.byref(out)) == q4k.Q4K_ERR_UNSUPPORTED
+    # 9-32 vectors need the one-pass sub-block kernels, which need 128-byte
     # aligned weights: refused, never split into two launches
     assert lib.q4k_plan(16, 256, 9, None, 0, MI355X_LDS, ctypes.byref(out)) == \
         q4k.Q4K_ERR_UNSUPPORTED
@@ -265,9 +265,13 @@ def test_plan_refusals(lib):
     (14336, 4096, 9, 7),
     (32000, 4096, 16, 7),
     (14336, 8192, 16, 6),     # four slabs x four quads: per-wave x
+    (14336, 4096, 32, 6),     # five to eight quads: per-wave x only
+    (4096, 14336, 32, 6),
+    (17, 1280, 17, 6),
+    (32000, 4096, 24, 6),
 ])
 def test_plan_wide_batches(n, k, m, kernel):
-    """9-16 vectors: one pass over the weights on a sub-block kernel."""
+    """9-32 vectors: one pass over the weights on a sub-block kernel."""
     p = q4k.q4k_plan(n, k, m, lds_max=MI355X_LDS)
     assert p.kernel == kernel
     assert p.lds_bytes <= MI355X_LDS
@@ -276,9 +280,10 @@ def test_plan_wide_batches(n, k, m, kernel):
 @pytest.mark.parametrize("n,k,m,aligned", [
     (14336, 4096, 9, False),  # weights not 128-byte aligned
     (64, 4096, 12, False),
+    (14336, 4096, 32, False),
 ])
 def test_plan_wide_batches_refused(n, k, m, aligned):
-    """9-16 vectors where no one-pass kernel applies: refused by name, not
+    """9-32 vectors where no one-pass kernel applies: refused by name, not
     split into launches of at most eight (turbospark-runtime 0.1.0,
     real_forward_dispatch.rs: doc of `encode_gemm_any`); eight still run."""
     with pytest.raises(q4k.Q4KError) as ei:
@@ -292,6 +297,14 @@ def test_plan_wide_batch_refusals():
         with pytest.raises(q4k.Q4KError) as ei:
             q4k.q4k_plan(14336, 4096, 9, lds_max=MI355X_LDS, **opts)
         assert ei.value.rc == q4k.Q4K_ERR_UNSUPPORTED
+    # more than sixteen vectors: kernel 6 only (eight quads of x do not fit
+    # kernel 5's stage or kernel 7's window)
+    for kern in (5, 7, 1, 4):
+        with pytest.raises(q4k.Q4KError) as ei:
+            q4k.q4k_plan(14336, 4096, 20, lds_max=MI355X_LDS, kernel=kern)
+        assert ei.value.rc == q4k.Q4K_ERR_UNSUPPORTED
+    p = q4k.q4k_plan(14336, 4096, 32, lds_max=MI355X_LDS, kernel=6)
+    assert p.kernel == 6 and p.threads == 256
     # kernel 6 with more than eight vectors runs four waves only
     with pytest.raises(q4k.Q4KError) as ei:
         q4k.q4k_plan(14336, 4096, 16, lds_max=MI355X_LDS, kernel=6, waves_per_block=8)

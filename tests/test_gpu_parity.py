@@ -833,14 +833,18 @@ def test_random_shapes_automatic_plan(oracle_mod, n, k, m, off):
     assert_within(y, y_ref, bound, "n=%d k=%d m=%d off=%d" % (n, k, m, off))
 
 
-# 9-16 vectors: one pass over the weights for up to four quads of vectors on
-# the sub-block kernels.  Per vector the digits, MFMAs and sums are those of
-# a single-vector launch of the same kernel and column grouping.
+# 9-32 vectors: one pass over the weights for up to eight quads of vectors on
+# the sub-block kernels (beyond four quads: kernel 6 only).  Per vector the
+# digits, MFMAs and sums are those of a single-vector launch of the same
+# kernel and column grouping.
 @pytest.mark.parametrize("n,k,m", [(300, 4096, 16), (130, 4096, 9), (17, 2048, 12), (64, 8192, 13),
                                    (33, 2048, 15), (1, 2048, 10), (257, 16384, 16),
                                    (40, 14336, 11),
                                    # rows of partial slabs: kernel 5's whole x stage
-                                   (17, 1280, 13), (5, 768, 16), (70, 1536, 9)])
+                                   (17, 1280, 13), (5, 768, 16), (70, 1536, 9),
+                                   # five to eight quads
+                                   (300, 4096, 32), (17, 1280, 17), (64, 8192, 24),
+                                   (40, 14336, 32), (5, 768, 20), (1, 2048, 29), (130, 11008, 27)])
 def test_wide_batch(oracle_mod, n, k, m):
     w, x = synth.make_inputs(n, k, m, seed=n * 37 + k + 11 * m)
     y_ref, bound = oracle_mod.gemv(w, x, n)
@@ -883,8 +887,28 @@ def test_wide_batch_full_size(oracle_mod):
         assert np.array_equal(y8.view(np.uint32), y16[8 * h:8 * h + 8].view(np.uint32)), h
 
 
+def test_wide_batch_32_full_size(oracle_mod):
+    """14336 x 4096 with 32 vectors (automatic: kernel 6 on eight quads, one
+    pass over the weights) against the oracle, and against two calls of
+    sixteen vectors on the same kernel and column grouping (bit-identical)."""
+    n, k, m = 14336, 4096, 32
+    w, x = synth.make_inputs(n, k, m, seed=14336 + 4096 + 32)
+    y_ref, bound = oracle_mod.gemv(w, x, n)
+    w_d = dev(w)
+    _say("wide batch automatic n=%d k=%d m=%d" % (n, k, m))
+    p = q4k.q4k_plan(n, k, m)
+    assert p.kernel == 6 and p.threads == 256
+    y = run_gemv(w_d, x, n, k, m)
+    assert_within(y, y_ref, bound, "14336 x 4096 m=32")
+    for h in range(2):
+        y16 = run_gemv(w_d, x[16 * h:16 * h + 16], n, k, 16, kernel=6,
+                       cols_per_task=p.cols_per_task)
+        assert np.array_equal(y16.view(np.uint32), y[16 * h:16 * h + 16].view(np.uint32)), h
+
+
 @pytest.mark.parametrize("n,k,m,off", [(300, 4096, 12, 0), (130, 11008, 16, 0), (33, 2304, 9, 48),
-                                       (4096, 14336, 16, 0)])
+                                       (4096, 14336, 16, 0), (4096, 14336, 32, 0),
+                                       (33, 2304, 20, 48)])
 def test_wide_batch_automatic(oracle_mod, n, k, m, off):
     """Automatic plans of 9-16 vectors: one pass against the oracle, or a
     refusal (unaligned weights; rows whose sixteen-vector plan exceeds the
