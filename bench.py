@@ -209,6 +209,50 @@ def time_q6k(q4k, synth, torch, lib, n, k, x_d, y_d, sp, stream, args):
     return res
 
 
+def time_wide_batches(q4k, synth, torch, lib, sp, stream, args, n=14336, k=4096, ms=(16, 32)):
+    """Time q4k_gemv with more vectors than the pages' batch of eight (one
+    pass over the weights on the sub-block matrix-core kernels) on seeded
+    Q4_K weights of n x k, cycling through >= rotate-gib of copies."""
+    w, x = synth.make_inputs(n, k, max(ms), seed=3000 + n + k)
+    nbytes = w.size
+    copies = max(4, math.ceil(args.rotate_gib * (1 << 30) / nbytes))
+    pool = torch.empty((copies, nbytes), dtype=torch.uint8, device="cuda")
+    src = torch.from_numpy(w).cuda()
+    for c in range(copies):
+        pool[c].copy_(src)
+    del src
+    ptrs = [pool[c].data_ptr() for c in range(copies)]
+    x_d = torch.from_numpy(x).cuda()
+    y_d = torch.empty((max(ms), n), dtype=torch.float32, device="cuda")
+    res = []
+    for m in ms:
+        def stepm(i):
+            rc = lib.q4k_gemv(ptrs[i % copies], x_d.data_ptr(), y_d.data_ptr(), n, k, m, sp)
+            if rc != 0:
+                raise q4k.Q4KError(rc, "q4k_gemv")
+        steps = max(100, min(args.steps, 2000))
+        for i in range(min(args.warmup, 500)):
+            stepm(i)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(steps):
+            stepm(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        plan = q4k.q4k_plan(n, k, m)
+        res.append({"entry": "q4k_gemv", "workload": "q4k_gemv_n%d_k%d_m%d" % (n, k, m),
+                    "kernel": KERNEL_NAMES.get(plan.kernel, str(plan.kernel)),
+                    "us_per_step": round(us, 3), "us_per_vector": round(us / m, 3),
+                    "steps": steps, "value": round(nbytes / us / 1e3, 2), "unit": "GB/s"})
+        log("bench: q4k_gemv n=%d k=%d m=%d: %.3f us" % (n, k, m, us))
+    del pool, x_d, y_d
+    torch.cuda.empty_cache()
+    return res
+
+
 def time_prefill(q4k, torch, sp, stream, args, m=512, shapes=((14336, 4096), (4096, 14336))):
     """Time q4k_f16_gemm (fp16 mirror x fp16 activations, f32 accumulation)
     at the prefill batch m on mirrors of the given (n, k) shapes (random
@@ -398,6 +442,14 @@ def main() -> int:
     # the prefill GEMM beside the decode path (fp16 mirror, m = 512)
     prefill = time_prefill(q4k, torch, sp, stream, args)
 
+    # batches beyond eight vectors (one pass over the weights)
+    wide = None
+    if m == 1:
+        if q6 is None:
+            del pool
+            torch.cuda.empty_cache()
+        wide = time_wide_batches(q4k, synth, torch, lib, sp, stream, args)
+
     alg_bytes = wb + 4 * k * m + 4 * n * m
     achieved = alg_bytes / t_launch / 1e9
     traffic = committed_traffic(wl.name)
@@ -449,6 +501,8 @@ def main() -> int:
     if q6:
         out["q6k"] = q6
     out["prefill_f16"] = prefill
+    if wide:
+        out["wide_batches"] = wide
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline(w, x, n, k, m, wb, y_last)

@@ -150,6 +150,12 @@ int make_plan_lines(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t
         }
     } else if (kernel == 7) {
         rpb = 16 * (nw / nslabs);            // a task for every wave
+    } else if (kernel == 6 && m > q4k::kMaxMStaged) {
+        // eight quads: each wave converts its own x, so workgroups cost no
+        // extra conversions; about two four-wave workgroups per CU (two
+        // waves a SIMD; measured on MI355X, 14336 x 4096 x 32: 148 us
+        // against 233 us with one)
+        rpb = 16 * ((ntiles + 511) / 512);
     } else {
         // at most about one workgroup per CU of a 256-CU part: each stages
         // all of x, which costs as much as decoding a few tiles
@@ -170,7 +176,8 @@ int make_plan_lines(int64_t n, int64_t k, int64_t m, const q4k_launch* o, size_t
         // the LDS (choices measured on MI355X: with fewer tiles than waves,
         // whole rows leave waves idle, 0.3-0.8 us on 16384-28672-row shapes)
         const bool fits = lds_x + (size_t)nslabs * rpb * 8 * m <= lds_max;
-        spt = (rpb / 16 >= nw || !fits) ? nslabs : 1;
+        const bool wide = kernel == 6 && m > q4k::kMaxMStaged;   // slab tasks measured faster
+        spt = ((rpb / 16 >= nw && !wide) || !fits) ? nslabs : 1;
     }
     const int64_t ncg = nslabs / spt;
     if (rpb > kInt32Max / (ncg * m)) {

@@ -19,10 +19,12 @@
  *    uses.rs: memory-layout doc of `batched_q4k_gemv_into`; turbospark-
  *    runtime 0.1.0, real_forward_dispatch.rs: doc of `encode_gemm_any`).
  *    The pages batch at most 8 vectors per call (uses.rs:
- *    `batched_q4k_gemv_into`, "max 8"); here 9-16 also run, in one pass over
- *    the weights, where the kernels that can hold them apply.  Anything else
- *    is refused by name, never looped (real_forward_dispatch.rs: doc of
- *    `encode_gemm_any`).
+ *    `batched_q4k_gemv_into`, "max 8"), except for 16 and 32, which share
+ *    one weight stream between warps (uses.rs: `batched_q4k_gemv_into` and
+ *    `batched_q4k_gemv_into_multi_warp`); here any 9-32 run, in one pass
+ *    over the weights, where the kernels that can hold them apply.
+ *    Anything else is refused by name, never looped (real_forward_dispatch.rs:
+ *    doc of `encode_gemm_any`).
  *  - Weights are uploaded once and reused by every call (realizar 0.8.5,
  *    q4k_gemv_cached.rs: doc of `q4k_gemv_cached`); the launch is
  *    asynchronous on the caller's stream and the caller synchronises
@@ -63,8 +65,8 @@ enum q4k_status {
     Q4K_ERR_SIZE = 3,        /* byte count does not match n rows of the format   */
     Q4K_ERR_ALIGN = 4,       /* a pointer (or a Q6_K row stride) is not 16-byte
                                 aligned                                         */
-    Q4K_ERR_UNSUPPORTED = 5, /* m > 16; 9-16 vectors where the one-pass
-                                kernels 5 and 6 do not apply; or a launch
+    Q4K_ERR_UNSUPPORTED = 5, /* m > 32; 9-32 vectors where the one-pass
+                                kernels 5-7 do not apply; or a launch
                                 option that cannot be honoured                  */
     Q4K_ERR_HIP = 1000       /* + hipError_t                                     */
 };
@@ -87,10 +89,10 @@ int q4k_load(void* w_dev, const void* src_host, size_t src_bytes,
  *  x : device, m*k f32, 16-byte aligned
  *  y : device, m*n f32, 16-byte aligned, fully overwritten (no accumulate)
  *  1 <= n <= 2^31-1, 256 <= k <= 2^31-1 with k % 256 == 0, 1 <= m <= 8.
- *  9 <= m <= 16 (beyond the pages' batch of 8): one pass over the weights on
- *  the sub-block matrix-core kernels (5-7) when w is 128-byte aligned and
- *  their LDS fits; otherwise Q4K_ERR_UNSUPPORTED.  m > 16:
- *  Q4K_ERR_UNSUPPORTED.  A batch is never split into several launches.
+ *  9 <= m <= 32 (beyond the pages' batch of 8): one pass over the weights on
+ *  the sub-block matrix-core kernels (5-7 up to 16 vectors, 6 beyond) when
+ *  w is 128-byte aligned and their LDS fits; otherwise Q4K_ERR_UNSUPPORTED.
+ *  m > 32: Q4K_ERR_UNSUPPORTED.  A batch is never split into several launches.
  * Asynchronous on `stream`; allocates nothing.  Results agree with the exact
  * dot product of the dequantized weights within 1e-5 * sum|w||x| per output
  * for every input whose exact result is finite (the tolerance the problem
@@ -154,7 +156,8 @@ const char* q4k_status_string(int rc);
  *   5  sub-block int8 matrix-core (m <= 16), one MFMA per sub-block and quad
  *      of vectors
  *   6  kernel 5 with x converted one superblock column at a time by each
- *      wave for itself (no whole x stage: any k and m)
+ *      wave for itself (no whole x stage: any k and m; the only kernel for
+ *      17-32 vectors, eight quads on four waves)
  *   7  kernel 5 with x converted once per workgroup, one column ahead, into
  *      a two-column window of every slab (one slab per task, eight waves;
  *      limits below; 16 * (8 / slabs) rows per workgroup by default)
