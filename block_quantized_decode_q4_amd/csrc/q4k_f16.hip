@@ -22,6 +22,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <type_traits>
 #include <mutex>
 
 #include "q4k_kernels.h"
@@ -59,7 +60,7 @@ f16_cvt_kernel(const float* __restrict__ x, _Float16* __restrict__ out, int64_t 
 // Grid: kGXcd * ceil(NT / kGXcd) * MT workgroups (MT, NT: tiles of x rows
 // and of mirror rows); k % 64 == 0.
 template <int BM, int BN>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256, 2)
 f16_gemm_kernel(const _Float16* __restrict__ w16, const _Float16* __restrict__ x16,
                 float* __restrict__ y, int m, int n, int k, int MT, int NT)
 {
@@ -104,26 +105,32 @@ f16_gemm_kernel(const _Float16* __restrict__ w16, const _Float16* __restrict__ x
         wsrc[i] = w16 + (int64_t)min(row_w0 + (idx >> 3), n - 1) * k + (idx & 7) * 8;
         woff[i] = kXs + (idx >> 3) * kGRow + (idx & 7) * 16;
     }
-    v4u_t xa[LA], wa[LB];
-    auto load = [&](int kb) __attribute__((always_inline)) {
+    // kSets register sets of loaded tiles: a set is refilled with the loads
+    // of step kb + 1 + kSets right after its tiles of step kb + 1 are staged,
+    // so a load has kSets steps of MFMAs to arrive in
+    constexpr int kSets = 2;
+    v4u_t xa[kSets][LA], wa[kSets][LB];
+    auto load = [&](int kb, auto set) __attribute__((always_inline)) {
+        constexpr int q = decltype(set)::value;
 #pragma unroll
         for (int i = 0; i < LA; ++i) {
-            xa[i] = *reinterpret_cast<const v4u_t*>(xsrc[i] + kb * kGK);
+            xa[q][i] = *reinterpret_cast<const v4u_t*>(xsrc[i] + kb * kGK);
         }
 #pragma unroll
         for (int i = 0; i < LB; ++i) {
-            wa[i] = *reinterpret_cast<const v4u_t*>(wsrc[i] + kb * kGK);
+            wa[q][i] = *reinterpret_cast<const v4u_t*>(wsrc[i] + kb * kGK);
         }
     };
-    auto stage = [&](int st) __attribute__((always_inline)) {
+    auto stage = [&](int st, auto set) __attribute__((always_inline)) {
+        constexpr int q = decltype(set)::value;
         unsigned char* base = smem + st * kStage;
 #pragma unroll
         for (int i = 0; i < LA; ++i) {
-            *reinterpret_cast<v4u_t*>(base + xoff[i]) = xa[i];
+            *reinterpret_cast<v4u_t*>(base + xoff[i]) = xa[q][i];
         }
 #pragma unroll
         for (int i = 0; i < LB; ++i) {
-            *reinterpret_cast<v4u_t*>(base + woff[i]) = wa[i];
+            *reinterpret_cast<v4u_t*>(base + woff[i]) = wa[q][i];
         }
     };
 
@@ -141,14 +148,20 @@ f16_gemm_kernel(const _Float16* __restrict__ w16, const _Float16* __restrict__ x
         }
     }
     const int KB = k / kGK;
-    load(0);
-    stage(0);
+    // set q holds steps q, q + kSets, q + 2 kSets, ...  Prologue: steps
+    // 0 .. kSets - 1 into the sets (past the end the last step again: no
+    // branch around a load), step 0 staged and its set refilled with step
+    // kSets
+    load(0, std::integral_constant<int, 0>());
+    load(min(1, KB - 1), std::integral_constant<int, 1>());
+    stage(0, std::integral_constant<int, 0>());
+    load(min(kSets, KB - 1), std::integral_constant<int, 0>());
     __syncthreads();
-    for (int kb = 0; kb < KB; ++kb) {
+    // step kb: its tiles are in LDS stage kb & 1; set (kb + 1) % kSets holds
+    // step kb + 1, staged after the MFMAs into the other stage and then
+    // refilled with step kb + 1 + kSets
+    auto step = [&](int kb, auto nset) __attribute__((always_inline)) {
         const int st = kb & 1;
-        // the next step's tiles (the last step loads and stages its own
-        // again, into the stage nobody reads any more: no branch around it)
-        load(min(kb + 1, KB - 1));
         const unsigned char* xs = smem + st * kStage;
         const unsigned char* ws = xs + kXs;
 #pragma unroll
@@ -173,8 +186,15 @@ f16_gemm_kernel(const _Float16* __restrict__ w16, const _Float16* __restrict__ x
                 }
             }
         }
-        stage(st ^ 1);
+        stage(st ^ 1, nset);
+        load(min(kb + 1 + kSets, KB - 1), nset);
         __syncthreads();
+    };
+    for (int kb = 0; kb < KB; kb += kSets) {
+        step(kb, std::integral_constant<int, 1>());
+        if (kb + 1 < KB) {
+            step(kb + 1, std::integral_constant<int, 0>());
+        }
     }
     // D[4 g + r][j] of block (a, b): x row (BM / 2) wm + 16 a + 4 g + r,
     // mirror row (BN / 2) wn + 16 b + j
