@@ -118,11 +118,11 @@ def test_f16_gemm_shapes(oracle_mod, m, n, k):
 
 
 @pytest.mark.parametrize("m,n,k,tile", [(512, 14336, 128, "128 x 128"), (512, 6144, 128, "64 x 128"),
-                                        (500, 4100, 192, "64 x 64")])
+                                        (500, 4100, 192, "64 x 128"), (500, 3000, 320, "64 x 64")])
 def test_f16_gemm_tile_variants(oracle_mod, m, n, k, tile):
     """Shapes whose tile count selects each tile size (at least 384 tiles of
-    128 x 128, else of 64 x 128, else 64 x 64), ragged where possible;
-    outputs checked on sampled blocks, the tile edges among them."""
+    128 x 128, else at least 256 of 64 x 128, else 64 x 64), ragged where
+    possible; outputs checked on sampled blocks, the tile edges among them."""
     rng = np.random.default_rng(4600 + n)
     w16 = oracle_mod.f16_cvt((rng.standard_normal((n, k)) * 0.05).astype(np.float32))
     x16 = oracle_mod.f16_cvt(rng.standard_normal((m, k)).astype(np.float32))
