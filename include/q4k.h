@@ -46,7 +46,10 @@
  *    detected before any HIP call and nothing is launched; nothing aborts or
  *    throws across the ABI.  A failing HIP call returns Q4K_ERR_HIP plus the
  *    hipError_t value.
- *  - Calls are thread-safe: the library keeps no mutable state.
+ *  - Calls are thread-safe.  The library's only state is set once per
+ *    device and read atomically: the device's LDS limit and the address of
+ *    the scratch array of q4k_f16_gemm_f32x_noalloc (whose calls, unlike
+ *    every other entry point's, share that array; see there).
  */
 #ifndef Q4K_H
 #define Q4K_H
