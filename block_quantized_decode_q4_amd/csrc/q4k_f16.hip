@@ -10,7 +10,10 @@
 // fill the chip) over k in steps of 64: both operands are k-contiguous
 // (x rows and mirror rows), staged through LDS in rows of 64 halves padded
 // to 144 bytes (consecutive rows start 16 bytes apart in the banks), two
-// stages so the next step's global loads overlap this step's MFMAs.  Wave
+// LDS stages and two register sets of loaded tiles, so a step's global
+// loads have two steps of MFMAs to arrive in.  (Mirror blocks loaded by
+// each wave straight into its operand registers, with only x staged,
+// measured 1.5-2.3 x slower.)  Wave
 // (wm, wn) of the 2 x 2 layout holds a quarter of the tile (64 x 64 for
 // 128 x 128) as 16 x 16 blocks of v_mfma_f32_16x16x32_f16 accumulators: lane l = 16 g + j holds
 // A[i = j][k = 8 g .. 8 g + 7] (an x row), B[k = 8 g .. 8 g + 7][j] (a
@@ -109,6 +112,7 @@ f16_gemm_kernel(const _Float16* __restrict__ w16, const _Float16* __restrict__ x
     // of step kb + 1 + kSets right after its tiles of step kb + 1 are staged,
     // so a load has kSets steps of MFMAs to arrive in
     constexpr int kSets = 2;
+    static_assert(kSets == 2, "the step loop below alternates two sets");
     v4u_t xa[kSets][LA], wa[kSets][LB];
     auto load = [&](int kb, auto set) __attribute__((always_inline)) {
         constexpr int q = decltype(set)::value;
