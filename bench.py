@@ -393,14 +393,22 @@ def main() -> int:
     # the same read at the GEMV's size: one weight copy per launch, cycling
     # through the copies as the steps do (the ceiling a launch of this size
     # reaches with plain loads)
+    # (the library call itself, as the timed steps make theirs, so that host
+    # overhead per call stays below a launch of this size)
     wbr = wb - wb % 16
     one_reps = max(50, min(2000, args.steps))
-    for i in range(20):
-        q4k.q4k_read_calibrate(ptrs[i % copies], wbr, cal_out, stream=sp)
+    cp = cal_out.data_ptr()
+
+    def read_one(i):
+        rc = lib.q4k_read_calibrate(ptrs[i % copies], wbr, cp, sp)
+        if rc != 0:
+            raise q4k.Q4KError(rc, "q4k_read_calibrate")
+    for i in range(200):
+        read_one(i)
     torch.cuda.synchronize()
     c0.record(stream)
     for i in range(one_reps):
-        q4k.q4k_read_calibrate(ptrs[i % copies], wbr, cal_out, stream=sp)
+        read_one(i)
     c1.record(stream)
     torch.cuda.synchronize()
     one_us = c0.elapsed_time(c1) * 1e3 / one_reps

@@ -16,7 +16,8 @@ constexpr int kSpan = kSpanSB * kQK;
 constexpr int kMaxM = 8;         // vectors per launch that every kernel takes
 constexpr int kMaxMStaged = 16;  // kernels 5 and 7: x of at most four vector quads in LDS
 constexpr int kMaxMWide = 32;    // kernel 6 (eight quads, x per wave and column)
-constexpr int kReadBlocks = 512;     // two 1024-lane workgroups per CU of a 256-CU part
+constexpr int kReadBlocks = 1024;    // four 512-lane workgroups per CU of a 256-CU part
+constexpr int kReadThreads = 512;
 
 // One resolved launch of the GEMV kernel.
 struct GemvPlan {
