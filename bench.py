@@ -21,8 +21,10 @@ Printed as one JSON line (rank 0):
                summary when it was taken on the current kernel source
   cpu_baseline the CPU oracle (f32 dequant + f64 dot, OpenMP) on the same
                workload; its sampled rows are also compared with the GPU y
-  calibration  a plain 16-byte-load streaming read over the rotation buffer:
-               the achievable read rate on this part
+  calibration  a plain 16-byte-load streaming read (the whole grid sweeping
+               the bytes in address order) over the rotation buffer and over
+               one weight copy per launch: the achievable read rate on this
+               part, and the one-launch read time of the workload's bytes
 """
 from __future__ import annotations
 
