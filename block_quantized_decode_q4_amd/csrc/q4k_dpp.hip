@@ -289,8 +289,10 @@ gemv_dot4_lines_kernel(const uint8_t* __restrict__ w, const float* __restrict__ 
             const uint4 q1 = *reinterpret_cast<const uint4*>(qa[cp] + 16);
             dot_math(h, q0, q1, c, corr);
         };
-        line_stream<NW, P>(w, x, n, S, rows_per_block, slabs_per_task, ring, issue_x, convert_x,
-                           step, task_end, slab_flag);
+        line_stream<NW, P, decltype(issue_x), decltype(convert_x), decltype(step),
+                    decltype(task_end), decltype(slab_flag), true>(
+            w, x, n, S, rows_per_block, slabs_per_task, ring, issue_x, convert_x, step, task_end,
+            slab_flag);
     }
 
     if (ncg > 1) {

@@ -84,7 +84,7 @@ __device__ __forceinline__ uint4 load_line_nt(const uint8_t* p)
 // line (slot 0) is dead once its last superblock has been read, and the
 // wave's LDS accesses complete in order.
 template <int NW, int P, typename IssueX, typename ConvertX, typename Step, typename TaskEnd,
-          typename SlabFlag = NoSlabFlag>
+          typename SlabFlag = NoSlabFlag, bool PREPUT = false>
 __device__ __forceinline__ void line_stream(const uint8_t* __restrict__ w,
                                             const float* __restrict__ x, int n, int S,
                                             int rows_per_block, int slabs_per_task,
@@ -177,9 +177,24 @@ __device__ __forceinline__ void line_stream(const uint8_t* __restrict__ w,
             lines[l][0] = load_line_nt(p[0]);
             lines[l][1] = load_line_nt(p[1]);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        convert_x();
+        if constexpr (PREPUT && P == 3) {
+            // lines 0 and 1 of the first slab into the ring now, their
+            // register slots refilled with lines 3 and 4 before the barrier
+#pragma unroll
+            for (int l = 0; l < 2; ++l) {
+                const uint32_t lpos = (uint32_t)l * 128u + 16u * (uint32_t)lunit;
+                *reinterpret_cast<uint4*>(ring + lrow * kRingRow + lpos) = lines[l][0];
+                *reinterpret_cast<uint4*>(ring + (8 + lrow) * kRingRow + lpos) = lines[l][1];
+                __builtin_amdgcn_sched_barrier(0x000F);
+                const uint8_t* p[2];
+                line_ptrs(sb0, l + P, p);
+                lines[l][0] = load_line_nt(p[0]);
+                lines[l][1] = load_line_nt(p[1]);
+            }
+        }
     }
-    __builtin_amdgcn_sched_barrier(0);
-    convert_x();
     __syncthreads();
 
     // Waves w and w + 4 of an 8-wave workgroup share a SIMD, and with equal
@@ -194,7 +209,8 @@ __device__ __forceinline__ void line_stream(const uint8_t* __restrict__ w,
         (ntasks - (wave - 4) + NW - 1) / NW == my_tasks) {
         __builtin_amdgcn_s_setprio(1);
     }
-    for (int sig = 0; sig < my_slabs; ++sig) {
+    auto slab_iter = [&](int sig, auto first) __attribute__((always_inline)) {
+        constexpr bool FIRST = decltype(first)::value;
         int tile, slab, tile_n, slab_n;
         slab_of(sig, tile, slab);
         slab_of(sig + 1, tile_n, slab_n);      // clamped: the last slab again at the end
@@ -226,10 +242,12 @@ __device__ __forceinline__ void line_stream(const uint8_t* __restrict__ w,
         auto slab_body = [&](auto corr) __attribute__((always_inline)) {
             static_for<8>([&](auto cpc) __attribute__((always_inline)) {
                 constexpr int cp = decltype(cpc)::value;
-                if constexpr (cp == 0) {
-                    put(std::integral_constant<int, 0>());
+                if constexpr (!(FIRST && cp == 0)) {
+                    if constexpr (cp == 0) {
+                        put(std::integral_constant<int, 0>());
+                    }
+                    put(std::integral_constant<int, cp + 1>());
                 }
-                put(std::integral_constant<int, cp + 1>());
                 if constexpr (kLookAhead<Step>) {
                     step(8 * slab + cp, 8 * slab + 8, 8 * slab_n, ring + j * kRingRow,
                          (uint32_t)(144 * cp), cp, true);
@@ -252,6 +270,16 @@ __device__ __forceinline__ void line_stream(const uint8_t* __restrict__ w,
         if (sig % slabs_per_task == slabs_per_task - 1) {
             task_end(wave + (sig / slabs_per_task) * NW);
         }
+    };
+    int sig0 = 0;
+    if constexpr (PREPUT && P == 3) {
+        if (my_slabs > 0) {
+            slab_iter(0, std::true_type());
+            sig0 = 1;
+        }
+    }
+    for (int sig = sig0; sig < my_slabs; ++sig) {
+        slab_iter(sig, std::false_type());
     }
 }
 

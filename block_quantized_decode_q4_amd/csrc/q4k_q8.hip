@@ -318,8 +318,10 @@ gemv_q8_lines_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
             const uint4 q1 = *reinterpret_cast<const uint4*>(qa[cp] + 16);
             dot_math(h, q0, q1, c);
         };
-        line_stream<NW, 3>(w, x, n, S, rows_per_block, slabs_per_task, ring, issue_x, convert_x,
-                           step, task_end);
+        line_stream<NW, 3, decltype(issue_x), decltype(convert_x), decltype(step),
+                    decltype(task_end), NoSlabFlag, true>(w, x, n, S, rows_per_block,
+                                                          slabs_per_task, ring, issue_x,
+                                                          convert_x, step, task_end);
     }
 
     if (ncg > 1) {
