@@ -133,7 +133,7 @@ __device__ __forceinline__ void convert_group_dot(const float4 (&v)[4], int G, b
 
 // ANY: rows of any whole number of superblocks (line_stream_any, four-line
 // rings, per-row start offsets); else S % 8 == 0 (line_stream).
-template <int NW, int P, int XC, bool ANY>
+template <int NW, int P, int XC, bool ANY, bool ONEBODY = false>
 __global__ void __launch_bounds__(NW * 64)
 gemv_dot4_lines_kernel(const uint8_t* __restrict__ w, const float* __restrict__ x,
                        float* __restrict__ y, int n, int S, int rows_per_block, int slabs_per_task)
@@ -290,7 +290,7 @@ gemv_dot4_lines_kernel(const uint8_t* __restrict__ w, const float* __restrict__ 
             dot_math(h, q0, q1, c, corr);
         };
         line_stream<NW, P, decltype(issue_x), decltype(convert_x), decltype(step),
-                    decltype(task_end), decltype(slab_flag), true>(
+                    decltype(task_end), decltype(slab_flag), true, ONEBODY>(
             w, x, n, S, rows_per_block, slabs_per_task, ring, issue_x, convert_x, step, task_end,
             slab_flag);
     }
@@ -316,6 +316,17 @@ static hipError_t launch_dot4_x(const GemvPlan& p, const uint8_t* w, const float
             hipLaunchKernelGGL((gemv_dot4_lines_kernel<NW, 3, XC, true>), dim3(p.grid),
                                dim3(NW * 64), p.lds_bytes, stream, w, x, y, p.n, p.S,
                                p.rows_per_block, p.cols_per_task / 8);
+            return hipGetLastError();
+        }
+    }
+    if constexpr (P == 3) {
+        // one slab per task: the slab body without the per-slab choice of a
+        // correction-free copy (FFN-down 11.20 -> 11.01 us; whole-row tasks,
+        // as on the LM head, keep the two copies: 14.55 against 14.74 us)
+        if (p.cols_per_task == 8) {
+            hipLaunchKernelGGL((gemv_dot4_lines_kernel<NW, 3, XC, false, true>), dim3(p.grid),
+                               dim3(NW * 64), p.lds_bytes, stream, w, x, y, p.n, p.S,
+                               p.rows_per_block, 1);
             return hipGetLastError();
         }
     }

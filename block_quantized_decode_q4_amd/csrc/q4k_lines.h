@@ -84,7 +84,7 @@ __device__ __forceinline__ uint4 load_line_nt(const uint8_t* p)
 // line (slot 0) is dead once its last superblock has been read, and the
 // wave's LDS accesses complete in order.
 template <int NW, int P, typename IssueX, typename ConvertX, typename Step, typename TaskEnd,
-          typename SlabFlag = NoSlabFlag, bool PREPUT = false>
+          typename SlabFlag = NoSlabFlag, bool PREPUT = false, bool ONEBODY = false>
 __device__ __forceinline__ void line_stream(const uint8_t* __restrict__ w,
                                             const float* __restrict__ x, int n, int S,
                                             int rows_per_block, int slabs_per_task,
@@ -258,7 +258,13 @@ __device__ __forceinline__ void line_stream(const uint8_t* __restrict__ w,
                 }
             });
         };
-        if constexpr (kFlagged<Step>) {
+        if constexpr (kFlagged<Step> && ONEBODY) {
+            // one body whose steps test their columns themselves: no join of
+            // two bodies' line registers (whose copies wait for every load in
+            // flight); measured faster with one slab per task
+            (void)slab_flag;
+            slab_body(std::true_type());
+        } else if constexpr (kFlagged<Step>) {
             if (slab_flag(slab)) {
                 slab_body(std::true_type());
             } else {
